@@ -1,0 +1,42 @@
+"""CPU oracle for the blockwise NF4 quantize / dequantize / dequant-matmul path.
+
+TEST INFRASTRUCTURE ONLY.  This package is the slow, plain, obviously-correct
+reference the HIP library is checked against.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import it; the product path (``dequant_gemm_nf4_amd``) never does, and the
+two share no code, tables or constant generators.
+
+Every function follows the passage of the pages it cites; where the pages are
+silent the reading taken is stated at the function.  Parity status:
+
+* codebook            -- pinned (invariants, mpmath / scipy recomputation,
+                         CDF round trip)
+* thresholds / encode -- pinned (brute-force nearest level in fp64, ties)
+* pack                -- pinned (hand-built bytes)
+* double quant        -- pinned (exact rational mean, bounds, saturation)
+* dequant             -- pinned (absmax 1 block, bounds)
+* matmul              -- pinned (unit vector, brute-force loops)
+* memory arithmetic   -- pinned against the figures the pages print
+"""
+
+from .nf4 import (  # noqa: F401
+    BLOCKSIZE,
+    DQ_GROUP,
+    bf16_bits_to_f32,
+    f32_to_bf16_bits,
+    normal_quantile,
+    codebook,
+    thresholds,
+    block_absmax,
+    encode,
+    pack_nibbles,
+    unpack_nibbles,
+    double_quant,
+    block_scales,
+    quantize,
+    dequantize,
+    matmul_ref,
+    dequant_matmul_ref,
+    rel_frobenius,
+    storage_bytes,
+)

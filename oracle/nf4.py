@@ -1,0 +1,335 @@
+"""Plain NumPy oracle of blockwise NF4 quantization and the 4-bit-storage /
+16-bit-compute linear layer.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Nothing here is tuned:
+each step is written the way the pages state it, with NumPy's IEEE binary32
+operations (round-to-nearest-even, no fusion) wherever the stored format is
+binary32, and binary64 for the reference matmul.
+
+Sources (five web pages about bitsandbytes; cited by page and section):
+
+* mlqm.cn bitsandbytes article (news/394670), section 3.2 "4bit: NF4":
+  16 non-uniform levels placed by the normal density, dense near zero,
+  sparse at the ends.
+* same article, section 3.3 "double quantization": one scale per block,
+  stored as FP32; the scales are themselves quantized a second time, saving a
+  few tenths of a bit per parameter.
+* same article, section 3.4 "compute dtype": weights are stored in 4 bits
+  and dequantized to FP16/BF16 before the matrix multiply ("4-bit storage,
+  16-bit compute").
+* pomoai.com bitsandbytes overview, module list: ``bitsandbytes.functional``
+  holds the blockwise quantization and the NF4 format; ``Linear4bit``
+  replaces ``torch.nn.Linear`` (weight laid out [out_features, in_features]).
+
+Parameters the pages leave open (blocksize 64, second-level groups of 256,
+int8 second level with the mean removed, lower-index tie rule) are the ones
+the build fixes for this path; every such reading is noted where it is used.
+"""
+
+from __future__ import annotations
+
+import math
+import statistics
+
+import numpy as np
+
+BLOCKSIZE = 64      # weights per first-level block (reading: fixed at 64)
+DQ_GROUP = 256      # first-level scales per second-level group (reading)
+ZERO_CODE = 7       # index of the exact 0.0 level in the ascending codebook
+
+
+# --------------------------------------------------------------------------
+# bfloat16 <-> binary32
+# --------------------------------------------------------------------------
+def bf16_bits_to_f32(bits) -> np.ndarray:
+    """Widen bfloat16 bit patterns (uint16) to binary32.  Exact: bfloat16 is
+    the top half of a binary32."""
+    u = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (u.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def f32_to_bf16_bits(values) -> np.ndarray:
+    """Round binary32 to bfloat16 with round-to-nearest, ties to even, and
+    return the bit patterns (uint16).  The mlqm.cn article, section 3.4, has
+    the weights dequantized to BF16 for the multiply; RNE is the IEEE default
+    rounding (reading: the pages name no rounding mode)."""
+    f = np.ascontiguousarray(values, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    # Add just under half an ulp of the kept part, plus one if the kept part
+    # is odd: a tie then rounds to the even neighbour.
+    kept_lsb = (u >> np.uint64(16)) & np.uint64(1)
+    out = ((u + np.uint64(0x7FFF) + kept_lsb) >> np.uint64(16)).astype(np.uint16)
+    nan = np.isnan(f)
+    if nan.any():  # keep NaNs NaN (quiet bit set) instead of rounding to inf
+        out[nan] = ((u[nan] >> np.uint64(16)) | np.uint64(0x40)).astype(np.uint16)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Step 1: the NF4 codebook
+# --------------------------------------------------------------------------
+# Probability offset of the outermost quantile.  Reading: the pages only say
+# the levels follow the normal density with an exact zero; the construction
+# below is the one of the QLoRA work the pages credit NF4 to (pomoai.com
+# overview, QLoRA paragraph; mlqm.cn article section 5.4): the ends sit at
+# the average of the 1/30 and 1/32 tail probabilities.
+NF4_OFFSET = 1.0 - 0.5 * (1.0 / 30.0 + 1.0 / 32.0)
+
+
+def normal_quantile(p: float) -> float:
+    """Inverse of the standard normal CDF, in binary64.
+
+    Library primitive: Python's ``statistics.NormalDist.inv_cdf`` (Wichura's
+    AS241 algorithm, relative error about 1e-16)."""
+    return statistics.NormalDist(0.0, 1.0).inv_cdf(p)
+
+
+def codebook() -> np.ndarray:
+    """The 16 NF4 levels, ascending, as binary32.
+
+    mlqm.cn article, section 3.2: the 16 levels are not evenly spaced but
+    follow the normal density, dense near 0 and sparse at the two ends.
+    Construction (reading, see NF4_OFFSET): 8 positive levels at the
+    standard-normal quantiles of 8 probabilities evenly spaced from the offset
+    down towards 1/2 (1/2 itself excluded), 7 negative levels mirrored from 7
+    evenly spaced probabilities over the same span, and an exact 0.  All are
+    divided by the outermost quantile so the ends are exactly -1 and +1.
+    Arithmetic in binary64, one rounding to binary32 at the end.
+    """
+    top = normal_quantile(NF4_OFFSET)
+    positive = [normal_quantile(NF4_OFFSET + i * (0.5 - NF4_OFFSET) / 8.0)
+                for i in range(8)]
+    negative = [-normal_quantile(NF4_OFFSET + i * (0.5 - NF4_OFFSET) / 7.0)
+                for i in range(7)]
+    values = sorted(negative + [0.0] + positive)
+    return np.array([v / top for v in values], dtype=np.float64).astype(np.float32)
+
+
+def thresholds(levels: np.ndarray) -> np.ndarray:
+    """Decision thresholds T[0..14] for nearest-level encoding.
+
+    The midpoint m_i of levels i and i+1 is exact in binary64.  T_i is the
+    smallest binary32 strictly above m_i, so that ``#{i : x >= T_i}`` is the
+    index of the nearest level and a value exactly on a midpoint goes to the
+    LOWER index (the tie rule this path fixes; the pages state none)."""
+    L = np.asarray(levels, dtype=np.float32).astype(np.float64)
+    out = np.empty(15, dtype=np.float32)
+    for i in range(15):
+        mid = (L[i] + L[i + 1]) / 2.0
+        t = np.float32(mid)
+        if float(t) <= mid:
+            t = np.nextafter(t, np.float32(np.inf), dtype=np.float32)
+        out[i] = t
+    return out
+
+
+# --------------------------------------------------------------------------
+# Steps 2-4: block absmax, normalise, encode, pack
+# --------------------------------------------------------------------------
+def _blocks(n: int, blocksize: int) -> int:
+    return -(-n // blocksize)
+
+
+def block_absmax(wf: np.ndarray, blocksize: int = BLOCKSIZE) -> np.ndarray:
+    """a_b = max |w| over each run of ``blocksize`` consecutive elements of the
+    flat weight (the last block may be short).  mlqm.cn article, section 3.3:
+    one scale per block, stored as FP32; the absmax scale is the basic
+    data-free quantizer the article points back to (section 2.3)."""
+    wf = np.ascontiguousarray(wf, dtype=np.float32).ravel()
+    n = wf.size
+    nb = _blocks(n, blocksize)
+    padded = np.zeros(nb * blocksize, dtype=np.float32)
+    padded[:n] = np.abs(wf)
+    return padded.reshape(nb, blocksize).max(axis=1)
+
+
+def encode(wf: np.ndarray, absmax: np.ndarray, thr: np.ndarray,
+           blocksize: int = BLOCKSIZE) -> np.ndarray:
+    """4-bit code of every weight (uint8 values 0..15).
+
+    Normalise into [-1, 1] with the block's binary32 reciprocal,
+    x = fl32(w * fl32(1 / a_b)) (reading: multiply by the reciprocal rather
+    than divide), then count the thresholds at or below x, which picks the
+    nearest level (section 3.2).  A block whose absmax is 0 is all zero
+    weights and takes the zero level's code for every element (reading)."""
+    wf = np.ascontiguousarray(wf, dtype=np.float32).ravel()
+    n = wf.size
+    block = np.arange(n) // blocksize
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        recip = (np.float32(1.0) / absmax.astype(np.float32)).astype(np.float32)
+        x = (wf * recip[block]).astype(np.float32)
+    codes = np.zeros(n, dtype=np.uint8)
+    with np.errstate(invalid="ignore"):
+        for t in np.asarray(thr, dtype=np.float32):
+            codes += (x >= t).astype(np.uint8)
+    zero_block = absmax[block] == 0
+    codes[zero_block] = ZERO_CODE
+    return codes
+
+
+def pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """Two codes per byte ("4-bit storage", section 3.4).  Reading: the even
+    (first) element goes in the high nibble.  The element count must be
+    even."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8).ravel()
+    if c.size % 2:
+        raise ValueError("odd element count cannot be packed two per byte")
+    return ((c[0::2] << np.uint8(4)) | c[1::2]).astype(np.uint8)
+
+
+def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
+    """Inverse of pack_nibbles."""
+    p = np.ascontiguousarray(packed, dtype=np.uint8).ravel()
+    out = np.empty(p.size * 2, dtype=np.uint8)
+    out[0::2] = p >> np.uint8(4)
+    out[1::2] = p & np.uint8(0x0F)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Step 5: double quantization of the first-level scales
+# --------------------------------------------------------------------------
+def double_quant(absmax: np.ndarray, group: int = DQ_GROUP):
+    """Quantize the FP32 block scales a second time (section 3.3: first
+    quantization gives the scales, the second compresses them).
+
+    Readings: remove the mean of all scales, then symmetric absmax int8
+    quantization in groups of ``group`` consecutive scales (last group may be
+    short).
+
+    * mean: S = sum of a_b, correctly rounded to binary64 (``math.fsum``),
+      mu = fl32(S / nb) with the division in binary64;
+    * c_b = fl32(a_b - mu);
+    * s_g = max |c_b| over the group;
+    * q_b = round-half-even(fl32(fl32(c_b / s_g) * 127)) in [-127, 127];
+      a group with s_g = 0 stores q_b = 0.
+
+    Returns (q int8[nb], s float32[ng], mu float32).
+    """
+    a = np.ascontiguousarray(absmax, dtype=np.float32).ravel()
+    nb = a.size
+    total = math.fsum(a.astype(np.float64).tolist())
+    mean = np.float32(total / nb)
+    centred = (a - mean).astype(np.float32)
+    ng = _blocks(nb, group)
+    padded = np.zeros(ng * group, dtype=np.float32)
+    padded[:nb] = np.abs(centred)
+    s = padded.reshape(ng, group).max(axis=1).astype(np.float32)
+    g = np.arange(nb) // group
+    q = np.zeros(nb, dtype=np.int8)
+    live = s[g] > 0
+    t = (centred[live] / s[g][live]).astype(np.float32)
+    u = (t * np.float32(127.0)).astype(np.float32)
+    q[live] = np.rint(u).astype(np.int8)
+    return q, s, mean
+
+
+def block_scales(state: dict) -> np.ndarray:
+    """The per-block scale the dequantizer uses, binary32.
+
+    Without double quant it is the stored a_b.  With it (reading):
+    step_g = fl32(s_g / 127), a_hat_b = fl32(fl32(q_b * step_g) + mu), each
+    operation rounded on its own (no fused multiply-add)."""
+    if not state["double_quant"]:
+        return np.asarray(state["absmax"], dtype=np.float32)
+    q = np.asarray(state["absmax"], dtype=np.int8)
+    s = np.asarray(state["absmax2"], dtype=np.float32)
+    mean = np.float32(state["absmax_mean"])
+    group = state.get("group", DQ_GROUP)
+    step = (s / np.float32(127.0)).astype(np.float32)
+    g = np.arange(q.size) // group
+    prod = (q.astype(np.float32) * step[g]).astype(np.float32)
+    return (prod + mean).astype(np.float32)
+
+
+def quantize(w_bits: np.ndarray, double_quant_on: bool,
+             blocksize: int = BLOCKSIZE, group: int = DQ_GROUP) -> dict:
+    """Blockwise NF4 quantize-on-load of a bfloat16 weight (bit patterns).
+
+    Returns a dict with ``codes`` (uint8[n]), ``packed`` (uint8[n/2]) and the
+    quant state: ``absmax`` (float32[nb], or int8[nb] with double quant),
+    ``absmax2`` (float32[ng]) and ``absmax_mean`` (float32) with double
+    quant, plus ``absmax_fp32`` (the first-level scales before the second
+    quantization)."""
+    wf = bf16_bits_to_f32(np.ascontiguousarray(w_bits).ravel())
+    levels = codebook()
+    thr = thresholds(levels)
+    a = block_absmax(wf, blocksize)
+    codes = encode(wf, a, thr, blocksize)
+    out = {
+        "n": wf.size,
+        "blocksize": blocksize,
+        "double_quant": bool(double_quant_on),
+        "group": group,
+        "codes": codes,
+        "packed": pack_nibbles(codes),
+        "absmax_fp32": a,
+    }
+    if double_quant_on:
+        q, s, mean = double_quant(a, group)
+        out.update(absmax=q, absmax2=s, absmax_mean=mean)
+    else:
+        out.update(absmax=a, absmax2=None, absmax_mean=None)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Step 6: dequantize to bfloat16
+# --------------------------------------------------------------------------
+def dequantize(packed: np.ndarray, state: dict, n: int | None = None) -> np.ndarray:
+    """W_hat_j = bf16(fl32(L[c_j] * a_hat_b)) as bfloat16 bit patterns
+    (section 3.4: dequantize back to the 16-bit compute dtype, BF16)."""
+    codes = unpack_nibbles(packed)
+    if n is None:
+        n = codes.size
+    codes = codes[:n]
+    levels = codebook()
+    blocksize = state.get("blocksize", BLOCKSIZE)
+    scale = block_scales(state)
+    b = np.arange(n) // blocksize
+    v = (levels[codes] * scale[b]).astype(np.float32)
+    return f32_to_bf16_bits(v)
+
+
+# --------------------------------------------------------------------------
+# Step 7/8: the 4-bit-storage / 16-bit-compute linear layer
+# --------------------------------------------------------------------------
+def matmul_ref(x_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+    """Y = X . W^T in binary64 (nn.Linear orientation, no bias; pomoai.com
+    overview, Linear4bit replacing torch.nn.Linear).  X is [M, K], W is
+    [N, K], both bfloat16 bit patterns; the result is float64 [M, N].
+    Library primitive: NumPy's binary64 matmul."""
+    x = bf16_bits_to_f32(x_bits).astype(np.float64)
+    w = bf16_bits_to_f32(w_bits).astype(np.float64)
+    return x @ w.T
+
+
+def dequant_matmul_ref(x_bits: np.ndarray, packed: np.ndarray, state: dict,
+                       N: int, K: int) -> np.ndarray:
+    """The reference the dequant-GEMV/GEMM is compared to: dequantize the
+    4-bit weight to BF16 (step 6), then multiply in binary64."""
+    w_hat = dequantize(packed, state, N * K).reshape(N, K)
+    return matmul_ref(np.asarray(x_bits).reshape(-1, K), w_hat)
+
+
+def rel_frobenius(y, y_ref) -> float:
+    """||y - y_ref||_F / ||y_ref||_F in binary64."""
+    y = np.asarray(y, dtype=np.float64)
+    r = np.asarray(y_ref, dtype=np.float64)
+    den = np.linalg.norm(r)
+    num = np.linalg.norm(y - r)
+    return float(num / den) if den > 0 else float(num)
+
+
+# --------------------------------------------------------------------------
+# Memory arithmetic
+# --------------------------------------------------------------------------
+def storage_bytes(n: int, double_quant_on: bool, blocksize: int = BLOCKSIZE,
+                  group: int = DQ_GROUP) -> int:
+    """Bytes a quantized tensor of n weights occupies: n/2 of packed codes,
+    plus FP32 scales per block (section 3.3, ordinary quantization), or int8
+    scales per block + FP32 per group + the FP32 mean (double quantization)."""
+    nb = _blocks(n, blocksize)
+    if not double_quant_on:
+        return n // 2 + 4 * nb
+    return n // 2 + nb + 4 * _blocks(nb, group) + 4

@@ -1,0 +1,412 @@
+"""Pins of the CPU oracle against things other than itself: closed forms,
+independent library routines (scipy, mpmath, PyTorch's bf16 cast), brute
+force on small inputs, invariants, and the figures the pages print
+(tests/golden/pages_figures.json).  CPU only."""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import nf4
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_figures.json")
+
+
+def f32_ulp(x) -> float:
+    x = np.float32(abs(x))
+    return float(np.nextafter(x, np.float32(np.inf), dtype=np.float32) - x)
+
+
+# --------------------------------------------------------------------------
+# bf16 rounding
+# --------------------------------------------------------------------------
+def test_bf16_rounding_matches_torch():
+    import torch
+
+    rng = np.random.default_rng(7)
+    f = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32) * np.float32(3.0),
+        (rng.standard_normal(1000) * 1e30).astype(np.float32),
+        np.array([0.0, -0.0, 1.0, -1.0, 3.0e38, -3.0e38, 1e-40, -1e-40], np.float32),
+    ])
+    # exact ties: low 16 bits 0x8000, both parities of the kept part
+    ties = (rng.integers(0, 2**15, 4000).astype(np.uint32) << 16) | np.uint32(0x8000)
+    f = np.concatenate([f, ties.view(np.float32)[np.isfinite(ties.view(np.float32))]])
+    ours = oracle.f32_to_bf16_bits(f)
+    ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_bf16_widen_exact():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f = oracle.bf16_bits_to_f32(bits)
+    back = oracle.f32_to_bf16_bits(f)
+    finite = np.isfinite(f)
+    assert np.array_equal(back[finite], bits[finite])
+
+
+# --------------------------------------------------------------------------
+# Standard normal quantile
+# --------------------------------------------------------------------------
+def test_normal_quantile_vs_scipy_and_cdf():
+    from scipy import special
+
+    for p in np.linspace(0.5, 0.99, 491):
+        x = oracle.normal_quantile(float(p))
+        assert x == pytest.approx(float(special.ndtri(p)), rel=1e-14, abs=1e-15)
+        # closed-form round trip through the CDF Phi(x) = erfc(-x/sqrt2)/2
+        assert 0.5 * math.erfc(-x / math.sqrt(2.0)) == pytest.approx(float(p), rel=1e-14)
+    assert oracle.normal_quantile(0.5) == 0.0
+    assert oracle.normal_quantile(0.975) == pytest.approx(-oracle.normal_quantile(0.025), rel=1e-15)
+
+
+# --------------------------------------------------------------------------
+# Codebook
+# --------------------------------------------------------------------------
+def test_codebook_invariants():
+    L = oracle.codebook()
+    assert L.dtype == np.float32 and L.shape == (16,)
+    assert np.all(np.diff(L) > 0)
+    assert L[0] == np.float32(-1.0) and L[7] == np.float32(0.0) and L[15] == np.float32(1.0)
+    assert np.sum(L < 0) == 7 and np.sum(L > 0) == 8
+    assert np.all(np.abs(L) <= 1)
+    # dense near 0, sparse at the ends (mlqm.cn article, section 3.2):
+    # gaps grow monotonically moving away from zero on each side.
+    gaps = np.diff(L.astype(np.float64))
+    assert np.all(np.diff(gaps[7:]) > 0)      # positive side, 0 -> +1
+    assert np.all(np.diff(gaps[:7]) < 0)      # negative side, -1 -> 0
+
+
+def test_codebook_is_correctly_rounded_exact_quantiles():
+    """Recompute each level in 50-digit arithmetic (mpmath erfinv) from the
+    stated construction; the oracle's binary32 level must be the correctly
+    rounded value."""
+    mpmath = pytest.importorskip("mpmath")
+    mpmath.mp.dps = 50
+    d = mpmath.mpf(1) - mpmath.mpf(1) / 2 * (mpmath.mpf(1) / 30 + mpmath.mpf(1) / 32)
+
+    def q(p):
+        return mpmath.sqrt(2) * mpmath.erfinv(2 * p - 1)
+
+    top = q(d)
+    half = mpmath.mpf(1) / 2
+    pos = [q(d + i * (half - d) / 8) / top for i in range(8)]
+    neg = [-q(d + i * (half - d) / 7) / top for i in range(7)]
+    exact = sorted(neg + [mpmath.mpf(0)] + pos)
+    L = oracle.codebook()
+    for li, ei in zip(L, exact):
+        err = abs(mpmath.mpf(float(li)) - ei)
+        assert err <= mpmath.mpf(f32_ulp(li)) / 2 * (1 + mpmath.mpf(2) ** -20) + mpmath.mpf(10) ** -45
+
+
+def test_codebook_levels_are_the_stated_quantiles():
+    """Phi(L_i * Phi^-1(offset)) must give back the evenly spaced
+    probabilities (positive side: 8 steps from the offset toward 1/2; negative
+    side mirrored, 7 steps)."""
+    from scipy.stats import norm
+
+    L = oracle.codebook().astype(np.float64)
+    top = oracle.normal_quantile(nf4.NF4_OFFSET)
+    d = nf4.NF4_OFFSET
+    pos = L[8:][::-1]      # +1 .. smallest positive
+    neg = -L[:7]           # 1 .. smallest |negative|
+    for i, v in enumerate(pos):
+        assert norm.cdf(v * top) == pytest.approx(d + i * (0.5 - d) / 8, abs=3e-8)
+    for i, v in enumerate(neg):
+        assert norm.cdf(v * top) == pytest.approx(d + i * (0.5 - d) / 7, abs=3e-8)
+
+
+# --------------------------------------------------------------------------
+# Thresholds and encode
+# --------------------------------------------------------------------------
+def test_thresholds_bracket_midpoints():
+    L = oracle.codebook().astype(np.float64)
+    T = oracle.thresholds(oracle.codebook())
+    for i in range(15):
+        m = Fraction(float(L[i])) / 2 + Fraction(float(L[i + 1])) / 2
+        assert Fraction(float(T[i])) > m
+        below = np.nextafter(T[i], np.float32(-np.inf), dtype=np.float32)
+        assert Fraction(float(below)) <= m
+
+
+def brute_codes(x: np.ndarray) -> np.ndarray:
+    """argmin_i |x - L_i| in binary64 (exact for binary32 x), lowest index
+    on ties -- independent of the threshold table."""
+    L = oracle.codebook().astype(np.float64)
+    d = np.abs(x.astype(np.float64)[:, None] - L[None, :])
+    return np.argmin(d, axis=1).astype(np.uint8)  # argmin returns the first minimum
+
+
+def _encode_unit(x):
+    # a block absmax of exactly 1 makes the normalisation the identity
+    x = np.asarray(x, dtype=np.float32)
+    n = x.size
+    pad = (-n) % 64
+    xx = np.concatenate([x, np.zeros(pad, np.float32)])
+    a = np.ones(xx.size // 64, dtype=np.float32)
+    return oracle.encode(xx, a, oracle.thresholds(oracle.codebook()))[:n]
+
+
+def test_encode_matches_bruteforce_near_every_threshold():
+    T = oracle.thresholds(oracle.codebook())
+    xs = []
+    for t in T:
+        v = np.float32(t)
+        lo = hi = v
+        xs.append(v)
+        for _ in range(64):
+            lo = np.nextafter(lo, np.float32(-np.inf), dtype=np.float32)
+            hi = np.nextafter(hi, np.float32(np.inf), dtype=np.float32)
+            xs += [lo, hi]
+    rng = np.random.default_rng(11)
+    xs = np.concatenate([np.array(xs, np.float32),
+                         rng.uniform(-1, 1, 200000).astype(np.float32),
+                         np.array([-1.0, 1.0, 0.0, -0.0], np.float32)])
+    assert np.array_equal(_encode_unit(xs), brute_codes(xs))
+
+
+def test_exact_midpoint_ties_go_to_lower_index():
+    L = oracle.codebook().astype(np.float64)
+    found = 0
+    for i in range(15):
+        m = (L[i] + L[i + 1]) / 2
+        if float(np.float32(m)) == m:         # midpoint representable in binary32
+            found += 1
+            c = _encode_unit(np.array([m], np.float32))[0]
+            assert c == i
+            assert brute_codes(np.array([m], np.float32))[0] == i
+    assert found >= 1
+
+
+def test_encode_exhaustive_bf16_against_bruteforce():
+    """Every finite bf16 weight, in blocks whose absmax sweeps many binades;
+    codes from the full quantize path vs brute-force nearest level of
+    x = fl32(w * fl32(1/a))."""
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f = oracle.bf16_bits_to_f32(allbits)
+    rng = np.random.default_rng(5)
+    anchors = oracle.f32_to_bf16_bits(
+        np.float32(2.0) ** rng.uniform(-30, 30, 24).astype(np.float32) *
+        rng.uniform(1, 2, 24).astype(np.float32))
+    anchors = np.concatenate([anchors, oracle.f32_to_bf16_bits(np.array([1.0, 0.02, 3.0], np.float32))])
+    for ab in anchors:
+        a = oracle.bf16_bits_to_f32(np.array([ab]))[0]
+        ok = np.isfinite(f) & (np.abs(f) <= a)
+        w = allbits[ok]
+        # lay out blocks of 63 weights + the anchor so each block's absmax is a
+        nblk = -(-w.size // 63)
+        body = np.zeros(nblk * 63, np.uint16)
+        body[:w.size] = w
+        blocks = np.concatenate([body.reshape(nblk, 63),
+                                 np.full((nblk, 1), ab, np.uint16)], axis=1).ravel()
+        q = oracle.quantize(blocks, False)
+        assert np.all(q["absmax"] == a)
+        r = np.float32(1.0) / np.float32(a)
+        x = (oracle.bf16_bits_to_f32(blocks) * r).astype(np.float32)
+        assert np.array_equal(q["codes"], brute_codes(x))
+
+
+def test_reconstruction_error_bound():
+    """|w - L[c] * a_b| <= a_b * (largest half gap) (+ binary32 slack), and
+    per element within half the gap around its level."""
+    L = oracle.codebook().astype(np.float64)
+    hmax = np.max(np.diff(L)) / 2
+    rng = np.random.default_rng(3)
+    for sigma in (0.02, 1.0, 300.0):
+        w = oracle.f32_to_bf16_bits(rng.standard_normal(64 * 500).astype(np.float32) * np.float32(sigma))
+        q = oracle.quantize(w, False)
+        wf = oracle.bf16_bits_to_f32(w).astype(np.float64)
+        a = np.repeat(q["absmax"].astype(np.float64), 64)
+        rec = L[q["codes"]] * a
+        assert np.all(np.abs(wf - rec) <= a * hmax * (1 + 2.0 ** -20))
+        # bf16 dequant adds at most half a bf16 ulp
+        deq = oracle.bf16_bits_to_f32(oracle.dequantize(q["packed"], q)).astype(np.float64)
+        assert np.all(np.abs(wf - deq) <= a * hmax * (1 + 2.0 ** -20) + np.abs(rec) * 2.0 ** -8)
+
+
+def test_zero_block_and_partial_block():
+    w = np.zeros(64 + 10, dtype=np.uint16)            # one zero block + a 10-wide tail
+    w[64:] = oracle.f32_to_bf16_bits(np.linspace(-0.5, 0.5, 10).astype(np.float32))
+    q = oracle.quantize(w, False)
+    assert q["absmax"].size == 2 and q["absmax"][0] == 0 and q["absmax"][1] == np.float32(0.5)
+    assert np.all(q["codes"][:64] == 7)
+    assert q["codes"][64] == 0 and q["codes"][73] == 15
+    deq = oracle.dequantize(q["packed"], q, w.size)
+    assert np.all(deq[:64] == 0)      # +0.0, not -0.0
+
+
+def test_pack_nibbles_hand_built():
+    codes = np.array([1, 2, 3, 4, 15, 0, 7, 8], np.uint8)
+    packed = oracle.pack_nibbles(codes)
+    assert packed.tolist() == [0x12, 0x34, 0xF0, 0x78]
+    assert np.array_equal(oracle.unpack_nibbles(packed), codes)
+    with pytest.raises(ValueError):
+        oracle.pack_nibbles(np.zeros(3, np.uint8))
+
+
+# --------------------------------------------------------------------------
+# Double quantization
+# --------------------------------------------------------------------------
+def test_double_quant_hand_example():
+    a = np.array([1.0, 2.0, 3.0], np.float32)
+    q, s, mean = oracle.double_quant(a)
+    assert mean == np.float32(2.0)
+    assert s.tolist() == [1.0]
+    assert q.tolist() == [-127, 0, 127]
+
+
+def test_double_quant_mean_is_exact_then_rounded():
+    rng = np.random.default_rng(9)
+    a = oracle.bf16_bits_to_f32(oracle.f32_to_bf16_bits(
+        np.abs(rng.standard_normal(3000)).astype(np.float32) * np.float32(0.05)))
+    a[::97] *= np.float32(2.0 ** 12)         # spread over many binades
+    q, s, mean = oracle.double_quant(a)
+    exact = sum(Fraction(float(v)) for v in a) / a.size
+    assert abs(Fraction(float(mean)) - exact) <= Fraction(f32_ulp(mean)) / 2 * (1 + Fraction(1, 2 ** 20))
+
+
+def test_double_quant_bounds_and_saturation():
+    rng = np.random.default_rng(4)
+    for nb in (1, 255, 256, 257, 1000, 4096 + 3):
+        a = oracle.bf16_bits_to_f32(oracle.f32_to_bf16_bits(
+            np.abs(rng.standard_normal(nb)).astype(np.float32) * np.float32(0.06)))
+        q, s, mean = oracle.double_quant(a)
+        ng = -(-nb // 256)
+        assert q.shape == (nb,) and s.shape == (ng,)
+        assert np.all(q >= -127) and np.all(q <= 127)
+        g = np.arange(nb) // 256
+        for gi in range(ng):
+            sel = g == gi
+            if s[gi] > 0:
+                assert np.max(np.abs(q[sel].astype(int))) == 127
+            else:
+                assert np.all(q[sel] == 0)
+        state = {"double_quant": True, "absmax": q, "absmax2": s, "absmax_mean": mean}
+        ahat = oracle.block_scales(state).astype(np.float64)
+        slack = 4 * np.array([f32_ulp(max(abs(float(mean)), float(s[gi]), float(ai)))
+                              for gi, ai in zip(g, a)])
+        assert np.all(np.abs(ahat - a) <= s[g].astype(np.float64) / 254 + slack)
+
+
+def test_double_quant_constant_scales():
+    a = np.full(300, 0.25, np.float32)
+    q, s, mean = oracle.double_quant(a)
+    assert mean == np.float32(0.25) and np.all(s == 0) and np.all(q == 0)
+    state = {"double_quant": True, "absmax": q, "absmax2": s, "absmax_mean": mean}
+    assert np.all(oracle.block_scales(state) == np.float32(0.25))
+
+
+# --------------------------------------------------------------------------
+# Dequant and matmul
+# --------------------------------------------------------------------------
+def test_dequant_with_unit_absmax_returns_levels():
+    L = oracle.codebook()
+    lv = oracle.f32_to_bf16_bits(L)
+    # 4 copies of the 16 levels -> one block of 64 whose absmax is exactly 1
+    w = np.tile(lv, 4)
+    q = oracle.quantize(w, False)
+    assert q["absmax"][0] == 1.0
+    assert np.array_equal(q["codes"], np.tile(np.arange(16, dtype=np.uint8), 4))
+    assert np.array_equal(oracle.dequantize(q["packed"], q), w)
+
+
+def test_matmul_unit_vector_is_exact_column():
+    from synth import normal_bf16
+
+    N, K = 48, 128
+    w = normal_bf16((N, K), 0.02, 99)
+    for dq in (False, True):
+        q = oracle.quantize(w, dq)
+        what = oracle.dequantize(q["packed"], q).reshape(N, K)
+        for k in (0, 5, 127):
+            x = np.zeros((1, K), np.uint16)
+            x[0, k] = 0x3F80                   # bf16 1.0
+            y = oracle.dequant_matmul_ref(x, q["packed"], q, N, K)
+            assert np.array_equal(y[0], oracle.bf16_bits_to_f32(what[:, k]).astype(np.float64))
+
+
+def test_matmul_bruteforce_loops():
+    from synth import normal_bf16
+
+    M, N, K = 2, 3, 64
+    x = normal_bf16((M, K), 1.0, 5)
+    w = normal_bf16((N, K), 0.5, 6)
+    y = oracle.matmul_ref(x, w)
+    xf = oracle.bf16_bits_to_f32(x).reshape(M, K)
+    wf = oracle.bf16_bits_to_f32(w).reshape(N, K)
+    for m in range(M):
+        for n in range(N):
+            acc = math.fsum(float(xf[m, k]) * float(wf[n, k]) for k in range(K))
+            assert y[m, n] == pytest.approx(acc, rel=1e-13, abs=1e-13)
+
+
+def test_rel_frobenius():
+    assert oracle.rel_frobenius([3.0, 4.0], [3.0, 4.0]) == 0.0
+    assert oracle.rel_frobenius([3.0, 5.0], [3.0, 4.0]) == pytest.approx(0.2)
+
+
+# --------------------------------------------------------------------------
+# Memory arithmetic and the pages' figures
+# --------------------------------------------------------------------------
+def test_storage_bits_per_weight():
+    n = 4096 * 4096
+    assert oracle.storage_bytes(n, False) * 8 / n == pytest.approx(4.5)
+    bits_dq = oracle.storage_bytes(n, True) * 8 / n
+    assert bits_dq == pytest.approx(4 + 8 / 64 + 32 / (64 * 256), abs=1e-5)
+    # sizes the quantizer actually returns agree with the formula
+    from synth import normal_bf16
+    w = normal_bf16((64, 1024), 0.02, 8)
+    for dq in (False, True):
+        q = oracle.quantize(w, dq)
+        got = q["packed"].nbytes + q["absmax"].nbytes
+        if dq:
+            got += q["absmax2"].nbytes + 4
+        assert got == oracle.storage_bytes(w.size, dq)
+
+
+def test_pages_memory_figures():
+    g = json.load(open(GOLDEN))
+    n7 = 7e9
+    # fp16 = 2 bytes per parameter reproduces both fp16 figures the pages print
+    assert n7 * 2 / 1e9 == pytest.approx(g["fp16_7b_model_gb"]["value"])
+    assert g["gpt3_params"]["value"] * 2 / 1e9 == pytest.approx(g["gpt3_fp16_gb_about"]["value"])
+    # NF4 + double quant: 7B weights take ~3.6 GB, i.e. "about 4 GB" (the rest
+    # of a real model, embeddings and norms, stays 16-bit)
+    n = 4096 * 4096
+    per_weight = oracle.storage_bytes(n, True) / n
+    gb = n7 * per_weight / 1e9
+    assert 3.0 < gb <= g["nf4_dq_7b_model_gb_about"]["value"]
+    # 4-bit saves about three quarters of 16-bit storage
+    saving = 1 - oracle.storage_bytes(n, False) / (2 * n)
+    assert saving == pytest.approx(g["four_bit_saving_fraction"]["value"], abs=0.05)
+    # double quant saves "a few tenths of a bit" per parameter
+    lo, hi = g["double_quant_saving_bits_per_param"]["range"]
+    d = (oracle.storage_bytes(n, False) - oracle.storage_bytes(n, True)) * 8 / n
+    assert lo <= d <= hi and d == pytest.approx(0.373, abs=1e-3)
+    # the measured table's ordering is the ordering of bits per weight
+    t = g["qwen2_5_1_5b_allocated_mb"]
+    assert t["nf4_double_quant"] < t["fp4"] < t["int8"] < t["fp16"]
+
+
+def test_nf4_error_below_uniform_int4():
+    """Direction of the pages' figure (NF4 error about 0.6x INT4, section
+    3.2): on normal weights in blocks of 64, NF4 mean squared error is below
+    that of blockwise absmax INT4 with 15 symmetric levels."""
+    rng = np.random.default_rng(12)
+    wf = rng.standard_normal(64 * 4000).astype(np.float32)
+    w = oracle.f32_to_bf16_bits(wf)
+    wf = oracle.bf16_bits_to_f32(w).astype(np.float64)
+    q = oracle.quantize(w, False)
+    L = oracle.codebook().astype(np.float64)
+    a = np.repeat(q["absmax"].astype(np.float64), 64)
+    mse_nf4 = np.mean((wf - L[q["codes"]] * a) ** 2)
+    int4 = np.round(wf / a * 7) / 7 * a
+    mse_int4 = np.mean((wf - int4) ** 2)
+    g = json.load(open(GOLDEN))
+    assert mse_nf4 < mse_int4
+    assert mse_nf4 / mse_int4 < 1.0 and g["nf4_vs_int4_error_ratio_about"]["value"] < 1.0
