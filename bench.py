@@ -1,0 +1,252 @@
+"""Benchmark of the NF4 hot path on one MI355X.
+
+One step is one pass of every step of the path over the decode workload:
+for each of L layers of Llama-7B-shaped linears (4096x4096, 11008x4096,
+4096x11008; bf16 weights N(0, 0.02), distinct per layer), quantize-on-load
+with double quantization, dequantize to bf16, and the M=1 decode GEMV
+(dequant fused); then one prefill GEMM, M=2048, N=K=8192, on a weight
+quantized once before timing.  Inputs are resident in HBM before timing.
+
+`value` is the decode GEMV throughput in GB/s of algorithmic bytes (packed
+codes + int8 scales + group scales + mean + X + Y) over the GEMV launches of
+the timed steps; the GEMM's TFLOP/s is reported beside it, with per-kernel
+timings, rooflines, and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+METRIC = "NF4 dequant-GEMV HBM GB/s (M=1) + GEMM TFLOP/s (M=2048), % of peak"
+DECODE_SHAPES = ((4096, 4096), (11008, 4096), (4096, 11008))
+PREFILL = (2048, 8192, 8192)
+
+
+def gemv_bytes(M, N, K):
+    n = N * K
+    nb = n // 64
+    ng = -(-nb // 256)
+    return n // 2 + nb + 4 * ng + 4 + 2 * M * K + 2 * M * N
+
+
+def quant_bytes(N, K):
+    n = N * K
+    nb = n // 64
+    ng = -(-nb // 256)
+    return 2 * n + n // 2 + nb + 4 * ng + 4
+
+
+def dequant_bytes(N, K):
+    n = N * K
+    nb = n // 64
+    ng = -(-nb // 256)
+    return n // 2 + nb + 4 * ng + 4 + 2 * n
+
+
+def cpu_baseline(budget_s: float = 12.0):
+    """The oracle as it stands, on one decode layer (4096x4096, double quant):
+    fp64 reference GEMV = dequantize + binary64 matmul, repeated until the
+    budget is spent.  Reported in the GEMV metric's unit."""
+    import numpy as np
+    import oracle
+    import synth
+
+    w, x = synth.decode(0)
+    N, K = DECODE_SHAPES[0]
+    state = oracle.quantize(w, True)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.dequant_matmul_ref(x, state["packed"], state, N, K)
+        reps += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    return {
+        "value": gemv_bytes(1, N, K) * reps / dt / 1e9,
+        "unit": "GB/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{reps} x fp64 reference GEMV (dequantize + matmul) of one 4096x4096 "
+                  f"double-quant layer, M=1, {dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(the multi-GPU sharding is described, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from dequant_gemm_nf4_amd import tensors as T
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    L = args.layers
+
+    # ---- inputs resident in HBM (device-side seeded draws) ----
+    gen = torch.Generator(device=dev)
+    weights = []
+    for l in range(L):
+        for s, (N, K) in enumerate(DECODE_SHAPES):
+            gen.manual_seed(5000 + 10 * l + s)
+            w = (torch.randn(N, K, generator=gen, device=dev, dtype=torch.float32) * 0.02)
+            weights.append(w.to(torch.bfloat16))
+    xs = []
+    for s, (N, K) in enumerate(DECODE_SHAPES):
+        gen.manual_seed(6000 + s)
+        xs.append(torch.randn(1, K, generator=gen, device=dev).to(torch.bfloat16))
+    qs = [T.empty_quantized(w.shape, True, dev) for w in weights]
+    maxn = max(N * K for N, K in DECODE_SHAPES)
+    ws = T.workspace_for(maxn, True, dev)
+    deq = torch.empty(maxn, dtype=torch.bfloat16, device=dev)
+    ys = [torch.empty(1, N, dtype=torch.bfloat16, device=dev) for N, K in DECODE_SHAPES]
+
+    Mp, Np, Kp = PREFILL
+    gen.manual_seed(7000)
+    wp = (torch.randn(Np, Kp, generator=gen, device=dev) * 0.015).to(torch.bfloat16)
+    gen.manual_seed(7001)
+    xp = torch.randn(Mp, Kp, generator=gen, device=dev)
+    gen.manual_seed(7002)
+    cols = torch.randperm(Kp, generator=gen, device=dev)[:4]
+    xp[:, cols] *= 50.0
+    xp = xp.to(torch.bfloat16)
+    qp = T.quantize(wp, True)
+    del wp
+    yp = torch.empty(Mp, Np, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    nlaunch = L * len(DECODE_SHAPES)
+
+    def step(timed):
+        marks = {}
+        for k in ("q0", "q1", "d0", "d1", "v0", "v1", "m0", "m1"):
+            marks[k] = ev()
+        marks["q0"].record(stream)
+        for i, w in enumerate(weights):
+            T.quantize(w, True, out=qs[i], workspace=ws, stream=stream)
+        marks["q1"].record(stream)
+        marks["d0"].record(stream)
+        for i, q in enumerate(qs):
+            T.dequantize(q, out=deq[: q.n].view(q.shape), stream=stream)
+        marks["d1"].record(stream)
+        marks["v0"].record(stream)
+        for i, q in enumerate(qs):
+            s = i % len(DECODE_SHAPES)
+            T.gemv(xs[s], q, out=ys[s], stream=stream)
+        marks["v1"].record(stream)
+        marks["m0"].record(stream)
+        T.gemm(xp, qp, out=yp, stream=stream)
+        marks["m1"].record(stream)
+        return marks
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+
+    all_marks = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        all_marks.append(step(True))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def stage_ms(a, b):
+        return sum(m[a].elapsed_time(m[b]) for m in all_marks)
+
+    t_q = stage_ms("q0", "q1") / 1e3
+    t_d = stage_ms("d0", "d1") / 1e3
+    t_v = stage_ms("v0", "v1") / 1e3
+    t_m = stage_ms("m0", "m1") / 1e3
+    K_ = args.steps
+    gb_v = K_ * L * sum(gemv_bytes(1, N, K) for N, K in DECODE_SHAPES)
+    gb_q = K_ * L * sum(quant_bytes(N, K) for N, K in DECODE_SHAPES)
+    gb_d = K_ * L * sum(dequant_bytes(N, K) for N, K in DECODE_SHAPES)
+    gemv_gbs = gb_v / t_v / 1e9
+    gemm_tflops = K_ * 2.0 * Mp * Np * Kp / t_m / 1e12
+    avg_gemv_us = t_v / (K_ * nlaunch) * 1e6
+    avg_gemv_bytes = gb_v / (K_ * nlaunch)
+
+    out = {
+        "metric": METRIC,
+        "value": round(gemv_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 (NF4 storage, fp32 accumulate)",
+        "data": "synthetic (seeded device draws, N(0,0.02) weights, N(0,1) activations)",
+        "config": {
+            "workload": "decode GEMV M=1 over Llama-7B-shaped linears 4096x4096, 11008x4096, "
+                        "4096x11008 (NF4 blocksize 64, double quant), "
+                        f"{L} distinct layers per shape; plus prefill GEMM M=2048 N=K=8192",
+            "layers": L,
+            "gemm": {"M": Mp, "N": Np, "K": Kp},
+        },
+        "roofline": {
+            "kernel": "gemv_valu_kernel",
+            "bound": "hbm",
+            "achieved": round(avg_gemv_bytes / (avg_gemv_us * 1e-6) / 1e9, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(avg_gemv_bytes / (avg_gemv_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "gemm": {
+            "tflops": round(gemm_tflops, 1),
+            "peak": BF16_PEAK_TFLOPS,
+            "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4),
+            "ms": round(t_m / K_ * 1e3, 4),
+        },
+        "kernels": {
+            "quantize_gbs": round(gb_q / t_q / 1e9, 1),
+            "quantize_input_read_gbs": round(K_ * L * sum(2 * N * K for N, K in DECODE_SHAPES) / t_q / 1e9, 1),
+            "dequantize_gbs": round(gb_d / t_d / 1e9, 1),
+            "gemv_gbs": round(gemv_gbs, 1),
+            "gemv_avg_launch_us": round(avg_gemv_us, 3),
+            "stage_ms_per_step": {"quantize": round(t_q / K_ * 1e3, 3),
+                                  "dequantize": round(t_d / K_ * 1e3, 3),
+                                  "gemv": round(t_v / K_ * 1e3, 3),
+                                  "gemm": round(t_m / K_ * 1e3, 3)},
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

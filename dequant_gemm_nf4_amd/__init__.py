@@ -1,0 +1,173 @@
+"""Python binding of libbnbx, the MI355X (gfx950) NF4 4-bit weight library.
+
+Argument marshalling only: every function here has the name of a C entry
+point declared in ``include/bnbx.h`` and forwards to it through ctypes.  All
+computation happens in the library's HIP kernels.  Device buffers may be
+passed as integers (device addresses) or as objects with ``data_ptr()``
+(torch tensors); ``stream`` is a hipStream_t handle (int), a torch stream, or
+None for the caller's current torch stream when torch has a GPU, else the
+null stream.
+
+If the shared library is missing, importing works but every call raises
+``BnbxLibraryMissing``: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "BNBX_OK", "BNBX_E_INVAL", "BNBX_E_ALIGN", "BNBX_E_UNSUPPORTED", "BNBX_E_WORKSPACE",
+    "BNBX_E_HIP", "BnbxError", "BnbxLibraryMissing", "Nf4State", "library_path", "lib",
+    "bnbx_status_str", "bnbx_nf4_codebook", "bnbx_quantize_nf4_workspace_bytes",
+    "bnbx_quantize_nf4", "bnbx_dequantize_nf4", "bnbx_gemv_nf4",
+    "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4", "EXPORTED_SYMBOLS",
+]
+
+BNBX_OK = 0
+BNBX_E_INVAL = -1
+BNBX_E_ALIGN = -2
+BNBX_E_UNSUPPORTED = -3
+BNBX_E_WORKSPACE = -4
+BNBX_E_HIP = -5
+
+EXPORTED_SYMBOLS = (
+    "bnbx_status_str", "bnbx_nf4_codebook", "bnbx_quantize_nf4_workspace_bytes",
+    "bnbx_quantize_nf4", "bnbx_dequantize_nf4", "bnbx_gemv_nf4",
+    "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4",
+)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libbnbx.so")
+
+
+class BnbxLibraryMissing(RuntimeError):
+    pass
+
+
+class BnbxError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {bnbx_status_str(status)} ({status})")
+
+
+class Nf4State(ctypes.Structure):
+    """bnbx_nf4_state: host descriptor holding device pointers."""
+
+    _fields_ = [
+        ("n", ctypes.c_int64),
+        ("blocksize", ctypes.c_int32),
+        ("double_quant", ctypes.c_int32),
+        ("absmax", ctypes.c_void_p),
+        ("absmax2", ctypes.c_void_p),
+        ("absmax_mean", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbnbx.so (built in-tree by dequant_gemm_nf4_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise BnbxLibraryMissing(
+            f"{path} is not built; run `python -m dequant_gemm_nf4_amd.build` (no fallback exists)")
+    L = ctypes.CDLL(path)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    sp = ctypes.POINTER(Nf4State)
+    L.bnbx_status_str.argtypes = [i32]
+    L.bnbx_status_str.restype = ctypes.c_char_p
+    L.bnbx_nf4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
+    L.bnbx_nf4_codebook.restype = i32
+    L.bnbx_quantize_nf4_workspace_bytes.argtypes = [i64, i32, i32]
+    L.bnbx_quantize_nf4_workspace_bytes.restype = sz
+    L.bnbx_quantize_nf4.argtypes = [vp, vp, sp, vp, sz, vp]
+    L.bnbx_quantize_nf4.restype = i32
+    L.bnbx_dequantize_nf4.argtypes = [vp, sp, vp, vp]
+    L.bnbx_dequantize_nf4.restype = i32
+    L.bnbx_gemv_nf4.argtypes = [vp, i64, vp, sp, i32, i32, i32, vp, i64, vp]
+    L.bnbx_gemv_nf4.restype = i32
+    L.bnbx_gemm_nf4_workspace_bytes.argtypes = [i32, i32, i32]
+    L.bnbx_gemm_nf4_workspace_bytes.restype = sz
+    L.bnbx_gemm_nf4.argtypes = [vp, i64, vp, sp, i32, i32, i32, vp, i64, vp, sz, vp]
+    L.bnbx_gemm_nf4.restype = i32
+    _lib = L
+    return L
+
+
+def _ptr(a) -> int | None:
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    return int(a.data_ptr())
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        try:
+            import torch
+            if torch.cuda.is_available():
+                return int(torch.cuda.current_stream().cuda_stream)
+        except ImportError:  # pragma: no cover
+            pass
+        return None
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def _check(status: int, where: str) -> None:
+    if status != BNBX_OK:
+        raise BnbxError(status, where)
+
+
+def bnbx_status_str(status: int) -> str:
+    return lib().bnbx_status_str(int(status)).decode()
+
+
+def bnbx_nf4_codebook() -> list[float]:
+    buf = (ctypes.c_float * 16)()
+    _check(lib().bnbx_nf4_codebook(buf), "bnbx_nf4_codebook")
+    return list(buf)
+
+
+def bnbx_quantize_nf4_workspace_bytes(n: int, blocksize: int = 64, double_quant: int = 1) -> int:
+    return int(lib().bnbx_quantize_nf4_workspace_bytes(int(n), int(blocksize), int(double_quant)))
+
+
+def bnbx_quantize_nf4(w, packed, state: Nf4State, workspace=None, workspace_bytes: int = 0,
+                      stream=None) -> None:
+    _check(lib().bnbx_quantize_nf4(_ptr(w), _ptr(packed), ctypes.byref(state), _ptr(workspace),
+                                   int(workspace_bytes), _stream(stream)), "bnbx_quantize_nf4")
+
+
+def bnbx_dequantize_nf4(packed, state: Nf4State, out, stream=None) -> None:
+    _check(lib().bnbx_dequantize_nf4(_ptr(packed), ctypes.byref(state), _ptr(out),
+                                     _stream(stream)), "bnbx_dequantize_nf4")
+
+
+def bnbx_gemv_nf4(x, ldx: int, packed, state: Nf4State, M: int, N: int, K: int, y, ldy: int,
+                  stream=None) -> None:
+    _check(lib().bnbx_gemv_nf4(_ptr(x), int(ldx), _ptr(packed), ctypes.byref(state), int(M),
+                               int(N), int(K), _ptr(y), int(ldy), _stream(stream)),
+           "bnbx_gemv_nf4")
+
+
+def bnbx_gemm_nf4_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().bnbx_gemm_nf4_workspace_bytes(int(M), int(N), int(K)))
+
+
+def bnbx_gemm_nf4(x, ldx: int, packed, state: Nf4State, M: int, N: int, K: int, y, ldy: int,
+                  workspace=None, workspace_bytes: int = 0, stream=None) -> None:
+    _check(lib().bnbx_gemm_nf4(_ptr(x), int(ldx), _ptr(packed), ctypes.byref(state), int(M),
+                               int(N), int(K), _ptr(y), int(ldy), _ptr(workspace),
+                               int(workspace_bytes), _stream(stream)), "bnbx_gemm_nf4")

@@ -1,0 +1,236 @@
+// C entry points of libbnbx (declared in include/bnbx.h): argument checks on
+// the host, the one-time codebook and encode tables, and kernel launches.
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <algorithm>
+#include <mutex>
+
+#include "../../include/bnbx.h"
+#include "bnbx_internal.hpp"
+
+namespace bnbx {
+namespace {
+
+// Standard normal CDF and density in binary64 (C library erfc / exp).
+double normal_cdf(double x) { return 0.5 * erfc(-x * 0.70710678118654752440); }
+double normal_pdf(double x) { return exp(-0.5 * x * x) * 0.39894228040143267794; }
+
+// Upper-half standard normal quantile by Newton's method on the CDF from 0.
+// The CDF is concave on [0, inf), so from the left every Newton step stays at
+// or below the root and the iterates rise monotonically to it; stop when a
+// step no longer moves x up.
+double normal_quantile_upper(double p) {
+  double x = 0.0;
+  for (int it = 0; it < 200; ++it) {
+    const double nx = x - (normal_cdf(x) - p) / normal_pdf(x);
+    if (!(nx > x)) break;
+    x = nx;
+  }
+  return x;
+}
+
+struct Tables {
+  float levels[16];
+  float thr[15];
+  EncodeTable enc;
+  LevelTable lv;
+};
+
+// NF4 codebook (mlqm.cn bitsandbytes article, sec. 3.2: 16 levels laid out
+// by the normal density, dense near 0, with exact 0 and ends at +-1): 8
+// positive quantiles of probabilities evenly spaced from the offset toward
+// 1/2, 7 mirrored negative ones over the same span, and 0, all divided by the
+// outermost quantile.  The offset averages the 1/30 and 1/32 tail masses.
+void build_tables(Tables& t) {
+  const double off = 1.0 - 0.5 * (1.0 / 30.0 + 1.0 / 32.0);
+  const double top = normal_quantile_upper(off);
+  double v[16];
+  int k = 0;
+  for (int i = 0; i < 7; ++i) v[k++] = -normal_quantile_upper(off + i * (0.5 - off) / 7.0);
+  v[k++] = 0.0;
+  for (int i = 0; i < 8; ++i) v[k++] = normal_quantile_upper(off + i * (0.5 - off) / 8.0);
+  std::sort(v, v + 16);
+  for (int i = 0; i < 16; ++i) t.levels[i] = (float)(v[i] / top);   // ends: +-top/top = +-1
+
+  // Nearest-level thresholds: smallest float strictly above each midpoint,
+  // so an exact tie takes the lower index.
+  for (int i = 0; i < 15; ++i) {
+    const double mid = ((double)t.levels[i] + (double)t.levels[i + 1]) * 0.5;
+    float th = (float)mid;
+    if ((double)th <= mid) th = nextafterf(th, INFINITY);
+    t.thr[i] = th;
+  }
+
+  // Encode buckets: bucket b holds x with round-half-even(16x + 16) == b,
+  // i.e. x in [(b - 1/2)/16 - 1, (b + 1/2)/16 - 1].  Each bucket must hold at
+  // most one threshold and no threshold may sit near a bucket edge (the
+  // rounding of 16x + 16 moves an edge by far less than the margin checked).
+  for (int b = 0; b < kBuckets; ++b) {
+    const double lo = (b - 0.5) / 16.0 - 1.0, hi = (b + 0.5) / 16.0 - 1.0;
+    uint32_t base = 0;
+    float inside = INFINITY;
+    int count = 0;
+    for (int i = 0; i < 15; ++i) {
+      const double th = t.thr[i];
+      if (fabs(th - lo) < 1e-4 || fabs(th - hi) < 1e-4) {
+        fprintf(stderr, "bnbx: NF4 threshold too close to an encode bucket edge\n");
+        abort();
+      }
+      if (th < lo) ++base;
+      else if (th < hi) { inside = t.thr[i]; ++count; }
+    }
+    if (count > 1) {
+      fprintf(stderr, "bnbx: two NF4 thresholds in one encode bucket\n");
+      abort();
+    }
+    t.enc.thr[b] = inside;
+    t.enc.base[b] = base;
+  }
+  for (int i = 0; i < 16; ++i) t.lv.level[i] = t.levels[i];
+}
+
+const Tables& tables() {
+  static Tables t;
+  static std::once_flag once;
+  std::call_once(once, [] { build_tables(t); });
+  return t;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int64_t nblocks(int64_t n) { return (n + kBlock - 1) / kBlock; }
+int64_t ngroups(int64_t nb) { return (nb + kGroup - 1) / kGroup; }
+
+int check_state(const bnbx_nf4_state* st) {
+  if (st == nullptr) return BNBX_E_INVAL;
+  if (st->n < 2 || (st->n & 1)) return BNBX_E_INVAL;
+  if (st->blocksize != kBlock) return BNBX_E_UNSUPPORTED;
+  if (st->double_quant != 0 && st->double_quant != 1) return BNBX_E_INVAL;
+  if (st->absmax == nullptr) return BNBX_E_INVAL;
+  if (st->double_quant && (st->absmax2 == nullptr || st->absmax_mean == nullptr))
+    return BNBX_E_INVAL;
+  return BNBX_OK;
+}
+
+int check_matmul(const uint16_t* x, int64_t ldx, const uint8_t* packed, const bnbx_nf4_state* st,
+                 int M, int N, int K, const uint16_t* y, int64_t ldy) {
+  if (x == nullptr || packed == nullptr || y == nullptr) return BNBX_E_INVAL;
+  const int s = check_state(st);
+  if (s != BNBX_OK) return s;
+  if (M < 1 || N < 1 || K < kBlock) return BNBX_E_INVAL;
+  if (K % kBlock != 0) return BNBX_E_INVAL;
+  if (st->n != (int64_t)N * (int64_t)K) return BNBX_E_INVAL;
+  if (ldx < K || ldy < N) return BNBX_E_INVAL;
+  if (ldx % 8 != 0) return BNBX_E_ALIGN;
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(y, 2)) return BNBX_E_ALIGN;
+  return BNBX_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? BNBX_OK : BNBX_E_HIP; }
+
+}  // namespace
+
+const float* levels_f32() { return tables().levels; }
+const float* thresholds_f32() { return tables().thr; }
+const EncodeTable& encode_table() { return tables().enc; }
+const LevelTable& level_table() { return tables().lv; }
+
+}  // namespace bnbx
+
+using namespace bnbx;
+
+extern "C" {
+
+const char* bnbx_status_str(int status) {
+  switch (status) {
+    case BNBX_OK: return "BNBX_OK";
+    case BNBX_E_INVAL: return "BNBX_E_INVAL: invalid argument";
+    case BNBX_E_ALIGN: return "BNBX_E_ALIGN: misaligned pointer or leading dimension";
+    case BNBX_E_UNSUPPORTED: return "BNBX_E_UNSUPPORTED: unsupported configuration";
+    case BNBX_E_WORKSPACE: return "BNBX_E_WORKSPACE: workspace missing or too small";
+    case BNBX_E_HIP: return "BNBX_E_HIP: HIP runtime error at launch";
+    default: return "BNBX: unknown status";
+  }
+}
+
+int bnbx_nf4_codebook(float levels_host[16]) {
+  if (levels_host == nullptr) return BNBX_E_INVAL;
+  const float* l = levels_f32();
+  for (int i = 0; i < 16; ++i) levels_host[i] = l[i];
+  return BNBX_OK;
+}
+
+size_t bnbx_quantize_nf4_workspace_bytes(int64_t n, int blocksize, int double_quant) {
+  if (n < 2 || (n & 1) || blocksize != kBlock) return 0;
+  if (!double_quant) return 0;
+  return dq_workspace_bytes(nblocks(n));
+}
+
+int bnbx_quantize_nf4(const uint16_t* w, uint8_t* packed, const bnbx_nf4_state* st,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (w == nullptr || packed == nullptr) return BNBX_E_INVAL;
+  const int s = check_state(st);
+  if (s != BNBX_OK) return s;
+  if (!aligned(w, 16) || !aligned(packed, 16)) return BNBX_E_ALIGN;
+  const int64_t n = st->n, nb = nblocks(n);
+  hipStream_t hs = (hipStream_t)stream;
+  if (!st->double_quant) {
+    return hip_status(launch_quantize(w, packed, n, (float*)st->absmax, nullptr, hs));
+  }
+  const size_t need = dq_workspace_bytes(nb);
+  if (workspace == nullptr || workspace_bytes < need) return BNBX_E_WORKSPACE;
+  if (!aligned(workspace, 256)) return BNBX_E_ALIGN;
+  unsigned long long* hist = (unsigned long long*)workspace;
+  float* a32 = (float*)((char*)workspace + kHistBytes);
+  hipError_t e = launch_zero_hist(hist, hs);
+  if (e == hipSuccess) e = launch_quantize(w, packed, n, a32, hist, hs);
+  if (e == hipSuccess)
+    e = launch_double_quant(a32, hist, nb, (int8_t*)st->absmax, st->absmax2, st->absmax_mean, hs);
+  return hip_status(e);
+}
+
+int bnbx_dequantize_nf4(const uint8_t* packed, const bnbx_nf4_state* st, uint16_t* out,
+                        void* stream) {
+  if (packed == nullptr || out == nullptr) return BNBX_E_INVAL;
+  const int s = check_state(st);
+  if (s != BNBX_OK) return s;
+  if (!aligned(packed, 16) || !aligned(out, 16)) return BNBX_E_ALIGN;
+  return hip_status(launch_dequantize(packed, st->n, st->absmax, st->absmax2, st->absmax_mean,
+                                      st->double_quant, out, (hipStream_t)stream));
+}
+
+int bnbx_gemv_nf4(const uint16_t* x, int64_t ldx, const uint8_t* packed,
+                  const bnbx_nf4_state* st, int M, int N, int K, uint16_t* y, int64_t ldy,
+                  void* stream) {
+  const int s = check_matmul(x, ldx, packed, st, M, N, K, y, ldy);
+  if (s != BNBX_OK) return s;
+  if (M > 16) return BNBX_E_INVAL;
+  const hipError_t e = launch_gemv(x, ldx, packed, st->absmax, st->absmax2, st->absmax_mean,
+                                   st->double_quant, M, N, K, y, ldy, (hipStream_t)stream);
+  if (e == hipErrorNotSupported) return BNBX_E_UNSUPPORTED;
+  return hip_status(e);
+}
+
+size_t bnbx_gemm_nf4_workspace_bytes(int M, int N, int K) {
+  (void)M;
+  (void)N;
+  (void)K;
+  return 0;
+}
+
+int bnbx_gemm_nf4(const uint16_t* x, int64_t ldx, const uint8_t* packed,
+                  const bnbx_nf4_state* st, int M, int N, int K, uint16_t* y, int64_t ldy,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  const int s = check_matmul(x, ldx, packed, st, M, N, K, y, ldy);
+  if (s != BNBX_OK) return s;
+  const hipError_t e = launch_gemm(x, ldx, packed, st->absmax, st->absmax2, st->absmax_mean,
+                                   st->double_quant, M, N, K, y, ldy, (hipStream_t)stream);
+  if (e == hipErrorNotSupported) return BNBX_E_UNSUPPORTED;
+  return hip_status(e);
+}
+
+}  // extern "C"

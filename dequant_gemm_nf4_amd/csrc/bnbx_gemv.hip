@@ -1,0 +1,224 @@
+// Decode GEMV with NF4 weights for gfx950: Y[M, N] = X[M, K] . W_hat[N, K]^T,
+// M <= 16 (mlqm.cn bitsandbytes article, sec. 3.4 "4-bit storage, 16-bit
+// compute", and the sec. 7 pitfall that 4-bit only pays off when the layer is
+// bound by weight traffic: so the packed weight is streamed exactly once).
+//
+// Layout of the work.  A row of W is C = K/32 chunks of 16 packed bytes
+// (32 weights, half a 64-block).  A workgroup is R "teams" of S threads
+// (S a multiple of 64, S >= C/P); slot s of a team owns chunks s, s+S, ... of
+// whatever row the team is on, so its slice of X stays in registers for the
+// whole kernel while the team walks G rows.  Every thread issues all of its
+// 16-byte weight loads before it builds the lookup table, so the HBM latency
+// overlaps the table build.
+//
+// Dequant in registers.  An LDS table maps each packed byte to the bf16 pair
+// (L[high nibble], L[low nibble]); it is replicated 64 times with a 256-byte
+// stride so that lane l always reads bank l (no conflicts), and the byte
+// address (byte << 8 | lane << 2) is formed by one v_perm_b32.  The pair feeds
+// v_dot2_f32_bf16 against the matching X pair; the 32-weight partial sum is
+// scaled once by the block scale (fp32), so dequant costs about one VALU
+// instruction per weight.
+#include "bnbx_device.hpp"
+#include "bnbx_internal.hpp"
+
+namespace bnbx {
+namespace {
+
+constexpr int kMaxThreads = 1024;
+constexpr int kGMax = 8;
+constexpr int kTabDwords = 256 * 64;   // 64 KB
+
+__device__ __forceinline__ float level_of(const LevelTable& lv, uint32_t c) {
+  float v = lv.level[0];
+#pragma unroll
+  for (uint32_t i = 1; i < 16; ++i) v = (c == i) ? lv.level[i] : v;
+  return v;
+}
+
+// Approximate block scale for the contraction (not bit-exact with the stored
+// format's dequant; the matmul tolerance covers the last-ulp difference).
+__device__ __forceinline__ float gemv_block_scale(int64_t blk, const void* absmax,
+                                                  const float* absmax2, float mu, int dq) {
+  if (!dq) return ((const float*)absmax)[blk];
+  const float q = (float)((const int8_t*)absmax)[blk];
+  return __builtin_fmaf(q, absmax2[blk / kGroup] * (1.0f / 127.0f), mu);
+}
+
+template <int MM, int P>
+__global__ __launch_bounds__(kMaxThreads) void gemv_valu_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ packed,
+    const void* __restrict__ absmax, const float* __restrict__ absmax2,
+    const float* __restrict__ mean, int dq, int N, int K, uint16_t* __restrict__ y, int64_t ldy,
+    int S, int R, int G, LevelTable lv) {
+  __shared__ __attribute__((aligned(16))) uint32_t tab[kTabDwords];
+  __shared__ float red[kGMax * MM * (kMaxThreads / 64)];
+
+  const int t = threadIdx.x;
+  const int T = blockDim.x;
+  const int team = t / S, s = t - team * S;
+  const int C = K >> 5;
+  const int64_t rowK2 = (int64_t)(K >> 1);
+  const int64_t row0 = (int64_t)blockIdx.x * R * G + team;
+  const float mu = dq ? *mean : 0.0f;
+
+  // 1. weight loads and block scales (all in flight before anything else)
+  uint4 wv[kGMax][P];
+  float sc[kGMax][P];
+#pragma unroll
+  for (int g = 0; g < kGMax; ++g) {
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const int64_t row = row0 + (int64_t)g * R;
+      const int c = s + j * S;
+      const bool ok = g < G && row < N && c < C;
+      wv[g][j] = ok ? load_nt16(packed + row * rowK2 + (int64_t)c * 16)
+                    : make_uint4(0, 0, 0, 0);
+      sc[g][j] = ok ? gemv_block_scale(row * (K >> 6) + (c >> 1), absmax, absmax2, mu, dq) : 0.0f;
+    }
+  }
+  // 2. this thread's X slice: 32 bf16 (16 pairs) per chunk per row of X
+  uint32_t xr[MM][P][16];
+#pragma unroll
+  for (int m = 0; m < MM; ++m) {
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const int c = s + j * S;
+      if (c < C) {
+        const uint4* src = (const uint4*)(x + (int64_t)m * ldx + (int64_t)c * 32);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4 v = src[q];
+          xr[m][j][4 * q] = v.x;
+          xr[m][j][4 * q + 1] = v.y;
+          xr[m][j][4 * q + 2] = v.z;
+          xr[m][j][4 * q + 3] = v.w;
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) xr[m][j][q] = 0u;
+      }
+    }
+  }
+  // 3. replicated byte -> bf16-pair table
+  for (int e = t; e < kTabDwords / 4; e += T) {
+    const uint32_t b = (uint32_t)e >> 4;
+    const uint32_t v = pack_bf16x2(level_of(lv, b >> 4), level_of(lv, b & 15u));
+    ((uint4*)tab)[e] = make_uint4(v, v, v, v);
+  }
+  __syncthreads();
+
+  // 4. dequant-in-register dot products
+  const uint32_t lanebyte = (uint32_t)(t & 63) << 2;
+  const unsigned char* tabb = (const unsigned char*)tab;
+  float acc[kGMax][MM];
+#pragma unroll
+  for (int g = 0; g < kGMax; ++g) {
+#pragma unroll
+    for (int m = 0; m < MM; ++m) acc[g][m] = 0.0f;
+  }
+#pragma unroll
+  for (int g = 0; g < kGMax; ++g) {
+    if (g < G) {
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        const uint32_t d[4] = {wv[g][j].x, wv[g][j].y, wv[g][j].z, wv[g][j].w};
+        float part[MM];
+#pragma unroll
+        for (int m = 0; m < MM; ++m) part[m] = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t addr = perm(d[q], lanebyte, 0x0c0c0000u | ((4u + i) << 8));
+            const uint32_t pair = *(const uint32_t*)(tabb + addr);
+#pragma unroll
+            for (int m = 0; m < MM; ++m) part[m] = dot2_bf16(pair, xr[m][j][4 * q + i], part[m]);
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < MM; ++m) acc[g][m] = __builtin_fmaf(part[m], sc[g][j], acc[g][m]);
+      }
+    }
+  }
+
+  // 5. reduce each row over its team: waves first, then across the team's waves
+  const int nw = T >> 6, wave = t >> 6, wpt = S >> 6;
+#pragma unroll
+  for (int g = 0; g < kGMax; ++g) {
+    if (g < G) {
+#pragma unroll
+      for (int m = 0; m < MM; ++m) {
+        const float v = wave_sum(acc[g][m]);
+        if ((t & 63) == 0) red[(g * MM + m) * nw + wave] = v;
+      }
+    }
+  }
+  __syncthreads();
+  const int nout = G * R * MM;
+  for (int o = t; o < nout; o += T) {
+    const int g = o / (R * MM);
+    const int rem = o - g * R * MM;
+    const int tm = rem / MM, m = rem - tm * MM;
+    const int64_t row = (int64_t)blockIdx.x * R * G + (int64_t)g * R + tm;
+    if (row < N) {
+      float v = 0.0f;
+      for (int w = tm * wpt; w < (tm + 1) * wpt; ++w) v += red[(g * MM + m) * nw + w];
+      y[(int64_t)m * ldy + row] = f32_to_bf16(v);
+    }
+  }
+}
+
+template <int MM, int P>
+hipError_t launch_valu(const uint16_t* x, int64_t ldx, const uint8_t* packed, const void* absmax,
+                       const float* absmax2, const float* mean, int dq, int N, int K,
+                       uint16_t* y, int64_t ldy, hipStream_t stream) {
+  const int C = K >> 5;
+  const int S = ((C + P - 1) / P + 63) / 64 * 64;
+  const int R = kMaxThreads / S >= 1 ? kMaxThreads / S : 1;
+  const int T = S * R;
+  int64_t G = ((int64_t)N + (int64_t)R * 512 - 1) / ((int64_t)R * 512);
+  if (G < 1) G = 1;
+  if (G > kGMax) G = kGMax;
+  const int64_t grid = ((int64_t)N + R * G - 1) / (R * G);
+  hipLaunchKernelGGL((gemv_valu_kernel<MM, P>), dim3((unsigned)grid), dim3(T), 0, stream, x, ldx,
+                     packed, absmax, absmax2, mean, dq, N, K, y, ldy, S, R, (int)G,
+                     level_table());
+  return hipGetLastError();
+}
+
+template <int P>
+hipError_t launch_valu_m(int MM, const uint16_t* x, int64_t ldx, const uint8_t* packed,
+                         const void* absmax, const float* absmax2, const float* mean, int dq,
+                         int N, int K, uint16_t* y, int64_t ldy, hipStream_t stream) {
+  switch (MM) {
+    case 1: return launch_valu<1, P>(x, ldx, packed, absmax, absmax2, mean, dq, N, K, y, ldy, stream);
+    case 2: return launch_valu<2, P>(x, ldx, packed, absmax, absmax2, mean, dq, N, K, y, ldy, stream);
+    case 3: return launch_valu<3, P>(x, ldx, packed, absmax, absmax2, mean, dq, N, K, y, ldy, stream);
+    default: return launch_valu<4, P>(x, ldx, packed, absmax, absmax2, mean, dq, N, K, y, ldy, stream);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* packed, const void* absmax,
+                       const float* absmax2, const float* mean, int double_quant, int M, int N,
+                       int K, uint16_t* y, int64_t ldy, hipStream_t stream) {
+  const int C = K >> 5;
+  const int P = C <= kMaxThreads ? 1 : (C <= 2 * kMaxThreads ? 2 : 0);
+  if (P == 0) return hipErrorNotSupported;
+  // Rows of X in groups of at most 4 (each group streams W once); with two
+  // chunks per thread one row at a time keeps the X slice in registers.
+  const int mstep = P == 1 ? 4 : 1;
+  for (int m0 = 0; m0 < M; m0 += mstep) {
+    const int mm = M - m0 < mstep ? M - m0 : mstep;
+    const hipError_t e =
+        P == 1 ? launch_valu_m<1>(mm, x + (int64_t)m0 * ldx, ldx, packed, absmax, absmax2, mean,
+                                  double_quant, N, K, y + (int64_t)m0 * ldy, ldy, stream)
+               : launch_valu<1, 2>(x + (int64_t)m0 * ldx, ldx, packed, absmax, absmax2, mean,
+                                   double_quant, N, K, y + (int64_t)m0 * ldy, ldy, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace bnbx

@@ -1,0 +1,63 @@
+// Internal declarations shared by the host entry points and the kernel
+// translation units of libbnbx.  Not part of the public ABI (include/bnbx.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bnbx {
+
+constexpr int kBlock = 64;    // weights per first-level block
+constexpr int kGroup = 256;   // first-level scales per second-level group
+constexpr int kBuckets = 33;  // encode buckets: round(16 x + 16), x in [-1, 1]
+
+// Host-computed tables derived from the 16 NF4 levels (mlqm.cn bitsandbytes
+// article, sec. 3.2).  Passed to kernels by value.
+struct EncodeTable {
+  // Bucket b holds the values x with round-half-even(16 x + 16) == b.  At most
+  // one decision threshold falls in a bucket (the thresholds are more than
+  // 1/16 apart), so code(x) = base[b] + (x >= thr[b]); thr is +inf when the
+  // bucket holds none.
+  float thr[kBuckets];
+  uint32_t base[kBuckets];
+};
+
+struct LevelTable {
+  float level[16];       // L[0..15], ascending, binary32
+};
+
+// The one-time host tables (built on first use, immutable afterwards).
+const float* levels_f32();          // float[16]
+const float* thresholds_f32();      // float[15]
+const EncodeTable& encode_table();
+const LevelTable& level_table();
+
+// Workspace layout of the double-quant quantize: an exact exponent histogram
+// of the block absmax values, then the fp32 absmax of every block.
+constexpr size_t kHistBins = 256;
+constexpr size_t kHistBytes = kHistBins * sizeof(unsigned long long);
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline size_t dq_workspace_bytes(int64_t nb) {
+  return kHistBytes + round_up((size_t)nb * sizeof(float), 256);
+}
+
+// ---- kernel launchers (return hipError_t of the launch) ----
+hipError_t launch_quantize(const uint16_t* w, uint8_t* packed, int64_t n, float* absmax_f32,
+                           unsigned long long* hist, hipStream_t stream);
+hipError_t launch_zero_hist(unsigned long long* hist, hipStream_t stream);
+hipError_t launch_double_quant(const float* absmax_f32, const unsigned long long* hist,
+                               int64_t nb, int8_t* q, float* absmax2, float* mean,
+                               hipStream_t stream);
+hipError_t launch_dequantize(const uint8_t* packed, int64_t n, const void* absmax,
+                             const float* absmax2, const float* mean, int double_quant,
+                             uint16_t* out, hipStream_t stream);
+// Returns hipErrorNotSupported if no GEMV variant covers (M, K).
+hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* packed, const void* absmax,
+                       const float* absmax2, const float* mean, int double_quant, int M, int N,
+                       int K, uint16_t* y, int64_t ldy, hipStream_t stream);
+hipError_t launch_gemm(const uint16_t* x, int64_t ldx, const uint8_t* packed, const void* absmax,
+                       const float* absmax2, const float* mean, int double_quant, int M, int N,
+                       int K, uint16_t* y, int64_t ldy, hipStream_t stream);
+
+}  // namespace bnbx

@@ -1,0 +1,279 @@
+// Blockwise NF4 quantize-on-load and double quantization of the block scales
+// for gfx950.
+//
+// mlqm.cn bitsandbytes article (news/394670): sec. 2.2 (weights are quantized
+// while they are loaded, with no calibration data), sec. 3.2 (nearest of 16
+// NormalFloat levels), sec. 3.3 (one FP32 absmax scale per block; double
+// quantization compresses those scales a second time).
+//
+// quantize_kernel streams the bf16 weight once (16-byte loads, 8 weights per
+// lane, 8 lanes per 64-weight block), reduces the block absmax with DPP,
+// normalises with the block's fp32 reciprocal and encodes each weight with one
+// bucket lookup plus one compare (see EncodeTable), packs two codes per byte
+// and writes 4 bytes per lane.  With double quantization it also writes the
+// fp32 absmax to the workspace and accumulates an exact exponent histogram of
+// the absmax values (sum of the 8-bit significands per binary exponent), from
+// which double_quant_kernel forms the exactly rounded mean.
+#include <float.h>
+
+#include "bnbx_device.hpp"
+#include "bnbx_internal.hpp"
+
+namespace bnbx {
+namespace {
+
+constexpr int kQThreads = 256;
+constexpr int kQWaves = kQThreads / 64;
+constexpr int kTabStride = 256;   // LDS bytes per bucket: 32 copies of an 8-byte entry
+constexpr int kUnroll = 2;        // 512-weight tiles in flight per wave
+constexpr int kTile = 512;        // weights per wave per tile (8 blocks)
+
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v, int ctrl_id) {
+  uint32_t o;
+  switch (ctrl_id) {
+    case 0: o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false); break;   // quad_perm 1,0,3,2
+    case 1: o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false); break;   // quad_perm 2,3,0,1
+    default: o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false); break; // row_half_mirror
+  }
+  return v > o ? v : o;
+}
+
+// Code of one normalised value x in [-1, 1] (or +-inf / NaN when the block
+// reciprocal overflowed, handled by the caller).
+__device__ __forceinline__ uint32_t encode_one(float x, const unsigned char* tab, uint32_t lanebase) {
+  // 2^23 + 16 + 16 x rounded once to an integer: the low byte is the bucket.
+  const float f = __builtin_fmaf(x, 16.0f, 8388624.0f);
+  const uint32_t addr = perm(__float_as_uint(f), lanebase, 0x0c0c0400u);
+  const uint2 e = *(const uint2*)(tab + addr);
+  return e.y + (x >= __uint_as_float(e.x) ? 1u : 0u);
+}
+
+__global__ __launch_bounds__(kQThreads) void quantize_kernel(
+    const uint16_t* __restrict__ w, uint8_t* __restrict__ packed, float* __restrict__ absmax,
+    unsigned long long* __restrict__ hist, int64_t n, EncodeTable et) {
+  __shared__ __attribute__((aligned(16))) unsigned char tab[kBuckets * kTabStride];
+  __shared__ uint32_t lhist[kHistBins];
+
+  const int tid = threadIdx.x;
+  for (int e = tid; e < kBuckets * 32; e += kQThreads) {
+    const int b = e >> 5, c = e & 31;
+    uint2 v;
+    v.x = __float_as_uint(et.thr[b]);
+    v.y = et.base[b];
+    *(uint2*)(tab + b * kTabStride + c * 8) = v;
+  }
+  for (int e = tid; e < (int)kHistBins; e += kQThreads) lhist[e] = 0;
+  __syncthreads();
+
+  const int lane = tid & 63;
+  const uint32_t lanebase = (uint32_t)(lane & 31) << 3;
+  const int64_t ntiles = (n + kTile - 1) / kTile;
+  const int64_t gw = (int64_t)blockIdx.x * kQWaves + (tid >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * kQWaves;
+
+  for (int64_t t0 = gw * kUnroll; t0 < ntiles; t0 += nwaves * kUnroll) {
+    uint4 v[kUnroll];
+    int64_t e0[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      e0[u] = (t0 + u) * kTile + lane * 8;
+      if (e0[u] + 8 <= n) {
+        v[u] = load_nt16(w + e0[u]);
+      } else {
+        uint16_t h[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) h[k] = (e0[u] + k < n) ? w[e0[u] + k] : (uint16_t)0;
+        v[u].x = h[0] | ((uint32_t)h[1] << 16);
+        v[u].y = h[2] | ((uint32_t)h[3] << 16);
+        v[u].z = h[4] | ((uint32_t)h[5] << 16);
+        v[u].w = h[6] | ((uint32_t)h[7] << 16);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t d[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      // |w| as bf16 bits: for non-negative floats integer order is value order.
+      uint32_t m = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t a = d[k] & 0x7fff7fffu;
+        const uint32_t lo = a & 0xffffu, hi = a >> 16;
+        m = max(m, max(lo, hi));
+      }
+      m = dpp_max_u32(m, 0);
+      m = dpp_max_u32(m, 1);
+      m = dpp_max_u32(m, 2);   // now the max over this lane's 8-lane block
+      const float amax = __uint_as_float(m << 16);
+      const float r = (amax == 0.0f) ? 0.0f : 1.0f / amax;
+
+      uint32_t word = 0;
+      if (__builtin_expect(r <= FLT_MAX, 1)) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float x0 = bf16lo_to_f32(d[k]) * r;   // even element -> high nibble
+          const float x1 = bf16hi_to_f32(d[k]) * r;
+          const uint32_t c0 = encode_one(x0, tab, lanebase);
+          const uint32_t c1 = encode_one(x1, tab, lanebase);
+          word |= ((c0 << 4) | c1) << (8 * k);
+        }
+      } else {
+        // Reciprocal overflowed (absmax below 2^-128): x is +inf, -inf or NaN,
+        // whose codes are 15, 0 and 0 (count of thresholds <= x).
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float x0 = bf16lo_to_f32(d[k]) * r;
+          const float x1 = bf16hi_to_f32(d[k]) * r;
+          const uint32_t c0 = x0 > 1.0f ? 15u : 0u, c1 = x1 > 1.0f ? 15u : 0u;
+          word |= ((c0 << 4) | c1) << (8 * k);
+        }
+      }
+
+      const int64_t e = e0[u];
+      if (e + 8 <= n) {
+        *(uint32_t*)(packed + (e >> 1)) = word;
+      } else if (e < n) {
+        const int nbytes = (int)((n - e) >> 1);
+        for (int k = 0; k < nbytes; ++k) packed[(e >> 1) + k] = (uint8_t)(word >> (8 * k));
+      }
+      if ((lane & 7) == 0 && e < n) {
+        const int64_t blk = e / kBlock;
+        absmax[blk] = amax;
+        if (hist != nullptr && m != 0) {
+          const uint32_t ex = m >> 7;          // binary exponent field
+          const uint32_t sig = (m & 0x7fu) | (ex ? 0x80u : 0u);
+          atomicAdd(&lhist[ex], sig);
+        }
+      }
+    }
+  }
+
+  if (hist != nullptr) {
+    __syncthreads();
+    for (int e = tid; e < (int)kHistBins; e += kQThreads)
+      if (lhist[e]) atomicAdd(&hist[e], (unsigned long long)lhist[e]);
+  }
+}
+
+__global__ void zero_hist_kernel(unsigned long long* __restrict__ hist) {
+  hist[threadIdx.x] = 0ull;
+}
+
+// Exact mean of the block absmax values.  absmax = sig * 2^(max(e,1) - 134)
+// for binary exponent field e and 8-bit significand sig, so
+// sum = I * 2^-133 with I = sum_e hist[e] * 2^(max(e,1)-1), an integer below
+// 2^320.  I is assembled in ten 32-bit digits, rounded once to binary64
+// (nearest even), divided by nb in binary64 and rounded to binary32.
+__device__ float exact_mean(const unsigned long long* __restrict__ hist, int64_t nb,
+                            unsigned long long* digits /* LDS[10] */) {
+  const int tid = threadIdx.x;
+  if (tid < 10) digits[tid] = 0ull;
+  __syncthreads();
+  for (int e = tid; e < (int)kHistBins; e += blockDim.x) {
+    const unsigned long long h = hist[e];
+    if (h) {
+      const int sh = (e > 1 ? e : 1) - 1;
+      const int k = sh >> 5, bit = sh & 31;
+      const unsigned long long pl = (h & 0xffffffffull) << bit;
+      const unsigned long long ph = (h >> 32) << bit;
+      atomicAdd(&digits[k], pl & 0xffffffffull);
+      atomicAdd(&digits[k + 1], (pl >> 32) + (ph & 0xffffffffull));
+      atomicAdd(&digits[k + 2], ph >> 32);
+    }
+  }
+  __syncthreads();
+  double S = 0.0;
+  if (tid == 0) {
+    uint32_t dig[10];
+    unsigned long long carry = 0;
+    for (int j = 0; j < 10; ++j) {
+      const unsigned long long t = digits[j] + carry;
+      dig[j] = (uint32_t)t;
+      carry = t >> 32;
+    }
+    int hj = 9;
+    while (hj >= 0 && dig[hj] == 0) --hj;
+    if (hj >= 0) {
+      const int lz = __clz(dig[hj]);
+      const unsigned long long whi = ((unsigned long long)dig[hj] << 32) | (hj >= 1 ? dig[hj - 1] : 0u);
+      const uint32_t wlo = hj >= 2 ? dig[hj - 2] : 0u;
+      bool sticky = false;
+      for (int j = 0; j < hj - 2; ++j) sticky |= dig[j] != 0u;
+      const unsigned long long top = lz ? (whi << lz) | (wlo >> (32 - lz)) : whi;
+      const uint32_t rest = lz ? (wlo << lz) : wlo;
+      sticky |= rest != 0u;
+      unsigned long long m = top >> 11;
+      const uint32_t drop = (uint32_t)(top & 0x7ffu);
+      if (drop > 0x400u || (drop == 0x400u && (sticky || (m & 1ull)))) ++m;
+      S = ldexp((double)m, 32 * (hj - 1) - lz + 11 - 133);
+    }
+    const double mean = S / (double)nb;
+    digits[0] = __double_as_longlong(mean);  // hand the result to the block
+  }
+  __syncthreads();
+  const double mean = __longlong_as_double((long long)digits[0]);
+  return (float)mean;
+}
+
+__global__ __launch_bounds__(256) void double_quant_kernel(
+    const float* __restrict__ a, const unsigned long long* __restrict__ hist, int64_t nb,
+    int8_t* __restrict__ q, float* __restrict__ s_out, float* __restrict__ mean_out) {
+  __shared__ unsigned long long digits[10];
+  __shared__ float red[4];
+  const float mu = exact_mean(hist, nb, digits);
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && tid == 0) *mean_out = mu;
+  const int64_t ng = (nb + kGroup - 1) / kGroup;
+  for (int64_t g = blockIdx.x; g < ng; g += gridDim.x) {
+    const int64_t b = g * kGroup + tid;
+    const bool valid = b < nb;
+    const float c = valid ? a[b] - mu : 0.0f;
+    float m = wave_max(fabsf(c));
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    const float s = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    int qv = 0;
+    if (s > 0.0f) {
+      const float t = c / s;          // correctly rounded binary32 division
+      const float u = t * 127.0f;
+      qv = (int)rintf(u);             // round half to even
+    }
+    if (valid) q[b] = (int8_t)qv;
+    if (tid == 0) s_out[g] = s;
+    __syncthreads();
+  }
+}
+
+int grid_for(int64_t work_items, int per_block, int cap) {
+  int64_t g = (work_items + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return (int)g;
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const uint16_t* w, uint8_t* packed, int64_t n, float* absmax_f32,
+                           unsigned long long* hist, hipStream_t stream) {
+  const int64_t ntiles = (n + kTile - 1) / kTile;
+  const int grid = grid_for(ntiles, kQWaves * kUnroll, 4096);
+  hipLaunchKernelGGL(quantize_kernel, dim3(grid), dim3(kQThreads), 0, stream, w, packed,
+                     absmax_f32, hist, n, encode_table());
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_hist(unsigned long long* hist, hipStream_t stream) {
+  hipLaunchKernelGGL(zero_hist_kernel, dim3(1), dim3((unsigned)kHistBins), 0, stream, hist);
+  return hipGetLastError();
+}
+
+hipError_t launch_double_quant(const float* absmax_f32, const unsigned long long* hist,
+                               int64_t nb, int8_t* q, float* absmax2, float* mean,
+                               hipStream_t stream) {
+  const int64_t ng = (nb + kGroup - 1) / kGroup;
+  const int grid = grid_for(ng, 1, 1024);
+  hipLaunchKernelGGL(double_quant_kernel, dim3(grid), dim3(256), 0, stream, absmax_f32, hist, nb,
+                     q, absmax2, mean);
+  return hipGetLastError();
+}
+
+}  // namespace bnbx

@@ -1,0 +1,99 @@
+"""Torch-tensor convenience layer over the C ABI: allocates device buffers
+with PyTorch (plumbing only) and calls the bnbx_* entry points.  Nothing is
+computed here."""
+
+from __future__ import annotations
+
+import dataclasses
+
+import torch
+
+from . import (Nf4State, bnbx_dequantize_nf4, bnbx_gemm_nf4, bnbx_gemm_nf4_workspace_bytes,
+               bnbx_gemv_nf4, bnbx_quantize_nf4, bnbx_quantize_nf4_workspace_bytes)
+
+BLOCKSIZE = 64
+GROUP = 256
+
+
+@dataclasses.dataclass
+class QuantizedWeight:
+    """Device buffers of one NF4 tensor plus its C descriptor."""
+
+    n: int
+    shape: tuple
+    double_quant: bool
+    packed: torch.Tensor          # uint8 [n/2]
+    absmax: torch.Tensor          # float32 [nb] or int8 [nb]
+    absmax2: torch.Tensor | None  # float32 [ng]
+    absmax_mean: torch.Tensor | None  # float32 [1]
+
+    @property
+    def state(self) -> Nf4State:
+        return Nf4State(
+            n=self.n, blocksize=BLOCKSIZE, double_quant=int(self.double_quant),
+            absmax=self.absmax.data_ptr(),
+            absmax2=self.absmax2.data_ptr() if self.absmax2 is not None else None,
+            absmax_mean=self.absmax_mean.data_ptr() if self.absmax_mean is not None else None)
+
+
+def empty_quantized(shape, double_quant: bool, device="cuda") -> QuantizedWeight:
+    n = 1
+    for s in shape:
+        n *= int(s)
+    nb = -(-n // BLOCKSIZE)
+    ng = -(-nb // GROUP)
+    packed = torch.empty(n // 2, dtype=torch.uint8, device=device)
+    if double_quant:
+        absmax = torch.empty(nb, dtype=torch.int8, device=device)
+        absmax2 = torch.empty(ng, dtype=torch.float32, device=device)
+        mean = torch.empty(1, dtype=torch.float32, device=device)
+    else:
+        absmax = torch.empty(nb, dtype=torch.float32, device=device)
+        absmax2 = mean = None
+    return QuantizedWeight(n, tuple(shape), double_quant, packed, absmax, absmax2, mean)
+
+
+def workspace_for(n: int, double_quant: bool, device="cuda") -> torch.Tensor | None:
+    nbytes = bnbx_quantize_nf4_workspace_bytes(n, BLOCKSIZE, int(double_quant))
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def quantize(w: torch.Tensor, double_quant: bool, out: QuantizedWeight | None = None,
+             workspace: torch.Tensor | None = None, stream=None) -> QuantizedWeight:
+    """bnbx_quantize_nf4 on a bf16 tensor (any shape, contiguous)."""
+    assert w.dtype == torch.bfloat16 and w.is_contiguous()
+    q = out if out is not None else empty_quantized(w.shape, double_quant, w.device)
+    ws = workspace if workspace is not None else workspace_for(q.n, double_quant, w.device)
+    bnbx_quantize_nf4(w, q.packed, q.state, ws, 0 if ws is None else ws.numel(), stream)
+    return q
+
+
+def dequantize(q: QuantizedWeight, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    o = out if out is not None else torch.empty(q.shape, dtype=torch.bfloat16,
+                                                device=q.packed.device)
+    bnbx_dequantize_nf4(q.packed, q.state, o, stream)
+    return o
+
+
+def gemv(x: torch.Tensor, q: QuantizedWeight, out: torch.Tensor | None = None,
+         stream=None) -> torch.Tensor:
+    """Y = X . W_hat^T for X [M, K] (M <= 16), W [N, K]."""
+    M, K = x.shape
+    N = q.shape[0]
+    y = out if out is not None else torch.empty(M, N, dtype=torch.bfloat16, device=x.device)
+    bnbx_gemv_nf4(x, x.stride(0), q.packed, q.state, M, N, K, y, y.stride(0), stream)
+    return y
+
+
+def gemm(x: torch.Tensor, q: QuantizedWeight, out: torch.Tensor | None = None,
+         stream=None) -> torch.Tensor:
+    """Y = X . W_hat^T for X [M, K], W [N, K], any M."""
+    M, K = x.shape
+    N = q.shape[0]
+    y = out if out is not None else torch.empty(M, N, dtype=torch.bfloat16, device=x.device)
+    nbytes = bnbx_gemm_nf4_workspace_bytes(M, N, K)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device) if nbytes else None
+    bnbx_gemm_nf4(x, x.stride(0), q.packed, q.state, M, N, K, y, y.stride(0), ws, nbytes, stream)
+    return y

@@ -1,0 +1,162 @@
+/*
+ * bnbx.h -- C ABI of the MI355X (gfx950) NF4 4-bit weight library.
+ *
+ * Blockwise NF4 quantize-on-load with double quantization of the block scales,
+ * dequantize to bfloat16, and the "4-bit storage, 16-bit compute" linear layer
+ * Y = X . W_hat^T as a decode GEMV (M <= 16) and a prefill GEMM (any M).
+ *
+ * Sources (five web pages about bitsandbytes, cited by page and section):
+ *   mlqm.cn bitsandbytes article (news/394670), sec. 2.2 (quantize while
+ *     loading, no calibration data), 3.2 (NF4: 16 levels placed by the normal
+ *     density), 3.3 (one FP32 scale per block; double quantization quantizes
+ *     the scales again), 3.4 (store 4-bit, dequantize to FP16/BF16, multiply);
+ *   pomoai.com bitsandbytes overview, module list (Linear4bit replaces
+ *     torch.nn.Linear: weight [out_features, in_features]; the functional
+ *     module holds blockwise quantization and the NF4 format).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - bf16 values are passed as uint16_t bit patterns.
+ * - Pointers named "device" are device (HBM) addresses; the caller allocates
+ *   and frees every buffer.  The library never allocates device memory, never
+ *   frees, and never synchronises: work is enqueued on `stream` (a
+ *   hipStream_t; NULL means the null stream) and results are ready when the
+ *   caller synchronises that stream.
+ * - Every call validates its arguments on the host before enqueueing anything
+ *   and returns a negative bnbx_status without side effects on failure.  A
+ *   launch failure reported by the HIP runtime returns BNBX_E_HIP.  Faults
+ *   during execution surface at the caller's next synchronisation.
+ * - The library keeps no mutable global state after its one-time codebook
+ *   initialisation, so calls on different streams may run concurrently.
+ *   Calls that share output or workspace buffers must be ordered by the caller.
+ * - Inputs must be finite.  A non-finite weight gives unspecified codes.
+ *
+ * Quantized tensor format (the "quant state")
+ * -------------------------------------------
+ * A weight of n elements (row-major [N, K] for a linear layer, n = N*K, n
+ * even) is split into nb = ceil(n / 64) blocks of 64 consecutive elements of
+ * the flat array (the last block may be short).
+ *   packed   uint8[n/2]   two 4-bit codes per byte; element 2j in the HIGH
+ *                         nibble of byte j, element 2j+1 in the low nibble.
+ *   Without double quant:
+ *     absmax   float[nb]  a_b = max |w| over block b.
+ *   With double quant (second-level groups of 256 consecutive blocks,
+ *   ng = ceil(nb / 256)):
+ *     absmax      int8_t[nb]  q_b, the block scale a_b minus the mean, in
+ *                             units of s_g / 127, rounded half-even
+ *     absmax2     float[ng]   s_g = max |a_b - mean| over group g
+ *     absmax_mean float[1]    mean = fl32(fl64(sum_b a_b) / nb), the sum exact
+ *   Dequantized scale: without DQ a_b; with DQ
+ *     fl32(fl32(q_b * fl32(s_g / 127)) + mean).
+ *   Code of element j: x = fl32(w_j * fl32(1 / a_b)); c = #{i : x >= T_i}
+ *   where T_i is the smallest float above the midpoint of levels i and i+1
+ *   (nearest level, exact ties to the lower index); an all-zero block takes
+ *   code 7 (the 0.0 level).
+ *   Dequantized weight: W_hat_j = bf16(fl32(L[c_j] * scale_b)), round to
+ *   nearest even.
+ */
+#ifndef BNBX_H
+#define BNBX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Only the entry points below are exported from libbnbx.so. */
+#define BNBX_API __attribute__((visibility("default")))
+
+typedef enum {
+  BNBX_OK = 0,
+  BNBX_E_INVAL = -1,        /* bad size, null pointer, out-of-range argument   */
+  BNBX_E_ALIGN = -2,        /* a pointer or leading dimension is misaligned    */
+  BNBX_E_UNSUPPORTED = -3,  /* valid request this build does not implement     */
+  BNBX_E_WORKSPACE = -4,    /* workspace missing or smaller than required      */
+  BNBX_E_HIP = -5           /* the HIP runtime reported an error at launch     */
+} bnbx_status;
+
+/* Caller-owned descriptor of one quantized tensor (host memory; the pointers
+ * inside are device addresses).  The library reads it during the call only. */
+typedef struct {
+  int64_t n;             /* number of weights, even, >= 2                      */
+  int32_t blocksize;     /* weights per block; only 64 is supported            */
+  int32_t double_quant;  /* 0: absmax is float[nb]; 1: int8 + absmax2 + mean  */
+  void*   absmax;        /* device: float[nb] (dq=0) or int8_t[nb] (dq=1)      */
+  float*  absmax2;       /* device: float[ng] (dq=1), else NULL                */
+  float*  absmax_mean;   /* device: float[1]  (dq=1), else NULL                */
+} bnbx_nf4_state;
+
+/* Human-readable name of a status code (static string, never NULL). */
+BNBX_API const char* bnbx_status_str(int status);
+
+/* The 16 NF4 levels, ascending, into host memory.
+ * mlqm.cn article sec. 3.2: 16 levels at standard-normal quantiles, dense
+ * near zero and sparse at the ends; here 8 positive quantiles of probabilities
+ * evenly spaced from 1 - (1/30 + 1/32)/2 toward 1/2, 7 mirrored negative ones
+ * over the same span, and 0, divided by the outermost quantile so that
+ * L[0] = -1, L[7] = 0, L[15] = +1 exactly.  Host-only, synchronous.
+ * Returns BNBX_E_INVAL if levels_host is NULL. */
+BNBX_API int bnbx_nf4_codebook(float levels_host[16]);
+
+/* Bytes of device workspace bnbx_quantize_nf4 needs for (n, blocksize,
+ * double_quant); 0 without double quant.  Returns 0 for invalid arguments. */
+BNBX_API size_t bnbx_quantize_nf4_workspace_bytes(int64_t n, int blocksize, int double_quant);
+
+/* Blockwise NF4 quantize-on-load (mlqm.cn article sec. 2.2, 3.2, 3.3).
+ *   w          device, bf16[n], 16-byte aligned (read only)
+ *   packed     device, uint8[n/2], 16-byte aligned (written)
+ *   st         host descriptor; st->absmax (and absmax2, absmax_mean with
+ *              double quant) are written
+ *   workspace  device, >= bnbx_quantize_nf4_workspace_bytes(...) bytes,
+ *              256-byte aligned (may be NULL when that is 0); contents are
+ *              scratch, overwritten by the call
+ * Errors: BNBX_E_INVAL (null pointer, n odd or < 2, blocksize != 64 is
+ * BNBX_E_UNSUPPORTED), BNBX_E_ALIGN, BNBX_E_WORKSPACE. */
+BNBX_API int bnbx_quantize_nf4(const uint16_t* w, uint8_t* packed, const bnbx_nf4_state* st,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Dequantize to bfloat16 (mlqm.cn article sec. 3.4).
+ *   packed  device, uint8[n/2], 16-byte aligned
+ *   st      host descriptor of the quant state (read)
+ *   out     device, bf16[n], 16-byte aligned (written)
+ * Errors: BNBX_E_INVAL, BNBX_E_ALIGN, BNBX_E_UNSUPPORTED. */
+BNBX_API int bnbx_dequantize_nf4(const uint8_t* packed, const bnbx_nf4_state* st, uint16_t* out,
+                        void* stream);
+
+/* Decode GEMV, Y[M, N] = X[M, K] . W_hat[N, K]^T, 1 <= M <= 16
+ * (mlqm.cn article sec. 3.4 and the "4-bit is not always faster" pitfall in
+ * sec. 7: the weight is streamed once from HBM in 4 bits and dequantized in
+ * registers; products accumulate in fp32; Y is rounded to bf16).
+ *   x       device, bf16, row m at x + m*ldx; ldx >= K, ldx % 8 == 0,
+ *           16-byte aligned
+ *   packed  device, the quantized [N, K] weight (st->n == N*K), 16-byte aligned
+ *   y       device, bf16, row m at y + m*ldy; ldy >= N, written
+ * K must be a multiple of 64 (blocks never straddle rows).
+ * Errors: BNBX_E_INVAL (sizes, M outside 1..16, null), BNBX_E_ALIGN,
+ * BNBX_E_UNSUPPORTED. */
+BNBX_API int bnbx_gemv_nf4(const uint16_t* x, int64_t ldx, const uint8_t* packed,
+                  const bnbx_nf4_state* st, int M, int N, int K,
+                  uint16_t* y, int64_t ldy, void* stream);
+
+/* Bytes of device workspace bnbx_gemm_nf4 needs for (M, N, K); this build
+ * needs none and returns 0 for valid sizes. */
+BNBX_API size_t bnbx_gemm_nf4_workspace_bytes(int M, int N, int K);
+
+/* Prefill GEMM, Y[M, N] = X[M, K] . W_hat[N, K]^T for any M >= 1: weight
+ * tiles are dequantized into LDS and fed to bf16 matrix cores with fp32
+ * accumulation; Y is rounded to bf16 (mlqm.cn article sec. 3.4, "4-bit
+ * storage, 16-bit compute").  Arguments as bnbx_gemv_nf4; workspace as
+ * sized by bnbx_gemm_nf4_workspace_bytes (may be NULL when that is 0).
+ * Errors: as bnbx_gemv_nf4 (M >= 1), BNBX_E_WORKSPACE. */
+BNBX_API int bnbx_gemm_nf4(const uint16_t* x, int64_t ldx, const uint8_t* packed,
+                  const bnbx_nf4_state* st, int M, int N, int K,
+                  uint16_t* y, int64_t ldy, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BNBX_H */

@@ -1,0 +1,71 @@
+"""Helpers for the GPU parity tests: move seeded inputs to the device, call the
+library through its C ABI (dequant_gemm_nf4_amd), bring results back as
+NumPy arrays in the oracle's formats."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from dequant_gemm_nf4_amd import tensors as T
+
+
+def dev_bf16(bits: np.ndarray, shape=None) -> torch.Tensor:
+    a = np.ascontiguousarray(bits, dtype=np.uint16)
+    t = torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16)
+    if shape is not None:
+        t = t.reshape(shape)
+    return t.cuda()
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16).ravel()
+
+
+def gpu_quantize(w_bits: np.ndarray, shape, dq: bool) -> dict:
+    w = dev_bf16(w_bits, shape)
+    q = T.quantize(w, dq)
+    torch.cuda.synchronize()
+    out = {"packed": q.packed.cpu().numpy(), "double_quant": dq, "n": q.n, "blocksize": 64}
+    if dq:
+        out["absmax"] = q.absmax.cpu().numpy()
+        out["absmax2"] = q.absmax2.cpu().numpy()
+        out["absmax_mean"] = np.float32(q.absmax_mean.cpu().numpy()[0])
+    else:
+        out["absmax"] = q.absmax.cpu().numpy()
+    out["_device"] = q
+    return out
+
+
+def upload_state(ostate: dict, shape) -> T.QuantizedWeight:
+    """Device copy of a quant state the oracle produced."""
+    dq = ostate["double_quant"]
+    q = T.empty_quantized(shape, dq)
+    q.packed.copy_(torch.from_numpy(np.ascontiguousarray(ostate["packed"])))
+    if dq:
+        q.absmax.copy_(torch.from_numpy(np.ascontiguousarray(ostate["absmax"], np.int8)))
+        q.absmax2.copy_(torch.from_numpy(np.ascontiguousarray(ostate["absmax2"], np.float32)))
+        q.absmax_mean.copy_(torch.tensor([float(ostate["absmax_mean"])], dtype=torch.float32))
+    else:
+        q.absmax.copy_(torch.from_numpy(np.ascontiguousarray(ostate["absmax"], np.float32)))
+    return q
+
+
+def same_f32_bits(a, b) -> bool:
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    b = np.ascontiguousarray(b, dtype=np.float32)
+    return a.shape == b.shape and np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def assert_state_equal(gpu: dict, ref: dict) -> None:
+    assert np.array_equal(gpu["packed"], ref["packed"]), \
+        f"packed differs at {np.flatnonzero(gpu['packed'] != ref['packed'])[:10]}"
+    if ref["double_quant"]:
+        assert np.array_equal(gpu["absmax"], ref["absmax"]), \
+            f"q differs at {np.flatnonzero(gpu['absmax'] != ref['absmax'])[:10]}"
+        assert same_f32_bits(gpu["absmax2"], ref["absmax2"])
+        assert same_f32_bits([gpu["absmax_mean"]], [ref["absmax_mean"]]), \
+            (gpu["absmax_mean"], ref["absmax_mean"])
+    else:
+        assert same_f32_bits(gpu["absmax"], ref["absmax"]), \
+            f"absmax differs at {np.flatnonzero(gpu['absmax'] != ref['absmax'])[:10]}"

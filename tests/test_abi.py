@@ -1,0 +1,169 @@
+"""The C-ABI library without a GPU: it loads, exports exactly the entry
+points include/bnbx.h declares, its host-side codebook equals the oracle's,
+and every invalid argument is rejected on the host before any launch (the
+pointers below are never dereferenced)."""
+
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import dequant_gemm_nf4_amd as bnbx
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bnbx.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"BNBX_API\s+[\w\s\*]*?\b(bnbx_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return bnbx.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = header_functions()
+    assert len(declared) == 8
+    assert sorted(bnbx.EXPORTED_SYMBOLS) == declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", bnbx.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = sorted(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
+    assert exported == declared
+
+
+def test_codebook_equals_oracle_bit_for_bit():
+    ours = np.array(bnbx.bnbx_nf4_codebook(), dtype=np.float32)
+    assert np.array_equal(ours.view(np.uint32), oracle.codebook().view(np.uint32))
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert bnbx.bnbx_status_str(code).startswith("BNBX")
+    assert "unknown" in bnbx.bnbx_status_str(7)
+
+
+def test_workspace_queries():
+    n = 4096 * 4096
+    nb = n // 64
+    assert bnbx.bnbx_quantize_nf4_workspace_bytes(n, 64, 0) == 0
+    ws = bnbx.bnbx_quantize_nf4_workspace_bytes(n, 64, 1)
+    assert ws >= 256 * 8 + 4 * nb and ws % 256 == 0
+    assert bnbx.bnbx_quantize_nf4_workspace_bytes(n + 1, 64, 1) == 0
+    assert bnbx.bnbx_quantize_nf4_workspace_bytes(n, 32, 1) == 0
+    assert bnbx.bnbx_gemm_nf4_workspace_bytes(2048, 8192, 8192) == 0
+
+
+A = 1 << 20          # fake, 256-byte aligned "device" addresses: never touched
+B = 2 << 20
+C = 3 << 20
+D = 4 << 20
+
+
+def state(n=4096, dq=1, blocksize=64, absmax=C, absmax2=D, mean=D + 4096):
+    return bnbx.Nf4State(n=n, blocksize=blocksize, double_quant=dq, absmax=absmax,
+                         absmax2=absmax2 if dq else None, absmax_mean=mean if dq else None)
+
+
+def status_of(fn, *args):
+    try:
+        fn(*args)
+    except bnbx.BnbxError as e:
+        return e.status
+    raise AssertionError("call was accepted (it would have launched)")
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_w", bnbx.BNBX_E_INVAL),
+    ("odd_n", bnbx.BNBX_E_INVAL),
+    ("tiny_n", bnbx.BNBX_E_INVAL),
+    ("blocksize", bnbx.BNBX_E_UNSUPPORTED),
+    ("dq_flag", bnbx.BNBX_E_INVAL),
+    ("null_absmax", bnbx.BNBX_E_INVAL),
+    ("null_absmax2", bnbx.BNBX_E_INVAL),
+    ("misaligned_w", bnbx.BNBX_E_ALIGN),
+    ("misaligned_packed", bnbx.BNBX_E_ALIGN),
+    ("no_workspace", bnbx.BNBX_E_WORKSPACE),
+    ("small_workspace", bnbx.BNBX_E_WORKSPACE),
+    ("misaligned_workspace", bnbx.BNBX_E_ALIGN),
+])
+def test_quantize_rejects(case, expect):
+    n = 4096
+    ws_need = bnbx.bnbx_quantize_nf4_workspace_bytes(n, 64, 1)
+    w, p, st, ws, wsb = A, B, state(n), C + (1 << 16), ws_need
+    if case == "null_w":
+        w = None
+    elif case == "odd_n":
+        st = state(n + 1)
+    elif case == "tiny_n":
+        st = state(0)
+    elif case == "blocksize":
+        st = state(n, blocksize=128)
+    elif case == "dq_flag":
+        st = state(n, dq=2)
+    elif case == "null_absmax":
+        st = state(n, absmax=None)
+    elif case == "null_absmax2":
+        st = state(n)
+        st.absmax2 = None
+    elif case == "misaligned_w":
+        w = A + 2
+    elif case == "misaligned_packed":
+        p = B + 8
+    elif case == "no_workspace":
+        ws = None
+    elif case == "small_workspace":
+        wsb = ws_need - 1
+    elif case == "misaligned_workspace":
+        ws = C + 128
+    assert status_of(bnbx.bnbx_quantize_nf4, w, p, st, ws, wsb, 0) == expect
+
+
+def test_dequantize_rejects():
+    assert status_of(bnbx.bnbx_dequantize_nf4, None, state(), B, 0) == bnbx.BNBX_E_INVAL
+    assert status_of(bnbx.bnbx_dequantize_nf4, A, state(), None, 0) == bnbx.BNBX_E_INVAL
+    assert status_of(bnbx.bnbx_dequantize_nf4, A + 1, state(), B, 0) == bnbx.BNBX_E_ALIGN
+    assert status_of(bnbx.bnbx_dequantize_nf4, A, state(), B + 2, 0) == bnbx.BNBX_E_ALIGN
+    assert status_of(bnbx.bnbx_dequantize_nf4, A, state(7), B, 0) == bnbx.BNBX_E_INVAL
+    assert status_of(bnbx.bnbx_dequantize_nf4, A, state(blocksize=32), B, 0) == \
+        bnbx.BNBX_E_UNSUPPORTED
+
+
+@pytest.mark.parametrize("fn", ["gemv", "gemm"])
+def test_matmul_rejects(fn):
+    N, K = 256, 512
+
+    def call(x=A, ldx=K, p=B, st=None, M=1, N_=N, K_=K, y=C, ldy=N):
+        st = st if st is not None else state(N * K)
+        if fn == "gemv":
+            return status_of(bnbx.bnbx_gemv_nf4, x, ldx, p, st, M, N_, K_, y, ldy, 0)
+        return status_of(bnbx.bnbx_gemm_nf4, x, ldx, p, st, M, N_, K_, y, ldy, None, 0, 0)
+
+    assert call(x=None) == bnbx.BNBX_E_INVAL
+    assert call(y=None) == bnbx.BNBX_E_INVAL
+    assert call(p=None) == bnbx.BNBX_E_INVAL
+    assert call(M=0) == bnbx.BNBX_E_INVAL
+    assert call(N_=0) == bnbx.BNBX_E_INVAL
+    assert call(K_=100, st=state(N * 100)) == bnbx.BNBX_E_INVAL      # K % 64 != 0
+    assert call(st=state(N * K + 2)) == bnbx.BNBX_E_INVAL           # n != N*K
+    assert call(ldx=K - 8) == bnbx.BNBX_E_INVAL
+    assert call(ldy=N - 1) == bnbx.BNBX_E_INVAL
+    assert call(ldx=K + 4) == bnbx.BNBX_E_ALIGN
+    assert call(x=A + 8) == bnbx.BNBX_E_ALIGN
+    assert call(p=B + 4) == bnbx.BNBX_E_ALIGN
+    assert call(y=C + 1) == bnbx.BNBX_E_ALIGN
+    assert call(st=state(N * K, blocksize=32)) == bnbx.BNBX_E_UNSUPPORTED
+    if fn == "gemv":
+        assert call(M=17) == bnbx.BNBX_E_INVAL
+
+
+def test_binding_names_match_header():
+    for name in header_functions():
+        assert callable(getattr(bnbx, name)), name

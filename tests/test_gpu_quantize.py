@@ -1,0 +1,144 @@
+"""GPU parity of bnbx_quantize_nf4 and bnbx_dequantize_nf4 against the
+oracle: codes, packed bytes, first- and second-level scales, the mean and the
+dequantized bf16 weights must be bit-identical (the stored format admits
+exactly one result).  Called through the C ABI."""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_helpers import assert_state_equal, gpu_quantize, host_bits, upload_state
+
+pytestmark = pytest.mark.gpu
+
+
+def check_quantize(bits, shape, dq):
+    ref = oracle.quantize(bits, dq)
+    got = gpu_quantize(bits, shape, dq)
+    assert_state_equal(got, ref)
+    return got, ref
+
+
+def test_quantize_tiny_no_double_quant():
+    w, _ = synth.tiny()
+    check_quantize(w, w.shape, False)
+
+
+@pytest.mark.parametrize("s", [0, 1, 2])
+def test_quantize_decode_shapes_double_quant(s):
+    w, _ = synth.decode(s)
+    check_quantize(w, w.shape, True)
+
+
+def test_quantize_batched_outliers_double_quant():
+    w, _ = synth.batched()
+    check_quantize(w, w.shape, True)
+
+
+@pytest.mark.parametrize("dq", [False, True])
+@pytest.mark.parametrize("n", [2, 10, 62, 64, 66, 510, 512, 514, 64 * 1000 + 6,
+                               64 * 256 * 3 + 2, 64 * 256 * 5 + 64 * 7])
+def test_quantize_ragged_sizes(n, dq):
+    bits = synth.normal_bf16((n,), 0.02, 500 + n)
+    check_quantize(bits, (n,), dq)
+
+
+def test_quantize_exhaustive_bf16_weights():
+    """All finite bf16 weights, placed in blocks whose absmax sweeps many
+    binades (each block holds 63 weights of magnitude <= a and one anchor a)."""
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f = oracle.bf16_bits_to_f32(allbits)
+    rng = np.random.default_rng(5)
+    anchors = oracle.f32_to_bf16_bits(
+        np.float32(2.0) ** rng.uniform(-30, 30, 12).astype(np.float32) *
+        rng.uniform(1, 2, 12).astype(np.float32))
+    anchors = np.concatenate([anchors, oracle.f32_to_bf16_bits(
+        np.array([1.0, 0.02, 3.0, 1e38, 6e-39], np.float32))])
+    pieces = []
+    for ab in anchors:
+        a = oracle.bf16_bits_to_f32(np.array([ab]))[0]
+        w = allbits[np.isfinite(f) & (np.abs(f) <= a)]
+        nblk = -(-w.size // 63)
+        body = np.zeros(nblk * 63, np.uint16)
+        body[:w.size] = w
+        pieces.append(np.concatenate([body.reshape(nblk, 63),
+                                      np.full((nblk, 1), ab, np.uint16)], axis=1).ravel())
+    bits = np.concatenate(pieces)
+    for dq in (False, True):
+        check_quantize(bits, bits.shape, dq)
+
+
+def test_quantize_special_blocks():
+    """Zero blocks, a subnormal absmax (the fp32 reciprocal overflows), the
+    largest finite values, and weights that land exactly on representable
+    midpoints between levels (ties go to the lower code)."""
+    L = oracle.codebook().astype(np.float64)
+    mids = [(L[i] + L[i + 1]) / 2 for i in range(15)]
+    mids = [m for m in mids if float(np.float32(m)) == m]
+    blocks = []
+    blocks.append(np.zeros(64, np.float32))                                  # all zero
+    b = np.zeros(64, np.float32)
+    b[0] = 1.0
+    b[1:1 + len(mids)] = mids                                                # exact ties
+    blocks.append(b)
+    blocks.append(np.linspace(-3.0e38, 3.0e38, 64).astype(np.float32))      # huge
+    tiny = np.zeros(64, np.float32)
+    tiny[::3] = np.float32(2.0 ** -131)                                       # subnormal bf16
+    tiny[1::3] = -np.float32(2.0 ** -132)
+    blocks.append(tiny)
+    blocks.append(np.full(64, -0.0, np.float32))                             # negative zeros
+    f = np.concatenate(blocks)
+    bits = oracle.f32_to_bf16_bits(f)
+    assert np.array_equal(oracle.bf16_bits_to_f32(bits)[64 + 1:64 + 1 + len(mids)],
+                          np.array(mids, np.float32))
+    for dq in (False, True):
+        got, ref = check_quantize(bits, bits.shape, dq)
+        assert np.all(ref["codes"][:64] == 7)
+
+
+def test_quantize_workspace_reuse_gives_same_result():
+    w, _ = synth.decode(0)
+    a = gpu_quantize(w, w.shape, True)
+    b = gpu_quantize(w, w.shape, True)
+    assert_state_equal(a, b)
+
+
+# --------------------------------------------------------------------------
+# dequantize
+# --------------------------------------------------------------------------
+def check_dequant(bits, shape, dq):
+    ref_state = oracle.quantize(bits, dq)
+    ref = oracle.dequantize(ref_state["packed"], ref_state)
+    from dequant_gemm_nf4_amd import tensors as T
+    q = upload_state(ref_state, shape)
+    out = host_bits(T.dequantize(q))
+    bad = np.flatnonzero(out != ref)
+    assert bad.size == 0, f"{bad.size} mismatches, first at {bad[:8]}: {out[bad[:8]]} vs {ref[bad[:8]]}"
+
+
+@pytest.mark.parametrize("dq", [False, True])
+def test_dequant_tiny_and_decode(dq):
+    w, _ = synth.tiny()
+    check_dequant(w, w.shape, dq)
+    w, _ = synth.decode(1)
+    check_dequant(w, w.shape, dq)
+
+
+@pytest.mark.parametrize("dq", [False, True])
+@pytest.mark.parametrize("n", [2, 30, 32, 34, 62, 64, 66, 64 * 257 + 18])
+def test_dequant_ragged(n, dq):
+    bits = synth.normal_bf16((n,), 0.3, 900 + n)
+    check_dequant(bits, (n,), dq)
+
+
+def test_dequant_batched_outliers_round_trip():
+    """GPU quantize then GPU dequantize equals the oracle's dequantized weight."""
+    from dequant_gemm_nf4_amd import tensors as T
+    w, _ = synth.batched()
+    got = gpu_quantize(w, w.shape, True)
+    ref_state = oracle.quantize(w, True)
+    assert_state_equal(got, ref_state)
+    out = host_bits(T.dequantize(got["_device"]))
+    ref = oracle.dequantize(ref_state["packed"], ref_state)
+    assert np.array_equal(out, ref)
