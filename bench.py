@@ -146,47 +146,63 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     nlaunch = L * len(DECODE_SHAPES)
 
-    def step(timed):
-        marks = {}
-        for k in ("q0", "q1", "d0", "d1", "v0", "v1", "m0", "m1"):
-            marks[k] = ev()
-        marks["q0"].record(stream)
+    # Each stage of a step is captured once into a HIP graph (replayed every
+    # step) so host-side launch overhead does not enter the kernel timings.
+    def stage_quantize():
         for i, w in enumerate(weights):
-            T.quantize(w, True, out=qs[i], workspace=ws, stream=stream)
-        marks["q1"].record(stream)
-        marks["d0"].record(stream)
-        for i, q in enumerate(qs):
-            T.dequantize(q, out=deq[: q.n].view(q.shape), stream=stream)
-        marks["d1"].record(stream)
-        marks["v0"].record(stream)
+            T.quantize(w, True, out=qs[i], workspace=ws)
+
+    def stage_dequantize():
+        for q in qs:
+            T.dequantize(q, out=deq[: q.n].view(q.shape))
+
+    def stage_gemv():
         for i, q in enumerate(qs):
             s = i % len(DECODE_SHAPES)
-            T.gemv(xs[s], q, out=ys[s], stream=stream)
-        marks["v1"].record(stream)
-        marks["m0"].record(stream)
-        T.gemm(xp, qp, out=yp, stream=stream)
-        marks["m1"].record(stream)
+            T.gemv(xs[s], q, out=ys[s])
+
+    def stage_gemm():
+        T.gemm(xp, qp, out=yp)
+
+    stages = [stage_quantize, stage_dequantize, stage_gemv, stage_gemm]
+    for fn in stages:        # eager warm-up (also loads every kernel)
+        fn()
+    torch.cuda.synchronize()
+    graphs = []
+    cap = torch.cuda.Stream()
+    for fn in stages:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            fn()
+        graphs.append(g)
+    torch.cuda.synchronize()
+
+    def step():
+        marks = [ev() for _ in range(2 * len(graphs))]
+        for k, g in enumerate(graphs):
+            marks[2 * k].record(stream)
+            g.replay()
+            marks[2 * k + 1].record(stream)
         return marks
 
     for _ in range(args.warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
 
     all_marks = []
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        all_marks.append(step(True))
+        all_marks.append(step())
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    def stage_ms(a, b):
-        return sum(m[a].elapsed_time(m[b]) for m in all_marks)
+    def stage_ms(k):
+        return sum(m[2 * k].elapsed_time(m[2 * k + 1]) for m in all_marks)
 
-    t_q = stage_ms("q0", "q1") / 1e3
-    t_d = stage_ms("d0", "d1") / 1e3
-    t_v = stage_ms("v0", "v1") / 1e3
-    t_m = stage_ms("m0", "m1") / 1e3
+    t_q = stage_ms(0) / 1e3
+    t_d = stage_ms(1) / 1e3
+    t_v = stage_ms(2) / 1e3
+    t_m = stage_ms(3) / 1e3
     K_ = args.steps
     gb_v = K_ * L * sum(gemv_bytes(1, N, K) for N, K in DECODE_SHAPES)
     gb_q = K_ * L * sum(quant_bytes(N, K) for N, K in DECODE_SHAPES)

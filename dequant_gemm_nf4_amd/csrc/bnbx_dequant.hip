@@ -13,67 +13,96 @@ namespace bnbx {
 namespace {
 
 constexpr int kDThreads = 256;
+constexpr int kDWaves = kDThreads / 64;
+constexpr int kChunk = 1024;    // packed bytes per wave per chunk (2048 weights, 32 blocks)
+constexpr int kDUnroll = 2;     // chunks per wave per round
+constexpr int kCopies = 4;      // LDS table copies (lane & 3) to spread bank conflicts
 
-__device__ __forceinline__ float level_of(const LevelTable& lv, uint32_t c) {
-  float v = lv.level[0];
-#pragma unroll
-  for (uint32_t i = 1; i < 16; ++i) v = (c == i) ? lv.level[i] : v;
-  return v;
-}
-
+template <bool DQ>
 __device__ __forceinline__ float exact_block_scale(int64_t blk, const void* absmax,
-                                                   const float* absmax2, float mu, int dq) {
-  if (!dq) return ((const float*)absmax)[blk];
+                                                   const float* absmax2, float mu) {
+  if (!DQ) return ((const float*)absmax)[blk];
   const float q = (float)((const int8_t*)absmax)[blk];
   const float step = absmax2[blk / kGroup] / 127.0f;   // correctly rounded
   const float prod = q * step;                        // rounded on its own ...
   return prod + mu;                                   // ... then the add (no FMA)
 }
 
+// 8 weights (one packed dword) -> 16 bytes of bf16.
+__device__ __forceinline__ uint4 expand8(uint32_t d, float sc, const float2* tab) {
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float2 lp = tab[(d >> (8 * i)) & 0xffu];
+    o[i] = pack_bf16x2(lp.x * sc, lp.y * sc);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Wave-level layout: in a 1 KB chunk of packed bytes, lane l handles packed
+// dwords l, 64+l, 128+l and 192+l, so every load instruction reads 256
+// contiguous bytes and every store instruction writes 1 KB contiguous.
+template <bool DQ>
 __global__ __launch_bounds__(kDThreads) void dequant_kernel(
     const uint8_t* __restrict__ packed, int64_t n, const void* __restrict__ absmax,
-    const float* __restrict__ absmax2, const float* __restrict__ mean, int dq,
+    const float* __restrict__ absmax2, const float* __restrict__ mean,
     uint16_t* __restrict__ out, LevelTable lv) {
-  __shared__ float2 tab[256];   // byte -> (L[high nibble], L[low nibble])
-  for (int e = threadIdx.x; e < 256; e += kDThreads)
-    tab[e] = make_float2(level_of(lv, (uint32_t)e >> 4), level_of(lv, (uint32_t)e & 15u));
-  __syncthreads();
-  const float mu = dq ? *mean : 0.0f;
+  __shared__ float2 tabs[kCopies][256];   // byte -> (L[high nibble], L[low nibble])
+  const int tid = threadIdx.x, lane = tid & 63;
   const int64_t nbytes = n >> 1;
-  const int64_t nchunks = (nbytes + 15) >> 4;
-  for (int64_t c = (int64_t)blockIdx.x * kDThreads + threadIdx.x; c < nchunks;
-       c += (int64_t)gridDim.x * kDThreads) {
-    const int64_t byte0 = c << 4;
-    const float sc = exact_block_scale((byte0 << 1) / kBlock, absmax, absmax2, mu, dq);
-    if (byte0 + 16 <= nbytes) {
-      const uint4 p = load_nt16(packed + byte0);
-      const uint32_t d[4] = {p.x, p.y, p.z, p.w};
-      uint32_t o[16];
+  const int64_t full = nbytes / kChunk;
+  const int64_t gw = (int64_t)blockIdx.x * kDWaves + (tid >> 6);
+  const int64_t nw = (int64_t)gridDim.x * kDWaves;
+
+  const int lvl = level_lanes(lv);
+  for (int e = tid; e < kCopies * 256; e += kDThreads) {
+    const uint32_t b = (uint32_t)e & 255u;
+    tabs[e >> 8][b] = make_float2(level_lookup(lvl, b >> 4), level_lookup(lvl, b & 15u));
+  }
+  __syncthreads();
+  const float2* tab = tabs[lane & (kCopies - 1)];
+  const float mu = DQ ? *mean : 0.0f;
+
+  for (int64_t c0 = gw; c0 < full; c0 += nw * kDUnroll) {
+    uint32_t d[kDUnroll][4];
+    float scl[kDUnroll];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+    for (int u = 0; u < kDUnroll; ++u) {
+      const int64_t c = c0 + u * nw < full ? c0 + u * nw : full - 1;   // clamped, uniform
+      const uint32_t* src = (const uint32_t*)(packed + c * kChunk);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float2 L = tab[(d[k] >> (8 * i)) & 0xffu];
-          o[4 * k + i] = pack_bf16x2(L.x * sc, L.y * sc);
+      for (int k = 0; k < 4; ++k) d[u][k] = __builtin_nontemporal_load(src + k * 64 + lane);
+    }
+#pragma unroll
+    for (int u = 0; u < kDUnroll; ++u) {
+      const int64_t c = c0 + u * nw < full ? c0 + u * nw : full - 1;
+      // lanes 0..31 each form one of the chunk's 32 block scales
+      scl[u] = exact_block_scale<DQ>(c * 32 + (lane & 31), absmax, absmax2, mu);
+    }
+#pragma unroll
+    for (int u = 0; u < kDUnroll; ++u) {
+      const int64_t c = c0 + u * nw;
+      if (c < full) {   // wave-uniform
+        uint4* dst = (uint4*)(out + c * (2 * kChunk));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          // dword k*64 + lane covers weights 8*(k*64+lane) .. +7: block 8k + lane/8
+          const float sc = __int_as_float(
+              __builtin_amdgcn_ds_bpermute((8 * k + (lane >> 3)) << 2, __float_as_int(scl[u])));
+          store_nt16(dst + k * 64 + lane, expand8(d[u][k], sc, tab));
         }
       }
-      uint4* dst = (uint4*)(out + (byte0 << 1));
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        uint4 v;
-        v.x = o[4 * k];
-        v.y = o[4 * k + 1];
-        v.z = o[4 * k + 2];
-        v.w = o[4 * k + 3];
-        store_nt16(dst + k, v);
-      }
-    } else {
-      for (int64_t b = byte0; b < nbytes; ++b) {
-        const float2 L = tab[packed[b]];
-        const uint32_t pr = pack_bf16x2(L.x * sc, L.y * sc);
-        out[2 * b] = (uint16_t)(pr & 0xffffu);
-        out[2 * b + 1] = (uint16_t)(pr >> 16);
-      }
+    }
+  }
+
+  // ragged tail (fewer than 1 KB of packed bytes) on the last wave, bytewise
+  if (full * kChunk < nbytes && gw == nw - 1) {
+    for (int64_t b = full * kChunk + lane; b < nbytes; b += 64) {
+      const float sc = exact_block_scale<DQ>((b << 1) / kBlock, absmax, absmax2, mu);
+      const float2 lp = tab[packed[b]];
+      const uint32_t pr = pack_bf16x2(lp.x * sc, lp.y * sc);
+      out[2 * b] = (uint16_t)(pr & 0xffffu);
+      out[2 * b + 1] = (uint16_t)(pr >> 16);
     }
   }
 }
@@ -83,12 +112,16 @@ __global__ __launch_bounds__(kDThreads) void dequant_kernel(
 hipError_t launch_dequantize(const uint8_t* packed, int64_t n, const void* absmax,
                              const float* absmax2, const float* mean, int double_quant,
                              uint16_t* out, hipStream_t stream) {
-  const int64_t nchunks = ((n >> 1) + 15) >> 4;
-  int64_t grid = (nchunks + kDThreads - 1) / kDThreads;
-  if (grid > 4096) grid = 4096;
+  const int64_t chunks = (n >> 1) / kChunk;
+  int64_t grid = (chunks + kDWaves * kDUnroll - 1) / (kDWaves * kDUnroll);
+  if (grid > 2048) grid = 2048;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)grid), dim3(kDThreads), 0, stream, packed, n,
-                     absmax, absmax2, mean, double_quant, out, level_table());
+  if (double_quant)
+    hipLaunchKernelGGL(dequant_kernel<true>, dim3((unsigned)grid), dim3(kDThreads), 0, stream,
+                       packed, n, absmax, absmax2, mean, out, level_table());
+  else
+    hipLaunchKernelGGL(dequant_kernel<false>, dim3((unsigned)grid), dim3(kDThreads), 0, stream,
+                       packed, n, absmax, absmax2, mean, out, level_table());
   return hipGetLastError();
 }
 

@@ -51,6 +51,32 @@ __device__ __forceinline__ void store_nt16(void* p, uint4 v) {
   __builtin_nontemporal_store(t, (u32x4_t*)p);
 }
 
+// The 16 levels held in lanes 0..15 of one VGPR, built from the
+// kernel-argument block with scalar loads and v_writelane only; a lookup is
+// one ds_bpermute.  Table builds therefore touch no vector memory and never
+// wait behind weight loads already in flight.
+template <int I>
+__device__ __forceinline__ void write_lane(int& v, int s) {
+  asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(s), "n"(I));
+}
+template <typename LevelTableT>
+__device__ __forceinline__ int level_lanes(const LevelTableT& lv) {
+  int v = 0;
+  int s[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s[i] = __builtin_amdgcn_readfirstlane(__float_as_int(lv.level[i]));
+  write_lane<0>(v, s[0]);   write_lane<1>(v, s[1]);   write_lane<2>(v, s[2]);
+  write_lane<3>(v, s[3]);   write_lane<4>(v, s[4]);   write_lane<5>(v, s[5]);
+  write_lane<6>(v, s[6]);   write_lane<7>(v, s[7]);   write_lane<8>(v, s[8]);
+  write_lane<9>(v, s[9]);   write_lane<10>(v, s[10]); write_lane<11>(v, s[11]);
+  write_lane<12>(v, s[12]); write_lane<13>(v, s[13]); write_lane<14>(v, s[14]);
+  write_lane<15>(v, s[15]);
+  return v;
+}
+__device__ __forceinline__ float level_lookup(int lanes, uint32_t c) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute((int)(c << 2), lanes));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);

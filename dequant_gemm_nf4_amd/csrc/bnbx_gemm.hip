@@ -17,13 +17,6 @@ constexpr int BM = 128, BN = 128, BK = 64;
 constexpr int LDS_ROW = BK + 8;   // bf16 per LDS row (8 of padding against bank conflicts)
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ float level_of(const LevelTable& lv, uint32_t c) {
-  float v = lv.level[0];
-#pragma unroll
-  for (uint32_t i = 1; i < 16; ++i) v = (c == i) ? lv.level[i] : v;
-  return v;
-}
-
 __device__ __forceinline__ float gemm_block_scale(int64_t blk, const void* absmax,
                                                   const float* absmax2, float mu, int dq) {
   if (!dq) return ((const float*)absmax)[blk];
@@ -45,8 +38,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t m0 = (int64_t)blockIdx.y * BM;
   const int64_t n0 = (int64_t)blockIdx.x * BN;
+  const int lvl = level_lanes(lv);
   for (int e = tid; e < 256; e += kThreads)
-    tab[e] = make_float2(level_of(lv, (uint32_t)e >> 4), level_of(lv, (uint32_t)e & 15u));
+    tab[e] = make_float2(level_lookup(lvl, (uint32_t)e >> 4), level_lookup(lvl, (uint32_t)e & 15u));
   const float mu = dq ? *mean : 0.0f;
   const int64_t rowK2 = (int64_t)(K >> 1);
   const int64_t nkb = K >> 6;
@@ -91,8 +85,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
       for (int k = 0; k < 4; ++k)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float2 L = tab[(d[k] >> (8 * i)) & 0xffu];
-          o[4 * k + i] = pack_bf16x2(L.x * sc, L.y * sc);
+          const float2 lp = tab[(d[k] >> (8 * i)) & 0xffu];
+          o[4 * k + i] = pack_bf16x2(lp.x * sc, lp.y * sc);
         }
       uint4* dst = (uint4*)(Bs + brow * LDS_ROW + bhalf * 32);
 #pragma unroll

@@ -24,32 +24,16 @@
 namespace bnbx {
 namespace {
 
-constexpr int kMaxThreads = 1024;
+constexpr int kMaxThreads = 512;
 constexpr int kGMax = 8;
 constexpr int kTabDwords = 256 * 64;   // 64 KB
 
-__device__ __forceinline__ float level_of(const LevelTable& lv, uint32_t c) {
-  float v = lv.level[0];
-#pragma unroll
-  for (uint32_t i = 1; i < 16; ++i) v = (c == i) ? lv.level[i] : v;
-  return v;
-}
-
-// Approximate block scale for the contraction (not bit-exact with the stored
-// format's dequant; the matmul tolerance covers the last-ulp difference).
-__device__ __forceinline__ float gemv_block_scale(int64_t blk, const void* absmax,
-                                                  const float* absmax2, float mu, int dq) {
-  if (!dq) return ((const float*)absmax)[blk];
-  const float q = (float)((const int8_t*)absmax)[blk];
-  return __builtin_fmaf(q, absmax2[blk / kGroup] * (1.0f / 127.0f), mu);
-}
-
-template <int MM, int P>
+template <int MM, int P, bool DQ, int G>
 __global__ __launch_bounds__(kMaxThreads) void gemv_valu_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ packed,
     const void* __restrict__ absmax, const float* __restrict__ absmax2,
-    const float* __restrict__ mean, int dq, int N, int K, uint16_t* __restrict__ y, int64_t ldy,
-    int S, int R, int G, LevelTable lv) {
+    const float* __restrict__ mean, int N, int K, uint16_t* __restrict__ y, int64_t ldy, int S,
+    int R, LevelTable lv) {
   __shared__ __attribute__((aligned(16))) uint32_t tab[kTabDwords];
   __shared__ float red[kGMax * MM * (kMaxThreads / 64)];
 
@@ -58,69 +42,91 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_valu_kernel(
   const int team = t / S, s = t - team * S;
   const int C = K >> 5;
   const int64_t rowK2 = (int64_t)(K >> 1);
+  const int64_t nkb = K >> 6;
   const int64_t row0 = (int64_t)blockIdx.x * R * G + team;
-  const float mu = dq ? *mean : 0.0f;
+  static_assert(G * P <= kGMax, "at most 8 chunks per thread");
+  constexpr int GM = G;
+  const int lvl = level_lanes(lv);
 
-  // 1. weight loads and block scales (all in flight before anything else)
-  uint4 wv[kGMax][P];
-  float sc[kGMax][P];
-#pragma unroll
-  for (int g = 0; g < kGMax; ++g) {
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
-      const int64_t row = row0 + (int64_t)g * R;
-      const int c = s + j * S;
-      const bool ok = g < G && row < N && c < C;
-      wv[g][j] = ok ? load_nt16(packed + row * rowK2 + (int64_t)c * 16)
-                    : make_uint4(0, 0, 0, 0);
-      sc[g][j] = ok ? gemv_block_scale(row * (K >> 6) + (c >> 1), absmax, absmax2, mu, dq) : 0.0f;
-    }
-  }
-  // 2. this thread's X slice: 32 bf16 (16 pairs) per chunk per row of X
+  // 1. this thread's X slice first (small, cache-resident): 32 bf16 (16
+  //    pairs) per chunk per row of X
   uint32_t xr[MM][P][16];
 #pragma unroll
   for (int m = 0; m < MM; ++m) {
 #pragma unroll
     for (int j = 0; j < P; ++j) {
       const int c = s + j * S;
-      if (c < C) {
-        const uint4* src = (const uint4*)(x + (int64_t)m * ldx + (int64_t)c * 32);
+      const int cc = c < C ? c : C - 1;
+      const uint4* src = (const uint4*)(x + (int64_t)m * ldx + (int64_t)cc * 32);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint4 v = src[q];
-          xr[m][j][4 * q] = v.x;
-          xr[m][j][4 * q + 1] = v.y;
-          xr[m][j][4 * q + 2] = v.z;
-          xr[m][j][4 * q + 3] = v.w;
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 16; ++q) xr[m][j][q] = 0u;
+      for (int q = 0; q < 4; ++q) {
+        const uint4 v = src[q];
+        xr[m][j][4 * q] = v.x;
+        xr[m][j][4 * q + 1] = v.y;
+        xr[m][j][4 * q + 2] = v.z;
+        xr[m][j][4 * q + 3] = v.w;
       }
     }
   }
+  // 2. then every weight load, each followed by its raw block-scale loads,
+  //    all in flight before anything waits (addresses clamped instead of
+  //    branched; out-of-range rows/chunks are zeroed through their scale).
+  //    Scales are converted only after the barrier, so using row g waits
+  //    only for the loads issued up to row g.
+  uint4 wv[GM][P];
+  int qraw[GM][P];
+  float sraw[GM][P], graw[GM][P];
+#pragma unroll
+  for (int g = 0; g < GM; ++g) {
+    {
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        const int64_t row = row0 + (int64_t)g * R;
+        const int c = s + j * S;
+        const int64_t rc = row < N ? row : N - 1;
+        const int cc = c < C ? c : C - 1;
+        wv[g][j] = load_nt16(packed + rc * rowK2 + (int64_t)cc * 16);
+        const int64_t blk = rc * nkb + (cc >> 1);
+        if (DQ) {
+          qraw[g][j] = ((const int8_t*)absmax)[blk];
+          graw[g][j] = absmax2[blk >> 8];
+          sraw[g][j] = 0.0f;
+        } else {
+          qraw[g][j] = 0;
+          sraw[g][j] = ((const float*)absmax)[blk];
+          graw[g][j] = 0.0f;
+        }
+      }
+    }
+  }
+  const float mu = DQ ? *mean : 0.0f;
   // 3. replicated byte -> bf16-pair table
   for (int e = t; e < kTabDwords / 4; e += T) {
     const uint32_t b = (uint32_t)e >> 4;
-    const uint32_t v = pack_bf16x2(level_of(lv, b >> 4), level_of(lv, b & 15u));
+    const uint32_t v = pack_bf16x2(level_lookup(lvl, b >> 4), level_lookup(lvl, b & 15u));
     ((uint4*)tab)[e] = make_uint4(v, v, v, v);
   }
   __syncthreads();
 
-  // 4. dequant-in-register dot products
+  // 4. dequant-in-register dot products, one block scale per 32 weights
   const uint32_t lanebyte = (uint32_t)(t & 63) << 2;
   const unsigned char* tabb = (const unsigned char*)tab;
-  float acc[kGMax][MM];
+  float acc[GM][MM];
 #pragma unroll
-  for (int g = 0; g < kGMax; ++g) {
+  for (int g = 0; g < GM; ++g) {
 #pragma unroll
     for (int m = 0; m < MM; ++m) acc[g][m] = 0.0f;
   }
 #pragma unroll
-  for (int g = 0; g < kGMax; ++g) {
-    if (g < G) {
+  for (int g = 0; g < GM; ++g) {
+    {
 #pragma unroll
       for (int j = 0; j < P; ++j) {
+        const int64_t row = row0 + (int64_t)g * R;
+        const bool ok = row < N && s + j * S < C;
+        float sc = DQ ? __builtin_fmaf((float)qraw[g][j], graw[g][j] * (1.0f / 127.0f), mu)
+                      : sraw[g][j];
+        sc = ok ? sc : 0.0f;
         const uint32_t d[4] = {wv[g][j].x, wv[g][j].y, wv[g][j].z, wv[g][j].w};
         float part[MM];
 #pragma unroll
@@ -136,7 +142,7 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_valu_kernel(
           }
         }
 #pragma unroll
-        for (int m = 0; m < MM; ++m) acc[g][m] = __builtin_fmaf(part[m], sc[g][j], acc[g][m]);
+        for (int m = 0; m < MM; ++m) acc[g][m] = __builtin_fmaf(part[m], sc, acc[g][m]);
       }
     }
   }
@@ -144,8 +150,8 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_valu_kernel(
   // 5. reduce each row over its team: waves first, then across the team's waves
   const int nw = T >> 6, wave = t >> 6, wpt = S >> 6;
 #pragma unroll
-  for (int g = 0; g < kGMax; ++g) {
-    if (g < G) {
+  for (int g = 0; g < GM; ++g) {
+    {
 #pragma unroll
       for (int m = 0; m < MM; ++m) {
         const float v = wave_sum(acc[g][m]);
@@ -168,6 +174,26 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_valu_kernel(
   }
 }
 
+template <int MM, int P, int G>
+hipError_t launch_valu_g(const uint16_t* x, int64_t ldx, const uint8_t* packed,
+                         const void* absmax, const float* absmax2, const float* mean, int dq,
+                         int N, int K, uint16_t* y, int64_t ldy, int S, int R,
+                         hipStream_t stream) {
+  const int64_t grid = ((int64_t)N + R * G - 1) / (R * G);
+  if (dq)
+    hipLaunchKernelGGL((gemv_valu_kernel<MM, P, true, G>), dim3((unsigned)grid), dim3(S * R), 0,
+                       stream, x, ldx, packed, absmax, absmax2, mean, N, K, y, ldy, S, R,
+                       level_table());
+  else
+    hipLaunchKernelGGL((gemv_valu_kernel<MM, P, false, G>), dim3((unsigned)grid), dim3(S * R), 0,
+                       stream, x, ldx, packed, absmax, absmax2, mean, N, K, y, ldy, S, R,
+                       level_table());
+  return hipGetLastError();
+}
+
+// Team size S covers a row's chunks (P per thread); R teams per workgroup;
+// G rows per team, picked so that about 512 workgroups (two per CU, the LDS
+// limit) cover N.
 template <int MM, int P>
 hipError_t launch_valu(const uint16_t* x, int64_t ldx, const uint8_t* packed, const void* absmax,
                        const float* absmax2, const float* mean, int dq, int N, int K,
@@ -175,15 +201,22 @@ hipError_t launch_valu(const uint16_t* x, int64_t ldx, const uint8_t* packed, co
   const int C = K >> 5;
   const int S = ((C + P - 1) / P + 63) / 64 * 64;
   const int R = kMaxThreads / S >= 1 ? kMaxThreads / S : 1;
-  const int T = S * R;
-  int64_t G = ((int64_t)N + (int64_t)R * 512 - 1) / ((int64_t)R * 512);
-  if (G < 1) G = 1;
-  if (G > kGMax) G = kGMax;
-  const int64_t grid = ((int64_t)N + R * G - 1) / (R * G);
-  hipLaunchKernelGGL((gemv_valu_kernel<MM, P>), dim3((unsigned)grid), dim3(T), 0, stream, x, ldx,
-                     packed, absmax, absmax2, mean, dq, N, K, y, ldy, S, R, (int)G,
-                     level_table());
-  return hipGetLastError();
+  const int64_t need = ((int64_t)N + (int64_t)R * 512 - 1) / ((int64_t)R * 512);
+  const int gmax = kGMax / P;
+  const int G = need <= 4 ? (int)(need < 1 ? 1 : need) : need <= 6 ? 6 : 8;
+  const int Gc = G < gmax ? G : gmax;
+#define BNBX_GEMV_G(GV)                                                                     \
+  if (Gc == GV)                                                                             \
+    return launch_valu_g<MM, P, (GV * P <= kGMax ? GV : 1)>(x, ldx, packed, absmax, absmax2, \
+                                                           mean, dq, N, K, y, ldy, S, R, stream);
+  BNBX_GEMV_G(1)
+  BNBX_GEMV_G(2)
+  BNBX_GEMV_G(3)
+  BNBX_GEMV_G(4)
+  BNBX_GEMV_G(6)
+  BNBX_GEMV_G(8)
+#undef BNBX_GEMV_G
+  return hipErrorNotSupported;
 }
 
 template <int P>
@@ -204,7 +237,7 @@ hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* packed, co
                        const float* absmax2, const float* mean, int double_quant, int M, int N,
                        int K, uint16_t* y, int64_t ldy, hipStream_t stream) {
   const int C = K >> 5;
-  const int P = C <= kMaxThreads ? 1 : (C <= 2 * kMaxThreads ? 2 : 0);
+  const int P = C <= kMaxThreads ? 1 : C <= 2 * kMaxThreads ? 2 : C <= 4 * kMaxThreads ? 4 : 0;
   if (P == 0) return hipErrorNotSupported;
   // Rows of X in groups of at most 4 (each group streams W once); with two
   // chunks per thread one row at a time keeps the X slice in registers.
@@ -214,7 +247,9 @@ hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* packed, co
     const hipError_t e =
         P == 1 ? launch_valu_m<1>(mm, x + (int64_t)m0 * ldx, ldx, packed, absmax, absmax2, mean,
                                   double_quant, N, K, y + (int64_t)m0 * ldy, ldy, stream)
-               : launch_valu<1, 2>(x + (int64_t)m0 * ldx, ldx, packed, absmax, absmax2, mean,
+      : P == 2 ? launch_valu<1, 2>(x + (int64_t)m0 * ldx, ldx, packed, absmax, absmax2, mean,
+                                   double_quant, N, K, y + (int64_t)m0 * ldy, ldy, stream)
+               : launch_valu<1, 4>(x + (int64_t)m0 * ldx, ldx, packed, absmax, absmax2, mean,
                                    double_quant, N, K, y + (int64_t)m0 * ldy, ldy, stream);
     if (e != hipSuccess) return e;
   }

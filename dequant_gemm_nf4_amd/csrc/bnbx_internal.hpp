@@ -33,10 +33,13 @@ const float* thresholds_f32();      // float[15]
 const EncodeTable& encode_table();
 const LevelTable& level_table();
 
-// Workspace layout of the double-quant quantize: an exact exponent histogram
-// of the block absmax values, then the fp32 absmax of every block.
+// Workspace layout of the double-quant quantize: kHistCopies exact exponent
+// histograms of the block absmax values (workgroup w adds into copy
+// w % kHistCopies, so no address sees more than a few dozen global atomics),
+// then the fp32 absmax of every block.
 constexpr size_t kHistBins = 256;
-constexpr size_t kHistBytes = kHistBins * sizeof(unsigned long long);
+constexpr size_t kHistCopies = 16;
+constexpr size_t kHistBytes = kHistCopies * kHistBins * sizeof(unsigned long long);
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline size_t dq_workspace_bytes(int64_t nb) {
   return kHistBytes + round_up((size_t)nb * sizeof(float), 256);

@@ -22,10 +22,10 @@
 namespace bnbx {
 namespace {
 
-constexpr int kQThreads = 256;
+constexpr int kQThreads = 1024;
 constexpr int kQWaves = kQThreads / 64;
 constexpr int kTabStride = 256;   // LDS bytes per bucket: 32 copies of an 8-byte entry
-constexpr int kUnroll = 2;        // 512-weight tiles in flight per wave
+constexpr int kUnroll = 4;        // 512-weight tiles per wave per round
 constexpr int kTile = 512;        // weights per wave per tile (8 blocks)
 
 __device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v, int ctrl_id) {
@@ -48,114 +48,137 @@ __device__ __forceinline__ uint32_t encode_one(float x, const unsigned char* tab
   return e.y + (x >= __uint_as_float(e.x) ? 1u : 0u);
 }
 
-__global__ __launch_bounds__(kQThreads) void quantize_kernel(
+// One lane's 8 consecutive weights (4 bf16 pairs) -> one packed word; also
+// returns the block absmax (bf16 bits in m, value in amax).  All 64 lanes of
+// the wave must execute this together (DPP reduction over 8-lane groups).
+__device__ __forceinline__ uint32_t encode8(const uint32_t d[4], const unsigned char* tab,
+                                            uint32_t lanebase, uint32_t& m_out, float& amax_out) {
+  // |w| as bf16 bits: for non-negative floats integer order is value order.
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t a = d[k] & 0x7fff7fffu;
+    m = max(m, max(a & 0xffffu, a >> 16));
+  }
+  m = dpp_max_u32(m, 0);
+  m = dpp_max_u32(m, 1);
+  m = dpp_max_u32(m, 2);   // now the max over this lane's 8-lane block
+  const float amax = __uint_as_float(m << 16);
+  const float r = (amax == 0.0f) ? 0.0f : 1.0f / amax;
+  uint32_t word = 0;
+  if (__builtin_expect(r <= FLT_MAX, 1)) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float x0 = bf16lo_to_f32(d[k]) * r;   // even element -> high nibble
+      const float x1 = bf16hi_to_f32(d[k]) * r;
+      const uint32_t c0 = encode_one(x0, tab, lanebase);
+      const uint32_t c1 = encode_one(x1, tab, lanebase);
+      word |= ((c0 << 4) | c1) << (8 * k);
+    }
+  } else {
+    // Reciprocal overflowed (absmax below 2^-128): x is +inf, -inf or NaN,
+    // whose codes are 15, 0 and 0 (count of thresholds <= x).
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float x0 = bf16lo_to_f32(d[k]) * r;
+      const float x1 = bf16hi_to_f32(d[k]) * r;
+      const uint32_t c0 = x0 > 1.0f ? 15u : 0u, c1 = x1 > 1.0f ? 15u : 0u;
+      word |= ((c0 << 4) | c1) << (8 * k);
+    }
+  }
+  m_out = m;
+  amax_out = amax;
+  return word;
+}
+
+__device__ __forceinline__ void record_block(int lane, int64_t e, uint32_t m, float amax,
+                                             float* absmax, uint32_t* lhist, bool dq) {
+  if ((lane & 7) == 0) {
+    absmax[e / kBlock] = amax;
+    if (dq && m != 0) {
+      const uint32_t ex = m >> 7;   // binary exponent field
+      atomicAdd(&lhist[ex], (m & 0x7fu) | (ex ? 0x80u : 0u));
+    }
+  }
+}
+
+template <bool DQ>
+__global__ __launch_bounds__(kQThreads, 2) void quantize_kernel(
     const uint16_t* __restrict__ w, uint8_t* __restrict__ packed, float* __restrict__ absmax,
     unsigned long long* __restrict__ hist, int64_t n, EncodeTable et) {
   __shared__ __attribute__((aligned(16))) unsigned char tab[kBuckets * kTabStride];
   __shared__ uint32_t lhist[kHistBins];
 
   const int tid = threadIdx.x;
-  for (int e = tid; e < kBuckets * 32; e += kQThreads) {
-    const int b = e >> 5, c = e & 31;
-    uint2 v;
-    v.x = __float_as_uint(et.thr[b]);
-    v.y = et.base[b];
-    *(uint2*)(tab + b * kTabStride + c * 8) = v;
-  }
-  for (int e = tid; e < (int)kHistBins; e += kQThreads) lhist[e] = 0;
-  __syncthreads();
-
   const int lane = tid & 63;
-  const uint32_t lanebase = (uint32_t)(lane & 31) << 3;
-  const int64_t ntiles = (n + kTile - 1) / kTile;
+  const int64_t full = n / kTile;                       // whole 512-weight tiles
   const int64_t gw = (int64_t)blockIdx.x * kQWaves + (tid >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * kQWaves;
 
-  for (int64_t t0 = gw * kUnroll; t0 < ntiles; t0 += nwaves * kUnroll) {
+  // Replicated bucket table in LDS (entry (b, copy) at b*256 + copy*8).
+  for (int e = tid; e < kBuckets * 32; e += kQThreads) {
+    uint2 t;
+    t.x = __float_as_uint(et.thr[e >> 5]);
+    t.y = et.base[e >> 5];
+    *(uint2*)(tab + (e >> 5) * kTabStride + (e & 31) * 8) = t;
+  }
+  if (DQ)
+    for (int e = tid; e < (int)kHistBins; e += kQThreads) lhist[e] = 0;
+  __syncthreads();
+  const uint32_t lanebase = (uint32_t)(lane & 31) << 3;
+
+  // Each round a wave loads kUnroll whole tiles (addresses clamped, so no
+  // per-lane branches), then encodes them; only the stores are skipped for
+  // tiles past the end.  Latency is hidden by the many resident waves.
+  for (int64_t t0 = gw * kUnroll; t0 < full; t0 += nwaves * kUnroll) {
     uint4 v[kUnroll];
-    int64_t e0[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      e0[u] = (t0 + u) * kTile + lane * 8;
-      if (e0[u] + 8 <= n) {
-        v[u] = load_nt16(w + e0[u]);
-      } else {
-        uint16_t h[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) h[k] = (e0[u] + k < n) ? w[e0[u] + k] : (uint16_t)0;
-        v[u].x = h[0] | ((uint32_t)h[1] << 16);
-        v[u].y = h[2] | ((uint32_t)h[3] << 16);
-        v[u].z = h[4] | ((uint32_t)h[5] << 16);
-        v[u].w = h[6] | ((uint32_t)h[7] << 16);
-      }
+      const int64_t tile = t0 + u < full ? t0 + u : full - 1;
+      v[u] = load_nt16(w + tile * kTile + lane * 8);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const uint32_t d[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-      // |w| as bf16 bits: for non-negative floats integer order is value order.
-      uint32_t m = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t a = d[k] & 0x7fff7fffu;
-        const uint32_t lo = a & 0xffffu, hi = a >> 16;
-        m = max(m, max(lo, hi));
-      }
-      m = dpp_max_u32(m, 0);
-      m = dpp_max_u32(m, 1);
-      m = dpp_max_u32(m, 2);   // now the max over this lane's 8-lane block
-      const float amax = __uint_as_float(m << 16);
-      const float r = (amax == 0.0f) ? 0.0f : 1.0f / amax;
-
-      uint32_t word = 0;
-      if (__builtin_expect(r <= FLT_MAX, 1)) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float x0 = bf16lo_to_f32(d[k]) * r;   // even element -> high nibble
-          const float x1 = bf16hi_to_f32(d[k]) * r;
-          const uint32_t c0 = encode_one(x0, tab, lanebase);
-          const uint32_t c1 = encode_one(x1, tab, lanebase);
-          word |= ((c0 << 4) | c1) << (8 * k);
-        }
-      } else {
-        // Reciprocal overflowed (absmax below 2^-128): x is +inf, -inf or NaN,
-        // whose codes are 15, 0 and 0 (count of thresholds <= x).
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float x0 = bf16lo_to_f32(d[k]) * r;
-          const float x1 = bf16hi_to_f32(d[k]) * r;
-          const uint32_t c0 = x0 > 1.0f ? 15u : 0u, c1 = x1 > 1.0f ? 15u : 0u;
-          word |= ((c0 << 4) | c1) << (8 * k);
-        }
-      }
-
-      const int64_t e = e0[u];
-      if (e + 8 <= n) {
+      uint32_t m;
+      float amax;
+      const uint32_t word = encode8(d, tab, lanebase, m, amax);
+      if (t0 + u < full) {   // wave-uniform
+        const int64_t e = (t0 + u) * kTile + lane * 8;
         *(uint32_t*)(packed + (e >> 1)) = word;
-      } else if (e < n) {
-        const int nbytes = (int)((n - e) >> 1);
-        for (int k = 0; k < nbytes; ++k) packed[(e >> 1) + k] = (uint8_t)(word >> (8 * k));
-      }
-      if ((lane & 7) == 0 && e < n) {
-        const int64_t blk = e / kBlock;
-        absmax[blk] = amax;
-        if (hist != nullptr && m != 0) {
-          const uint32_t ex = m >> 7;          // binary exponent field
-          const uint32_t sig = (m & 0x7fu) | (ex ? 0x80u : 0u);
-          atomicAdd(&lhist[ex], sig);
-        }
+        record_block(lane, e, m, amax, absmax, lhist, DQ);
       }
     }
   }
 
-  if (hist != nullptr) {
+  // The ragged last tile (fewer than 512 weights) goes to the last wave.
+  if (n % kTile != 0 && gw == nwaves - 1) {
+    const int64_t e = full * kTile + lane * 8;
+    uint16_t h[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) h[k] = (e + k < n) ? w[e + k] : (uint16_t)0;
+    const uint32_t d[4] = {h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
+                           h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16)};
+    uint32_t m;
+    float amax;
+    const uint32_t word = encode8(d, tab, lanebase, m, amax);
+    if (e < n) {
+      const int nbytes = (int)((n - e) < 8 ? (n - e) >> 1 : 4);
+      for (int k = 0; k < nbytes; ++k) packed[(e >> 1) + k] = (uint8_t)(word >> (8 * k));
+      record_block(lane, e, m, amax, absmax, lhist, DQ);
+    }
+  }
+
+  if (DQ) {
     __syncthreads();
+    unsigned long long* h = hist + (blockIdx.x % kHistCopies) * kHistBins;
     for (int e = tid; e < (int)kHistBins; e += kQThreads)
-      if (lhist[e]) atomicAdd(&hist[e], (unsigned long long)lhist[e]);
+      if (lhist[e]) atomicAdd(&h[e], (unsigned long long)lhist[e]);
   }
 }
 
 __global__ void zero_hist_kernel(unsigned long long* __restrict__ hist) {
-  hist[threadIdx.x] = 0ull;
+  hist[blockIdx.x * blockDim.x + threadIdx.x] = 0ull;
 }
 
 // Exact mean of the block absmax values.  absmax = sig * 2^(max(e,1) - 134)
@@ -169,7 +192,9 @@ __device__ float exact_mean(const unsigned long long* __restrict__ hist, int64_t
   if (tid < 10) digits[tid] = 0ull;
   __syncthreads();
   for (int e = tid; e < (int)kHistBins; e += blockDim.x) {
-    const unsigned long long h = hist[e];
+    unsigned long long h = 0;
+#pragma unroll
+    for (int c = 0; c < (int)kHistCopies; ++c) h += hist[c * kHistBins + e];
     if (h) {
       const int sh = (e > 1 ? e : 1) - 1;
       const int k = sh >> 5, bit = sh & 31;
@@ -255,14 +280,19 @@ int grid_for(int64_t work_items, int per_block, int cap) {
 hipError_t launch_quantize(const uint16_t* w, uint8_t* packed, int64_t n, float* absmax_f32,
                            unsigned long long* hist, hipStream_t stream) {
   const int64_t ntiles = (n + kTile - 1) / kTile;
-  const int grid = grid_for(ntiles, kQWaves * kUnroll, 4096);
-  hipLaunchKernelGGL(quantize_kernel, dim3(grid), dim3(kQThreads), 0, stream, w, packed,
-                     absmax_f32, hist, n, encode_table());
+  const int grid = grid_for(ntiles, kQWaves * kUnroll, 512);
+  if (hist != nullptr)
+    hipLaunchKernelGGL(quantize_kernel<true>, dim3(grid), dim3(kQThreads), 0, stream, w, packed,
+                       absmax_f32, hist, n, encode_table());
+  else
+    hipLaunchKernelGGL(quantize_kernel<false>, dim3(grid), dim3(kQThreads), 0, stream, w, packed,
+                       absmax_f32, hist, n, encode_table());
   return hipGetLastError();
 }
 
 hipError_t launch_zero_hist(unsigned long long* hist, hipStream_t stream) {
-  hipLaunchKernelGGL(zero_hist_kernel, dim3(1), dim3((unsigned)kHistBins), 0, stream, hist);
+  hipLaunchKernelGGL(zero_hist_kernel, dim3((unsigned)kHistCopies), dim3((unsigned)kHistBins), 0,
+                     stream, hist);
   return hipGetLastError();
 }
 
@@ -270,7 +300,7 @@ hipError_t launch_double_quant(const float* absmax_f32, const unsigned long long
                                int64_t nb, int8_t* q, float* absmax2, float* mean,
                                hipStream_t stream) {
   const int64_t ng = (nb + kGroup - 1) / kGroup;
-  const int grid = grid_for(ng, 1, 1024);
+  const int grid = grid_for(ng, 4, 512);
   hipLaunchKernelGGL(double_quant_kernel, dim3(grid), dim3(256), 0, stream, absmax_f32, hist, nb,
                      q, absmax2, mean);
   return hipGetLastError();

@@ -71,17 +71,28 @@ def test_quantize_exhaustive_bf16_weights():
 
 def test_quantize_special_blocks():
     """Zero blocks, a subnormal absmax (the fp32 reciprocal overflows), the
-    largest finite values, and weights that land exactly on representable
-    midpoints between levels (ties go to the lower code)."""
-    L = oracle.codebook().astype(np.float64)
-    mids = [(L[i] + L[i + 1]) / 2 for i in range(15)]
-    mids = [m for m in mids if float(np.float32(m)) == m]
+    largest finite values, negative zeros, and a block with absmax 1 holding
+    the bf16 neighbours on both sides of every decision threshold.
+
+    No bf16 weight and bf16 absmax put x exactly on a level midpoint (searched
+    over every absmax in [1e-3, 1e3] for the midpoints that are binary32
+    values), so the tie rule is reachable only from binary32 inputs and is
+    pinned on the oracle (tests/test_oracle.py)."""
+    T = oracle.thresholds(oracle.codebook())
     blocks = []
     blocks.append(np.zeros(64, np.float32))                                  # all zero
-    b = np.zeros(64, np.float32)
-    b[0] = 1.0
-    b[1:1 + len(mids)] = mids                                                # exact ties
-    blocks.append(b)
+    near = np.zeros(64, np.float32)
+    near[0] = 1.0
+    tb = oracle.f32_to_bf16_bits(T)
+    tf = oracle.bf16_bits_to_f32(tb)
+    below = np.where(tf < T, tb, tb - np.where(T > 0, 1, -1).astype(np.int64)).astype(np.uint16)
+    above = np.where(tf >= T, tb, tb + np.where(T > 0, 1, -1).astype(np.int64)).astype(np.uint16)
+    nb_ = oracle.bf16_bits_to_f32(below)
+    na_ = oracle.bf16_bits_to_f32(above)
+    assert np.all(nb_ < T) and np.all(na_ >= T)
+    near[1:16] = nb_
+    near[16:31] = na_
+    blocks.append(near)
     blocks.append(np.linspace(-3.0e38, 3.0e38, 64).astype(np.float32))      # huge
     tiny = np.zeros(64, np.float32)
     tiny[::3] = np.float32(2.0 ** -131)                                       # subnormal bf16
@@ -90,11 +101,11 @@ def test_quantize_special_blocks():
     blocks.append(np.full(64, -0.0, np.float32))                             # negative zeros
     f = np.concatenate(blocks)
     bits = oracle.f32_to_bf16_bits(f)
-    assert np.array_equal(oracle.bf16_bits_to_f32(bits)[64 + 1:64 + 1 + len(mids)],
-                          np.array(mids, np.float32))
     for dq in (False, True):
         got, ref = check_quantize(bits, bits.shape, dq)
         assert np.all(ref["codes"][:64] == 7)
+        assert np.array_equal(ref["codes"][64 + 1:64 + 16], np.arange(15))
+        assert np.array_equal(ref["codes"][64 + 16:64 + 31], np.arange(1, 16))
 
 
 def test_quantize_workspace_reuse_gives_same_result():
