@@ -55,6 +55,21 @@ def dequant_bytes(N, K):
     return n // 2 + nb + 4 * ng + 4 + 2 * n
 
 
+def recorded_gemv_traffic():
+    """Per-launch HBM bytes of the GEMV from the committed counter runs
+    (profiles/gemv_traffic.txt), or None if the kernel source changed since."""
+    import hashlib
+    try:
+        rec = dict(line.split(None, 1) for line in open(os.path.join(ROOT, "profiles", "gemv_traffic.txt"))
+                   if line.strip() and not line.startswith("#"))
+        src = open(os.path.join(ROOT, "dequant_gemm_nf4_amd", "csrc", "bnbx_gemv.hip"), "rb").read()
+        if hashlib.sha256(src).hexdigest() != rec["source_sha256"].strip():
+            return None
+        return int(rec["bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(budget_s: float = 12.0):
     """The oracle as it stands, on one decode layer (4096x4096, double quant):
     fp64 reference GEMV = dequantize + binary64 matmul, repeated until the
@@ -96,6 +111,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-calibration", action="store_true",
+                    help="run a 256 MiB plain copy first (counter scaling reference)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
@@ -146,8 +163,11 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     nlaunch = L * len(DECODE_SHAPES)
 
-    # Each stage of a step is captured once into a HIP graph (replayed every
-    # step) so host-side launch overhead does not enter the kernel timings.
+    # Every stage is captured once into a HIP graph and replayed each step, so
+    # host launch overhead stays out of the timings; the decode GEMVs get one
+    # graph per shape (L launches each) bracketed by events, so the average
+    # launch time of each shape is the graph time over L (kernel time plus
+    # the GPU's back-to-back dispatch gap).
     def stage_quantize():
         for i, w in enumerate(weights):
             T.quantize(w, True, out=qs[i], workspace=ws)
@@ -156,15 +176,17 @@ def main():
         for q in qs:
             T.dequantize(q, out=deq[: q.n].view(q.shape))
 
-    def stage_gemv():
-        for i, q in enumerate(qs):
-            s = i % len(DECODE_SHAPES)
-            T.gemv(xs[s], q, out=ys[s])
+    def stage_gemv(s):
+        def run():
+            for i in range(s, nlaunch, len(DECODE_SHAPES)):
+                T.gemv(xs[s], qs[i], out=ys[s])
+        return run
 
     def stage_gemm():
         T.gemm(xp, qp, out=yp)
 
-    stages = [stage_quantize, stage_dequantize, stage_gemv, stage_gemm]
+    stages = [stage_quantize, stage_dequantize] + \
+        [stage_gemv(s) for s in range(len(DECODE_SHAPES))] + [stage_gemm]
     for fn in stages:        # eager warm-up (also loads every kernel)
         fn()
     torch.cuda.synchronize()
@@ -185,6 +207,16 @@ def main():
             marks[2 * k + 1].record(stream)
         return marks
 
+    if args.pmc_calibration:
+        # a plain copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE
+        # counters of the kernels (256 MiB read + 256 MiB written per copy)
+        src = torch.empty(128 * 1024 * 1024, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -201,8 +233,11 @@ def main():
 
     t_q = stage_ms(0) / 1e3
     t_d = stage_ms(1) / 1e3
-    t_v = stage_ms(2) / 1e3
-    t_m = stage_ms(3) / 1e3
+    t_shape = [stage_ms(2 + s) / 1e3 for s in range(len(DECODE_SHAPES))]
+    t_v = sum(t_shape)
+    t_m = stage_ms(2 + len(DECODE_SHAPES)) / 1e3
+    shape_us = {f"{N}x{K}": round(t / (args.steps * L) * 1e6, 3)
+                for (N, K), t in zip(DECODE_SHAPES, t_shape)}
     K_ = args.steps
     gb_v = K_ * L * sum(gemv_bytes(1, N, K) for N, K in DECODE_SHAPES)
     gb_q = K_ * L * sum(quant_bytes(N, K) for N, K in DECODE_SHAPES)
@@ -239,7 +274,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(avg_gemv_bytes / (avg_gemv_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": recorded_gemv_traffic(),
         },
         "gemm": {
             "tflops": round(gemm_tflops, 1),
@@ -253,6 +288,7 @@ def main():
             "dequantize_gbs": round(gb_d / t_d / 1e9, 1),
             "gemv_gbs": round(gemv_gbs, 1),
             "gemv_avg_launch_us": round(avg_gemv_us, 3),
+            "gemv_launch_us_by_shape": shape_us,
             "stage_ms_per_step": {"quantize": round(t_q / K_ * 1e3, 3),
                                   "dequantize": round(t_d / K_ * 1e3, 3),
                                   "gemv": round(t_v / K_ * 1e3, 3),

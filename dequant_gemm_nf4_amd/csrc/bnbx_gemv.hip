@@ -24,12 +24,29 @@
 namespace bnbx {
 namespace {
 
-constexpr int kMaxThreads = 512;
+// Tunables (compile-time; the defaults are the measured best on MI355X).
+#ifndef BNBX_GEMV_MAX_THREADS
+#define BNBX_GEMV_MAX_THREADS 512     // threads per workgroup
+#endif
+#ifndef BNBX_GEMV_TAB_COPIES
+#define BNBX_GEMV_TAB_COPIES 32       // lane copies of the byte table (32 or 64)
+#endif
+#ifndef BNBX_GEMV_MIN_WAVES
+#define BNBX_GEMV_MIN_WAVES 1         // launch-bounds occupancy hint (waves per SIMD)
+#endif
+#ifndef BNBX_GEMV_WG_TARGET
+#define BNBX_GEMV_WG_TARGET 512       // workgroups the rows are spread over
+#endif
+#ifndef BNBX_GEMV_W_FIRST
+#define BNBX_GEMV_W_FIRST 0           // 1: issue weight loads before the X loads
+#endif
+constexpr int kMaxThreads = BNBX_GEMV_MAX_THREADS;
 constexpr int kGMax = 8;
-constexpr int kTabDwords = 256 * 64;   // 64 KB
+constexpr int kCopies = BNBX_GEMV_TAB_COPIES;
+constexpr int kTabDwords = 256 * 64;   // 256 B per byte value; kCopies dwords used
 
 template <int MM, int P, bool DQ, int G>
-__global__ __launch_bounds__(kMaxThreads) void gemv_valu_kernel(
+__global__ __launch_bounds__(kMaxThreads, BNBX_GEMV_MIN_WAVES) void gemv_valu_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ packed,
     const void* __restrict__ absmax, const float* __restrict__ absmax2,
     const float* __restrict__ mean, int N, int K, uint16_t* __restrict__ y, int64_t ldy, int S,
@@ -48,31 +65,33 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_valu_kernel(
   constexpr int GM = G;
   const int lvl = level_lanes(lv);
 
-  // 1. this thread's X slice first (small, cache-resident): 32 bf16 (16
-  //    pairs) per chunk per row of X
+  // X slice of this thread: 32 bf16 (16 pairs) per chunk per row of X
   uint32_t xr[MM][P][16];
+  auto load_x = [&]() {
 #pragma unroll
-  for (int m = 0; m < MM; ++m) {
+    for (int m = 0; m < MM; ++m) {
 #pragma unroll
-    for (int j = 0; j < P; ++j) {
-      const int c = s + j * S;
-      const int cc = c < C ? c : C - 1;
-      const uint4* src = (const uint4*)(x + (int64_t)m * ldx + (int64_t)cc * 32);
+      for (int j = 0; j < P; ++j) {
+        const int c = s + j * S;
+        const int cc = c < C ? c : C - 1;
+        const uint4* src = (const uint4*)(x + (int64_t)m * ldx + (int64_t)cc * 32);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint4 v = src[q];
-        xr[m][j][4 * q] = v.x;
-        xr[m][j][4 * q + 1] = v.y;
-        xr[m][j][4 * q + 2] = v.z;
-        xr[m][j][4 * q + 3] = v.w;
+        for (int q = 0; q < 4; ++q) {
+          const uint4 v = src[q];
+          xr[m][j][4 * q] = v.x;
+          xr[m][j][4 * q + 1] = v.y;
+          xr[m][j][4 * q + 2] = v.z;
+          xr[m][j][4 * q + 3] = v.w;
+        }
       }
     }
-  }
-  // 2. then every weight load, each followed by its raw block-scale loads,
-  //    all in flight before anything waits (addresses clamped instead of
-  //    branched; out-of-range rows/chunks are zeroed through their scale).
-  //    Scales are converted only after the barrier, so using row g waits
-  //    only for the loads issued up to row g.
+  };
+  // 1. X (small, cache-resident) and every weight load, each followed by its
+  //    raw block-scale loads, all in flight before anything waits (addresses
+  //    clamped instead of branched; out-of-range rows/chunks are zeroed
+  //    through their scale).  Scales are converted only after the barrier,
+  //    so using row g waits only for the loads issued up to row g.
+  if (!BNBX_GEMV_W_FIRST) load_x();
   uint4 wv[GM][P];
   int qraw[GM][P];
   float sraw[GM][P], graw[GM][P];
@@ -99,17 +118,18 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_valu_kernel(
       }
     }
   }
+  if (BNBX_GEMV_W_FIRST) load_x();
   const float mu = DQ ? *mean : 0.0f;
-  // 3. replicated byte -> bf16-pair table
-  for (int e = t; e < kTabDwords / 4; e += T) {
-    const uint32_t b = (uint32_t)e >> 4;
+  // 2. replicated byte -> bf16-pair table
+  for (int e = t; e < 256 * kCopies / 4; e += T) {
+    const uint32_t b = (uint32_t)e / (kCopies / 4);
     const uint32_t v = pack_bf16x2(level_lookup(lvl, b >> 4), level_lookup(lvl, b & 15u));
-    ((uint4*)tab)[e] = make_uint4(v, v, v, v);
+    ((uint4*)tab)[b * 16 + (uint32_t)e % (kCopies / 4)] = make_uint4(v, v, v, v);
   }
   __syncthreads();
 
-  // 4. dequant-in-register dot products, one block scale per 32 weights
-  const uint32_t lanebyte = (uint32_t)(t & 63) << 2;
+  // 3. dequant-in-register dot products, one block scale per 32 weights
+  const uint32_t lanebyte = (uint32_t)(t & (kCopies - 1)) << 2;
   const unsigned char* tabb = (const unsigned char*)tab;
   float acc[GM][MM];
 #pragma unroll
@@ -147,7 +167,7 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_valu_kernel(
     }
   }
 
-  // 5. reduce each row over its team: waves first, then across the team's waves
+  // 4. reduce each row over its team: waves first, then across the team's waves
   const int nw = T >> 6, wave = t >> 6, wpt = S >> 6;
 #pragma unroll
   for (int g = 0; g < GM; ++g) {
@@ -201,7 +221,8 @@ hipError_t launch_valu(const uint16_t* x, int64_t ldx, const uint8_t* packed, co
   const int C = K >> 5;
   const int S = ((C + P - 1) / P + 63) / 64 * 64;
   const int R = kMaxThreads / S >= 1 ? kMaxThreads / S : 1;
-  const int64_t need = ((int64_t)N + (int64_t)R * 512 - 1) / ((int64_t)R * 512);
+  const int64_t need = ((int64_t)N + (int64_t)R * BNBX_GEMV_WG_TARGET - 1) /
+                       ((int64_t)R * BNBX_GEMV_WG_TARGET);
   const int gmax = kGMax / P;
   const int G = need <= 4 ? (int)(need < 1 ? 1 : need) : need <= 6 ? 6 : 8;
   const int Gc = G < gmax ? G : gmax;
