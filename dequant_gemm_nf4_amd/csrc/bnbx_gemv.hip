@@ -1,255 +1,483 @@
 // Decode GEMV with NF4 weights for gfx950: Y[M, N] = X[M, K] . W_hat[N, K]^T,
 // M <= 16 (mlqm.cn bitsandbytes article, sec. 3.4 "4-bit storage, 16-bit
 // compute", and the sec. 7 pitfall that 4-bit only pays off when the layer is
-// bound by weight traffic: so the packed weight is streamed exactly once).
+// bound by weight traffic: so the packed weight is streamed exactly once per
+// group of up to four rows of X).
 //
-// Layout of the work.  A row of W is C = K/32 chunks of 16 packed bytes
-// (32 weights, half a 64-block).  A workgroup is R "teams" of S threads
-// (S a multiple of 64, S >= C/P); slot s of a team owns chunks s, s+S, ... of
-// whatever row the team is on, so its slice of X stays in registers for the
-// whole kernel while the team walks G rows.  Every thread issues all of its
-// 16-byte weight loads before it builds the lookup table, so the HBM latency
-// overlaps the table build.
+// Work layout.  A row of W is C = K/32 chunks of 16 packed bytes (32
+// weights, half of one 64-block).  A row is owned by a team of TW waves
+// (S = 64 TW lanes); lane s of a team owns chunks s, s+S, ..., s+(NI-1)S of
+// every row the team takes, so its slice of X is read once into registers.
+// A workgroup is 16 waves and the grid has at most one workgroup per CU; a
+// team takes RR rows per pass, so for the decode shapes one pass covers the
+// matrix.  The first row's loads go out before the lookup table is built,
+// the others right after the workgroup barrier (a wave stalled issuing loads
+// into a full memory pipeline would otherwise hold the barrier for all).
+//
+// Loads are buffer loads whose resource is the row (a scalar base and a
+// length), with a per-lane offset fixed for the whole kernel.  The hardware
+// range check returns zero past the end of the row (the ragged last chunks)
+// and for rows past N, so there is no per-load address arithmetic or bounds
+// branch.  With double quant a row's int8 codes come in one dword per lane and
+// reach the lanes that need them by ds_bpermute, and its (at most two) group
+// scales by scalar loads.  X is staged once per workgroup in LDS.
 //
 // Dequant in registers.  An LDS table maps each packed byte to the bf16 pair
-// (L[high nibble], L[low nibble]); it is replicated 64 times with a 256-byte
-// stride so that lane l always reads bank l (no conflicts), and the byte
-// address (byte << 8 | lane << 2) is formed by one v_perm_b32.  The pair feeds
-// v_dot2_f32_bf16 against the matching X pair; the 32-weight partial sum is
-// scaled once by the block scale (fp32), so dequant costs about one VALU
-// instruction per weight.
+// (L[high nibble], L[low nibble]); it is replicated in 32 lane columns with a
+// 256-byte stride so that the lanes of each half-wave read distinct banks, and
+// the byte address (byte << 8 | lane << 2) is one v_perm_b32.  The pair feeds
+// v_dot2_f32_bf16 against the matching X pair and the 32-weight partial sum
+// is scaled once by its block scale, so dequant costs one VALU instruction per
+// weight plus one LDS read per two.  Chunks are consumed one at a time in
+// load order (scheduling barriers keep the compiler from hoisting work above
+// the waits).  Sums over a wave use DPP row shifts and row broadcasts; a
+// multi-wave team adds its waves' sums through LDS.
 #include "bnbx_device.hpp"
 #include "bnbx_internal.hpp"
 
 namespace bnbx {
 namespace {
 
-// Tunables (compile-time; the defaults are the measured best on MI355X).
-#ifndef BNBX_GEMV_MAX_THREADS
-#define BNBX_GEMV_MAX_THREADS 512     // threads per workgroup
+#ifndef BNBX_GEMV_WAVES
+#define BNBX_GEMV_WAVES 16
 #endif
-#ifndef BNBX_GEMV_TAB_COPIES
-#define BNBX_GEMV_TAB_COPIES 32       // lane copies of the byte table (32 or 64)
+constexpr int kWaves = BNBX_GEMV_WAVES;     // waves per workgroup
+constexpr int kThreads = kWaves * 64;
+constexpr int kCopies = 32;                 // lane columns of the byte table (128 B)
+constexpr int kTabBytes = 256 * 256;        // 256 B per byte value
+#ifndef BNBX_GEMV_WG_PER_CU
+#define BNBX_GEMV_WG_PER_CU 1
 #endif
-#ifndef BNBX_GEMV_MIN_WAVES
-#define BNBX_GEMV_MIN_WAVES 1         // launch-bounds occupancy hint (waves per SIMD)
+#ifndef BNBX_GEMV_XLAZY
+#define BNBX_GEMV_XLAZY 0
 #endif
-#ifndef BNBX_GEMV_WG_TARGET
-#define BNBX_GEMV_WG_TARGET 512       // workgroups the rows are spread over
-#endif
-#ifndef BNBX_GEMV_W_FIRST
-#define BNBX_GEMV_W_FIRST 0           // 1: issue weight loads before the X loads
-#endif
-constexpr int kMaxThreads = BNBX_GEMV_MAX_THREADS;
-constexpr int kGMax = 8;
-constexpr int kCopies = BNBX_GEMV_TAB_COPIES;
-constexpr int kTabDwords = 256 * 64;   // 256 B per byte value; kCopies dwords used
+constexpr int kWgPerCu = BNBX_GEMV_WG_PER_CU;   // workgroups resident per CU
+// X staged in LDS when MM*K*2 fits (the table takes 64 KB of the CU's 160 KB).
+constexpr int kXBytes = kWgPerCu == 1 ? 64 * 1024 : 16 * 1024;
+// Waves per SIMD that must fit at once (caps the VGPRs at 512 / this).
+constexpr int kMinWavesPerSimd = kWgPerCu * kWaves / 4 < 4 ? kWgPerCu * kWaves / 4 : 4;
+constexpr int kMaxMM = 4;
+constexpr int kMaxRR = 4;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
 
-template <int MM, int P, bool DQ, int G>
-__global__ __launch_bounds__(kMaxThreads, BNBX_GEMV_MIN_WAVES) void gemv_valu_kernel(
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           (int)kRsrcWord3);
+}
+template <int AUX>
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+template <int CTRL, int ROWMASK, bool BOUND_ZERO>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWMASK, 0xf, BOUND_ZERO));
+}
+// Sum over the 64 lanes of a wave, left in lane 63: prefix sums within each
+// row of 16 lanes (row_shr 1, 2, 4, 8), then row_bcast:15 and row_bcast:31
+// carry the row totals up to lane 63.
+__device__ __forceinline__ float wave_sum_to_63(float v) {
+  v += dpp<0x111, 0xf, true>(v);
+  v += dpp<0x112, 0xf, true>(v);
+  v += dpp<0x114, 0xf, true>(v);
+  v += dpp<0x118, 0xf, true>(v);
+  v += dpp<0x142, 0xa, false>(v);
+  v += dpp<0x143, 0xc, false>(v);
+  return v;
+}
+
+// Block-scale storage: fp32 absmax, or double quant (int8 code + fp32 group
+// scale + mean) read per lane, or double quant read per row.  The row-wise
+// read loads whole dwords of codes, and the buffer range check zeroes a dword
+// that is only partly inside the row, so it needs a row of 4k blocks (at most
+// 256: K <= 16384, K % 256 == 0) and 4-byte aligned codes.
+enum ScaleMode { kScaleF32 = 0, kScaleDqLane = 1, kScaleDqRow = 2 };
+
+// MM rows of X per launch (rows >= mvalid are zero), NI chunks per lane, RR
+// rows of W per team and pass.  TW = 1 << twl waves per team.
+template <int MM, int NI, int RR, int SM>
+__global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void gemv_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ packed,
     const void* __restrict__ absmax, const float* __restrict__ absmax2,
-    const float* __restrict__ mean, int N, int K, uint16_t* __restrict__ y, int64_t ldy, int S,
-    int R, LevelTable lv) {
-  __shared__ __attribute__((aligned(16))) uint32_t tab[kTabDwords];
-  __shared__ float red[kGMax * MM * (kMaxThreads / 64)];
+    const float* __restrict__ mean, int mvalid, int N, int K, uint16_t* __restrict__ y,
+    int64_t ldy, int twl, int xlds, LevelTable lv) {
+  constexpr bool DQ = SM != kScaleF32;
+  // One LDS block with the table at offset 0, so that a table address is the
+  // v_perm result itself (the ds_read offset field cannot hold a 64 KB base),
+  // then X, then the team sums.  X is stored in 64-byte chunks whose four
+  // 16-byte pieces are rotated by (chunk / 4) % 4: piece q of chunk c sits at
+  // 64 c + 16 (q ^ ((c >> 2) & 3)), so that 16 lanes reading piece q of 16
+  // consecutive chunks hit 64 distinct banks.
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kTabBytes + kXBytes +
+                                                             kWaves * MM * RR * 4];
+  unsigned char* const tab = smem;
+  unsigned char* const xs = smem + kTabBytes;
+  float* const red = (float*)(smem + kTabBytes + kXBytes);
 
   const int t = threadIdx.x;
-  const int T = blockDim.x;
-  const int team = t / S, s = t - team * S;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int TW = 1 << twl;
+  const int tpw = kWaves >> twl;              // teams per workgroup
+  const int team_l = wave >> twl;
+  const int wit = wave - (team_l << twl);     // wave within team
+  const int S = 64 << twl;
+  const int s = wit * 64 + lane;              // lane slot within team
   const int C = K >> 5;
-  const int64_t rowK2 = (int64_t)(K >> 1);
-  const int64_t nkb = K >> 6;
-  const int64_t row0 = (int64_t)blockIdx.x * R * G + team;
-  static_assert(G * P <= kGMax, "at most 8 chunks per thread");
-  constexpr int GM = G;
-  const int lvl = level_lanes(lv);
+  const uint32_t rowK2 = (uint32_t)K >> 1;
+  const uint32_t nkb = (uint32_t)K >> 6;
+  const uint32_t xbytes = (uint32_t)K * 2u;
+  const int64_t pass_rows = (int64_t)gridDim.x * tpw * RR;
+  const int64_t rb_first = (int64_t)blockIdx.x * tpw * RR;   // workgroup's first row
+  const uint32_t ng_bytes = DQ ? (uint32_t)((((uint64_t)N * nkb + 255) >> 8) * 4) : 0u;
+  const rsrc_t rg = make_rsrc(absmax2, ng_bytes);
 
-  // X slice of this thread: 32 bf16 (16 pairs) per chunk per row of X
-  uint32_t xr[MM][P][16];
-  auto load_x = [&]() {
+  // Fixed per-lane offsets: chunk c of the row (bytes), its block (index).
+  uint32_t woff[NI], boff[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const uint32_t c = (uint32_t)(s + i * S);
+    woff[i] = c * 16u;
+    boff[i] = c >> 1;
+  }
+
+  // 1. X: staging loads (LDS path) or the lane's slice directly.
+  uint32_t xr[MM][NI][16];
+  constexpr int kStage = kXBytes / 16 / kThreads;   // 16-byte pieces per thread (max)
+  uint4 xst[kStage];
+  const int xpieces = (int)(xbytes >> 4);          // per row of X
+  if (xlds) {
+    // One resource over the valid rows of X; rows at or past mvalid (and
+    // pieces past MM rows) fall outside it and read as zero.
+    const rsrc_t rx = make_rsrc(x, (uint32_t)((int64_t)(mvalid - 1) * ldx * 2) + xbytes);
+#pragma unroll
+    for (int k = 0; k < kStage; ++k) {
+      const int e = t + k * kThreads;
+      if (e < MM * xpieces) {          // whole waves drop out: no idle loads
+        const int m = e / xpieces;
+        const int p = e - m * xpieces;
+        xst[k] = buf_load16<0>(rx, (uint32_t)((int64_t)m * ldx * 2) + (uint32_t)p * 16u);
+      }
+    }
+  } else {
 #pragma unroll
     for (int m = 0; m < MM; ++m) {
+      const rsrc_t rx = make_rsrc(x + (int64_t)m * ldx, m < mvalid ? xbytes : 0u);
 #pragma unroll
-      for (int j = 0; j < P; ++j) {
-        const int c = s + j * S;
-        const int cc = c < C ? c : C - 1;
-        const uint4* src = (const uint4*)(x + (int64_t)m * ldx + (int64_t)cc * 32);
+      for (int i = 0; i < NI; ++i) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint4 v = src[q];
-          xr[m][j][4 * q] = v.x;
-          xr[m][j][4 * q + 1] = v.y;
-          xr[m][j][4 * q + 2] = v.z;
-          xr[m][j][4 * q + 3] = v.w;
+          const uint4 v = buf_load16<0>(rx, woff[i] * 4u + q * 16u);
+          xr[m][i][4 * q] = v.x;
+          xr[m][i][4 * q + 1] = v.y;
+          xr[m][i][4 * q + 2] = v.z;
+          xr[m][i][4 * q + 3] = v.w;
+        }
+      }
+    }
+  }
+
+  // 2. Weight and scale loads of RR rows.  Rows past N get an empty resource.
+  //    Double quant with rows of at most 256 blocks (K <= 16384) loads a
+  //    row's int8 codes with one dword per lane (lane l: blocks 4l..4l+3,
+  //    handed to the lanes that need them by ds_bpermute) and its group
+  //    scales with scalar loads (a row spans at most two groups); otherwise
+  //    every lane loads its own block's scales.
+  constexpr bool rowsc = SM == kScaleDqRow;
+  const uint32_t ng = DQ ? (uint32_t)(((uint64_t)N * nkb + 255) >> 8) : 1u;
+  uint4 w[RR][NI];
+  int qv[RR][NI];
+  float gv[RR][NI];
+  int qd[RR];
+  float gs0[RR], gs1[RR];
+  uint32_t split[RR];
+  auto issue_part = [&](int64_t rb, int lo, int hi) {
+#pragma unroll
+    for (int j = 0; j < RR; ++j) {
+      if ((j + 1) * NI <= lo || j * NI >= hi) continue;
+      const int64_t row = rb + j;
+      const bool ok = row < N;
+      const rsrc_t rw = make_rsrc(packed + row * rowK2, ok ? rowK2 : 0u);
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        if (j * NI + i >= lo && j * NI + i < hi) w[j][i] = buf_load16<2>(rw, woff[i]);   // nt
+      if (j * NI < lo) continue;              // the row's scales went with its first chunk
+      if (rowsc) {
+        const rsrc_t rq = make_rsrc((const int8_t*)absmax + row * nkb, ok ? nkb : 0u);
+        qd[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(rq, (uint32_t)lane * 4u, 0, 0);
+        const uint32_t blk0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(row * nkb));
+        uint32_t g0 = blk0 >> 8;
+        g0 = g0 < ng ? g0 : ng - 1u;
+        const uint32_t g1 = g0 + 1u < ng ? g0 + 1u : ng - 1u;
+        gs0[j] = absmax2[g0];
+        gs1[j] = absmax2[g1];
+        split[j] = 256u - (blk0 & 255u);     // blocks of the row in group g0
+      } else if (DQ) {
+        const rsrc_t rq = make_rsrc((const int8_t*)absmax + row * nkb, ok ? nkb : 0u);
+        const uint32_t blk0 = (uint32_t)(row * nkb);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          qv[j][i] = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(rq, boff[i], 0, 0);
+          gv[j][i] = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(rg, ((blk0 + boff[i]) >> 8) * 4u, 0, 0));
+        }
+      } else {
+        const rsrc_t ra = make_rsrc((const float*)absmax + row * nkb, ok ? nkb * 4u : 0u);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          qv[j][i] = 0;
+          gv[j][i] = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(ra, boff[i] * 4u, 0, 0));
         }
       }
     }
   };
-  // 1. X (small, cache-resident) and every weight load, each followed by its
-  //    raw block-scale loads, all in flight before anything waits (addresses
-  //    clamped instead of branched; out-of-range rows/chunks are zeroed
-  //    through their scale).  Scales are converted only after the barrier,
-  //    so using row g waits only for the loads issued up to row g.
-  if (!BNBX_GEMV_W_FIRST) load_x();
-  uint4 wv[GM][P];
-  int qraw[GM][P];
-  float sraw[GM][P], graw[GM][P];
+  auto issue = [&](int64_t rb) { issue_part(rb, 0, RR * NI); };
+  // The first row of the first pass goes out now, before the table build;
+  // the other rows after the barrier, so that a wave held up issuing loads
+  // into a full memory pipeline does not hold the barrier for the others.
+  issue_part(rb_first + (int64_t)team_l * RR, 0, NI);
+
+  // 3. Byte -> bf16-pair table, then X into LDS.
+  const int lvl = level_lanes(lv);
+  for (int e = t; e < 256 * kCopies / 4; e += kThreads) {
+    const uint32_t b = (uint32_t)e / (kCopies / 4);
+    const uint32_t v = pack_bf16x2(level_lookup(lvl, b >> 4), level_lookup(lvl, b & 15u));
+    *(uint4*)(tab + b * 256u + ((uint32_t)e % (kCopies / 4)) * 16u) = make_uint4(v, v, v, v);
+  }
+  if (xlds) {
 #pragma unroll
-  for (int g = 0; g < GM; ++g) {
-    {
-#pragma unroll
-      for (int j = 0; j < P; ++j) {
-        const int64_t row = row0 + (int64_t)g * R;
-        const int c = s + j * S;
-        const int64_t rc = row < N ? row : N - 1;
-        const int cc = c < C ? c : C - 1;
-        wv[g][j] = load_nt16(packed + rc * rowK2 + (int64_t)cc * 16);
-        const int64_t blk = rc * nkb + (cc >> 1);
-        if (DQ) {
-          qraw[g][j] = ((const int8_t*)absmax)[blk];
-          graw[g][j] = absmax2[blk >> 8];
-          sraw[g][j] = 0.0f;
-        } else {
-          qraw[g][j] = 0;
-          sraw[g][j] = ((const float*)absmax)[blk];
-          graw[g][j] = 0.0f;
-        }
+    for (int k = 0; k < kStage; ++k) {
+      const int e = t + k * kThreads;
+      if (e < MM * xpieces) {
+        const uint32_t c = (uint32_t)e >> 2, q = (uint32_t)e & 3u;   // chunk and piece
+        *(uint4*)(xs + c * 64u + ((q ^ ((c >> 2) & 3u)) << 4)) = xst[k];
       }
     }
   }
-  if (BNBX_GEMV_W_FIRST) load_x();
-  const float mu = DQ ? *mean : 0.0f;
-  // 2. replicated byte -> bf16-pair table
-  for (int e = t; e < 256 * kCopies / 4; e += T) {
-    const uint32_t b = (uint32_t)e / (kCopies / 4);
-    const uint32_t v = pack_bf16x2(level_lookup(lvl, b >> 4), level_lookup(lvl, b & 15u));
-    ((uint4*)tab)[b * 16 + (uint32_t)e % (kCopies / 4)] = make_uint4(v, v, v, v);
-  }
+  // Nothing may move across the barrier: a weight use hoisted above it would
+  // make every wave wait there for its first row.
+  __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
-
-  // 3. dequant-in-register dot products, one block scale per 32 weights
-  const uint32_t lanebyte = (uint32_t)(t & (kCopies - 1)) << 2;
-  const unsigned char* tabb = (const unsigned char*)tab;
-  float acc[GM][MM];
+  __builtin_amdgcn_sched_barrier(0);
+  // X slice of this lane (LDS path): read up front, or at the first use of
+  // each chunk when BNBX_GEMV_XLAZY is set.
+  auto read_x = [&](int i) {
 #pragma unroll
-  for (int g = 0; g < GM; ++g) {
+    for (int m = 0; m < MM; ++m) {
+      {
+        const int c = s + i * S;
+        const bool in = c < C;
+        const uint32_t cg = (uint32_t)(m * C + (in ? c : 0));   // chunk of the staged X
+        const unsigned char* src = xs + cg * 64u;
+        const uint32_t rot = (cg >> 2) & 3u;
 #pragma unroll
-    for (int m = 0; m < MM; ++m) acc[g][m] = 0.0f;
+        for (int q = 0; q < 4; ++q) {
+          const uint4 v = *(const uint4*)(src + (((uint32_t)q ^ rot) << 4));
+          xr[m][i][4 * q] = in ? v.x : 0u;
+          xr[m][i][4 * q + 1] = in ? v.y : 0u;
+          xr[m][i][4 * q + 2] = in ? v.z : 0u;
+          xr[m][i][4 * q + 3] = in ? v.w : 0u;
+        }
+      }
+    }
+  };
+  if (xlds && !BNBX_GEMV_XLAZY) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) read_x(i);
   }
+
+  issue_part(rb_first + (int64_t)team_l * RR, NI, RR * NI);
+  const float mu = DQ ? *mean : 0.0f;
+  const uint32_t lanebyte = (uint32_t)(lane & (kCopies - 1)) << 2;
+  // 4. Dequant-in-register dot products of one pass, one chunk at a time in
+  //    load order, then the sums over the team and the stores.
+  auto pass = [&](int64_t rb, bool first) {
+    float acc[MM][RR];
 #pragma unroll
-  for (int g = 0; g < GM; ++g) {
-    {
+    for (int j = 0; j < RR; ++j) {
 #pragma unroll
-      for (int j = 0; j < P; ++j) {
-        const int64_t row = row0 + (int64_t)g * R;
-        const bool ok = row < N && s + j * S < C;
-        float sc = DQ ? __builtin_fmaf((float)qraw[g][j], graw[g][j] * (1.0f / 127.0f), mu)
-                      : sraw[g][j];
-        sc = ok ? sc : 0.0f;
-        const uint32_t d[4] = {wv[g][j].x, wv[g][j].y, wv[g][j].z, wv[g][j].w};
+      for (int m = 0; m < MM; ++m) acc[m][j] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        if (BNBX_GEMV_XLAZY && first && j == 0 && xlds) read_x(i);
+        float sc;
+        if (rowsc) {
+          const int qw = __builtin_amdgcn_ds_bpermute((int)((boff[i] >> 2) << 2), qd[j]);
+          const int q = __builtin_amdgcn_sbfe(qw, (boff[i] & 3u) * 8u, 8);
+          const float g = boff[i] < split[j] ? gs0[j] : gs1[j];
+          sc = __builtin_fmaf((float)q, g * (1.0f / 127.0f), mu);
+        } else {
+          sc = DQ ? __builtin_fmaf((float)qv[j][i], gv[j][i] * (1.0f / 127.0f), mu) : gv[j][i];
+        }
+        const uint32_t d[4] = {w[j][i].x, w[j][i].y, w[j][i].z, w[j][i].w};
         float part[MM];
 #pragma unroll
         for (int m = 0; m < MM; ++m) part[m] = 0.0f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t addr = perm(d[q], lanebyte, 0x0c0c0000u | ((4u + i) << 8));
-            const uint32_t pair = *(const uint32_t*)(tabb + addr);
+          for (int b = 0; b < 4; ++b) {
+            const uint32_t addr = perm(d[q], lanebyte, 0x0c0c0000u | ((4u + b) << 8));
+            const uint32_t pair = *(const uint32_t*)(tab + addr);
 #pragma unroll
-            for (int m = 0; m < MM; ++m) part[m] = dot2_bf16(pair, xr[m][j][4 * q + i], part[m]);
+            for (int m = 0; m < MM; ++m) part[m] = dot2_bf16(pair, xr[m][i][4 * q + b], part[m]);
           }
         }
 #pragma unroll
-        for (int m = 0; m < MM; ++m) acc[g][m] = __builtin_fmaf(part[m], sc, acc[g][m]);
+        for (int m = 0; m < MM; ++m) acc[m][j] = __builtin_fmaf(part[m], sc, acc[m][j]);
+        // Only one chunk's table addresses and pairs live at a time.
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-  }
-
-  // 4. reduce each row over its team: waves first, then across the team's waves
-  const int nw = T >> 6, wave = t >> 6, wpt = S >> 6;
 #pragma unroll
-  for (int g = 0; g < GM; ++g) {
-    {
+    for (int j = 0; j < RR; ++j)
 #pragma unroll
-      for (int m = 0; m < MM; ++m) {
-        const float v = wave_sum(acc[g][m]);
-        if ((t & 63) == 0) red[(g * MM + m) * nw + wave] = v;
+      for (int m = 0; m < MM; ++m) acc[m][j] = wave_sum_to_63(acc[m][j]);
+    if (TW == 1) {
+      if (lane == 63) {
+#pragma unroll
+        for (int j = 0; j < RR; ++j)
+#pragma unroll
+          for (int m = 0; m < MM; ++m)
+            if (rb + j < N && m < mvalid) y[(int64_t)m * ldy + rb + j] = f32_to_bf16(acc[m][j]);
       }
+    } else {
+      if (lane == 63) {
+#pragma unroll
+        for (int j = 0; j < RR; ++j)
+#pragma unroll
+          for (int m = 0; m < MM; ++m) red[(wave * MM + m) * RR + j] = acc[m][j];
+      }
+      __syncthreads();
+      if (wit == 0 && lane < MM * RR) {
+        const int m = lane / RR, j = lane - (lane / RR) * RR;
+        float v = 0.0f;
+        for (int u = 0; u < TW; ++u) v += red[((team_l * TW + u) * MM + m) * RR + j];
+        if (rb + j < N && m < mvalid) y[(int64_t)m * ldy + rb + j] = f32_to_bf16(v);
+      }
+      __syncthreads();
     }
-  }
-  __syncthreads();
-  const int nout = G * R * MM;
-  for (int o = t; o < nout; o += T) {
-    const int g = o / (R * MM);
-    const int rem = o - g * R * MM;
-    const int tm = rem / MM, m = rem - tm * MM;
-    const int64_t row = (int64_t)blockIdx.x * R * G + (int64_t)g * R + tm;
-    if (row < N) {
-      float v = 0.0f;
-      for (int w = tm * wpt; w < (tm + 1) * wpt; ++w) v += red[(g * MM + m) * nw + w];
-      y[(int64_t)m * ldy + row] = f32_to_bf16(v);
-    }
+  };
+  // The first pass uses the loads issued before the table build; later
+  // passes (more rows than the grid holds at once) issue their own.  The
+  // loop condition is the workgroup's, so its barriers are uniform.
+  pass(rb_first + (int64_t)team_l * RR, true);
+  for (int64_t rb0 = rb_first + pass_rows; rb0 < N; rb0 += pass_rows) {
+    issue(rb0 + (int64_t)team_l * RR);
+    pass(rb0 + (int64_t)team_l * RR, false);
   }
 }
 
-template <int MM, int P, int G>
-hipError_t launch_valu_g(const uint16_t* x, int64_t ldx, const uint8_t* packed,
-                         const void* absmax, const float* absmax2, const float* mean, int dq,
-                         int N, int K, uint16_t* y, int64_t ldy, int S, int R,
-                         hipStream_t stream) {
-  const int64_t grid = ((int64_t)N + R * G - 1) / (R * G);
-  if (dq)
-    hipLaunchKernelGGL((gemv_valu_kernel<MM, P, true, G>), dim3((unsigned)grid), dim3(S * R), 0,
-                       stream, x, ldx, packed, absmax, absmax2, mean, N, K, y, ldy, S, R,
-                       level_table());
+// ---------------------------------------------------------------------------
+// host side: plan and dispatch
+// ---------------------------------------------------------------------------
+struct Plan {
+  int mm, ni, rr, twl, grid, xlds;
+};
+
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
+// Largest rows-per-pass the registers allow for (mm, ni): the X slice takes
+// 16*mm*ni VGPRs and each row 6*ni more (weights and scales), within the
+// 128 VGPRs of four waves per SIMD.
+int rr_max(int mm, int ni) {
+  int r = (100 - 16 * mm * ni) / (6 * ni);
+  if (r > kMaxRR) r = kMaxRR;
+  if (r < 1) r = 1;
+  if (mm == 1 && ni == 3) r = 2;
+  if (mm == 1 && ni == 4) r = 1;
+  if (mm == 2 && ni == 2) r = 2;
+  return r;
+}
+
+bool make_plan(int mm, int N, int K, Plan& p) {
+  const int C = K >> 5;
+  const int nimax = 4 / mm;
+  int best_twl = -1, best_ni = 0;
+  double best_util = 0.0;
+  for (int twl = 0; (1 << twl) <= kWaves; ++twl) {
+    const int S = 64 << twl;
+    const int ni = (C + S - 1) / S;
+    if (ni > nimax) continue;
+    const double util = (double)C / ((double)S * ni);
+    if (util > best_util + 1e-9) {
+      best_util = util;
+      best_twl = twl;
+      best_ni = ni;
+    }
+  }
+  if (best_twl < 0) return false;
+  const int tpw = kWaves >> best_twl;
+  const int cus = cu_count();
+  const int rmax = rr_max(mm, best_ni);
+  const int64_t slots = (int64_t)cus * kWgPerCu * tpw;   // teams resident at once
+  int64_t rr = ((int64_t)N + slots - 1) / slots;
+  if (rr < 1) rr = 1;
+  if (rr > rmax) rr = rmax;
+  int64_t grid = ((int64_t)N + tpw * rr - 1) / (tpw * rr);
+  if (grid > (int64_t)cus * kWgPerCu) grid = (int64_t)cus * kWgPerCu;
+  p.mm = mm;
+  p.ni = best_ni;
+  p.rr = (int)rr;
+  p.twl = best_twl;
+  p.grid = (int)grid;
+  p.xlds = (int64_t)mm * K * 2 <= kXBytes ? 1 : 0;
+  return true;
+}
+
+template <int MM, int NI, int RR>
+hipError_t launch_k(const Plan& p, const uint16_t* x, int64_t ldx, const uint8_t* packed,
+                    const void* absmax, const float* absmax2, const float* mean, int dq,
+                    int mvalid, int N, int K, uint16_t* y, int64_t ldy, hipStream_t stream) {
+  const LevelTable& lv = level_table();
+  if (!dq)
+    hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, kScaleF32>), dim3(p.grid), dim3(kThreads), 0,
+                       stream, x, ldx, packed, absmax, absmax2, mean, mvalid, N, K, y, ldy, p.twl,
+                       p.xlds, lv);
+  else if ((K >> 6) <= 256 && (K >> 6) % 4 == 0 && ((uintptr_t)absmax & 3u) == 0)
+    hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, kScaleDqRow>), dim3(p.grid), dim3(kThreads), 0,
+                       stream, x, ldx, packed, absmax, absmax2, mean, mvalid, N, K, y, ldy, p.twl,
+                       p.xlds, lv);
   else
-    hipLaunchKernelGGL((gemv_valu_kernel<MM, P, false, G>), dim3((unsigned)grid), dim3(S * R), 0,
-                       stream, x, ldx, packed, absmax, absmax2, mean, N, K, y, ldy, S, R,
-                       level_table());
+    hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, kScaleDqLane>), dim3(p.grid), dim3(kThreads), 0,
+                       stream, x, ldx, packed, absmax, absmax2, mean, mvalid, N, K, y, ldy, p.twl,
+                       p.xlds, lv);
   return hipGetLastError();
 }
 
-// Team size S covers a row's chunks (P per thread); R teams per workgroup;
-// G rows per team, picked so that about 512 workgroups (two per CU, the LDS
-// limit) cover N.
-template <int MM, int P>
-hipError_t launch_valu(const uint16_t* x, int64_t ldx, const uint8_t* packed, const void* absmax,
-                       const float* absmax2, const float* mean, int dq, int N, int K,
-                       uint16_t* y, int64_t ldy, hipStream_t stream) {
-  const int C = K >> 5;
-  const int S = ((C + P - 1) / P + 63) / 64 * 64;
-  const int R = kMaxThreads / S >= 1 ? kMaxThreads / S : 1;
-  const int64_t need = ((int64_t)N + (int64_t)R * BNBX_GEMV_WG_TARGET - 1) /
-                       ((int64_t)R * BNBX_GEMV_WG_TARGET);
-  const int gmax = kGMax / P;
-  const int G = need <= 4 ? (int)(need < 1 ? 1 : need) : need <= 6 ? 6 : 8;
-  const int Gc = G < gmax ? G : gmax;
-#define BNBX_GEMV_G(GV)                                                                     \
-  if (Gc == GV)                                                                             \
-    return launch_valu_g<MM, P, (GV * P <= kGMax ? GV : 1)>(x, ldx, packed, absmax, absmax2, \
-                                                           mean, dq, N, K, y, ldy, S, R, stream);
-  BNBX_GEMV_G(1)
-  BNBX_GEMV_G(2)
-  BNBX_GEMV_G(3)
-  BNBX_GEMV_G(4)
-  BNBX_GEMV_G(6)
-  BNBX_GEMV_G(8)
-#undef BNBX_GEMV_G
+hipError_t dispatch(const Plan& p, const uint16_t* x, int64_t ldx, const uint8_t* packed,
+                    const void* absmax, const float* absmax2, const float* mean, int dq,
+                    int mvalid, int N, int K, uint16_t* y, int64_t ldy, hipStream_t stream) {
+#define BNBX_GEMV_CASE(MM, NI, RR)                                                            \
+  if (p.mm == MM && p.ni == NI && p.rr == RR)                                                 \
+    return launch_k<MM, NI, RR>(p, x, ldx, packed, absmax, absmax2, mean, dq, mvalid, N, K, y, \
+                                ldy, stream);
+  BNBX_GEMV_CASE(1, 1, 1) BNBX_GEMV_CASE(1, 1, 2) BNBX_GEMV_CASE(1, 1, 3) BNBX_GEMV_CASE(1, 1, 4)
+  BNBX_GEMV_CASE(1, 2, 1) BNBX_GEMV_CASE(1, 2, 2) BNBX_GEMV_CASE(1, 2, 3) BNBX_GEMV_CASE(1, 2, 4)
+  BNBX_GEMV_CASE(1, 3, 1) BNBX_GEMV_CASE(1, 3, 2)
+  BNBX_GEMV_CASE(1, 4, 1)
+  BNBX_GEMV_CASE(2, 1, 1) BNBX_GEMV_CASE(2, 1, 2) BNBX_GEMV_CASE(2, 1, 3) BNBX_GEMV_CASE(2, 1, 4)
+  BNBX_GEMV_CASE(2, 2, 1) BNBX_GEMV_CASE(2, 2, 2)
+  BNBX_GEMV_CASE(4, 1, 1) BNBX_GEMV_CASE(4, 1, 2) BNBX_GEMV_CASE(4, 1, 3) BNBX_GEMV_CASE(4, 1, 4)
+#undef BNBX_GEMV_CASE
   return hipErrorNotSupported;
-}
-
-template <int P>
-hipError_t launch_valu_m(int MM, const uint16_t* x, int64_t ldx, const uint8_t* packed,
-                         const void* absmax, const float* absmax2, const float* mean, int dq,
-                         int N, int K, uint16_t* y, int64_t ldy, hipStream_t stream) {
-  switch (MM) {
-    case 1: return launch_valu<1, P>(x, ldx, packed, absmax, absmax2, mean, dq, N, K, y, ldy, stream);
-    case 2: return launch_valu<2, P>(x, ldx, packed, absmax, absmax2, mean, dq, N, K, y, ldy, stream);
-    case 3: return launch_valu<3, P>(x, ldx, packed, absmax, absmax2, mean, dq, N, K, y, ldy, stream);
-    default: return launch_valu<4, P>(x, ldx, packed, absmax, absmax2, mean, dq, N, K, y, ldy, stream);
-  }
 }
 
 }  // namespace
@@ -257,22 +485,37 @@ hipError_t launch_valu_m(int MM, const uint16_t* x, int64_t ldx, const uint8_t* 
 hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* packed, const void* absmax,
                        const float* absmax2, const float* mean, int double_quant, int M, int N,
                        int K, uint16_t* y, int64_t ldy, hipStream_t stream) {
-  const int C = K >> 5;
-  const int P = C <= kMaxThreads ? 1 : C <= 2 * kMaxThreads ? 2 : C <= 4 * kMaxThreads ? 4 : 0;
-  if (P == 0) return hipErrorNotSupported;
-  // Rows of X in groups of at most 4 (each group streams W once); with two
-  // chunks per thread one row at a time keeps the X slice in registers.
-  const int mstep = P == 1 ? 4 : 1;
-  for (int m0 = 0; m0 < M; m0 += mstep) {
-    const int mm = M - m0 < mstep ? M - m0 : mstep;
-    const hipError_t e =
-        P == 1 ? launch_valu_m<1>(mm, x + (int64_t)m0 * ldx, ldx, packed, absmax, absmax2, mean,
-                                  double_quant, N, K, y + (int64_t)m0 * ldy, ldy, stream)
-      : P == 2 ? launch_valu<1, 2>(x + (int64_t)m0 * ldx, ldx, packed, absmax, absmax2, mean,
-                                   double_quant, N, K, y + (int64_t)m0 * ldy, ldy, stream)
-               : launch_valu<1, 4>(x + (int64_t)m0 * ldx, ldx, packed, absmax, absmax2, mean,
-                                   double_quant, N, K, y + (int64_t)m0 * ldy, ldy, stream);
-    if (e != hipSuccess) return e;
+  // Slabs of rows keep every byte offset of a launch below 2^31.
+  const int64_t rowK2 = K >> 1, nkb = K >> 6;
+  int64_t slab = ((int64_t)1 << 30) / rowK2;
+  slab -= slab % 256;
+  // Rows of X in groups of up to four (each group streams W once); a group
+  // of three runs the four-row kernel with its last row empty.  Long rows
+  // take smaller groups (the X slice must fit the registers).
+  for (int m0 = 0; m0 < M;) {
+    const int left = M - m0;
+    Plan p;
+    int mv = 0;
+    for (int mm : {4, 2, 1}) {
+      if (left < (mm == 4 ? 3 : mm)) continue;       // a group of 3 uses mm = 4
+      if (make_plan(mm, N < slab ? N : (int)slab, K, p)) {
+        mv = left < mm ? left : mm;
+        break;
+      }
+    }
+    if (mv == 0) return hipErrorNotSupported;
+    for (int64_t r0 = 0; r0 < N; r0 += slab) {
+      const int n = (int)(N - r0 < slab ? N - r0 : slab);
+      if (!make_plan(p.mm, n, K, p)) return hipErrorNotSupported;
+      const void* am = double_quant ? (const void*)((const int8_t*)absmax + r0 * nkb)
+                                    : (const void*)((const float*)absmax + r0 * nkb);
+      const float* am2 = double_quant ? absmax2 + (r0 * nkb) / 256 : absmax2;
+      const hipError_t e =
+          dispatch(p, x + (int64_t)m0 * ldx, ldx, packed + r0 * rowK2, am, am2, mean,
+                   double_quant, mv, n, K, y + (int64_t)m0 * ldy + r0, ldy, stream);
+      if (e != hipSuccess) return e;
+    }
+    m0 += mv;
   }
   return hipSuccess;
 }
