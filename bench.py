@@ -1,16 +1,24 @@
 """Benchmark of the NF4 hot path on one MI355X.
 
-One step is one pass of every step of the path over the decode workload:
-for each of L layers of Llama-7B-shaped linears (4096x4096, 11008x4096,
-4096x11008; bf16 weights N(0, 0.02), distinct per layer), quantize-on-load
-with double quantization, dequantize to bf16, and the M=1 decode GEMV
-(dequant fused); then one prefill GEMM, M=2048, N=K=8192, on a weight
-quantized once before timing.  Inputs are resident in HBM before timing.
+The workload is every linear weight of an L-layer Llama-7B-shaped stack
+(L = 32 by default: per layer q, k, v, o 4096x4096, gate and up 11008x4096,
+down 4096x11008; bf16 weights N(0, 0.02), distinct per layer; 6.5e9
+parameters, 13 GB in bf16, 3.3 GB in NF4).  One step is one pass of every
+step of the path over it: quantize-on-load with double quantization of the
+whole stack, dequantize of the whole stack to bf16, the M=1 decode GEMV
+(dequant fused) on every weight, and one prefill GEMM, M=2048, N=K=8192, on a
+weight quantized once before timing.  Inputs are resident in HBM before
+timing; no GEMV weight is re-read before the other weights of its shape have
+streamed through, so the 256 MB last-level cache holds none of them.
 
 `value` is the decode GEMV throughput in GB/s of algorithmic bytes (packed
-codes + int8 scales + group scales + mean + X + Y) over the GEMV launches of
-the timed steps; the GEMM's TFLOP/s is reported beside it, with per-kernel
-timings, rooflines, and the CPU oracle timed on a bounded sample.
+codes + int8 scales + group scales + mean + X + Y) for the three decode shapes
+4096x4096, 11008x4096 and 4096x11008 weighted equally: the sum of their
+bytes per launch over the sum of their average launch times (each averaged
+over all of that shape's weights in the stack).  The stack-weighted decode
+rate (7 linears per layer), the GEMM's TFLOP/s, per-kernel timings,
+rooflines, and the CPU oracle timed on a bounded sample are reported beside
+it.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L]
 """
@@ -31,6 +39,8 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 METRIC = "NF4 dequant-GEMV HBM GB/s (M=1) + GEMM TFLOP/s (M=2048), % of peak"
 DECODE_SHAPES = ((4096, 4096), (11008, 4096), (4096, 11008))
+# the linears of one Llama-7B-shaped layer: (name, shape index)
+LAYER = (("q", 0), ("k", 0), ("v", 0), ("o", 0), ("gate", 1), ("up", 1), ("down", 2))
 PREFILL = (2048, 8192, 8192)
 
 
@@ -109,7 +119,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="run a 256 MiB plain copy first (counter scaling reference)")
@@ -130,12 +140,15 @@ def main():
 
     # ---- inputs resident in HBM (device-side seeded draws) ----
     gen = torch.Generator(device=dev)
-    weights = []
+    weights, wshape = [], []          # stack order: layer by layer, LAYER order
     for l in range(L):
-        for s, (N, K) in enumerate(DECODE_SHAPES):
-            gen.manual_seed(5000 + 10 * l + s)
+        for li, (name, si) in enumerate(LAYER):
+            N, K = DECODE_SHAPES[si]
+            gen.manual_seed(5000 + 10 * l + li)
             w = (torch.randn(N, K, generator=gen, device=dev, dtype=torch.float32) * 0.02)
             weights.append(w.to(torch.bfloat16))
+            wshape.append(si)
+            del w
     xs = []
     for s, (N, K) in enumerate(DECODE_SHAPES):
         gen.manual_seed(6000 + s)
@@ -145,6 +158,7 @@ def main():
     ws = T.workspace_for(maxn, True, dev)
     deq = torch.empty(maxn, dtype=torch.bfloat16, device=dev)
     ys = [torch.empty(1, N, dtype=torch.bfloat16, device=dev) for N, K in DECODE_SHAPES]
+    by_shape = [[i for i, si in enumerate(wshape) if si == s] for s in range(len(DECODE_SHAPES))]
 
     Mp, Np, Kp = PREFILL
     gen.manual_seed(7000)
@@ -161,13 +175,13 @@ def main():
     torch.cuda.synchronize()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    nlaunch = L * len(DECODE_SHAPES)
 
     # Every stage is captured once into a HIP graph and replayed each step, so
     # host launch overhead stays out of the timings; the decode GEMVs get one
-    # graph per shape (L launches each) bracketed by events, so the average
-    # launch time of each shape is the graph time over L (kernel time plus
-    # the GPU's back-to-back dispatch gap).
+    # graph per shape (every weight of that shape in the stack, in stack
+    # order) bracketed by events, so the average launch time of each shape is
+    # the graph time over its launches (kernel time plus the GPU's
+    # back-to-back dispatch gap).
     def stage_quantize():
         for i, w in enumerate(weights):
             T.quantize(w, True, out=qs[i], workspace=ws)
@@ -178,7 +192,7 @@ def main():
 
     def stage_gemv(s):
         def run():
-            for i in range(s, nlaunch, len(DECODE_SHAPES)):
+            for i in by_shape[s]:
                 T.gemv(xs[s], qs[i], out=ys[s])
         return run
 
@@ -236,16 +250,22 @@ def main():
     t_shape = [stage_ms(2 + s) / 1e3 for s in range(len(DECODE_SHAPES))]
     t_v = sum(t_shape)
     t_m = stage_ms(2 + len(DECODE_SHAPES)) / 1e3
-    shape_us = {f"{N}x{K}": round(t / (args.steps * L) * 1e6, 3)
-                for (N, K), t in zip(DECODE_SHAPES, t_shape)}
     K_ = args.steps
-    gb_v = K_ * L * sum(gemv_bytes(1, N, K) for N, K in DECODE_SHAPES)
-    gb_q = K_ * L * sum(quant_bytes(N, K) for N, K in DECODE_SHAPES)
-    gb_d = K_ * L * sum(dequant_bytes(N, K) for N, K in DECODE_SHAPES)
-    gemv_gbs = gb_v / t_v / 1e9
+    # average launch time and bytes per launch of each decode shape
+    us_shape = [t / (K_ * len(by_shape[s])) * 1e6 for s, t in enumerate(t_shape)]
+    b_shape = [gemv_bytes(1, N, K) for N, K in DECODE_SHAPES]
+    shape_us = {f"{N}x{K}": round(u, 3) for (N, K), u in zip(DECODE_SHAPES, us_shape)}
+    # headline: the three decode shapes weighted equally
+    avg_gemv_bytes = sum(b_shape) / len(b_shape)
+    avg_gemv_us = sum(us_shape) / len(us_shape)
+    gemv_gbs = avg_gemv_bytes / (avg_gemv_us * 1e-6) / 1e9
+    # the whole stack (7 linears per layer)
+    gb_stack = K_ * sum(b_shape[si] for si in wshape)
+    stack_gbs = gb_stack / t_v / 1e9
+    gb_q = K_ * sum(quant_bytes(*DECODE_SHAPES[si]) for si in wshape)
+    gb_d = K_ * sum(dequant_bytes(*DECODE_SHAPES[si]) for si in wshape)
+    gb_in = K_ * sum(2 * DECODE_SHAPES[si][0] * DECODE_SHAPES[si][1] for si in wshape)
     gemm_tflops = K_ * 2.0 * Mp * Np * Kp / t_m / 1e12
-    avg_gemv_us = t_v / (K_ * nlaunch) * 1e6
-    avg_gemv_bytes = gb_v / (K_ * nlaunch)
 
     out = {
         "metric": METRIC,
@@ -261,14 +281,16 @@ def main():
         "dtype": "bf16 (NF4 storage, fp32 accumulate)",
         "data": "synthetic (seeded device draws, N(0,0.02) weights, N(0,1) activations)",
         "config": {
-            "workload": "decode GEMV M=1 over Llama-7B-shaped linears 4096x4096, 11008x4096, "
-                        "4096x11008 (NF4 blocksize 64, double quant), "
-                        f"{L} distinct layers per shape; plus prefill GEMM M=2048 N=K=8192",
+            "workload": "decode GEMV M=1 on Llama-7B-shaped linears 4096x4096, 11008x4096, "
+                        "4096x11008 (NF4 blocksize 64, double quant), every weight of a "
+                        f"{L}-layer stack (q,k,v,o,gate,up,down per layer, distinct weights, "
+                        "streamed from HBM); plus quantize and dequantize of the stack and a "
+                        "prefill GEMM M=2048 N=K=8192",
             "layers": L,
             "gemm": {"M": Mp, "N": Np, "K": Kp},
         },
         "roofline": {
-            "kernel": "gemv_valu_kernel",
+            "kernel": "gemv_kernel",
             "bound": "hbm",
             "achieved": round(avg_gemv_bytes / (avg_gemv_us * 1e-6) / 1e9, 1),
             "peak": HBM_PEAK_GBS,
@@ -284,9 +306,10 @@ def main():
         },
         "kernels": {
             "quantize_gbs": round(gb_q / t_q / 1e9, 1),
-            "quantize_input_read_gbs": round(K_ * L * sum(2 * N * K for N, K in DECODE_SHAPES) / t_q / 1e9, 1),
+            "quantize_input_read_gbs": round(gb_in / t_q / 1e9, 1),
             "dequantize_gbs": round(gb_d / t_d / 1e9, 1),
             "gemv_gbs": round(gemv_gbs, 1),
+            "gemv_stack_gbs": round(stack_gbs, 1),
             "gemv_avg_launch_us": round(avg_gemv_us, 3),
             "gemv_launch_us_by_shape": shape_us,
             "stage_ms_per_step": {"quantize": round(t_q / K_ * 1e3, 3),
