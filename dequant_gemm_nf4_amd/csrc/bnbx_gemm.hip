@@ -299,9 +299,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     // the compiler relaxes a builtin wait to what it believes this wave needs,
     // and it does not count the other waves reading these LDS writes.
     if (DQ)
-      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4)
     else
-      asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0x0F73);   // vmcnt(3)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
