@@ -2,41 +2,52 @@
 // (mlqm.cn bitsandbytes article, sec. 3.4: 4-bit storage, dequantize to BF16,
 // multiply in 16-bit with fp32 accumulation).
 //
-// Tiling.  A workgroup (4 waves, one per SIMD) owns a 256 x 256 tile of Y;
-// each wave a 128 x 128 quarter, i.e. 4 x 4 tiles of
-// v_mfma_f32_32x32x16_bf16 with the 256 accumulators per lane in AGPRs.  K is
-// walked in steps of 64 = one NF4 block per weight row, so a weight-tile row
-// shares one block scale per step.
+// Tiling.  A workgroup (4 waves, one per SIMD) owns a 256 x 256 tile of Y.
+// Wave w owns all 256 rows and the 64 columns [64 w, 64 w + 64): 8 x 2 tiles
+// of v_mfma_f32_32x32x16_bf16, 256 accumulators per lane in AGPRs.  K is
+// walked in steps of 64 = one NF4 block per weight row, so a weight row
+// shares one block scale per step; a step is four 16-wide substeps.
 //
-// Pipeline.  LDS holds two buffers of the X tile and of the dequantized
-// weight tile.
-//   - X goes from global memory straight into LDS (global_load_lds, 16 B per
-//     lane, no registers).  Its rows are 128 B with the eight 16-byte chunks
-//     of row r rotated by (r / 2) % 8, so that 16 lanes reading the same
-//     chunk of 16 consecutive rows hit 64 distinct banks.
-//   - Each thread owns one weight row: it stages the row's 32 packed bytes
-//     and block code/scale of a K step in registers, four steps ahead (four
-//     staging sets), and writes the row dequantized into LDS (rows padded to
-//     144 B).  The dequant is vector-only: the 16 values bf16(L[i] * scale)
-//     of the row's block form a byte table in 8 registers that v_perm_b32
-//     indexes by the 4-bit codes (no LDS lookups).
-// In step t a wave issues the X copy of step t+1 and the weight loads of step
-// t+4, then runs 64 MFMAs - the last substep of step t-1 (its operands were
-// read before the barrier, so the first MFMAs after the barrier wait for no
-// LDS read) and substeps 0..2 of step t - and between them dequantizes step
-// t+1's weights into the other buffer.  The step ends with one barrier
-// preceded by a wait for this wave's LDS writes and X copies only: the weight
-// loads, issued after the copies, stay in flight (the memory counter retires
-// in order).  Scheduling-group barriers lay each substep out as one MFMA
-// followed by a share of the LDS reads, vector ops and LDS writes, so that
-// vector and LDS work issues while the matrix core is busy.  Each LDS buffer
-// is its own object, picked at compile time, so the compiler can tell reads
-// of one buffer from copies in flight into another.  Steps past the end of K
-// load and write clamped (redundant) data into a buffer no MFMA reads.
+// Weights never touch LDS.  The B operand of a 32x32x16 MFMA gives lane l
+// column l % 32 and eight consecutive k of the 16; which eight k of the step
+// feed which lane half and substep is free, as long as X uses the same
+// assignment.  Lane half h takes, in substep s, the 8-wide k chunk 4h + s, so
+// over a step it needs bytes [16h, 16h + 16) of each of its two weight rows'
+// 32 packed bytes: one 16-byte load per row, whose four dwords are the four
+// substeps' operands.  Each wave therefore dequantizes exactly the weights it
+// multiplies, straight into MFMA operand registers, and every weight is
+// dequantized once per workgroup.  The dequant is vector-only: the 16 values
+// bf16(L[i] * scale) of a row's block form a byte table in 8 registers that
+// v_perm_b32 indexes by the 4-bit codes.
 //
-// Tile order is XCD-aware: workgroup b runs on XCD b % 8, so consecutive
-// tile ids (which share the same 256 rows of X) are given to the same XCD
-// and meet in its L2.
+// X goes from global memory straight into LDS (buffer_load ... lds, 16 B per
+// lane, no registers), two buffers.  Its rows are 128 B with the eight
+// 16-byte chunks of row r rotated by (r / 2) % 8, so that 16 lanes reading
+// the same chunk of 16 consecutive rows hit 64 distinct banks.
+//
+// Pipeline of step t (one scheduling region per substep, each laid out as
+// single MFMAs interleaved with LDS reads and vector ops):
+//   region 0: weight loads of step t+3, half the X copy of step t+1 (other
+//             buffer), operand reads of (t, 0), MFMAs of (t-1, 3), dequant of
+//             (t, 0);
+//   region s = 1..3: operand reads of (t, s), MFMAs of (t, s-1), dequant of
+//             (t, s); the rest of the X copy in region 1, the block tables of
+//             step t+1 in regions 2 (own row) and 3 (shared);
+//   then a wait for all of this wave's loads, X copies and LDS reads, and one
+//   barrier.  The weight loads go out before the copies: a copy's arrival in
+//   LDS is not ordered with later loads, so the memory counter can only be
+//   trusted down to zero.
+// Block codes come four steps at a time (one dword of four int8 codes per
+// row) when the shape allows it.  Each LDS buffer is its own object, picked
+// at compile time, so the compiler can tell reads of one buffer from copies
+// in flight into another.  Steps past the end of K load clamped (redundant)
+// data that no MFMA uses.
+//
+// Addresses are 32-bit offsets from buffer resources (per-lane parts fixed,
+// the per-step part a scalar); the host splits M so that the X offsets fit.
+// Tile order is XCD-aware: workgroup b runs on XCD b % 8, so consecutive tile
+// ids (which share the same 256 rows of X) go to the same XCD and meet in
+// its L2.
 #include <type_traits>
 
 #include "bnbx_device.hpp"
@@ -46,61 +57,106 @@ namespace bnbx {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int LDS_ROW = BK + 8;             // bf16 per weight-tile LDS row (144 B)
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
-constexpr int kABuf = BM * BK;              // bf16 elements per X buffer (128 B rows)
-constexpr int kBBuf = BN * LDS_ROW;         // bf16 elements per weight buffer
+constexpr int kABuf = BM * BK;   // bf16 elements per X buffer (128 B rows)
 
 // Scheduling-group masks (AMDGPU sched_group_barrier).
-constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100, kSgDsWrite = 0x200;
+constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgSalu = 0x004, kSgVmem = 0x010,
+              kSgDsRead = 0x100;
 
-// One thread's weight row for one K step.
-struct Stage {
-  uint4 w[2];   // 32 packed bytes (64 weights)
-  uint32_t q;   // int8 block code (double quant), as loaded (zero-extended byte)
-  float s;      // group scale (double quant) or block absmax
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// The 16 values bf16(L[i] * scale) of one row block, split into a table of
+// their high bytes (h[j] holds entries 4j..4j+3) and one of their low bytes.
+struct Tab16 {
+  uint32_t h[4], l[4];
 };
 
-template <bool DQ>
-__device__ __forceinline__ void load_stage(Stage& st, const uint8_t* __restrict__ packed,
-                                           const void* __restrict__ absmax,
-                                           const float* __restrict__ absmax2, int64_t gn,
-                                           int64_t rowK2, int64_t nkb, int64_t kb) {
-  kb = kb < nkb ? kb : nkb - 1;   // past the end: the last step again (never used)
-  const int64_t k0 = kb * BK;
-  const uint4* src = (const uint4*)(packed + gn * rowK2 + (k0 >> 1));
-  st.w[0] = src[0];
-  st.w[1] = src[1];
-  const int64_t blk = gn * nkb + kb;
-  if (DQ) {
-    // Kept as the raw byte: a sign extension here would be an instruction on
-    // the loaded value that the compiler may place before the step's barrier
-    // (making it wait for these loads); it is done where the scale is formed.
-    st.q = ((const uint8_t*)absmax)[blk];
-    st.s = absmax2[blk >> 8];
-  } else {
-    st.q = 0u;
-    st.s = ((const float*)absmax)[blk];
+__device__ __forceinline__ Tab16 make_tab16(const LevelTable& lv, float sc) {
+  uint32_t pk[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) pk[k] = pack_bf16x2(lv.level[2 * k] * sc, lv.level[2 * k + 1] * sc);
+  Tab16 t;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    t.h[j] = perm(pk[2 * j + 1], pk[2 * j], 0x07050301u);
+    t.l[j] = perm(pk[2 * j + 1], pk[2 * j], 0x06040200u);
+  }
+  return t;
+}
+
+// 8 weights (one packed dword: byte j = codes of weights 2j (high nibble) and
+// 2j+1) -> 4 dwords of bf16 pairs in weight order.  Four 4-bit codes held one
+// per byte select their entries with v_perm_b32 from each half of the table
+// (entries 0-7 and 8-15); a per-byte mask made from bit 3 of the codes
+// (v_perm's sign-replicating selectors 8-11) picks between the halves.
+__device__ __forceinline__ void decode8(uint32_t d, const Tab16& t, uint32_t* o) {
+  auto pick = [&](uint32_t sel, uint32_t m, const uint32_t* tt) {
+    const uint32_t a = perm(tt[1], tt[0], sel), b = perm(tt[3], tt[2], sel);
+    return (m & b) | (~m & a);
+  };
+  const uint32_t sE = (d >> 4) & 0x07070707u, sO = d & 0x07070707u;
+  const uint32_t mE = perm(d << 8, d, 0x090B080Au);     // bit 7 of each byte
+  const uint32_t d4 = d << 4;
+  const uint32_t mO = perm(d4 << 8, d4, 0x090B080Au);   // bit 3 of each byte
+  const uint32_t hiE = pick(sE, mE, t.h), loE = pick(sE, mE, t.l);
+  const uint32_t hiO = pick(sO, mO, t.h), loO = pick(sO, mO, t.l);
+  const uint32_t t0 = perm(hiE, loE, 0x05010400u), t1 = perm(hiE, loE, 0x07030602u);
+  const uint32_t u0 = perm(hiO, loO, 0x05010400u), u1 = perm(hiO, loO, 0x07030602u);
+  o[0] = perm(u0, t0, 0x05040100u);
+  o[1] = perm(u0, t0, 0x07060302u);
+  o[2] = perm(u1, t1, 0x05040100u);
+  o[3] = perm(u1, t1, 0x07060302u);
+}
+
+// One K step of a lane's weights: 16 packed bytes (32 weights) of each of
+// its two rows.
+struct WSet {
+  u32x4_t w[2];
+};
+// Block scale of a lane's own row: the int8 block code(s) as loaded (one per
+// step, or four per dword) and the group scale (double quant), or the fp32
+// block absmax bits (no double quant).
+struct QSet {
+  uint32_t q;
+  float s;
+};
+
+// Both rows' tables from each lane's own one: lanes l and l + 32 hold the
+// tables of rows 0 and 1 of lane l % 32; v_permlane32_swap exchanges the
+// upper half of its first operand with the lower half of its second, so
+// with both operands the own table its two results are row 0's table and
+// row 1's table in every lane.
+__device__ __forceinline__ void share_tab16(const Tab16& own, Tab16* t) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const auto h = __builtin_amdgcn_permlane32_swap(own.h[k], own.h[k], false, false);
+    const auto l = __builtin_amdgcn_permlane32_swap(own.l[k], own.l[k], false, false);
+    t[0].h[k] = h[0];
+    t[1].h[k] = h[1];
+    t[0].l[k] = l[0];
+    t[1].l[k] = l[1];
   }
 }
 
-template <bool DQ>
+template <bool DQ, bool Q4>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ packed,
     const void* __restrict__ absmax, const float* __restrict__ absmax2,
     const float* __restrict__ mean, int M, int N, int K, uint16_t* __restrict__ y, int64_t ldy,
     int tiles_m, int tiles_n, LevelTable lv) {
-  // Every buffer is an LDS object of its own and is picked at compile time,
-  // so that the compiler can tell reads of one buffer from the X copies in
-  // flight into another (a read that might alias a copy waits for all of them).
-  __shared__ __attribute__((aligned(16))) uint16_t As0[kABuf], As1[kABuf];   // X, rotated chunks
-  __shared__ __attribute__((aligned(16))) uint16_t Bs0[kBBuf], Bs1[kBBuf];   // weights, padded rows
+  __shared__ __attribute__((aligned(16))) uint16_t As0[kABuf], As1[kABuf];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases in SGPRs
-  const int wm = wave >> 1, wn = wave & 1;
+  const int half = lane >> 5, col = lane & 31;
 
   // XCD-aware tile id: workgroups b, b+8, b+16, ... share an XCD.
   const int ntiles = tiles_m * tiles_n;
@@ -108,256 +164,296 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   const int b = blockIdx.x;
   const int tile = (b % kXcds) * per_xcd + b / kXcds;
   if (tile >= ntiles) return;
-  const int64_t m0 = (int64_t)(tile / tiles_n) * BM;
-  const int64_t n0 = (int64_t)(tile % tiles_n) * BN;
+  const int m0 = (tile / tiles_n) * BM;
+  const int n0 = (tile % tiles_n) * BN;
 
   const float mu = DQ ? *mean : 0.0f;
-  const int64_t rowK2 = (int64_t)(K >> 1);
-  const int64_t nkb = K >> 6;
+  const uint32_t rowK2 = (uint32_t)K >> 1;   // packed bytes per weight row
+  const int nkb = K >> 6;
 
-  const int64_t gnr = n0 + tid;
-  const bool bok = gnr < N;
-  const int64_t gn = bok ? gnr : N - 1;
+  // The lane's weight rows (B columns) n0 + 64 w + 32 j + l % 32, j = 0, 1;
+  // rows past N are clamped to N-1 (their tables are zero).
+  uint32_t gn[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + wave * 64 + 32 * j + col;
+    gn[j] = (uint32_t)(n < N ? n : N - 1);
+  }
+  // The lane's own row for block scales and tables: n0 + 64 w + l (row j = h
+  // of lane l % 32).
+  const int no = n0 + wave * 64 + lane;
+  const bool boko = no < N;
+  const uint32_t qvoff = (uint32_t)(boko ? no : N - 1) * (uint32_t)nkb;   // its first block
+  const uint32_t nblocks = (uint32_t)N * (uint32_t)nkb;
+  const rsrc_t rw = make_rsrc(packed, (uint32_t)N * rowK2);
+  const rsrc_t rq = make_rsrc(absmax, DQ ? nblocks : nblocks * 4u);
+  const rsrc_t rg = make_rsrc(absmax2, DQ ? (nblocks + 255u) / 256u * 4u : 4u);
+  uint32_t wvoff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) wvoff[j] = gn[j] * rowK2 + 16u * (uint32_t)half;
 
-  f32x16_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  auto load = [&](Stage& st, int64_t kb) {
-    load_stage<DQ>(st, packed, absmax, absmax2, gn, rowK2, nkb, kb);
-  };
-  // X copy of one K step into LDS buffer `buf`: wave w copies rows
+  // X copy of one K step into an LDS buffer: wave w copies rows
   // [64 w, 64 w + 64) in 8 instructions of 8 rows; lane l fills chunk slot
   // l % 8 of row l / 8 with the chunk that the rotation puts there.  Rows past
   // M are clamped to row M-1 (they only feed rows of Y that are never stored).
-  const int xr_l = lane >> 3, xslot = lane & 7;
-  auto copy_x = [&](uint16_t* xbuf, int64_t kb) {
-    kb = kb < nkb ? kb : nkb - 1;
-    const int64_t k0 = kb * BK;
+  const rsrc_t rx = make_rsrc(x, (uint32_t)((int64_t)(M - 1) * ldx * 2 + (int64_t)K * 2));
+  uint32_t xvoff[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = wave * 64 + i * 8 + xr_l;
-      const int chunk = xslot ^ ((r >> 1) & 7);
-      int64_t gm = m0 + r;
-      gm = gm < M ? gm : M - 1;
-      __builtin_amdgcn_global_load_lds((const void*)(x + gm * ldx + k0 + chunk * 8),
-                                       (void __attribute__((address_space(3)))*)(xbuf + (wave * 64 + i * 8) * BK),
-                                       16, 0, 0);
-    }
-  };
-  // Quarter p (0..3) of the weight row (16 weights), dequantized.
-  auto scale_of = [&](const Stage& st) {
-    // (float)(int8)q = (float)(int32)(q << 24) * 2^-24, both steps exact
-    const float qf = (float)(int32_t)(st.q << 24) * 0x1p-24f;
-    const float sc = DQ ? __builtin_fmaf(qf, st.s * (1.0f / 127.0f), mu) : st.s;
-    return bok ? sc : 0.0f;
-  };
-  // Vector-only dequant.  The 16 values bf16(L[i] * scale) of the row's block
-  // are split into a table of their high bytes (h[j] holds entries 4j..4j+3)
-  // and one of their low bytes; four 4-bit codes held one per byte select
-  // their entries with v_perm_b32 from each half (entries 0-7 and 8-15) and a
-  // per-byte mask made from bit 3 of the codes (v_perm's sign-replicating
-  // selectors 8-11) picks between the halves.
-  struct Tab16 {
-    uint32_t h[4], l[4];
-  };
-  auto make_tab16 = [&](float sc) {
-    uint32_t pk[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) pk[k] = pack_bf16x2(lv.level[2 * k] * sc, lv.level[2 * k + 1] * sc);
-    Tab16 t;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      t.h[j] = perm(pk[2 * j + 1], pk[2 * j], 0x07050301u);
-      t.l[j] = perm(pk[2 * j + 1], pk[2 * j], 0x06040200u);
-    }
-    return t;
-  };
-  // 8 weights (one packed dword: byte j = codes of weights 2j (high nibble)
-  // and 2j+1) -> 4 dwords of bf16 pairs in weight order.
-  auto decode8 = [&](uint32_t d, const Tab16& t, uint32_t* o) {
-    auto pick = [&](uint32_t sel, uint32_t m, const uint32_t* tt) {
-      const uint32_t a = perm(tt[1], tt[0], sel), b = perm(tt[3], tt[2], sel);
-      return (m & b) | (~m & a);
-    };
-    const uint32_t sE = (d >> 4) & 0x07070707u, sO = d & 0x07070707u;
-    const uint32_t mE = perm(d << 8, d, 0x090B080Au);          // bit 7 of each byte
-    const uint32_t d4 = d << 4;
-    const uint32_t mO = perm(d4 << 8, d4, 0x090B080Au);        // bit 3 of each byte
-    const uint32_t hiE = pick(sE, mE, t.h), loE = pick(sE, mE, t.l);
-    const uint32_t hiO = pick(sO, mO, t.h), loO = pick(sO, mO, t.l);
-    const uint32_t t0 = perm(hiE, loE, 0x05010400u), t1 = perm(hiE, loE, 0x07030602u);
-    const uint32_t u0 = perm(hiO, loO, 0x05010400u), u1 = perm(hiO, loO, 0x07030602u);
-    o[0] = perm(u0, t0, 0x05040100u);
-    o[1] = perm(u0, t0, 0x07060302u);
-    o[2] = perm(u1, t1, 0x05040100u);
-    o[3] = perm(u1, t1, 0x07060302u);
-  };
-  auto put_w_valu = [&](const Stage& st, uint16_t* wbuf, int p, const Tab16& t) {
-    const uint32_t d0 = p == 0 ? st.w[0].x : p == 1 ? st.w[0].z : p == 2 ? st.w[1].x : st.w[1].z;
-    const uint32_t d1 = p == 0 ? st.w[0].y : p == 1 ? st.w[0].w : p == 2 ? st.w[1].y : st.w[1].w;
-    uint32_t o[8];
-    decode8(d0, t, o);
-    decode8(d1, t, o + 4);
-    uint16_t* bw = wbuf + tid * LDS_ROW + p * 16;
-    *(uint4*)(bw) = make_uint4(o[0], o[1], o[2], o[3]);
-    *(uint4*)(bw + 8) = make_uint4(o[4], o[5], o[6], o[7]);
-  };
-  // Prologue: step 0 into buffer 0; the weights of steps 1..3 staged in sets
-  // 1..3.
-  Stage s0, s1, s2, s3;
-  copy_x(As0, 0);
-  load(s0, 0);
-  {
-    const Tab16 t = make_tab16(scale_of(s0));
-#pragma unroll
-    for (int p = 0; p < 4; ++p) put_w_valu(s0, Bs0, p, t);
+  for (int i = 0; i < 8; ++i) {
+    const int r = wave * 64 + i * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+    int gm = m0 + r;
+    gm = gm < M ? gm : M - 1;
+    xvoff[i] = (uint32_t)(((int64_t)gm * ldx + chunk * 8) * 2);
   }
-  load(s1, 1);
-  load(s2, 2);
-  load(s3, 3);
-  __syncthreads();
+  auto copy_x = [&](uint16_t* xbuf, int kb, int i0, int i1) {
+    kb = kb < nkb ? kb : nkb - 1;
+#pragma unroll
+    for (int i = i0; i < i1; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (void __attribute__((address_space(3)))*)(xbuf + (wave * 64 + i * 8) * BK), 16,
+          xvoff[i], (uint32_t)kb * (BK * 2), 0, 0);
+  };
+  auto load_w = [&](WSet& s, int kb) {
+    kb = kb < nkb ? kb : nkb - 1;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      s.w[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, wvoff[j], (uint32_t)kb * 32u, 0);
+  };
+  // Own-row scale of one step (Q4 = false) or of the four steps 4g..4g+3 (Q4).
+  auto load_q = [&](QSet& s, int idx) {
+    if (Q4) {
+      const int g = idx < (nkb >> 2) ? idx : (nkb >> 2) - 1;
+      const uint32_t blk = qvoff + 4u * (uint32_t)g;
+      s.q = __builtin_amdgcn_raw_buffer_load_b32(rq, blk, 0, 0);
+      s.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, (blk >> 8) * 4u, 0, 0));
+    } else {
+      const int kb = idx < nkb ? idx : nkb - 1;
+      const uint32_t blk = qvoff + (uint32_t)kb;
+      if (DQ) {
+        // Kept as the raw byte; the sign extension is done where the scale
+        // is formed.
+        s.q = __builtin_amdgcn_raw_buffer_load_b8(rq, blk, 0, 0);
+        s.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, (blk >> 8) * 4u, 0, 0));
+      } else {
+        s.q = __builtin_amdgcn_raw_buffer_load_b32(rq, blk * 4u, 0, 0);
+        s.s = 0.0f;
+      }
+    }
+  };
+  // Own-row block scale from code byte `byte` of the set.
+  auto scale_of = [&](const QSet& s, int byte) {
+    float sc;
+    if (DQ) {
+      // (float)(int8)q = (float)(int32)(q << 24) * 2^-24, both steps exact
+      const uint32_t t = (s.q >> (8 * byte)) << 24;
+      const float qf = (float)(int32_t)t * 0x1p-24f;
+      sc = __builtin_fmaf(qf, s.s * (1.0f / 127.0f), mu);
+    } else {
+      sc = __builtin_bit_cast(float, s.q);
+    }
+    return boko ? sc : 0.0f;
+  };
 
-  // MFMA operands.  A: lane l reads row wm*128 + i*32 + l%32, 16-byte chunk
-  // 2*ks + l/32, at its rotated slot (the rotation (r/2)%8 is the same for
-  // all i).  B: weight rows wn*128 + j*32 + l%32, padded rows.
-  const int arow_op = wm * 128 + (lane & 31);
-  const int akey = (arow_op >> 1) & 7;
+  f32x16_t acc[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  // A operands: lane l reads row 32 i + l % 32, chunk 4 h + s at its rotated
+  // slot (the rotation (r / 2) % 8 does not depend on i).
   uint32_t aoff[BK / 16];
 #pragma unroll
-  for (int ks = 0; ks < BK / 16; ++ks)
-    aoff[ks] = (uint32_t)(arow_op * BK + (((2 * ks + (lane >> 5)) ^ akey) << 3));
-  const int brow_op = wn * 128 + (lane & 31);
-  const int kcol = (lane >> 5) * 8;
-
-  // One K step.  Its MFMAs are the last substep of step kb-1 (operands read
-  // before the barrier) and substeps 0..2 of step kb; substep 3 of step kb
-  // opens the next step.  So each barrier is followed by 16 MFMAs that need
-  // no LDS read, while the first operands of the new buffer are read.
-  // Between the MFMAs: the dequantized weights of step kb+1 (from staging set
-  // `sn`) are written to the other buffer; `sl` is refilled with step kb+4.
-  // R[0] / R[1] hold operands, R[0] holding substep 3 of the previous step.
-  bf16x8_t av[2][4], bv[2][4];
-  auto read_ops = [&](const uint16_t* a, const uint16_t* bb, int ks, int r) {
+  for (int s = 0; s < BK / 16; ++s)
+    aoff[s] = (uint32_t)(col * BK + (((4 * half + s) ^ ((col >> 1) & 7)) << 3));
+  bf16x8_t av[2][8], bv[2][2];
+  auto read_ops = [&](const uint16_t* a, int s, int r) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      av[r][i] = *(const bf16x8_t*)(a + aoff[ks] + i * 32 * BK);
-      bv[r][i] = *(const bf16x8_t*)(bb + (brow_op + i * 32) * LDS_ROW + ks * 16 + kcol);
-    }
+    for (int i = 0; i < 8; ++i) av[r][i] = *(const bf16x8_t*)(a + aoff[s] + i * 32 * BK);
   };
   auto mfmas = [&](int r) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[r][i], bv[r][j], acc[i][j], 0, 0, 0);
   };
-  auto step = [&](auto buf_tag, auto first_tag, int64_t kb, Stage& sn, Stage& sl) {
-    constexpr int buf = decltype(buf_tag)::value;      // kb % 2
-    constexpr bool first = decltype(first_tag)::value; // no step kb-1
-    uint16_t* const a = buf ? As1 : As0;
-    uint16_t* const bb = buf ? Bs1 : Bs0;
-    uint16_t* const an = buf ? As0 : As1;
-    uint16_t* const bn = buf ? Bs0 : Bs1;
-    // The staged registers of step kb+1 arrived before the last barrier.  Using
-    // them here, before this step's copies and loads are issued, makes the
-    // compiler's wait for them land where nothing is outstanding; a first use
-    // after the copies would wait for the copies too (the counter is in order).
-    asm volatile("" ::"v"(sn.w[0].x), "v"(sn.w[0].y), "v"(sn.w[0].z), "v"(sn.w[0].w),
-                 "v"(sn.w[1].x), "v"(sn.w[1].y), "v"(sn.w[1].z), "v"(sn.w[1].w), "v"(sn.q),
-                 "v"(sn.s));
-    copy_x(an, kb + 1);
-    __builtin_amdgcn_sched_barrier(0);   // the weight loads go out after the X copies
-    load(sl, kb + 4);
-    const Tab16 t16 = make_tab16(scale_of(sn));
+  auto dequant = [&](const WSet& w, const Tab16* t, int s, int r) {
 #pragma unroll
-    for (int ss = 0; ss < BK / 16; ++ss) {
-      read_ops(a, bb, ss, (ss + 1) & 1);          // substep ss of step kb
-      if (!first || ss > 0) mfmas(ss & 1);        // substep 3 of kb-1, then 0..2 of kb
-      put_w_valu(sn, bn, ss, t16);                // a quarter of step kb+1's weights
-      // 16 x {1 MFMA, an operand read (first 8), 4 vector ops}; the two LDS
-      // writes after MFMAs 10 and 11, so that they have retired when the next
-      // substep waits for its operands (the LDS counter is in order).
+    for (int j = 0; j < 2; ++j) {
+      uint32_t o[4];
+      decode8(w.w[j][s], t[j], o);
+      u32x4_t v = {o[0], o[1], o[2], o[3]};
+      bv[r][j] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  };
+
+  // Staging: four weight sets (step t in set t % 4), scales either four
+  // per-step sets alike or two 4-step groups (current and next).
+  WSet ws0, ws1, ws2, ws3;
+  QSet qs0, qs1, qs2, qs3;
+  Tab16 tA[2], tB[2];
+  auto wset = [&](int i) -> WSet& { return i == 0 ? ws0 : i == 1 ? ws1 : i == 2 ? ws2 : ws3; };
+  auto qset = [&](int i) -> QSet& { return i == 0 ? qs0 : i == 1 ? qs1 : i == 2 ? qs2 : qs3; };
+
+  // Prologue: X of step 0, weights of steps 0..2, scales, tables of step 0.
+  copy_x(As0, 0, 0, 8);
+  load_w(ws0, 0);
+  load_w(ws1, 1);
+  load_w(ws2, 2);
+  if (Q4) {
+    load_q(qs0, 0);   // current group
+    load_q(qs1, 1);   // next group
+  } else {
+    load_q(qs0, 0);
+    load_q(qs1, 1);
+    load_q(qs2, 2);
+  }
+  share_tab16(make_tab16(lv, scale_of(qs0, 0)), tA);
+  Tab16 own;
+  __syncthreads();
+
+  // One K step t with t % 4 == KM (so that every set is fixed at compile
+  // time).  `tc` holds step t's tables, `tn` receives step t+1's.
+  auto step = [&](auto km_tag, auto first_tag, int kb, Tab16* tc, Tab16* tn) {
+    constexpr int KM = decltype(km_tag)::value;
+    constexpr bool first = decltype(first_tag)::value;   // no step t-1
+    uint16_t* const a = (KM & 1) ? As1 : As0;
+    uint16_t* const an = (KM & 1) ? As0 : As1;
+    WSet& wc = wset(KM);
+    WSet& wl = wset((KM + 3) & 3);
+    constexpr int kn = (KM + 1) & 3;   // (t + 1) % 4: code byte of step t+1
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      if (s == 0) {
+        // Loads first, then the X copies, all waited for at the end of the
+        // step (the copies' completion into LDS is not ordered with the
+        // loads', so no wait may leave loads in flight).
+        load_w(wl, kb + 3);
+        if (Q4) {
+          if (kn == 0) {
+            // Step t+1 opens a new group of four: move to the next group's
+            // codes (loaded four steps ago) and fetch the one after it.
+            qs0 = qs1;
+            load_q(qs1, (kb + 1) / 4 + 1);
+          }
+        } else {
+          load_q(qset((KM + 3) & 3), kb + 3);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        copy_x(an, kb + 1, 0, 4);
+      }
+      if (s == 1) copy_x(an, kb + 1, 4, 8);
+      read_ops(a, s, s & 1);                      // substep s of step t
+      if (!first || s > 0) mfmas((s + 1) & 1);    // substep 3 of t-1, then 0..2 of t
+      dequant(wc, tc, s, s & 1);
+      // Tables of step t+1: the own row's in region 2, shared in region 3.
+      if (s == 2) own = make_tab16(lv, Q4 ? scale_of(qs0, kn) : scale_of(qset(kn), 0));
+      if (s == 3) share_tab16(own, tn);
+      // 16 x {1 MFMA, an operand read (first 8), copies, vector ops}.
 #pragma unroll
       for (int g = 0; g < 16; ++g) {
         __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
         if (g < 8) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgValu, 4, 0);
-        if (g == 10 || g == 11) __builtin_amdgcn_sched_group_barrier(kSgDsWrite, 1, 0);
+        // A copy with the scalar move that sets its LDS address.
+        if (s < 2 && (g & (s == 0 ? 1 : 3)) == 0) {
+          __builtin_amdgcn_sched_group_barrier(kSgSalu, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
+        }
+        if (s == 2)
+          __builtin_amdgcn_sched_group_barrier(kSgValu, 6, 0);
+        else
+          __builtin_amdgcn_sched_group_barrier(kSgValu, 4, 0);
       }
       __builtin_amdgcn_sched_barrier(0);   // one substep per scheduling region
     }
-    // End of step: this step's LDS writes done and its X copies landed.  The
-    // copies were issued before the weight loads of step kb+4 and the memory
-    // counter retires in order, so waiting until only those loads are left
-    // (4 instructions, 3 without double quant) covers the copies while the
-    // weight loads stay in flight across the barrier.  Written as inline asm:
-    // the compiler relaxes a builtin wait to what it believes this wave needs,
-    // and it does not count the other waves reading these LDS writes.
-    if (DQ)
-      __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4)
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F73);   // vmcnt(3)
+    // End of step: this wave's X copies landed (with the loads issued before
+    // them) and its operand reads done.  The memory wait is a builtin, so
+    // that the compiler knows the copies are complete; the LDS wait and the
+    // barrier are inline asm: the compiler relaxes a builtin wait to what it
+    // believes this wave needs, and it does not count the other waves.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
+  using K0 = std::integral_constant<int, 0>;
+  using K1 = std::integral_constant<int, 1>;
+  using K2 = std::integral_constant<int, 2>;
+  using K3 = std::integral_constant<int, 3>;
   using F0 = std::integral_constant<bool, false>;
   using F1 = std::integral_constant<bool, true>;
-  // Four staging sets rotate (step t writes set (t+1)%4 and refills set t%4),
-  // two LDS buffers alternate: after the first step, the loop is unrolled four
-  // times so that both are fixed at compile time.
-  step(B0{}, F1{}, 0, s1, s0);
-  int64_t kb = 1;
+  step(K0{}, F1{}, 0, tA, tB);
+  int kb = 1;
   for (; kb + 3 < nkb; kb += 4) {
-    step(B1{}, F0{}, kb, s2, s1);
-    step(B0{}, F0{}, kb + 1, s3, s2);
-    step(B1{}, F0{}, kb + 2, s0, s3);
-    step(B0{}, F0{}, kb + 3, s1, s0);
+    step(K1{}, F0{}, kb, tB, tA);
+    step(K2{}, F0{}, kb + 1, tA, tB);
+    step(K3{}, F0{}, kb + 2, tB, tA);
+    step(K0{}, F0{}, kb + 3, tA, tB);
   }
-  if (kb < nkb) step(B1{}, F0{}, kb, s2, s1);
-  if (kb + 1 < nkb) step(B0{}, F0{}, kb + 1, s3, s2);
-  if (kb + 2 < nkb) step(B1{}, F0{}, kb + 2, s0, s3);
-  mfmas(0);   // substep 3 of the last step
+  if (kb < nkb) step(K1{}, F0{}, kb, tB, tA);
+  if (kb + 1 < nkb) step(K2{}, F0{}, kb + 1, tA, tB);
+  if (kb + 2 < nkb) step(K3{}, F0{}, kb + 2, tB, tA);
+  mfmas(1);   // substep 3 of the last step
 
   // D layout of a 32x32 MFMA tile: lane l, value v -> column l%32,
   // row 8*(v/4) + 4*(l/32) + v%4.
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j) {
+      const int c = n0 + wave * 64 + 32 * j + col;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t row = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const int64_t col = n0 + wn * 128 + j * 32 + (lane & 31);
-        if (row < M && col < N) y[row * ldy + col] = f32_to_bf16(acc[i][j][v]);
+        const int r = m0 + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+        if (r < M && c < N) y[(int64_t)r * ldy + c] = f32_to_bf16(acc[i][j][v]);
       }
+    }
 }
 
+template <bool DQ, bool Q4>
+void launch_one(const uint16_t* x, int64_t ldx, const uint8_t* packed, const void* absmax,
+                const float* absmax2, const float* mean, int M, int N, int K, uint16_t* y,
+                int64_t ldy, hipStream_t stream) {
+  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  const int per_xcd = (tm * tn + kXcds - 1) / kXcds;
+  hipLaunchKernelGGL((gemm_kernel<DQ, Q4>), dim3((unsigned)(per_xcd * kXcds)), dim3(kThreads), 0,
+                     stream, x, ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, tm, tn,
+                     level_table());
+}
 
 }  // namespace
 
 hipError_t launch_gemm(const uint16_t* x, int64_t ldx, const uint8_t* packed, const void* absmax,
                        const float* absmax2, const float* mean, int double_quant, int M, int N,
                        int K, uint16_t* y, int64_t ldy, hipStream_t stream) {
-  const int64_t tm = ((int64_t)M + BM - 1) / BM, tn = ((int64_t)N + BN - 1) / BN;
-  const int64_t ntiles = tm * tn;
-  if (ntiles > (int64_t)1 << 30) return hipErrorNotSupported;
-  const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
-  const unsigned grid = (unsigned)(per_xcd * kXcds);
-  if (double_quant)
-    hipLaunchKernelGGL(gemm_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, x, ldx,
-                       packed, absmax, absmax2, mean, M, N, K, y, ldy, (int)tm, (int)tn,
-                       level_table());
-  else
-    hipLaunchKernelGGL(gemm_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, x, ldx,
-                       packed, absmax, absmax2, mean, M, N, K, y, ldy, (int)tm, (int)tn,
-                       level_table());
-  return hipGetLastError();
+  // Buffer offsets are 32-bit: the weights and their scales must fit, and M
+  // is walked in slabs whose X rows do.
+  const int64_t kLimit = (int64_t)1 << 31;
+  if ((int64_t)N * (K / 2) >= kLimit) return hipErrorNotSupported;
+  int64_t slab = (kLimit - (int64_t)K * 2) / (ldx * 2);
+  slab = slab / BM * BM;
+  if (slab < BM) return hipErrorNotSupported;
+  const int nkb = K / 64;
+  // Four block codes per dword load: needs whole groups of four blocks per
+  // row (then four blocks never straddle a group of 256) and an aligned
+  // code array.
+  const bool q4 = double_quant && nkb % 4 == 0 && ((uintptr_t)absmax & 3) == 0;
+  for (int64_t r0 = 0; r0 < M; r0 += slab) {
+    const int m = (int)(M - r0 < slab ? M - r0 : slab);
+    const uint16_t* xs = x + r0 * ldx;
+    uint16_t* ys = y + r0 * ldy;
+    if (!double_quant)
+      launch_one<false, false>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys, ldy, stream);
+    else if (q4)
+      launch_one<true, true>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys, ldy, stream);
+    else
+      launch_one<true, false>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys, ldy, stream);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace bnbx
