@@ -78,10 +78,20 @@ struct Tab16 {
   uint32_t h[4], l[4];
 };
 
+// The codebook's ends and middle are exactly -1 (L[0]), 0 (L[7]) and +1
+// (L[15]), so those three products need no multiply: -sc, a zero with sc's
+// sign, and sc.
 __device__ __forceinline__ Tab16 make_tab16(const LevelTable& lv, float sc) {
+  const uint32_t sb = __builtin_bit_cast(uint32_t, sc);
+  const float neg = __builtin_bit_cast(float, sb ^ 0x80000000u);
+  const float zero = __builtin_bit_cast(float, sb & 0x80000000u);
   uint32_t pk[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) pk[k] = pack_bf16x2(lv.level[2 * k] * sc, lv.level[2 * k + 1] * sc);
+  for (int k = 0; k < 8; ++k) {
+    const float a = k == 0 ? neg : lv.level[2 * k] * sc;
+    const float b = k == 3 ? zero : k == 7 ? sc : lv.level[2 * k + 1] * sc;
+    pk[k] = pack_bf16x2(a, b);
+  }
   Tab16 t;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
