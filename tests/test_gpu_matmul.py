@@ -149,3 +149,51 @@ def test_gemv_equals_gemm_across_m():
         a = run("gemv", x, M, K, q)
         b = run("gemm", x, M, K, q)
         assert oracle.rel_frobenius(a, b) <= TOL
+
+
+def test_gemm_x_past_32bit_offsets_sampled_rows():
+    """X of more than 2 GiB (M = 131372, K = 8192, N = 300): the GEMM addresses
+    X with 32-bit buffer offsets and walks M in slabs that keep them in range.
+    Rows at both sides of every slab seam the offsets force (multiples of
+    130816 rows here), the ends and random rows are checked against the
+    oracle.  X comes from a seeded device generator (2.15 GB would take the
+    host generator minutes); the checked rows are copied back as they are."""
+    N, K, M = 300, 8192, 131072 + 300
+    w = synth.normal_bf16((N, K), 0.02, 7900)
+    ref, q = setup(w, (N, K), True, check_state=False)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7901)
+    x = torch.randn((M, K), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    y = T.gemm(x, q)
+    torch.cuda.synchronize()
+    seam = (2 ** 31 - 2 * K) // (2 * K) // 256 * 256
+    rows = {0, 1, M - 2, M - 1}
+    for s in range(seam, M, seam):
+        rows.update({s - 2, s - 1, s, s + 1})
+    rows.update(np.random.default_rng(7902).choice(M, 24, replace=False).tolist())
+    rows = np.array(sorted(rows))
+    idx = torch.from_numpy(rows).cuda()
+    xs = host_bits(x.index_select(0, idx)).reshape(len(rows), K)
+    got = y_of(y.index_select(0, idx))
+    del x, y
+    torch.cuda.empty_cache()
+    err = oracle.rel_frobenius(got, ref_product(xs, ref, N, K))
+    assert err <= TOL, err
+
+
+def test_gemm_weights_past_32bit_offsets_rejected():
+    """Weights of 2^31 packed bytes or more (N*K/2 >= 2^31) are outside what the
+    GEMM's 32-bit offsets reach: the call returns BNBX_E_UNSUPPORTED before any
+    launch (checked with small buffers, which are never touched)."""
+    import dequant_gemm_nf4_amd as B
+    N, K = 65536, 65536
+    q = T.empty_quantized((64, 64), True)
+    st = q.state
+    st.n = N * K
+    x = torch.zeros((1, K), dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros((1, N), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(B.BnbxError) as e:
+        B.bnbx_gemm_nf4(x, K, q.packed, st, 1, N, K, y, N)
+    assert e.value.status == B.BNBX_E_UNSUPPORTED
+    torch.cuda.synchronize()
