@@ -374,6 +374,211 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void gemv_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// 4 < M <= 16: the weights streamed once into v_mfma_f32_16x16x32_bf16.
+//
+// A workgroup of 16 waves takes groups of 16 weight rows (16 columns of Y)
+// in turn; wave w owns the K slice of blocks [w nkb / 16, (w+1) nkb / 16)
+// (at most BPW blocks) and keeps its X slice for all 16 rows of X in
+// registers as MFMA A operands.  In an MFMA, lane l supplies column l % 16
+// and eight k of the 32; the 32 k of each MFMA are one half of one block,
+// lane quarter q taking k [16q + 8h, 16q + 8h + 8) of half h, so a lane needs
+// 8 packed bytes per block of its row (one 8-byte load) and every MFMA sits
+// inside one block.  The B operand is the bf16 levels from the byte -> pair
+// table (as in gemv_kernel, no per-weight arithmetic); a block's two MFMAs
+// go to a zeroed accumulator that is then scaled by the block scale of the
+// lane's column (its own row's) and added to the running sums.  The 16
+// waves' partial sums of a row group meet in LDS.
+// ---------------------------------------------------------------------------
+constexpr int kMfWaves = 16;
+
+template <int BPW, int GD, int SM>
+__global__ __launch_bounds__(kMfWaves * 64, 1) void gemv_mfma_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ packed,
+    const void* __restrict__ absmax, const float* __restrict__ absmax2,
+    const float* __restrict__ mean, int M, int N, int K, uint16_t* __restrict__ y, int64_t ldy,
+    LevelTable lv) {
+  constexpr bool DQ = SM != kScaleF32;
+  // Table at LDS offset 0 (its addresses are v_perm results), then two
+  // buffers of the waves' partial sums (16 waves x 64 lanes x 4 values).
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kTabBytes + 2 * kMfWaves * 1024];
+  unsigned char* const tab = smem;
+  float* const red = (float*)(smem + kTabBytes);
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int c = lane & 15, q = lane >> 4;
+  const int nkb = K >> 6;
+  const int b0 = wave * nkb / kMfWaves;
+  const int nbw = (wave + 1) * nkb / kMfWaves - b0;   // blocks of this wave, <= BPW
+  const uint32_t rowK2 = (uint32_t)K >> 1;
+  const int ngroups = (N + 15) >> 4;
+
+  // X slice: A operand of half h of block i, lane (row l % 16, quarter q):
+  // X[row][64 (b0 + i) + 16 q + 8 h ..+8]; rows >= M read as zero.
+  const rsrc_t rx = make_rsrc(x, (uint32_t)((int64_t)(M - 1) * ldx * 2 + (int64_t)K * 2));
+  bf16x8_t xa[BPW][2];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (i < nbw)
+        v = __builtin_amdgcn_raw_buffer_load_b128(
+            rx, (uint32_t)((int64_t)c * ldx * 2) + (uint32_t)(64 * (b0 + i) + 16 * q + 8 * h) * 2u,
+            0, 0);
+      xa[i][h] = __builtin_bit_cast(bf16x8_t, v);
+    }
+
+  // Weights and scales of row group g for this lane's row 16 g + l % 16
+  // (rows past N read as zero and are never stored).
+  const rsrc_t rw = make_rsrc(packed, (uint32_t)N * rowK2);
+  const uint32_t nblocks = (uint32_t)N * (uint32_t)nkb;
+  const rsrc_t rq = make_rsrc(absmax, DQ ? nblocks : nblocks * 4u);
+  const rsrc_t rg = make_rsrc(absmax2, DQ ? (nblocks + 255u) / 256u * 4u : 4u);
+  const float mu = DQ ? *mean : 0.0f;
+  struct Stage {
+    uint32_t w[BPW][2];   // 8 packed bytes per block
+    uint32_t qc[BPW];     // block codes (DQ per block), or 4 codes per dword (row mode)
+    float s[BPW];         // group scale (DQ), or fp32 absmax
+  };
+  auto load = [&](Stage& st, int g) {
+    const uint32_t n = (uint32_t)(16 * g + c);
+    const uint32_t wbase = n * rowK2 + (uint32_t)(32 * b0 + 8 * q);
+    const uint32_t blk0 = n * (uint32_t)nkb + (uint32_t)b0;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      if (i >= nbw) continue;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rw, wbase + 32u * i, 0, 0);
+      st.w[i][0] = v[0];
+      st.w[i][1] = v[1];
+      if (SM == kScaleDqRow) {
+        // nbw is a multiple of 4 and the wave's blocks sit in one group.
+        if ((i & 3) == 0) st.qc[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, blk0 + i, 0, 0);
+        if (i == 0)
+          st.s[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, (blk0 >> 8) * 4u, 0, 0));
+      } else if (DQ) {
+        st.qc[i] = __builtin_amdgcn_raw_buffer_load_b8(rq, blk0 + i, 0, 0);
+        st.s[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, ((blk0 + i) >> 8) * 4u, 0, 0));
+      } else {
+        st.s[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rq, (blk0 + i) * 4u, 0, 0));
+      }
+    }
+  };
+  auto scale = [&](const Stage& st, int i) {
+    if (!DQ) return st.s[i];
+    int code;
+    float g;
+    if (SM == kScaleDqRow) {
+      code = __builtin_amdgcn_sbfe((int)st.qc[i & ~3], (i & 3) * 8, 8);
+      g = st.s[0];
+    } else {
+      code = (int)(int8_t)st.qc[i];
+      g = st.s[i];
+    }
+    return __builtin_fmaf((float)code, g * (1.0f / 127.0f), mu);
+  };
+
+  // The loads of the first GD groups go out first (for the decode shapes
+  // that is every group of the workgroup), then the byte -> pair table.
+  Stage st[GD];
+#pragma unroll
+  for (int j = 0; j < GD; ++j)
+    if ((int)blockIdx.x + j * (int)gridDim.x < ngroups) load(st[j], blockIdx.x + j * gridDim.x);
+  const int lvl = level_lanes(lv);
+  for (int e = t; e < 256 * kCopies / 4; e += kMfWaves * 64) {
+    const uint32_t b = (uint32_t)e / (kCopies / 4);
+    const uint32_t v = pack_bf16x2(level_lookup(lvl, b >> 4), level_lookup(lvl, b & 15u));
+    *(uint4*)(tab + b * 256u + ((uint32_t)e % (kCopies / 4)) * 16u) = make_uint4(v, v, v, v);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+  const uint32_t lanebyte = (uint32_t)(lane & (kCopies - 1)) << 2;
+
+  // One row group: the wave's blocks, then the sums over the waves.
+  auto group = [&](const Stage& st, int gg, int rb) {
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      if (i >= nbw) continue;
+      f32x4_t blk = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t d = st.w[i][h];
+        u32x4_t bw;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t addr = perm(d, lanebyte, 0x0c0c0000u | ((4u + j) << 8));
+          bw[j] = *(const uint32_t*)(tab + addr);
+        }
+        blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i][h], __builtin_bit_cast(bf16x8_t, bw),
+                                                      blk, 0, 0, 0);
+      }
+      const float sc = scale(st, i);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(blk[v], sc, acc[v]);
+    }
+    // Lane l holds Y[4 (l / 16) + v][16 gg + l % 16], v = 0..3.
+    float* const r = red + rb * (kMfWaves * 256);
+    *(f32x4_t*)(r + wave * 256 + lane * 4) = acc;
+    __syncthreads();
+    if (t < 256) {
+      const int m = t >> 4, cc = t & 15;
+      const int src = (((m >> 2) * 16 + cc) << 2) + (m & 3);
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kMfWaves; ++w) sum += r[w * 256 + src];
+      const int n = 16 * gg + cc;
+      if (m < M && n < N) y[(int64_t)m * ldy + n] = f32_to_bf16(sum);
+    }
+  };
+  // Groups blockIdx.x + k * grid, k = 0, 1, ...: group k uses stage k % GD,
+  // which then takes the loads of group k + GD.  The sums alternate between
+  // two LDS buffers, so one barrier per group suffices.
+  int rb = 0;
+  for (int k0 = 0;; k0 += GD) {
+#pragma unroll
+    for (int j = 0; j < GD; ++j) {
+      const int gg = (int)blockIdx.x + (k0 + j) * (int)gridDim.x;
+      if (gg >= ngroups) return;
+      group(st[j], gg, rb);
+      rb ^= 1;
+      const int gn = gg + GD * (int)gridDim.x;
+      if (gn < ngroups) load(st[j], gn);
+    }
+  }
+}
+
+// Row-wise scales in the MFMA path: every wave's blocks are whole dwords of
+// codes inside one group (K/64 a multiple of 64) and the codes 4-byte aligned.
+bool mfma_row_scales(int dq, int K, const void* absmax) {
+  return dq && (K >> 6) % (4 * kMfWaves) == 0 && ((uintptr_t)absmax & 3u) == 0;
+}
+
+template <int BPW>
+hipError_t launch_mfma(int grid, const uint16_t* x, int64_t ldx, const uint8_t* packed,
+                       const void* absmax, const float* absmax2, const float* mean, int dq,
+                       int M, int N, int K, uint16_t* y, int64_t ldy, hipStream_t stream) {
+  const LevelTable& lv = level_table();
+  if (mfma_row_scales(dq, K, absmax))
+    hipLaunchKernelGGL((gemv_mfma_kernel<BPW, (BPW <= 4 ? 4 : 2), kScaleDqRow>), dim3(grid), dim3(kMfWaves * 64), 0,
+                       stream, x, ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, lv);
+  else if constexpr (BPW <= 4) {
+    // (Eight blocks per wave fit the registers only with row-wise scales.)
+    if (!dq)
+      hipLaunchKernelGGL((gemv_mfma_kernel<BPW, 4, kScaleF32>), dim3(grid), dim3(kMfWaves * 64), 0,
+                         stream, x, ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, lv);
+    else
+      hipLaunchKernelGGL((gemv_mfma_kernel<BPW, 4, kScaleDqLane>), dim3(grid), dim3(kMfWaves * 64),
+                         0, stream, x, ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, lv);
+  } else {
+    return hipErrorNotSupported;
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // host side: plan and dispatch
 // ---------------------------------------------------------------------------
 struct Plan {
@@ -485,8 +690,26 @@ hipError_t dispatch(const Plan& p, const uint16_t* x, int64_t ldx, const uint8_t
 hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* packed, const void* absmax,
                        const float* absmax2, const float* mean, int double_quant, int M, int N,
                        int K, uint16_t* y, int64_t ldy, hipStream_t stream) {
-  // Slabs of rows keep every byte offset of a launch below 2^31.
   const int64_t rowK2 = K >> 1, nkb = K >> 6;
+  // 4 < M <= 16: one MFMA launch streams the weights once, when each wave's
+  // K slice fits its registers (K <= 4096, or K <= 8192 with row-wise
+  // scales) and the offsets fit 32 bits.
+  if (M > 4) {
+    const int64_t bpw = (nkb + kMfWaves - 1) / kMfWaves;
+    const bool fits = (bpw <= 4 || (bpw <= 8 && mfma_row_scales(double_quant, K, absmax))) &&
+                      (int64_t)N * rowK2 < ((int64_t)1 << 31) &&
+                      15 * ldx * 2 + (int64_t)K * 2 < ((int64_t)1 << 31);
+    if (fits) {
+      const int ngroups = (N + 15) / 16;
+      const int grid = ngroups < cu_count() ? ngroups : cu_count();
+      if (bpw <= 4)
+        return launch_mfma<4>(grid, x, ldx, packed, absmax, absmax2, mean, double_quant, M, N, K,
+                              y, ldy, stream);
+      return launch_mfma<8>(grid, x, ldx, packed, absmax, absmax2, mean, double_quant, M, N, K, y,
+                            ldy, stream);
+    }
+  }
+  // Slabs of rows keep every byte offset of a launch below 2^31.
   int64_t slab = ((int64_t)1 << 30) / rowK2;
   slab -= slab % 256;
   // Rows of X in groups of up to four (each group streams W once); a group

@@ -88,6 +88,21 @@ def test_every_m_ragged_n(kind, M):
     assert err <= TOL, err
 
 
+@pytest.mark.parametrize("M", [5, 8, 16])
+@pytest.mark.parametrize("N,K,dq", [(200, 64, True), (200, 1088, True), (130, 4096, False),
+                                    (70, 2048, True), (130, 8192, True), (50, 8192, False),
+                                    (40, 16384, True)])
+def test_gemv_more_than_four_rows(M, N, K, dq):
+    """4 < M <= 16 (one launch streaming W once where the shape allows, else
+    groups of four rows): K from one block to 256 blocks, ragged row groups,
+    both scale layouts."""
+    w = synth.normal_bf16((N, K), 0.05, 8000 + K + M)
+    x = synth.normal_bf16((M, K), 1.0, 8100 + K + M)
+    ref, q = setup(w, (N, K), dq, check_state=False)
+    err = oracle.rel_frobenius(run("gemv", x, M, K, q), ref_product(x, ref, N, K))
+    assert err <= TOL, err
+
+
 @pytest.mark.parametrize("kind", ["gemv", "gemm"])
 @pytest.mark.parametrize("N,K,dq", [(33, 64, False), (64, 192, True), (300, 11008, True),
                                     (40, 40960, True), (7, 4096 + 64, False)])
