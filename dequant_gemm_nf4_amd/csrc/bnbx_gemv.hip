@@ -378,16 +378,22 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void gemv_kernel(
 //
 // A workgroup of 16 waves takes groups of 16 weight rows (16 columns of Y)
 // in turn; wave w owns the K slice of blocks [w nkb / 16, (w+1) nkb / 16)
-// (at most BPW blocks) and keeps its X slice for all 16 rows of X in
-// registers as MFMA A operands.  In an MFMA, lane l supplies column l % 16
-// and eight k of the 32; the 32 k of each MFMA are one half of one block,
-// lane quarter q taking k [16q + 8h, 16q + 8h + 8) of half h, so a lane needs
-// 8 packed bytes per block of its row (one 8-byte load) and every MFMA sits
-// inside one block.  The B operand is the bf16 levels from the byte -> pair
-// table (as in gemv_kernel, no per-weight arithmetic); a block's two MFMAs
-// go to a zeroed accumulator that is then scaled by the block scale of the
-// lane's column (its own row's) and added to the running sums.  The 16
-// waves' partial sums of a row group meet in LDS.
+// (BPW = 4 blocks: K = 4096) and keeps its X slice for all 16
+// rows of X in registers as MFMA A operands.  In an MFMA, lane l supplies
+// column l % 16 and eight k of the 32; the 32 k of each MFMA are one half of
+// one block, lane quarter q taking k [16q + 8h, 16q + 8h + 8) of half h, so
+// every MFMA sits inside one block.  The B operand is the bf16 levels from
+// the byte -> pair table (as in gemv_kernel, no per-weight arithmetic); a
+// block's two MFMAs go to a zeroed accumulator that is then scaled by the
+// block scale of the lane's column (its own row's) and added to the running
+// sums.  The 16 waves' partial sums meet in LDS once per round of GD row
+// groups.
+//
+// Weights and X are loaded row-contiguous (16 bytes per lane, eight lanes
+// per 128-byte line: an MFMA layout would touch 16 rows per load) and turned
+// into the MFMA layout through a 512 BPW-byte LDS region private to the
+// wave: 16-byte pieces of a row are stored at piece ^ f(row), which makes
+// the layout reads conflict-free.
 // ---------------------------------------------------------------------------
 constexpr int kMfWaves = 16;
 
@@ -398,62 +404,100 @@ __global__ __launch_bounds__(kMfWaves * 64, 1) void gemv_mfma_kernel(
     const float* __restrict__ mean, int M, int N, int K, uint16_t* __restrict__ y, int64_t ldy,
     LevelTable lv) {
   constexpr bool DQ = SM != kScaleF32;
-  // Table at LDS offset 0 (its addresses are v_perm results), then two
-  // buffers of the waves' partial sums (16 waves x 64 lanes x 4 values).
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kTabBytes + 2 * kMfWaves * 1024];
+  constexpr int kPieces = 2 * BPW;                 // 16-byte pieces per row of a slice
+  constexpr int kRow = 16 * kPieces;               // bytes per row of a slice
+  constexpr int kLoads = 16 * kPieces / 64;        // row-contiguous loads per 16 rows
+  constexpr int kRegion = 16 * kRow;               // bytes of a wave's region
+  // Table at LDS offset 0 (its addresses are v_perm results), then the
+  // waves' partial sums of GD row groups (16 waves x 64 lanes x 4 values
+  // each), then the waves' transpose regions.
+  __shared__ __attribute__((aligned(16))) unsigned char
+      smem[kTabBytes + GD * kMfWaves * 1024 + kMfWaves * kRegion];
   unsigned char* const tab = smem;
   float* const red = (float*)(smem + kTabBytes);
 
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  unsigned char* const reg = smem + kTabBytes + GD * kMfWaves * 1024 + wave * kRegion;
   const int c = lane & 15, q = lane >> 4;
   const int nkb = K >> 6;
-  const int b0 = wave * nkb / kMfWaves;
-  const int nbw = (wave + 1) * nkb / kMfWaves - b0;   // blocks of this wave, <= BPW
+  const int b0 = wave * BPW;                       // nkb == 16 BPW
   const uint32_t rowK2 = (uint32_t)K >> 1;
   const int ngroups = (N + 15) >> 4;
 
-  // X slice: A operand of half h of block i, lane (row l % 16, quarter q):
-  // X[row][64 (b0 + i) + 16 q + 8 h ..+8]; rows >= M read as zero.
+  // Region layout: piece p of row r at r * kRow + 16 (p ^ swz(r)).
+  static_assert(BPW == 4, "slices of 4 blocks");
+  auto swz = [](int r) { return (r >> 1) & 7; };
+  // A row-contiguous load covers 64 / kPieces rows: lane l of load u takes
+  // piece (64 u + l) % kPieces of row (64 u + l) / kPieces.
+  auto put = [&](const u32x4_t (&v)[kLoads]) {
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      const int e = 64 * u + lane, r = e / kPieces, p = e % kPieces;
+      *(u32x4_t*)(reg + r * kRow + 16 * (p ^ swz(r))) = v[u];
+    }
+  };
+
+  // X slice, A operand of half h of block i, lane (row l % 16, quarter q):
+  // X[row][64 (b0 + i) + 16 q + 8 h ..+8] = piece 8 i + 2 q + h of the
+  // row's slice; rows >= M read as zero.
   const rsrc_t rx = make_rsrc(x, (uint32_t)((int64_t)(M - 1) * ldx * 2 + (int64_t)K * 2));
   bf16x8_t xa[BPW][2];
+  {
+    // The slice is 16 rows x 8 BPW pieces; it passes through the region in
+    // four rounds of kPieces pieces per row (BPW / 4 blocks).
+    constexpr int kBr = BPW / 4;
+    u32x4_t xv[2][kLoads];   // two rounds in flight
+    auto xload = [&](int R) {
 #pragma unroll
-  for (int i = 0; i < BPW; ++i)
+      for (int u = 0; u < kLoads; ++u) {
+        const int e = 64 * u + lane, r = e / kPieces, p = e % kPieces;
+        xv[R & 1][u] = __builtin_amdgcn_raw_buffer_load_b128(
+            rx, (uint32_t)((int64_t)r * ldx * 2) + (uint32_t)(128 * b0 + 16 * (R * kPieces + p)), 0, 0);
+      }
+    };
+    xload(0);
+    xload(1);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (i < nbw)
-        v = __builtin_amdgcn_raw_buffer_load_b128(
-            rx, (uint32_t)((int64_t)c * ldx * 2) + (uint32_t)(64 * (b0 + i) + 16 * q + 8 * h) * 2u,
-            0, 0);
-      xa[i][h] = __builtin_bit_cast(bf16x8_t, v);
+    for (int R = 0; R < 4; ++R) {
+      put(xv[R & 1]);
+      if (R + 2 < 4) xload(R + 2);
+#pragma unroll
+      for (int ib = 0; ib < kBr; ++ib)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int pc = 8 * ib + 2 * q + h;     // piece within this round
+          xa[R * kBr + ib][h] = *(const bf16x8_t*)(reg + c * kRow + 16 * (pc ^ swz(c)));
+        }
     }
+  }
 
-  // Weights and scales of row group g for this lane's row 16 g + l % 16
-  // (rows past N read as zero and are never stored).
+  // Weights of row group g: row-contiguous 16-byte pieces of the 16 rows'
+  // slices (rows past N read as zero and are never stored), and the block
+  // scales of the lane's own row 16 g + l % 16.
   const rsrc_t rw = make_rsrc(packed, (uint32_t)N * rowK2);
   const uint32_t nblocks = (uint32_t)N * (uint32_t)nkb;
   const rsrc_t rq = make_rsrc(absmax, DQ ? nblocks : nblocks * 4u);
   const rsrc_t rg = make_rsrc(absmax2, DQ ? (nblocks + 255u) / 256u * 4u : 4u);
   const float mu = DQ ? *mean : 0.0f;
   struct Stage {
-    uint32_t w[BPW][2];   // 8 packed bytes per block
-    uint32_t qc[BPW];     // block codes (DQ per block), or 4 codes per dword (row mode)
-    float s[BPW];         // group scale (DQ), or fp32 absmax
+    u32x4_t w[kLoads];
+    uint32_t qc[BPW];   // block codes (DQ per block), or 4 codes per dword (row mode)
+    float s[BPW];       // group scale (DQ), or fp32 absmax
   };
   auto load = [&](Stage& st, int g) {
-    const uint32_t n = (uint32_t)(16 * g + c);
-    const uint32_t wbase = n * rowK2 + (uint32_t)(32 * b0 + 8 * q);
-    const uint32_t blk0 = n * (uint32_t)nkb + (uint32_t)b0;
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      const int e = 64 * u + lane, r = e / kPieces, p = e % kPieces;
+      st.w[u] = __builtin_amdgcn_raw_buffer_load_b128(
+          rw, (uint32_t)(16 * g + r) * rowK2 + (uint32_t)(32 * b0 + 16 * p), 0, 0);
+    }
+    const uint32_t blk0 = (uint32_t)(16 * g + c) * (uint32_t)nkb + (uint32_t)b0;
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
-      if (i >= nbw) continue;
-      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rw, wbase + 32u * i, 0, 0);
-      st.w[i][0] = v[0];
-      st.w[i][1] = v[1];
       if (SM == kScaleDqRow) {
-        // nbw is a multiple of 4 and the wave's blocks sit in one group.
+        // BPW is a multiple of 4 and the wave's blocks sit in one group.
         if ((i & 3) == 0) st.qc[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, blk0 + i, 0, 0);
         if (i == 0)
           st.s[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, (blk0 >> 8) * 4u, 0, 0));
@@ -496,16 +540,20 @@ __global__ __launch_bounds__(kMfWaves * 64, 1) void gemv_mfma_kernel(
   __builtin_amdgcn_sched_barrier(0);
   const uint32_t lanebyte = (uint32_t)(lane & (kCopies - 1)) << 2;
 
-  // One row group: the wave's blocks, then the sums over the waves.
-  auto group = [&](const Stage& st, int gg, int rb) {
+  // One row group: the wave's partial sums over its blocks.  Lane l holds
+  // Y[4 (l / 16) + v][16 g + l % 16], v = 0..3.
+  auto group = [&](const Stage& st) {
+    put(st.w);
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
-      if (i >= nbw) continue;
+      // Bytes [8 q, 8 q + 8) of block i of the lane's row: piece 2 i + q / 2.
+      const int pc = 2 * i + (q >> 1);
+      const uint2 d2 = *(const uint2*)(reg + c * kRow + 16 * (pc ^ swz(c)) + 8 * (q & 1));
       f32x4_t blk = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const uint32_t d = st.w[i][h];
+        const uint32_t d = h ? d2.y : d2.x;
         u32x4_t bw;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -519,62 +567,55 @@ __global__ __launch_bounds__(kMfWaves * 64, 1) void gemv_mfma_kernel(
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(blk[v], sc, acc[v]);
     }
-    // Lane l holds Y[4 (l / 16) + v][16 gg + l % 16], v = 0..3.
-    float* const r = red + rb * (kMfWaves * 256);
-    *(f32x4_t*)(r + wave * 256 + lane * 4) = acc;
-    __syncthreads();
-    if (t < 256) {
-      const int m = t >> 4, cc = t & 15;
-      const int src = (((m >> 2) * 16 + cc) << 2) + (m & 3);
-      float sum = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kMfWaves; ++w) sum += r[w * 256 + src];
-      const int n = 16 * gg + cc;
-      if (m < M && n < N) y[(int64_t)m * ldy + n] = f32_to_bf16(sum);
-    }
+    return acc;
   };
-  // Groups blockIdx.x + k * grid, k = 0, 1, ...: group k uses stage k % GD,
-  // which then takes the loads of group k + GD.  The sums alternate between
-  // two LDS buffers, so one barrier per group suffices.
-  int rb = 0;
-  for (int k0 = 0;; k0 += GD) {
+  // Rounds of GD row groups: group blockIdx.x + k * grid uses stage k % GD,
+  // which then takes the loads of group k + GD.  The waves run a round's
+  // groups without synchronizing (their LDS regions are private), then add
+  // up the round's partial sums in one pass.  The loop condition is the
+  // workgroup's, so its barriers are uniform.
+  for (int k0 = 0; (int)blockIdx.x + k0 * (int)gridDim.x < ngroups; k0 += GD) {
 #pragma unroll
     for (int j = 0; j < GD; ++j) {
       const int gg = (int)blockIdx.x + (k0 + j) * (int)gridDim.x;
-      if (gg >= ngroups) return;
-      group(st[j], gg, rb);
-      rb ^= 1;
-      const int gn = gg + GD * (int)gridDim.x;
-      if (gn < ngroups) load(st[j], gn);
+      if (gg < ngroups) {
+        *(f32x4_t*)(red + (j * kMfWaves + wave) * 256 + lane * 4) = group(st[j]);
+        const int gn = gg + GD * (int)gridDim.x;
+        if (gn < ngroups) load(st[j], gn);
+      }
     }
+    __syncthreads();
+    for (int e = t; e < GD * 256; e += kMfWaves * 64) {
+      const int j = e >> 8, m = (e >> 4) & 15, cc = e & 15;
+      const int gg = (int)blockIdx.x + (k0 + j) * (int)gridDim.x;
+      const int n = 16 * gg + cc;
+      if (gg < ngroups && m < M && n < N) {
+        const int src = (((m >> 2) * 16 + cc) << 2) + (m & 3);
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kMfWaves; ++w) sum += red[(j * kMfWaves + w) * 256 + src];
+        y[(int64_t)m * ldy + n] = f32_to_bf16(sum);
+      }
+    }
+    __syncthreads();
   }
 }
 
-// Row-wise scales in the MFMA path: every wave's blocks are whole dwords of
-// codes inside one group (K/64 a multiple of 64) and the codes 4-byte aligned.
-bool mfma_row_scales(int dq, int K, const void* absmax) {
-  return dq && (K >> 6) % (4 * kMfWaves) == 0 && ((uintptr_t)absmax & 3u) == 0;
-}
-
-template <int BPW>
+// Row-wise scales in the MFMA path: every wave's four blocks are one dword of
+// codes inside one group; needs 4-byte aligned codes.
 hipError_t launch_mfma(int grid, const uint16_t* x, int64_t ldx, const uint8_t* packed,
                        const void* absmax, const float* absmax2, const float* mean, int dq,
                        int M, int N, int K, uint16_t* y, int64_t ldy, hipStream_t stream) {
   const LevelTable& lv = level_table();
-  if (mfma_row_scales(dq, K, absmax))
-    hipLaunchKernelGGL((gemv_mfma_kernel<BPW, (BPW <= 4 ? 4 : 2), kScaleDqRow>), dim3(grid), dim3(kMfWaves * 64), 0,
+  if (dq && ((uintptr_t)absmax & 3u) == 0)
+    hipLaunchKernelGGL((gemv_mfma_kernel<4, 4, kScaleDqRow>), dim3(grid), dim3(kMfWaves * 64), 0,
                        stream, x, ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, lv);
-  else if constexpr (BPW <= 4) {
-    // (Eight blocks per wave fit the registers only with row-wise scales.)
-    if (!dq)
-      hipLaunchKernelGGL((gemv_mfma_kernel<BPW, 4, kScaleF32>), dim3(grid), dim3(kMfWaves * 64), 0,
-                         stream, x, ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, lv);
-    else
-      hipLaunchKernelGGL((gemv_mfma_kernel<BPW, 4, kScaleDqLane>), dim3(grid), dim3(kMfWaves * 64),
-                         0, stream, x, ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, lv);
-  } else {
-    return hipErrorNotSupported;
-  }
+  else if (dq)
+    hipLaunchKernelGGL((gemv_mfma_kernel<4, 2, kScaleDqLane>), dim3(grid), dim3(kMfWaves * 64), 0,
+                       stream, x, ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, lv);
+  else
+    hipLaunchKernelGGL((gemv_mfma_kernel<4, 2, kScaleF32>), dim3(grid), dim3(kMfWaves * 64), 0,
+                       stream, x, ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, lv);
   return hipGetLastError();
 }
 
@@ -691,22 +732,17 @@ hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* packed, co
                        const float* absmax2, const float* mean, int double_quant, int M, int N,
                        int K, uint16_t* y, int64_t ldy, hipStream_t stream) {
   const int64_t rowK2 = K >> 1, nkb = K >> 6;
-  // 4 < M <= 16: one MFMA launch streams the weights once, when each wave's
-  // K slice fits its registers (K <= 4096, or K <= 8192 with row-wise
-  // scales) and the offsets fit 32 bits.
+  // 4 < M <= 16 at K = 4096 (each wave's K slice in its registers): one
+  // MFMA launch streams the weights once, when the offsets fit 32 bits.
   if (M > 4) {
-    const int64_t bpw = (nkb + kMfWaves - 1) / kMfWaves;
-    const bool fits = (bpw <= 4 || (bpw <= 8 && mfma_row_scales(double_quant, K, absmax))) &&
+    const bool fits = nkb == 64 &&
                       (int64_t)N * rowK2 < ((int64_t)1 << 31) &&
                       15 * ldx * 2 + (int64_t)K * 2 < ((int64_t)1 << 31);
     if (fits) {
       const int ngroups = (N + 15) / 16;
       const int grid = ngroups < cu_count() ? ngroups : cu_count();
-      if (bpw <= 4)
-        return launch_mfma<4>(grid, x, ldx, packed, absmax, absmax2, mean, double_quant, M, N, K,
-                              y, ldy, stream);
-      return launch_mfma<8>(grid, x, ldx, packed, absmax, absmax2, mean, double_quant, M, N, K, y,
-                            ldy, stream);
+      return launch_mfma(grid, x, ldx, packed, absmax, absmax2, mean, double_quant, M, N, K, y, ldy,
+                         stream);
     }
   }
   // Slabs of rows keep every byte offset of a launch below 2^31.
