@@ -42,6 +42,8 @@ DECODE_SHAPES = ((4096, 4096), (11008, 4096), (4096, 11008))
 # the linears of one Llama-7B-shaped layer: (name, shape index)
 LAYER = (("q", 0), ("k", 0), ("v", 0), ("o", 0), ("gate", 1), ("up", 1), ("down", 2))
 PREFILL = (2048, 8192, 8192)
+BATCHED = (16, 14336, 4096)     # batched decode: M, N, K
+BATCHED_COPIES = 20             # 20 x 29.4 MB of distinct weights (> 512 MB)
 
 
 def gemv_bytes(M, N, K):
@@ -172,6 +174,23 @@ def main():
     qp = T.quantize(wp, True)
     del wp
     yp = torch.empty(Mp, Np, dtype=torch.bfloat16, device=dev)
+
+    # batched decode, M=16 on 14336x4096 (weights N(0,0.02) with 0.1% of
+    # entries x20): distinct weights over more than 512 MB, so each launch
+    # streams its weight from HBM
+    Mb, Nb, Kb = BATCHED
+    qb = []
+    for i in range(BATCHED_COPIES):
+        gen.manual_seed(8000 + i)
+        w = torch.randn(Nb * Kb, generator=gen, device=dev, dtype=torch.float32) * 0.02
+        gen.manual_seed(8200 + i)
+        idx = torch.randperm(Nb * Kb, generator=gen, device=dev)[: Nb * Kb // 1000]
+        w[idx] *= 20.0
+        qb.append(T.quantize(w.view(Nb, Kb).to(torch.bfloat16), True))
+        del w, idx
+    gen.manual_seed(8100)
+    xb = torch.randn(Mb, Kb, generator=gen, device=dev).to(torch.bfloat16)
+    yb = torch.empty(Mb, Nb, dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -199,8 +218,12 @@ def main():
     def stage_gemm():
         T.gemm(xp, qp, out=yp)
 
+    def stage_batched():
+        for q in qb:
+            T.gemv(xb, q, out=yb)
+
     stages = [stage_quantize, stage_dequantize] + \
-        [stage_gemv(s) for s in range(len(DECODE_SHAPES))] + [stage_gemm]
+        [stage_gemv(s) for s in range(len(DECODE_SHAPES))] + [stage_gemm, stage_batched]
     for fn in stages:        # eager warm-up (also loads every kernel)
         fn()
     torch.cuda.synchronize()
@@ -266,6 +289,9 @@ def main():
     gb_d = K_ * sum(dequant_bytes(*DECODE_SHAPES[si]) for si in wshape)
     gb_in = K_ * sum(2 * DECODE_SHAPES[si][0] * DECODE_SHAPES[si][1] for si in wshape)
     gemm_tflops = K_ * 2.0 * Mp * Np * Kp / t_m / 1e12
+    t_b = stage_ms(3 + len(DECODE_SHAPES)) / 1e3
+    us_b = t_b / (K_ * BATCHED_COPIES) * 1e6
+    b_b = gemv_bytes(Mb, Nb, Kb)
 
     out = {
         "metric": METRIC,
@@ -285,7 +311,8 @@ def main():
                         "4096x11008 (NF4 blocksize 64, double quant), every weight of a "
                         f"{L}-layer stack (q,k,v,o,gate,up,down per layer, distinct weights, "
                         "streamed from HBM); plus quantize and dequantize of the stack and a "
-                        "prefill GEMM M=2048 N=K=8192",
+                        "prefill GEMM M=2048 N=K=8192; batched decode M=16 on 14336x4096 "
+                        "(0.1% of weights x20) in kernels.gemv_m16",
             "layers": L,
             "gemm": {"M": Mp, "N": Np, "K": Kp},
         },
@@ -312,10 +339,15 @@ def main():
             "gemv_stack_gbs": round(stack_gbs, 1),
             "gemv_avg_launch_us": round(avg_gemv_us, 3),
             "gemv_launch_us_by_shape": shape_us,
+            "gemv_m16": {"shape": f"{Mb}x{Nb}x{Kb}", "launch_us": round(us_b, 3),
+                         "gbs": round(b_b / (us_b * 1e-6) / 1e9, 1),
+                         "hbm_frac": round(b_b / (us_b * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "tflops": round(2.0 * Mb * Nb * Kb / (us_b * 1e-6) / 1e12, 2)},
             "stage_ms_per_step": {"quantize": round(t_q / K_ * 1e3, 3),
                                   "dequantize": round(t_d / K_ * 1e3, 3),
                                   "gemv": round(t_v / K_ * 1e3, 3),
-                                  "gemm": round(t_m / K_ * 1e3, 3)},
+                                  "gemm": round(t_m / K_ * 1e3, 3),
+                                  "gemv_m16": round(t_b / K_ * 1e3, 3)},
         },
     }
     if not args.no_cpu_baseline:
