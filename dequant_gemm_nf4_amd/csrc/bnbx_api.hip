@@ -182,12 +182,12 @@ int bnbx_quantize_nf4(const uint16_t* w, uint8_t* packed, const bnbx_nf4_state* 
   const size_t need = dq_workspace_bytes(nb);
   if (workspace == nullptr || workspace_bytes < need) return BNBX_E_WORKSPACE;
   if (!aligned(workspace, 256)) return BNBX_E_ALIGN;
-  unsigned long long* hist = (unsigned long long*)workspace;
-  float* a32 = (float*)((char*)workspace + kHistBytes);
-  hipError_t e = launch_zero_hist(hist, hs);
-  if (e == hipSuccess) e = launch_quantize(w, packed, n, a32, hist, hs);
+  unsigned long long* slots = (unsigned long long*)workspace;
+  float* a32 = (float*)((char*)workspace + round_up(kSlotBytes, 256));
+  hipError_t e = launch_quantize(w, packed, n, a32, slots, hs);
   if (e == hipSuccess)
-    e = launch_double_quant(a32, hist, nb, (int8_t*)st->absmax, st->absmax2, st->absmax_mean, hs);
+    e = launch_double_quant(a32, slots, quantize_grid(n), nb, (int8_t*)st->absmax, st->absmax2,
+                            st->absmax_mean, hs);
   return hip_status(e);
 }
 

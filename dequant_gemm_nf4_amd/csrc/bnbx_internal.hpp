@@ -33,24 +33,28 @@ const float* thresholds_f32();      // float[15]
 const EncodeTable& encode_table();
 const LevelTable& level_table();
 
-// Workspace layout of the double-quant quantize: kHistCopies exact exponent
-// histograms of the block absmax values (workgroup w adds into copy
-// w % kHistCopies, so no address sees more than a few dozen global atomics),
-// then the fp32 absmax of every block.
-constexpr size_t kHistBins = 256;
-constexpr size_t kHistCopies = 16;
-constexpr size_t kHistBytes = kHistCopies * kHistBins * sizeof(unsigned long long);
+// Workspace layout of the double-quant quantize: one slot per quantize
+// workgroup (at most kMaxQGrid) holding that workgroup's exact partial sum of
+// its block absmax values as kSumDigits base-2^32 digits (each slot is fully
+// overwritten by every call, so nothing needs clearing), then the fp32
+// absmax of every block.
+constexpr int kMaxQGrid = 512;
+constexpr int kSumDigits = 10;
+constexpr size_t kHistBins = 256;   // binary exponent fields of a bf16 absmax
+constexpr size_t kSlotBytes = (size_t)kMaxQGrid * kSumDigits * sizeof(unsigned long long);
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline size_t dq_workspace_bytes(int64_t nb) {
-  return kHistBytes + round_up((size_t)nb * sizeof(float), 256);
+  return round_up(kSlotBytes, 256) + round_up((size_t)nb * sizeof(float), 256);
 }
 
 // ---- kernel launchers (return hipError_t of the launch) ----
+// quantize_grid(n) workgroups write slots [0, quantize_grid(n)) when
+// `slots` is given (double quant); double_quant reads as many.
+int quantize_grid(int64_t n);
 hipError_t launch_quantize(const uint16_t* w, uint8_t* packed, int64_t n, float* absmax_f32,
-                           unsigned long long* hist, hipStream_t stream);
-hipError_t launch_zero_hist(unsigned long long* hist, hipStream_t stream);
-hipError_t launch_double_quant(const float* absmax_f32, const unsigned long long* hist,
-                               int64_t nb, int8_t* q, float* absmax2, float* mean,
+                           unsigned long long* slots, hipStream_t stream);
+hipError_t launch_double_quant(const float* absmax_f32, const unsigned long long* slots,
+                               int nslots, int64_t nb, int8_t* q, float* absmax2, float* mean,
                                hipStream_t stream);
 hipError_t launch_dequantize(const uint8_t* packed, int64_t n, const void* absmax,
                              const float* absmax2, const float* mean, int double_quant,

@@ -11,9 +11,11 @@
 // normalises with the block's fp32 reciprocal and encodes each weight with one
 // bucket lookup plus one compare (see EncodeTable), packs two codes per byte
 // and writes 4 bytes per lane.  With double quantization it also writes the
-// fp32 absmax to the workspace and accumulates an exact exponent histogram of
-// the absmax values (sum of the 8-bit significands per binary exponent), from
-// which double_quant_kernel forms the exactly rounded mean.
+// fp32 absmax to the workspace and, per workgroup, an exact exponent
+// histogram of its absmax values (sum of the 8-bit significands per binary
+// exponent) in LDS, which it turns into its exact partial sum (an integer in
+// base-2^32 digits) and writes to its own workspace slot; double_quant_kernel
+// adds the slots and forms the exactly rounded mean.
 #include <float.h>
 
 #include "bnbx_device.hpp"
@@ -105,9 +107,10 @@ __device__ __forceinline__ void record_block(int lane, int64_t e, uint32_t m, fl
 template <bool DQ>
 __global__ __launch_bounds__(kQThreads, 2) void quantize_kernel(
     const uint16_t* __restrict__ w, uint8_t* __restrict__ packed, float* __restrict__ absmax,
-    unsigned long long* __restrict__ hist, int64_t n, EncodeTable et) {
+    unsigned long long* __restrict__ slots, int64_t n, EncodeTable et) {
   __shared__ __attribute__((aligned(16))) unsigned char tab[kBuckets * kTabStride];
   __shared__ uint32_t lhist[kHistBins];
+  __shared__ unsigned long long ldig[kSumDigits];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -122,8 +125,10 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_kernel(
     t.y = et.base[e >> 5];
     *(uint2*)(tab + (e >> 5) * kTabStride + (e & 31) * 8) = t;
   }
-  if (DQ)
+  if (DQ) {
     for (int e = tid; e < (int)kHistBins; e += kQThreads) lhist[e] = 0;
+    if (tid < kSumDigits) ldig[tid] = 0ull;
+  }
   __syncthreads();
   const uint32_t lanebase = (uint32_t)(lane & 31) << 3;
 
@@ -170,40 +175,56 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_kernel(
   }
 
   if (DQ) {
+    // The workgroup's partial sum I_w = sum_e lhist[e] * 2^(max(e,1)-1) (see
+    // exact_mean) in base-2^32 digits: a bin (below 2^32) shifted by less
+    // than 32 spans two digits.  Every workgroup writes its whole slot.
     __syncthreads();
-    unsigned long long* h = hist + (blockIdx.x % kHistCopies) * kHistBins;
-    for (int e = tid; e < (int)kHistBins; e += kQThreads)
-      if (lhist[e]) atomicAdd(&h[e], (unsigned long long)lhist[e]);
+    for (int e = tid; e < (int)kHistBins; e += kQThreads) {
+      const unsigned long long h = lhist[e];
+      if (h) {
+        const int sh = (e > 1 ? e : 1) - 1;
+        const int k = sh >> 5, bit = sh & 31;
+        const unsigned long long p = h << bit;
+        atomicAdd(&ldig[k], p & 0xffffffffull);
+        if (p >> 32) atomicAdd(&ldig[k + 1], p >> 32);
+      }
+    }
+    __syncthreads();
+    if (tid < kSumDigits) slots[(int64_t)blockIdx.x * kSumDigits + tid] = ldig[tid];
   }
-}
-
-__global__ void zero_hist_kernel(unsigned long long* __restrict__ hist) {
-  hist[blockIdx.x * blockDim.x + threadIdx.x] = 0ull;
 }
 
 // Exact mean of the block absmax values.  absmax = sig * 2^(max(e,1) - 134)
 // for binary exponent field e and 8-bit significand sig, so
 // sum = I * 2^-133 with I = sum_e hist[e] * 2^(max(e,1)-1), an integer below
-// 2^320.  I is assembled in ten 32-bit digits, rounded once to binary64
-// (nearest even), divided by nb in binary64 and rounded to binary32.
-__device__ float exact_mean(const unsigned long long* __restrict__ hist, int64_t nb,
-                            unsigned long long* digits /* LDS[10] */) {
+// 2^320.  I arrives as the quantize workgroups' partial sums in ten base-2^32
+// digits each (digits below 2^40); they are added digit-wise, carried,
+// rounded once to binary64 (nearest even), divided by nb in binary64 and
+// rounded to binary32.
+__device__ float exact_mean(const unsigned long long* __restrict__ slots, int nslots, int64_t nb,
+                            unsigned long long* digits /* LDS[kSumDigits], 256 threads */) {
   const int tid = threadIdx.x;
-  if (tid < 10) digits[tid] = 0ull;
+  if (tid < kSumDigits) digits[tid] = 0ull;
   __syncthreads();
-  for (int e = tid; e < (int)kHistBins; e += blockDim.x) {
-    unsigned long long h = 0;
+  // Thread t adds digit t % 10 of slots t / 10, t / 10 + P, ... (P = 25
+  // threads per digit of a 256-thread block) in a register, all loads in
+  // flight at once, then one LDS add per thread.
+  constexpr int P = 256 / kSumDigits;
+  constexpr int kPer = (kMaxQGrid + P - 1) / P;
+  if (tid < P * kSumDigits) {
+    const int d = tid % kSumDigits, j0 = tid / kSumDigits;
+    unsigned long long v = 0ull;
+    // Unconditional loads (an index past nslots reads slot 0 and is
+    // discarded), so that none waits for another.
+    unsigned long long x[kPer];
 #pragma unroll
-    for (int c = 0; c < (int)kHistCopies; ++c) h += hist[c * kHistBins + e];
-    if (h) {
-      const int sh = (e > 1 ? e : 1) - 1;
-      const int k = sh >> 5, bit = sh & 31;
-      const unsigned long long pl = (h & 0xffffffffull) << bit;
-      const unsigned long long ph = (h >> 32) << bit;
-      atomicAdd(&digits[k], pl & 0xffffffffull);
-      atomicAdd(&digits[k + 1], (pl >> 32) + (ph & 0xffffffffull));
-      atomicAdd(&digits[k + 2], ph >> 32);
+    for (int r = 0; r < kPer; ++r) {
+      const int j = j0 + r * P;
+      x[r] = slots[(j < nslots ? j : 0) * kSumDigits + d];
     }
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) v += j0 + r * P < nslots ? x[r] : 0ull;
+    if (v) atomicAdd(&digits[d], v);
   }
   __syncthreads();
   double S = 0.0;
@@ -239,32 +260,49 @@ __device__ float exact_mean(const unsigned long long* __restrict__ hist, int64_t
   return (float)mean;
 }
 
+// Groups per double_quant workgroup; their absmax values are loaded before
+// the mean is formed, so that one memory latency covers both.
+constexpr int kDqGroups = 4;
+
 __global__ __launch_bounds__(256) void double_quant_kernel(
-    const float* __restrict__ a, const unsigned long long* __restrict__ hist, int64_t nb,
-    int8_t* __restrict__ q, float* __restrict__ s_out, float* __restrict__ mean_out) {
-  __shared__ unsigned long long digits[10];
-  __shared__ float red[4];
-  const float mu = exact_mean(hist, nb, digits);
+    const float* __restrict__ a, const unsigned long long* __restrict__ slots, int nslots,
+    int64_t nb, int8_t* __restrict__ q, float* __restrict__ s_out, float* __restrict__ mean_out) {
+  __shared__ unsigned long long digits[kSumDigits];
+  __shared__ float red[kDqGroups][4];
   const int tid = threadIdx.x;
+  const int64_t g0 = (int64_t)blockIdx.x * kDqGroups;
+  float v[kDqGroups];
+#pragma unroll
+  for (int i = 0; i < kDqGroups; ++i) {
+    const int64_t b = (g0 + i) * kGroup + tid;
+    v[i] = b < nb ? a[b] : 0.0f;
+  }
+  const float mu = exact_mean(slots, nslots, nb, digits);
   if (blockIdx.x == 0 && tid == 0) *mean_out = mu;
   const int64_t ng = (nb + kGroup - 1) / kGroup;
-  for (int64_t g = blockIdx.x; g < ng; g += gridDim.x) {
+  float c[kDqGroups];
+#pragma unroll
+  for (int i = 0; i < kDqGroups; ++i) {
+    const int64_t b = (g0 + i) * kGroup + tid;
+    c[i] = b < nb ? v[i] - mu : 0.0f;
+    const float m = wave_max(fabsf(c[i]));
+    if ((tid & 63) == 0) red[i][tid >> 6] = m;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kDqGroups; ++i) {
+    const int64_t g = g0 + i;
+    if (g >= ng) break;   // uniform
     const int64_t b = g * kGroup + tid;
-    const bool valid = b < nb;
-    const float c = valid ? a[b] - mu : 0.0f;
-    float m = wave_max(fabsf(c));
-    if ((tid & 63) == 0) red[tid >> 6] = m;
-    __syncthreads();
-    const float s = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float s = fmaxf(fmaxf(red[i][0], red[i][1]), fmaxf(red[i][2], red[i][3]));
     int qv = 0;
     if (s > 0.0f) {
-      const float t = c / s;          // correctly rounded binary32 division
+      const float t = c[i] / s;       // correctly rounded binary32 division
       const float u = t * 127.0f;
       qv = (int)rintf(u);             // round half to even
     }
-    if (valid) q[b] = (int8_t)qv;
+    if (b < nb) q[b] = (int8_t)qv;
     if (tid == 0) s_out[g] = s;
-    __syncthreads();
   }
 }
 
@@ -277,32 +315,31 @@ int grid_for(int64_t work_items, int per_block, int cap) {
 
 }  // namespace
 
-hipError_t launch_quantize(const uint16_t* w, uint8_t* packed, int64_t n, float* absmax_f32,
-                           unsigned long long* hist, hipStream_t stream) {
+int quantize_grid(int64_t n) {
   const int64_t ntiles = (n + kTile - 1) / kTile;
-  const int grid = grid_for(ntiles, kQWaves * kUnroll, 512);
-  if (hist != nullptr)
+  return grid_for(ntiles, kQWaves * kUnroll, kMaxQGrid);
+}
+
+hipError_t launch_quantize(const uint16_t* w, uint8_t* packed, int64_t n, float* absmax_f32,
+                           unsigned long long* slots, hipStream_t stream) {
+  const int grid = quantize_grid(n);
+  if (slots != nullptr)
     hipLaunchKernelGGL(quantize_kernel<true>, dim3(grid), dim3(kQThreads), 0, stream, w, packed,
-                       absmax_f32, hist, n, encode_table());
+                       absmax_f32, slots, n, encode_table());
   else
     hipLaunchKernelGGL(quantize_kernel<false>, dim3(grid), dim3(kQThreads), 0, stream, w, packed,
-                       absmax_f32, hist, n, encode_table());
+                       absmax_f32, slots, n, encode_table());
   return hipGetLastError();
 }
 
-hipError_t launch_zero_hist(unsigned long long* hist, hipStream_t stream) {
-  hipLaunchKernelGGL(zero_hist_kernel, dim3((unsigned)kHistCopies), dim3((unsigned)kHistBins), 0,
-                     stream, hist);
-  return hipGetLastError();
-}
-
-hipError_t launch_double_quant(const float* absmax_f32, const unsigned long long* hist,
-                               int64_t nb, int8_t* q, float* absmax2, float* mean,
+hipError_t launch_double_quant(const float* absmax_f32, const unsigned long long* slots,
+                               int nslots, int64_t nb, int8_t* q, float* absmax2, float* mean,
                                hipStream_t stream) {
   const int64_t ng = (nb + kGroup - 1) / kGroup;
-  const int grid = grid_for(ng, 4, 512);
-  hipLaunchKernelGGL(double_quant_kernel, dim3(grid), dim3(256), 0, stream, absmax_f32, hist, nb,
-                     q, absmax2, mean);
+  const int64_t grid = (ng + kDqGroups - 1) / kDqGroups;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(double_quant_kernel, dim3((unsigned)grid), dim3(256), 0, stream, absmax_f32,
+                     slots, nslots, nb, q, absmax2, mean);
   return hipGetLastError();
 }
 
