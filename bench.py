@@ -268,6 +268,36 @@ def main():
     def stage_ms(k):
         return sum(m[2 * k].elapsed_time(m[2 * k + 1]) for m in all_marks)
 
+    # Achievable ceiling, outside the timed steps: a plain streaming read of
+    # each weight's packed bytes and block codes (what the GEMV streams),
+    # launched back to back over the same weights as the GEMV stage.
+    import dequant_gemm_nf4_amd as bnbx
+    sink = torch.zeros(bnbx.BNBX_PROBE_SINK_WORDS, dtype=torch.int32, device=dev)
+    read_bytes = [N * K // 2 + N * K // 64 for N, K in DECODE_SHAPES]
+
+    def stage_read(s):
+        def run():
+            for i in by_shape[s]:
+                bnbx.bnbx_probe_stream_read(qs[i].packed, qs[i].packed.numel(), qs[i].absmax,
+                                            qs[i].absmax.numel(), sink)
+        return run
+    read_us = []
+    for s in range(len(DECODE_SHAPES)):
+        stage_read(s)()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            stage_read(s)()
+        g.replay()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        read_us.append(e0.elapsed_time(e1) * 1e3 / (args.steps * len(by_shape[s])))
+        del g
+    read_gbs = (sum(read_bytes) / len(read_bytes)) / (sum(read_us) / len(read_us) * 1e-6) / 1e9
+
     t_q = stage_ms(0) / 1e3
     t_d = stage_ms(1) / 1e3
     t_shape = [stage_ms(2 + s) / 1e3 for s in range(len(DECODE_SHAPES))]
@@ -343,6 +373,16 @@ def main():
                          "gbs": round(b_b / (us_b * 1e-6) / 1e9, 1),
                          "hbm_frac": round(b_b / (us_b * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                          "tflops": round(2.0 * Mb * Nb * Kb / (us_b * 1e-6) / 1e12, 2)},
+            "read_ceiling": {
+                "what": "plain streaming read of each weight's packed bytes and block codes, "
+                        "back to back over the same weights (bnbx_probe_stream_read)",
+                "bytes_by_shape": {f"{N}x{K}": b for (N, K), b in zip(DECODE_SHAPES, read_bytes)},
+                "launch_us_by_shape": {f"{N}x{K}": round(u, 3)
+                                       for (N, K), u in zip(DECODE_SHAPES, read_us)},
+                "gbs": round(read_gbs, 1),
+                "hbm_frac": round(read_gbs / HBM_PEAK_GBS, 4),
+                "gemv_over_ceiling": round(gemv_gbs / read_gbs, 4),
+            },
             "stage_ms_per_step": {"quantize": round(t_q / K_ * 1e3, 3),
                                   "dequantize": round(t_d / K_ * 1e3, 3),
                                   "gemv": round(t_v / K_ * 1e3, 3),

@@ -22,7 +22,8 @@ __all__ = [
     "BNBX_E_HIP", "BnbxError", "BnbxLibraryMissing", "Nf4State", "library_path", "lib",
     "bnbx_status_str", "bnbx_nf4_codebook", "bnbx_quantize_nf4_workspace_bytes",
     "bnbx_quantize_nf4", "bnbx_dequantize_nf4", "bnbx_gemv_nf4",
-    "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4", "EXPORTED_SYMBOLS",
+    "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4", "bnbx_probe_stream_read",
+    "BNBX_PROBE_SINK_WORDS", "EXPORTED_SYMBOLS",
 ]
 
 BNBX_OK = 0
@@ -36,7 +37,9 @@ EXPORTED_SYMBOLS = (
     "bnbx_status_str", "bnbx_nf4_codebook", "bnbx_quantize_nf4_workspace_bytes",
     "bnbx_quantize_nf4", "bnbx_dequantize_nf4", "bnbx_gemv_nf4",
     "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4",
+    "bnbx_probe_stream_read",          # include/bnbx_probe.h (measurement aid)
 )
+BNBX_PROBE_SINK_WORDS = 1024
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -99,6 +102,8 @@ def lib() -> ctypes.CDLL:
     L.bnbx_gemm_nf4_workspace_bytes.restype = sz
     L.bnbx_gemm_nf4.argtypes = [vp, i64, vp, sp, i32, i32, i32, vp, i64, vp, sz, vp]
     L.bnbx_gemm_nf4.restype = i32
+    L.bnbx_probe_stream_read.argtypes = [vp, sz, vp, sz, vp, vp]
+    L.bnbx_probe_stream_read.restype = i32
     _lib = L
     return L
 
@@ -171,3 +176,18 @@ def bnbx_gemm_nf4(x, ldx: int, packed, state: Nf4State, M: int, N: int, K: int, 
     _check(lib().bnbx_gemm_nf4(_ptr(x), int(ldx), _ptr(packed), ctypes.byref(state), int(M),
                                int(N), int(K), _ptr(y), int(ldy), _ptr(workspace),
                                int(workspace_bytes), _stream(stream)), "bnbx_gemm_nf4")
+
+
+def _nbytes(t) -> int | None:
+    return None if t is None or isinstance(t, int) else int(t.numel() * t.element_size())
+
+
+def bnbx_probe_stream_read(a, a_bytes: int, b, b_bytes: int, sink, stream=None) -> None:
+    # The library cannot see buffer sizes: for tensors, a byte count past the
+    # end is rejected here rather than read.
+    for t, n in ((a, a_bytes), (b, b_bytes), (sink, 4 * BNBX_PROBE_SINK_WORDS)):
+        size = _nbytes(t)
+        if size is not None and n > size:
+            raise BnbxError(BNBX_E_INVAL, "bnbx_probe_stream_read: byte count past the buffer")
+    _check(lib().bnbx_probe_stream_read(_ptr(a), int(a_bytes), _ptr(b), int(b_bytes), _ptr(sink),
+                                        _stream(stream)), "bnbx_probe_stream_read")

@@ -12,7 +12,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbnbx.so")
-SOURCES = ["bnbx_api.hip", "bnbx_quant.hip", "bnbx_dequant.hip", "bnbx_gemv.hip", "bnbx_gemm.hip"]
+SOURCES = ["bnbx_api.hip", "bnbx_quant.hip", "bnbx_dequant.hip", "bnbx_gemv.hip", "bnbx_gemm.hip",
+           "bnbx_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

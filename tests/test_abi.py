@@ -1,5 +1,5 @@
 """The C-ABI library without a GPU: it loads, exports exactly the entry
-points include/bnbx.h declares, its host-side codebook equals the oracle's,
+points include/*.h declare, its host-side codebook equals the oracle's,
 and every invalid argument is rejected on the host before any launch (the
 pointers below are never dereferenced)."""
 
@@ -14,11 +14,12 @@ import dequant_gemm_nf4_amd as bnbx
 import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "bnbx.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 def header_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"BNBX_API\s+[\w\s\*]*?\b(bnbx_\w+)\s*\(", text)))
 
 
@@ -29,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 8
+    assert len(declared) == 9
     assert sorted(bnbx.EXPORTED_SYMBOLS) == declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -134,6 +135,31 @@ def test_dequantize_rejects():
     assert status_of(bnbx.bnbx_dequantize_nf4, A, state(7), B, 0) == bnbx.BNBX_E_INVAL
     assert status_of(bnbx.bnbx_dequantize_nf4, A, state(blocksize=32), B, 0) == \
         bnbx.BNBX_E_UNSUPPORTED
+
+
+def test_probe_stream_read_rejects():
+    f = bnbx.bnbx_probe_stream_read
+    assert status_of(f, None, 16, None, 0, C, 0) == bnbx.BNBX_E_INVAL      # a NULL, a_bytes > 0
+    assert status_of(f, A, 16, None, 16, C, 0) == bnbx.BNBX_E_INVAL       # b NULL, b_bytes > 0
+    assert status_of(f, A, 16, None, 0, None, 0) == bnbx.BNBX_E_INVAL     # no sink
+    assert status_of(f, A, 0, None, 0, C, 0) == bnbx.BNBX_E_INVAL         # nothing to read
+    assert status_of(f, A, 24, None, 0, C, 0) == bnbx.BNBX_E_INVAL        # not whole 16 B units
+    assert status_of(f, A + 8, 16, None, 0, C, 0) == bnbx.BNBX_E_ALIGN
+    assert status_of(f, A, 16, B + 4, 16, C, 0) == bnbx.BNBX_E_ALIGN
+    assert status_of(f, A, 16, None, 0, C + 2, 0) == bnbx.BNBX_E_ALIGN
+
+
+def test_probe_binding_rejects_byte_counts_past_a_tensor():
+    torch = pytest.importorskip("torch")
+    a = torch.zeros(64, dtype=torch.uint8)          # never handed to the library
+    sink = torch.zeros(bnbx.BNBX_PROBE_SINK_WORDS, dtype=torch.int32)
+    with pytest.raises(bnbx.BnbxError) as e:
+        bnbx.bnbx_probe_stream_read(a, 80, None, 0, sink, 0)
+    assert e.value.status == bnbx.BNBX_E_INVAL
+    with pytest.raises(bnbx.BnbxError):
+        bnbx.bnbx_probe_stream_read(a, 32, a, 96, sink, 0)
+    with pytest.raises(bnbx.BnbxError):
+        bnbx.bnbx_probe_stream_read(a, 16, None, 0, sink[:10], 0)
 
 
 @pytest.mark.parametrize("fn", ["gemv", "gemm"])
