@@ -12,10 +12,10 @@
 namespace bnbx {
 namespace {
 
-constexpr int kDThreads = 256;
+constexpr int kDThreads = 1024;  // 1024 threads, one chunk per wave per round: measured fastest
 constexpr int kDWaves = kDThreads / 64;
 constexpr int kChunk = 1024;    // packed bytes per wave per chunk (2048 weights, 32 blocks)
-constexpr int kDUnroll = 2;     // chunks per wave per round
+constexpr int kDUnroll = 1;     // chunks per wave per round
 constexpr int kCopies = 4;      // LDS table copies (lane & 3) to spread bank conflicts
 
 template <bool DQ>
