@@ -446,23 +446,24 @@ __global__ __launch_bounds__(kMfWaves * 64, 1) void gemv_mfma_kernel(
   bf16x8_t xa[BPW][2];
   {
     // The slice is 16 rows x 8 BPW pieces; it passes through the region in
-    // four rounds of kPieces pieces per row (BPW / 4 blocks).
+    // four rounds of kPieces pieces per row (BPW / 4 blocks), whose loads all
+    // go out first (every workgroup reads all of X at once, so a round often
+    // waits for a miss; two rounds in flight took 3% longer).
     constexpr int kBr = BPW / 4;
-    u32x4_t xv[2][kLoads];   // two rounds in flight
+    u32x4_t xv[4][kLoads];
     auto xload = [&](int R) {
 #pragma unroll
       for (int u = 0; u < kLoads; ++u) {
         const int e = 64 * u + lane, r = e / kPieces, p = e % kPieces;
-        xv[R & 1][u] = __builtin_amdgcn_raw_buffer_load_b128(
+        xv[R][u] = __builtin_amdgcn_raw_buffer_load_b128(
             rx, (uint32_t)((int64_t)r * ldx * 2) + (uint32_t)(128 * b0 + 16 * (R * kPieces + p)), 0, 0);
       }
     };
-    xload(0);
-    xload(1);
+#pragma unroll
+    for (int R = 0; R < 4; ++R) xload(R);
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
-      put(xv[R & 1]);
-      if (R + 2 < 4) xload(R + 2);
+      put(xv[R]);
 #pragma unroll
       for (int ib = 0; ib < kBr; ++ib)
 #pragma unroll
