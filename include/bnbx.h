@@ -72,7 +72,7 @@ typedef enum {
   BNBX_OK = 0,
   BNBX_E_INVAL = -1,        /* bad size, null pointer, out-of-range argument   */
   BNBX_E_ALIGN = -2,        /* a pointer or leading dimension is misaligned    */
-  BNBX_E_UNSUPPORTED = -3,  /* valid request this build does not implement     */
+  BNBX_E_UNSUPPORTED = -3,  /* valid request the library does not implement    */
   BNBX_E_WORKSPACE = -4,    /* workspace missing or smaller than required      */
   BNBX_E_HIP = -5           /* the HIP runtime reported an error at launch     */
 } bnbx_status;
@@ -140,8 +140,8 @@ BNBX_API int bnbx_gemv_nf4(const uint16_t* x, int64_t ldx, const uint8_t* packed
                   const bnbx_nf4_state* st, int M, int N, int K,
                   uint16_t* y, int64_t ldy, void* stream);
 
-/* Bytes of device workspace bnbx_gemm_nf4 needs for (M, N, K); this build
- * needs none and returns 0 for valid sizes. */
+/* Bytes of device workspace bnbx_gemm_nf4 needs for (M, N, K); the current
+ * kernels need none, so it returns 0 for valid sizes. */
 BNBX_API size_t bnbx_gemm_nf4_workspace_bytes(int M, int N, int K);
 
 /* Prefill GEMM, Y[M, N] = X[M, K] . W_hat[N, K]^T for any M >= 1: weight
