@@ -17,6 +17,10 @@ silent the reading taken is stated at the function.  Parity status:
 * dequant             -- pinned (absmax 1 block, bounds)
 * matmul              -- pinned (unit vector, brute-force loops)
 * memory arithmetic   -- pinned against the figures the pages print
+* FP4 levels          -- pinned (the E2M1 value table, brute-force nearest
+                         level over the 15 distinct values, error bound)
+* FP16 rounding       -- pinned (hand-worked ties, subnormals, overflow;
+                         torch's own float -> half conversion)
 """
 
 from .nf4 import (  # noqa: F401
@@ -24,6 +28,15 @@ from .nf4 import (  # noqa: F401
     DQ_GROUP,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
+    f16_bits_to_f32,
+    f32_to_f16_bits,
+    bits_to_f32,
+    f32_to_bits,
+    QUANT_TYPES,
+    DTYPES,
+    fp4_codebook,
+    levels_by_code,
+    sorted_codes,
     normal_quantile,
     codebook,
     thresholds,

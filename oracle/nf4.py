@@ -21,9 +21,15 @@ Sources (five web pages about bitsandbytes; cited by page and section):
   holds the blockwise quantization and the NF4 format; ``Linear4bit``
   replaces ``torch.nn.Linear`` (weight laid out [out_features, in_features]).
 
+* same article, section 4 (the 4-bit loading options): the 4-bit quant type
+  is ``nf4`` (the NormalFloat levels) or ``fp4`` (a plain 4-bit float,
+  usually worse than nf4), and the compute dtype is BF16 or FP16; the
+  csdn.net feature page (example 2) loads a model with FP4 the same way.
+
 Parameters the pages leave open (blocksize 64, second-level groups of 256,
-int8 second level with the mean removed, lower-index tie rule) are the ones
-the build fixes for this path; every such reading is noted where it is used.
+int8 second level with the mean removed, lower-index tie rule, the FP4 bit
+layout) are the ones this path fixes; every such reading is noted where it
+is used.
 """
 
 from __future__ import annotations
@@ -36,6 +42,8 @@ import numpy as np
 BLOCKSIZE = 64      # weights per first-level block (reading: fixed at 64)
 DQ_GROUP = 256      # first-level scales per second-level group (reading)
 ZERO_CODE = 7       # index of the exact 0.0 level in the ascending codebook
+QUANT_TYPES = ("nf4", "fp4")
+DTYPES = ("bf16", "f16")
 
 
 # --------------------------------------------------------------------------
@@ -63,6 +71,40 @@ def f32_to_bf16_bits(values) -> np.ndarray:
     if nan.any():  # keep NaNs NaN (quiet bit set) instead of rounding to inf
         out[nan] = ((u[nan] >> np.uint64(16)) | np.uint64(0x40)).astype(np.uint16)
     return out
+
+
+def f16_bits_to_f32(bits) -> np.ndarray:
+    """Widen IEEE binary16 bit patterns (uint16) to binary32 (exact)."""
+    u = np.ascontiguousarray(bits, dtype=np.uint16)
+    return u.view(np.float16).astype(np.float32)
+
+
+def f32_to_f16_bits(values) -> np.ndarray:
+    """Round binary32 to IEEE binary16 (round to nearest even, subnormals
+    kept, overflow to infinity) and return the bit patterns.  FP16 is the
+    other compute dtype of section 4 of the mlqm.cn article.  Library
+    primitive: NumPy's float32 -> float16 conversion."""
+    f = np.ascontiguousarray(values, dtype=np.float32)
+    with np.errstate(over="ignore"):
+        return f.astype(np.float16).view(np.uint16)
+
+
+def bits_to_f32(bits, dtype: str = "bf16") -> np.ndarray:
+    """16-bit patterns of the compute dtype ("bf16" or "f16") to binary32."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(bits)
+    if dtype == "f16":
+        return f16_bits_to_f32(bits)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def f32_to_bits(values, dtype: str = "bf16") -> np.ndarray:
+    """Round binary32 to the compute dtype ("bf16" or "f16"), RNE."""
+    if dtype == "bf16":
+        return f32_to_bf16_bits(values)
+    if dtype == "f16":
+        return f32_to_f16_bits(values)
+    raise ValueError(f"unknown dtype {dtype!r}")
 
 
 # --------------------------------------------------------------------------
@@ -106,21 +148,69 @@ def codebook() -> np.ndarray:
 
 
 def thresholds(levels: np.ndarray) -> np.ndarray:
-    """Decision thresholds T[0..14] for nearest-level encoding.
+    """Decision thresholds T[0..len-2] for nearest-level encoding over
+    ascending levels (15 for NF4).
 
     The midpoint m_i of levels i and i+1 is exact in binary64.  T_i is the
     smallest binary32 strictly above m_i, so that ``#{i : x >= T_i}`` is the
     index of the nearest level and a value exactly on a midpoint goes to the
     LOWER index (the tie rule this path fixes; the pages state none)."""
     L = np.asarray(levels, dtype=np.float32).astype(np.float64)
-    out = np.empty(15, dtype=np.float32)
-    for i in range(15):
+    out = np.empty(L.size - 1, dtype=np.float32)
+    for i in range(L.size - 1):
         mid = (L[i] + L[i + 1]) / 2.0
         t = np.float32(mid)
         if float(t) <= mid:
             t = np.nextafter(t, np.float32(np.inf), dtype=np.float32)
         out[i] = t
     return out
+
+
+# --------------------------------------------------------------------------
+# Step 1b: the FP4 codebook (the other 4-bit quant type)
+# --------------------------------------------------------------------------
+def fp4_codebook() -> np.ndarray:
+    """The 16 FP4 levels indexed by code, as binary32.
+
+    mlqm.cn article, section 4: besides nf4 the 4-bit quant type may be
+    ``fp4``, a plain 4-bit floating-point format; the pages give no bit
+    layout.  Reading: the common E2M1 layout -- bit 3 the sign, bits 2-1 a
+    biased exponent e, bit 0 a mantissa bit m; the magnitude is m/2 for
+    e = 0 (zero and the one subnormal) and 2^(e-1) * (1 + m/2) otherwise,
+    so codes 0..7 hold 0, 1/2, 1, 3/2, 2, 3, 4, 6.  Every level is divided
+    by the largest magnitude, 6, so that the block absmax maps to +-1 as
+    with NF4.  Binary64 arithmetic, one rounding to binary32."""
+    out = []
+    for c in range(16):
+        sign = -1.0 if c & 8 else 1.0
+        e = (c >> 1) & 3
+        m = c & 1
+        mag = m / 2.0 if e == 0 else 2.0 ** (e - 1) * (1.0 + m / 2.0)
+        out.append(sign * mag / 6.0)
+    return np.array(out, dtype=np.float64).astype(np.float32)
+
+
+def levels_by_code(quant_type: str = "nf4") -> np.ndarray:
+    """Level of each 4-bit code (float32[16]): the ascending NF4 codebook, or
+    the FP4 levels in code order."""
+    if quant_type == "nf4":
+        return codebook()
+    if quant_type == "fp4":
+        return fp4_codebook()
+    raise ValueError(f"unknown quant type {quant_type!r}")
+
+
+def sorted_codes(quant_type: str = "nf4") -> np.ndarray:
+    """Codes of the distinct levels, by ascending level value.  NF4 codes
+    are already in value order.  For FP4 both zero codes decode to 0; the
+    encoder emits only code 0 (+0), so code 8 (-0) is left out and the 15
+    remaining levels are sorted (reading)."""
+    if quant_type == "nf4":
+        return np.arange(16, dtype=np.uint8)
+    levels = levels_by_code(quant_type)
+    codes = [c for c in range(16) if c != 8]
+    codes.sort(key=lambda c: float(levels[c]))
+    return np.array(codes, dtype=np.uint8)
 
 
 # --------------------------------------------------------------------------
@@ -144,14 +234,17 @@ def block_absmax(wf: np.ndarray, blocksize: int = BLOCKSIZE) -> np.ndarray:
 
 
 def encode(wf: np.ndarray, absmax: np.ndarray, thr: np.ndarray,
-           blocksize: int = BLOCKSIZE) -> np.ndarray:
+           blocksize: int = BLOCKSIZE, order: np.ndarray | None = None,
+           zero_code: int = ZERO_CODE) -> np.ndarray:
     """4-bit code of every weight (uint8 values 0..15).
 
     Normalise into [-1, 1] with the block's binary32 reciprocal,
     x = fl32(w * fl32(1 / a_b)) (reading: multiply by the reciprocal rather
     than divide), then count the thresholds at or below x, which picks the
-    nearest level (section 3.2).  A block whose absmax is 0 is all zero
-    weights and takes the zero level's code for every element (reading)."""
+    nearest level (section 3.2).  ``order`` maps that ascending level index
+    to its code (identity for NF4, ``sorted_codes("fp4")`` for FP4).  A
+    block whose absmax is 0 is all zero weights and takes the zero level's
+    code for every element (reading)."""
     wf = np.ascontiguousarray(wf, dtype=np.float32).ravel()
     n = wf.size
     block = np.arange(n) // blocksize
@@ -162,8 +255,10 @@ def encode(wf: np.ndarray, absmax: np.ndarray, thr: np.ndarray,
     with np.errstate(invalid="ignore"):
         for t in np.asarray(thr, dtype=np.float32):
             codes += (x >= t).astype(np.uint8)
+    if order is not None:
+        codes = np.asarray(order, dtype=np.uint8)[codes]
     zero_block = absmax[block] == 0
-    codes[zero_block] = ZERO_CODE
+    codes[zero_block] = zero_code
     return codes
 
 
@@ -243,8 +338,10 @@ def block_scales(state: dict) -> np.ndarray:
 
 
 def quantize(w_bits: np.ndarray, double_quant_on: bool,
-             blocksize: int = BLOCKSIZE, group: int = DQ_GROUP) -> dict:
-    """Blockwise NF4 quantize-on-load of a bfloat16 weight (bit patterns).
+             blocksize: int = BLOCKSIZE, group: int = DQ_GROUP,
+             quant_type: str = "nf4") -> dict:
+    """Blockwise 4-bit (NF4 or FP4) quantize-on-load of a bfloat16 weight
+    (bit patterns).
 
     Returns a dict with ``codes`` (uint8[n]), ``packed`` (uint8[n/2]) and the
     quant state: ``absmax`` (float32[nb], or int8[nb] with double quant),
@@ -252,11 +349,14 @@ def quantize(w_bits: np.ndarray, double_quant_on: bool,
     quant, plus ``absmax_fp32`` (the first-level scales before the second
     quantization)."""
     wf = bf16_bits_to_f32(np.ascontiguousarray(w_bits).ravel())
-    levels = codebook()
-    thr = thresholds(levels)
+    levels = levels_by_code(quant_type)
+    order = sorted_codes(quant_type)
+    thr = thresholds(levels[order])
+    zero_code = int(order[int(np.flatnonzero(levels[order] == 0)[0])])
     a = block_absmax(wf, blocksize)
-    codes = encode(wf, a, thr, blocksize)
+    codes = encode(wf, a, thr, blocksize, order=order, zero_code=zero_code)
     out = {
+        "quant_type": quant_type,
         "n": wf.size,
         "blocksize": blocksize,
         "double_quant": bool(double_quant_on),
@@ -276,40 +376,43 @@ def quantize(w_bits: np.ndarray, double_quant_on: bool,
 # --------------------------------------------------------------------------
 # Step 6: dequantize to bfloat16
 # --------------------------------------------------------------------------
-def dequantize(packed: np.ndarray, state: dict, n: int | None = None) -> np.ndarray:
-    """W_hat_j = bf16(fl32(L[c_j] * a_hat_b)) as bfloat16 bit patterns
-    (section 3.4: dequantize back to the 16-bit compute dtype, BF16)."""
+def dequantize(packed: np.ndarray, state: dict, n: int | None = None,
+               dtype: str = "bf16") -> np.ndarray:
+    """W_hat_j = rnd(fl32(L[c_j] * a_hat_b)) as 16-bit patterns of the compute
+    dtype, rnd = round to nearest even into BF16 or FP16 (section 3.4:
+    dequantize back to the 16-bit compute dtype; section 4: BF16 or FP16).
+    L is the level of each code for the state's quant type."""
     codes = unpack_nibbles(packed)
     if n is None:
         n = codes.size
     codes = codes[:n]
-    levels = codebook()
+    levels = levels_by_code(state.get("quant_type", "nf4"))
     blocksize = state.get("blocksize", BLOCKSIZE)
     scale = block_scales(state)
     b = np.arange(n) // blocksize
     v = (levels[codes] * scale[b]).astype(np.float32)
-    return f32_to_bf16_bits(v)
+    return f32_to_bits(v, dtype)
 
 
 # --------------------------------------------------------------------------
 # Step 7/8: the 4-bit-storage / 16-bit-compute linear layer
 # --------------------------------------------------------------------------
-def matmul_ref(x_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+def matmul_ref(x_bits: np.ndarray, w_bits: np.ndarray, dtype: str = "bf16") -> np.ndarray:
     """Y = X . W^T in binary64 (nn.Linear orientation, no bias; pomoai.com
     overview, Linear4bit replacing torch.nn.Linear).  X is [M, K], W is
-    [N, K], both bfloat16 bit patterns; the result is float64 [M, N].
-    Library primitive: NumPy's binary64 matmul."""
-    x = bf16_bits_to_f32(x_bits).astype(np.float64)
-    w = bf16_bits_to_f32(w_bits).astype(np.float64)
+    [N, K], both 16-bit patterns of the compute dtype; the result is float64
+    [M, N].  Library primitive: NumPy's binary64 matmul."""
+    x = bits_to_f32(x_bits, dtype).astype(np.float64)
+    w = bits_to_f32(w_bits, dtype).astype(np.float64)
     return x @ w.T
 
 
 def dequant_matmul_ref(x_bits: np.ndarray, packed: np.ndarray, state: dict,
-                       N: int, K: int) -> np.ndarray:
+                       N: int, K: int, dtype: str = "bf16") -> np.ndarray:
     """The reference the dequant-GEMV/GEMM is compared to: dequantize the
-    4-bit weight to BF16 (step 6), then multiply in binary64."""
-    w_hat = dequantize(packed, state, N * K).reshape(N, K)
-    return matmul_ref(np.asarray(x_bits).reshape(-1, K), w_hat)
+    4-bit weight to the compute dtype (step 6), then multiply in binary64."""
+    w_hat = dequantize(packed, state, N * K, dtype).reshape(N, K)
+    return matmul_ref(np.asarray(x_bits).reshape(-1, K), w_hat, dtype)
 
 
 def rel_frobenius(y, y_ref) -> float:

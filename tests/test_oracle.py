@@ -410,3 +410,180 @@ def test_nf4_error_below_uniform_int4():
     g = json.load(open(GOLDEN))
     assert mse_nf4 < mse_int4
     assert mse_nf4 / mse_int4 < 1.0 and g["nf4_vs_int4_error_ratio_about"]["value"] < 1.0
+
+
+# --------------------------------------------------------------------------
+# FP4, the other 4-bit quant type (mlqm.cn article, section 4)
+# --------------------------------------------------------------------------
+# The E2M1 element values as the OCP Microscaling Formats specification
+# (v1.0, FP4 E2M1 table) lists them for codes 0b0000 .. 0b0111; codes with
+# bit 3 set are their negatives.  Typed in from the standard, independent of
+# the oracle's bit-field decoding.
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_fp4_levels_are_the_e2m1_table():
+    L = oracle.fp4_codebook()
+    want = np.array(E2M1_TABLE + [-v for v in E2M1_TABLE], dtype=np.float64) / 6.0
+    assert np.array_equal(L, want.astype(np.float32))
+    assert L[7] == 1.0 and L[15] == -1.0 and L[0] == 0.0 and L[8] == 0.0
+    assert np.all(L[8:] == -L[:8])
+    assert np.max(np.abs(L)) == 1.0
+
+
+def test_fp4_sorted_codes():
+    L = oracle.fp4_codebook()
+    order = oracle.sorted_codes("fp4")
+    assert order.size == 15 and 8 not in order.tolist()
+    assert np.all(np.diff(L[order].astype(np.float64)) > 0)
+    assert list(order[:8]) == [15, 14, 13, 12, 11, 10, 9, 0]
+    assert np.array_equal(oracle.sorted_codes("nf4"), np.arange(16))
+
+
+def brute_fp4_codes(x: np.ndarray) -> np.ndarray:
+    """Nearest of the 15 distinct FP4 levels in binary64, the lower value on
+    ties, as its code: a direct search over the codes, independent of the
+    threshold table and of the code order used by the encoder."""
+    L = oracle.fp4_codebook().astype(np.float64)
+    codes = [c for c in range(16) if c != 8]
+    best = np.full(x.size, -1, dtype=np.int64)
+    bestd = np.full(x.size, np.inf)
+    xd = x.astype(np.float64)
+    for c in codes:
+        d = np.abs(xd - L[c])
+        better = (d < bestd) | ((d == bestd) & (L[c] < L[np.maximum(best, 0)]))
+        best = np.where(better, c, best)
+        bestd = np.where(better, d, bestd)
+    return best.astype(np.uint8)
+
+
+def _quantize_unit_fp4(x):
+    # blocks of 63 values plus a +1 anchor: the absmax is exactly 1, so the
+    # normalisation is the identity
+    x = np.asarray(x, dtype=np.float32)
+    nblk = -(-x.size // 63)
+    body = np.zeros(nblk * 63, np.float32)
+    body[:x.size] = x
+    w = np.concatenate([body.reshape(nblk, 63), np.ones((nblk, 1), np.float32)], axis=1).ravel()
+    bits = oracle.f32_to_bf16_bits(w)
+    assert np.array_equal(oracle.bf16_bits_to_f32(bits), w)   # inputs are bf16 values
+    q = oracle.quantize(bits, False, quant_type="fp4")
+    assert np.all(q["absmax"] == 1.0)
+    return q["codes"].reshape(nblk, 64)[:, :63].ravel()[:x.size]
+
+
+def test_fp4_encode_matches_bruteforce():
+    L = oracle.fp4_codebook().astype(np.float64)
+    order = oracle.sorted_codes("fp4")
+    xs = []
+    for a, b in zip(L[order][:-1], L[order][1:]):     # bf16 values around each midpoint
+        m = np.float32((a + b) / 2)
+        bits = oracle.f32_to_bf16_bits(np.array([m], np.float32))[0].astype(np.int32)
+        xs += [oracle.bf16_bits_to_f32(np.array([(bits + k) & 0xFFFF], np.uint16))[0]
+               for k in range(-40, 41)]
+    rng = np.random.default_rng(21)
+    xs = np.concatenate([np.array(xs, np.float32),
+                         oracle.bf16_bits_to_f32(oracle.f32_to_bf16_bits(
+                             rng.uniform(-1, 1, 60000).astype(np.float32))),
+                         np.array([-1.0, 1.0, 0.0, -0.0, -2.0 ** -100, 2.0 ** -100], np.float32)])
+    xs = xs[np.abs(xs) <= 1]
+    assert np.array_equal(_quantize_unit_fp4(xs), brute_fp4_codes(xs))
+
+
+def test_fp4_exact_midpoint_ties_go_to_lower_value():
+    L = oracle.fp4_codebook().astype(np.float64)
+    order = oracle.sorted_codes("fp4")
+    found = 0
+    for i in range(14):
+        m = (L[order[i]] + L[order[i + 1]]) / 2
+        if float(np.float32(m)) == m:
+            found += 1
+            x = np.array([m], np.float32)
+            assert oracle.encode(x, np.ones(1, np.float32),
+                                 oracle.thresholds(L[order].astype(np.float32)),
+                                 order=order, zero_code=0)[0] == order[i]
+            assert brute_fp4_codes(x)[0] == order[i]
+    assert found >= 2     # the two midpoints next to 0 (+-fl32(1/12)/2) are exact
+
+
+def test_fp4_zero_block_negative_zero_never_emitted():
+    w = np.zeros(64 + 64, dtype=np.uint16)
+    rng = np.random.default_rng(8)
+    tail = rng.standard_normal(64).astype(np.float32) * np.float32(1e-6)
+    tail[0] = 5.0
+    w[64:] = oracle.f32_to_bf16_bits(tail)
+    q = oracle.quantize(w, False, quant_type="fp4")
+    assert np.all(q["codes"][:64] == 0)
+    assert not np.any(q["codes"] == 8)
+    assert np.all(q["codes"][65:] == 0)          # tiny values of either sign -> +0
+    deq = oracle.dequantize(q["packed"], q, w.size)
+    assert np.all(deq[:64] == 0) and np.all(deq[65:] == 0)
+
+
+def test_fp4_reconstruction_error_bound():
+    L = oracle.fp4_codebook().astype(np.float64)
+    srt = np.sort(np.unique(L))
+    hmax = np.max(np.diff(srt)) / 2
+    assert abs(hmax - 1.0 / 6.0) < 1e-7        # the 2/3 .. 1 gap
+    rng = np.random.default_rng(4)
+    for dq in (False, True):
+        w = oracle.f32_to_bf16_bits(rng.standard_normal(64 * 600).astype(np.float32) * np.float32(0.02))
+        q = oracle.quantize(w, dq, quant_type="fp4")
+        wf = oracle.bf16_bits_to_f32(w).astype(np.float64)
+        a = np.repeat(q["absmax_fp32"].astype(np.float64), 64)
+        rec = L[q["codes"]] * a
+        assert np.all(np.abs(wf - rec) <= a * hmax * (1 + 2.0 ** -20))
+
+
+def test_fp4_dequant_with_unit_absmax_returns_levels():
+    L = oracle.fp4_codebook()
+    order = oracle.sorted_codes("fp4")
+    vals = np.concatenate([L[order], L[order], L[order], L[order][:19]])   # 64 values, max 1
+    w = oracle.f32_to_bf16_bits(vals)
+    q = oracle.quantize(w, False, quant_type="fp4")
+    assert q["absmax"][0] == 1.0
+    assert np.array_equal(q["codes"], np.concatenate([order, order, order, order[:19]]))
+    assert np.array_equal(oracle.dequantize(q["packed"], q), oracle.f32_to_bf16_bits(vals))
+
+
+# --------------------------------------------------------------------------
+# FP16 compute dtype (mlqm.cn article, section 4)
+# --------------------------------------------------------------------------
+def test_f16_rounding_hand_cases():
+    f = np.array([65504.0, 65519.996, 65520.0, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -25,
+                  1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, -2.0, 0.0, -0.0, 2.0 ** -14], np.float32)
+    want = [0x7BFF, 0x7BFF, 0x7C00, 0x0001, 0x0000, 0x0002,
+            0x3C00, 0x3C02, 0xC000, 0x0000, 0x8000, 0x0400]
+    assert oracle.f32_to_f16_bits(f).tolist() == want
+    assert oracle.f16_bits_to_f32(np.array(want[:2], np.uint16)).tolist() == [65504.0, 65504.0]
+
+
+def test_f16_rounding_matches_torch():
+    import torch
+
+    rng = np.random.default_rng(9)
+    f = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32) * np.float32(3.0),
+        (rng.standard_normal(2000) * 1e-6).astype(np.float32),      # subnormal range
+        (rng.standard_normal(2000) * 7e4).astype(np.float32),       # around overflow
+    ])
+    # binary32 values exactly halfway between two binary16 neighbours
+    h = rng.integers(0, 0x7BFF, 4000).astype(np.uint16)
+    lo = oracle.f16_bits_to_f32(h).astype(np.float64)
+    hi = oracle.f16_bits_to_f32(h + np.uint16(1)).astype(np.float64)
+    f = np.concatenate([f, ((lo + hi) / 2).astype(np.float32)])
+    ours = oracle.f32_to_f16_bits(f)
+    ref = torch.from_numpy(f).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_f16_dequant_hand_example():
+    L = oracle.codebook()
+    lv = oracle.f32_to_bf16_bits(L * np.float32(3.0))
+    w = np.tile(lv, 4)                               # absmax 3, every level once per 16
+    q = oracle.quantize(w, False)
+    assert q["absmax"][0] == 3.0
+    deq = oracle.dequantize(q["packed"], q, dtype="f16")
+    assert deq[15] == 0x4200 and deq[0] == 0xC200 and deq[7] == 0x0000   # 3, -3, +0
+    want = oracle.f32_to_f16_bits((L * np.float32(3.0)).astype(np.float32))
+    assert np.array_equal(deq, np.tile(want, 4))
