@@ -20,10 +20,12 @@ import os
 __all__ = [
     "BNBX_OK", "BNBX_E_INVAL", "BNBX_E_ALIGN", "BNBX_E_UNSUPPORTED", "BNBX_E_WORKSPACE",
     "BNBX_E_HIP", "BnbxError", "BnbxLibraryMissing", "Nf4State", "library_path", "lib",
-    "bnbx_status_str", "bnbx_nf4_codebook", "bnbx_quantize_nf4_workspace_bytes",
+    "bnbx_status_str", "bnbx_nf4_codebook", "bnbx_fp4_codebook",
+    "bnbx_quantize_nf4_workspace_bytes",
     "bnbx_quantize_nf4", "bnbx_dequantize_nf4", "bnbx_gemv_nf4",
     "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4", "bnbx_probe_stream_read",
-    "BNBX_PROBE_SINK_WORDS", "EXPORTED_SYMBOLS",
+    "BNBX_PROBE_SINK_WORDS", "EXPORTED_SYMBOLS", "BNBX_QUANT_NF4", "BNBX_QUANT_FP4",
+    "BNBX_DTYPE_BF16", "BNBX_DTYPE_F16",
 ]
 
 BNBX_OK = 0
@@ -33,8 +35,14 @@ BNBX_E_UNSUPPORTED = -3
 BNBX_E_WORKSPACE = -4
 BNBX_E_HIP = -5
 
+BNBX_QUANT_NF4 = 0
+BNBX_QUANT_FP4 = 1
+BNBX_DTYPE_BF16 = 0
+BNBX_DTYPE_F16 = 1
+
 EXPORTED_SYMBOLS = (
-    "bnbx_status_str", "bnbx_nf4_codebook", "bnbx_quantize_nf4_workspace_bytes",
+    "bnbx_status_str", "bnbx_nf4_codebook", "bnbx_fp4_codebook",
+    "bnbx_quantize_nf4_workspace_bytes",
     "bnbx_quantize_nf4", "bnbx_dequantize_nf4", "bnbx_gemv_nf4",
     "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4",
     "bnbx_probe_stream_read",          # include/bnbx_probe.h (measurement aid)
@@ -65,6 +73,8 @@ class Nf4State(ctypes.Structure):
         ("n", ctypes.c_int64),
         ("blocksize", ctypes.c_int32),
         ("double_quant", ctypes.c_int32),
+        ("quant_type", ctypes.c_int32),
+        ("compute_dtype", ctypes.c_int32),
         ("absmax", ctypes.c_void_p),
         ("absmax2", ctypes.c_void_p),
         ("absmax_mean", ctypes.c_void_p),
@@ -90,6 +100,8 @@ def lib() -> ctypes.CDLL:
     L.bnbx_status_str.restype = ctypes.c_char_p
     L.bnbx_nf4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
     L.bnbx_nf4_codebook.restype = i32
+    L.bnbx_fp4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
+    L.bnbx_fp4_codebook.restype = i32
     L.bnbx_quantize_nf4_workspace_bytes.argtypes = [i64, i32, i32]
     L.bnbx_quantize_nf4_workspace_bytes.restype = sz
     L.bnbx_quantize_nf4.argtypes = [vp, vp, sp, vp, sz, vp]
@@ -142,6 +154,12 @@ def bnbx_status_str(status: int) -> str:
 def bnbx_nf4_codebook() -> list[float]:
     buf = (ctypes.c_float * 16)()
     _check(lib().bnbx_nf4_codebook(buf), "bnbx_nf4_codebook")
+    return list(buf)
+
+
+def bnbx_fp4_codebook() -> list[float]:
+    buf = (ctypes.c_float * 16)()
+    _check(lib().bnbx_fp4_codebook(buf), "bnbx_fp4_codebook")
     return list(buf)
 
 

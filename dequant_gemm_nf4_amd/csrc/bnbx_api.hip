@@ -32,8 +32,7 @@ double normal_quantile_upper(double p) {
 }
 
 struct Tables {
-  float levels[16];
-  float thr[15];
+  float levels[16];   // level of each code
   EncodeTable enc;
   LevelTable lv;
 };
@@ -43,7 +42,8 @@ struct Tables {
 // positive quantiles of probabilities evenly spaced from the offset toward
 // 1/2, 7 mirrored negative ones over the same span, and 0, all divided by the
 // outermost quantile.  The offset averages the 1/30 and 1/32 tail masses.
-void build_tables(Tables& t) {
+// Codes are in ascending level order.
+void nf4_levels(float* levels) {
   const double off = 1.0 - 0.5 * (1.0 / 30.0 + 1.0 / 32.0);
   const double top = normal_quantile_upper(off);
   double v[16];
@@ -52,50 +52,94 @@ void build_tables(Tables& t) {
   v[k++] = 0.0;
   for (int i = 0; i < 8; ++i) v[k++] = normal_quantile_upper(off + i * (0.5 - off) / 8.0);
   std::sort(v, v + 16);
-  for (int i = 0; i < 16; ++i) t.levels[i] = (float)(v[i] / top);   // ends: +-top/top = +-1
+  for (int i = 0; i < 16; ++i) levels[i] = (float)(v[i] / top);   // ends: +-top/top = +-1
+}
 
-  // Nearest-level thresholds: smallest float strictly above each midpoint,
-  // so an exact tie takes the lower index.
-  for (int i = 0; i < 15; ++i) {
-    const double mid = ((double)t.levels[i] + (double)t.levels[i + 1]) * 0.5;
+// FP4 (mlqm.cn article, sec. 4: the plain 4-bit float quant type; the pages
+// give no layout, E2M1 is taken): code bit 3 is the sign, bits 2-1 the
+// exponent e, bit 0 the mantissa m; magnitude m/2 for e = 0, else
+// 2^(e-1) (1 + m/2), i.e. 0, 0.5, 1, 1.5, 2, 3, 4, 6 for codes 0-7, divided by
+// 6 so the block absmax maps to +-1.
+void fp4_levels(float* levels) {
+  for (int c = 0; c < 16; ++c) {
+    const int e = (c >> 1) & 3, m = c & 1;
+    const double mag = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    levels[c] = (float)((c & 8 ? -mag : mag) / 6.0);
+  }
+}
+
+// Encode tables of a codebook.  `order` lists the codes of the distinct
+// levels by ascending value (count of them in `nl`; FP4 leaves out -0, code
+// 8, which the encoder never emits).  Thresholds: the smallest float strictly
+// above each midpoint of neighbouring levels, so the nearest level wins and
+// an exact tie takes the lower one.
+void build_encode(const float* levels, const int* order, int nl, bool in_order, EncodeTable& enc) {
+  float thr[15];
+  for (int i = 0; i + 1 < nl; ++i) {
+    const double mid = ((double)levels[order[i]] + (double)levels[order[i + 1]]) * 0.5;
     float th = (float)mid;
     if ((double)th <= mid) th = nextafterf(th, INFINITY);
-    t.thr[i] = th;
+    thr[i] = th;
   }
-
   // Encode buckets: bucket b holds x with round-half-even(16x + 16) == b,
   // i.e. x in [(b - 1/2)/16 - 1, (b + 1/2)/16 - 1].  Each bucket must hold at
   // most one threshold and no threshold may sit near a bucket edge (the
   // rounding of 16x + 16 moves an edge by far less than the margin checked).
   for (int b = 0; b < kBuckets; ++b) {
     const double lo = (b - 0.5) / 16.0 - 1.0, hi = (b + 0.5) / 16.0 - 1.0;
-    uint32_t base = 0;
+    uint32_t below = 0;
     float inside = INFINITY;
     int count = 0;
-    for (int i = 0; i < 15; ++i) {
-      const double th = t.thr[i];
+    for (int i = 0; i + 1 < nl; ++i) {
+      const double th = thr[i];
       if (fabs(th - lo) < 1e-4 || fabs(th - hi) < 1e-4) {
-        fprintf(stderr, "bnbx: NF4 threshold too close to an encode bucket edge\n");
+        fprintf(stderr, "bnbx: codebook threshold too close to an encode bucket edge\n");
         abort();
       }
-      if (th < lo) ++base;
-      else if (th < hi) { inside = t.thr[i]; ++count; }
+      if (th < lo) ++below;
+      else if (th < hi) { inside = thr[i]; ++count; }
     }
     if (count > 1) {
-      fprintf(stderr, "bnbx: two NF4 thresholds in one encode bucket\n");
+      fprintf(stderr, "bnbx: two codebook thresholds in one encode bucket\n");
       abort();
     }
-    t.enc.thr[b] = inside;
-    t.enc.base[b] = base;
+    enc.thr[b] = inside;
+    if (in_order) {
+      enc.base[b] = below;
+    } else {
+      const uint32_t c0 = (uint32_t)order[below];
+      const uint32_t c1 = count ? (uint32_t)order[below + 1] : c0;
+      enc.base[b] = c0 | (c1 << 4);
+    }
   }
+  enc.code_min = (uint32_t)order[0];
+  enc.code_max = (uint32_t)order[nl - 1];
+}
+
+void build_tables(int quant_type, Tables& t) {
+  int order[16];
+  int nl = 0;
+  if (quant_type == kQuantNF4) {
+    nf4_levels(t.levels);
+    for (int c = 0; c < 16; ++c) order[nl++] = c;
+  } else {
+    fp4_levels(t.levels);
+    for (int c = 0; c < 16; ++c)
+      if (c != 8) order[nl++] = c;
+    std::sort(order, order + nl, [&](int a, int b) { return t.levels[a] < t.levels[b]; });
+  }
+  build_encode(t.levels, order, nl, quant_type == kQuantNF4, t.enc);
   for (int i = 0; i < 16; ++i) t.lv.level[i] = t.levels[i];
 }
 
-const Tables& tables() {
-  static Tables t;
+const Tables& tables(int quant_type) {
+  static Tables t[2];
   static std::once_flag once;
-  std::call_once(once, [] { build_tables(t); });
-  return t;
+  std::call_once(once, [] {
+    build_tables(kQuantNF4, t[0]);
+    build_tables(kQuantFP4, t[1]);
+  });
+  return t[quant_type == kQuantFP4 ? 1 : 0];
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -108,6 +152,9 @@ int check_state(const bnbx_nf4_state* st) {
   if (st->n < 2 || (st->n & 1)) return BNBX_E_INVAL;
   if (st->blocksize != kBlock) return BNBX_E_UNSUPPORTED;
   if (st->double_quant != 0 && st->double_quant != 1) return BNBX_E_INVAL;
+  if (st->quant_type != BNBX_QUANT_NF4 && st->quant_type != BNBX_QUANT_FP4) return BNBX_E_INVAL;
+  if (st->compute_dtype != BNBX_DTYPE_BF16 && st->compute_dtype != BNBX_DTYPE_F16)
+    return BNBX_E_INVAL;
   if (st->absmax == nullptr) return BNBX_E_INVAL;
   if (st->double_quant && (st->absmax2 == nullptr || st->absmax_mean == nullptr))
     return BNBX_E_INVAL;
@@ -132,10 +179,9 @@ int hip_status(hipError_t e) { return e == hipSuccess ? BNBX_OK : BNBX_E_HIP; }
 
 }  // namespace
 
-const float* levels_f32() { return tables().levels; }
-const float* thresholds_f32() { return tables().thr; }
-const EncodeTable& encode_table() { return tables().enc; }
-const LevelTable& level_table() { return tables().lv; }
+const float* levels_f32(int quant_type) { return tables(quant_type).levels; }
+const EncodeTable& encode_table(int quant_type) { return tables(quant_type).enc; }
+const LevelTable& level_table(int quant_type) { return tables(quant_type).lv; }
 
 }  // namespace bnbx
 
@@ -157,7 +203,14 @@ const char* bnbx_status_str(int status) {
 
 int bnbx_nf4_codebook(float levels_host[16]) {
   if (levels_host == nullptr) return BNBX_E_INVAL;
-  const float* l = levels_f32();
+  const float* l = levels_f32(kQuantNF4);
+  for (int i = 0; i < 16; ++i) levels_host[i] = l[i];
+  return BNBX_OK;
+}
+
+int bnbx_fp4_codebook(float levels_host[16]) {
+  if (levels_host == nullptr) return BNBX_E_INVAL;
+  const float* l = levels_f32(kQuantFP4);
   for (int i = 0; i < 16; ++i) levels_host[i] = l[i];
   return BNBX_OK;
 }
@@ -177,14 +230,14 @@ int bnbx_quantize_nf4(const uint16_t* w, uint8_t* packed, const bnbx_nf4_state* 
   const int64_t n = st->n, nb = nblocks(n);
   hipStream_t hs = (hipStream_t)stream;
   if (!st->double_quant) {
-    return hip_status(launch_quantize(w, packed, n, (float*)st->absmax, nullptr, hs));
+    return hip_status(launch_quantize(w, packed, n, (float*)st->absmax, nullptr, st->quant_type, hs));
   }
   const size_t need = dq_workspace_bytes(nb);
   if (workspace == nullptr || workspace_bytes < need) return BNBX_E_WORKSPACE;
   if (!aligned(workspace, 256)) return BNBX_E_ALIGN;
   unsigned long long* slots = (unsigned long long*)workspace;
   float* a32 = (float*)((char*)workspace + round_up(kSlotBytes, 256));
-  hipError_t e = launch_quantize(w, packed, n, a32, slots, hs);
+  hipError_t e = launch_quantize(w, packed, n, a32, slots, st->quant_type, hs);
   if (e == hipSuccess)
     e = launch_double_quant(a32, slots, quantize_grid(n), nb, (int8_t*)st->absmax, st->absmax2,
                             st->absmax_mean, hs);
@@ -198,7 +251,9 @@ int bnbx_dequantize_nf4(const uint8_t* packed, const bnbx_nf4_state* st, uint16_
   if (s != BNBX_OK) return s;
   if (!aligned(packed, 16) || !aligned(out, 16)) return BNBX_E_ALIGN;
   return hip_status(launch_dequantize(packed, st->n, st->absmax, st->absmax2, st->absmax_mean,
-                                      st->double_quant, out, (hipStream_t)stream));
+                                      st->double_quant, st->quant_type,
+                                      st->compute_dtype == BNBX_DTYPE_F16, out,
+                                      (hipStream_t)stream));
 }
 
 int bnbx_gemv_nf4(const uint16_t* x, int64_t ldx, const uint8_t* packed,
@@ -208,7 +263,9 @@ int bnbx_gemv_nf4(const uint16_t* x, int64_t ldx, const uint8_t* packed,
   if (s != BNBX_OK) return s;
   if (M > 16) return BNBX_E_INVAL;
   const hipError_t e = launch_gemv(x, ldx, packed, st->absmax, st->absmax2, st->absmax_mean,
-                                   st->double_quant, M, N, K, y, ldy, (hipStream_t)stream);
+                                   st->double_quant, st->quant_type,
+                                   st->compute_dtype == BNBX_DTYPE_F16, M, N, K, y, ldy,
+                                   (hipStream_t)stream);
   if (e == hipErrorNotSupported) return BNBX_E_UNSUPPORTED;
   return hip_status(e);
 }
@@ -228,7 +285,9 @@ int bnbx_gemm_nf4(const uint16_t* x, int64_t ldx, const uint8_t* packed,
   const int s = check_matmul(x, ldx, packed, st, M, N, K, y, ldy);
   if (s != BNBX_OK) return s;
   const hipError_t e = launch_gemm(x, ldx, packed, st->absmax, st->absmax2, st->absmax_mean,
-                                   st->double_quant, M, N, K, y, ldy, (hipStream_t)stream);
+                                   st->double_quant, st->quant_type,
+                                   st->compute_dtype == BNBX_DTYPE_F16, M, N, K, y, ldy,
+                                   (hipStream_t)stream);
   if (e == hipErrorNotSupported) return BNBX_E_UNSUPPORTED;
   return hip_status(e);
 }

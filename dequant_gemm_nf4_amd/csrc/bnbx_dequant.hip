@@ -1,10 +1,11 @@
-// Dequantize NF4 to bfloat16 for gfx950 (mlqm.cn bitsandbytes article, sec.
-// 3.4: weights stored in 4 bits are turned back into BF16 for the multiply).
+// Dequantize 4-bit codes (NF4 or FP4 levels) to bfloat16 or FP16 for gfx950
+// (mlqm.cn bitsandbytes article, sec. 3.4: weights stored in 4 bits are
+// turned back into BF16 or FP16 for the multiply; sec. 4: the compute dtype).
 //
 // Each lane reads 16 packed bytes (32 weights, half a block), looks up the
 // level pair of each byte in an LDS table, multiplies by the block scale in
-// binary32 and rounds the pair to bf16 with one v_cvt_pk_bf16_f32, writing
-// 64 bytes.  The block scale follows the stored format exactly:
+// binary32 and rounds the pair to the compute type (one v_cvt_pk_bf16_f32,
+// or two v_cvt_f16_f32), writing 64 bytes.  The block scale follows the stored format exactly:
 // a_b, or fl32(fl32(q_b * fl32(s_g / 127)) + mean) with double quantization.
 #include "bnbx_device.hpp"
 #include "bnbx_internal.hpp"
@@ -28,13 +29,14 @@ __device__ __forceinline__ float exact_block_scale(int64_t blk, const void* absm
   return prod + mu;                                   // ... then the add (no FMA)
 }
 
-// 8 weights (one packed dword) -> 16 bytes of bf16.
+// 8 weights (one packed dword) -> 16 bytes of the compute type.
+template <bool F16>
 __device__ __forceinline__ uint4 expand8(uint32_t d, float sc, const float2* tab) {
   uint32_t o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float2 lp = tab[(d >> (8 * i)) & 0xffu];
-    o[i] = pack_bf16x2(lp.x * sc, lp.y * sc);
+    o[i] = pack16x2<F16>(lp.x * sc, lp.y * sc);
   }
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
@@ -42,7 +44,7 @@ __device__ __forceinline__ uint4 expand8(uint32_t d, float sc, const float2* tab
 // Wave-level layout: in a 1 KB chunk of packed bytes, lane l handles packed
 // dwords l, 64+l, 128+l and 192+l, so every load instruction reads 256
 // contiguous bytes and every store instruction writes 1 KB contiguous.
-template <bool DQ>
+template <bool DQ, bool F16>
 __global__ __launch_bounds__(kDThreads) void dequant_kernel(
     const uint8_t* __restrict__ packed, int64_t n, const void* __restrict__ absmax,
     const float* __restrict__ absmax2, const float* __restrict__ mean,
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(kDThreads) void dequant_kernel(
           // dword k*64 + lane covers weights 8*(k*64+lane) .. +7: block 8k + lane/8
           const float sc = __int_as_float(
               __builtin_amdgcn_ds_bpermute((8 * k + (lane >> 3)) << 2, __float_as_int(scl[u])));
-          store_nt16(dst + k * 64 + lane, expand8(d[u][k], sc, tab));
+          store_nt16(dst + k * 64 + lane, expand8<F16>(d[u][k], sc, tab));
         }
       }
     }
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(kDThreads) void dequant_kernel(
     for (int64_t b = full * kChunk + lane; b < nbytes; b += 64) {
       const float sc = exact_block_scale<DQ>((b << 1) / kBlock, absmax, absmax2, mu);
       const float2 lp = tab[packed[b]];
-      const uint32_t pr = pack_bf16x2(lp.x * sc, lp.y * sc);
+      const uint32_t pr = pack16x2<F16>(lp.x * sc, lp.y * sc);
       out[2 * b] = (uint16_t)(pr & 0xffffu);
       out[2 * b + 1] = (uint16_t)(pr >> 16);
     }
@@ -111,17 +113,23 @@ __global__ __launch_bounds__(kDThreads) void dequant_kernel(
 
 hipError_t launch_dequantize(const uint8_t* packed, int64_t n, const void* absmax,
                              const float* absmax2, const float* mean, int double_quant,
-                             uint16_t* out, hipStream_t stream) {
+                             int quant_type, bool f16, uint16_t* out, hipStream_t stream) {
   const int64_t chunks = (n >> 1) / kChunk;
   int64_t grid = (chunks + kDWaves * kDUnroll - 1) / (kDWaves * kDUnroll);
   if (grid > 2048) grid = 2048;
   if (grid < 1) grid = 1;
-  if (double_quant)
-    hipLaunchKernelGGL(dequant_kernel<true>, dim3((unsigned)grid), dim3(kDThreads), 0, stream,
-                       packed, n, absmax, absmax2, mean, out, level_table());
-  else
-    hipLaunchKernelGGL(dequant_kernel<false>, dim3((unsigned)grid), dim3(kDThreads), 0, stream,
-                       packed, n, absmax, absmax2, mean, out, level_table());
+  const LevelTable& lv = level_table(quant_type);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kDThreads), 0, stream, packed, n, absmax,
+                       absmax2, mean, out, lv);
+  };
+  if (double_quant) {
+    if (f16) go(dequant_kernel<true, true>);
+    else go(dequant_kernel<true, false>);
+  } else {
+    if (f16) go(dequant_kernel<false, true>);
+    else go(dequant_kernel<false, false>);
+  }
   return hipGetLastError();
 }
 

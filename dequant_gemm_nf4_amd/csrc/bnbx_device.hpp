@@ -11,6 +11,8 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 
 // bfloat16 bits -> binary32 (exact).
 __device__ __forceinline__ float bf16lo_to_f32(uint32_t pair) { return __uint_as_float(pair << 16); }
@@ -30,6 +32,24 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(pack_bf16x2(f, 0.0f) & 0xffffu);
 }
 
+// The same for the compute type: bfloat16, or IEEE binary16 when F16
+// (v_cvt_f16_f32: round to nearest even, subnormals kept, overflow to inf).
+template <bool F16>
+__device__ __forceinline__ uint32_t pack16x2(float lo, float hi) {
+  if constexpr (F16) {
+    f16x2_t v;
+    v[0] = (_Float16)lo;
+    v[1] = (_Float16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    return pack_bf16x2(lo, hi);
+  }
+}
+template <bool F16>
+__device__ __forceinline__ uint16_t f32_to_16(float f) {
+  return (uint16_t)(pack16x2<F16>(f, 0.0f) & 0xffffu);
+}
+
 // v_perm_b32: byte k of the result is byte sel[k] of the 8-byte value
 // {hi, lo} (0..3 pick lo's bytes, 4..7 hi's bytes, 0x0c gives 0).
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
@@ -39,6 +59,35 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+// a.lo * b.lo + a.hi * b.hi + c over pairs of the compute type.
+template <bool F16>
+__device__ __forceinline__ float dot2_16(uint32_t a, uint32_t b, float c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b),
+                                  c, false);
+  else
+    return dot2_bf16(a, b, c);
+}
+
+// Matrix-core products over 8-element operands of the compute type (raw bits).
+template <bool F16>
+__device__ __forceinline__ f32x4_t mfma_16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+template <bool F16>
+__device__ __forceinline__ f32x16_t mfma_32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
 // 16-byte streaming load / store (non-temporal hint: data used once).

@@ -78,19 +78,28 @@ struct Tab16 {
   uint32_t h[4], l[4];
 };
 
-// The codebook's ends and middle are exactly -1 (L[0]), 0 (L[7]) and +1
-// (L[15]), so those three products need no multiply: -sc, a zero with sc's
-// sign, and sc.
+// Levels that are exactly -1, +0, -0 or +1 need no multiply: their products
+// are -sc, a zero with sc's sign, one with the opposite sign, and sc.  NF4:
+// L[0] = -1, L[7] = 0, L[15] = +1.  FP4 (E2M1 / 6, by code): L[0] = +0,
+// L[7] = +1, L[8] = -0, L[15] = -1.
+template <bool FP4, bool F16>
 __device__ __forceinline__ Tab16 make_tab16(const LevelTable& lv, float sc) {
   const uint32_t sb = __builtin_bit_cast(uint32_t, sc);
   const float neg = __builtin_bit_cast(float, sb ^ 0x80000000u);
   const float zero = __builtin_bit_cast(float, sb & 0x80000000u);
+  const float nzero = __builtin_bit_cast(float, (sb ^ 0x80000000u) & 0x80000000u);
   uint32_t pk[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const float a = k == 0 ? neg : lv.level[2 * k] * sc;
-    const float b = k == 3 ? zero : k == 7 ? sc : lv.level[2 * k + 1] * sc;
-    pk[k] = pack_bf16x2(a, b);
+    float a, b;
+    if (FP4) {
+      a = k == 0 ? zero : k == 4 ? nzero : lv.level[2 * k] * sc;
+      b = k == 3 ? sc : k == 7 ? neg : lv.level[2 * k + 1] * sc;
+    } else {
+      a = k == 0 ? neg : lv.level[2 * k] * sc;
+      b = k == 3 ? zero : k == 7 ? sc : lv.level[2 * k + 1] * sc;
+    }
+    pk[k] = pack16x2<F16>(a, b);
   }
   Tab16 t;
 #pragma unroll
@@ -155,7 +164,7 @@ __device__ __forceinline__ void share_tab16(const Tab16& own, Tab16* t) {
   }
 }
 
-template <bool DQ, bool Q4>
+template <bool DQ, bool Q4, bool FP4, bool F16>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ packed,
     const void* __restrict__ absmax, const float* __restrict__ absmax2,
@@ -279,25 +288,24 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 #pragma unroll
   for (int s = 0; s < BK / 16; ++s)
     aoff[s] = (uint32_t)(col * BK + (((4 * half + s) ^ ((col >> 1) & 7)) << 3));
-  bf16x8_t av[2][8], bv[2][2];
+  u32x4_t av[2][8], bv[2][2];
   auto read_ops = [&](const uint16_t* a, int s, int r) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) av[r][i] = *(const bf16x8_t*)(a + aoff[s] + i * 32 * BK);
+    for (int i = 0; i < 8; ++i) av[r][i] = *(const u32x4_t*)(a + aoff[s] + i * 32 * BK);
   };
   auto mfmas = [&](int r) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[r][i], bv[r][j], acc[i][j], 0, 0, 0);
+        acc[i][j] = mfma_32x32x16<F16>(av[r][i], bv[r][j], acc[i][j]);
   };
   auto dequant = [&](const WSet& w, const Tab16* t, int s, int r) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       uint32_t o[4];
       decode8(w.w[j][s], t[j], o);
-      u32x4_t v = {o[0], o[1], o[2], o[3]};
-      bv[r][j] = __builtin_bit_cast(bf16x8_t, v);
+      bv[r][j] = u32x4_t{o[0], o[1], o[2], o[3]};
     }
   };
 
@@ -322,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     load_q(qs1, 1);
     load_q(qs2, 2);
   }
-  share_tab16(make_tab16(lv, scale_of(qs0, 0)), tA);
+  share_tab16(make_tab16<FP4, F16>(lv, scale_of(qs0, 0)), tA);
   Tab16 own;
   __syncthreads();
 
@@ -361,7 +369,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
       if (!first || s > 0) mfmas((s + 1) & 1);    // substep 3 of t-1, then 0..2 of t
       dequant(wc, tc, s, s & 1);
       // Tables of step t+1: the own row's in region 2, shared in region 3.
-      if (s == 2) own = make_tab16(lv, Q4 ? scale_of(qs0, kn) : scale_of(qset(kn), 0));
+      if (s == 2) own = make_tab16<FP4, F16>(lv, Q4 ? scale_of(qs0, kn) : scale_of(qset(kn), 0));
       if (s == 3) share_tab16(own, tn);
       // 16 x {1 MFMA, an operand read (first 8), copies, vector ops}.
 #pragma unroll
@@ -417,7 +425,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = m0 + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-        if (r < M && c < N) y[(int64_t)r * ldy + c] = f32_to_bf16(acc[i][j][v]);
+        if (r < M && c < N) y[(int64_t)r * ldy + c] = f32_to_16<F16>(acc[i][j][v]);
       }
     }
 }
@@ -425,19 +433,29 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 template <bool DQ, bool Q4>
 void launch_one(const uint16_t* x, int64_t ldx, const uint8_t* packed, const void* absmax,
                 const float* absmax2, const float* mean, int M, int N, int K, uint16_t* y,
-                int64_t ldy, hipStream_t stream) {
+                int64_t ldy, int quant_type, bool f16, hipStream_t stream) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
   const int per_xcd = (tm * tn + kXcds - 1) / kXcds;
-  hipLaunchKernelGGL((gemm_kernel<DQ, Q4>), dim3((unsigned)(per_xcd * kXcds)), dim3(kThreads), 0,
-                     stream, x, ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, tm, tn,
-                     level_table());
+  const LevelTable& lv = level_table(quant_type);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(per_xcd * kXcds)), dim3(kThreads), 0, stream, x,
+                       ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, tm, tn, lv);
+  };
+  if (quant_type == kQuantFP4) {
+    if (f16) go(gemm_kernel<DQ, Q4, true, true>);
+    else go(gemm_kernel<DQ, Q4, true, false>);
+  } else {
+    if (f16) go(gemm_kernel<DQ, Q4, false, true>);
+    else go(gemm_kernel<DQ, Q4, false, false>);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const uint16_t* x, int64_t ldx, const uint8_t* packed, const void* absmax,
-                       const float* absmax2, const float* mean, int double_quant, int M, int N,
-                       int K, uint16_t* y, int64_t ldy, hipStream_t stream) {
+                       const float* absmax2, const float* mean, int double_quant, int quant_type,
+                       bool f16, int M, int N, int K, uint16_t* y, int64_t ldy,
+                       hipStream_t stream) {
   // Buffer offsets are 32-bit: the weights and their scales must fit, and M
   // is walked in slabs whose X rows do.
   const int64_t kLimit = (int64_t)1 << 31;
@@ -455,11 +473,14 @@ hipError_t launch_gemm(const uint16_t* x, int64_t ldx, const uint8_t* packed, co
     const uint16_t* xs = x + r0 * ldx;
     uint16_t* ys = y + r0 * ldy;
     if (!double_quant)
-      launch_one<false, false>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys, ldy, stream);
+      launch_one<false, false>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys, ldy,
+                               quant_type, f16, stream);
     else if (q4)
-      launch_one<true, true>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys, ldy, stream);
+      launch_one<true, true>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys, ldy, quant_type,
+                             f16, stream);
     else
-      launch_one<true, false>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys, ldy, stream);
+      launch_one<true, false>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys, ldy,
+                              quant_type, f16, stream);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

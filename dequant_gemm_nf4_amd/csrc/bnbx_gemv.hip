@@ -1,4 +1,5 @@
-// Decode GEMV with NF4 weights for gfx950: Y[M, N] = X[M, K] . W_hat[N, K]^T,
+// Decode GEMV with 4-bit (NF4 or FP4) weights for gfx950:
+// Y[M, N] = X[M, K] . W_hat[N, K]^T,
 // M <= 16 (mlqm.cn bitsandbytes article, sec. 3.4 "4-bit storage, 16-bit
 // compute", and the sec. 7 pitfall that 4-bit only pays off when the layer is
 // bound by weight traffic: so the packed weight is streamed exactly once per
@@ -22,8 +23,9 @@
 // reach the lanes that need them by ds_bpermute, and its (at most two) group
 // scales by scalar loads.  X is staged once per workgroup in LDS.
 //
-// Dequant in registers.  An LDS table maps each packed byte to the bf16 pair
-// (L[high nibble], L[low nibble]); it is replicated in 32 lane columns with a
+// Dequant in registers.  An LDS table maps each packed byte to the level pair
+// (L[high nibble], L[low nibble]) in the compute type (bf16, or FP16 with
+// v_dot2_f32_f16 and the _f16 MFMA); it is replicated in 32 lane columns with a
 // 256-byte stride so that the lanes of each half-wave read distinct banks, and
 // the byte address (byte << 8 | lane << 2) is one v_perm_b32.  The pair feeds
 // v_dot2_f32_bf16 against the matching X pair and the 32-weight partial sum
@@ -99,7 +101,7 @@ enum ScaleMode { kScaleF32 = 0, kScaleDqLane = 1, kScaleDqRow = 2 };
 
 // MM rows of X per launch (rows >= mvalid are zero), NI chunks per lane, RR
 // rows of W per team and pass.  TW = 1 << twl waves per team.
-template <int MM, int NI, int RR, int SM>
+template <int MM, int NI, int RR, int SM, bool F16>
 __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void gemv_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ packed,
     const void* __restrict__ absmax, const float* __restrict__ absmax2,
@@ -242,11 +244,11 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void gemv_kernel(
   // into a full memory pipeline does not hold the barrier for the others.
   issue_part(rb_first + (int64_t)team_l * RR, 0, NI);
 
-  // 3. Byte -> bf16-pair table, then X into LDS.
+  // 3. Byte -> level-pair table (compute type), then X into LDS.
   const int lvl = level_lanes(lv);
   for (int e = t; e < 256 * kCopies / 4; e += kThreads) {
     const uint32_t b = (uint32_t)e / (kCopies / 4);
-    const uint32_t v = pack_bf16x2(level_lookup(lvl, b >> 4), level_lookup(lvl, b & 15u));
+    const uint32_t v = pack16x2<F16>(level_lookup(lvl, b >> 4), level_lookup(lvl, b & 15u));
     *(uint4*)(tab + b * 256u + ((uint32_t)e % (kCopies / 4)) * 16u) = make_uint4(v, v, v, v);
   }
   if (xlds) {
@@ -325,7 +327,7 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void gemv_kernel(
             const uint32_t addr = perm(d[q], lanebyte, 0x0c0c0000u | ((4u + b) << 8));
             const uint32_t pair = *(const uint32_t*)(tab + addr);
 #pragma unroll
-            for (int m = 0; m < MM; ++m) part[m] = dot2_bf16(pair, xr[m][i][4 * q + b], part[m]);
+            for (int m = 0; m < MM; ++m) part[m] = dot2_16<F16>(pair, xr[m][i][4 * q + b], part[m]);
           }
         }
 #pragma unroll
@@ -344,7 +346,7 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void gemv_kernel(
         for (int j = 0; j < RR; ++j)
 #pragma unroll
           for (int m = 0; m < MM; ++m)
-            if (rb + j < N && m < mvalid) y[(int64_t)m * ldy + rb + j] = f32_to_bf16(acc[m][j]);
+            if (rb + j < N && m < mvalid) y[(int64_t)m * ldy + rb + j] = f32_to_16<F16>(acc[m][j]);
       }
     } else {
       if (lane == 63) {
@@ -358,7 +360,7 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void gemv_kernel(
         const int m = lane / RR, j = lane - (lane / RR) * RR;
         float v = 0.0f;
         for (int u = 0; u < TW; ++u) v += red[((team_l * TW + u) * MM + m) * RR + j];
-        if (rb + j < N && m < mvalid) y[(int64_t)m * ldy + rb + j] = f32_to_bf16(v);
+        if (rb + j < N && m < mvalid) y[(int64_t)m * ldy + rb + j] = f32_to_16<F16>(v);
       }
       __syncthreads();
     }
@@ -374,7 +376,8 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void gemv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// 4 < M <= 16: the weights streamed once into v_mfma_f32_16x16x32_bf16.
+// 4 < M <= 16: the weights streamed once into v_mfma_f32_16x16x32_bf16 (or
+// _f16 with the FP16 compute dtype).
 //
 // A workgroup of 16 waves takes groups of 16 weight rows (16 columns of Y)
 // in turn; wave w owns the K slice of blocks [w nkb / 16, (w+1) nkb / 16)
@@ -397,7 +400,7 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void gemv_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kMfWaves = 16;
 
-template <int BPW, int GD, int SM>
+template <int BPW, int GD, int SM, bool F16>
 __global__ __launch_bounds__(kMfWaves * 64, 1) void gemv_mfma_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ packed,
     const void* __restrict__ absmax, const float* __restrict__ absmax2,
@@ -443,7 +446,7 @@ __global__ __launch_bounds__(kMfWaves * 64, 1) void gemv_mfma_kernel(
   // X[row][64 (b0 + i) + 16 q + 8 h ..+8] = piece 8 i + 2 q + h of the
   // row's slice; rows >= M read as zero.
   const rsrc_t rx = make_rsrc(x, (uint32_t)((int64_t)(M - 1) * ldx * 2 + (int64_t)K * 2));
-  bf16x8_t xa[BPW][2];
+  u32x4_t xa[BPW][2];
   {
     // The slice is 16 rows x 8 BPW pieces; it passes through the region in
     // four rounds of kPieces pieces per row (BPW / 4 blocks), whose loads all
@@ -469,7 +472,7 @@ __global__ __launch_bounds__(kMfWaves * 64, 1) void gemv_mfma_kernel(
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int pc = 8 * ib + 2 * q + h;     // piece within this round
-          xa[R * kBr + ib][h] = *(const bf16x8_t*)(reg + c * kRow + 16 * (pc ^ swz(c)));
+          xa[R * kBr + ib][h] = *(const u32x4_t*)(reg + c * kRow + 16 * (pc ^ swz(c)));
         }
     }
   }
@@ -533,7 +536,7 @@ __global__ __launch_bounds__(kMfWaves * 64, 1) void gemv_mfma_kernel(
   const int lvl = level_lanes(lv);
   for (int e = t; e < 256 * kCopies / 4; e += kMfWaves * 64) {
     const uint32_t b = (uint32_t)e / (kCopies / 4);
-    const uint32_t v = pack_bf16x2(level_lookup(lvl, b >> 4), level_lookup(lvl, b & 15u));
+    const uint32_t v = pack16x2<F16>(level_lookup(lvl, b >> 4), level_lookup(lvl, b & 15u));
     *(uint4*)(tab + b * 256u + ((uint32_t)e % (kCopies / 4)) * 16u) = make_uint4(v, v, v, v);
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -561,8 +564,7 @@ __global__ __launch_bounds__(kMfWaves * 64, 1) void gemv_mfma_kernel(
           const uint32_t addr = perm(d, lanebyte, 0x0c0c0000u | ((4u + j) << 8));
           bw[j] = *(const uint32_t*)(tab + addr);
         }
-        blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i][h], __builtin_bit_cast(bf16x8_t, bw),
-                                                      blk, 0, 0, 0);
+        blk = mfma_16x16x32<F16>(xa[i][h], bw, blk);
       }
       const float sc = scale(st, i);
 #pragma unroll
@@ -595,7 +597,7 @@ __global__ __launch_bounds__(kMfWaves * 64, 1) void gemv_mfma_kernel(
         float sum = 0.0f;
 #pragma unroll
         for (int w = 0; w < kMfWaves; ++w) sum += red[(j * kMfWaves + w) * 256 + src];
-        y[(int64_t)m * ldy + n] = f32_to_bf16(sum);
+        y[(int64_t)m * ldy + n] = f32_to_16<F16>(sum);
       }
     }
     __syncthreads();
@@ -604,19 +606,22 @@ __global__ __launch_bounds__(kMfWaves * 64, 1) void gemv_mfma_kernel(
 
 // Row-wise scales in the MFMA path: every wave's four blocks are one dword of
 // codes inside one group; needs 4-byte aligned codes.
+template <bool F16>
 hipError_t launch_mfma(int grid, const uint16_t* x, int64_t ldx, const uint8_t* packed,
                        const void* absmax, const float* absmax2, const float* mean, int dq,
-                       int M, int N, int K, uint16_t* y, int64_t ldy, hipStream_t stream) {
-  const LevelTable& lv = level_table();
+                       int M, int N, int K, uint16_t* y, int64_t ldy, const LevelTable& lv,
+                       hipStream_t stream) {
   if (dq && ((uintptr_t)absmax & 3u) == 0)
-    hipLaunchKernelGGL((gemv_mfma_kernel<4, 4, kScaleDqRow>), dim3(grid), dim3(kMfWaves * 64), 0,
-                       stream, x, ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, lv);
+    hipLaunchKernelGGL((gemv_mfma_kernel<4, 4, kScaleDqRow, F16>), dim3(grid),
+                       dim3(kMfWaves * 64), 0, stream, x, ldx, packed, absmax, absmax2, mean, M, N,
+                       K, y, ldy, lv);
   else if (dq)
-    hipLaunchKernelGGL((gemv_mfma_kernel<4, 2, kScaleDqLane>), dim3(grid), dim3(kMfWaves * 64), 0,
-                       stream, x, ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, lv);
+    hipLaunchKernelGGL((gemv_mfma_kernel<4, 2, kScaleDqLane, F16>), dim3(grid),
+                       dim3(kMfWaves * 64), 0, stream, x, ldx, packed, absmax, absmax2, mean, M, N,
+                       K, y, ldy, lv);
   else
-    hipLaunchKernelGGL((gemv_mfma_kernel<4, 2, kScaleF32>), dim3(grid), dim3(kMfWaves * 64), 0,
-                       stream, x, ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, lv);
+    hipLaunchKernelGGL((gemv_mfma_kernel<4, 2, kScaleF32, F16>), dim3(grid), dim3(kMfWaves * 64),
+                       0, stream, x, ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, lv);
   return hipGetLastError();
 }
 
@@ -689,33 +694,36 @@ bool make_plan(int mm, int N, int K, Plan& p) {
   return true;
 }
 
-template <int MM, int NI, int RR>
+template <int MM, int NI, int RR, bool F16>
 hipError_t launch_k(const Plan& p, const uint16_t* x, int64_t ldx, const uint8_t* packed,
                     const void* absmax, const float* absmax2, const float* mean, int dq,
-                    int mvalid, int N, int K, uint16_t* y, int64_t ldy, hipStream_t stream) {
-  const LevelTable& lv = level_table();
+                    int mvalid, int N, int K, uint16_t* y, int64_t ldy, const LevelTable& lv,
+                    hipStream_t stream) {
   if (!dq)
-    hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, kScaleF32>), dim3(p.grid), dim3(kThreads), 0,
+    hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, kScaleF32, F16>), dim3(p.grid), dim3(kThreads), 0,
                        stream, x, ldx, packed, absmax, absmax2, mean, mvalid, N, K, y, ldy, p.twl,
                        p.xlds, lv);
   else if ((K >> 6) <= 256 && (K >> 6) % 4 == 0 && ((uintptr_t)absmax & 3u) == 0)
-    hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, kScaleDqRow>), dim3(p.grid), dim3(kThreads), 0,
-                       stream, x, ldx, packed, absmax, absmax2, mean, mvalid, N, K, y, ldy, p.twl,
-                       p.xlds, lv);
+    hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, kScaleDqRow, F16>), dim3(p.grid), dim3(kThreads),
+                       0, stream, x, ldx, packed, absmax, absmax2, mean, mvalid, N, K, y, ldy,
+                       p.twl, p.xlds, lv);
   else
-    hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, kScaleDqLane>), dim3(p.grid), dim3(kThreads), 0,
-                       stream, x, ldx, packed, absmax, absmax2, mean, mvalid, N, K, y, ldy, p.twl,
-                       p.xlds, lv);
+    hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, kScaleDqLane, F16>), dim3(p.grid), dim3(kThreads),
+                       0, stream, x, ldx, packed, absmax, absmax2, mean, mvalid, N, K, y, ldy,
+                       p.twl, p.xlds, lv);
   return hipGetLastError();
 }
 
 hipError_t dispatch(const Plan& p, const uint16_t* x, int64_t ldx, const uint8_t* packed,
                     const void* absmax, const float* absmax2, const float* mean, int dq,
-                    int mvalid, int N, int K, uint16_t* y, int64_t ldy, hipStream_t stream) {
-#define BNBX_GEMV_CASE(MM, NI, RR)                                                            \
-  if (p.mm == MM && p.ni == NI && p.rr == RR)                                                 \
-    return launch_k<MM, NI, RR>(p, x, ldx, packed, absmax, absmax2, mean, dq, mvalid, N, K, y, \
-                                ldy, stream);
+                    int mvalid, int N, int K, uint16_t* y, int64_t ldy, const LevelTable& lv,
+                    bool f16, hipStream_t stream) {
+#define BNBX_GEMV_CASE(MM, NI, RR)                                                              \
+  if (p.mm == MM && p.ni == NI && p.rr == RR)                                                   \
+    return f16 ? launch_k<MM, NI, RR, true>(p, x, ldx, packed, absmax, absmax2, mean, dq, mvalid, \
+                                            N, K, y, ldy, lv, stream)                           \
+               : launch_k<MM, NI, RR, false>(p, x, ldx, packed, absmax, absmax2, mean, dq,      \
+                                             mvalid, N, K, y, ldy, lv, stream);
   BNBX_GEMV_CASE(1, 1, 1) BNBX_GEMV_CASE(1, 1, 2) BNBX_GEMV_CASE(1, 1, 3) BNBX_GEMV_CASE(1, 1, 4)
   BNBX_GEMV_CASE(1, 2, 1) BNBX_GEMV_CASE(1, 2, 2) BNBX_GEMV_CASE(1, 2, 3) BNBX_GEMV_CASE(1, 2, 4)
   BNBX_GEMV_CASE(1, 3, 1) BNBX_GEMV_CASE(1, 3, 2)
@@ -730,9 +738,11 @@ hipError_t dispatch(const Plan& p, const uint16_t* x, int64_t ldx, const uint8_t
 }  // namespace
 
 hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* packed, const void* absmax,
-                       const float* absmax2, const float* mean, int double_quant, int M, int N,
-                       int K, uint16_t* y, int64_t ldy, hipStream_t stream) {
+                       const float* absmax2, const float* mean, int double_quant, int quant_type,
+                       bool f16, int M, int N, int K, uint16_t* y, int64_t ldy,
+                       hipStream_t stream) {
   const int64_t rowK2 = K >> 1, nkb = K >> 6;
+  const LevelTable& lv = level_table(quant_type);
   // 4 < M <= 16 at K = 4096 (each wave's K slice in its registers): one
   // MFMA launch streams the weights once, when the offsets fit 32 bits.
   if (M > 4) {
@@ -742,8 +752,10 @@ hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* packed, co
     if (fits) {
       const int ngroups = (N + 15) / 16;
       const int grid = ngroups < cu_count() ? ngroups : cu_count();
-      return launch_mfma(grid, x, ldx, packed, absmax, absmax2, mean, double_quant, M, N, K, y, ldy,
-                         stream);
+      return f16 ? launch_mfma<true>(grid, x, ldx, packed, absmax, absmax2, mean, double_quant, M,
+                                     N, K, y, ldy, lv, stream)
+                 : launch_mfma<false>(grid, x, ldx, packed, absmax, absmax2, mean, double_quant, M,
+                                      N, K, y, ldy, lv, stream);
     }
   }
   // Slabs of rows keep every byte offset of a launch below 2^31.
@@ -772,7 +784,7 @@ hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* packed, co
       const float* am2 = double_quant ? absmax2 + (r0 * nkb) / 256 : absmax2;
       const hipError_t e =
           dispatch(p, x + (int64_t)m0 * ldx, ldx, packed + r0 * rowK2, am, am2, mean,
-                   double_quant, mv, n, K, y + (int64_t)m0 * ldy + r0, ldy, stream);
+                   double_quant, mv, n, K, y + (int64_t)m0 * ldy + r0, ldy, lv, f16, stream);
       if (e != hipSuccess) return e;
     }
     m0 += mv;

@@ -12,26 +12,33 @@ constexpr int kBlock = 64;    // weights per first-level block
 constexpr int kGroup = 256;   // first-level scales per second-level group
 constexpr int kBuckets = 33;  // encode buckets: round(16 x + 16), x in [-1, 1]
 
-// Host-computed tables derived from the 16 NF4 levels (mlqm.cn bitsandbytes
-// article, sec. 3.2).  Passed to kernels by value.
+// The two 4-bit quant types (mlqm.cn bitsandbytes article, sec. 4: nf4 or
+// fp4); values of bnbx_nf4_state.quant_type.
+constexpr int kQuantNF4 = 0;
+constexpr int kQuantFP4 = 1;
+
+// Host-computed tables derived from a quant type's 16 levels (mlqm.cn
+// bitsandbytes article, sec. 3.2).  Passed to kernels by value.
 struct EncodeTable {
   // Bucket b holds the values x with round-half-even(16 x + 16) == b.  At most
   // one decision threshold falls in a bucket (the thresholds are more than
-  // 1/16 apart), so code(x) = base[b] + (x >= thr[b]); thr is +inf when the
-  // bucket holds none.
+  // 1/16 apart).  NF4 (codes in level order): code(x) = base[b] + (x >=
+  // thr[b]).  FP4: base[b] holds the codes below and above the bucket's
+  // threshold in bits 0-3 and 4-7, and code(x) is the field (x >= thr[b])
+  // selects.  thr is +inf when the bucket holds no threshold.
   float thr[kBuckets];
   uint32_t base[kBuckets];
+  uint32_t code_min, code_max;   // codes of the lowest and highest level
 };
 
 struct LevelTable {
-  float level[16];       // L[0..15], ascending, binary32
+  float level[16];       // level of each code, binary32 (NF4: ascending)
 };
 
 // The one-time host tables (built on first use, immutable afterwards).
-const float* levels_f32();          // float[16]
-const float* thresholds_f32();      // float[15]
-const EncodeTable& encode_table();
-const LevelTable& level_table();
+const float* levels_f32(int quant_type);   // float[16], by code
+const EncodeTable& encode_table(int quant_type);
+const LevelTable& level_table(int quant_type);
 
 // Workspace layout of the double-quant quantize: one slot per quantize
 // workgroup (at most kMaxQGrid) holding that workgroup's exact partial sum of
@@ -52,19 +59,22 @@ inline size_t dq_workspace_bytes(int64_t nb) {
 // `slots` is given (double quant); double_quant reads as many.
 int quantize_grid(int64_t n);
 hipError_t launch_quantize(const uint16_t* w, uint8_t* packed, int64_t n, float* absmax_f32,
-                           unsigned long long* slots, hipStream_t stream);
+                           unsigned long long* slots, int quant_type, hipStream_t stream);
 hipError_t launch_double_quant(const float* absmax_f32, const unsigned long long* slots,
                                int nslots, int64_t nb, int8_t* q, float* absmax2, float* mean,
                                hipStream_t stream);
+// `f16`: the 16-bit compute type is IEEE binary16 instead of bfloat16.
 hipError_t launch_dequantize(const uint8_t* packed, int64_t n, const void* absmax,
                              const float* absmax2, const float* mean, int double_quant,
-                             uint16_t* out, hipStream_t stream);
+                             int quant_type, bool f16, uint16_t* out, hipStream_t stream);
 // Returns hipErrorNotSupported if no GEMV variant covers (M, K).
 hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* packed, const void* absmax,
-                       const float* absmax2, const float* mean, int double_quant, int M, int N,
-                       int K, uint16_t* y, int64_t ldy, hipStream_t stream);
+                       const float* absmax2, const float* mean, int double_quant, int quant_type,
+                       bool f16, int M, int N, int K, uint16_t* y, int64_t ldy,
+                       hipStream_t stream);
 hipError_t launch_gemm(const uint16_t* x, int64_t ldx, const uint8_t* packed, const void* absmax,
-                       const float* absmax2, const float* mean, int double_quant, int M, int N,
-                       int K, uint16_t* y, int64_t ldy, hipStream_t stream);
+                       const float* absmax2, const float* mean, int double_quant, int quant_type,
+                       bool f16, int M, int N, int K, uint16_t* y, int64_t ldy,
+                       hipStream_t stream);
 
 }  // namespace bnbx

@@ -1,10 +1,11 @@
-// Blockwise NF4 quantize-on-load and double quantization of the block scales
-// for gfx950.
+// Blockwise 4-bit (NF4 or FP4) quantize-on-load and double quantization of
+// the block scales for gfx950.
 //
 // mlqm.cn bitsandbytes article (news/394670): sec. 2.2 (weights are quantized
 // while they are loaded, with no calibration data), sec. 3.2 (nearest of 16
 // NormalFloat levels), sec. 3.3 (one FP32 absmax scale per block; double
-// quantization compresses those scales a second time).
+// quantization compresses those scales a second time), sec. 4 (fp4, the
+// other 4-bit quant type: the same kernel with the FP4 encode tables).
 //
 // quantize_kernel streams the bf16 weight once (16-byte loads, 8 weights per
 // lane, 8 lanes per 64-weight block), reduces the block absmax with DPP,
@@ -41,20 +42,26 @@ __device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v, int ctrl_id) {
 }
 
 // Code of one normalised value x in [-1, 1] (or +-inf / NaN when the block
-// reciprocal overflowed, handled by the caller).
+// reciprocal overflowed, handled by the caller).  NF4 codes are level
+// indices (bucket base + 1 past the threshold); FP4 picks one of the two
+// codes the bucket entry holds.
+template <bool FP4>
 __device__ __forceinline__ uint32_t encode_one(float x, const unsigned char* tab, uint32_t lanebase) {
   // 2^23 + 16 + 16 x rounded once to an integer: the low byte is the bucket.
   const float f = __builtin_fmaf(x, 16.0f, 8388624.0f);
   const uint32_t addr = perm(__float_as_uint(f), lanebase, 0x0c0c0400u);
   const uint2 e = *(const uint2*)(tab + addr);
+  if (FP4) return __builtin_amdgcn_ubfe(e.y, x >= __uint_as_float(e.x) ? 4u : 0u, 4u);
   return e.y + (x >= __uint_as_float(e.x) ? 1u : 0u);
 }
 
 // One lane's 8 consecutive weights (4 bf16 pairs) -> one packed word; also
 // returns the block absmax (bf16 bits in m, value in amax).  All 64 lanes of
 // the wave must execute this together (DPP reduction over 8-lane groups).
+template <bool FP4>
 __device__ __forceinline__ uint32_t encode8(const uint32_t d[4], const unsigned char* tab,
-                                            uint32_t lanebase, uint32_t& m_out, float& amax_out) {
+                                            uint32_t lanebase, uint32_t cmin, uint32_t cmax,
+                                            uint32_t& m_out, float& amax_out) {
   // |w| as bf16 bits: for non-negative floats integer order is value order.
   uint32_t m = 0;
 #pragma unroll
@@ -73,18 +80,19 @@ __device__ __forceinline__ uint32_t encode8(const uint32_t d[4], const unsigned 
     for (int k = 0; k < 4; ++k) {
       const float x0 = bf16lo_to_f32(d[k]) * r;   // even element -> high nibble
       const float x1 = bf16hi_to_f32(d[k]) * r;
-      const uint32_t c0 = encode_one(x0, tab, lanebase);
-      const uint32_t c1 = encode_one(x1, tab, lanebase);
+      const uint32_t c0 = encode_one<FP4>(x0, tab, lanebase);
+      const uint32_t c1 = encode_one<FP4>(x1, tab, lanebase);
       word |= ((c0 << 4) | c1) << (8 * k);
     }
   } else {
     // Reciprocal overflowed (absmax below 2^-128): x is +inf, -inf or NaN,
-    // whose codes are 15, 0 and 0 (count of thresholds <= x).
+    // which are at or above every threshold (+inf: the highest level) or
+    // none (the lowest level).
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float x0 = bf16lo_to_f32(d[k]) * r;
       const float x1 = bf16hi_to_f32(d[k]) * r;
-      const uint32_t c0 = x0 > 1.0f ? 15u : 0u, c1 = x1 > 1.0f ? 15u : 0u;
+      const uint32_t c0 = x0 > 1.0f ? cmax : cmin, c1 = x1 > 1.0f ? cmax : cmin;
       word |= ((c0 << 4) | c1) << (8 * k);
     }
   }
@@ -104,7 +112,7 @@ __device__ __forceinline__ void record_block(int lane, int64_t e, uint32_t m, fl
   }
 }
 
-template <bool DQ>
+template <bool DQ, bool FP4>
 __global__ __launch_bounds__(kQThreads, 2) void quantize_kernel(
     const uint16_t* __restrict__ w, uint8_t* __restrict__ packed, float* __restrict__ absmax,
     unsigned long long* __restrict__ slots, int64_t n, EncodeTable et) {
@@ -147,7 +155,7 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_kernel(
       const uint32_t d[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
       uint32_t m;
       float amax;
-      const uint32_t word = encode8(d, tab, lanebase, m, amax);
+      const uint32_t word = encode8<FP4>(d, tab, lanebase, et.code_min, et.code_max, m, amax);
       if (t0 + u < full) {   // wave-uniform
         const int64_t e = (t0 + u) * kTile + lane * 8;
         *(uint32_t*)(packed + (e >> 1)) = word;
@@ -166,7 +174,7 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_kernel(
                            h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16)};
     uint32_t m;
     float amax;
-    const uint32_t word = encode8(d, tab, lanebase, m, amax);
+    const uint32_t word = encode8<FP4>(d, tab, lanebase, et.code_min, et.code_max, m, amax);
     if (e < n) {
       const int nbytes = (int)((n - e) < 8 ? (n - e) >> 1 : 4);
       for (int k = 0; k < nbytes; ++k) packed[(e >> 1) + k] = (uint8_t)(word >> (8 * k));
@@ -321,14 +329,25 @@ int quantize_grid(int64_t n) {
 }
 
 hipError_t launch_quantize(const uint16_t* w, uint8_t* packed, int64_t n, float* absmax_f32,
-                           unsigned long long* slots, hipStream_t stream) {
+                           unsigned long long* slots, int quant_type, hipStream_t stream) {
   const int grid = quantize_grid(n);
-  if (slots != nullptr)
-    hipLaunchKernelGGL(quantize_kernel<true>, dim3(grid), dim3(kQThreads), 0, stream, w, packed,
-                       absmax_f32, slots, n, encode_table());
-  else
-    hipLaunchKernelGGL(quantize_kernel<false>, dim3(grid), dim3(kQThreads), 0, stream, w, packed,
-                       absmax_f32, slots, n, encode_table());
+  const EncodeTable& et = encode_table(quant_type);
+  const bool dq = slots != nullptr;
+  if (quant_type == kQuantFP4) {
+    if (dq)
+      hipLaunchKernelGGL((quantize_kernel<true, true>), dim3(grid), dim3(kQThreads), 0, stream, w,
+                         packed, absmax_f32, slots, n, et);
+    else
+      hipLaunchKernelGGL((quantize_kernel<false, true>), dim3(grid), dim3(kQThreads), 0, stream, w,
+                         packed, absmax_f32, slots, n, et);
+  } else {
+    if (dq)
+      hipLaunchKernelGGL((quantize_kernel<true, false>), dim3(grid), dim3(kQThreads), 0, stream, w,
+                         packed, absmax_f32, slots, n, et);
+    else
+      hipLaunchKernelGGL((quantize_kernel<false, false>), dim3(grid), dim3(kQThreads), 0, stream,
+                         w, packed, absmax_f32, slots, n, et);
+  }
   return hipGetLastError();
 }
 

@@ -13,11 +13,15 @@ from . import (Nf4State, bnbx_dequantize_nf4, bnbx_gemm_nf4, bnbx_gemm_nf4_works
 
 BLOCKSIZE = 64
 GROUP = 256
+QUANT_TYPES = {"nf4": 0, "fp4": 1}
+DTYPES = {torch.bfloat16: 0, torch.float16: 1}
 
 
 @dataclasses.dataclass
 class QuantizedWeight:
-    """Device buffers of one NF4 tensor plus its C descriptor."""
+    """Device buffers of one 4-bit tensor plus its C descriptor.  ``dtype``
+    is the compute dtype (bf16 or fp16) of its dequantized values and of the
+    activations it multiplies."""
 
     n: int
     shape: tuple
@@ -26,17 +30,21 @@ class QuantizedWeight:
     absmax: torch.Tensor          # float32 [nb] or int8 [nb]
     absmax2: torch.Tensor | None  # float32 [ng]
     absmax_mean: torch.Tensor | None  # float32 [1]
+    quant_type: str = "nf4"
+    dtype: torch.dtype = torch.bfloat16
 
     @property
     def state(self) -> Nf4State:
         return Nf4State(
             n=self.n, blocksize=BLOCKSIZE, double_quant=int(self.double_quant),
+            quant_type=QUANT_TYPES[self.quant_type], compute_dtype=DTYPES[self.dtype],
             absmax=self.absmax.data_ptr(),
             absmax2=self.absmax2.data_ptr() if self.absmax2 is not None else None,
             absmax_mean=self.absmax_mean.data_ptr() if self.absmax_mean is not None else None)
 
 
-def empty_quantized(shape, double_quant: bool, device="cuda") -> QuantizedWeight:
+def empty_quantized(shape, double_quant: bool, device="cuda", quant_type: str = "nf4",
+                    dtype: torch.dtype = torch.bfloat16) -> QuantizedWeight:
     n = 1
     for s in shape:
         n *= int(s)
@@ -50,7 +58,8 @@ def empty_quantized(shape, double_quant: bool, device="cuda") -> QuantizedWeight
     else:
         absmax = torch.empty(nb, dtype=torch.float32, device=device)
         absmax2 = mean = None
-    return QuantizedWeight(n, tuple(shape), double_quant, packed, absmax, absmax2, mean)
+    return QuantizedWeight(n, tuple(shape), double_quant, packed, absmax, absmax2, mean,
+                           quant_type, dtype)
 
 
 def workspace_for(n: int, double_quant: bool, device="cuda") -> torch.Tensor | None:
@@ -61,18 +70,21 @@ def workspace_for(n: int, double_quant: bool, device="cuda") -> torch.Tensor | N
 
 
 def quantize(w: torch.Tensor, double_quant: bool, out: QuantizedWeight | None = None,
-             workspace: torch.Tensor | None = None, stream=None) -> QuantizedWeight:
-    """bnbx_quantize_nf4 on a bf16 tensor (any shape, contiguous)."""
+             workspace: torch.Tensor | None = None, stream=None, quant_type: str = "nf4",
+             dtype: torch.dtype = torch.bfloat16) -> QuantizedWeight:
+    """bnbx_quantize_nf4 on a bf16 tensor (any shape, contiguous); ``dtype``
+    is the compute dtype recorded for later dequantize / matmul calls."""
     assert w.dtype == torch.bfloat16 and w.is_contiguous()
-    q = out if out is not None else empty_quantized(w.shape, double_quant, w.device)
+    q = out if out is not None else empty_quantized(w.shape, double_quant, w.device, quant_type,
+                                                    dtype)
     ws = workspace if workspace is not None else workspace_for(q.n, double_quant, w.device)
     bnbx_quantize_nf4(w, q.packed, q.state, ws, 0 if ws is None else ws.numel(), stream)
     return q
 
 
 def dequantize(q: QuantizedWeight, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    o = out if out is not None else torch.empty(q.shape, dtype=torch.bfloat16,
-                                                device=q.packed.device)
+    o = out if out is not None else torch.empty(q.shape, dtype=q.dtype, device=q.packed.device)
+    assert o.dtype == q.dtype
     bnbx_dequantize_nf4(q.packed, q.state, o, stream)
     return o
 
@@ -82,7 +94,8 @@ def gemv(x: torch.Tensor, q: QuantizedWeight, out: torch.Tensor | None = None,
     """Y = X . W_hat^T for X [M, K] (M <= 16), W [N, K]."""
     M, K = x.shape
     N = q.shape[0]
-    y = out if out is not None else torch.empty(M, N, dtype=torch.bfloat16, device=x.device)
+    assert x.dtype == q.dtype
+    y = out if out is not None else torch.empty(M, N, dtype=q.dtype, device=x.device)
     bnbx_gemv_nf4(x, x.stride(0), q.packed, q.state, M, N, K, y, y.stride(0), stream)
     return y
 
@@ -92,7 +105,8 @@ def gemm(x: torch.Tensor, q: QuantizedWeight, out: torch.Tensor | None = None,
     """Y = X . W_hat^T for X [M, K], W [N, K], any M."""
     M, K = x.shape
     N = q.shape[0]
-    y = out if out is not None else torch.empty(M, N, dtype=torch.bfloat16, device=x.device)
+    assert x.dtype == q.dtype
+    y = out if out is not None else torch.empty(M, N, dtype=q.dtype, device=x.device)
     nbytes = bnbx_gemm_nf4_workspace_bytes(M, N, K)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device) if nbytes else None
     bnbx_gemm_nf4(x, x.stride(0), q.packed, q.state, M, N, K, y, y.stride(0), ws, nbytes, stream)

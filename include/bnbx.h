@@ -1,22 +1,26 @@
 /*
  * bnbx.h -- C ABI of the MI355X (gfx950) NF4 4-bit weight library.
  *
- * Blockwise NF4 quantize-on-load with double quantization of the block scales,
- * dequantize to bfloat16, and the "4-bit storage, 16-bit compute" linear layer
- * Y = X . W_hat^T as a decode GEMV (M <= 16) and a prefill GEMM (any M).
+ * Blockwise NF4 (or FP4) quantize-on-load with double quantization of the
+ * block scales, dequantize to bfloat16 (or FP16), and the "4-bit storage,
+ * 16-bit compute" linear layer Y = X . W_hat^T as a decode GEMV (M <= 16) and
+ * a prefill GEMM (any M).
  *
  * Sources (five web pages about bitsandbytes, cited by page and section):
  *   mlqm.cn bitsandbytes article (news/394670), sec. 2.2 (quantize while
  *     loading, no calibration data), 3.2 (NF4: 16 levels placed by the normal
  *     density), 3.3 (one FP32 scale per block; double quantization quantizes
- *     the scales again), 3.4 (store 4-bit, dequantize to FP16/BF16, multiply);
+ *     the scales again), 3.4 (store 4-bit, dequantize to FP16/BF16, multiply),
+ *     4 (loading options: 4-bit quant type nf4 or fp4, compute dtype BF16 or
+ *     FP16);
  *   pomoai.com bitsandbytes overview, module list (Linear4bit replaces
  *     torch.nn.Linear: weight [out_features, in_features]; the functional
  *     module holds blockwise quantization and the NF4 format).
  *
  * Conventions shared by every call
  * --------------------------------
- * - bf16 values are passed as uint16_t bit patterns.
+ * - 16-bit values (bf16, or IEEE binary16 where the state's compute_dtype
+ *   says so) are passed as uint16_t bit patterns.
  * - Pointers named "device" are device (HBM) addresses; the caller allocates
  *   and frees every buffer.  The library never allocates device memory, never
  *   frees, and never synchronises: work is enqueued on `stream` (a
@@ -48,12 +52,22 @@
  *     absmax_mean float[1]    mean = fl32(fl64(sum_b a_b) / nb), the sum exact
  *   Dequantized scale: without DQ a_b; with DQ
  *     fl32(fl32(q_b * fl32(s_g / 127)) + mean).
- *   Code of element j: x = fl32(w_j * fl32(1 / a_b)); c = #{i : x >= T_i}
- *   where T_i is the smallest float above the midpoint of levels i and i+1
- *   (nearest level, exact ties to the lower index); an all-zero block takes
- *   code 7 (the 0.0 level).
- *   Dequantized weight: W_hat_j = bf16(fl32(L[c_j] * scale_b)), round to
- *   nearest even.
+ *   Code of element j: x = fl32(w_j * fl32(1 / a_b)); s = #{i : x >= T_i}
+ *   where T_i is the smallest float above the midpoint of the i-th and
+ *   (i+1)-th smallest distinct levels (nearest level, exact ties to the lower
+ *   level); c is the code of the s-th smallest level.  An all-zero block
+ *   takes the code of the 0.0 level.
+ *   NF4 (quant_type 0): codes are the levels in ascending order, L[0] = -1,
+ *   L[7] = 0, L[15] = +1 (bnbx_nf4_codebook).
+ *   FP4 (quant_type 1; the pages give no layout, E2M1 is taken): bit 3 the
+ *   sign, bits 2-1 the exponent e, bit 0 the mantissa m; L[c] =
+ *   fl32(+-mag / 6) with mag = m/2 for e = 0, else 2^(e-1) (1 + m/2), i.e.
+ *   0, 1/12, 1/6, 1/4, 1/3, 1/2, 2/3, 1 for codes 0-7 and their negatives for
+ *   8-15 (bnbx_fp4_codebook).  The encoder never emits code 8 (-0); zero
+ *   blocks take code 0.
+ *   Dequantized weight: W_hat_j = rnd(fl32(L[c_j] * scale_b)), rnd = round
+ *   to nearest even into the compute dtype (bf16 or binary16; binary16
+ *   keeps subnormals and overflows to infinity).
  */
 #ifndef BNBX_H
 #define BNBX_H
@@ -77,12 +91,21 @@ typedef enum {
   BNBX_E_HIP = -5           /* the HIP runtime reported an error at launch     */
 } bnbx_status;
 
+/* 4-bit quant types (bnbx_nf4_state.quant_type). */
+enum { BNBX_QUANT_NF4 = 0, BNBX_QUANT_FP4 = 1 };
+/* 16-bit compute types (bnbx_nf4_state.compute_dtype). */
+enum { BNBX_DTYPE_BF16 = 0, BNBX_DTYPE_F16 = 1 };
+
 /* Caller-owned descriptor of one quantized tensor (host memory; the pointers
  * inside are device addresses).  The library reads it during the call only. */
 typedef struct {
   int64_t n;             /* number of weights, even, >= 2                      */
   int32_t blocksize;     /* weights per block; only 64 is supported            */
   int32_t double_quant;  /* 0: absmax is float[nb]; 1: int8 + absmax2 + mean  */
+  int32_t quant_type;    /* BNBX_QUANT_NF4 (0) or BNBX_QUANT_FP4 (1)            */
+  int32_t compute_dtype; /* BNBX_DTYPE_BF16 (0) or BNBX_DTYPE_F16 (1): the type
+                            of dequantized weights and of X and Y; the quantize
+                            input is always bf16 and ignores it               */
   void*   absmax;        /* device: float[nb] (dq=0) or int8_t[nb] (dq=1)      */
   float*  absmax2;       /* device: float[ng] (dq=1), else NULL                */
   float*  absmax_mean;   /* device: float[1]  (dq=1), else NULL                */
@@ -100,11 +123,18 @@ BNBX_API const char* bnbx_status_str(int status);
  * Returns BNBX_E_INVAL if levels_host is NULL. */
 BNBX_API int bnbx_nf4_codebook(float levels_host[16]);
 
+/* The 16 FP4 levels by code (E2M1 divided by 6, see the format notes above)
+ * into host memory.  mlqm.cn article sec. 4: fp4, the plain 4-bit float
+ * quant type offered beside nf4.  Host-only, synchronous.
+ * Returns BNBX_E_INVAL if levels_host is NULL. */
+BNBX_API int bnbx_fp4_codebook(float levels_host[16]);
+
 /* Bytes of device workspace bnbx_quantize_nf4 needs for (n, blocksize,
  * double_quant); 0 without double quant.  Returns 0 for invalid arguments. */
 BNBX_API size_t bnbx_quantize_nf4_workspace_bytes(int64_t n, int blocksize, int double_quant);
 
-/* Blockwise NF4 quantize-on-load (mlqm.cn article sec. 2.2, 3.2, 3.3).
+/* Blockwise 4-bit quantize-on-load, NF4 or FP4 by st->quant_type (mlqm.cn
+ * article sec. 2.2, 3.2, 3.3, 4).
  *   w          device, bf16[n], 16-byte aligned (read only)
  *   packed     device, uint8[n/2], 16-byte aligned (written)
  *   st         host descriptor; st->absmax (and absmax2, absmax_mean with
@@ -112,15 +142,17 @@ BNBX_API size_t bnbx_quantize_nf4_workspace_bytes(int64_t n, int blocksize, int 
  *   workspace  device, >= bnbx_quantize_nf4_workspace_bytes(...) bytes,
  *              256-byte aligned (may be NULL when that is 0); contents are
  *              scratch, overwritten by the call
- * Errors: BNBX_E_INVAL (null pointer, n odd or < 2, blocksize != 64 is
- * BNBX_E_UNSUPPORTED), BNBX_E_ALIGN, BNBX_E_WORKSPACE. */
+ * Errors: BNBX_E_INVAL (null pointer, n odd or < 2, quant_type or
+ * compute_dtype out of range; blocksize != 64 is BNBX_E_UNSUPPORTED),
+ * BNBX_E_ALIGN, BNBX_E_WORKSPACE. */
 BNBX_API int bnbx_quantize_nf4(const uint16_t* w, uint8_t* packed, const bnbx_nf4_state* st,
                       void* workspace, size_t workspace_bytes, void* stream);
 
-/* Dequantize to bfloat16 (mlqm.cn article sec. 3.4).
+/* Dequantize to the compute dtype, bf16 or binary16 (mlqm.cn article
+ * sec. 3.4, 4).
  *   packed  device, uint8[n/2], 16-byte aligned
  *   st      host descriptor of the quant state (read)
- *   out     device, bf16[n], 16-byte aligned (written)
+ *   out     device, 16-bit[n] of st->compute_dtype, 16-byte aligned (written)
  * Errors: BNBX_E_INVAL, BNBX_E_ALIGN, BNBX_E_UNSUPPORTED. */
 BNBX_API int bnbx_dequantize_nf4(const uint8_t* packed, const bnbx_nf4_state* st, uint16_t* out,
                         void* stream);
@@ -128,11 +160,12 @@ BNBX_API int bnbx_dequantize_nf4(const uint8_t* packed, const bnbx_nf4_state* st
 /* Decode GEMV, Y[M, N] = X[M, K] . W_hat[N, K]^T, 1 <= M <= 16
  * (mlqm.cn article sec. 3.4 and the "4-bit is not always faster" pitfall in
  * sec. 7: the weight is streamed once from HBM in 4 bits and dequantized in
- * registers; products accumulate in fp32; Y is rounded to bf16).
- *   x       device, bf16, row m at x + m*ldx; ldx >= K, ldx % 8 == 0,
+ * registers; products accumulate in fp32; Y is rounded to the compute dtype).
+ * X, Y and the dequantized weights are of st->compute_dtype (sec. 4).
+ *   x       device, 16-bit, row m at x + m*ldx; ldx >= K, ldx % 8 == 0,
  *           16-byte aligned
  *   packed  device, the quantized [N, K] weight (st->n == N*K), 16-byte aligned
- *   y       device, bf16, row m at y + m*ldy; ldy >= N, written
+ *   y       device, 16-bit, row m at y + m*ldy; ldy >= N, written
  * K must be a multiple of 64 (blocks never straddle rows).
  * Errors: BNBX_E_INVAL (sizes, M outside 1..16, null), BNBX_E_ALIGN,
  * BNBX_E_UNSUPPORTED. */
@@ -144,10 +177,11 @@ BNBX_API int bnbx_gemv_nf4(const uint16_t* x, int64_t ldx, const uint8_t* packed
  * kernels need none, so it returns 0 for valid sizes. */
 BNBX_API size_t bnbx_gemm_nf4_workspace_bytes(int M, int N, int K);
 
-/* Prefill GEMM, Y[M, N] = X[M, K] . W_hat[N, K]^T for any M >= 1: weight
- * tiles are dequantized into LDS and fed to bf16 matrix cores with fp32
- * accumulation; Y is rounded to bf16 (mlqm.cn article sec. 3.4, "4-bit
- * storage, 16-bit compute").  Arguments as bnbx_gemv_nf4; workspace as
+/* Prefill GEMM, Y[M, N] = X[M, K] . W_hat[N, K]^T for any M >= 1: weights
+ * are dequantized in registers straight into 16-bit matrix-core operands
+ * (bf16 or binary16 MFMA by st->compute_dtype) with fp32 accumulation; Y is
+ * rounded to the compute dtype (mlqm.cn article sec. 3.4, "4-bit storage,
+ * 16-bit compute").  Arguments as bnbx_gemv_nf4; workspace as
  * sized by bnbx_gemm_nf4_workspace_bytes (may be NULL when that is 0).
  * Errors: as bnbx_gemv_nf4 (M >= 1), BNBX_E_WORKSPACE. */
 BNBX_API int bnbx_gemm_nf4(const uint16_t* x, int64_t ldx, const uint8_t* packed,

@@ -1,8 +1,8 @@
 """Seeded synthetic inputs for the NF4 path (shared by the tests, the smoke
 check and the benchmark).
 
-This module only draws random numbers and rounds them to bfloat16 for
-storage; it holds none of the quantization arithmetic, and neither the oracle
+This module only draws random numbers and rounds them to bfloat16 (or, for
+FP16-compute activations, IEEE binary16) for storage; it holds none of the quantization arithmetic, and neither the oracle
 nor the HIP library imports the other through it.
 
 Recipe (NumPy PCG64 ``default_rng(seed)``, ``standard_normal`` in binary32,
@@ -20,6 +20,10 @@ batched    W 14336x4096 N(0, 0.02), 0.1% of entries (without replacement) 2001
 prefill    W 8192x8192 N(0, 0.015); X 2048x8192 N(0, 1) with 4 of the     3001
            8192 feature columns scaled x50; double quant                  3002, 3003
 =========  =============================================================  ======
+
+FP16 compute dtype: the activations X are drawn with the same seeds and
+rounded to binary16 instead (``x_dtype="f16"``); weights stay bfloat16, the
+quantize input type.
 
 The bulk quantize-on-load stack (32 layers of Llama-7B-shaped linears) is
 drawn on the device by the benchmark, because 6.5e9 host draws would take
@@ -48,9 +52,27 @@ def to_bf16_bits(f: np.ndarray) -> np.ndarray:
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
 
 
+def to_f16_bits(f: np.ndarray) -> np.ndarray:
+    """Round binary32 samples to IEEE binary16 storage (PyTorch CPU,
+    nearest-even) and return the uint16 bit patterns."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(f, dtype=np.float32))
+    return t.to(torch.float16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def normal_16(shape, sigma: float, seed: int, dtype: str = "bf16", **kw) -> np.ndarray:
+    """``normal_bf16`` rounded to bfloat16 ("bf16") or binary16 ("f16")."""
+    if dtype == "bf16":
+        return normal_bf16(shape, sigma, seed, **kw)
+    if dtype == "f16":
+        return normal_bf16(shape, sigma, seed, _round=to_f16_bits, **kw)
+    raise ValueError(dtype)
+
+
 def normal_bf16(shape, sigma: float, seed: int, outlier_frac: float = 0.0,
                 outlier_scale: float = 1.0, outlier_seed: int | None = None,
-                outlier_cols: int = 0) -> np.ndarray:
+                outlier_cols: int = 0, _round=None) -> np.ndarray:
     """bfloat16 bit patterns of N(0, sigma^2) samples.
 
     ``outlier_frac``: that fraction of all entries (chosen without
@@ -71,30 +93,31 @@ def normal_bf16(shape, sigma: float, seed: int, outlier_frac: float = 0.0,
         cols = np.random.default_rng(outlier_seed).choice(shape[-1], size=outlier_cols,
                                                           replace=False)
         f[..., cols] *= np.float32(outlier_scale)
-    return to_bf16_bits(f)
+    return (_round or to_bf16_bits)(f)
 
 
-def tiny():
+def tiny(x_dtype: str = "bf16"):
     M, N, K = TINY_SHAPE
-    return normal_bf16((N, K), 0.02, 1), normal_bf16((M, K), 1.0, 2)
+    return normal_bf16((N, K), 0.02, 1), normal_16((M, K), 1.0, 2, x_dtype)
 
 
-def decode(s: int):
+def decode(s: int, x_dtype: str = "bf16"):
     N, K = DECODE_SHAPES[s]
-    return normal_bf16((N, K), 0.02, 1001 + 10 * s), normal_bf16((1, K), 1.0, 1002 + 10 * s)
+    return (normal_bf16((N, K), 0.02, 1001 + 10 * s),
+            normal_16((1, K), 1.0, 1002 + 10 * s, x_dtype))
 
 
-def batched():
+def batched(x_dtype: str = "bf16"):
     M, N, K = BATCHED_SHAPE
     w = normal_bf16((N, K), 0.02, 2001, outlier_frac=0.001, outlier_scale=20.0,
                     outlier_seed=2003)
-    return w, normal_bf16((M, K), 1.0, 2002)
+    return w, normal_16((M, K), 1.0, 2002, x_dtype)
 
 
-def prefill():
+def prefill(x_dtype: str = "bf16"):
     M, N, K = PREFILL_SHAPE
     w = normal_bf16((N, K), 0.015, 3001)
-    x = normal_bf16((M, K), 1.0, 3002, outlier_scale=50.0, outlier_seed=3003,
-                    outlier_cols=4)
+    x = normal_16((M, K), 1.0, 3002, x_dtype, outlier_scale=50.0, outlier_seed=3003,
+                  outlier_cols=4)
     return w, x
 

@@ -10,9 +10,13 @@ import torch
 from dequant_gemm_nf4_amd import tensors as T
 
 
-def dev_bf16(bits: np.ndarray, shape=None) -> torch.Tensor:
+TORCH_DTYPE = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def dev_bf16(bits: np.ndarray, shape=None, dtype: str = "bf16") -> torch.Tensor:
+    """16-bit patterns (bf16, or binary16 with dtype="f16") to a device tensor."""
     a = np.ascontiguousarray(bits, dtype=np.uint16)
-    t = torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16)
+    t = torch.from_numpy(a.view(np.int16).copy()).view(TORCH_DTYPE[dtype])
     if shape is not None:
         t = t.reshape(shape)
     return t.cuda()
@@ -22,9 +26,10 @@ def host_bits(t: torch.Tensor) -> np.ndarray:
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16).ravel()
 
 
-def gpu_quantize(w_bits: np.ndarray, shape, dq: bool) -> dict:
+def gpu_quantize(w_bits: np.ndarray, shape, dq: bool, quant_type: str = "nf4",
+                 dtype: str = "bf16") -> dict:
     w = dev_bf16(w_bits, shape)
-    q = T.quantize(w, dq)
+    q = T.quantize(w, dq, quant_type=quant_type, dtype=TORCH_DTYPE[dtype])
     torch.cuda.synchronize()
     out = {"packed": q.packed.cpu().numpy(), "double_quant": dq, "n": q.n, "blocksize": 64}
     if dq:
@@ -37,10 +42,12 @@ def gpu_quantize(w_bits: np.ndarray, shape, dq: bool) -> dict:
     return out
 
 
-def upload_state(ostate: dict, shape) -> T.QuantizedWeight:
-    """Device copy of a quant state the oracle produced."""
+def upload_state(ostate: dict, shape, dtype: str = "bf16") -> T.QuantizedWeight:
+    """Device copy of a quant state the oracle produced (its quant type; the
+    given compute dtype)."""
     dq = ostate["double_quant"]
-    q = T.empty_quantized(shape, dq)
+    q = T.empty_quantized(shape, dq, quant_type=ostate.get("quant_type", "nf4"),
+                          dtype=TORCH_DTYPE[dtype])
     q.packed.copy_(torch.from_numpy(np.ascontiguousarray(ostate["packed"])))
     if dq:
         q.absmax.copy_(torch.from_numpy(np.ascontiguousarray(ostate["absmax"], np.int8)))

@@ -30,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 9
+    assert len(declared) == 10
     assert sorted(bnbx.EXPORTED_SYMBOLS) == declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -43,6 +43,11 @@ def test_exports_every_declared_symbol(lib):
 def test_codebook_equals_oracle_bit_for_bit():
     ours = np.array(bnbx.bnbx_nf4_codebook(), dtype=np.float32)
     assert np.array_equal(ours.view(np.uint32), oracle.codebook().view(np.uint32))
+
+
+def test_fp4_codebook_equals_oracle_bit_for_bit():
+    ours = np.array(bnbx.bnbx_fp4_codebook(), dtype=np.float32)
+    assert np.array_equal(ours.view(np.uint32), oracle.fp4_codebook().view(np.uint32))
 
 
 def test_status_strings():
@@ -68,8 +73,9 @@ C = 3 << 20
 D = 4 << 20
 
 
-def state(n=4096, dq=1, blocksize=64, absmax=C, absmax2=D, mean=D + 4096):
-    return bnbx.Nf4State(n=n, blocksize=blocksize, double_quant=dq, absmax=absmax,
+def state(n=4096, dq=1, blocksize=64, absmax=C, absmax2=D, mean=D + 4096, qt=0, dt=0):
+    return bnbx.Nf4State(n=n, blocksize=blocksize, double_quant=dq, quant_type=qt,
+                         compute_dtype=dt, absmax=absmax,
                          absmax2=absmax2 if dq else None, absmax_mean=mean if dq else None)
 
 
@@ -87,6 +93,8 @@ def status_of(fn, *args):
     ("tiny_n", bnbx.BNBX_E_INVAL),
     ("blocksize", bnbx.BNBX_E_UNSUPPORTED),
     ("dq_flag", bnbx.BNBX_E_INVAL),
+    ("quant_type", bnbx.BNBX_E_INVAL),
+    ("compute_dtype", bnbx.BNBX_E_INVAL),
     ("null_absmax", bnbx.BNBX_E_INVAL),
     ("null_absmax2", bnbx.BNBX_E_INVAL),
     ("misaligned_w", bnbx.BNBX_E_ALIGN),
@@ -109,6 +117,10 @@ def test_quantize_rejects(case, expect):
         st = state(n, blocksize=128)
     elif case == "dq_flag":
         st = state(n, dq=2)
+    elif case == "quant_type":
+        st = state(n, qt=2)
+    elif case == "compute_dtype":
+        st = state(n, dt=-1)
     elif case == "null_absmax":
         st = state(n, absmax=None)
     elif case == "null_absmax2":
@@ -135,6 +147,8 @@ def test_dequantize_rejects():
     assert status_of(bnbx.bnbx_dequantize_nf4, A, state(7), B, 0) == bnbx.BNBX_E_INVAL
     assert status_of(bnbx.bnbx_dequantize_nf4, A, state(blocksize=32), B, 0) == \
         bnbx.BNBX_E_UNSUPPORTED
+    assert status_of(bnbx.bnbx_dequantize_nf4, A, state(qt=5), B, 0) == bnbx.BNBX_E_INVAL
+    assert status_of(bnbx.bnbx_dequantize_nf4, A, state(dt=2), B, 0) == bnbx.BNBX_E_INVAL
 
 
 def test_probe_stream_read_rejects():

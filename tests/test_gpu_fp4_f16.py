@@ -1,0 +1,307 @@
+"""GPU parity of the other 4-bit quant type (FP4, E2M1 levels divided by 6)
+and the other compute dtype (FP16) against the oracle, through the C ABI.
+
+Quantize and dequantize must be bit-identical to the oracle (the stored
+format and the rounding into bf16 / binary16 admit one result).  GEMV and
+GEMM are held to the same bar as with NF4 and bf16: relative Frobenius error
+<= 5e-3 against the oracle's binary64 product with its dequantized weight.
+With FP16 the kernels' own roundings (binary16 levels, binary16 Y) are
+smaller than with bf16, so the bar leaves more room."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from dequant_gemm_nf4_amd import tensors as T
+from tests.gpu_helpers import (assert_state_equal, dev_bf16, gpu_quantize, host_bits,
+                               upload_state)
+
+pytestmark = pytest.mark.gpu
+
+TOL = 5e-3
+COMBOS = [("fp4", "bf16"), ("nf4", "f16"), ("fp4", "f16")]
+
+
+# --------------------------------------------------------------------------
+# FP4 quantize (bit-exact)
+# --------------------------------------------------------------------------
+def check_quantize(bits, shape, dq, qt="fp4"):
+    ref = oracle.quantize(bits, dq, quant_type=qt)
+    got = gpu_quantize(bits, shape, dq, quant_type=qt)
+    assert_state_equal(got, ref)
+    return got, ref
+
+
+@pytest.mark.parametrize("dq", [False, True])
+def test_fp4_quantize_tiny_and_decode(dq):
+    w, _ = synth.tiny()
+    check_quantize(w, w.shape, dq)
+    w, _ = synth.decode(0)
+    check_quantize(w, w.shape, dq)
+
+
+def test_fp4_quantize_batched_outliers():
+    w, _ = synth.batched()
+    check_quantize(w, w.shape, True)
+
+
+@pytest.mark.parametrize("dq", [False, True])
+@pytest.mark.parametrize("n", [2, 62, 66, 514, 64 * 1000 + 6, 64 * 256 * 3 + 2])
+def test_fp4_quantize_ragged(n, dq):
+    bits = synth.normal_bf16((n,), 0.02, 600 + n)
+    check_quantize(bits, (n,), dq)
+
+
+def test_fp4_quantize_exhaustive_bf16_weights():
+    """Every finite bf16 weight in blocks whose absmax sweeps many binades."""
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f = oracle.bf16_bits_to_f32(allbits)
+    rng = np.random.default_rng(6)
+    anchors = oracle.f32_to_bf16_bits(
+        np.float32(2.0) ** rng.uniform(-30, 30, 8).astype(np.float32) *
+        rng.uniform(1, 2, 8).astype(np.float32))
+    anchors = np.concatenate([anchors, oracle.f32_to_bf16_bits(
+        np.array([1.0, 0.02, 6.0, 1e38, 6e-39], np.float32))])
+    pieces = []
+    for ab in anchors:
+        a = oracle.bf16_bits_to_f32(np.array([ab]))[0]
+        w = allbits[np.isfinite(f) & (np.abs(f) <= a)]
+        nblk = -(-w.size // 63)
+        body = np.zeros(nblk * 63, np.uint16)
+        body[:w.size] = w
+        pieces.append(np.concatenate([body.reshape(nblk, 63),
+                                      np.full((nblk, 1), ab, np.uint16)], axis=1).ravel())
+    bits = np.concatenate(pieces)
+    for dq in (False, True):
+        check_quantize(bits, bits.shape, dq)
+
+
+def test_fp4_quantize_special_blocks():
+    """Zero block (code 0), both bf16 neighbours of every FP4 decision
+    threshold at absmax 1, huge values, a subnormal absmax (the reciprocal
+    overflows: +inf takes the code of +1, -inf and NaN that of -1) and
+    negative zeros (code 0, never 8)."""
+    L = oracle.fp4_codebook()
+    order = oracle.sorted_codes("fp4")
+    Tf = oracle.thresholds(L[order])
+    blocks = [np.zeros(64, np.float32)]
+    near = np.zeros(64, np.float32)
+    near[0] = 1.0
+    tb = oracle.f32_to_bf16_bits(Tf)
+    tf = oracle.bf16_bits_to_f32(tb)
+    below = np.where(tf < Tf, tb, tb - np.where(Tf > 0, 1, -1).astype(np.int64)).astype(np.uint16)
+    above = np.where(tf >= Tf, tb, tb + np.where(Tf > 0, 1, -1).astype(np.int64)).astype(np.uint16)
+    nb_ = oracle.bf16_bits_to_f32(below)
+    na_ = oracle.bf16_bits_to_f32(above)
+    assert np.all(nb_ < Tf) and np.all(na_ >= Tf)
+    near[1:15] = nb_
+    near[15:29] = na_
+    blocks.append(near)
+    blocks.append(np.linspace(-3.0e38, 3.0e38, 64).astype(np.float32))
+    tiny = np.zeros(64, np.float32)
+    tiny[::3] = np.float32(2.0 ** -131)
+    tiny[1::3] = -np.float32(2.0 ** -132)
+    blocks.append(tiny)
+    blocks.append(np.full(64, -0.0, np.float32))
+    bits = oracle.f32_to_bf16_bits(np.concatenate(blocks))
+    for dq in (False, True):
+        got, ref = check_quantize(bits, bits.shape, dq)
+        c = ref["codes"]
+        assert np.all(c[:64] == 0) and not np.any(c == 8)
+        assert np.array_equal(c[64 + 1:64 + 15], order[:14])
+        assert np.array_equal(c[64 + 15:64 + 29], order[1:15])
+        assert np.all(c[4 * 64:5 * 64] == 0)
+
+
+# --------------------------------------------------------------------------
+# dequantize: FP4 levels and/or binary16 output (bit-exact)
+# --------------------------------------------------------------------------
+def check_dequant(bits, shape, dq, qt, dt):
+    ref_state = oracle.quantize(bits, dq, quant_type=qt)
+    ref = oracle.dequantize(ref_state["packed"], ref_state, dtype=dt)
+    q = upload_state(ref_state, shape, dt)
+    out = host_bits(T.dequantize(q))
+    bad = np.flatnonzero(out != ref)
+    assert bad.size == 0, \
+        f"{bad.size} mismatches, first at {bad[:8]}: {out[bad[:8]]} vs {ref[bad[:8]]}"
+
+
+@pytest.mark.parametrize("qt,dt", COMBOS)
+@pytest.mark.parametrize("dq", [False, True])
+def test_dequant_tiny_decode(qt, dt, dq):
+    w, _ = synth.tiny()
+    check_dequant(w, w.shape, dq, qt, dt)
+    w, _ = synth.decode(1)
+    check_dequant(w, w.shape, dq, qt, dt)
+
+
+@pytest.mark.parametrize("qt,dt", COMBOS)
+@pytest.mark.parametrize("n", [2, 34, 66, 64 * 257 + 18])
+def test_dequant_ragged(qt, dt, n):
+    bits = synth.normal_bf16((n,), 0.3, 950 + n)
+    check_dequant(bits, (n,), True, qt, dt)
+
+
+@pytest.mark.parametrize("qt", ["nf4", "fp4"])
+def test_dequant_f16_overflow_and_subnormals(qt):
+    """Blocks whose products overflow binary16 (absmax near 1e5: +-inf) and
+    blocks whose products are binary16 subnormals (absmax near 1e-6)."""
+    rng = np.random.default_rng(12)
+    f = []
+    for a in (1.0e5, 7.0e4, 3.0e4, 1.0e-6, 3.0e-7, 6.0e-5):
+        blk = rng.uniform(-a, a, 64).astype(np.float32)
+        blk[0] = a
+        blk[1] = -a
+        f.append(blk)
+    bits = oracle.f32_to_bf16_bits(np.concatenate(f))
+    for dq in (False, True):
+        ref_state = oracle.quantize(bits, dq, quant_type=qt)
+        ref = oracle.dequantize(ref_state["packed"], ref_state, dtype="f16")
+        assert np.any(ref == 0x7C00) and np.any((ref & 0x7C00) == 0)   # inf and subnormals
+        check_dequant(bits, bits.shape, dq, qt, "f16")
+
+
+# --------------------------------------------------------------------------
+# GEMV / GEMM
+# --------------------------------------------------------------------------
+def y_of(t, dt):
+    return oracle.bits_to_f32(host_bits(t), dt).astype(np.float64).reshape(t.shape)
+
+
+def setup(w_bits, shape, dq, qt, dt, check_state=True):
+    ref = oracle.quantize(w_bits, dq, quant_type=qt)
+    if check_state:
+        got = gpu_quantize(w_bits, shape, dq, quant_type=qt, dtype=dt)
+        assert_state_equal(got, ref)
+        q = got["_device"]
+    else:
+        q = upload_state(ref, shape, dt)
+    return ref, q
+
+
+def ref_product(x_bits, ref, N, K, dt, rows=None):
+    x = np.asarray(x_bits).reshape(-1, K)
+    if rows is not None:
+        x = x[rows]
+    return oracle.dequant_matmul_ref(x, ref["packed"], ref, N, K, dt)
+
+
+def run(kind, x_bits, M, K, q, dt):
+    x = dev_bf16(x_bits, (M, K), dt)
+    y = T.gemv(x, q) if kind == "gemv" else T.gemm(x, q)
+    torch.cuda.synchronize()
+    return y_of(y, dt)
+
+
+@pytest.mark.parametrize("qt,dt", COMBOS)
+@pytest.mark.parametrize("kind", ["gemv", "gemm"])
+def test_tiny(kind, qt, dt):
+    w, x = synth.tiny(dt)
+    M, N, K = synth.TINY_SHAPE
+    ref, q = setup(w, (N, K), False, qt, dt)
+    err = oracle.rel_frobenius(run(kind, x, M, K, q, dt), ref_product(x, ref, N, K, dt))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("qt,dt", COMBOS)
+@pytest.mark.parametrize("kind", ["gemv", "gemm"])
+@pytest.mark.parametrize("s", [0, 1, 2])
+def test_decode_shapes_m1(kind, s, qt, dt):
+    w, x = synth.decode(s, dt)
+    N, K = synth.DECODE_SHAPES[s]
+    ref, q = setup(w, (N, K), True, qt, dt, check_state=(kind == "gemv"))
+    err = oracle.rel_frobenius(run(kind, x, 1, K, q, dt), ref_product(x, ref, N, K, dt))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("qt,dt", COMBOS)
+@pytest.mark.parametrize("kind", ["gemv", "gemm"])
+def test_batched_m16_outliers(kind, qt, dt):
+    w, x = synth.batched(dt)
+    M, N, K = synth.BATCHED_SHAPE
+    ref, q = setup(w, (N, K), True, qt, dt)
+    err = oracle.rel_frobenius(run(kind, x, M, K, q, dt), ref_product(x, ref, N, K, dt))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("qt,dt", COMBOS)
+@pytest.mark.parametrize("kind", ["gemv", "gemm"])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 9, 16])
+def test_m_ragged_n(kind, M, qt, dt):
+    N, K = 1000, 4096
+    w = synth.normal_bf16((N, K), 0.02, 9000 + M)
+    x = synth.normal_16((M, K), 1.0, 9100 + M, dt)
+    ref, q = setup(w, (N, K), True, qt, dt, check_state=False)
+    err = oracle.rel_frobenius(run(kind, x, M, K, q, dt), ref_product(x, ref, N, K, dt))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("qt,dt", COMBOS)
+@pytest.mark.parametrize("M", [6, 16])
+@pytest.mark.parametrize("N,K,dq", [(200, 1088, True), (130, 4096, False), (130, 8192, True)])
+def test_gemv_more_than_four_rows(M, N, K, dq, qt, dt):
+    w = synth.normal_bf16((N, K), 0.05, 9200 + K + M)
+    x = synth.normal_16((M, K), 1.0, 9300 + K + M, dt)
+    ref, q = setup(w, (N, K), dq, qt, dt, check_state=False)
+    err = oracle.rel_frobenius(run("gemv", x, M, K, q, dt), ref_product(x, ref, N, K, dt))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("qt,dt", COMBOS)
+@pytest.mark.parametrize("kind", ["gemv", "gemm"])
+@pytest.mark.parametrize("N,K,dq", [(33, 64, False), (64, 192, True), (300, 11008, True),
+                                    (7, 4096 + 64, False)])
+def test_k_variants(kind, N, K, dq, qt, dt):
+    M = 3
+    w = synth.normal_bf16((N, K), 0.05, 9400 + K)
+    x = synth.normal_16((M, K), 1.0, 9500 + K, dt)
+    ref, q = setup(w, (N, K), dq, qt, dt, check_state=False)
+    err = oracle.rel_frobenius(run(kind, x, M, K, q, dt), ref_product(x, ref, N, K, dt))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("qt,dt", COMBOS)
+@pytest.mark.parametrize("M,N,K", [(7, 200, 512), (300, 260, 1024), (513, 384, 256)])
+def test_gemm_tiles_and_tails(M, N, K, qt, dt):
+    w = synth.normal_bf16((N, K), 0.02, 9600 + M)
+    x = synth.normal_16((M, K), 1.0, 9700 + M, dt)
+    ref, q = setup(w, (N, K), True, qt, dt, check_state=False)
+    err = oracle.rel_frobenius(run("gemm", x, M, K, q, dt), ref_product(x, ref, N, K, dt))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("qt,dt", COMBOS)
+def test_prefill_full_size_sampled_rows(qt, dt):
+    """M=2048, N=K=8192 with double quant and outlier feature columns, as the
+    benchmark launches it; 34 sampled rows of Y checked."""
+    w, x = synth.prefill(dt)
+    M, N, K = synth.PREFILL_SHAPE
+    ref, q = setup(w, (N, K), True, qt, dt)
+    y = run("gemm", x, M, K, q, dt)
+    rows = np.sort(np.random.default_rng(32).choice(M, 32, replace=False))
+    rows = np.unique(np.concatenate([rows, [0, M - 1]]))
+    err = oracle.rel_frobenius(y[rows], ref_product(x, ref, N, K, dt, rows))
+    assert err <= TOL, err
+    assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("qt,dt", COMBOS)
+@pytest.mark.parametrize("kind", ["gemv", "gemm"])
+def test_unit_vector_picks_a_column(kind, qt, dt):
+    """X = e_k: Y is column k of W_hat up to the roundings of the level and of
+    the product into the compute type (2^-7 relative for bf16, 2^-10 for
+    binary16)."""
+    N, K = 512, 1024
+    w = synth.normal_bf16((N, K), 0.02, 9800)
+    ref, q = setup(w, (N, K), True, qt, dt, check_state=False)
+    what = oracle.bits_to_f32(oracle.dequantize(ref["packed"], ref, dtype=dt), dt).reshape(N, K)
+    one = 0x3F80 if dt == "bf16" else 0x3C00
+    rel = 2.0 ** -7 if dt == "bf16" else 2.0 ** -10
+    for k in (0, 1, 63, 64, 1023):
+        x = np.zeros((1, K), np.uint16)
+        x[0, k] = one
+        y = run(kind, x, 1, K, q, dt)[0]
+        col = what[:, k].astype(np.float64)
+        assert np.all(np.abs(y - col) <= np.abs(col) * rel + 2.0 ** -24)
