@@ -26,6 +26,7 @@ it.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -36,7 +37,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
-BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published (fp16: the same)
 METRIC = "NF4 dequant-GEMV HBM GB/s (M=1) + GEMM TFLOP/s (M=2048), % of peak"
 DECODE_SHAPES = ((4096, 4096), (11008, 4096), (4096, 11008))
 # the linears of one Llama-7B-shaped layer: (name, shape index)
@@ -123,6 +124,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the FP4 / FP16 measurements (profiling runs)")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="run a 256 MiB plain copy first (counter scaling reference)")
     args = ap.parse_args()
@@ -298,6 +301,85 @@ def main():
         del g
     read_gbs = (sum(read_bytes) / len(read_bytes)) / (sum(read_us) / len(read_us) * 1e-6) / 1e9
 
+    # The other 4-bit quant type and compute dtype (FP4 levels; FP16 compute),
+    # timed after the steps like the read ceiling: the stack quantized again
+    # as FP4, then per (quant type, dtype) the dequantize of the stack, the
+    # decode GEMVs per shape and the prefill GEMM, each replayed in a graph.
+    def timed_ms(fn, reps):
+        fn()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            fn()
+        g.replay()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1) / reps
+
+    def measure_variants():
+        reps = max(2, args.steps)
+        xs16 = []
+        for s, (N, K) in enumerate(DECODE_SHAPES):
+            gen.manual_seed(6000 + s)
+            xs16.append(torch.randn(1, K, generator=gen, device=dev).to(torch.float16))
+        gen.manual_seed(7000)
+        wp = (torch.randn(Np, Kp, generator=gen, device=dev) * 0.015).to(torch.bfloat16)
+        gen.manual_seed(7001)
+        xp16 = torch.randn(Mp, Kp, generator=gen, device=dev)
+        gen.manual_seed(7002)
+        xp16[:, torch.randperm(Kp, generator=gen, device=dev)[:4]] *= 50.0
+        xp16 = xp16.to(torch.float16)
+        qp_by = {"nf4": qp, "fp4": T.quantize(wp, True, quant_type="fp4")}
+        del wp
+        qs_fp4 = [T.empty_quantized(w.shape, True, dev, "fp4") for w in weights]
+        q_fp4_ms = timed_ms(lambda: [T.quantize(w, True, out=qs_fp4[i], workspace=ws)
+                                     for i, w in enumerate(weights)], reps)
+        stack_by = {"nf4": qs, "fp4": qs_fp4}
+        deq16 = torch.empty(maxn, dtype=torch.float16, device=dev)
+        ys16 = [torch.empty(1, N, dtype=torch.float16, device=dev) for N, K in DECODE_SHAPES]
+        yp16 = torch.empty(Mp, Np, dtype=torch.float16, device=dev)
+        variants = {}
+        for qt, dt in (("fp4", "bf16"), ("nf4", "f16"), ("fp4", "f16")):
+            tdt = torch.float16 if dt == "f16" else torch.bfloat16
+            sv = [dataclasses.replace(q, dtype=tdt) for q in stack_by[qt]]
+            qpv = dataclasses.replace(qp_by[qt], dtype=tdt)
+            dbuf = deq16 if dt == "f16" else deq
+            xv, yv = (xs16, ys16) if dt == "f16" else (xs, ys)
+            xpv, ypv = (xp16, yp16) if dt == "f16" else (xp, yp)
+            d_ms = timed_ms(lambda: [T.dequantize(q, out=dbuf[: q.n].view(q.shape)) for q in sv],
+                            reps)
+            v_us = []
+            for s in range(len(DECODE_SHAPES)):
+                ms = timed_ms(lambda: [T.gemv(xv[s], sv[i], out=yv[s]) for i in by_shape[s]],
+                              reps)
+                v_us.append(ms * 1e3 / len(by_shape[s]))
+            m_ms = timed_ms(lambda: T.gemm(xpv, qpv, out=ypv), reps)
+            gbs = (sum(gemv_bytes(1, N, K) for N, K in DECODE_SHAPES) / len(DECODE_SHAPES)) / \
+                (sum(v_us) / len(v_us) * 1e-6) / 1e9
+            tf = 2.0 * Mp * Np * Kp / (m_ms * 1e-3) / 1e12
+            entry = {
+                "dequantize_gbs": round(sum(dequant_bytes(*DECODE_SHAPES[si]) for si in wshape)
+                                        / (d_ms * 1e-3) / 1e9, 1),
+                "gemv_gbs": round(gbs, 1),
+                "gemv_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                "gemv_launch_us_by_shape": {f"{N}x{K}": round(u, 3)
+                                            for (N, K), u in zip(DECODE_SHAPES, v_us)},
+                "gemm_tflops": round(tf, 1),
+                "gemm_frac": round(tf / BF16_PEAK_TFLOPS, 4),
+            }
+            if qt == "fp4" and dt == "bf16":
+                entry["quantize_input_read_gbs"] = round(
+                    sum(2 * DECODE_SHAPES[si][0] * DECODE_SHAPES[si][1] for si in wshape)
+                    / (q_fp4_ms * 1e-3) / 1e9, 1)
+            variants[f"{qt}_{dt}"] = entry
+        return variants
+
+    variants = None if args.no_variants else measure_variants()
+
     t_q = stage_ms(0) / 1e3
     t_d = stage_ms(1) / 1e3
     t_shape = [stage_ms(2 + s) / 1e3 for s in range(len(DECODE_SHAPES))]
@@ -383,6 +465,7 @@ def main():
                 "hbm_frac": round(read_gbs / HBM_PEAK_GBS, 4),
                 "gemv_over_ceiling": round(gemv_gbs / read_gbs, 4),
             },
+            "variants": variants,
             "stage_ms_per_step": {"quantize": round(t_q / K_ * 1e3, 3),
                                   "dequantize": round(t_d / K_ * 1e3, 3),
                                   "gemv": round(t_v / K_ * 1e3, 3),
