@@ -1,0 +1,121 @@
+"""PyTorch custom op and module over the C ABI: the 4-bit linear layer as
+``torch.ops.bnbx.linear4bit`` and a ``Linear4bit`` module that quantizes its
+weight on load.
+
+The pomoai.com overview (module list) has ``Linear4bit`` replacing
+``torch.nn.Linear`` and the mlqm.cn article (section 4) loads a model in
+4 bits with a quant type (nf4 / fp4), double quantization and a compute
+dtype (bf16 / fp16); its section 1 credits 4-bit inference under
+``torch.compile(fullgraph=True)``.  The op is an opaque custom op with a
+fake (shape-only) implementation, so it traces into a full graph; the
+arithmetic runs in the library's kernels (GEMV for at most 16 rows of X,
+GEMM otherwise) on the current stream.  Nothing here computes.
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import tensors as T
+
+_DTYPES = (torch.bfloat16, torch.float16)
+
+
+def _state(x: torch.Tensor, packed, absmax, absmax2, absmax_mean, out_features: int,
+           quant_type: str) -> T.QuantizedWeight:
+    K = x.shape[-1]
+    return T.QuantizedWeight(n=out_features * K, shape=(out_features, K),
+                             double_quant=absmax2 is not None, packed=packed, absmax=absmax,
+                             absmax2=absmax2, absmax_mean=absmax_mean, quant_type=quant_type,
+                             dtype=x.dtype)
+
+
+@torch.library.custom_op("bnbx::linear4bit", mutates_args=())
+def linear4bit(x: torch.Tensor, packed: torch.Tensor, absmax: torch.Tensor,
+               absmax2: Optional[torch.Tensor], absmax_mean: Optional[torch.Tensor],
+               out_features: int, quant_type: str) -> torch.Tensor:
+    """Y[..., N] = X[..., K] . W_hat[N, K]^T with W_hat the dequantized 4-bit
+    weight; X, Y and W_hat in X's dtype (bf16 or fp16)."""
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"linear4bit: x must be bfloat16 or float16, not {x.dtype}")
+    K = x.shape[-1]
+    x2 = x.reshape(-1, K)
+    if x2.stride(-1) != 1 or x2.stride(0) % 8 != 0 or x2.data_ptr() % 16 != 0:
+        x2 = x2.contiguous()
+    M = x2.shape[0]
+    y = torch.empty(M, out_features, dtype=x.dtype, device=x.device)
+    if M > 0:
+        q = _state(x, packed, absmax, absmax2, absmax_mean, out_features, quant_type)
+        (T.gemv if M <= 16 else T.gemm)(x2, q, out=y)
+    return y.reshape(*x.shape[:-1], out_features)
+
+
+@linear4bit.register_fake
+def _(x, packed, absmax, absmax2, absmax_mean, out_features, quant_type):
+    return x.new_empty(*x.shape[:-1], out_features)
+
+
+class Linear4bit(torch.nn.Module):
+    """A bias-free ``nn.Linear(in_features, out_features)`` whose weight is
+    held as 4-bit codes (NF4 or FP4, blocks of 64, optional double quant) and
+    whose forward runs ``torch.ops.bnbx.linear4bit`` in ``compute_dtype``.
+    ``load_weight`` quantizes a bf16 [out, in] weight on the device."""
+
+    def __init__(self, in_features: int, out_features: int, quant_type: str = "nf4",
+                 double_quant: bool = True, compute_dtype: torch.dtype = torch.bfloat16,
+                 device="cuda"):
+        super().__init__()
+        if quant_type not in T.QUANT_TYPES:
+            raise ValueError(f"quant_type must be one of {sorted(T.QUANT_TYPES)}")
+        if compute_dtype not in _DTYPES:
+            raise ValueError("compute_dtype must be torch.bfloat16 or torch.float16")
+        if in_features % 64 != 0:
+            raise ValueError("in_features must be a multiple of 64 (one block per row step)")
+        self.in_features, self.out_features = in_features, out_features
+        self.quant_type, self.double_quant, self.compute_dtype = quant_type, double_quant, \
+            compute_dtype
+        q = T.empty_quantized((out_features, in_features), double_quant, device, quant_type,
+                              compute_dtype)
+        self.register_buffer("packed", q.packed)
+        self.register_buffer("absmax", q.absmax)
+        self.register_buffer("absmax2", q.absmax2)
+        self.register_buffer("absmax_mean", q.absmax_mean)
+
+    def quantized(self) -> T.QuantizedWeight:
+        return T.QuantizedWeight(self.in_features * self.out_features,
+                                 (self.out_features, self.in_features), self.double_quant,
+                                 self.packed, self.absmax, self.absmax2, self.absmax_mean,
+                                 self.quant_type, self.compute_dtype)
+
+    @torch.no_grad()
+    def load_weight(self, w: torch.Tensor) -> "Linear4bit":
+        """Quantize-on-load of a bf16 weight [out_features, in_features]."""
+        if tuple(w.shape) != (self.out_features, self.in_features):
+            raise ValueError(f"weight shape {tuple(w.shape)} != "
+                             f"{(self.out_features, self.in_features)}")
+        w = w.to(device=self.packed.device, dtype=torch.bfloat16).contiguous()
+        T.quantize(w, self.double_quant, out=self.quantized())
+        return self
+
+    @classmethod
+    def from_linear(cls, linear: torch.nn.Linear, **kw) -> "Linear4bit":
+        if linear.bias is not None:
+            raise ValueError("Linear4bit has no bias")
+        m = cls(linear.in_features, linear.out_features, device=linear.weight.device, **kw)
+        return m.load_weight(linear.weight)
+
+    def dequantize(self) -> torch.Tensor:
+        return T.dequantize(self.quantized())
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        if x.dtype != self.compute_dtype:
+            raise TypeError(f"input dtype {x.dtype} != compute dtype {self.compute_dtype}")
+        return torch.ops.bnbx.linear4bit(x, self.packed, self.absmax, self.absmax2,
+                                         self.absmax_mean, self.out_features, self.quant_type)
+
+    def extra_repr(self) -> str:
+        return (f"in_features={self.in_features}, out_features={self.out_features}, "
+                f"quant_type={self.quant_type}, double_quant={self.double_quant}, "
+                f"compute_dtype={self.compute_dtype}")

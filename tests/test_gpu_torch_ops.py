@@ -1,0 +1,104 @@
+"""GPU checks of torch.ops.bnbx.linear4bit and Linear4bit: the module's
+output against the oracle (rel. Frobenius <= 5e-3), the same output from a
+torch.compile(fullgraph=True) graph and from a captured HIP graph, and
+torch.library.opcheck of the op."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from dequant_gemm_nf4_amd.torch_ops import Linear4bit
+from tests.gpu_helpers import TORCH_DTYPE, dev_bf16, host_bits
+
+pytestmark = pytest.mark.gpu
+
+TOL = 5e-3
+
+
+def make(N, K, qt, dt, dq=True, seed=9900):
+    w = synth.normal_bf16((N, K), 0.02, seed)
+    m = Linear4bit(K, N, quant_type=qt, double_quant=dq, compute_dtype=TORCH_DTYPE[dt])
+    m.load_weight(dev_bf16(w, (N, K)))
+    torch.cuda.synchronize()
+    return w, m
+
+
+@pytest.mark.parametrize("qt,dt", [("nf4", "bf16"), ("fp4", "f16")])
+@pytest.mark.parametrize("dq", [False, True])
+@pytest.mark.parametrize("lead", [(1,), (5,), (2, 32)])
+def test_module_against_oracle(qt, dt, dq, lead):
+    N, K = 384, 1024
+    w, m = make(N, K, qt, dt, dq)
+    ref = oracle.quantize(w, dq, quant_type=qt)
+    assert np.array_equal(m.packed.cpu().numpy(), ref["packed"])
+    M = int(np.prod(lead))
+    xb = synth.normal_16((M, K), 1.0, 9901 + M, dt)
+    x = dev_bf16(xb, (*lead, K), dt)
+    y = m(x)
+    torch.cuda.synchronize()
+    assert y.shape == (*lead, N) and y.dtype == TORCH_DTYPE[dt]
+    got = oracle.bits_to_f32(host_bits(y), dt).astype(np.float64).reshape(M, N)
+    err = oracle.rel_frobenius(got, oracle.dequant_matmul_ref(xb, ref["packed"], ref, N, K, dt))
+    assert err <= TOL, err
+
+
+def test_module_dequantize_and_from_linear():
+    N, K = 128, 256
+    lin = torch.nn.Linear(K, N, bias=False, device="cuda", dtype=torch.bfloat16)
+    m = Linear4bit.from_linear(lin, quant_type="nf4")
+    wb = host_bits(lin.weight)
+    ref = oracle.quantize(wb, True)
+    assert np.array_equal(host_bits(m.dequantize()), oracle.dequantize(ref["packed"], ref))
+
+
+class TwoLayers(torch.nn.Module):
+    def __init__(self, a, b):
+        super().__init__()
+        self.a, self.b = a, b
+
+    def forward(self, x):
+        return self.b(self.a(x))
+
+
+@pytest.mark.parametrize("M", [1, 40])
+def test_torch_compile_fullgraph_equals_eager(M):
+    K, H, N = 512, 256, 192
+    _, a = make(H, K, "nf4", "bf16", seed=9910)
+    _, b = make(N, H, "nf4", "bf16", seed=9911)
+    net = TwoLayers(a, b)
+    x = dev_bf16(synth.normal_16((M, K), 1.0, 9912), (M, K))
+    eager = net(x)
+    compiled = torch.compile(net, fullgraph=True, backend="aot_eager")
+    out = compiled(x)
+    torch.cuda.synchronize()
+    assert torch.equal(out, eager)
+
+
+def test_opcheck():
+    N, K = 64, 256
+    _, m = make(N, K, "fp4", "f16", dq=True, seed=9920)
+    x = dev_bf16(synth.normal_16((3, K), 1.0, 9921, "f16"), (3, K), "f16")
+    torch.library.opcheck(torch.ops.bnbx.linear4bit.default,
+                          (x, m.packed, m.absmax, m.absmax2, m.absmax_mean, N, "fp4"))
+
+
+def test_captured_graph_replays_match_eager():
+    N, K = 256, 1024
+    _, m = make(N, K, "nf4", "bf16", seed=9930)
+    x = dev_bf16(synth.normal_16((4, K), 1.0, 9931), (4, K))
+    eager = m(x)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        m(x)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        y = m(x)
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager)

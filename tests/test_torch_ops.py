@@ -1,0 +1,52 @@
+"""The torch custom op and Linear4bit module without a GPU: registration,
+shape inference through the fake implementation (meta tensors), argument
+checks."""
+
+import pytest
+import torch
+
+from dequant_gemm_nf4_amd import torch_ops  # noqa: F401  (registers bnbx::linear4bit)
+from dequant_gemm_nf4_amd.torch_ops import Linear4bit
+
+
+def test_op_is_registered():
+    assert hasattr(torch.ops.bnbx, "linear4bit")
+    schema = str(torch.ops.bnbx.linear4bit.default._schema)
+    assert "out_features" in schema and "quant_type" in schema
+
+
+@pytest.mark.parametrize("dq", [False, True])
+@pytest.mark.parametrize("shape", [(1, 128), (5, 128), (2, 3, 128), (0, 128)])
+def test_fake_shapes_on_meta(shape, dq):
+    m = Linear4bit(128, 96, double_quant=dq, device="meta")
+    assert m.packed.shape == (96 * 128 // 2,) and m.packed.dtype == torch.uint8
+    assert m.absmax.dtype == (torch.int8 if dq else torch.float32)
+    assert (m.absmax2 is None) == (not dq)
+    x = torch.empty(*shape, dtype=torch.bfloat16, device="meta")
+    y = m(x)
+    assert y.shape == (*shape[:-1], 96) and y.dtype == torch.bfloat16
+
+
+def test_fake_shapes_under_fake_tensor_mode():
+    from torch._subclasses.fake_tensor import FakeTensorMode
+    with FakeTensorMode():
+        x = torch.empty(4, 256, dtype=torch.float16)
+        p = torch.empty(64 * 256 // 2, dtype=torch.uint8)
+        a = torch.empty(64 * 256 // 64, dtype=torch.float32)
+        y = torch.ops.bnbx.linear4bit(x, p, a, None, None, 64, "fp4")
+        assert y.shape == (4, 64) and y.dtype == torch.float16
+
+
+def test_argument_checks():
+    with pytest.raises(ValueError):
+        Linear4bit(100, 32, device="meta")                 # in_features % 64
+    with pytest.raises(ValueError):
+        Linear4bit(128, 32, quant_type="int4", device="meta")
+    with pytest.raises(ValueError):
+        Linear4bit(128, 32, compute_dtype=torch.float32, device="meta")
+    m = Linear4bit(128, 32, compute_dtype=torch.float16, device="meta")
+    with pytest.raises(TypeError):
+        m(torch.empty(1, 128, dtype=torch.bfloat16, device="meta"))
+    with pytest.raises(ValueError):
+        m.load_weight(torch.empty(32, 64, dtype=torch.bfloat16, device="meta"))
+    assert "quant_type=nf4" in repr(m)
