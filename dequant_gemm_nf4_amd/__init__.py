@@ -23,8 +23,8 @@ __all__ = [
     "bnbx_status_str", "bnbx_nf4_codebook", "bnbx_fp4_codebook",
     "bnbx_quantize_nf4_workspace_bytes",
     "bnbx_quantize_nf4", "bnbx_dequantize_nf4", "bnbx_gemv_nf4",
-    "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4", "bnbx_probe_stream_read",
-    "BNBX_PROBE_SINK_WORDS", "EXPORTED_SYMBOLS", "BNBX_QUANT_NF4", "BNBX_QUANT_FP4",
+    "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4", "bnbx_gemm_nf4_dx",
+    "bnbx_probe_stream_read", "BNBX_PROBE_SINK_WORDS", "EXPORTED_SYMBOLS", "BNBX_QUANT_NF4", "BNBX_QUANT_FP4",
     "BNBX_DTYPE_BF16", "BNBX_DTYPE_F16",
 ]
 
@@ -44,7 +44,7 @@ EXPORTED_SYMBOLS = (
     "bnbx_status_str", "bnbx_nf4_codebook", "bnbx_fp4_codebook",
     "bnbx_quantize_nf4_workspace_bytes",
     "bnbx_quantize_nf4", "bnbx_dequantize_nf4", "bnbx_gemv_nf4",
-    "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4",
+    "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4", "bnbx_gemm_nf4_dx",
     "bnbx_probe_stream_read",          # include/bnbx_probe.h (measurement aid)
 )
 BNBX_PROBE_SINK_WORDS = 1024
@@ -114,6 +114,8 @@ def lib() -> ctypes.CDLL:
     L.bnbx_gemm_nf4_workspace_bytes.restype = sz
     L.bnbx_gemm_nf4.argtypes = [vp, i64, vp, sp, i32, i32, i32, vp, i64, vp, sz, vp]
     L.bnbx_gemm_nf4.restype = i32
+    L.bnbx_gemm_nf4_dx.argtypes = [vp, i64, vp, sp, i32, i32, i32, vp, i64, vp]
+    L.bnbx_gemm_nf4_dx.restype = i32
     L.bnbx_probe_stream_read.argtypes = [vp, sz, vp, sz, vp, vp]
     L.bnbx_probe_stream_read.restype = i32
     _lib = L
@@ -194,6 +196,13 @@ def bnbx_gemm_nf4(x, ldx: int, packed, state: Nf4State, M: int, N: int, K: int, 
     _check(lib().bnbx_gemm_nf4(_ptr(x), int(ldx), _ptr(packed), ctypes.byref(state), int(M),
                                int(N), int(K), _ptr(y), int(ldy), _ptr(workspace),
                                int(workspace_bytes), _stream(stream)), "bnbx_gemm_nf4")
+
+
+def bnbx_gemm_nf4_dx(dy, lddy: int, packed, state: Nf4State, M: int, N: int, K: int, dx,
+                     lddx: int, stream=None) -> None:
+    _check(lib().bnbx_gemm_nf4_dx(_ptr(dy), int(lddy), _ptr(packed), ctypes.byref(state), int(M),
+                                  int(N), int(K), _ptr(dx), int(lddx), _stream(stream)),
+           "bnbx_gemm_nf4_dx")
 
 
 def _nbytes(t) -> int | None:

@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbnbx.so")
 SOURCES = ["bnbx_api.hip", "bnbx_quant.hip", "bnbx_dequant.hip", "bnbx_gemv.hip", "bnbx_gemm.hip",
-           "bnbx_probe.hip"]
+           "bnbx_gemm_dx.hip", "bnbx_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -292,4 +292,24 @@ int bnbx_gemm_nf4(const uint16_t* x, int64_t ldx, const uint8_t* packed,
   return hip_status(e);
 }
 
+int bnbx_gemm_nf4_dx(const uint16_t* dy, int64_t lddy, const uint8_t* packed,
+                     const bnbx_nf4_state* st, int M, int N, int K, uint16_t* dx, int64_t lddx,
+                     void* stream) {
+  // dY [M, N] plays the part of X (ld >= N) and dX [M, K] that of Y (ld >= K).
+  if (dy == nullptr || packed == nullptr || dx == nullptr) return BNBX_E_INVAL;
+  const int s = check_state(st);
+  if (s != BNBX_OK) return s;
+  if (M < 1 || N < 1 || K < kBlock || K % kBlock != 0) return BNBX_E_INVAL;
+  if (st->n != (int64_t)N * (int64_t)K) return BNBX_E_INVAL;
+  if (lddy < N || lddx < K) return BNBX_E_INVAL;
+  if (lddy % 8 != 0) return BNBX_E_ALIGN;
+  if (!aligned(dy, 16) || !aligned(packed, 16) || !aligned(dx, 2)) return BNBX_E_ALIGN;
+  const hipError_t e = launch_gemm_dx(dy, lddy, packed, st->absmax, st->absmax2, st->absmax_mean,
+                                      st->double_quant, st->quant_type,
+                                      st->compute_dtype == BNBX_DTYPE_F16, M, N, K, dx, lddx,
+                                      (hipStream_t)stream);
+  if (e == hipErrorNotSupported) return BNBX_E_UNSUPPORTED;
+  return hip_status(e);
+}
+
 }  // extern "C"

@@ -76,5 +76,11 @@ hipError_t launch_gemm(const uint16_t* x, int64_t ldx, const uint8_t* packed, co
                        const float* absmax2, const float* mean, int double_quant, int quant_type,
                        bool f16, int M, int N, int K, uint16_t* y, int64_t ldy,
                        hipStream_t stream);
+// dX[M, K] = dY[M, N] . W_hat[N, K]; hipErrorNotSupported unless N % 64 == 0
+// and the offsets fit 32 bits.
+hipError_t launch_gemm_dx(const uint16_t* dy, int64_t lddy, const uint8_t* packed,
+                          const void* absmax, const float* absmax2, const float* mean,
+                          int double_quant, int quant_type, bool f16, int M, int N, int K,
+                          uint16_t* dx, int64_t lddx, hipStream_t stream);
 
 }  // namespace bnbx

@@ -8,8 +8,8 @@ import dataclasses
 
 import torch
 
-from . import (Nf4State, bnbx_dequantize_nf4, bnbx_gemm_nf4, bnbx_gemm_nf4_workspace_bytes,
-               bnbx_gemv_nf4, bnbx_quantize_nf4, bnbx_quantize_nf4_workspace_bytes)
+from . import (Nf4State, bnbx_dequantize_nf4, bnbx_gemm_nf4, bnbx_gemm_nf4_dx,
+               bnbx_gemm_nf4_workspace_bytes, bnbx_gemv_nf4, bnbx_quantize_nf4, bnbx_quantize_nf4_workspace_bytes)
 
 BLOCKSIZE = 64
 GROUP = 256
@@ -111,3 +111,14 @@ def gemm(x: torch.Tensor, q: QuantizedWeight, out: torch.Tensor | None = None,
     ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device) if nbytes else None
     bnbx_gemm_nf4(x, x.stride(0), q.packed, q.state, M, N, K, y, y.stride(0), ws, nbytes, stream)
     return y
+
+
+def gemm_dx(dy: torch.Tensor, q: QuantizedWeight, out: torch.Tensor | None = None,
+            stream=None) -> torch.Tensor:
+    """dX = dY . W_hat for dY [M, N], W [N, K] (the input gradient of gemm)."""
+    M, N = dy.shape
+    K = q.shape[1]
+    assert dy.dtype == q.dtype and N == q.shape[0]
+    dx = out if out is not None else torch.empty(M, K, dtype=q.dtype, device=dy.device)
+    bnbx_gemm_nf4_dx(dy, dy.stride(0), q.packed, q.state, M, N, K, dx, dx.stride(0), stream)
+    return dx

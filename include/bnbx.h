@@ -189,6 +189,23 @@ BNBX_API int bnbx_gemm_nf4(const uint16_t* x, int64_t ldx, const uint8_t* packed
                   uint16_t* y, int64_t ldy, void* workspace, size_t workspace_bytes,
                   void* stream);
 
+/* Input gradient of the 4-bit linear layer, dX[M, K] = dY[M, N] . W_hat[N, K]
+ * (the weights stay frozen, as for the 4-bit base layer under QLoRA in the
+ * pomoai.com overview; W_hat as in bnbx_dequantize_nf4, mlqm.cn article
+ * sec. 3.4): the weights are dequantized into LDS, transposed, and fed to
+ * 16-bit matrix cores with fp32 accumulation; dX is rounded to the compute
+ * dtype.  dY, dX and W_hat are of st->compute_dtype.
+ *   dy      device, 16-bit, row m at dy + m*lddy; lddy >= N, lddy % 8 == 0,
+ *           16-byte aligned
+ *   packed  device, the quantized [N, K] weight (st->n == N*K), 16-byte aligned
+ *   dx      device, 16-bit, row m at dx + m*lddx; lddx >= K, written
+ * K must be a multiple of 64 and N a multiple of 64 (else
+ * BNBX_E_UNSUPPORTED), M >= 1.
+ * Errors: BNBX_E_INVAL (sizes, null), BNBX_E_ALIGN, BNBX_E_UNSUPPORTED. */
+BNBX_API int bnbx_gemm_nf4_dx(const uint16_t* dy, int64_t lddy, const uint8_t* packed,
+                     const bnbx_nf4_state* st, int M, int N, int K,
+                     uint16_t* dx, int64_t lddx, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -15,7 +15,8 @@ silent the reading taken is stated at the function.  Parity status:
 * pack                -- pinned (hand-built bytes)
 * double quant        -- pinned (exact rational mean, bounds, saturation)
 * dequant             -- pinned (absmax 1 block, bounds)
-* matmul              -- pinned (unit vector, brute-force loops)
+* matmul              -- pinned (unit vector, brute-force loops; the dX
+                         product by its transpose identity with the forward)
 * memory arithmetic   -- pinned against the figures the pages print
 * FP4 levels          -- pinned (the E2M1 value table, brute-force nearest
                          level over the 15 distinct values, error bound)
@@ -50,6 +51,7 @@ from .nf4 import (  # noqa: F401
     dequantize,
     matmul_ref,
     dequant_matmul_ref,
+    dequant_matmul_dx_ref,
     rel_frobenius,
     storage_bytes,
 )

@@ -415,6 +415,18 @@ def dequant_matmul_ref(x_bits: np.ndarray, packed: np.ndarray, state: dict,
     return matmul_ref(np.asarray(x_bits).reshape(-1, K), w_hat, dtype)
 
 
+def dequant_matmul_dx_ref(dy_bits: np.ndarray, packed: np.ndarray, state: dict,
+                          N: int, K: int, dtype: str = "bf16") -> np.ndarray:
+    """Input gradient of the layer above: dX = dY . W_hat for dY [M, N] and
+    the dequantized weight W_hat [N, K] (step 6), in binary64.  The weight is
+    frozen (the 4-bit base layer under QLoRA, pomoai.com overview), so this
+    is the only gradient that flows through it.  Library primitive: NumPy's
+    binary64 matmul."""
+    w_hat = bits_to_f32(dequantize(packed, state, N * K, dtype), dtype).astype(np.float64)
+    dy = bits_to_f32(np.asarray(dy_bits).reshape(-1, N), dtype).astype(np.float64)
+    return dy @ w_hat.reshape(N, K)
+
+
 def rel_frobenius(y, y_ref) -> float:
     """||y - y_ref||_F / ||y_ref||_F in binary64."""
     y = np.asarray(y, dtype=np.float64)

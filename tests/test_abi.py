@@ -30,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 10
+    assert len(declared) == 11
     assert sorted(bnbx.EXPORTED_SYMBOLS) == declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -207,3 +207,18 @@ def test_matmul_rejects(fn):
 def test_binding_names_match_header():
     for name in header_functions():
         assert callable(getattr(bnbx, name)), name
+
+
+def test_gemm_dx_rejects():
+    st = state(n=128 * 256)
+    f = bnbx.bnbx_gemm_nf4_dx
+    assert status_of(f, None, 128, B, st, 4, 128, 256, C, 256, 0) == bnbx.BNBX_E_INVAL
+    assert status_of(f, A, 128, B, st, 0, 128, 256, C, 256, 0) == bnbx.BNBX_E_INVAL
+    assert status_of(f, A, 100, B, st, 4, 128, 256, C, 256, 0) == bnbx.BNBX_E_INVAL   # lddy < N
+    assert status_of(f, A, 128, B, st, 4, 128, 256, C, 200, 0) == bnbx.BNBX_E_INVAL   # lddx < K
+    assert status_of(f, A, 132, B, st, 4, 128, 256, C, 256, 0) == bnbx.BNBX_E_ALIGN   # lddy % 8
+    assert status_of(f, A + 8, 128, B, st, 4, 128, 256, C, 256, 0) == bnbx.BNBX_E_ALIGN
+    assert status_of(f, A, 128, B, state(n=96 * 256), 4, 96, 256, C, 256, 0) == \
+        bnbx.BNBX_E_UNSUPPORTED                                                        # N % 64
+    assert status_of(f, A, 128, B, state(n=128 * 250), 4, 128, 250, C, 256, 0) == \
+        bnbx.BNBX_E_INVAL                                                              # K % 64

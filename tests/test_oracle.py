@@ -587,3 +587,28 @@ def test_f16_dequant_hand_example():
     assert deq[15] == 0x4200 and deq[0] == 0xC200 and deq[7] == 0x0000   # 3, -3, +0
     want = oracle.f32_to_f16_bits((L * np.float32(3.0)).astype(np.float32))
     assert np.array_equal(deq, np.tile(want, 4))
+
+
+def test_dx_reference_is_the_transposed_product():
+    """dX = dY . W_hat: for dY = e_n (one-hot rows) it is row n of W_hat, and
+    <dX, X> = <dY, X . W_hat^T> for any X (the adjoint identity between the
+    forward product and its input gradient), by brute-force loops."""
+    rng = np.random.default_rng(41)
+    N, K, M = 64, 128, 3
+    w = oracle.f32_to_bf16_bits(rng.standard_normal(N * K).astype(np.float32) * np.float32(0.05))
+    for qt in ("nf4", "fp4"):
+        q = oracle.quantize(w, True, quant_type=qt)
+        what = oracle.bf16_bits_to_f32(oracle.dequantize(q["packed"], q)).astype(np.float64)
+        what = what.reshape(N, K)
+        eye = np.zeros((N, N), np.uint16)
+        eye[np.arange(N), np.arange(N)] = 0x3F80
+        assert np.array_equal(oracle.dequant_matmul_dx_ref(eye, q["packed"], q, N, K), what)
+        dy = oracle.f32_to_bf16_bits(rng.standard_normal((M, N)).astype(np.float32))
+        x = oracle.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+        dx = oracle.dequant_matmul_dx_ref(dy, q["packed"], q, N, K)
+        y = oracle.dequant_matmul_ref(x, q["packed"], q, N, K)
+        dyf = oracle.bf16_bits_to_f32(dy).astype(np.float64)
+        xf = oracle.bf16_bits_to_f32(x).astype(np.float64)
+        lhs = sum(dx[m, k] * xf[m, k] for m in range(M) for k in range(K))
+        rhs = sum(dyf[m, n] * y[m, n] for m in range(M) for n in range(N))
+        assert abs(lhs - rhs) <= 1e-9 * (abs(lhs) + 1)
