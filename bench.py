@@ -380,6 +380,15 @@ def main():
 
     variants = None if args.no_variants else measure_variants()
 
+    # Input gradient of the prefill layer, dX = dY . W_hat (M=2048, N=K=8192,
+    # the same NF4 double-quant weight), timed after the steps like the above.
+    gen.manual_seed(7003)
+    dyp = torch.randn(Mp, Np, generator=gen, device=dev).to(torch.bfloat16)
+    dxp = torch.empty(Mp, Kp, dtype=torch.bfloat16, device=dev)
+    dx_ms = timed_ms(lambda: T.gemm_dx(dyp, qp, out=dxp), max(2, args.steps))
+    dx_tflops = 2.0 * Mp * Np * Kp / (dx_ms * 1e-3) / 1e12
+    del dyp, dxp
+
     t_q = stage_ms(0) / 1e3
     t_d = stage_ms(1) / 1e3
     t_shape = [stage_ms(2 + s) / 1e3 for s in range(len(DECODE_SHAPES))]
@@ -466,6 +475,9 @@ def main():
                 "gemv_over_ceiling": round(gemv_gbs / read_gbs, 4),
             },
             "variants": variants,
+            "gemm_dx": {"what": "dX = dY . W_hat, M=2048 N=K=8192, NF4 double quant, bf16",
+                        "ms": round(dx_ms, 4), "tflops": round(dx_tflops, 1),
+                        "frac": round(dx_tflops / BF16_PEAK_TFLOPS, 4)},
             "stage_ms_per_step": {"quantize": round(t_q / K_ * 1e3, 3),
                                   "dequantize": round(t_d / K_ * 1e3, 3),
                                   "gemv": round(t_v / K_ * 1e3, 3),

@@ -9,7 +9,10 @@ dtype (bf16 / fp16); its section 1 credits 4-bit inference under
 ``torch.compile(fullgraph=True)``.  The op is an opaque custom op with a
 fake (shape-only) implementation, so it traces into a full graph; the
 arithmetic runs in the library's kernels (GEMV for at most 16 rows of X,
-GEMM otherwise) on the current stream.  Nothing here computes.
+GEMM otherwise) on the current stream.  Its backward is
+``torch.ops.bnbx.linear4bit_dx`` (dX = dY . W_hat, the input gradient; the
+4-bit weights are frozen, as the base layer under QLoRA in the pomoai.com
+overview, and get none).  Nothing here computes.
 """
 
 from __future__ import annotations
@@ -57,11 +60,58 @@ def _(x, packed, absmax, absmax2, absmax_mean, out_features, quant_type):
     return x.new_empty(*x.shape[:-1], out_features)
 
 
+@torch.library.custom_op("bnbx::linear4bit_dx", mutates_args=())
+def linear4bit_dx(dy: torch.Tensor, packed: torch.Tensor, absmax: torch.Tensor,
+                  absmax2: Optional[torch.Tensor], absmax_mean: Optional[torch.Tensor],
+                  in_features: int, quant_type: str) -> torch.Tensor:
+    """dX[..., K] = dY[..., N] . W_hat[N, K] in dY's dtype (N % 64 == 0)."""
+    if dy.dtype not in _DTYPES:
+        raise TypeError(f"linear4bit_dx: dy must be bfloat16 or float16, not {dy.dtype}")
+    N = dy.shape[-1]
+    dy2 = dy.reshape(-1, N)
+    if dy2.stride(-1) != 1 or dy2.stride(0) % 8 != 0 or dy2.data_ptr() % 16 != 0:
+        dy2 = dy2.contiguous()
+    M = dy2.shape[0]
+    dx = torch.empty(M, in_features, dtype=dy.dtype, device=dy.device)
+    if M > 0:
+        q = T.QuantizedWeight(n=N * in_features, shape=(N, in_features),
+                              double_quant=absmax2 is not None, packed=packed, absmax=absmax,
+                              absmax2=absmax2, absmax_mean=absmax_mean, quant_type=quant_type,
+                              dtype=dy.dtype)
+        T.gemm_dx(dy2, q, out=dx)
+    return dx.reshape(*dy.shape[:-1], in_features)
+
+
+@linear4bit_dx.register_fake
+def _(dy, packed, absmax, absmax2, absmax_mean, in_features, quant_type):
+    return dy.new_empty(*dy.shape[:-1], in_features)
+
+
+def _setup_context(ctx, inputs, output):
+    x, packed, absmax, absmax2, absmax_mean, out_features, quant_type = inputs
+    ctx.save_for_backward(packed, absmax, absmax2, absmax_mean)
+    ctx.in_features = x.shape[-1]
+    ctx.quant_type = quant_type
+
+
+def _backward(ctx, grad):
+    packed, absmax, absmax2, absmax_mean = ctx.saved_tensors
+    dx = None
+    if ctx.needs_input_grad[0]:
+        dx = torch.ops.bnbx.linear4bit_dx(grad, packed, absmax, absmax2, absmax_mean,
+                                          ctx.in_features, ctx.quant_type)
+    return dx, None, None, None, None, None, None
+
+
+linear4bit.register_autograd(_backward, setup_context=_setup_context)
+
+
 class Linear4bit(torch.nn.Module):
     """A bias-free ``nn.Linear(in_features, out_features)`` whose weight is
     held as 4-bit codes (NF4 or FP4, blocks of 64, optional double quant) and
     whose forward runs ``torch.ops.bnbx.linear4bit`` in ``compute_dtype``.
-    ``load_weight`` quantizes a bf16 [out, in] weight on the device."""
+    ``load_weight`` quantizes a bf16 [out, in] weight on the device.  The
+    input gradient (backward) needs out_features % 64 == 0."""
 
     def __init__(self, in_features: int, out_features: int, quant_type: str = "nf4",
                  double_quant: bool = True, compute_dtype: torch.dtype = torch.bfloat16,

@@ -102,3 +102,45 @@ def test_captured_graph_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, eager)
+
+
+@pytest.mark.parametrize("qt,dt", [("nf4", "bf16"), ("fp4", "f16")])
+def test_backward_against_oracle(qt, dt):
+    """x.grad of sum(g * Linear4bit(x)) is g . W_hat (the bnbx_gemm_nf4_dx
+    kernel through the op's autograd), against the oracle."""
+    N, K, M = 256, 512, 48
+    w, m = make(N, K, qt, dt, True, seed=9940)
+    ref = oracle.quantize(w, True, quant_type=qt)
+    x = dev_bf16(synth.normal_16((M, K), 1.0, 9941, dt), (M, K), dt).requires_grad_(True)
+    gb = synth.normal_16((M, N), 1.0, 9942, dt)
+    m(x).backward(dev_bf16(gb, (M, N), dt))
+    torch.cuda.synchronize()
+    got = oracle.bits_to_f32(host_bits(x.grad), dt).astype(np.float64).reshape(M, K)
+    err = oracle.rel_frobenius(got, oracle.dequant_matmul_dx_ref(gb, ref["packed"], ref, N, K, dt))
+    assert err <= TOL, err
+
+
+def test_compiled_backward_equals_eager():
+    K, H, N, M = 512, 256, 192, 40
+    _, a = make(H, K, "nf4", "bf16", seed=9950)
+    _, b = make(N, H, "nf4", "bf16", seed=9951)
+    net = TwoLayers(a, b)
+    xb = synth.normal_16((M, K), 1.0, 9952)
+    g = dev_bf16(synth.normal_16((M, N), 1.0, 9953), (M, N))
+    x1 = dev_bf16(xb, (M, K)).requires_grad_(True)
+    net(x1).backward(g)
+    x2 = dev_bf16(xb, (M, K)).requires_grad_(True)
+    torch.compile(net, fullgraph=True, backend="aot_eager")(x2).backward(g)
+    torch.cuda.synchronize()
+    assert torch.equal(x1.grad, x2.grad)
+
+
+def test_opcheck_with_grad():
+    N, K = 128, 256
+    _, m = make(N, K, "nf4", "bf16", dq=True, seed=9960)
+    x = dev_bf16(synth.normal_16((3, K), 1.0, 9961), (3, K)).requires_grad_(True)
+    torch.library.opcheck(torch.ops.bnbx.linear4bit.default,
+                          (x, m.packed, m.absmax, m.absmax2, m.absmax_mean, N, "nf4"))
+    dy = dev_bf16(synth.normal_16((3, N), 1.0, 9962), (3, N))
+    torch.library.opcheck(torch.ops.bnbx.linear4bit_dx.default,
+                          (dy, m.packed, m.absmax, m.absmax2, m.absmax_mean, K, "nf4"))

@@ -50,3 +50,20 @@ def test_argument_checks():
     with pytest.raises(ValueError):
         m.load_weight(torch.empty(32, 64, dtype=torch.bfloat16, device="meta"))
     assert "quant_type=nf4" in repr(m)
+
+
+def test_backward_op_fake_shapes():
+    assert hasattr(torch.ops.bnbx, "linear4bit_dx")
+    dy = torch.empty(2, 3, 64, dtype=torch.bfloat16, device="meta")
+    p = torch.empty(64 * 128 // 2, dtype=torch.uint8, device="meta")
+    a = torch.empty(64 * 128 // 64, dtype=torch.float32, device="meta")
+    dx = torch.ops.bnbx.linear4bit_dx(dy, p, a, None, None, 128, "nf4")
+    assert dx.shape == (2, 3, 128)
+
+
+def test_autograd_shapes_on_meta():
+    m = Linear4bit(128, 64, device="meta")
+    x = torch.empty(5, 128, dtype=torch.bfloat16, device="meta", requires_grad=True)
+    y = m(x)
+    (g,) = torch.autograd.grad(y, x, torch.empty_like(y))
+    assert g.shape == x.shape and g.dtype == x.dtype
