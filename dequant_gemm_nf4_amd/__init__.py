@@ -93,6 +93,13 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(path):
         raise BnbxLibraryMissing(
             f"{path} is not built; run `python -m dequant_gemm_nf4_amd.build` (no fallback exists)")
+    # torch loads its own HIP runtime; loading the library before torch has
+    # done so bound it to another runtime instance whose launches then failed
+    # on torch's memory.  Importing torch first makes both use one runtime.
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # pragma: no cover
+        pass
     L = ctypes.CDLL(path)
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     sp = ctypes.POINTER(Nf4State)
