@@ -93,9 +93,9 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(path):
         raise BnbxLibraryMissing(
             f"{path} is not built; run `python -m dequant_gemm_nf4_amd.build` (no fallback exists)")
-    # torch loads its own HIP runtime; loading the library before torch has
-    # done so bound it to another runtime instance whose launches then failed
-    # on torch's memory.  Importing torch first makes both use one runtime.
+    # Loaded before torch had initialized HIP, the library's launches on
+    # torch's memory failed (most likely two HIP runtime instances: torch
+    # bundles its own).  Importing torch first avoided it in every run.
     try:
         import torch  # noqa: F401
     except ImportError:  # pragma: no cover
