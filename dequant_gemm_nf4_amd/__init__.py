@@ -23,7 +23,7 @@ __all__ = [
     "bnbx_status_str", "bnbx_nf4_codebook", "bnbx_fp4_codebook",
     "bnbx_quantize_nf4_workspace_bytes",
     "bnbx_quantize_nf4", "bnbx_dequantize_nf4", "bnbx_gemv_nf4",
-    "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4", "bnbx_gemm_nf4_dx",
+    "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4", "bnbx_gemm_nf4_dx", "bnbx_gemm_nf4_lora",
     "bnbx_probe_stream_read", "BNBX_PROBE_SINK_WORDS", "EXPORTED_SYMBOLS", "BNBX_QUANT_NF4", "BNBX_QUANT_FP4",
     "BNBX_DTYPE_BF16", "BNBX_DTYPE_F16",
 ]
@@ -44,7 +44,7 @@ EXPORTED_SYMBOLS = (
     "bnbx_status_str", "bnbx_nf4_codebook", "bnbx_fp4_codebook",
     "bnbx_quantize_nf4_workspace_bytes",
     "bnbx_quantize_nf4", "bnbx_dequantize_nf4", "bnbx_gemv_nf4",
-    "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4", "bnbx_gemm_nf4_dx",
+    "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4", "bnbx_gemm_nf4_dx", "bnbx_gemm_nf4_lora",
     "bnbx_probe_stream_read",          # include/bnbx_probe.h (measurement aid)
 )
 BNBX_PROBE_SINK_WORDS = 1024
@@ -121,6 +121,9 @@ def lib() -> ctypes.CDLL:
     L.bnbx_gemm_nf4_workspace_bytes.restype = sz
     L.bnbx_gemm_nf4.argtypes = [vp, i64, vp, sp, i32, i32, i32, vp, i64, vp, sz, vp]
     L.bnbx_gemm_nf4.restype = i32
+    L.bnbx_gemm_nf4_lora.argtypes = [vp, i64, vp, sp, i32, i32, i32, vp, i64, vp, i64, i32, vp,
+                                     i64, vp]
+    L.bnbx_gemm_nf4_lora.restype = i32
     L.bnbx_gemm_nf4_dx.argtypes = [vp, i64, vp, sp, i32, i32, i32, vp, i64, vp]
     L.bnbx_gemm_nf4_dx.restype = i32
     L.bnbx_probe_stream_read.argtypes = [vp, sz, vp, sz, vp, vp]
@@ -203,6 +206,14 @@ def bnbx_gemm_nf4(x, ldx: int, packed, state: Nf4State, M: int, N: int, K: int, 
     _check(lib().bnbx_gemm_nf4(_ptr(x), int(ldx), _ptr(packed), ctypes.byref(state), int(M),
                                int(N), int(K), _ptr(y), int(ldy), _ptr(workspace),
                                int(workspace_bytes), _stream(stream)), "bnbx_gemm_nf4")
+
+
+def bnbx_gemm_nf4_lora(x, ldx: int, packed, state: Nf4State, M: int, N: int, K: int, xa,
+                       ldxa: int, lora_b, ldb: int, r: int, y, ldy: int, stream=None) -> None:
+    _check(lib().bnbx_gemm_nf4_lora(_ptr(x), int(ldx), _ptr(packed), ctypes.byref(state), int(M),
+                                    int(N), int(K), _ptr(xa), int(ldxa), _ptr(lora_b), int(ldb),
+                                    int(r), _ptr(y), int(ldy), _stream(stream)),
+           "bnbx_gemm_nf4_lora")
 
 
 def bnbx_gemm_nf4_dx(dy, lddy: int, packed, state: Nf4State, M: int, N: int, K: int, dx,

@@ -292,6 +292,25 @@ int bnbx_gemm_nf4(const uint16_t* x, int64_t ldx, const uint8_t* packed,
   return hip_status(e);
 }
 
+int bnbx_gemm_nf4_lora(const uint16_t* x, int64_t ldx, const uint8_t* packed,
+                       const bnbx_nf4_state* st, int M, int N, int K, const uint16_t* xa,
+                       int64_t ldxa, const uint16_t* lora_b, int64_t ldb, int r, uint16_t* y,
+                       int64_t ldy, void* stream) {
+  const int s = check_matmul(x, ldx, packed, st, M, N, K, y, ldy);
+  if (s != BNBX_OK) return s;
+  if (xa == nullptr || lora_b == nullptr) return BNBX_E_INVAL;
+  if (r < 16 || r > 256 || r % 16 != 0) return BNBX_E_INVAL;
+  if (ldxa < r || ldb < r) return BNBX_E_INVAL;
+  if (ldxa % 8 != 0 || ldb % 8 != 0) return BNBX_E_ALIGN;
+  if (!aligned(xa, 16) || !aligned(lora_b, 16)) return BNBX_E_ALIGN;
+  const hipError_t e = launch_gemm_lora(x, ldx, packed, st->absmax, st->absmax2, st->absmax_mean,
+                                        st->double_quant, st->quant_type,
+                                        st->compute_dtype == BNBX_DTYPE_F16, M, N, K, xa, ldxa,
+                                        lora_b, ldb, r, y, ldy, (hipStream_t)stream);
+  if (e == hipErrorNotSupported) return BNBX_E_UNSUPPORTED;
+  return hip_status(e);
+}
+
 int bnbx_gemm_nf4_dx(const uint16_t* dy, int64_t lddy, const uint8_t* packed,
                      const bnbx_nf4_state* st, int M, int N, int K, uint16_t* dx, int64_t lddx,
                      void* stream) {

@@ -164,12 +164,22 @@ __device__ __forceinline__ void share_tab16(const Tab16& own, Tab16* t) {
   }
 }
 
-template <bool DQ, bool Q4, bool FP4, bool F16>
+// Low-rank term added in the epilogue (LoRA: Y += XA . B^T, XA = s X A^T
+// given as [M, r], B the up-projection [N, r]); r a multiple of 16.
+struct LoraArgs {
+  const uint16_t* xa;
+  int64_t ldxa;
+  const uint16_t* b;
+  int64_t ldb;
+  int r;
+};
+
+template <bool DQ, bool Q4, bool FP4, bool F16, bool LORA>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ packed,
     const void* __restrict__ absmax, const float* __restrict__ absmax2,
     const float* __restrict__ mean, int M, int N, int K, uint16_t* __restrict__ y, int64_t ldy,
-    int tiles_m, int tiles_n, LevelTable lv) {
+    int tiles_m, int tiles_n, LevelTable lv, LoraArgs la) {
   __shared__ __attribute__((aligned(16))) uint16_t As0[kABuf], As1[kABuf];
 
   const int tid = threadIdx.x;
@@ -415,6 +425,34 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   if (kb + 2 < nkb) step(K3{}, F0{}, kb + 2, tB, tA);
   mfmas(1);   // substep 3 of the last step
 
+  if constexpr (LORA) {
+    // The low-rank term as r / 16 more MFMAs per tile, with XA rows as A and
+    // rows of B as B operands in the same lane layout as X and the weights
+    // (lane half h takes k 8h .. 8h + 8 of each 16); rows past M or N read
+    // zero through the buffer range check.
+    const rsrc_t ra = make_rsrc(la.xa, (uint32_t)((int64_t)(M - 1) * la.ldxa * 2 + la.r * 2));
+    const rsrc_t rb = make_rsrc(la.b, (uint32_t)((int64_t)(N - 1) * la.ldb * 2 + la.r * 2));
+    for (int k0 = 0; k0 < la.r; k0 += 16) {
+      u32x4_t xa[8], lb[2];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t row = m0 + 32 * i + col;
+        xa[i] = __builtin_amdgcn_raw_buffer_load_b128(
+            ra, (uint32_t)((row * la.ldxa + k0 + 8 * half) * 2), 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t n = n0 + wave * 64 + 32 * j + col;
+        lb[j] = __builtin_amdgcn_raw_buffer_load_b128(
+            rb, (uint32_t)((n * la.ldb + k0 + 8 * half) * 2), 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16<F16>(xa[i], lb[j], acc[i][j]);
+    }
+  }
+
   // D layout of a 32x32 MFMA tile: lane l, value v -> column l%32,
   // row 8*(v/4) + 4*(l/32) + v%4.
 #pragma unroll
@@ -430,37 +468,42 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     }
 }
 
-template <bool DQ, bool Q4>
+template <bool DQ, bool Q4, bool LORA>
 void launch_one(const uint16_t* x, int64_t ldx, const uint8_t* packed, const void* absmax,
                 const float* absmax2, const float* mean, int M, int N, int K, uint16_t* y,
-                int64_t ldy, int quant_type, bool f16, hipStream_t stream) {
+                int64_t ldy, int quant_type, bool f16, const LoraArgs& la, hipStream_t stream) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
   const int per_xcd = (tm * tn + kXcds - 1) / kXcds;
   const LevelTable& lv = level_table(quant_type);
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3((unsigned)(per_xcd * kXcds)), dim3(kThreads), 0, stream, x,
-                       ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, tm, tn, lv);
+                       ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, tm, tn, lv, la);
   };
   if (quant_type == kQuantFP4) {
-    if (f16) go(gemm_kernel<DQ, Q4, true, true>);
-    else go(gemm_kernel<DQ, Q4, true, false>);
+    if (f16) go(gemm_kernel<DQ, Q4, true, true, LORA>);
+    else go(gemm_kernel<DQ, Q4, true, false, LORA>);
   } else {
-    if (f16) go(gemm_kernel<DQ, Q4, false, true>);
-    else go(gemm_kernel<DQ, Q4, false, false>);
+    if (f16) go(gemm_kernel<DQ, Q4, false, true, LORA>);
+    else go(gemm_kernel<DQ, Q4, false, false, LORA>);
   }
 }
 
-}  // namespace
-
-hipError_t launch_gemm(const uint16_t* x, int64_t ldx, const uint8_t* packed, const void* absmax,
-                       const float* absmax2, const float* mean, int double_quant, int quant_type,
-                       bool f16, int M, int N, int K, uint16_t* y, int64_t ldy,
-                       hipStream_t stream) {
+// The M-slab loop of both entry points.
+template <bool LORA>
+hipError_t launch_gemm_any(const uint16_t* x, int64_t ldx, const uint8_t* packed,
+                           const void* absmax, const float* absmax2, const float* mean,
+                           int double_quant, int quant_type, bool f16, int M, int N, int K,
+                           uint16_t* y, int64_t ldy, LoraArgs la, hipStream_t stream) {
   // Buffer offsets are 32-bit: the weights and their scales must fit, and M
-  // is walked in slabs whose X rows do.
+  // is walked in slabs whose X (and XA) rows do.
   const int64_t kLimit = (int64_t)1 << 31;
   if ((int64_t)N * (K / 2) >= kLimit) return hipErrorNotSupported;
+  if (LORA && (int64_t)N * la.ldb * 2 >= kLimit) return hipErrorNotSupported;
   int64_t slab = (kLimit - (int64_t)K * 2) / (ldx * 2);
+  if (LORA) {
+    const int64_t s2 = (kLimit - (int64_t)la.r * 2) / (la.ldxa * 2);
+    slab = s2 < slab ? s2 : slab;
+  }
   slab = slab / BM * BM;
   if (slab < BM) return hipErrorNotSupported;
   const int nkb = K / 64;
@@ -472,19 +515,40 @@ hipError_t launch_gemm(const uint16_t* x, int64_t ldx, const uint8_t* packed, co
     const int m = (int)(M - r0 < slab ? M - r0 : slab);
     const uint16_t* xs = x + r0 * ldx;
     uint16_t* ys = y + r0 * ldy;
+    LoraArgs ls = la;
+    if (LORA) ls.xa = la.xa + r0 * la.ldxa;
     if (!double_quant)
-      launch_one<false, false>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys, ldy,
-                               quant_type, f16, stream);
+      launch_one<false, false, LORA>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys, ldy,
+                                     quant_type, f16, ls, stream);
     else if (q4)
-      launch_one<true, true>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys, ldy, quant_type,
-                             f16, stream);
+      launch_one<true, true, LORA>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys, ldy,
+                                   quant_type, f16, ls, stream);
     else
-      launch_one<true, false>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys, ldy,
-                              quant_type, f16, stream);
+      launch_one<true, false, LORA>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys, ldy,
+                                    quant_type, f16, ls, stream);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const uint16_t* x, int64_t ldx, const uint8_t* packed, const void* absmax,
+                       const float* absmax2, const float* mean, int double_quant, int quant_type,
+                       bool f16, int M, int N, int K, uint16_t* y, int64_t ldy,
+                       hipStream_t stream) {
+  return launch_gemm_any<false>(x, ldx, packed, absmax, absmax2, mean, double_quant, quant_type,
+                                f16, M, N, K, y, ldy, LoraArgs{nullptr, 0, nullptr, 0, 0}, stream);
+}
+
+hipError_t launch_gemm_lora(const uint16_t* x, int64_t ldx, const uint8_t* packed,
+                            const void* absmax, const float* absmax2, const float* mean,
+                            int double_quant, int quant_type, bool f16, int M, int N, int K,
+                            const uint16_t* xa, int64_t ldxa, const uint16_t* lora_b,
+                            int64_t ldb, int r, uint16_t* y, int64_t ldy, hipStream_t stream) {
+  return launch_gemm_any<true>(x, ldx, packed, absmax, absmax2, mean, double_quant, quant_type,
+                               f16, M, N, K, y, ldy, LoraArgs{xa, ldxa, lora_b, ldb, r}, stream);
 }
 
 }  // namespace bnbx

@@ -76,6 +76,12 @@ hipError_t launch_gemm(const uint16_t* x, int64_t ldx, const uint8_t* packed, co
                        const float* absmax2, const float* mean, int double_quant, int quant_type,
                        bool f16, int M, int N, int K, uint16_t* y, int64_t ldy,
                        hipStream_t stream);
+// Y = X . W_hat^T + XA . B^T (XA [M, r], B [N, r], r % 16 == 0).
+hipError_t launch_gemm_lora(const uint16_t* x, int64_t ldx, const uint8_t* packed,
+                            const void* absmax, const float* absmax2, const float* mean,
+                            int double_quant, int quant_type, bool f16, int M, int N, int K,
+                            const uint16_t* xa, int64_t ldxa, const uint16_t* lora_b,
+                            int64_t ldb, int r, uint16_t* y, int64_t ldy, hipStream_t stream);
 // dX[M, K] = dY[M, N] . W_hat[N, K]; hipErrorNotSupported unless N % 64 == 0
 // and the offsets fit 32 bits.
 hipError_t launch_gemm_dx(const uint16_t* dy, int64_t lddy, const uint8_t* packed,

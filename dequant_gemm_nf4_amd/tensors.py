@@ -8,7 +8,7 @@ import dataclasses
 
 import torch
 
-from . import (Nf4State, bnbx_dequantize_nf4, bnbx_gemm_nf4, bnbx_gemm_nf4_dx,
+from . import (Nf4State, bnbx_dequantize_nf4, bnbx_gemm_nf4, bnbx_gemm_nf4_dx, bnbx_gemm_nf4_lora,
                bnbx_gemm_nf4_workspace_bytes, bnbx_gemv_nf4, bnbx_quantize_nf4, bnbx_quantize_nf4_workspace_bytes)
 
 BLOCKSIZE = 64
@@ -122,3 +122,16 @@ def gemm_dx(dy: torch.Tensor, q: QuantizedWeight, out: torch.Tensor | None = Non
     dx = out if out is not None else torch.empty(M, K, dtype=q.dtype, device=dy.device)
     bnbx_gemm_nf4_dx(dy, dy.stride(0), q.packed, q.state, M, N, K, dx, dx.stride(0), stream)
     return dx
+
+
+def gemm_lora(x: torch.Tensor, q: QuantizedWeight, xa: torch.Tensor, lora_b: torch.Tensor,
+              out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Y = X . W_hat^T + XA . B^T for X [M, K], XA [M, r] (= s X A^T), B [N, r]."""
+    M, K = x.shape
+    N = q.shape[0]
+    r = xa.shape[1]
+    assert x.dtype == q.dtype == xa.dtype == lora_b.dtype and lora_b.shape == (N, r)
+    y = out if out is not None else torch.empty(M, N, dtype=q.dtype, device=x.device)
+    bnbx_gemm_nf4_lora(x, x.stride(0), q.packed, q.state, M, N, K, xa, xa.stride(0), lora_b,
+                       lora_b.stride(0), r, y, y.stride(0), stream)
+    return y

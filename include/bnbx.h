@@ -189,6 +189,26 @@ BNBX_API int bnbx_gemm_nf4(const uint16_t* x, int64_t ldx, const uint8_t* packed
                   uint16_t* y, int64_t ldy, void* workspace, size_t workspace_bytes,
                   void* stream);
 
+/* Prefill GEMM with a LoRA term fused into its epilogue:
+ * Y = X . W_hat^T + XA . B^T, where XA [M, r] = s . X . A^T is the
+ * adapter's down-projection already applied (and scaled) by the caller and
+ * B [N, r] its up-projection (the nn.Linear(r, N) weight).  The pomoai.com
+ * overview: QLoRA trains low-rank adapters beside the frozen 4-bit base
+ * layer.  The adapter term runs as r / 16 more matrix-core products per
+ * output tile before Y is rounded once to the compute dtype.
+ *   x, packed, st, M, N, K, y, ldy  as bnbx_gemm_nf4
+ *   xa      device, 16-bit, row m at xa + m*ldxa; ldxa >= r, ldxa % 8 == 0,
+ *           16-byte aligned
+ *   lora_b  device, 16-bit, row n at lora_b + n*ldb; ldb >= r, ldb % 8 == 0,
+ *           16-byte aligned
+ *   r       adapter rank, a multiple of 16, 16 <= r <= 256
+ * Errors: as bnbx_gemm_nf4 (BNBX_E_INVAL for r or a leading dimension out of
+ * range, BNBX_E_ALIGN for xa / lora_b alignment). */
+BNBX_API int bnbx_gemm_nf4_lora(const uint16_t* x, int64_t ldx, const uint8_t* packed,
+                       const bnbx_nf4_state* st, int M, int N, int K,
+                       const uint16_t* xa, int64_t ldxa, const uint16_t* lora_b, int64_t ldb,
+                       int r, uint16_t* y, int64_t ldy, void* stream);
+
 /* Input gradient of the 4-bit linear layer, dX[M, K] = dY[M, N] . W_hat[N, K]
  * (the weights stay frozen, as for the 4-bit base layer under QLoRA in the
  * pomoai.com overview; W_hat as in bnbx_dequantize_nf4, mlqm.cn article

@@ -52,6 +52,7 @@ from .nf4 import (  # noqa: F401
     matmul_ref,
     dequant_matmul_ref,
     dequant_matmul_dx_ref,
+    lora_matmul_ref,
     rel_frobenius,
     storage_bytes,
 )

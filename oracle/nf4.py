@@ -427,6 +427,18 @@ def dequant_matmul_dx_ref(dy_bits: np.ndarray, packed: np.ndarray, state: dict,
     return dy @ w_hat.reshape(N, K)
 
 
+def lora_matmul_ref(x_bits: np.ndarray, packed: np.ndarray, state: dict, N: int, K: int,
+                    xa_bits: np.ndarray, b_bits: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    """The 4-bit layer plus a low-rank adapter term (QLoRA, pomoai.com
+    overview: adapters trained beside the frozen 4-bit base):
+    Y = X . W_hat^T + XA . B^T with XA [M, r] (the scaled down-projection) and
+    B [N, r] (the up-projection), in binary64."""
+    r = np.asarray(b_bits).reshape(N, -1).shape[1]
+    xa = bits_to_f32(np.asarray(xa_bits).reshape(-1, r), dtype).astype(np.float64)
+    b = bits_to_f32(np.asarray(b_bits).reshape(N, r), dtype).astype(np.float64)
+    return dequant_matmul_ref(x_bits, packed, state, N, K, dtype) + xa @ b.T
+
+
 def rel_frobenius(y, y_ref) -> float:
     """||y - y_ref||_F / ||y_ref||_F in binary64."""
     y = np.asarray(y, dtype=np.float64)

@@ -30,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 11
+    assert len(declared) == 12
     assert sorted(bnbx.EXPORTED_SYMBOLS) == declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -222,3 +222,23 @@ def test_gemm_dx_rejects():
         bnbx.BNBX_E_UNSUPPORTED                                                        # N % 64
     assert status_of(f, A, 128, B, state(n=128 * 250), 4, 128, 250, C, 256, 0) == \
         bnbx.BNBX_E_INVAL                                                              # K % 64
+
+
+def test_gemm_lora_rejects():
+    st = state(n=128 * 256)
+    f = bnbx.bnbx_gemm_nf4_lora
+    D2 = D + (1 << 16)
+    ok = (A, 256, B, st, 4, 128, 256, C, 16, D2, 16, 16, D2 + 4096, 128, 0)
+    def case(i, v):
+        a = list(ok)
+        a[i] = v
+        return status_of(f, *a)
+    assert case(7, None) == bnbx.BNBX_E_INVAL        # xa
+    assert case(9, None) == bnbx.BNBX_E_INVAL        # lora_b
+    assert case(11, 8) == bnbx.BNBX_E_INVAL          # r < 16
+    assert case(11, 24) == bnbx.BNBX_E_INVAL         # r % 16
+    assert case(8, 8) == bnbx.BNBX_E_INVAL           # ldxa < r
+    assert case(10, 8) == bnbx.BNBX_E_INVAL          # ldb < r
+    assert case(8, 20) == bnbx.BNBX_E_ALIGN          # ldxa % 8
+    assert case(7, C + 8) == bnbx.BNBX_E_ALIGN       # xa alignment
+    assert case(4, 0) == bnbx.BNBX_E_INVAL           # M

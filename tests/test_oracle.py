@@ -612,3 +612,27 @@ def test_dx_reference_is_the_transposed_product():
         lhs = sum(dx[m, k] * xf[m, k] for m in range(M) for k in range(K))
         rhs = sum(dyf[m, n] * y[m, n] for m in range(M) for n in range(N))
         assert abs(lhs - rhs) <= 1e-9 * (abs(lhs) + 1)
+
+
+def test_lora_reference_adds_the_low_rank_term():
+    """Y = X . W_hat^T + XA . B^T: with B = 0 it is the plain product, and
+    with XA one-hot (row m picks rank k) the added term is column k of B,
+    checked by brute-force loops."""
+    rng = np.random.default_rng(43)
+    N, K, M, r = 32, 128, 4, 16
+    w = oracle.f32_to_bf16_bits(rng.standard_normal(N * K).astype(np.float32) * np.float32(0.05))
+    q = oracle.quantize(w, True)
+    x = oracle.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    base = oracle.dequant_matmul_ref(x, q["packed"], q, N, K)
+    zero_b = np.zeros((N, r), np.uint16)
+    xa = oracle.f32_to_bf16_bits(rng.standard_normal((M, r)).astype(np.float32))
+    assert np.array_equal(oracle.lora_matmul_ref(x, q["packed"], q, N, K, xa, zero_b), base)
+    onehot = np.zeros((M, r), np.uint16)
+    for m in range(M):
+        onehot[m, (3 * m) % r] = 0x3F80
+    b = oracle.f32_to_bf16_bits(rng.standard_normal((N, r)).astype(np.float32))
+    bf = oracle.bf16_bits_to_f32(b).astype(np.float64)
+    got = oracle.lora_matmul_ref(x, q["packed"], q, N, K, onehot, b) - base
+    for m in range(M):
+        for n in range(N):
+            assert abs(got[m, n] - bf[n, (3 * m) % r]) <= 1e-12
