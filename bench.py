@@ -389,6 +389,20 @@ def main():
     dx_tflops = 2.0 * Mp * Np * Kp / (dx_ms * 1e-3) / 1e12
     del dyp, dxp
 
+    # The GEMM with a LoRA term in its epilogue (ranks 16 and 64), same
+    # weight and X, and the plain GEMM timed the same way beside it.
+    plain_ms = timed_ms(lambda: T.gemm(xp, qp, out=yp), max(2, args.steps))
+    lora = {"plain_ms": round(plain_ms, 4)}
+    for r in (16, 64):
+        gen.manual_seed(7100 + r)
+        xa = (torch.randn(Mp, r, generator=gen, device=dev) * 0.5).to(torch.bfloat16)
+        lb = (torch.randn(Np, r, generator=gen, device=dev) * 0.05).to(torch.bfloat16)
+        ms = timed_ms(lambda: T.gemm_lora(xp, qp, xa, lb, out=yp), max(2, args.steps))
+        lora[f"r{r}"] = {"ms": round(ms, 4),
+                         "tflops": round(2.0 * Mp * Np * (Kp + r) / (ms * 1e-3) / 1e12, 1),
+                         "over_plain": round(ms / plain_ms, 4)}
+        del xa, lb
+
     t_q = stage_ms(0) / 1e3
     t_d = stage_ms(1) / 1e3
     t_shape = [stage_ms(2 + s) / 1e3 for s in range(len(DECODE_SHAPES))]
@@ -475,6 +489,7 @@ def main():
                 "gemv_over_ceiling": round(gemv_gbs / read_gbs, 4),
             },
             "variants": variants,
+            "gemm_lora": lora,
             "gemm_dx": {"what": "dX = dY . W_hat, M=2048 N=K=8192, NF4 double quant, bf16",
                         "ms": round(dx_ms, 4), "tflops": round(dx_tflops, 1),
                         "frac": round(dx_tflops / BF16_PEAK_TFLOPS, 4)},
