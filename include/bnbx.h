@@ -219,8 +219,8 @@ BNBX_API int bnbx_gemm_nf4_lora(const uint16_t* x, int64_t ldx, const uint8_t* p
  *           16-byte aligned
  *   packed  device, the quantized [N, K] weight (st->n == N*K), 16-byte aligned
  *   dx      device, 16-bit, row m at dx + m*lddx; lddx >= K, written
- * K must be a multiple of 64 and N a multiple of 64 (else
- * BNBX_E_UNSUPPORTED), M >= 1.
+ * M >= 1; K must be a multiple of 64 (else BNBX_E_INVAL) and N a multiple
+ * of 64 (else BNBX_E_UNSUPPORTED: the kernel takes whole 64-row steps).
  * Errors: BNBX_E_INVAL (sizes, null), BNBX_E_ALIGN, BNBX_E_UNSUPPORTED. */
 BNBX_API int bnbx_gemm_nf4_dx(const uint16_t* dy, int64_t lddy, const uint8_t* packed,
                      const bnbx_nf4_state* st, int M, int N, int K,
