@@ -99,8 +99,8 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(
   {
     const int lvl = level_lanes(lv);
     for (int e = tid; e < kCopies * 256; e += kThreads) {
-      const uint32_t bb = (uint32_t)e >> 3;
-      tabs[bb][e & (kCopies - 1)] =
+      const uint32_t bb = (uint32_t)e / kCopies;
+      tabs[bb][e % kCopies] =
           make_float2(level_lookup(lvl, bb >> 4), level_lookup(lvl, bb & 15u));
     }
   }
