@@ -1,0 +1,65 @@
+"""Seeded sweep of random shapes over every product entry point (GEMV, GEMM,
+GEMM with a LoRA term, dX), quant type, compute dtype and double quant,
+against the oracle: relative Frobenius error <= 5e-3.  The shapes (fixed by
+the seed) are ragged in M, N and K within each entry point's limits."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from dequant_gemm_nf4_amd import tensors as T
+from tests.gpu_helpers import dev_bf16, host_bits, upload_state
+
+pytestmark = pytest.mark.gpu
+
+TOL = 5e-3
+
+
+def cases(n=32, seed=20261203):
+    rng = np.random.default_rng(seed)
+    out = []
+    kinds = ["gemv", "gemm", "lora", "dx"]
+    for i in range(n):
+        kind = kinds[i % 4]
+        qt = ["nf4", "fp4"][rng.integers(2)]
+        dt = ["bf16", "f16"][rng.integers(2)]
+        dq = bool(rng.integers(2))
+        K = 64 * int(rng.integers(1, 41))
+        if kind == "gemv":
+            M = int(rng.integers(1, 17))
+        else:
+            M = int(rng.integers(1, 601))
+        N = 64 * int(rng.integers(1, 11)) if kind == "dx" else int(rng.integers(1, 701))
+        r = 16 * int(rng.integers(1, 5))
+        out.append((i, kind, qt, dt, dq, M, N, K, r))
+    return out
+
+
+@pytest.mark.parametrize("i,kind,qt,dt,dq,M,N,K,r", cases())
+def test_random_shape(i, kind, qt, dt, dq, M, N, K, r):
+    w = synth.normal_bf16((N, K), 0.03, 12000 + i)
+    ref = oracle.quantize(w, dq, quant_type=qt)
+    q = upload_state(ref, (N, K), dt)
+    if kind == "dx":
+        dy = synth.normal_16((M, N), 1.0, 12100 + i, dt)
+        got = T.gemm_dx(dev_bf16(dy, (M, N), dt), q)
+        want = oracle.dequant_matmul_dx_ref(dy, ref["packed"], ref, N, K, dt)
+        shape = (M, K)
+    else:
+        x = synth.normal_16((M, K), 1.0, 12200 + i, dt)
+        xd = dev_bf16(x, (M, K), dt)
+        if kind == "lora":
+            xa = synth.normal_16((M, r), 0.5, 12300 + i, dt)
+            b = synth.normal_16((N, r), 0.05, 12400 + i, dt)
+            got = T.gemm_lora(xd, q, dev_bf16(xa, (M, r), dt), dev_bf16(b, (N, r), dt))
+            want = oracle.lora_matmul_ref(x, ref["packed"], ref, N, K, xa, b, dt)
+        else:
+            got = (T.gemv if kind == "gemv" else T.gemm)(xd, q)
+            want = oracle.dequant_matmul_ref(x, ref["packed"], ref, N, K, dt)
+        shape = (M, N)
+    torch.cuda.synchronize()
+    y = oracle.bits_to_f32(host_bits(got), dt).astype(np.float64).reshape(shape)
+    err = oracle.rel_frobenius(y, want)
+    assert err <= TOL, (kind, qt, dt, dq, M, N, K, err)
