@@ -63,3 +63,28 @@ def test_random_shape(i, kind, qt, dt, dq, M, N, K, r):
     y = oracle.bits_to_f32(host_bits(got), dt).astype(np.float64).reshape(shape)
     err = oracle.rel_frobenius(y, want)
     assert err <= TOL, (kind, qt, dt, dq, M, N, K, err)
+
+
+def qcases(n=16, seed=20261204):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        size = 2 * int(rng.integers(1, 150001))
+        sigma = float(10.0 ** rng.uniform(-4, 2))
+        out.append((i, size, sigma, ["nf4", "fp4"][i % 2], bool((i // 2) % 2),
+                    ["bf16", "f16"][(i // 4) % 2]))
+    return out
+
+
+@pytest.mark.parametrize("i,size,sigma,qt,dq,dt", qcases())
+def test_random_size_quantize_dequantize_bit_exact(i, size, sigma, qt, dq, dt):
+    """Quantize on the GPU equals the oracle's codes and scales, and the GPU
+    dequantize of the oracle's state equals the oracle's, bit for bit."""
+    from tests.gpu_helpers import assert_state_equal, gpu_quantize
+    bits = synth.normal_bf16((size,), sigma, 13000 + i)
+    ref = oracle.quantize(bits, dq, quant_type=qt)
+    got = gpu_quantize(bits, (size,), dq, quant_type=qt, dtype=dt)
+    assert_state_equal(got, ref)
+    q = upload_state(ref, (size,), dt)
+    out = host_bits(T.dequantize(q))
+    assert np.array_equal(out, oracle.dequantize(ref["packed"], ref, dtype=dt))
