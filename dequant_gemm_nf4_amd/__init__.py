@@ -19,7 +19,7 @@ import os
 
 __all__ = [
     "BNBX_OK", "BNBX_E_INVAL", "BNBX_E_ALIGN", "BNBX_E_UNSUPPORTED", "BNBX_E_WORKSPACE",
-    "BNBX_E_HIP", "BnbxError", "BnbxLibraryMissing", "Nf4State", "library_path", "lib",
+    "BNBX_E_HIP", "BNBX_E_INTERNAL", "BnbxError", "BnbxLibraryMissing", "Nf4State", "library_path", "lib",
     "bnbx_status_str", "bnbx_nf4_codebook", "bnbx_fp4_codebook",
     "bnbx_quantize_nf4_workspace_bytes",
     "bnbx_quantize_nf4", "bnbx_dequantize_nf4", "bnbx_gemv_nf4",
@@ -34,6 +34,7 @@ BNBX_E_ALIGN = -2
 BNBX_E_UNSUPPORTED = -3
 BNBX_E_WORKSPACE = -4
 BNBX_E_HIP = -5
+BNBX_E_INTERNAL = -6
 
 BNBX_QUANT_NF4 = 0
 BNBX_QUANT_FP4 = 1

@@ -1,8 +1,6 @@
 // C entry points of libbnbx (declared in include/bnbx.h): argument checks on
 // the host, the one-time codebook and encode tables, and kernel launches.
 #include <math.h>
-#include <stdio.h>
-#include <stdlib.h>
 
 #include <algorithm>
 #include <mutex>
@@ -72,8 +70,10 @@ void fp4_levels(float* levels) {
 // levels by ascending value (count of them in `nl`; FP4 leaves out -0, code
 // 8, which the encoder never emits).  Thresholds: the smallest float strictly
 // above each midpoint of neighbouring levels, so the nearest level wins and
-// an exact tie takes the lower one.
-void build_encode(const float* levels, const int* order, int nl, bool in_order, EncodeTable& enc) {
+// an exact tie takes the lower one.  Returns false if the codebook does not
+// fit the bucket scheme (never for the two fixed codebooks; checked anyway,
+// and reported by every call as BNBX_E_INTERNAL).
+bool build_encode(const float* levels, const int* order, int nl, bool in_order, EncodeTable& enc) {
   float thr[15];
   for (int i = 0; i + 1 < nl; ++i) {
     const double mid = ((double)levels[order[i]] + (double)levels[order[i + 1]]) * 0.5;
@@ -92,17 +92,11 @@ void build_encode(const float* levels, const int* order, int nl, bool in_order, 
     int count = 0;
     for (int i = 0; i + 1 < nl; ++i) {
       const double th = thr[i];
-      if (fabs(th - lo) < 1e-4 || fabs(th - hi) < 1e-4) {
-        fprintf(stderr, "bnbx: codebook threshold too close to an encode bucket edge\n");
-        abort();
-      }
+      if (fabs(th - lo) < 1e-4 || fabs(th - hi) < 1e-4) return false;   // too near an edge
       if (th < lo) ++below;
       else if (th < hi) { inside = thr[i]; ++count; }
     }
-    if (count > 1) {
-      fprintf(stderr, "bnbx: two codebook thresholds in one encode bucket\n");
-      abort();
-    }
+    if (count > 1) return false;   // two thresholds in one bucket
     enc.thr[b] = inside;
     if (in_order) {
       enc.base[b] = below;
@@ -112,11 +106,10 @@ void build_encode(const float* levels, const int* order, int nl, bool in_order, 
       enc.base[b] = c0 | (c1 << 4);
     }
   }
-  enc.code_min = (uint32_t)order[0];
-  enc.code_max = (uint32_t)order[nl - 1];
+  return true;
 }
 
-void build_tables(int quant_type, Tables& t) {
+bool build_tables(int quant_type, Tables& t) {
   int order[16];
   int nl = 0;
   if (quant_type == kQuantNF4) {
@@ -128,19 +121,27 @@ void build_tables(int quant_type, Tables& t) {
       if (c != 8) order[nl++] = c;
     std::sort(order, order + nl, [&](int a, int b) { return t.levels[a] < t.levels[b]; });
   }
-  build_encode(t.levels, order, nl, quant_type == kQuantNF4, t.enc);
   for (int i = 0; i < 16; ++i) t.lv.level[i] = t.levels[i];
+  return build_encode(t.levels, order, nl, quant_type == kQuantNF4, t.enc);
 }
 
-const Tables& tables(int quant_type) {
-  static Tables t[2];
+struct AllTables {
+  Tables t[2];
+  bool ok;
+};
+
+const AllTables& all_tables() {
+  static AllTables a;
   static std::once_flag once;
   std::call_once(once, [] {
-    build_tables(kQuantNF4, t[0]);
-    build_tables(kQuantFP4, t[1]);
+    const bool nf4 = build_tables(kQuantNF4, a.t[0]);
+    const bool fp4 = build_tables(kQuantFP4, a.t[1]);
+    a.ok = nf4 && fp4;
   });
-  return t[quant_type == kQuantFP4 ? 1 : 0];
+  return a;
 }
+
+const Tables& tables(int quant_type) { return all_tables().t[quant_type == kQuantFP4 ? 1 : 0]; }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -148,6 +149,7 @@ int64_t nblocks(int64_t n) { return (n + kBlock - 1) / kBlock; }
 int64_t ngroups(int64_t nb) { return (nb + kGroup - 1) / kGroup; }
 
 int check_state(const bnbx_nf4_state* st) {
+  if (!all_tables().ok) return BNBX_E_INTERNAL;
   if (st == nullptr) return BNBX_E_INVAL;
   if (st->n < 2 || (st->n & 1)) return BNBX_E_INVAL;
   if (st->blocksize != kBlock) return BNBX_E_UNSUPPORTED;
@@ -177,6 +179,20 @@ int check_matmul(const uint16_t* x, int64_t ldx, const uint8_t* packed, const bn
 
 int hip_status(hipError_t e) { return e == hipSuccess ? BNBX_OK : BNBX_E_HIP; }
 
+// Double quant: quantize (slots + fp32 absmax into the workspace), then the
+// second-level quantization reading them.
+int quantize_dq(const uint16_t* w, uint8_t* packed, const bnbx_nf4_state* st, void* workspace,
+                hipStream_t hs) {
+  const int64_t n = st->n, nb = (n + kBlock - 1) / kBlock;
+  unsigned long long* slots = (unsigned long long*)workspace;
+  float* a32 = (float*)((char*)workspace + round_up(kSlotBytes, 256));
+  hipError_t e = launch_quantize(w, packed, n, a32, slots, st->quant_type, hs);
+  if (e == hipSuccess)
+    e = launch_double_quant(a32, slots, quantize_grid(n), nb, (int8_t*)st->absmax, st->absmax2,
+                            st->absmax_mean, hs);
+  return hip_status(e);
+}
+
 }  // namespace
 
 const float* levels_f32(int quant_type) { return tables(quant_type).levels; }
@@ -197,12 +213,14 @@ const char* bnbx_status_str(int status) {
     case BNBX_E_UNSUPPORTED: return "BNBX_E_UNSUPPORTED: unsupported configuration";
     case BNBX_E_WORKSPACE: return "BNBX_E_WORKSPACE: workspace missing or too small";
     case BNBX_E_HIP: return "BNBX_E_HIP: HIP runtime error at launch";
+    case BNBX_E_INTERNAL: return "BNBX_E_INTERNAL: codebook tables failed their self-check";
     default: return "BNBX: unknown status";
   }
 }
 
 int bnbx_nf4_codebook(float levels_host[16]) {
   if (levels_host == nullptr) return BNBX_E_INVAL;
+  if (!all_tables().ok) return BNBX_E_INTERNAL;
   const float* l = levels_f32(kQuantNF4);
   for (int i = 0; i < 16; ++i) levels_host[i] = l[i];
   return BNBX_OK;
@@ -210,6 +228,7 @@ int bnbx_nf4_codebook(float levels_host[16]) {
 
 int bnbx_fp4_codebook(float levels_host[16]) {
   if (levels_host == nullptr) return BNBX_E_INVAL;
+  if (!all_tables().ok) return BNBX_E_INTERNAL;
   const float* l = levels_f32(kQuantFP4);
   for (int i = 0; i < 16; ++i) levels_host[i] = l[i];
   return BNBX_OK;
@@ -235,13 +254,7 @@ int bnbx_quantize_nf4(const uint16_t* w, uint8_t* packed, const bnbx_nf4_state* 
   const size_t need = dq_workspace_bytes(nb);
   if (workspace == nullptr || workspace_bytes < need) return BNBX_E_WORKSPACE;
   if (!aligned(workspace, 256)) return BNBX_E_ALIGN;
-  unsigned long long* slots = (unsigned long long*)workspace;
-  float* a32 = (float*)((char*)workspace + round_up(kSlotBytes, 256));
-  hipError_t e = launch_quantize(w, packed, n, a32, slots, st->quant_type, hs);
-  if (e == hipSuccess)
-    e = launch_double_quant(a32, slots, quantize_grid(n), nb, (int8_t*)st->absmax, st->absmax2,
-                            st->absmax_mean, hs);
-  return hip_status(e);
+  return quantize_dq(w, packed, st, workspace, hs);
 }
 
 int bnbx_dequantize_nf4(const uint8_t* packed, const bnbx_nf4_state* st, uint16_t* out,

@@ -50,6 +50,30 @@ __device__ __forceinline__ uint16_t f32_to_16(float f) {
   return (uint16_t)(pack16x2<F16>(f, 0.0f) & 0xffffu);
 }
 
+// Double-quant block scale as the stored format defines it,
+// fl32(fl32(q * fl32(s_g / 127)) + mean), each operation rounded on its own.
+// fl32(s_g / 127) is s_g * fl32(1/127) corrected once with its exact
+// residual: that equals the correctly rounded quotient for every positive
+// binary32 except the smallest subnormals, which take the division.
+// dq_step_normal is the corrected product alone: exact for s_g >= 2^-120,
+// within one subnormal ulp below.  The GEMV kernels use it (they scale bf16
+// levels by the fp32 block scale, so their products are not bit-exact
+// anyway, and the division's registers made their larger variants spill).
+__device__ __forceinline__ float dq_step_normal(float s) {
+  constexpr float kR = 1.0f / 127.0f;
+  const float q0 = s * kR;
+  return __builtin_fmaf(__builtin_fmaf(-q0, 127.0f, s), kR, q0);
+}
+__device__ __forceinline__ float dq_step(float s) {
+  float st = dq_step_normal(s);
+  if (__builtin_expect(s < 0x1p-120f, 0)) st = s / 127.0f;
+  return st;
+}
+__device__ __forceinline__ float dq_scale(float qf, float s, float mean) {
+  const float prod = qf * dq_step(s);
+  return prod + mean;
+}
+
 // v_perm_b32: byte k of the result is byte sel[k] of the 8-byte value
 // {hi, lo} (0..3 pick lo's bytes, 4..7 hi's bytes, 0x0c gives 0).
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {

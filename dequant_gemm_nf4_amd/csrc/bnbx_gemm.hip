@@ -277,7 +277,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
       // (float)(int8)q = (float)(int32)(q << 24) * 2^-24, both steps exact
       const uint32_t t = (s.q >> (8 * byte)) << 24;
       const float qf = (float)(int32_t)t * 0x1p-24f;
-      sc = __builtin_fmaf(qf, s.s * (1.0f / 127.0f), mu);
+      sc = dq_scale(qf, s.s, mu);
     } else {
       sc = __builtin_bit_cast(float, s.q);
     }

@@ -151,10 +151,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(
 
   // Block scales of a step: 64 rows x the tile's 4 blocks, one per thread of
   // the first 256 (row tid / 4, block tid % 4).  Exactly as stored: a_b, or
-  // fl32(fl32(q * fl32(s_g / 127)) + mean), where fl32(s_g / 127) is
-  // s_g * fl32(1/127) corrected once with the exact residual (checked on every
-  // positive binary32 against the correctly rounded quotient: exact except
-  // for the 63 smallest subnormals, which take the division).
+  // fl32(fl32(q * fl32(s_g / 127)) + mean) (dq_scale).
   const uint32_t nblocks = (uint32_t)N * (uint32_t)nkb;
   const rsrc_t rq = make_rsrc(absmax, DQ ? nblocks : nblocks * 4u);
   const rsrc_t rg2 = make_rsrc(absmax2, DQ ? (nblocks + 255u) / 256u * 4u : 4u);
@@ -185,13 +182,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(
     if (!scaler) return;
     float sc;
     if (DQ) {
-      const float qf = (float)(int8_t)(uint8_t)r.q;
-      constexpr float kR = 1.0f / 127.0f;
-      const float q0 = r.s * kR;
-      float st = __builtin_fmaf(__builtin_fmaf(-q0, 127.0f, r.s), kR, q0);
-      if (__builtin_expect(r.s < 0x1p-120f, 0)) st = r.s / 127.0f;
-      const float prod = qf * st;
-      sc = prod + mu;
+      sc = dq_scale((float)(int8_t)(uint8_t)r.q, r.s, mu);
     } else {
       sc = __builtin_bit_cast(float, r.q);
     }

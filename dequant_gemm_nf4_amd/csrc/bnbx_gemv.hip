@@ -40,24 +40,12 @@
 namespace bnbx {
 namespace {
 
-#ifndef BNBX_GEMV_WAVES
-#define BNBX_GEMV_WAVES 16
-#endif
-constexpr int kWaves = BNBX_GEMV_WAVES;     // waves per workgroup
+constexpr int kWaves = 16;                  // waves per workgroup (one workgroup per CU)
 constexpr int kThreads = kWaves * 64;
 constexpr int kCopies = 32;                 // lane columns of the byte table (128 B)
 constexpr int kTabBytes = 256 * 256;        // 256 B per byte value
-#ifndef BNBX_GEMV_WG_PER_CU
-#define BNBX_GEMV_WG_PER_CU 1
-#endif
-#ifndef BNBX_GEMV_XLAZY
-#define BNBX_GEMV_XLAZY 0
-#endif
-constexpr int kWgPerCu = BNBX_GEMV_WG_PER_CU;   // workgroups resident per CU
 // X staged in LDS when MM*K*2 fits (the table takes 64 KB of the CU's 160 KB).
-constexpr int kXBytes = kWgPerCu == 1 ? 64 * 1024 : 16 * 1024;
-// Waves per SIMD that must fit at once (caps the VGPRs at 512 / this).
-constexpr int kMinWavesPerSimd = kWgPerCu * kWaves / 4 < 4 ? kWgPerCu * kWaves / 4 : 4;
+constexpr int kXBytes = 64 * 1024;
 constexpr int kMaxMM = 4;
 constexpr int kMaxRR = 4;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
@@ -102,7 +90,7 @@ enum ScaleMode { kScaleF32 = 0, kScaleDqLane = 1, kScaleDqRow = 2 };
 // MM rows of X per launch (rows >= mvalid are zero), NI chunks per lane, RR
 // rows of W per team and pass.  TW = 1 << twl waves per team.
 template <int MM, int NI, int RR, int SM, bool F16>
-__global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void gemv_kernel(
+__global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ packed,
     const void* __restrict__ absmax, const float* __restrict__ absmax2,
     const float* __restrict__ mean, int mvalid, int N, int K, uint16_t* __restrict__ y,
@@ -266,8 +254,7 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void gemv_kernel(
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
   __builtin_amdgcn_sched_barrier(0);
-  // X slice of this lane (LDS path): read up front, or at the first use of
-  // each chunk when BNBX_GEMV_XLAZY is set.
+  // X slice of this lane (LDS path), read up front.
   auto read_x = [&](int i) {
 #pragma unroll
     for (int m = 0; m < MM; ++m) {
@@ -288,7 +275,7 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void gemv_kernel(
       }
     }
   };
-  if (xlds && !BNBX_GEMV_XLAZY) {
+  if (xlds) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) read_x(i);
   }
@@ -298,23 +285,25 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void gemv_kernel(
   const uint32_t lanebyte = (uint32_t)(lane & (kCopies - 1)) << 2;
   // 4. Dequant-in-register dot products of one pass, one chunk at a time in
   //    load order, then the sums over the team and the stores.
-  auto pass = [&](int64_t rb, bool first) {
+  auto pass = [&](int64_t rb) {
     float acc[MM][RR];
 #pragma unroll
     for (int j = 0; j < RR; ++j) {
 #pragma unroll
       for (int m = 0; m < MM; ++m) acc[m][j] = 0.0f;
+      // the row's (at most two) group steps fl32(s_g / 127), once per row
+      const float step0 = rowsc ? dq_step_normal(gs0[j]) : 0.0f;
+      const float step1 = rowsc ? dq_step_normal(gs1[j]) : 0.0f;
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        if (BNBX_GEMV_XLAZY && first && j == 0 && xlds) read_x(i);
         float sc;
         if (rowsc) {
           const int qw = __builtin_amdgcn_ds_bpermute((int)((boff[i] >> 2) << 2), qd[j]);
           const int q = __builtin_amdgcn_sbfe(qw, (boff[i] & 3u) * 8u, 8);
-          const float g = boff[i] < split[j] ? gs0[j] : gs1[j];
-          sc = __builtin_fmaf((float)q, g * (1.0f / 127.0f), mu);
+          const float prod = (float)q * (boff[i] < split[j] ? step0 : step1);
+          sc = prod + mu;
         } else {
-          sc = DQ ? __builtin_fmaf((float)qv[j][i], gv[j][i] * (1.0f / 127.0f), mu) : gv[j][i];
+          sc = DQ ? (float)qv[j][i] * dq_step_normal(gv[j][i]) + mu : gv[j][i];
         }
         const uint32_t d[4] = {w[j][i].x, w[j][i].y, w[j][i].z, w[j][i].w};
         float part[MM];
@@ -368,10 +357,10 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void gemv_kernel(
   // The first pass uses the loads issued before the table build; later
   // passes (more rows than the grid holds at once) issue their own.  The
   // loop condition is the workgroup's, so its barriers are uniform.
-  pass(rb_first + (int64_t)team_l * RR, true);
+  pass(rb_first + (int64_t)team_l * RR);
   for (int64_t rb0 = rb_first + pass_rows; rb0 < N; rb0 += pass_rows) {
     issue(rb0 + (int64_t)team_l * RR);
-    pass(rb0 + (int64_t)team_l * RR, false);
+    pass(rb0 + (int64_t)team_l * RR);
   }
 }
 
@@ -524,7 +513,8 @@ __global__ __launch_bounds__(kMfWaves * 64, 1) void gemv_mfma_kernel(
       code = (int)(int8_t)st.qc[i];
       g = st.s[i];
     }
-    return __builtin_fmaf((float)code, g * (1.0f / 127.0f), mu);
+    const float prod = (float)code * dq_step_normal(g);
+    return prod + mu;
   };
 
   // The loads of the first GD groups go out first (for the decode shapes
@@ -679,12 +669,12 @@ bool make_plan(int mm, int N, int K, Plan& p) {
   const int tpw = kWaves >> best_twl;
   const int cus = cu_count();
   const int rmax = rr_max(mm, best_ni);
-  const int64_t slots = (int64_t)cus * kWgPerCu * tpw;   // teams resident at once
+  const int64_t slots = (int64_t)cus * tpw;   // teams resident at once
   int64_t rr = ((int64_t)N + slots - 1) / slots;
   if (rr < 1) rr = 1;
   if (rr > rmax) rr = rmax;
   int64_t grid = ((int64_t)N + tpw * rr - 1) / (tpw * rr);
-  if (grid > (int64_t)cus * kWgPerCu) grid = (int64_t)cus * kWgPerCu;
+  if (grid > (int64_t)cus) grid = (int64_t)cus;
   p.mm = mm;
   p.ni = best_ni;
   p.rr = (int)rr;

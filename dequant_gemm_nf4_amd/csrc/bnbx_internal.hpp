@@ -28,7 +28,6 @@ struct EncodeTable {
   // selects.  thr is +inf when the bucket holds no threshold.
   float thr[kBuckets];
   uint32_t base[kBuckets];
-  uint32_t code_min, code_max;   // codes of the lowest and highest level
 };
 
 struct LevelTable {
@@ -49,7 +48,7 @@ constexpr int kMaxQGrid = 512;
 constexpr int kSumDigits = 10;
 constexpr size_t kHistBins = 256;   // binary exponent fields of a bf16 absmax
 constexpr size_t kSlotBytes = (size_t)kMaxQGrid * kSumDigits * sizeof(unsigned long long);
-inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+constexpr size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline size_t dq_workspace_bytes(int64_t nb) {
   return round_up(kSlotBytes, 256) + round_up((size_t)nb * sizeof(float), 256);
 }

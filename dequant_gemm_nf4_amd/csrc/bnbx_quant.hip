@@ -17,8 +17,6 @@
 // exponent) in LDS, which it turns into its exact partial sum (an integer in
 // base-2^32 digits) and writes to its own workspace slot; double_quant_kernel
 // adds the slots and forms the exactly rounded mean.
-#include <float.h>
-
 #include "bnbx_device.hpp"
 #include "bnbx_internal.hpp"
 
@@ -41,8 +39,7 @@ __device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v, int ctrl_id) {
   return v > o ? v : o;
 }
 
-// Code of one normalised value x in [-1, 1] (or +-inf / NaN when the block
-// reciprocal overflowed, handled by the caller).  NF4 codes are level
+// Code of one normalised value x in [-1, 1].  NF4 codes are level
 // indices (bucket base + 1 past the threshold); FP4 picks one of the two
 // codes the bucket entry holds.
 template <bool FP4>
@@ -60,7 +57,7 @@ __device__ __forceinline__ uint32_t encode_one(float x, const unsigned char* tab
 // the wave must execute this together (DPP reduction over 8-lane groups).
 template <bool FP4>
 __device__ __forceinline__ uint32_t encode8(const uint32_t d[4], const unsigned char* tab,
-                                            uint32_t lanebase, uint32_t cmin, uint32_t cmax,
+                                            uint32_t lanebase,
                                             uint32_t& m_out, float& amax_out) {
   // |w| as bf16 bits: for non-negative floats integer order is value order.
   uint32_t m = 0;
@@ -73,9 +70,15 @@ __device__ __forceinline__ uint32_t encode8(const uint32_t d[4], const unsigned 
   m = dpp_max_u32(m, 1);
   m = dpp_max_u32(m, 2);   // now the max over this lane's 8-lane block
   const float amax = __uint_as_float(m << 16);
-  const float r = (amax == 0.0f) ? 0.0f : 1.0f / amax;
+  // A nonzero absmax below 2^-100 is scaled by 2^64 together with its
+  // weights (exact), so that its reciprocal stays finite; for any absmax
+  // above 2^-128 this gives the same x as the plain product.  Such blocks
+  // are rare, so the scaled form runs only in waves that hold one.
+  const bool tiny = amax < 0x1p-100f && amax != 0.0f;
+  const float pre = tiny ? 0x1p64f : 1.0f;
+  const float r = (amax == 0.0f) ? 0.0f : 1.0f / (amax * pre);
   uint32_t word = 0;
-  if (__builtin_expect(r <= FLT_MAX, 1)) {
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(tiny) == 0, 1)) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float x0 = bf16lo_to_f32(d[k]) * r;   // even element -> high nibble
@@ -85,14 +88,12 @@ __device__ __forceinline__ uint32_t encode8(const uint32_t d[4], const unsigned 
       word |= ((c0 << 4) | c1) << (8 * k);
     }
   } else {
-    // Reciprocal overflowed (absmax below 2^-128): x is +inf, -inf or NaN,
-    // which are at or above every threshold (+inf: the highest level) or
-    // none (the lowest level).
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float x0 = bf16lo_to_f32(d[k]) * r;
-      const float x1 = bf16hi_to_f32(d[k]) * r;
-      const uint32_t c0 = x0 > 1.0f ? cmax : cmin, c1 = x1 > 1.0f ? cmax : cmin;
+      const float x0 = (bf16lo_to_f32(d[k]) * pre) * r;
+      const float x1 = (bf16hi_to_f32(d[k]) * pre) * r;
+      const uint32_t c0 = encode_one<FP4>(x0, tab, lanebase);
+      const uint32_t c1 = encode_one<FP4>(x1, tab, lanebase);
       word |= ((c0 << 4) | c1) << (8 * k);
     }
   }
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_kernel(
       const uint32_t d[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
       uint32_t m;
       float amax;
-      const uint32_t word = encode8<FP4>(d, tab, lanebase, et.code_min, et.code_max, m, amax);
+      const uint32_t word = encode8<FP4>(d, tab, lanebase, m, amax);
       if (t0 + u < full) {   // wave-uniform
         const int64_t e = (t0 + u) * kTile + lane * 8;
         *(uint32_t*)(packed + (e >> 1)) = word;
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_kernel(
                            h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16)};
     uint32_t m;
     float amax;
-    const uint32_t word = encode8<FP4>(d, tab, lanebase, et.code_min, et.code_max, m, amax);
+    const uint32_t word = encode8<FP4>(d, tab, lanebase, m, amax);
     if (e < n) {
       const int nbytes = (int)((n - e) < 8 ? (n - e) >> 1 : 4);
       for (int k = 0; k < nbytes; ++k) packed[(e >> 1) + k] = (uint8_t)(word >> (8 * k));

@@ -52,7 +52,9 @@
  *     absmax_mean float[1]    mean = fl32(fl64(sum_b a_b) / nb), the sum exact
  *   Dequantized scale: without DQ a_b; with DQ
  *     fl32(fl32(q_b * fl32(s_g / 127)) + mean).
- *   Code of element j: x = fl32(w_j * fl32(1 / a_b)); s = #{i : x >= T_i}
+ *   Code of element j: x = fl32(w_j * fl32(1 / a_b)) (for a nonzero a_b
+ *   below 2^-100, w_j and a_b are first multiplied by 2^64, exactly, so the
+ *   reciprocal stays finite); s = #{i : x >= T_i}
  *   where T_i is the smallest float above the midpoint of the i-th and
  *   (i+1)-th smallest distinct levels (nearest level, exact ties to the lower
  *   level); c is the code of the s-th smallest level.  An all-zero block
@@ -88,7 +90,9 @@ typedef enum {
   BNBX_E_ALIGN = -2,        /* a pointer or leading dimension is misaligned    */
   BNBX_E_UNSUPPORTED = -3,  /* valid request the library does not implement    */
   BNBX_E_WORKSPACE = -4,    /* workspace missing or smaller than required      */
-  BNBX_E_HIP = -5           /* the HIP runtime reported an error at launch     */
+  BNBX_E_HIP = -5,          /* the HIP runtime reported an error at launch     */
+  BNBX_E_INTERNAL = -6      /* the library's codebook tables failed their
+                               one-time self-check (not expected to happen)    */
 } bnbx_status;
 
 /* 4-bit quant types (bnbx_nf4_state.quant_type). */

@@ -244,13 +244,24 @@ def encode(wf: np.ndarray, absmax: np.ndarray, thr: np.ndarray,
     nearest level (section 3.2).  ``order`` maps that ascending level index
     to its code (identity for NF4, ``sorted_codes("fp4")`` for FP4).  A
     block whose absmax is 0 is all zero weights and takes the zero level's
-    code for every element (reading)."""
+    code for every element (reading).
+
+    A block whose absmax is below 2^-100 is first scaled, weights and absmax
+    alike, by 2^64 (exact for binary32 values that small): without it the
+    reciprocal of an absmax at or below 2^-128 overflows to infinity, the
+    zeros of the block turn into NaN and nothing is the nearest level any
+    more.  For every absmax above 2^-128 the scaled form gives the same x as
+    the plain one (the two products are the same real number), so only the
+    blocks that used to overflow change."""
     wf = np.ascontiguousarray(wf, dtype=np.float32).ravel()
     n = wf.size
     block = np.arange(n) // blocksize
+    a32 = absmax.astype(np.float32)
+    tiny = a32 < np.float32(2.0 ** -100)
+    pre = np.where(tiny, np.float32(2.0 ** 64), np.float32(1.0)).astype(np.float32)
     with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
-        recip = (np.float32(1.0) / absmax.astype(np.float32)).astype(np.float32)
-        x = (wf * recip[block]).astype(np.float32)
+        recip = (np.float32(1.0) / (a32 * pre).astype(np.float32)).astype(np.float32)
+        x = ((wf * pre[block]).astype(np.float32) * recip[block]).astype(np.float32)
     codes = np.zeros(n, dtype=np.uint8)
     with np.errstate(invalid="ignore"):
         for t in np.asarray(thr, dtype=np.float32):

@@ -76,3 +76,31 @@ def assert_state_equal(gpu: dict, ref: dict) -> None:
     else:
         assert same_f32_bits(gpu["absmax"], ref["absmax"]), \
             f"absmax differs at {np.flatnonzero(gpu['absmax'] != ref['absmax'])[:10]}"
+
+
+def product_error(y, ref, tile: int = 32) -> float:
+    """Worst relative Frobenius error of a product against its reference over
+    the whole matrix, every row, and every tile x tile block of the output
+    (the last row and column blocks may be short): a single wrong MFMA
+    sub-tile, row group or output element shows up in its row and its tile
+    even when the matrix-wide figure hides it.  Where a row's or tile's
+    reference is all zero the absolute error is used."""
+    r = np.asarray(ref, dtype=np.float64)
+    r = r.reshape(-1, r.shape[-1])
+    d = np.asarray(y, dtype=np.float64).reshape(r.shape) - r
+
+    def ratio(num2, den2):
+        num, den = np.sqrt(num2), np.sqrt(den2)
+        return np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+
+    worst = float(ratio((d * d).sum(), (r * r).sum()))
+    worst = max(worst, float(ratio((d * d).sum(axis=1), (r * r).sum(axis=1)).max()))
+    M, N = r.shape
+    tm, tn = -(-M // tile), -(-N // tile)
+    pd = np.zeros((tm * tile, tn * tile))
+    pr = np.zeros((tm * tile, tn * tile))
+    pd[:M, :N] = d * d
+    pr[:M, :N] = r * r
+    td = pd.reshape(tm, tile, tn, tile).sum(axis=(1, 3))
+    tr = pr.reshape(tm, tile, tn, tile).sum(axis=(1, 3))
+    return max(worst, float(ratio(td, tr).max()))

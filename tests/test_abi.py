@@ -242,3 +242,4 @@ def test_gemm_lora_rejects():
     assert case(8, 20) == bnbx.BNBX_E_ALIGN          # ldxa % 8
     assert case(7, C + 8) == bnbx.BNBX_E_ALIGN       # xa alignment
     assert case(4, 0) == bnbx.BNBX_E_INVAL           # M
+

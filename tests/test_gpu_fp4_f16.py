@@ -15,7 +15,7 @@ import torch
 import oracle
 import synth
 from dequant_gemm_nf4_amd import tensors as T
-from tests.gpu_helpers import (assert_state_equal, dev_bf16, gpu_quantize, host_bits,
+from tests.gpu_helpers import (assert_state_equal, dev_bf16, gpu_quantize, host_bits, product_error,
                                upload_state)
 
 pytestmark = pytest.mark.gpu
@@ -80,8 +80,8 @@ def test_fp4_quantize_exhaustive_bf16_weights():
 
 def test_fp4_quantize_special_blocks():
     """Zero block (code 0), both bf16 neighbours of every FP4 decision
-    threshold at absmax 1, huge values, a subnormal absmax (the reciprocal
-    overflows: +inf takes the code of +1, -inf and NaN that of -1) and
+    threshold at absmax 1, huge values, a subnormal absmax (weights and absmax
+    pre-scaled by 2^64, so the codes are still the nearest levels) and
     negative zeros (code 0, never 8)."""
     L = oracle.fp4_codebook()
     order = oracle.sorted_codes("fp4")
@@ -201,7 +201,7 @@ def test_tiny(kind, qt, dt):
     w, x = synth.tiny(dt)
     M, N, K = synth.TINY_SHAPE
     ref, q = setup(w, (N, K), False, qt, dt)
-    err = oracle.rel_frobenius(run(kind, x, M, K, q, dt), ref_product(x, ref, N, K, dt))
+    err = product_error(run(kind, x, M, K, q, dt), ref_product(x, ref, N, K, dt))
     assert err <= TOL, err
 
 
@@ -212,7 +212,7 @@ def test_decode_shapes_m1(kind, s, qt, dt):
     w, x = synth.decode(s, dt)
     N, K = synth.DECODE_SHAPES[s]
     ref, q = setup(w, (N, K), True, qt, dt, check_state=(kind == "gemv"))
-    err = oracle.rel_frobenius(run(kind, x, 1, K, q, dt), ref_product(x, ref, N, K, dt))
+    err = product_error(run(kind, x, 1, K, q, dt), ref_product(x, ref, N, K, dt))
     assert err <= TOL, err
 
 
@@ -222,7 +222,7 @@ def test_batched_m16_outliers(kind, qt, dt):
     w, x = synth.batched(dt)
     M, N, K = synth.BATCHED_SHAPE
     ref, q = setup(w, (N, K), True, qt, dt)
-    err = oracle.rel_frobenius(run(kind, x, M, K, q, dt), ref_product(x, ref, N, K, dt))
+    err = product_error(run(kind, x, M, K, q, dt), ref_product(x, ref, N, K, dt))
     assert err <= TOL, err
 
 
@@ -234,7 +234,7 @@ def test_m_ragged_n(kind, M, qt, dt):
     w = synth.normal_bf16((N, K), 0.02, 9000 + M)
     x = synth.normal_16((M, K), 1.0, 9100 + M, dt)
     ref, q = setup(w, (N, K), True, qt, dt, check_state=False)
-    err = oracle.rel_frobenius(run(kind, x, M, K, q, dt), ref_product(x, ref, N, K, dt))
+    err = product_error(run(kind, x, M, K, q, dt), ref_product(x, ref, N, K, dt))
     assert err <= TOL, err
 
 
@@ -245,7 +245,7 @@ def test_gemv_more_than_four_rows(M, N, K, dq, qt, dt):
     w = synth.normal_bf16((N, K), 0.05, 9200 + K + M)
     x = synth.normal_16((M, K), 1.0, 9300 + K + M, dt)
     ref, q = setup(w, (N, K), dq, qt, dt, check_state=False)
-    err = oracle.rel_frobenius(run("gemv", x, M, K, q, dt), ref_product(x, ref, N, K, dt))
+    err = product_error(run("gemv", x, M, K, q, dt), ref_product(x, ref, N, K, dt))
     assert err <= TOL, err
 
 
@@ -258,7 +258,7 @@ def test_k_variants(kind, N, K, dq, qt, dt):
     w = synth.normal_bf16((N, K), 0.05, 9400 + K)
     x = synth.normal_16((M, K), 1.0, 9500 + K, dt)
     ref, q = setup(w, (N, K), dq, qt, dt, check_state=False)
-    err = oracle.rel_frobenius(run(kind, x, M, K, q, dt), ref_product(x, ref, N, K, dt))
+    err = product_error(run(kind, x, M, K, q, dt), ref_product(x, ref, N, K, dt))
     assert err <= TOL, err
 
 
@@ -268,23 +268,22 @@ def test_gemm_tiles_and_tails(M, N, K, qt, dt):
     w = synth.normal_bf16((N, K), 0.02, 9600 + M)
     x = synth.normal_16((M, K), 1.0, 9700 + M, dt)
     ref, q = setup(w, (N, K), True, qt, dt, check_state=False)
-    err = oracle.rel_frobenius(run("gemm", x, M, K, q, dt), ref_product(x, ref, N, K, dt))
+    err = product_error(run("gemm", x, M, K, q, dt), ref_product(x, ref, N, K, dt))
     assert err <= TOL, err
 
 
 @pytest.mark.parametrize("qt,dt", COMBOS)
-def test_prefill_full_size_sampled_rows(qt, dt):
+def test_prefill_full_size_every_row(qt, dt):
     """M=2048, N=K=8192 with double quant and outlier feature columns, as the
-    benchmark launches it; 34 sampled rows of Y checked."""
+    benchmark launches it; all of Y checked (whole matrix, every row, every
+    32x32 tile)."""
     w, x = synth.prefill(dt)
     M, N, K = synth.PREFILL_SHAPE
     ref, q = setup(w, (N, K), True, qt, dt)
     y = run("gemm", x, M, K, q, dt)
-    rows = np.sort(np.random.default_rng(32).choice(M, 32, replace=False))
-    rows = np.unique(np.concatenate([rows, [0, M - 1]]))
-    err = oracle.rel_frobenius(y[rows], ref_product(x, ref, N, K, dt, rows))
-    assert err <= TOL, err
     assert np.all(np.isfinite(y))
+    err = product_error(y, ref_product(x, ref, N, K, dt))
+    assert err <= TOL, err
 
 
 @pytest.mark.parametrize("qt,dt", COMBOS)
@@ -305,3 +304,5 @@ def test_unit_vector_picks_a_column(kind, qt, dt):
         y = run(kind, x, 1, K, q, dt)[0]
         col = what[:, k].astype(np.float64)
         assert np.all(np.abs(y - col) <= np.abs(col) * rel + 2.0 ** -24)
+        if kind == "gemm":   # operands are the dequantized weights exactly
+            assert np.array_equal(y, col), np.flatnonzero(y != col)[:8]

@@ -12,7 +12,7 @@ import torch
 import oracle
 import synth
 from dequant_gemm_nf4_amd import tensors as T
-from tests.gpu_helpers import dev_bf16, host_bits, upload_state
+from tests.gpu_helpers import dev_bf16, host_bits, upload_state, product_error
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +37,7 @@ def test_dx_shapes(M, N, K, dq, qt, dt):
     dy = synth.normal_16((M, N), 1.0, 9600 + M, dt)
     ref = oracle.quantize(w, dq, quant_type=qt)
     got = run_dx(dy, M, N, K, ref, dt)
-    err = oracle.rel_frobenius(got, oracle.dequant_matmul_dx_ref(dy, ref["packed"], ref, N, K, dt))
+    err = product_error(got, oracle.dequant_matmul_dx_ref(dy, ref["packed"], ref, N, K, dt))
     assert err <= TOL, err
 
 
@@ -58,17 +58,16 @@ def test_dx_one_hot_rows_are_weight_rows(qt, dt):
 
 
 @pytest.mark.parametrize("qt,dt", [("nf4", "bf16"), ("fp4", "f16")])
-def test_dx_prefill_shape_sampled_rows(qt, dt):
+def test_dx_prefill_shape_every_row(qt, dt):
     """M=2048, N=K=8192 (the prefill layer's input gradient), double quant:
-    the full product runs; 24 sampled rows are checked."""
+    the full product runs and all of dX is checked (whole matrix, every row,
+    every 32x32 tile)."""
     M, N, K = synth.PREFILL_SHAPE
     w, _ = synth.prefill()
     dy = synth.normal_16((M, N), 1.0, 9800, dt)
     ref = oracle.quantize(w, True, quant_type=qt)
     got = run_dx(dy, M, N, K, ref, dt)
-    rows = np.unique(np.concatenate([np.random.default_rng(33).choice(M, 22, replace=False),
-                                     [0, M - 1]]))
-    want = oracle.dequant_matmul_dx_ref(dy.reshape(M, N)[rows], ref["packed"], ref, N, K, dt)
-    err = oracle.rel_frobenius(got[rows], want)
-    assert err <= TOL, err
     assert np.all(np.isfinite(got))
+    want = oracle.dequant_matmul_dx_ref(dy.reshape(M, N), ref["packed"], ref, N, K, dt)
+    err = product_error(got, want)
+    assert err <= TOL, err

@@ -13,7 +13,7 @@ import torch
 import oracle
 import synth
 from dequant_gemm_nf4_amd import tensors as T
-from tests.gpu_helpers import assert_state_equal, dev_bf16, gpu_quantize, host_bits, upload_state
+from tests.gpu_helpers import assert_state_equal, dev_bf16, gpu_quantize, host_bits, upload_state, product_error
 
 pytestmark = pytest.mark.gpu
 
@@ -54,7 +54,7 @@ def test_tiny(kind):
     w, x = synth.tiny()
     M, N, K = synth.TINY_SHAPE
     ref, q = setup(w, (N, K), False)
-    err = oracle.rel_frobenius(run(kind, x, M, K, q), ref_product(x, ref, N, K))
+    err = product_error(run(kind, x, M, K, q), ref_product(x, ref, N, K))
     assert err <= TOL, err
 
 
@@ -64,7 +64,7 @@ def test_decode_shapes_m1(kind, s):
     w, x = synth.decode(s)
     N, K = synth.DECODE_SHAPES[s]
     ref, q = setup(w, (N, K), True)
-    err = oracle.rel_frobenius(run(kind, x, 1, K, q), ref_product(x, ref, N, K))
+    err = product_error(run(kind, x, 1, K, q), ref_product(x, ref, N, K))
     assert err <= TOL, err
 
 
@@ -73,7 +73,7 @@ def test_batched_m16_outliers(kind):
     w, x = synth.batched()
     M, N, K = synth.BATCHED_SHAPE
     ref, q = setup(w, (N, K), True)
-    err = oracle.rel_frobenius(run(kind, x, M, K, q), ref_product(x, ref, N, K))
+    err = product_error(run(kind, x, M, K, q), ref_product(x, ref, N, K))
     assert err <= TOL, err
 
 
@@ -84,7 +84,7 @@ def test_every_m_ragged_n(kind, M):
     w = synth.normal_bf16((N, K), 0.02, 7000 + M)
     x = synth.normal_bf16((M, K), 1.0, 7100 + M)
     ref, q = setup(w, (N, K), True, check_state=False)
-    err = oracle.rel_frobenius(run(kind, x, M, K, q), ref_product(x, ref, N, K))
+    err = product_error(run(kind, x, M, K, q), ref_product(x, ref, N, K))
     assert err <= TOL, err
 
 
@@ -99,7 +99,7 @@ def test_gemv_more_than_four_rows(M, N, K, dq):
     w = synth.normal_bf16((N, K), 0.05, 8000 + K + M)
     x = synth.normal_bf16((M, K), 1.0, 8100 + K + M)
     ref, q = setup(w, (N, K), dq, check_state=False)
-    err = oracle.rel_frobenius(run("gemv", x, M, K, q), ref_product(x, ref, N, K))
+    err = product_error(run("gemv", x, M, K, q), ref_product(x, ref, N, K))
     assert err <= TOL, err
 
 
@@ -111,7 +111,7 @@ def test_k_variants(kind, N, K, dq):
     w = synth.normal_bf16((N, K), 0.05, 7200 + K)
     x = synth.normal_bf16((M, K), 1.0, 7300 + K)
     ref, q = setup(w, (N, K), dq, check_state=False)
-    err = oracle.rel_frobenius(run(kind, x, M, K, q), ref_product(x, ref, N, K))
+    err = product_error(run(kind, x, M, K, q), ref_product(x, ref, N, K))
     assert err <= TOL, err
 
 
@@ -121,28 +121,32 @@ def test_gemm_tiles_and_tails(M, N, K):
     w = synth.normal_bf16((N, K), 0.02, 7400 + M)
     x = synth.normal_bf16((M, K), 1.0, 7500 + M)
     ref, q = setup(w, (N, K), True, check_state=False)
-    err = oracle.rel_frobenius(run("gemm", x, M, K, q), ref_product(x, ref, N, K))
+    err = product_error(run("gemm", x, M, K, q), ref_product(x, ref, N, K))
     assert err <= TOL, err
 
 
-def test_prefill_full_size_sampled_rows():
+def test_prefill_full_size_every_row():
     """M=2048, N=K=8192 (double quant, outlier feature columns): the full GEMM
-    runs as the benchmark launches it; 48 sampled rows of Y are checked."""
+    runs as the benchmark launches it, and all of Y is checked against the
+    oracle's binary64 product, over the whole matrix, per row and per 32x32
+    output tile."""
     w, x = synth.prefill()
     M, N, K = synth.PREFILL_SHAPE
     ref, q = setup(w, (N, K), True)
     y = run("gemm", x, M, K, q)
-    rows = np.sort(np.random.default_rng(31).choice(M, 48, replace=False))
-    rows = np.unique(np.concatenate([rows, [0, M - 1]]))
-    err = oracle.rel_frobenius(y[rows], ref_product(x, ref, N, K, rows))
-    assert err <= TOL, err
     assert np.all(np.isfinite(y))
+    err = product_error(y, ref_product(x, ref, N, K))
+    assert err <= TOL, err
 
 
 @pytest.mark.parametrize("kind", ["gemv", "gemm"])
 def test_unit_vector_picks_a_column(kind):
-    """X = e_k: Y is column k of W_hat, up to the bf16 rounding of the level
-    and of the product (elementwise relative error <= 2^-7)."""
+    """X = e_k: Y is column k of W_hat.  The GEMM's operands are the
+    dequantized weights themselves (the double-quant block scale formed
+    exactly as the stored format defines it), so its Y equals the column
+    exactly; the GEMV scales bf16 levels by the fp32 block scale, which is
+    within the bf16 rounding of the level and of the product (2^-7
+    relative)."""
     N, K = 512, 1024
     w = synth.normal_bf16((N, K), 0.02, 7600)
     ref, q = setup(w, (N, K), True, check_state=False)
@@ -153,6 +157,8 @@ def test_unit_vector_picks_a_column(kind):
         y = run(kind, x, 1, K, q)[0]
         col = what[:, k].astype(np.float64)
         assert np.all(np.abs(y - col) <= np.abs(col) * 2.0 ** -7 + 1e-30)
+        if kind == "gemm":
+            assert np.array_equal(y, col), np.flatnonzero(y != col)[:8]
 
 
 def test_gemv_equals_gemm_across_m():
@@ -163,7 +169,7 @@ def test_gemv_equals_gemm_across_m():
         x = synth.normal_bf16((M, K), 1.0, 7800 + M)
         a = run("gemv", x, M, K, q)
         b = run("gemm", x, M, K, q)
-        assert oracle.rel_frobenius(a, b) <= TOL
+        assert product_error(a, b) <= TOL
 
 
 def test_gemm_x_past_32bit_offsets_sampled_rows():
@@ -193,7 +199,7 @@ def test_gemm_x_past_32bit_offsets_sampled_rows():
     got = y_of(y.index_select(0, idx))
     del x, y
     torch.cuda.empty_cache()
-    err = oracle.rel_frobenius(got, ref_product(xs, ref, N, K))
+    err = product_error(got, ref_product(xs, ref, N, K))
     assert err <= TOL, err
 
 

@@ -99,6 +99,16 @@ def test_quantize_special_blocks():
     tiny[1::3] = -np.float32(2.0 ** -132)
     blocks.append(tiny)
     blocks.append(np.full(64, -0.0, np.float32))                             # negative zeros
+    # absmax from the smallest bf16 subnormal up past 2^-100 (the reciprocal
+    # of an absmax at or below 2^-128 would overflow without the 2^64
+    # pre-scaling): zeros keep the zero code, +-absmax the end levels
+    for e in (-133, -130, -128, -127, -126, -101, -100):
+        blk = np.zeros(64, np.float32)
+        blk[0] = np.float32(2.0 ** e)
+        blk[3] = -np.float32(2.0 ** e)
+        blk[7] = np.float32(2.0 ** e) * np.float32(0.5)
+        blk[9] = -np.float32(2.0 ** e) * np.float32(0.25)
+        blocks.append(blk)
     f = np.concatenate(blocks)
     bits = oracle.f32_to_bf16_bits(f)
     for dq in (False, True):
@@ -106,6 +116,28 @@ def test_quantize_special_blocks():
         assert np.all(ref["codes"][:64] == 7)
         assert np.array_equal(ref["codes"][64 + 1:64 + 16], np.arange(15))
         assert np.array_equal(ref["codes"][64 + 16:64 + 31], np.arange(1, 16))
+        c = ref["codes"]
+        for b in range(5, len(blocks)):
+            blk = c[64 * b:64 * b + 64]
+            wb = f[64 * b:64 * b + 64]
+            assert np.all(blk[wb == 0] == 7)
+            if b >= 6:
+                assert blk[0] == 15 and blk[3] == 0
+
+
+def test_double_quant_exact_tie_rounds_half_even():
+    """Four blocks whose absmax values are 0, 31.75, 15.9375 and 15.8125: the
+    mean is 15.875, the group scale 15.875, and fl32(fl32(+-1/16 / 15.875) *
+    127) is exactly +-1/2, which rounds half to even to 0 (half away from zero
+    would give +-1).  The GPU's int8 codes must be [-127, 127, 0, 0]."""
+    f = np.zeros(256, np.float32)
+    f[64] = 31.75
+    f[128 + 5] = -15.9375
+    f[192 + 9] = 15.8125
+    bits = oracle.f32_to_bf16_bits(f)
+    got, ref = check_quantize(bits, bits.shape, True)
+    assert ref["absmax_mean"] == np.float32(15.875)
+    assert ref["absmax"].tolist() == [-127, 127, 0, 0]
 
 
 def test_quantize_workspace_reuse_gives_same_result():

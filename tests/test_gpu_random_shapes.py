@@ -10,7 +10,7 @@ import torch
 import oracle
 import synth
 from dequant_gemm_nf4_amd import tensors as T
-from tests.gpu_helpers import dev_bf16, host_bits, upload_state
+from tests.gpu_helpers import dev_bf16, host_bits, upload_state, product_error
 
 pytestmark = pytest.mark.gpu
 
@@ -61,7 +61,7 @@ def test_random_shape(i, kind, qt, dt, dq, M, N, K, r):
         shape = (M, N)
     torch.cuda.synchronize()
     y = oracle.bits_to_f32(host_bits(got), dt).astype(np.float64).reshape(shape)
-    err = oracle.rel_frobenius(y, want)
+    err = product_error(y, want)
     assert err <= TOL, (kind, qt, dt, dq, M, N, K, err)
 
 

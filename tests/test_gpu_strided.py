@@ -10,7 +10,7 @@ import torch
 import dequant_gemm_nf4_amd as B
 import oracle
 import synth
-from tests.gpu_helpers import TORCH_DTYPE, dev_bf16, host_bits, upload_state
+from tests.gpu_helpers import TORCH_DTYPE, dev_bf16, host_bits, upload_state, product_error
 
 pytestmark = pytest.mark.gpu
 
@@ -43,7 +43,7 @@ def test_forward_strided(kind, M, qt, dt):
     yb = host_bits(y).reshape(M, ldy)
     assert np.all(yb[:, N:] == SENTINEL)
     got = oracle.bits_to_f32(yb[:, :N], dt).astype(np.float64)
-    err = oracle.rel_frobenius(got, oracle.dequant_matmul_ref(xb, ref["packed"], ref, N, K, dt))
+    err = product_error(got, oracle.dequant_matmul_ref(xb, ref["packed"], ref, N, K, dt))
     assert err <= TOL, err
 
 
@@ -64,5 +64,5 @@ def test_dx_strided(M, qt, dt):
     xb = host_bits(dx).reshape(M, lddx)
     assert np.all(xb[:, K:] == SENTINEL)
     got = oracle.bits_to_f32(xb[:, :K], dt).astype(np.float64)
-    err = oracle.rel_frobenius(got, oracle.dequant_matmul_dx_ref(dyb, ref["packed"], ref, N, K, dt))
+    err = product_error(got, oracle.dequant_matmul_dx_ref(dyb, ref["packed"], ref, N, K, dt))
     assert err <= TOL, err

@@ -10,7 +10,7 @@ import torch
 import oracle
 import synth
 from dequant_gemm_nf4_amd.torch_ops import Linear4bit
-from tests.gpu_helpers import TORCH_DTYPE, dev_bf16, host_bits
+from tests.gpu_helpers import TORCH_DTYPE, dev_bf16, host_bits, product_error
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +40,7 @@ def test_module_against_oracle(qt, dt, dq, lead):
     torch.cuda.synchronize()
     assert y.shape == (*lead, N) and y.dtype == TORCH_DTYPE[dt]
     got = oracle.bits_to_f32(host_bits(y), dt).astype(np.float64).reshape(M, N)
-    err = oracle.rel_frobenius(got, oracle.dequant_matmul_ref(xb, ref["packed"], ref, N, K, dt))
+    err = product_error(got, oracle.dequant_matmul_ref(xb, ref["packed"], ref, N, K, dt))
     assert err <= TOL, err
 
 
@@ -116,7 +116,7 @@ def test_backward_against_oracle(qt, dt):
     m(x).backward(dev_bf16(gb, (M, N), dt))
     torch.cuda.synchronize()
     got = oracle.bits_to_f32(host_bits(x.grad), dt).astype(np.float64).reshape(M, K)
-    err = oracle.rel_frobenius(got, oracle.dequant_matmul_dx_ref(gb, ref["packed"], ref, N, K, dt))
+    err = product_error(got, oracle.dequant_matmul_dx_ref(gb, ref["packed"], ref, N, K, dt))
     assert err <= TOL, err
 
 

@@ -229,6 +229,65 @@ def test_reconstruction_error_bound():
         assert np.all(np.abs(wf - deq) <= a * hmax * (1 + 2.0 ** -20) + np.abs(rec) * 2.0 ** -8)
 
 
+def test_reconstruction_error_bound_tiny_blocks():
+    """Blocks whose absmax lies anywhere from the smallest bf16 subnormal
+    (2^-133) up past 2^-100, with zeros and both signs inside: every code is
+    still the nearest level and the bound holds.  Without the 2^64
+    pre-scaling the reciprocal of an absmax at or below 2^-128 overflows and
+    a block's zeros would take code 0 (dequantized to -absmax)."""
+    L = oracle.codebook().astype(np.float64)
+    hmax = np.max(np.diff(L)) / 2
+    rng = np.random.default_rng(17)
+    blocks = []
+    for e in list(range(-133, -96)) + [-126, -127, -128]:
+        a = np.float32(2.0 ** e)
+        for mant in (1.0, 1.5, 1.9921875):
+            am = np.float32(a * np.float32(mant))
+            blk = np.zeros(64, np.float32)
+            blk[0] = am
+            blk[1] = -am
+            blk[2:40] = (rng.uniform(-1, 1, 38) * am).astype(np.float32)
+            blocks.append(blk)
+    w = oracle.f32_to_bf16_bits(np.concatenate(blocks))
+    for qt in ("nf4", "fp4"):
+        q = oracle.quantize(w, False, quant_type=qt)
+        Lq = oracle.levels_by_code(qt).astype(np.float64)
+        hq = np.max(np.diff(np.sort(np.unique(Lq)))) / 2
+        wf = oracle.bf16_bits_to_f32(w).astype(np.float64)
+        a = np.repeat(q["absmax"].astype(np.float64), 64)
+        assert np.all(a > 0)
+        rec = Lq[q["codes"]] * a
+        assert np.all(np.abs(wf - rec) <= a * hq * (1 + 2.0 ** -20))
+        zero_code = 7 if qt == "nf4" else 0
+        assert np.all(q["codes"][wf == 0] == zero_code)
+        if qt == "nf4":
+            assert hq == hmax
+
+
+def test_tiny_block_prescale_only_changes_overflowing_blocks():
+    """x = fl32(fl32(w * 2^64) * fl32(1 / (a * 2^64))) equals the plain
+    fl32(w * fl32(1 / a)) bit for bit for every bf16 absmax a in
+    (2^-128, 2^-100) (all of them) against weights spread over [-a, a]: the
+    pre-scaling only alters blocks whose plain reciprocal overflowed."""
+    bits = np.arange(0x0000, 0x8000, dtype=np.uint32).astype(np.uint16)
+    vals = oracle.bf16_bits_to_f32(bits)
+    a = vals[(vals > np.float32(2.0 ** -128)) & (vals < np.float32(2.0 ** -100))]
+    assert a.size > 3000
+    frac = np.linspace(-1.0, 1.0, 257, dtype=np.float64)
+    w = oracle.bf16_bits_to_f32(oracle.f32_to_bf16_bits(
+        (a[:, None].astype(np.float64) * frac[None, :]).astype(np.float32)))
+    with np.errstate(over="ignore"):
+        plain = (w * (np.float32(1.0) / a)[:, None]).astype(np.float32)
+        pre = np.float32(2.0 ** 64)
+        scaled = ((w * pre).astype(np.float32) *
+                  (np.float32(1.0) / (a * pre).astype(np.float32))[:, None]).astype(np.float32)
+    assert np.all(np.isfinite(plain))
+    assert np.array_equal(plain.view(np.uint32), scaled.view(np.uint32))
+    # and at 2^-128 itself the plain reciprocal overflows
+    with np.errstate(over="ignore", divide="ignore"):
+        assert np.isinf(np.float32(1.0) / np.float32(2.0 ** -128))
+
+
 def test_zero_block_and_partial_block():
     w = np.zeros(64 + 10, dtype=np.uint16)            # one zero block + a 10-wide tail
     w[64:] = oracle.f32_to_bf16_bits(np.linspace(-0.5, 0.5, 10).astype(np.float32))
@@ -291,6 +350,34 @@ def test_double_quant_bounds_and_saturation():
         slack = 4 * np.array([f32_ulp(max(abs(float(mean)), float(s[gi]), float(ai)))
                               for gi, ai in zip(g, a)])
         assert np.all(np.abs(ahat - a) <= s[g].astype(np.float64) / 254 + slack)
+
+
+def test_double_quant_exact_ties_round_half_even():
+    """Constructed scales where fl32(fl32(c_b / s_g) * 127) lands exactly on
+    k + 1/2 with k even: q takes k (ties to even), where rounding half away
+    from zero would take k + 1.  Scales [0, 2m, m + c, m - c] have mean m, so
+    c_b = -m, m, c, -c and s_g = m.  First a binary32 case (m = 1, tie at
+    32.5), then one in bf16 values (m = 15.875, c = 1/16: u = 1/2 exactly)
+    that the GPU quantize test reaches from real weights."""
+    for m, c, k in ((1.0, None, 32), (15.875, 0.0625, 0)):
+        m = np.float32(m)
+        if c is None:
+            # the binary32 c nearest (k + 1/2) / 127 whose product rounds to the tie
+            c0 = np.float32((k + 0.5) / 127.0)
+            cands = [np.array([int(c0.view(np.uint32)) + d], np.uint32).view(np.float32)[0]
+                     for d in range(-8, 9)]
+            c = next(cc for cc in cands
+                     if float(np.float32(np.float32(cc / m) * np.float32(127.0))) == k + 0.5)
+        c = np.float32(c)
+        a = np.array([0.0, 2 * m, m + c, m - c], np.float32)
+        assert float(a[2]) == float(m) + float(c) and float(a[3]) == float(m) - float(c)
+        q, s, mean = oracle.double_quant(a)
+        assert mean == m and s.tolist() == [float(m)]
+        u = np.float32(np.float32(c / m) * np.float32(127.0))
+        assert float(u) == k + 0.5
+        assert q.tolist() == [-127, 127, k, -k]
+        away = int(np.floor(float(u) + 0.5))
+        assert away == k + 1 and away != q[2]
 
 
 def test_double_quant_constant_scales():
