@@ -22,7 +22,8 @@ __all__ = [
     "BNBX_E_HIP", "BNBX_E_INTERNAL", "BnbxError", "BnbxLibraryMissing", "Nf4State", "library_path", "lib",
     "bnbx_status_str", "bnbx_nf4_codebook", "bnbx_fp4_codebook",
     "bnbx_quantize_nf4_workspace_bytes",
-    "bnbx_quantize_nf4", "bnbx_dequantize_nf4", "bnbx_gemv_nf4",
+    "bnbx_quantize_nf4", "bnbx_quantize_nf4_noalloc", "BNBX_NOALLOC_MAX_WEIGHTS",
+    "bnbx_dequantize_nf4", "bnbx_gemv_nf4",
     "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4", "bnbx_gemm_nf4_dx", "bnbx_gemm_nf4_lora",
     "bnbx_probe_stream_read", "BNBX_PROBE_SINK_WORDS", "EXPORTED_SYMBOLS", "BNBX_QUANT_NF4", "BNBX_QUANT_FP4",
     "BNBX_DTYPE_BF16", "BNBX_DTYPE_F16",
@@ -41,10 +42,12 @@ BNBX_QUANT_FP4 = 1
 BNBX_DTYPE_BF16 = 0
 BNBX_DTYPE_F16 = 1
 
+BNBX_NOALLOC_MAX_WEIGHTS = 1 << 28
+
 EXPORTED_SYMBOLS = (
     "bnbx_status_str", "bnbx_nf4_codebook", "bnbx_fp4_codebook",
     "bnbx_quantize_nf4_workspace_bytes",
-    "bnbx_quantize_nf4", "bnbx_dequantize_nf4", "bnbx_gemv_nf4",
+    "bnbx_quantize_nf4", "bnbx_quantize_nf4_noalloc", "bnbx_dequantize_nf4", "bnbx_gemv_nf4",
     "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4", "bnbx_gemm_nf4_dx", "bnbx_gemm_nf4_lora",
     "bnbx_probe_stream_read",          # include/bnbx_probe.h (measurement aid)
 )
@@ -114,6 +117,8 @@ def lib() -> ctypes.CDLL:
     L.bnbx_quantize_nf4_workspace_bytes.restype = sz
     L.bnbx_quantize_nf4.argtypes = [vp, vp, sp, vp, sz, vp]
     L.bnbx_quantize_nf4.restype = i32
+    L.bnbx_quantize_nf4_noalloc.argtypes = [vp, vp, sp, vp]
+    L.bnbx_quantize_nf4_noalloc.restype = i32
     L.bnbx_dequantize_nf4.argtypes = [vp, sp, vp, vp]
     L.bnbx_dequantize_nf4.restype = i32
     L.bnbx_gemv_nf4.argtypes = [vp, i64, vp, sp, i32, i32, i32, vp, i64, vp]
@@ -184,6 +189,11 @@ def bnbx_quantize_nf4(w, packed, state: Nf4State, workspace=None, workspace_byte
                       stream=None) -> None:
     _check(lib().bnbx_quantize_nf4(_ptr(w), _ptr(packed), ctypes.byref(state), _ptr(workspace),
                                    int(workspace_bytes), _stream(stream)), "bnbx_quantize_nf4")
+
+
+def bnbx_quantize_nf4_noalloc(w, packed, state: Nf4State, stream=None) -> None:
+    _check(lib().bnbx_quantize_nf4_noalloc(_ptr(w), _ptr(packed), ctypes.byref(state),
+                                           _stream(stream)), "bnbx_quantize_nf4_noalloc")
 
 
 def bnbx_dequantize_nf4(packed, state: Nf4State, out, stream=None) -> None:

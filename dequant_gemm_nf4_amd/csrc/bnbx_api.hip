@@ -179,6 +179,38 @@ int check_matmul(const uint16_t* x, int64_t ldx, const uint8_t* packed, const bn
 
 int hip_status(hipError_t e) { return e == hipSuccess ? BNBX_OK : BNBX_E_HIP; }
 
+// The double-quant quantize with a library-owned workspace
+// (bnbx_quantize_nf4_noalloc): a file-scope device array, one copy per GPU
+// the library runs on, held until the process ends.  Its size is the
+// workspace of BNBX_NOALLOC_MAX_WEIGHTS weights.
+constexpr size_t kNoAllocScratchBytes = (size_t)round_up(kSlotBytes, 256) +
+                                        (size_t)(BNBX_NOALLOC_MAX_WEIGHTS / kBlock) * sizeof(float);
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device.  In host code the array's
+// name is only a stand-in for the symbol, so kernels get this address instead;
+// it is looked up once per device.
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 // Double quant: quantize (slots + fp32 absmax into the workspace), then the
 // second-level quantization reading them.
 int quantize_dq(const uint16_t* w, uint8_t* packed, const bnbx_nf4_state* st, void* workspace,
@@ -255,6 +287,25 @@ int bnbx_quantize_nf4(const uint16_t* w, uint8_t* packed, const bnbx_nf4_state* 
   if (workspace == nullptr || workspace_bytes < need) return BNBX_E_WORKSPACE;
   if (!aligned(workspace, 256)) return BNBX_E_ALIGN;
   return quantize_dq(w, packed, st, workspace, hs);
+}
+
+int bnbx_quantize_nf4_noalloc(const uint16_t* w, uint8_t* packed, const bnbx_nf4_state* st,
+                              void* stream) {
+  if (w == nullptr || packed == nullptr) return BNBX_E_INVAL;
+  const int s = check_state(st);
+  if (s != BNBX_OK) return s;
+  if (!aligned(w, 16) || !aligned(packed, 16)) return BNBX_E_ALIGN;
+  hipStream_t hs = (hipStream_t)stream;
+  if (!st->double_quant)
+    return hip_status(launch_quantize(w, packed, st->n, (float*)st->absmax, nullptr,
+                                      st->quant_type, hs));
+  if (st->n > BNBX_NOALLOC_MAX_WEIGHTS) return BNBX_E_WORKSPACE;
+  static_assert(kNoAllocScratchBytes >= kSlotBytes, "scratch holds the slots");
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return BNBX_E_HIP;
+  if (dq_workspace_bytes((st->n + kBlock - 1) / kBlock) > kNoAllocScratchBytes) return BNBX_E_WORKSPACE;
+  return quantize_dq(w, packed, st, ws, hs);
 }
 
 int bnbx_dequantize_nf4(const uint8_t* packed, const bnbx_nf4_state* st, uint16_t* out,

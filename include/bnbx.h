@@ -152,6 +152,29 @@ BNBX_API size_t bnbx_quantize_nf4_workspace_bytes(int64_t n, int blocksize, int 
 BNBX_API int bnbx_quantize_nf4(const uint16_t* w, uint8_t* packed, const bnbx_nf4_state* st,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* Largest weight count bnbx_quantize_nf4_noalloc takes with double quant
+ * (2^28: every linear of a 70B-class model fits). */
+#define BNBX_NOALLOC_MAX_WEIGHTS ((int64_t)1 << 28)
+
+/* bnbx_quantize_nf4 for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the double-quant scratch (per-workgroup exact partial sums of
+ * the block scales and the fp32 block scales, the workspace
+ * bnbx_quantize_nf4 takes from its caller) lives in a fixed device array of
+ * the library instead, 16 MiB plus 40 KiB on each GPU the library runs on,
+ * held until the process ends.  The call allocates nothing: no hipMalloc, no
+ * hipFree.  Results are identical to bnbx_quantize_nf4's.
+ *   w, packed, st  as bnbx_quantize_nf4
+ * Every call on one GPU shares that GPU's array, and nothing in it needs to
+ * start at zero (each call overwrites what it reads).  Calls that overlap in
+ * time on one GPU (different streams, or different host threads) race on it
+ * and give undefined results: the caller must order them.
+ * Errors: as bnbx_quantize_nf4; BNBX_E_WORKSPACE with double quant when
+ * st->n > BNBX_NOALLOC_MAX_WEIGHTS; BNBX_E_HIP if the array's device address
+ * cannot be obtained. */
+BNBX_API int bnbx_quantize_nf4_noalloc(const uint16_t* w, uint8_t* packed,
+                                       const bnbx_nf4_state* st, void* stream);
+
 /* Dequantize to the compute dtype, bf16 or binary16 (mlqm.cn article
  * sec. 3.4, 4).
  *   packed  device, uint8[n/2], 16-byte aligned

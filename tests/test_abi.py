@@ -30,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 12
+    assert len(declared) == 13
     assert sorted(bnbx.EXPORTED_SYMBOLS) == declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -243,3 +243,40 @@ def test_gemm_lora_rejects():
     assert case(7, C + 8) == bnbx.BNBX_E_ALIGN       # xa alignment
     assert case(4, 0) == bnbx.BNBX_E_INVAL           # M
 
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_w", bnbx.BNBX_E_INVAL),
+    ("null_packed", bnbx.BNBX_E_INVAL),
+    ("odd_n", bnbx.BNBX_E_INVAL),
+    ("blocksize", bnbx.BNBX_E_UNSUPPORTED),
+    ("null_absmax2", bnbx.BNBX_E_INVAL),
+    ("misaligned_w", bnbx.BNBX_E_ALIGN),
+    ("past_max", bnbx.BNBX_E_WORKSPACE),
+])
+def test_quantize_noalloc_rejects(case, expect):
+    """The no-allocation quantize checks its arguments like bnbx_quantize_nf4
+    and rejects double-quant sizes past its fixed scratch before any launch."""
+    n = 4096
+    w, p, st = A, B, state(n)
+    if case == "null_w":
+        w = None
+    elif case == "null_packed":
+        p = None
+    elif case == "odd_n":
+        st = state(n + 1)
+    elif case == "blocksize":
+        st = state(n, blocksize=128)
+    elif case == "null_absmax2":
+        st = state(n)
+        st.absmax2 = None
+    elif case == "misaligned_w":
+        w = A + 2
+    elif case == "past_max":
+        st = state(bnbx.BNBX_NOALLOC_MAX_WEIGHTS + 2)
+    assert status_of(bnbx.bnbx_quantize_nf4_noalloc, w, p, st, 0) == expect
+
+
+def test_noalloc_limit_matches_header():
+    text = open(os.path.join(ROOT, "include", "bnbx.h")).read()
+    m = re.search(r"#define BNBX_NOALLOC_MAX_WEIGHTS \(\(int64_t\)1 << (\d+)\)", text)
+    assert m and (1 << int(m.group(1))) == bnbx.BNBX_NOALLOC_MAX_WEIGHTS
