@@ -13,7 +13,10 @@ silent the reading taken is stated at the function.  Parity status:
                          CDF round trip)
 * thresholds / encode -- pinned (brute-force nearest level in fp64, ties)
 * pack                -- pinned (hand-built bytes)
-* double quant        -- pinned (exact rational mean, bounds, saturation)
+* double quant        -- pinned (exact rational mean, bounds, saturation,
+                         constructed half-way ties)
+* dynamic 8-bit map   -- pinned (the bit layout decoded independently, the
+                         decade structure, brute-force nearest value)
 * dequant             -- pinned (absmax 1 block, bounds)
 * matmul              -- pinned (unit vector, brute-force loops; the dX
                          product by its transpose identity with the forward)
@@ -46,6 +49,9 @@ from .nf4 import (  # noqa: F401
     pack_nibbles,
     unpack_nibbles,
     double_quant,
+    DQ_MAPS,
+    dynamic_map,
+    double_quant_dynamic,
     block_scales,
     quantize,
     dequantize,

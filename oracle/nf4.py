@@ -330,18 +330,85 @@ def double_quant(absmax: np.ndarray, group: int = DQ_GROUP):
     return q, s, mean
 
 
+# --------------------------------------------------------------------------
+# Step 5b: the "dynamic" 8-bit map for the second level
+# --------------------------------------------------------------------------
+DQ_MAPS = ("linear", "dynamic")
+
+
+def dynamic_map() -> np.ndarray:
+    """The 256 values of the "dynamic" 8-bit quantization map, ascending, as
+    binary32.
+
+    The csdn.net feature page (section 1, item 5) lists quantile, linear and
+    dynamic 8-bit quantization among the library's types, and the mlqm.cn
+    article (section 3.3) quantizes the FP32 block scales a second time; no
+    page defines the dynamic map.  Reading: dynamic tree quantization as
+    published by Dettmers (8-bit approximations for parallelism in deep
+    learning, 2016; reused as the 8-bit code of block-wise quantization,
+    2021).  After the sign bit, E zero bits give a decimal exponent 10^-E, a
+    one bit ends them, and the remaining 6 - E bits index 2^(6-E) equal bins
+    of [0.1, 1], the value being the bin's midpoint:
+    |v| = 10^-E * (0.1 + 0.9 (f + 1/2) / 2^(6-E)), E = 0..6.  That gives 127
+    magnitudes of each sign; 0 and 1.0 complete the 256.  Binary64
+    arithmetic, one rounding to binary32, sorted."""
+    vals = [0.0, 1.0]
+    for e in range(7):
+        nf = 2 ** (6 - e)
+        for f in range(nf):
+            mag = 10.0 ** (-e) * (0.1 + 0.9 * (f + 0.5) / nf)
+            vals += [mag, -mag]
+    return np.array(sorted(vals), dtype=np.float64).astype(np.float32)
+
+
+def double_quant_dynamic(absmax: np.ndarray, group: int = DQ_GROUP):
+    """Second-level quantization with the dynamic map (reading, see
+    dynamic_map): the mean and the group scales as in ``double_quant``;
+    t_b = fl32(c_b / s_g) (correctly rounded division), and the code q_b is
+    the index of the map value nearest t_b, exact ties to the lower index
+    (the rule of the 4-bit codes: thresholds just above the midpoints).  A
+    group with s_g = 0 stores the index of 0.0.
+
+    Returns (q uint8[nb], s float32[ng], mu float32)."""
+    a = np.ascontiguousarray(absmax, dtype=np.float32).ravel()
+    nb = a.size
+    total = math.fsum(a.astype(np.float64).tolist())
+    mean = np.float32(total / nb)
+    centred = (a - mean).astype(np.float32)
+    ng = _blocks(nb, group)
+    padded = np.zeros(ng * group, dtype=np.float32)
+    padded[:nb] = np.abs(centred)
+    s = padded.reshape(ng, group).max(axis=1).astype(np.float32)
+    g = np.arange(nb) // group
+    dmap = dynamic_map()
+    thr = thresholds(dmap)
+    zero_index = int(np.flatnonzero(dmap == 0)[0])
+    q = np.full(nb, zero_index, dtype=np.uint8)
+    live = s[g] > 0
+    t = (centred[live] / s[g][live]).astype(np.float32)
+    q[live] = np.searchsorted(thr, t, side="right").astype(np.uint8)
+    return q, s, mean
+
+
 def block_scales(state: dict) -> np.ndarray:
     """The per-block scale the dequantizer uses, binary32.
 
-    Without double quant it is the stored a_b.  With it (reading):
-    step_g = fl32(s_g / 127), a_hat_b = fl32(fl32(q_b * step_g) + mu), each
-    operation rounded on its own (no fused multiply-add)."""
+    Without double quant it is the stored a_b.  With the linear int8 second
+    level (reading): step_g = fl32(s_g / 127), a_hat_b =
+    fl32(fl32(q_b * step_g) + mu); with the dynamic map: a_hat_b =
+    fl32(fl32(map[q_b] * s_g) + mu).  Each operation is rounded on its own
+    (no fused multiply-add)."""
     if not state["double_quant"]:
         return np.asarray(state["absmax"], dtype=np.float32)
-    q = np.asarray(state["absmax"], dtype=np.int8)
     s = np.asarray(state["absmax2"], dtype=np.float32)
     mean = np.float32(state["absmax_mean"])
     group = state.get("group", DQ_GROUP)
+    if state.get("dq_map", "linear") == "dynamic":
+        q = np.asarray(state["absmax"], dtype=np.uint8)
+        g = np.arange(q.size) // group
+        prod = (dynamic_map()[q] * s[g]).astype(np.float32)
+        return (prod + mean).astype(np.float32)
+    q = np.asarray(state["absmax"], dtype=np.int8)
     step = (s / np.float32(127.0)).astype(np.float32)
     g = np.arange(q.size) // group
     prod = (q.astype(np.float32) * step[g]).astype(np.float32)
@@ -350,7 +417,7 @@ def block_scales(state: dict) -> np.ndarray:
 
 def quantize(w_bits: np.ndarray, double_quant_on: bool,
              blocksize: int = BLOCKSIZE, group: int = DQ_GROUP,
-             quant_type: str = "nf4") -> dict:
+             quant_type: str = "nf4", dq_map: str = "linear") -> dict:
     """Blockwise 4-bit (NF4 or FP4) quantize-on-load of a bfloat16 weight
     (bit patterns).
 
@@ -377,8 +444,13 @@ def quantize(w_bits: np.ndarray, double_quant_on: bool,
         "absmax_fp32": a,
     }
     if double_quant_on:
-        q, s, mean = double_quant(a, group)
-        out.update(absmax=q, absmax2=s, absmax_mean=mean)
+        if dq_map == "dynamic":
+            q, s, mean = double_quant_dynamic(a, group)
+        elif dq_map == "linear":
+            q, s, mean = double_quant(a, group)
+        else:
+            raise ValueError(f"unknown second-level map {dq_map!r}")
+        out.update(absmax=q, absmax2=s, absmax_mean=mean, dq_map=dq_map)
     else:
         out.update(absmax=a, absmax2=None, absmax_mean=None)
     return out

@@ -389,6 +389,138 @@ def test_double_quant_constant_scales():
 
 
 # --------------------------------------------------------------------------
+# The "dynamic" 8-bit second-level map
+# --------------------------------------------------------------------------
+def decode_dynamic_bits(code: int) -> float:
+    """Value of an 8-bit dynamic-tree code read from its bit fields: bit 7
+    the sign, then E zero bits (decimal exponent 10^-E), a one bit, and
+    6 - E fraction bits f naming the midpoint of the f-th of 2^(6-E) equal
+    bins of [0.1, 1].  Seven zero bits leave no indicator: the value 0."""
+    sign = -1.0 if code & 0x80 else 1.0
+    rest = code & 0x7F
+    if rest == 0:
+        return 0.0
+    e = 7 - rest.bit_length()
+    nbits = 6 - e
+    f = rest & ((1 << nbits) - 1)
+    return sign * (10.0 ** -e) * (0.1 + 0.9 * (f + 0.5) / (1 << nbits))
+
+
+def test_dynamic_map_is_the_bit_layout():
+    """The sorted map equals the values the 256 bit patterns decode to (both
+    zero codes give 0), with 1.0 in the place of the second zero."""
+    m = oracle.dynamic_map().astype(np.float64)
+    decoded = sorted(set(float(np.float32(decode_dynamic_bits(c))) for c in range(256)) | {1.0})
+    assert len(decoded) == 256
+    assert np.array_equal(m, np.array(decoded))
+
+
+def test_dynamic_map_structure():
+    m = oracle.dynamic_map()
+    assert m.dtype == np.float32 and m.size == 256
+    assert np.all(np.diff(m.astype(np.float64)) > 0)
+    assert m[-1] == np.float32(1.0) and m[0] == np.float32(-0.99296875)
+    assert np.count_nonzero(m == 0) == 1
+    assert np.count_nonzero(m < 0) == 127 and np.count_nonzero(m > 0) == 128
+    mag = np.abs(m[m > 0].astype(np.float64))[:-1]    # without 1.0
+    for e in range(7):
+        lo, hi = 0.1 * 10.0 ** -e, 10.0 ** -e
+        d = np.sort(mag[(mag > lo) & (mag < hi)])
+        assert d.size == 2 ** (6 - e)                  # 2^(6-E) bins per decade
+        step = 0.9 * hi / 2 ** (6 - e)
+        if d.size > 1:                                 # equal bins, to binary32 rounding
+            assert np.allclose(np.diff(d), step, rtol=0, atol=4 * hi * 2.0 ** -24)
+        assert abs(d[0] - (lo + step / 2)) <= hi * 2.0 ** -24
+    assert np.array_equal(-m[:127][::-1], m[128:255])  # symmetric but for 1.0
+
+
+def test_dynamic_double_quant_hand_example():
+    q, s, mean = oracle.double_quant_dynamic(np.array([1.0, 2.0, 3.0], np.float32))
+    assert mean == np.float32(2.0) and s.tolist() == [1.0]
+    assert q.tolist() == [0, 127, 255]
+    state = {"double_quant": True, "dq_map": "dynamic", "absmax": q, "absmax2": s,
+             "absmax_mean": mean}
+    ahat = oracle.block_scales(state)
+    assert ahat.tolist() == [float(np.float32(np.float32(-0.99296875) + np.float32(2.0))), 2.0, 3.0]
+    # a group scale other than 1: each binary32 operation's exact result is a
+    # binary64 value here, so one rounding of it to binary32 is the format
+    a = np.array([0.0, 1.5, 0.8125, 0.6875, 0.703125], np.float32)
+    q, s, mean = oracle.double_quant_dynamic(a)
+    m = oracle.dynamic_map()
+    state = {"double_quant": True, "dq_map": "dynamic", "absmax": q, "absmax2": s,
+             "absmax_mean": mean}
+    ahat = oracle.block_scales(state)
+    for i in range(a.size):
+        prod = np.float32(float(m[q[i]]) * float(s[0]))
+        assert ahat[i] == np.float32(float(prod) + float(mean))
+
+
+def test_dynamic_codes_are_the_nearest_map_value():
+    """Scales [0, 2, 1 + c, 1 - c] have mean 1 and group scale 1, so the
+    normalised value of the last two is exactly +-c: their codes must be the
+    brute-force nearest map index (lowest index on a tie), for c spread over
+    every decade, on the map values and on both sides of every midpoint."""
+    m = oracle.dynamic_map().astype(np.float64)
+    mids = (m[:-1] + m[1:]) / 2
+    cs = set()
+    rng = np.random.default_rng(12)
+    for v in np.concatenate([np.abs(m), np.abs(mids), 10.0 ** rng.uniform(-7, 0, 400)]):
+        for c in (v, v * (1 + 2.0 ** -20), v * (1 - 2.0 ** -20)):
+            c = float(np.float32(c))
+            # 1 + c and 1 - c must be binary32 values for the construction
+            if 0 < c < 1 and float(np.float32(1 + c)) == 1 + c and float(np.float32(1 - c)) == 1 - c:
+                cs.add(c)
+    cs = sorted(cs)
+    assert len(cs) > 100
+    for c in cs:
+        a = np.array([0.0, 2.0, 1.0 + c, 1.0 - c], np.float32)
+        q, s, mean = oracle.double_quant_dynamic(a)
+        assert mean == 1.0 and s[0] == 1.0
+        for t, code in ((c, q[2]), (-c, q[3])):
+            dist = np.abs(m - t)
+            best = int(np.flatnonzero(dist == dist.min())[0])
+            assert code == best, (t, code, best)
+
+
+def test_dynamic_double_quant_bounds():
+    """|a_hat - a| <= s_g * (largest half gap of the map) + rounding slack;
+    a group with s_g = 0 dequantizes to the mean exactly."""
+    m = oracle.dynamic_map().astype(np.float64)
+    hmax = np.max(np.diff(m)) / 2
+    rng = np.random.default_rng(14)
+    for nb in (1, 255, 256, 257, 1000, 4096 + 3):
+        a = oracle.bf16_bits_to_f32(oracle.f32_to_bf16_bits(
+            np.abs(rng.standard_normal(nb)).astype(np.float32) * np.float32(0.06)))
+        q, s, mean = oracle.double_quant_dynamic(a)
+        g = np.arange(nb) // 256
+        state = {"double_quant": True, "dq_map": "dynamic", "absmax": q, "absmax2": s,
+                 "absmax_mean": mean}
+        ahat = oracle.block_scales(state).astype(np.float64)
+        slack = 4 * np.array([f32_ulp(max(abs(float(mean)), float(s[gi]), float(ai)))
+                              for gi, ai in zip(g, a)])
+        assert np.all(np.abs(ahat - a) <= s[g].astype(np.float64) * hmax + slack)
+    a = np.full(300, 0.25, np.float32)
+    q, s, mean = oracle.double_quant_dynamic(a)
+    assert np.all(s == 0) and np.all(oracle.dynamic_map()[q] == 0)
+    state = {"double_quant": True, "dq_map": "dynamic", "absmax": q, "absmax2": s,
+             "absmax_mean": mean}
+    assert np.all(oracle.block_scales(state) == np.float32(0.25))
+
+
+def test_dynamic_map_quantize_state():
+    w = oracle.f32_to_bf16_bits(np.random.default_rng(15).standard_normal(64 * 600)
+                                .astype(np.float32) * np.float32(0.02))
+    lin = oracle.quantize(w, True)
+    dyn = oracle.quantize(w, True, dq_map="dynamic")
+    assert np.array_equal(lin["packed"], dyn["packed"])       # codes use the true a_b
+    assert dyn["absmax"].dtype == np.uint8 and dyn["dq_map"] == "dynamic"
+    assert dyn["absmax_mean"] == lin["absmax_mean"]
+    assert np.array_equal(dyn["absmax2"], lin["absmax2"])
+    with pytest.raises(ValueError):
+        oracle.quantize(w, True, dq_map="quantile")
+
+
+# --------------------------------------------------------------------------
 # Dequant and matmul
 # --------------------------------------------------------------------------
 def test_dequant_with_unit_absmax_returns_levels():
