@@ -380,6 +380,23 @@ def main():
 
     variants = None if args.no_variants else measure_variants()
 
+    # Batched decode on the down projection, M=16 on 4096x11008 (K = 11008:
+    # three 4096-k chunks per wave), one launch per weight, over 24 distinct
+    # weights (540 MB), timed after the steps like the above.
+    Nd, Kd = 4096, 11008
+    qdown = []
+    for i in range(24):
+        gen.manual_seed(8300 + i)
+        w = (torch.randn(Nd, Kd, generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+        qdown.append(T.quantize(w, True))
+        del w
+    gen.manual_seed(8400)
+    xdown = torch.randn(Mb, Kd, generator=gen, device=dev).to(torch.bfloat16)
+    ydown = torch.empty(Mb, Nd, dtype=torch.bfloat16, device=dev)
+    down_us = timed_ms(lambda: [T.gemv(xdown, q, out=ydown) for q in qdown],
+                       max(2, args.steps)) * 1e3 / len(qdown)
+    del qdown, xdown, ydown
+
     # Input gradient of the prefill layer, dX = dY . W_hat (M=2048, N=K=8192,
     # the same NF4 double-quant weight), timed after the steps like the above.
     gen.manual_seed(7003)
@@ -478,6 +495,11 @@ def main():
                          "gbs": round(b_b / (us_b * 1e-6) / 1e9, 1),
                          "hbm_frac": round(b_b / (us_b * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                          "tflops": round(2.0 * Mb * Nb * Kb / (us_b * 1e-6) / 1e12, 2)},
+            "gemv_m16_down": {"shape": f"{Mb}x{Nd}x{Kd}", "launches_per_call": 1,
+                              "launch_us": round(down_us, 3),
+                              "gbs": round(gemv_bytes(Mb, Nd, Kd) / (down_us * 1e-6) / 1e9, 1),
+                              "hbm_frac": round(gemv_bytes(Mb, Nd, Kd) / (down_us * 1e-6) / 1e9
+                                                / HBM_PEAK_GBS, 4)},
             "read_ceiling": {
                 "what": "plain streaming read of each weight's packed bytes and block codes, "
                         "back to back over the same weights (bnbx_probe_stream_read)",

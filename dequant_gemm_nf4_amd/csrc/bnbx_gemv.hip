@@ -2,8 +2,9 @@
 // Y[M, N] = X[M, K] . W_hat[N, K]^T,
 // M <= 16 (mlqm.cn bitsandbytes article, sec. 3.4 "4-bit storage, 16-bit
 // compute", and the sec. 7 pitfall that 4-bit only pays off when the layer is
-// bound by weight traffic: so the packed weight is streamed exactly once per
-// group of up to four rows of X).
+// bound by weight traffic: so the packed weight is streamed exactly once:
+// gemv_kernel below for up to four rows of X, gemv16_kernel further down for
+// 4 < M <= 16).
 //
 // Work layout.  A row of W is C = K/32 chunks of 16 packed bytes (32
 // weights, half of one 64-block).  A row is owned by a team of TW waves
@@ -21,7 +22,11 @@
 // and for rows past N, so there is no per-load address arithmetic or bounds
 // branch.  With double quant a row's int8 codes come in one dword per lane and
 // reach the lanes that need them by ds_bpermute, and its (at most two) group
-// scales by scalar loads.  X is staged once per workgroup in LDS.
+// scales in one vector load.  Nothing the table build needs waits on a
+// memory load: the kernel issues no scalar loads from memory (the table
+// build's wait for its scalar kernel-argument loads would cover them too),
+// and the mean is loaded first so that its use waits for nothing else.  X is
+// staged once per workgroup in LDS.
 //
 // Dequant in registers.  An LDS table maps each packed byte to the level pair
 // (L[high nibble], L[low nibble]) in the compute type (bf16, or FP16 with
@@ -135,6 +140,13 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
     boff[i] = c >> 1;
   }
 
+  // 0. The mean, by lane 0 alone and before every other load: loads
+  //    complete in issue order, so its first use (broadcast with
+  //    v_readfirstlane) then waits for nothing else.
+  float mul = 0.0f;
+  if (DQ && lane == 0)
+    mul = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(mean, 4u), 0u, 0, 0));
+
   // 1. X: staging loads (LDS path) or the lane's slice directly.
   uint32_t xr[MM][NI][16];
   constexpr int kStage = kXBytes / 16 / kThreads;   // 16-byte pieces per thread (max)
@@ -183,7 +195,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
   int qv[RR][NI];
   float gv[RR][NI];
   int qd[RR];
-  float gs0[RR], gs1[RR];
+  float gsl[RR];      // the row's group scales: g0 in even lanes, g1 in odd ones
   uint32_t split[RR];
   auto issue_part = [&](int64_t rb, int lo, int hi) {
 #pragma unroll
@@ -203,8 +215,14 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
         uint32_t g0 = blk0 >> 8;
         g0 = g0 < ng ? g0 : ng - 1u;
         const uint32_t g1 = g0 + 1u < ng ? g0 + 1u : ng - 1u;
-        gs0[j] = absmax2[g0];
-        gs1[j] = absmax2[g1];
+        // Both group scales in one vector load, g0 in the even lanes and g1
+        // in the odd ones, spread to every lane by DPP where they are used.
+        // (A scalar load here would make the table build, which waits for all
+        // scalar loads, wait for a memory latency: 4.5 against 4.1 us per
+        // 4096^2 launch.  Loading them with two lanes active, or broadcasting
+        // with v_readlane, measured slower still.)
+        gsl[j] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rg, ((lane & 1) ? g1 : g0) * 4u, 0, 0));
         split[j] = 256u - (blk0 & 255u);     // blocks of the row in group g0
       } else if (DQ) {
         const rsrc_t rq = make_rsrc((const int8_t*)absmax + row * nkb, ok ? nkb : 0u);
@@ -281,19 +299,26 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
   }
 
   issue_part(rb_first + (int64_t)team_l * RR, NI, RR * NI);
-  const float mu = DQ ? *mean : 0.0f;
   const uint32_t lanebyte = (uint32_t)(lane & (kCopies - 1)) << 2;
   // 4. Dequant-in-register dot products of one pass, one chunk at a time in
   //    load order, then the sums over the team and the stores.
   auto pass = [&](int64_t rb) {
+    const float mu = DQ ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mul))) : 0.0f;
     float acc[MM][RR];
 #pragma unroll
     for (int j = 0; j < RR; ++j) {
 #pragma unroll
       for (int m = 0; m < MM; ++m) acc[m][j] = 0.0f;
       // the row's (at most two) group steps fl32(s_g / 127), once per row
-      const float step0 = rowsc ? dq_step_normal(gs0[j]) : 0.0f;
-      const float step1 = rowsc ? dq_step_normal(gs1[j]) : 0.0f;
+      // quad_perm(0,0,0,0) / (1,1,1,1): every lane takes its quad's g0 / g1
+      const float step0 =
+          rowsc ? dq_step_normal(__int_as_float(__builtin_amdgcn_update_dpp(
+                      0, __float_as_int(gsl[j]), 0x00, 0xF, 0xF, false)))
+                : 0.0f;
+      const float step1 =
+          rowsc ? dq_step_normal(__int_as_float(__builtin_amdgcn_update_dpp(
+                      0, __float_as_int(gsl[j]), 0x55, 0xF, 0xF, false)))
+                : 0.0f;
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         float sc;
@@ -365,254 +390,339 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// 4 < M <= 16: the weights streamed once into v_mfma_f32_16x16x32_bf16 (or
-// _f16 with the FP16 compute dtype).
+// 4 < M <= 16: one launch for any K; the weights are streamed once into
+// v_mfma_f32_16x16x32_bf16 (or _f16) operands.
 //
-// A workgroup of 16 waves takes groups of 16 weight rows (16 columns of Y)
-// in turn; wave w owns the K slice of blocks [w nkb / 16, (w+1) nkb / 16)
-// (BPW = 4 blocks: K = 4096) and keeps its X slice for all 16
-// rows of X in registers as MFMA A operands.  In an MFMA, lane l supplies
-// column l % 16 and eight k of the 32; the 32 k of each MFMA are one half of
-// one block, lane quarter q taking k [16q + 8h, 16q + 8h + 8) of half h, so
-// every MFMA sits inside one block.  The B operand is the bf16 levels from
-// the byte -> pair table (as in gemv_kernel, no per-weight arithmetic); a
-// block's two MFMAs go to a zeroed accumulator that is then scaled by the
-// block scale of the lane's column (its own row's) and added to the running
-// sums.  The 16 waves' partial sums meet in LDS once per round of GD row
-// groups.
+// MFMA roles: A is X (lane l: row l % 16, eight k), B is the dequantized
+// weight (lane l: weight row l % 16 of a group of 16, eight k), and lane l
+// ends with Y[4 (l / 16) + v][16 g + l % 16], v = 0..3.
 //
-// Weights and X are loaded row-contiguous (16 bytes per lane, eight lanes
-// per 128-byte line: an MFMA layout would touch 16 rows per load) and turned
-// into the MFMA layout through a 512 BPW-byte LDS region private to the
-// wave: 16-byte pieces of a row are stored at piece ^ f(row), which makes
-// the layout reads conflict-free.
+// Loads are quad-coalesced: lane x reads 16 bytes of row x / 4 at piece
+// x % 4, so the four lanes of a quad read 64 contiguous bytes and one
+// instruction covers 16 rows x 64 bytes.  (MFMA-layout loads, where
+// neighbouring lanes read different rows, made every lane its own memory
+// request; the address path then held the kernel at 17 us on 14336 x 4096.)
+// A per-wave 1 KB LDS stage turns that into the MFMA layout: lane x writes
+// its piece to slot 16 p + ((r + 4 p) mod 16) and lane (q, r) reads slot
+// 16 q + ((r + 4 q) mod 16), both bank-conflict free; lane (q, r) then holds
+// piece q of row r.  For the weights, a 4 x 4 transpose across the quarters
+// (two v_permlane32_swap, two v_permlane16_swap) then gives lane (q, r) the
+// dword q of every piece m: MFMA m covers the 32 k [128 h + 32 m, +32) of
+// the slice, half of block 2 h + m / 2, and its B operand is four byte ->
+// level-pair lookups in the LDS table of gemv_kernel.  The two MFMAs of a
+// block go to a zeroed accumulator scaled by the block scale of the lane's
+// weight row; scales are formed where they load (lane x: row x / 4, block
+// x % 4) and fetched with ds_bpermute.
+//
+// Work split.  K is cut into slices of 256 k (4 blocks); wave w of the
+// 16-wave workgroup owns slices w, w + 16, ... (one per chunk of 4096 k)
+// and keeps the X operands of its current slice in registers.  The
+// workgroup owns row groups blockIdx.x + j * gridDim.x and takes NB of them
+// at a time.  Every load is unconditional (items past the end get offsets
+// outside their buffer, which read as zero), so each wait names exactly the
+// loads it needs.  With one chunk (K <= 4096) all of a batch's loads go out
+// at once; with more, each half of the next chunk's X goes into the
+// registers of the half just multiplied, and the weights two chunks ahead
+// into the set just used.  The 16 waves' partial sums meet in LDS, two row
+// groups at a time.
 // ---------------------------------------------------------------------------
-constexpr int kMfWaves = 16;
+constexpr int k16Waves = 16;
+constexpr int k16SliceK = 256;    // k per wave slice (4 blocks)
+constexpr int k16ChunkK = k16Waves * k16SliceK;
+constexpr uint32_t kFar = 0x80000000u;   // an offset past every buffer resource
 
-template <int BPW, int GD, int SM, bool F16>
-__global__ __launch_bounds__(kMfWaves * 64, 1) void gemv_mfma_kernel(
+template <int SM, bool F16, int NB, bool MULTI>
+__global__ __launch_bounds__(k16Waves * 64, 1) void gemv16_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ packed,
     const void* __restrict__ absmax, const float* __restrict__ absmax2,
     const float* __restrict__ mean, int M, int N, int K, uint16_t* __restrict__ y, int64_t ldy,
     LevelTable lv) {
   constexpr bool DQ = SM != kScaleF32;
-  constexpr int kPieces = 2 * BPW;                 // 16-byte pieces per row of a slice
-  constexpr int kRow = 16 * kPieces;               // bytes per row of a slice
-  constexpr int kLoads = 16 * kPieces / 64;        // row-contiguous loads per 16 rows
-  constexpr int kRegion = 16 * kRow;               // bytes of a wave's region
+  constexpr int kSets = MULTI ? 2 : 1;
+  constexpr int kRed = NB < 2 ? NB : 2;   // row groups reduced at once
+  static_assert(!MULTI || NB == 1, "several chunks take one row group at a time");
   // Table at LDS offset 0 (its addresses are v_perm results), then the
-  // waves' partial sums of GD row groups (16 waves x 64 lanes x 4 values
-  // each), then the waves' transpose regions.
+  // waves' 1 KB stages, then the partial sums.
   __shared__ __attribute__((aligned(16))) unsigned char
-      smem[kTabBytes + GD * kMfWaves * 1024 + kMfWaves * kRegion];
+      smem[kTabBytes + k16Waves * 1024 + kRed * k16Waves * 256 * 4];
   unsigned char* const tab = smem;
-  float* const red = (float*)(smem + kTabBytes);
-
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  unsigned char* const reg = smem + kTabBytes + GD * kMfWaves * 1024 + wave * kRegion;
-  const int c = lane & 15, q = lane >> 4;
-  const int nkb = K >> 6;
-  const int b0 = wave * BPW;                       // nkb == 16 BPW
+  unsigned char* const stage = smem + kTabBytes + wave * 1024;
+  float* const red = (float*)(smem + kTabBytes + k16Waves * 1024);
+  const int r = lane & 15, q = lane >> 4;        // MFMA layout
+  const int lr = lane >> 2, lp = lane & 3;       // load layout: row, piece
+  const uint32_t wslot = 16u * (uint32_t)(16 * lp + ((lr + 4 * lp) & 15));
+  const uint32_t rslot = 16u * (uint32_t)(16 * q + ((r + 4 * q) & 15));
   const uint32_t rowK2 = (uint32_t)K >> 1;
+  const uint32_t nkb = (uint32_t)K >> 6;
+  const int nchunks = (K + k16ChunkK - 1) / k16ChunkK;
   const int ngroups = (N + 15) >> 4;
+  const int nrg = ngroups > (int)blockIdx.x
+                      ? (ngroups - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x
+                      : 0;
 
-  // Region layout: piece p of row r at r * kRow + 16 (p ^ swz(r)).
-  static_assert(BPW == 4, "slices of 4 blocks");
-  auto swz = [](int r) { return (r >> 1) & 7; };
-  // A row-contiguous load covers 64 / kPieces rows: lane l of load u takes
-  // piece (64 u + l) % kPieces of row (64 u + l) / kPieces.
-  auto put = [&](const u32x4_t (&v)[kLoads]) {
-#pragma unroll
-    for (int u = 0; u < kLoads; ++u) {
-      const int e = 64 * u + lane, r = e / kPieces, p = e % kPieces;
-      *(u32x4_t*)(reg + r * kRow + 16 * (p ^ swz(r))) = v[u];
-    }
-  };
+  // The mean first, by lane 0 (loads complete in issue order, so its use
+  // waits for nothing else); broadcast where it is used.
+  float mul = 0.0f;
+  if (DQ && lane == 0)
+    mul = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(mean, 4u), 0u, 0, 0));
 
-  // X slice, A operand of half h of block i, lane (row l % 16, quarter q):
-  // X[row][64 (b0 + i) + 16 q + 8 h ..+8] = piece 8 i + 2 q + h of the
-  // row's slice; rows >= M read as zero.
-  const rsrc_t rx = make_rsrc(x, (uint32_t)((int64_t)(M - 1) * ldx * 2 + (int64_t)K * 2));
-  u32x4_t xa[BPW][2];
-  {
-    // The slice is 16 rows x 8 BPW pieces; it passes through the region in
-    // four rounds of kPieces pieces per row (BPW / 4 blocks), whose loads all
-    // go out first (every workgroup reads all of X at once, so a round often
-    // waits for a miss; two rounds in flight took 3% longer).
-    constexpr int kBr = BPW / 4;
-    u32x4_t xv[4][kLoads];
-    auto xload = [&](int R) {
-#pragma unroll
-      for (int u = 0; u < kLoads; ++u) {
-        const int e = 64 * u + lane, r = e / kPieces, p = e % kPieces;
-        xv[R][u] = __builtin_amdgcn_raw_buffer_load_b128(
-            rx, (uint32_t)((int64_t)r * ldx * 2) + (uint32_t)(128 * b0 + 16 * (R * kPieces + p)), 0, 0);
-      }
-    };
-#pragma unroll
-    for (int R = 0; R < 4; ++R) xload(R);
-#pragma unroll
-    for (int R = 0; R < 4; ++R) {
-      put(xv[R]);
-#pragma unroll
-      for (int ib = 0; ib < kBr; ++ib)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int pc = 8 * ib + 2 * q + h;     // piece within this round
-          xa[R * kBr + ib][h] = *(const u32x4_t*)(reg + c * kRow + 16 * (pc ^ swz(c)));
-        }
-    }
-  }
-
-  // Weights of row group g: row-contiguous 16-byte pieces of the 16 rows'
-  // slices (rows past N read as zero and are never stored), and the block
-  // scales of the lane's own row 16 g + l % 16.
   const rsrc_t rw = make_rsrc(packed, (uint32_t)N * rowK2);
-  const uint32_t nblocks = (uint32_t)N * (uint32_t)nkb;
+  const uint32_t nblocks = (uint32_t)N * nkb;
   const rsrc_t rq = make_rsrc(absmax, DQ ? nblocks : nblocks * 4u);
   const rsrc_t rg = make_rsrc(absmax2, DQ ? (nblocks + 255u) / 256u * 4u : 4u);
-  const float mu = DQ ? *mean : 0.0f;
-  struct Stage {
-    u32x4_t w[kLoads];
-    uint32_t qc[BPW];   // block codes (DQ per block), or 4 codes per dword (row mode)
-    float s[BPW];       // group scale (DQ), or fp32 absmax
+  const rsrc_t rx = make_rsrc(x, (uint32_t)((int64_t)(M - 1) * ldx * 2 + (int64_t)K * 2));
+  const uint32_t xrow = (uint32_t)((int64_t)lr * ldx * 2);
+
+  // One item (a row group's piece of one slice), in the load layout: the
+  // lane's two 16-byte weight pieces (row 16 g + x / 4, bytes 64 h + 16 (x %
+  // 4) of the slice) and the raw scale of block x % 4 of that row.
+  struct Item {
+    u32x4_t w[2];
+    uint32_t qc;   // int8 code(s): kScaleDqRow the row's four codes
+    float gs;      // group scale, or the fp32 absmax
   };
-  auto load = [&](Stage& st, int g) {
+  struct Set {
+    Item it[NB];
+  };
+  // X of slice u, half h, in the load layout: xa[h][m] holds row x / 4,
+  // k [256 u + 128 h + 32 m + 8 (x % 4), +8) (zero past K; rows past M read
+  // as zero through the resource).
+  u32x4_t xa[2][4];
+  auto load_x = [&](int u, int h) {
 #pragma unroll
-    for (int u = 0; u < kLoads; ++u) {
-      const int e = 64 * u + lane, r = e / kPieces, p = e % kPieces;
-      st.w[u] = __builtin_amdgcn_raw_buffer_load_b128(
-          rw, (uint32_t)(16 * g + r) * rowK2 + (uint32_t)(32 * b0 + 16 * p), 0, 0);
+    for (int m = 0; m < 4; ++m) {
+      const int k0 = u * k16SliceK + 128 * h + 32 * m;
+      xa[h][m] = __builtin_amdgcn_raw_buffer_load_b128(
+          rx, k0 < K ? xrow + (uint32_t)(k0 + 8 * lp) * 2u : kFar, 0, 0);
     }
-    const uint32_t blk0 = (uint32_t)(16 * g + c) * (uint32_t)nkb + (uint32_t)b0;
+  };
+  // Item of slice u, row group j of the workgroup.
+  auto load_item = [&](Item& it, int u, int j) {
+    {
+      const bool uin = u * k16SliceK < K;
+      const int g = (int)blockIdx.x + j * (int)gridDim.x;
+      const bool in = uin && j < nrg;
+      const uint32_t row = (uint32_t)(16 * g + lr);
+      const uint32_t wo = in ? row * rowK2 + (uint32_t)u * (k16SliceK / 2) + 16u * (uint32_t)lp : kFar;
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) {
+      for (int h = 0; h < 2; ++h) it.w[h] = __builtin_amdgcn_raw_buffer_load_b128(rw, wo + 64u * h, 0, 2);
+      const uint32_t blk = row * nkb + 4u * (uint32_t)u;   // the slice's first block in the row
       if (SM == kScaleDqRow) {
-        // BPW is a multiple of 4 and the wave's blocks sit in one group.
-        if ((i & 3) == 0) st.qc[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, blk0 + i, 0, 0);
-        if (i == 0)
-          st.s[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, (blk0 >> 8) * 4u, 0, 0));
+        it.qc = __builtin_amdgcn_raw_buffer_load_b32(rq, in ? blk : kFar, 0, 0);
+        it.gs = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rg, in ? (blk >> 8) * 4u : kFar, 0, 0));
       } else if (DQ) {
-        st.qc[i] = __builtin_amdgcn_raw_buffer_load_b8(rq, blk0 + i, 0, 0);
-        st.s[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, ((blk0 + i) >> 8) * 4u, 0, 0));
+        const uint32_t b = blk + (uint32_t)lp;
+        it.qc = __builtin_amdgcn_raw_buffer_load_b8(rq, in ? b : kFar, 0, 0);
+        it.gs = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rg, in ? (b >> 8) * 4u : kFar, 0, 0));
       } else {
-        st.s[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rq, (blk0 + i) * 4u, 0, 0));
+        it.qc = 0u;
+        it.gs = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rq, in ? (blk + lp) * 4u : kFar, 0, 0));
       }
     }
   };
-  auto scale = [&](const Stage& st, int i) {
-    if (!DQ) return st.s[i];
-    int code;
-    float g;
-    if (SM == kScaleDqRow) {
-      code = __builtin_amdgcn_sbfe((int)st.qc[i & ~3], (i & 3) * 8, 8);
-      g = st.s[0];
-    } else {
-      code = (int)(int8_t)st.qc[i];
-      g = st.s[i];
-    }
-    const float prod = (float)code * dq_step_normal(g);
+  auto load_set = [&](Set& st, int u, int j0) {
+#pragma unroll
+    for (int jj = 0; jj < NB; ++jj) load_item(st.it[jj], u, j0 + jj);
+  };
+  // Scale of block x % 4 of row x / 4 (load layout).
+  auto load_scale = [&](const Item& it, float mu) {
+    if (!DQ) return it.gs;
+    const int code = SM == kScaleDqRow ? __builtin_amdgcn_sbfe((int)it.qc, lp * 8, 8)
+                                       : (int)(int8_t)(uint8_t)it.qc;
+    const float prod = (float)code * dq_step_normal(it.gs);
     return prod + mu;
   };
+  // Load layout -> lane (q, r) holds piece q of row r, through the stage.
+  auto relayout = [&](u32x4_t& v) {
+    *(u32x4_t*)(stage + wslot) = v;
+    v = *(const u32x4_t*)(stage + rslot);
+  };
 
-  // The loads of the first GD groups go out first (for the decode shapes
-  // that is every group of the workgroup), then the byte -> pair table.
-  Stage st[GD];
-#pragma unroll
-  for (int j = 0; j < GD; ++j)
-    if ((int)blockIdx.x + j * (int)gridDim.x < ngroups) load(st[j], blockIdx.x + j * gridDim.x);
-  const int lvl = level_lanes(lv);
-  for (int e = t; e < 256 * kCopies / 4; e += kMfWaves * 64) {
-    const uint32_t b = (uint32_t)e / (kCopies / 4);
-    const uint32_t v = pack16x2<F16>(level_lookup(lvl, b >> 4), level_lookup(lvl, b & 15u));
-    *(uint4*)(tab + b * 256u + ((uint32_t)e % (kCopies / 4)) * 16u) = make_uint4(v, v, v, v);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  __syncthreads();
-  __builtin_amdgcn_sched_barrier(0);
   const uint32_t lanebyte = (uint32_t)(lane & (kCopies - 1)) << 2;
-
-  // One row group: the wave's partial sums over its blocks.  Lane l holds
-  // Y[4 (l / 16) + v][16 g + l % 16], v = 0..3.
-  auto group = [&](const Stage& st) {
-    put(st.w);
-    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto lut = [&](uint32_t d) {
+    u32x4_t b;
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-      // Bytes [8 q, 8 q + 8) of block i of the lane's row: piece 2 i + q / 2.
-      const int pc = 2 * i + (q >> 1);
-      const uint2 d2 = *(const uint2*)(reg + c * kRow + 16 * (pc ^ swz(c)) + 8 * (q & 1));
+    for (int j = 0; j < 4; ++j)
+      b[j] = *(const uint32_t*)(tab + perm(d, lanebyte, 0x0c0c0000u | ((4u + j) << 8)));
+    return b;
+  };
+  // One item's half h (128 k of its row group) into its sums; X must be in
+  // the MFMA layout.
+  auto mul_item_half = [&](Item& it, int h, f32x4_t& acc, float sl) {
+    relayout(it.w[h]);
+    const auto a = __builtin_amdgcn_permlane32_swap(it.w[h][0], it.w[h][2], false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(it.w[h][1], it.w[h][3], false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+    const auto e = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    const uint32_t E[4] = {c[0], c[1], e[0], e[1]};
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
       f32x4_t blk = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t d = h ? d2.y : d2.x;
-        u32x4_t bw;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t addr = perm(d, lanebyte, 0x0c0c0000u | ((4u + j) << 8));
-          bw[j] = *(const uint32_t*)(tab + addr);
-        }
-        blk = mfma_16x16x32<F16>(xa[i][h], bw, blk);
-      }
-      const float sc = scale(st, i);
+      blk = mfma_16x16x32<F16>(xa[h][2 * hb], lut(E[2 * hb]), blk);
+      blk = mfma_16x16x32<F16>(xa[h][2 * hb + 1], lut(E[2 * hb + 1]), blk);
+      // block 2 h + hb of row r was formed by lane 4 r + 2 h + hb
+      const float sc = __int_as_float(
+          __builtin_amdgcn_ds_bpermute((4 * r + 2 * h + hb) << 2, __float_as_int(sl)));
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(blk[v], sc, acc[v]);
     }
-    return acc;
   };
-  // Rounds of GD row groups: group blockIdx.x + k * grid uses stage k % GD,
-  // which then takes the loads of group k + GD.  The waves run a round's
-  // groups without synchronizing (their LDS regions are private), then add
-  // up the round's partial sums in one pass.  The loop condition is the
-  // workgroup's, so its barriers are uniform.
-  for (int k0 = 0; (int)blockIdx.x + k0 * (int)gridDim.x < ngroups; k0 += GD) {
+  // A set's slice into the batch's sums, item by item (each item's work
+  // starts as soon as its own loads are in).
+  auto mul_set = [&](Set& st, f32x4_t (&acc)[NB], float mu) {
 #pragma unroll
-    for (int j = 0; j < GD; ++j) {
-      const int gg = (int)blockIdx.x + (k0 + j) * (int)gridDim.x;
-      if (gg < ngroups) {
-        *(f32x4_t*)(red + (j * kMfWaves + wave) * 256 + lane * 4) = group(st[j]);
-        const int gn = gg + GD * (int)gridDim.x;
-        if (gn < ngroups) load(st[j], gn);
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) relayout(xa[h][m]);
+#pragma unroll
+    for (int jj = 0; jj < NB; ++jj) {
+      const float sl = load_scale(st.it[jj], mu);
+      mul_item_half(st.it[jj], 0, acc[jj], sl);
+      mul_item_half(st.it[jj], 1, acc[jj], sl);
+    }
+  };
+
+  Set sets[kSets];
+  for (int j0 = 0; j0 < nrg; j0 += NB) {   // the workgroup's loop: barriers are uniform
+    // Only the first item's loads go out before the table build: the
+    // barrier after it waits for the slowest wave, and a wave issuing many
+    // loads into a full memory pipeline stalls for microseconds.  Then X
+    // (cache hits) and the other items.
+    load_item(sets[0].it[0], wave, j0);
+    if (j0 == 0) {
+      // byte -> level-pair table, behind the first loads (no memory waits)
+      const int lvl = level_lanes(lv);
+      for (int e = t; e < 256 * kCopies / 4; e += k16Waves * 64) {
+        const uint32_t b = (uint32_t)e / (kCopies / 4);
+        const uint32_t v = pack16x2<F16>(level_lookup(lvl, b >> 4), level_lookup(lvl, b & 15u));
+        *(uint4*)(tab + b * 256u + ((uint32_t)e % (kCopies / 4)) * 16u) = make_uint4(v, v, v, v);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    load_x(wave, 0);
+    load_x(wave, 1);
+#pragma unroll
+    for (int jj = 1; jj < NB; ++jj) load_item(sets[0].it[jj], wave, j0 + jj);
+    if (MULTI) load_set(sets[kSets - 1], k16Waves + wave, j0);
+    const float mu = DQ ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mul))) : 0.0f;
+    f32x4_t acc[NB];
+#pragma unroll
+    for (int jj = 0; jj < NB; ++jj) acc[jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    if (!MULTI) {
+      mul_set(sets[0], acc, mu);
+    } else {
+      // Chunk c uses weight set c % 2 (one row group).  Once half h of
+      // chunk c is multiplied, half h of chunk c + 1's X goes into the same
+      // registers; once the whole chunk is, chunk c + 2's weights go into its
+      // set.
+      for (int c = 0; c < nchunks; c += 2) {
+        const int u = c * k16Waves + wave;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) relayout(xa[0][m]);
+        const float s0 = load_scale(sets[0].it[0], mu);
+        mul_item_half(sets[0].it[0], 0, acc[0], s0);
+        load_x(u + k16Waves, 0);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) relayout(xa[1][m]);
+        mul_item_half(sets[0].it[0], 1, acc[0], s0);
+        load_x(u + k16Waves, 1);
+        load_set(sets[0], u + 2 * k16Waves, j0);
+        if (c + 1 < nchunks) {   // workgroup-uniform, no loads inside
+#pragma unroll
+          for (int m = 0; m < 4; ++m) relayout(xa[0][m]);
+          const float s1 = load_scale(sets[kSets - 1].it[0], mu);
+          mul_item_half(sets[kSets - 1].it[0], 0, acc[0], s1);
+        }
+        load_x(u + 2 * k16Waves, 0);
+        if (c + 1 < nchunks) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) relayout(xa[1][m]);
+          const float s1 = load_scale(sets[kSets - 1].it[0], mu);
+          mul_item_half(sets[kSets - 1].it[0], 1, acc[0], s1);
+        }
+        load_x(u + 2 * k16Waves, 1);
+        load_set(sets[kSets - 1], u + 3 * k16Waves, j0);
       }
     }
-    __syncthreads();
-    for (int e = t; e < GD * 256; e += kMfWaves * 64) {
-      const int j = e >> 8, m = (e >> 4) & 15, cc = e & 15;
-      const int gg = (int)blockIdx.x + (k0 + j) * (int)gridDim.x;
-      const int n = 16 * gg + cc;
-      if (gg < ngroups && m < M && n < N) {
-        const int src = (((m >> 2) * 16 + cc) << 2) + (m & 3);
-        float sum = 0.0f;
+
+    // the batch's partial sums meet in LDS, kRed row groups at a time;
+    // Y[m][16 g + n] sits at lane 16 (m / 4) + n, value m % 4 of every
+    // wave's fragment
 #pragma unroll
-        for (int w = 0; w < kMfWaves; ++w) sum += red[(j * kMfWaves + w) * 256 + src];
-        y[(int64_t)m * ldy + n] = f32_to_16<F16>(sum);
+    for (int j1 = 0; j1 < NB; j1 += kRed) {
+#pragma unroll
+      for (int jj = 0; jj < kRed; ++jj)
+        *(f32x4_t*)(red + (jj * k16Waves + wave) * 256 + lane * 4) = acc[j1 + jj];
+      __syncthreads();
+      for (int e = t; e < kRed * 256; e += k16Waves * 64) {
+        const int jj = e >> 8, m = (e >> 4) & 15, nn = e & 15;
+        const int n = 16 * ((int)blockIdx.x + (j0 + j1 + jj) * (int)gridDim.x) + nn;
+        if (j0 + j1 + jj < nrg && m < M && n < N) {
+          const int src = ((m >> 2) * 16 + nn) * 4 + (m & 3);
+          float sum = 0.0f;
+#pragma unroll
+          for (int w = 0; w < k16Waves; ++w) sum += red[(jj * k16Waves + w) * 256 + src];
+          y[(int64_t)m * ldy + n] = f32_to_16<F16>(sum);
+        }
       }
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 
-// Row-wise scales in the MFMA path: every wave's four blocks are one dword of
-// codes inside one group; needs 4-byte aligned codes.
-template <bool F16>
-hipError_t launch_mfma(int grid, const uint16_t* x, int64_t ldx, const uint8_t* packed,
-                       const void* absmax, const float* absmax2, const float* mean, int dq,
-                       int M, int N, int K, uint16_t* y, int64_t ldy, const LevelTable& lv,
-                       hipStream_t stream) {
-  if (dq && ((uintptr_t)absmax & 3u) == 0)
-    hipLaunchKernelGGL((gemv_mfma_kernel<4, 4, kScaleDqRow, F16>), dim3(grid),
-                       dim3(kMfWaves * 64), 0, stream, x, ldx, packed, absmax, absmax2, mean, M, N,
-                       K, y, ldy, lv);
-  else if (dq)
-    hipLaunchKernelGGL((gemv_mfma_kernel<4, 2, kScaleDqLane, F16>), dim3(grid),
-                       dim3(kMfWaves * 64), 0, stream, x, ldx, packed, absmax, absmax2, mean, M, N,
-                       K, y, ldy, lv);
-  else
-    hipLaunchKernelGGL((gemv_mfma_kernel<4, 2, kScaleF32, F16>), dim3(grid), dim3(kMfWaves * 64),
-                       0, stream, x, ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, lv);
+// Scale layout of the M > 4 kernel: the four codes of a slice as one dword
+// (shared by a quad) when every row holds a multiple of 4 blocks and the
+// codes are 4-byte aligned (the four blocks then share one group), else one
+// code per lane.  NB, the
+// row groups a workgroup multiplies at once: up to 4 with one chunk of K,
+// 1 with several (two weight sets); larger counts spill registers.
+template <int SM, bool F16>
+hipError_t launch_gemv16_sm(int grid, int nb, bool multi, const uint16_t* x, int64_t ldx,
+                            const uint8_t* packed, const void* absmax, const float* absmax2,
+                            const float* mean, int M, int N, int K, uint16_t* y, int64_t ldy,
+                            const LevelTable& lv, hipStream_t stream) {
+#define BNBX_G16(NB, MULTI)                                                                    \
+  hipLaunchKernelGGL((gemv16_kernel<SM, F16, NB, MULTI>), dim3(grid), dim3(k16Waves * 64), 0, \
+                     stream, x, ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, lv)
+  if (multi) {
+    BNBX_G16(1, true);
+  } else if (nb == 1) {
+    BNBX_G16(1, false);
+  } else if (nb == 2) {
+    BNBX_G16(2, false);
+  } else {
+    BNBX_G16(4, false);
+  }
+#undef BNBX_G16
   return hipGetLastError();
+}
+
+template <bool F16>
+hipError_t launch_gemv16(int grid, const uint16_t* x, int64_t ldx, const uint8_t* packed,
+                         const void* absmax, const float* absmax2, const float* mean, int dq,
+                         int M, int N, int K, uint16_t* y, int64_t ldy, const LevelTable& lv,
+                         hipStream_t stream) {
+  const bool multi = K > k16ChunkK;
+  const int ngroups = (N + 15) / 16;
+  const int per_wg = (ngroups + grid - 1) / grid;
+  const int nb = multi ? 1 : (per_wg >= 3 ? 4 : per_wg);
+  const bool rowq = dq && ((K >> 6) % 4 == 0) && ((uintptr_t)absmax & 3u) == 0;
+  if (rowq)
+    return launch_gemv16_sm<kScaleDqRow, F16>(grid, nb, multi, x, ldx, packed, absmax, absmax2,
+                                              mean, M, N, K, y, ldy, lv, stream);
+  if (dq)
+    return launch_gemv16_sm<kScaleDqLane, F16>(grid, nb, multi, x, ldx, packed, absmax, absmax2,
+                                               mean, M, N, K, y, ldy, lv, stream);
+  return launch_gemv16_sm<kScaleF32, F16>(grid, nb, multi, x, ldx, packed, absmax, absmax2, mean,
+                                          M, N, K, y, ldy, lv, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -733,24 +843,30 @@ hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* packed, co
                        hipStream_t stream) {
   const int64_t rowK2 = K >> 1, nkb = K >> 6;
   const LevelTable& lv = level_table(quant_type);
-  // 4 < M <= 16 at K = 4096 (each wave's K slice in its registers): one
-  // MFMA launch streams the weights once, when the offsets fit 32 bits.
-  if (M > 4) {
-    const bool fits = nkb == 64 &&
-                      (int64_t)N * rowK2 < ((int64_t)1 << 31) &&
-                      15 * ldx * 2 + (int64_t)K * 2 < ((int64_t)1 << 31);
-    if (fits) {
-      const int ngroups = (N + 15) / 16;
-      const int grid = ngroups < cu_count() ? ngroups : cu_count();
-      return f16 ? launch_mfma<true>(grid, x, ldx, packed, absmax, absmax2, mean, double_quant, M,
-                                     N, K, y, ldy, lv, stream)
-                 : launch_mfma<false>(grid, x, ldx, packed, absmax, absmax2, mean, double_quant, M,
-                                      N, K, y, ldy, lv, stream);
-    }
-  }
-  // Slabs of rows keep every byte offset of a launch below 2^31.
+  // Slabs of rows keep every byte offset of a launch below 2^31 (whole
+  // 256-row multiples, so the slabs' double-quant groups stay whole).
   int64_t slab = ((int64_t)1 << 30) / rowK2;
   slab -= slab % 256;
+  if (slab < 256) return hipErrorNotSupported;
+  // 4 < M <= 16: one launch per slab streams the weights once.
+  if (M > 4) {
+    if (15 * ldx * 2 + (int64_t)K * 2 >= ((int64_t)1 << 31)) return hipErrorNotSupported;
+    for (int64_t r0 = 0; r0 < N; r0 += slab) {
+      const int n = (int)(N - r0 < slab ? N - r0 : slab);
+      const int ngroups = (n + 15) / 16;
+      const int grid = ngroups < cu_count() ? ngroups : cu_count();
+      const void* am = double_quant ? (const void*)((const int8_t*)absmax + r0 * nkb)
+                                    : (const void*)((const float*)absmax + r0 * nkb);
+      const float* am2 = double_quant ? absmax2 + (r0 * nkb) / 256 : absmax2;
+      const hipError_t e =
+          f16 ? launch_gemv16<true>(grid, x, ldx, packed + r0 * rowK2, am, am2, mean, double_quant,
+                                    M, n, K, y + r0, ldy, lv, stream)
+              : launch_gemv16<false>(grid, x, ldx, packed + r0 * rowK2, am, am2, mean,
+                                     double_quant, M, n, K, y + r0, ldy, lv, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   // Rows of X in groups of up to four (each group streams W once); a group
   // of three runs the four-row kernel with its last row empty.  Long rows
   // take smaller groups (the X slice must fit the registers).

@@ -91,14 +91,29 @@ def test_every_m_ragged_n(kind, M):
 @pytest.mark.parametrize("M", [5, 8, 16])
 @pytest.mark.parametrize("N,K,dq", [(200, 64, True), (200, 1088, True), (130, 4096, False),
                                     (70, 2048, True), (130, 8192, True), (50, 8192, False),
-                                    (40, 16384, True)])
+                                    (40, 16384, True), (300, 4160, True), (33, 320, False),
+                                    (20000, 512, True)])
 def test_gemv_more_than_four_rows(M, N, K, dq):
-    """4 < M <= 16 (one launch streaming W once where the shape allows, else
-    groups of four rows): K from one block to 256 blocks, ragged row groups,
-    both scale layouts."""
+    """4 < M <= 16 (one launch that streams W once, any K): K from one block
+    to 256 blocks, K not a multiple of the 256-k slices, ragged row groups,
+    more row groups than one batch per workgroup holds, both scale
+    layouts."""
     w = synth.normal_bf16((N, K), 0.05, 8000 + K + M)
     x = synth.normal_bf16((M, K), 1.0, 8100 + K + M)
     ref, q = setup(w, (N, K), dq, check_state=False)
+    err = product_error(run("gemv", x, M, K, q), ref_product(x, ref, N, K))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("N,K", [(4096, 11008), (11008, 4096)])
+def test_gemv_m16_llama_shapes(N, K):
+    """M=16 on the Llama-7B down projection (K = 11008, three chunks of
+    slices per wave) and the gate/up shape, double quant: all of Y against
+    the oracle (whole matrix, every row, every tile)."""
+    M = 16
+    w = synth.normal_bf16((N, K), 0.02, 8300 + K)
+    x = synth.normal_bf16((M, K), 1.0, 8400 + K)
+    ref, q = setup(w, (N, K), True, check_state=False)
     err = product_error(run("gemv", x, M, K, q), ref_product(x, ref, N, K))
     assert err <= TOL, err
 
