@@ -20,13 +20,13 @@ import os
 __all__ = [
     "BNBX_OK", "BNBX_E_INVAL", "BNBX_E_ALIGN", "BNBX_E_UNSUPPORTED", "BNBX_E_WORKSPACE",
     "BNBX_E_HIP", "BNBX_E_INTERNAL", "BnbxError", "BnbxLibraryMissing", "Nf4State", "library_path", "lib",
-    "bnbx_status_str", "bnbx_nf4_codebook", "bnbx_fp4_codebook",
+    "bnbx_status_str", "bnbx_nf4_codebook", "bnbx_fp4_codebook", "bnbx_dynamic_map",
     "bnbx_quantize_nf4_workspace_bytes",
     "bnbx_quantize_nf4", "bnbx_quantize_nf4_noalloc", "BNBX_NOALLOC_MAX_WEIGHTS",
     "bnbx_dequantize_nf4", "bnbx_gemv_nf4",
     "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4", "bnbx_gemm_nf4_dx", "bnbx_gemm_nf4_lora",
     "bnbx_probe_stream_read", "BNBX_PROBE_SINK_WORDS", "EXPORTED_SYMBOLS", "BNBX_QUANT_NF4", "BNBX_QUANT_FP4",
-    "BNBX_DTYPE_BF16", "BNBX_DTYPE_F16",
+    "BNBX_DTYPE_BF16", "BNBX_DTYPE_F16", "BNBX_DQ_NONE", "BNBX_DQ_LINEAR", "BNBX_DQ_DYNAMIC",
 ]
 
 BNBX_OK = 0
@@ -41,11 +41,14 @@ BNBX_QUANT_NF4 = 0
 BNBX_QUANT_FP4 = 1
 BNBX_DTYPE_BF16 = 0
 BNBX_DTYPE_F16 = 1
+BNBX_DQ_NONE = 0
+BNBX_DQ_LINEAR = 1
+BNBX_DQ_DYNAMIC = 2
 
 BNBX_NOALLOC_MAX_WEIGHTS = 1 << 28
 
 EXPORTED_SYMBOLS = (
-    "bnbx_status_str", "bnbx_nf4_codebook", "bnbx_fp4_codebook",
+    "bnbx_status_str", "bnbx_nf4_codebook", "bnbx_fp4_codebook", "bnbx_dynamic_map",
     "bnbx_quantize_nf4_workspace_bytes",
     "bnbx_quantize_nf4", "bnbx_quantize_nf4_noalloc", "bnbx_dequantize_nf4", "bnbx_gemv_nf4",
     "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4", "bnbx_gemm_nf4_dx", "bnbx_gemm_nf4_lora",
@@ -113,6 +116,8 @@ def lib() -> ctypes.CDLL:
     L.bnbx_nf4_codebook.restype = i32
     L.bnbx_fp4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
     L.bnbx_fp4_codebook.restype = i32
+    L.bnbx_dynamic_map.argtypes = [ctypes.POINTER(ctypes.c_float)]
+    L.bnbx_dynamic_map.restype = i32
     L.bnbx_quantize_nf4_workspace_bytes.argtypes = [i64, i32, i32]
     L.bnbx_quantize_nf4_workspace_bytes.restype = sz
     L.bnbx_quantize_nf4.argtypes = [vp, vp, sp, vp, sz, vp]
@@ -178,6 +183,12 @@ def bnbx_nf4_codebook() -> list[float]:
 def bnbx_fp4_codebook() -> list[float]:
     buf = (ctypes.c_float * 16)()
     _check(lib().bnbx_fp4_codebook(buf), "bnbx_fp4_codebook")
+    return list(buf)
+
+
+def bnbx_dynamic_map() -> list[float]:
+    buf = (ctypes.c_float * 256)()
+    _check(lib().bnbx_dynamic_map(buf), "bnbx_dynamic_map")
     return list(buf)
 
 

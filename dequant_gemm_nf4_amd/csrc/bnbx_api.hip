@@ -153,7 +153,9 @@ int check_state(const bnbx_nf4_state* st) {
   if (st == nullptr) return BNBX_E_INVAL;
   if (st->n < 2 || (st->n & 1)) return BNBX_E_INVAL;
   if (st->blocksize != kBlock) return BNBX_E_UNSUPPORTED;
-  if (st->double_quant != 0 && st->double_quant != 1) return BNBX_E_INVAL;
+  if (st->double_quant != kDqNone && st->double_quant != kDqLinear &&
+      st->double_quant != kDqDynamic)
+    return BNBX_E_INVAL;
   if (st->quant_type != BNBX_QUANT_NF4 && st->quant_type != BNBX_QUANT_FP4) return BNBX_E_INVAL;
   if (st->compute_dtype != BNBX_DTYPE_BF16 && st->compute_dtype != BNBX_DTYPE_F16)
     return BNBX_E_INVAL;
@@ -220,10 +222,22 @@ int quantize_dq(const uint16_t* w, uint8_t* packed, const bnbx_nf4_state* st, vo
   float* a32 = (float*)((char*)workspace + round_up(kSlotBytes, 256));
   hipError_t e = launch_quantize(w, packed, n, a32, slots, st->quant_type, hs);
   if (e == hipSuccess)
-    e = launch_double_quant(a32, slots, quantize_grid(n), nb, (int8_t*)st->absmax, st->absmax2,
-                            st->absmax_mean, hs);
+    e = launch_double_quant(a32, slots, quantize_grid(n), nb, (uint8_t*)st->absmax, st->absmax2,
+                            st->absmax_mean, st->double_quant, hs);
   return hip_status(e);
 }
+
+// The dynamic map ascends strictly, holds 0 at its zero code and 1 at the
+// top, and is symmetric below the top.
+constexpr bool dyn_map_ok() {
+  constexpr DynMap m = make_dyn_map();
+  for (int i = 0; i < 255; ++i)
+    if (!(m.v[i] < m.v[i + 1]) || !(m.v[i] < m.mid[i] && m.mid[i] < m.v[i + 1])) return false;
+  for (int i = 0; i < 127; ++i)
+    if (m.v[i] != -m.v[254 - i]) return false;
+  return m.v[kDynZeroCode] == 0.0f && m.v[255] == 1.0f;
+}
+static_assert(dyn_map_ok(), "dynamic 8-bit map");
 
 }  // namespace
 
@@ -263,6 +277,13 @@ int bnbx_fp4_codebook(float levels_host[16]) {
   if (!all_tables().ok) return BNBX_E_INTERNAL;
   const float* l = levels_f32(kQuantFP4);
   for (int i = 0; i < 16; ++i) levels_host[i] = l[i];
+  return BNBX_OK;
+}
+
+int bnbx_dynamic_map(float values_host[256]) {
+  if (values_host == nullptr) return BNBX_E_INVAL;
+  constexpr DynMap m = make_dyn_map();
+  for (int i = 0; i < 256; ++i) values_host[i] = m.v[i];
   return BNBX_OK;
 }
 

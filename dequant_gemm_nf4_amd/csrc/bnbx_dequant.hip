@@ -6,7 +6,9 @@
 // level pair of each byte in an LDS table, multiplies by the block scale in
 // binary32 and rounds the pair to the compute type (one v_cvt_pk_bf16_f32,
 // or two v_cvt_f16_f32), writing 64 bytes.  The block scale follows the stored format exactly:
-// a_b, or fl32(fl32(q_b * fl32(s_g / 127)) + mean) with double quantization.
+// a_b, or with double quantization fl32(fl32(q_b * fl32(s_g / 127)) + mean)
+// (linear map) or fl32(fl32(map[q_b] * s_g) + mean) (dynamic map, read from
+// a copy in LDS).
 #include "bnbx_device.hpp"
 #include "bnbx_internal.hpp"
 
@@ -23,10 +25,16 @@ constexpr int kDUnroll = 1;     // chunks per wave per round
 // its HBM writes, not by these reads.
 constexpr int kCopies = 4;
 
-template <bool DQ>
+template <int DQ>
 __device__ __forceinline__ float exact_block_scale(int64_t blk, const void* absmax,
-                                                   const float* absmax2, float mu) {
-  if (!DQ) return ((const float*)absmax)[blk];
+                                                   const float* absmax2, float mu,
+                                                   const float* dmap) {
+  if (DQ == kDqNone) return ((const float*)absmax)[blk];
+  if (DQ == kDqDynamic) {
+    const float v = dmap[((const uint8_t*)absmax)[blk]];
+    const float prod = v * absmax2[blk / kGroup];
+    return prod + mu;
+  }
   const float q = (float)((const int8_t*)absmax)[blk];
   const float step = absmax2[blk / kGroup] / 127.0f;   // correctly rounded
   const float prod = q * step;                        // rounded on its own ...
@@ -48,12 +56,13 @@ __device__ __forceinline__ uint4 expand8(uint32_t d, float sc, const float2* tab
 // Wave-level layout: in a 1 KB chunk of packed bytes, lane l handles packed
 // dwords l, 64+l, 128+l and 192+l, so every load instruction reads 256
 // contiguous bytes and every store instruction writes 1 KB contiguous.
-template <bool DQ, bool F16>
+template <int DQ, bool F16>
 __global__ __launch_bounds__(kDThreads) void dequant_kernel(
     const uint8_t* __restrict__ packed, int64_t n, const void* __restrict__ absmax,
     const float* __restrict__ absmax2, const float* __restrict__ mean,
     uint16_t* __restrict__ out, LevelTable lv) {
   __shared__ float2 tabs[kCopies][256];   // byte -> (L[high nibble], L[low nibble])
+  __shared__ float dmap[DQ == kDqDynamic ? 256 : 1];
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t nbytes = n >> 1;
   const int64_t full = nbytes / kChunk;
@@ -65,9 +74,10 @@ __global__ __launch_bounds__(kDThreads) void dequant_kernel(
     const uint32_t b = (uint32_t)e & 255u;
     tabs[e >> 8][b] = make_float2(level_lookup(lvl, b >> 4), level_lookup(lvl, b & 15u));
   }
+  if (DQ == kDqDynamic && tid < 256) dmap[tid] = kDynMapDev.v[tid];
   __syncthreads();
   const float2* tab = tabs[lane & (kCopies - 1)];
-  const float mu = DQ ? *mean : 0.0f;
+  const float mu = DQ != kDqNone ? *mean : 0.0f;
 
   for (int64_t c0 = gw; c0 < full; c0 += nw * kDUnroll) {
     uint32_t d[kDUnroll][4];
@@ -83,7 +93,7 @@ __global__ __launch_bounds__(kDThreads) void dequant_kernel(
     for (int u = 0; u < kDUnroll; ++u) {
       const int64_t c = c0 + u * nw < full ? c0 + u * nw : full - 1;
       // lanes 0..31 each form one of the chunk's 32 block scales
-      scl[u] = exact_block_scale<DQ>(c * 32 + (lane & 31), absmax, absmax2, mu);
+      scl[u] = exact_block_scale<DQ>(c * 32 + (lane & 31), absmax, absmax2, mu, dmap);
     }
 #pragma unroll
     for (int u = 0; u < kDUnroll; ++u) {
@@ -104,7 +114,7 @@ __global__ __launch_bounds__(kDThreads) void dequant_kernel(
   // ragged tail (fewer than 1 KB of packed bytes) on the last wave, bytewise
   if (full * kChunk < nbytes && gw == nw - 1) {
     for (int64_t b = full * kChunk + lane; b < nbytes; b += 64) {
-      const float sc = exact_block_scale<DQ>((b << 1) / kBlock, absmax, absmax2, mu);
+      const float sc = exact_block_scale<DQ>((b << 1) / kBlock, absmax, absmax2, mu, dmap);
       const float2 lp = tab[packed[b]];
       const uint32_t pr = pack16x2<F16>(lp.x * sc, lp.y * sc);
       out[2 * b] = (uint16_t)(pr & 0xffffu);
@@ -127,12 +137,15 @@ hipError_t launch_dequantize(const uint8_t* packed, int64_t n, const void* absma
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kDThreads), 0, stream, packed, n, absmax,
                        absmax2, mean, out, lv);
   };
-  if (double_quant) {
-    if (f16) go(dequant_kernel<true, true>);
-    else go(dequant_kernel<true, false>);
+  if (double_quant == kDqDynamic) {
+    if (f16) go(dequant_kernel<kDqDynamic, true>);
+    else go(dequant_kernel<kDqDynamic, false>);
+  } else if (double_quant) {
+    if (f16) go(dequant_kernel<kDqLinear, true>);
+    else go(dequant_kernel<kDqLinear, false>);
   } else {
-    if (f16) go(dequant_kernel<false, true>);
-    else go(dequant_kernel<false, false>);
+    if (f16) go(dequant_kernel<kDqNone, true>);
+    else go(dequant_kernel<kDqNone, false>);
   }
   return hipGetLastError();
 }

@@ -37,8 +37,9 @@
 //   barrier.  The weight loads go out before the copies: a copy's arrival in
 //   LDS is not ordered with later loads, so the memory counter can only be
 //   trusted down to zero.
-// Block codes come four steps at a time (one dword of four int8 codes per
-// row) when the shape allows it.  Each LDS buffer is its own object, picked
+// Block codes come four steps at a time (one dword of four code bytes per
+// row) when the shape allows it; codes into the dynamic 8-bit map are looked
+// up in a copy of the map in LDS.  Each LDS buffer is its own object, picked
 // at compile time, so the compiler can tell reads of one buffer from copies
 // in flight into another.  Steps past the end of K load clamped (redundant)
 // data that no MFMA uses.
@@ -139,7 +140,7 @@ __device__ __forceinline__ void decode8(uint32_t d, const Tab16& t, uint32_t* o)
 struct WSet {
   u32x4_t w[2];
 };
-// Block scale of a lane's own row: the int8 block code(s) as loaded (one per
+// Block scale of a lane's own row: the block code byte(s) as loaded (one per
 // step, or four per dword) and the group scale (double quant), or the fp32
 // block absmax bits (no double quant).
 struct QSet {
@@ -174,13 +175,15 @@ struct LoraArgs {
   int r;
 };
 
-template <bool DQ, bool Q4, bool FP4, bool F16, bool LORA>
+template <int DQ, bool Q4, bool FP4, bool F16, bool LORA>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ packed,
     const void* __restrict__ absmax, const float* __restrict__ absmax2,
     const float* __restrict__ mean, int M, int N, int K, uint16_t* __restrict__ y, int64_t ldy,
     int tiles_m, int tiles_n, LevelTable lv, LoraArgs la) {
   __shared__ __attribute__((aligned(16))) uint16_t As0[kABuf], As1[kABuf];
+  constexpr bool DYN = DQ == kDqDynamic;
+  __shared__ float dmap[DYN ? 256 : 1];   // the dynamic 8-bit map (DYN)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -196,6 +199,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   const int m0 = (tile / tiles_n) * BM;
   const int n0 = (tile % tiles_n) * BN;
 
+  if (DYN) {
+    dmap[tid] = kDynMapDev.v[tid];
+    __syncthreads();
+  }
   const float mu = DQ ? *mean : 0.0f;
   const uint32_t rowK2 = (uint32_t)K >> 1;   // packed bytes per weight row
   const int nkb = K >> 6;
@@ -273,7 +280,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   // Own-row block scale from code byte `byte` of the set.
   auto scale_of = [&](const QSet& s, int byte) {
     float sc;
-    if (DQ) {
+    if (DYN) {
+      // fl32(fl32(map[q] * s_g) + mean)
+      const float prod = dmap[(s.q >> (8 * byte)) & 0xffu] * s.s;
+      sc = prod + mu;
+    } else if (DQ) {
       // (float)(int8)q = (float)(int32)(q << 24) * 2^-24, both steps exact
       const uint32_t t = (s.q >> (8 * byte)) << 24;
       const float qf = (float)(int32_t)t * 0x1p-24f;
@@ -468,7 +479,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     }
 }
 
-template <bool DQ, bool Q4, bool LORA>
+template <int DQ, bool Q4, bool LORA>
 void launch_one(const uint16_t* x, int64_t ldx, const uint8_t* packed, const void* absmax,
                 const float* absmax2, const float* mean, int M, int N, int K, uint16_t* y,
                 int64_t ldy, int quant_type, bool f16, const LoraArgs& la, hipStream_t stream) {
@@ -518,14 +529,20 @@ hipError_t launch_gemm_any(const uint16_t* x, int64_t ldx, const uint8_t* packed
     LoraArgs ls = la;
     if (LORA) ls.xa = la.xa + r0 * la.ldxa;
     if (!double_quant)
-      launch_one<false, false, LORA>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys, ldy,
-                                     quant_type, f16, ls, stream);
+      launch_one<kDqNone, false, LORA>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys, ldy,
+                                       quant_type, f16, ls, stream);
+    else if (double_quant == kDqDynamic && q4)
+      launch_one<kDqDynamic, true, LORA>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys,
+                                         ldy, quant_type, f16, ls, stream);
+    else if (double_quant == kDqDynamic)
+      launch_one<kDqDynamic, false, LORA>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys,
+                                          ldy, quant_type, f16, ls, stream);
     else if (q4)
-      launch_one<true, true, LORA>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys, ldy,
-                                   quant_type, f16, ls, stream);
+      launch_one<kDqLinear, true, LORA>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys, ldy,
+                                        quant_type, f16, ls, stream);
     else
-      launch_one<true, false, LORA>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys, ldy,
-                                    quant_type, f16, ls, stream);
+      launch_one<kDqLinear, false, LORA>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys,
+                                         ldy, quant_type, f16, ls, stream);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

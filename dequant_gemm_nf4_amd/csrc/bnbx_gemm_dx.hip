@@ -60,7 +60,7 @@ __device__ __forceinline__ uint32_t tile_off(int r, int c) {
   return (uint32_t)(r * (TN * 2) + (((c >> 3) ^ ((r >> 1) & 7)) << 4) + ((c & 7) << 1));
 }
 
-template <bool DQ, bool F16>
+template <int DQ, bool F16>
 __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(
     const uint16_t* __restrict__ dy, int64_t lddy, const uint8_t* __restrict__ packed,
     const void* __restrict__ absmax, const float* __restrict__ absmax2,
@@ -79,6 +79,8 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(
   // so lanes of different copies read different banks whatever e they read
   __shared__ float2 tabs[256][kCopies];
   __shared__ float scl[2][4][TN];   // block scales of a step: [block][row]
+  constexpr bool DYN = DQ == kDqDynamic;
+  __shared__ float dmap[DYN ? 256 : 1];   // the dynamic 8-bit map (DYN)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -96,6 +98,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(
   const int m0 = (tile / tiles_k) * TM;
   const int k0 = (tile % tiles_k) * TK;
 
+  if (DYN && tid < 256) dmap[tid] = kDynMapDev.v[tid];
   {
     const int lvl = level_lanes(lv);
     for (int e = tid; e < kCopies * 256; e += kThreads) {
@@ -151,7 +154,8 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(
 
   // Block scales of a step: 64 rows x the tile's 4 blocks, one per thread of
   // the first 256 (row tid / 4, block tid % 4).  Exactly as stored: a_b, or
-  // fl32(fl32(q * fl32(s_g / 127)) + mean) (dq_scale).
+  // fl32(fl32(q * fl32(s_g / 127)) + mean) (dq_scale), or with the dynamic
+  // map fl32(fl32(map[q] * s_g) + mean).
   const uint32_t nblocks = (uint32_t)N * (uint32_t)nkb;
   const rsrc_t rq = make_rsrc(absmax, DQ ? nblocks : nblocks * 4u);
   const rsrc_t rg2 = make_rsrc(absmax2, DQ ? (nblocks + 255u) / 256u * 4u : 4u);
@@ -181,7 +185,10 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(
   auto put_scale = [&](const SRaw& r, int buf) {
     if (!scaler) return;
     float sc;
-    if (DQ) {
+    if (DYN) {
+      const float prod = dmap[r.q & 0xffu] * r.s;
+      sc = prod + mu;
+    } else if (DQ) {
       sc = dq_scale((float)(int8_t)(uint8_t)r.q, r.s, mu);
     } else {
       sc = __builtin_bit_cast(float, r.q);
@@ -247,6 +254,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(
   const SRaw r0 = load_scale(0), r1 = load_scale(clampstep(1));
   load_unit(wb, clampstep(1));
   __builtin_amdgcn_s_waitcnt(0);
+  if (DYN) __syncthreads();   // the map in LDS
   put_scale(r0, 0);
   put_scale(r1, 1);
   __syncthreads();   // byte table and first scales complete
@@ -327,12 +335,15 @@ hipError_t launch_gemm_dx(const uint16_t* dy, int64_t lddy, const uint8_t* packe
                          dys, lddy, packed, absmax, absmax2, mean, m, N, K, dxs, lddx, tm, tk,
                          lv);
     };
-    if (double_quant) {
-      if (f16) go(gemm_dx_kernel<true, true>);
-      else go(gemm_dx_kernel<true, false>);
+    if (double_quant == kDqDynamic) {
+      if (f16) go(gemm_dx_kernel<kDqDynamic, true>);
+      else go(gemm_dx_kernel<kDqDynamic, false>);
+    } else if (double_quant) {
+      if (f16) go(gemm_dx_kernel<kDqLinear, true>);
+      else go(gemm_dx_kernel<kDqLinear, false>);
     } else {
-      if (f16) go(gemm_dx_kernel<false, true>);
-      else go(gemm_dx_kernel<false, false>);
+      if (f16) go(gemm_dx_kernel<kDqNone, true>);
+      else go(gemm_dx_kernel<kDqNone, false>);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -85,12 +85,31 @@ __device__ __forceinline__ float wave_sum_to_63(float v) {
   return v;
 }
 
-// Block-scale storage: fp32 absmax, or double quant (int8 code + fp32 group
-// scale + mean) read per lane, or double quant read per row.  The row-wise
-// read loads whole dwords of codes, and the buffer range check zeroes a dword
-// that is only partly inside the row, so it needs a row of 4k blocks (at most
-// 256: K <= 16384, K % 256 == 0) and 4-byte aligned codes.
-enum ScaleMode { kScaleF32 = 0, kScaleDqLane = 1, kScaleDqRow = 2 };
+// Block-scale storage: fp32 absmax, or double quant (code byte + fp32 group
+// scale + mean) read per lane, or double quant read per row; the code bytes
+// are int8 steps of s_g / 127 (linear map) or indices into the dynamic 8-bit
+// map (Dyn modes, a copy of the map in LDS).  The row-wise read loads whole
+// dwords of codes, and the buffer range check zeroes a dword that is only
+// partly inside the row, so it needs a row of 4k blocks (at most 256:
+// K <= 16384, K % 256 == 0) and 4-byte aligned codes.
+enum ScaleMode {
+  kScaleF32 = 0,
+  kScaleDqLane = 1,
+  kScaleDqRow = 2,
+  kScaleDynLane = 3,
+  kScaleDynRow = 4
+};
+constexpr bool scale_dyn(int sm) { return sm == kScaleDynLane || sm == kScaleDynRow; }
+constexpr bool scale_row(int sm) { return sm == kScaleDqRow || sm == kScaleDynRow; }
+constexpr int kMapBytes = 256 * 4;
+
+// Lane t % 256's value of the dynamic map, one load per lane with no
+// condition (so that the wait for it, in load order, names nothing later).
+__device__ __forceinline__ float dyn_map_value(int t) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(kDynMapDev.v, (uint32_t)kMapBytes),
+                                                  (uint32_t)(t & 255) * 4u, 0, 0));
+}
 
 // MM rows of X per launch (rows >= mvalid are zero), NI chunks per lane, RR
 // rows of W per team and pass.  TW = 1 << twl waves per team.
@@ -101,17 +120,20 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
     const float* __restrict__ mean, int mvalid, int N, int K, uint16_t* __restrict__ y,
     int64_t ldy, int twl, int xlds, LevelTable lv) {
   constexpr bool DQ = SM != kScaleF32;
+  constexpr bool DYN = scale_dyn(SM);
   // One LDS block with the table at offset 0, so that a table address is the
   // v_perm result itself (the ds_read offset field cannot hold a 64 KB base),
-  // then X, then the team sums.  X is stored in 64-byte chunks whose four
+  // then X, then the team sums, then the dynamic map (DYN).  X is stored in 64-byte chunks whose four
   // 16-byte pieces are rotated by (chunk / 4) % 4: piece q of chunk c sits at
   // 64 c + 16 (q ^ ((c >> 2) & 3)), so that 16 lanes reading piece q of 16
   // consecutive chunks hit 64 distinct banks.
   __shared__ __attribute__((aligned(16))) unsigned char smem[kTabBytes + kXBytes +
-                                                             kWaves * MM * RR * 4];
+                                                             kWaves * MM * RR * 4 +
+                                                             (DYN ? kMapBytes : 0)];
   unsigned char* const tab = smem;
   unsigned char* const xs = smem + kTabBytes;
   float* const red = (float*)(smem + kTabBytes + kXBytes);
+  unsigned char* const dmap = smem + kTabBytes + kXBytes + kWaves * MM * RR * 4;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -146,6 +168,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
   float mul = 0.0f;
   if (DQ && lane == 0)
     mul = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(mean, 4u), 0u, 0, 0));
+  const float dmv = DYN ? dyn_map_value(t) : 0.0f;
 
   // 1. X: staging loads (LDS path) or the lane's slice directly.
   uint32_t xr[MM][NI][16];
@@ -189,7 +212,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
   //    handed to the lanes that need them by ds_bpermute) and its group
   //    scales with scalar loads (a row spans at most two groups); otherwise
   //    every lane loads its own block's scales.
-  constexpr bool rowsc = SM == kScaleDqRow;
+  constexpr bool rowsc = scale_row(SM);
   const uint32_t ng = DQ ? (uint32_t)(((uint64_t)N * nkb + 255) >> 8) : 1u;
   uint4 w[RR][NI];
   int qv[RR][NI];
@@ -229,7 +252,8 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
         const uint32_t blk0 = (uint32_t)(row * nkb);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-          qv[j][i] = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(rq, boff[i], 0, 0);
+          const uint32_t cb = __builtin_amdgcn_raw_buffer_load_b8(rq, boff[i], 0, 0);
+          qv[j][i] = DYN ? (int)(uint8_t)cb : (int)(int8_t)(uint8_t)cb;
           gv[j][i] = __builtin_bit_cast(
               float, __builtin_amdgcn_raw_buffer_load_b32(rg, ((blk0 + boff[i]) >> 8) * 4u, 0, 0));
         }
@@ -257,6 +281,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
     const uint32_t v = pack16x2<F16>(level_lookup(lvl, b >> 4), level_lookup(lvl, b & 15u));
     *(uint4*)(tab + b * 256u + ((uint32_t)e % (kCopies / 4)) * 16u) = make_uint4(v, v, v, v);
   }
+  if (DYN && t < 256) *(float*)(dmap + t * 4) = dmv;
   if (xlds) {
 #pragma unroll
     for (int k = 0; k < kStage; ++k) {
@@ -309,14 +334,16 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
     for (int j = 0; j < RR; ++j) {
 #pragma unroll
       for (int m = 0; m < MM; ++m) acc[m][j] = 0.0f;
-      // the row's (at most two) group steps fl32(s_g / 127), once per row
+      // the row's (at most two) group factors, once per row: the steps
+      // fl32(s_g / 127) (linear map) or s_g itself (dynamic map);
       // quad_perm(0,0,0,0) / (1,1,1,1): every lane takes its quad's g0 / g1
+      auto factor = [&](float g) { return DYN ? g : dq_step_normal(g); };
       const float step0 =
-          rowsc ? dq_step_normal(__int_as_float(__builtin_amdgcn_update_dpp(
+          rowsc ? factor(__int_as_float(__builtin_amdgcn_update_dpp(
                       0, __float_as_int(gsl[j]), 0x00, 0xF, 0xF, false)))
                 : 0.0f;
       const float step1 =
-          rowsc ? dq_step_normal(__int_as_float(__builtin_amdgcn_update_dpp(
+          rowsc ? factor(__int_as_float(__builtin_amdgcn_update_dpp(
                       0, __float_as_int(gsl[j]), 0x55, 0xF, 0xF, false)))
                 : 0.0f;
 #pragma unroll
@@ -324,8 +351,15 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
         float sc;
         if (rowsc) {
           const int qw = __builtin_amdgcn_ds_bpermute((int)((boff[i] >> 2) << 2), qd[j]);
-          const int q = __builtin_amdgcn_sbfe(qw, (boff[i] & 3u) * 8u, 8);
-          const float prod = (float)q * (boff[i] < split[j] ? step0 : step1);
+          float qf;
+          if (DYN)
+            qf = *(const float*)(dmap + __builtin_amdgcn_ubfe((uint32_t)qw, (boff[i] & 3u) * 8u, 8) * 4u);
+          else
+            qf = (float)(int)__builtin_amdgcn_sbfe(qw, (boff[i] & 3u) * 8u, 8);   // signed
+          const float prod = qf * (boff[i] < split[j] ? step0 : step1);
+          sc = prod + mu;
+        } else if (DYN) {
+          const float prod = *(const float*)(dmap + (uint32_t)qv[j][i] * 4u) * gv[j][i];
           sc = prod + mu;
         } else {
           sc = DQ ? (float)qv[j][i] * dq_step_normal(gv[j][i]) + mu : gv[j][i];
@@ -438,19 +472,21 @@ __global__ __launch_bounds__(k16Waves * 64, 1) void gemv16_kernel(
     const float* __restrict__ mean, int M, int N, int K, uint16_t* __restrict__ y, int64_t ldy,
     LevelTable lv) {
   constexpr bool DQ = SM != kScaleF32;
+  constexpr bool DYN = scale_dyn(SM);
   constexpr int kSets = MULTI ? 2 : 1;
   constexpr int kRed = NB < 2 ? NB : 2;   // row groups reduced at once
   static_assert(!MULTI || NB == 1, "several chunks take one row group at a time");
   // Table at LDS offset 0 (its addresses are v_perm results), then the
-  // waves' 1 KB stages, then the partial sums.
+  // waves' 1 KB stages, then the partial sums, then the dynamic map (DYN).
   __shared__ __attribute__((aligned(16))) unsigned char
-      smem[kTabBytes + k16Waves * 1024 + kRed * k16Waves * 256 * 4];
+      smem[kTabBytes + k16Waves * 1024 + kRed * k16Waves * 256 * 4 + (DYN ? kMapBytes : 0)];
   unsigned char* const tab = smem;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   unsigned char* const stage = smem + kTabBytes + wave * 1024;
   float* const red = (float*)(smem + kTabBytes + k16Waves * 1024);
+  unsigned char* const dmap = smem + kTabBytes + k16Waves * 1024 + kRed * k16Waves * 256 * 4;
   const int r = lane & 15, q = lane >> 4;        // MFMA layout
   const int lr = lane >> 2, lp = lane & 3;       // load layout: row, piece
   const uint32_t wslot = 16u * (uint32_t)(16 * lp + ((lr + 4 * lp) & 15));
@@ -468,6 +504,7 @@ __global__ __launch_bounds__(k16Waves * 64, 1) void gemv16_kernel(
   float mul = 0.0f;
   if (DQ && lane == 0)
     mul = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(mean, 4u), 0u, 0, 0));
+  const float dmv = DYN ? dyn_map_value(t) : 0.0f;
 
   const rsrc_t rw = make_rsrc(packed, (uint32_t)N * rowK2);
   const uint32_t nblocks = (uint32_t)N * nkb;
@@ -481,7 +518,7 @@ __global__ __launch_bounds__(k16Waves * 64, 1) void gemv16_kernel(
   // 4) of the slice) and the raw scale of block x % 4 of that row.
   struct Item {
     u32x4_t w[2];
-    uint32_t qc;   // int8 code(s): kScaleDqRow the row's four codes
+    uint32_t qc;   // code byte(s): the row modes hold the row's four codes
     float gs;      // group scale, or the fp32 absmax
   };
   struct Set {
@@ -510,7 +547,7 @@ __global__ __launch_bounds__(k16Waves * 64, 1) void gemv16_kernel(
 #pragma unroll
       for (int h = 0; h < 2; ++h) it.w[h] = __builtin_amdgcn_raw_buffer_load_b128(rw, wo + 64u * h, 0, 2);
       const uint32_t blk = row * nkb + 4u * (uint32_t)u;   // the slice's first block in the row
-      if (SM == kScaleDqRow) {
+      if (scale_row(SM)) {
         it.qc = __builtin_amdgcn_raw_buffer_load_b32(rq, in ? blk : kFar, 0, 0);
         it.gs = __builtin_bit_cast(
             float, __builtin_amdgcn_raw_buffer_load_b32(rg, in ? (blk >> 8) * 4u : kFar, 0, 0));
@@ -533,8 +570,13 @@ __global__ __launch_bounds__(k16Waves * 64, 1) void gemv16_kernel(
   // Scale of block x % 4 of row x / 4 (load layout).
   auto load_scale = [&](const Item& it, float mu) {
     if (!DQ) return it.gs;
-    const int code = SM == kScaleDqRow ? __builtin_amdgcn_sbfe((int)it.qc, lp * 8, 8)
-                                       : (int)(int8_t)(uint8_t)it.qc;
+    if (DYN) {
+      const uint32_t code = scale_row(SM) ? __builtin_amdgcn_ubfe(it.qc, lp * 8, 8) : it.qc & 0xffu;
+      const float prod = *(const float*)(dmap + code * 4u) * it.gs;
+      return prod + mu;
+    }
+    const int code = scale_row(SM) ? __builtin_amdgcn_sbfe((int)it.qc, lp * 8, 8)
+                                   : (int)(int8_t)(uint8_t)it.qc;
     const float prod = (float)code * dq_step_normal(it.gs);
     return prod + mu;
   };
@@ -603,6 +645,7 @@ __global__ __launch_bounds__(k16Waves * 64, 1) void gemv16_kernel(
         const uint32_t v = pack16x2<F16>(level_lookup(lvl, b >> 4), level_lookup(lvl, b & 15u));
         *(uint4*)(tab + b * 256u + ((uint32_t)e % (kCopies / 4)) * 16u) = make_uint4(v, v, v, v);
       }
+      if (DYN && t < 256) *(float*)(dmap + t * 4) = dmv;
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
@@ -715,6 +758,12 @@ hipError_t launch_gemv16(int grid, const uint16_t* x, int64_t ldx, const uint8_t
   const int per_wg = (ngroups + grid - 1) / grid;
   const int nb = multi ? 1 : (per_wg >= 3 ? 4 : per_wg);
   const bool rowq = dq && ((K >> 6) % 4 == 0) && ((uintptr_t)absmax & 3u) == 0;
+  if (dq == kDqDynamic && rowq)
+    return launch_gemv16_sm<kScaleDynRow, F16>(grid, nb, multi, x, ldx, packed, absmax, absmax2,
+                                               mean, M, N, K, y, ldy, lv, stream);
+  if (dq == kDqDynamic)
+    return launch_gemv16_sm<kScaleDynLane, F16>(grid, nb, multi, x, ldx, packed, absmax, absmax2,
+                                                mean, M, N, K, y, ldy, lv, stream);
   if (rowq)
     return launch_gemv16_sm<kScaleDqRow, F16>(grid, nb, multi, x, ldx, packed, absmax, absmax2,
                                               mean, M, N, K, y, ldy, lv, stream);
@@ -799,18 +848,23 @@ hipError_t launch_k(const Plan& p, const uint16_t* x, int64_t ldx, const uint8_t
                     const void* absmax, const float* absmax2, const float* mean, int dq,
                     int mvalid, int N, int K, uint16_t* y, int64_t ldy, const LevelTable& lv,
                     hipStream_t stream) {
-  if (!dq)
-    hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, kScaleF32, F16>), dim3(p.grid), dim3(kThreads), 0,
-                       stream, x, ldx, packed, absmax, absmax2, mean, mvalid, N, K, y, ldy, p.twl,
-                       p.xlds, lv);
-  else if ((K >> 6) <= 256 && (K >> 6) % 4 == 0 && ((uintptr_t)absmax & 3u) == 0)
-    hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, kScaleDqRow, F16>), dim3(p.grid), dim3(kThreads),
-                       0, stream, x, ldx, packed, absmax, absmax2, mean, mvalid, N, K, y, ldy,
+  const bool rowq = (K >> 6) <= 256 && (K >> 6) % 4 == 0 && ((uintptr_t)absmax & 3u) == 0;
+  int sm = kScaleF32;
+  if (dq == kDqDynamic)
+    sm = rowq ? kScaleDynRow : kScaleDynLane;
+  else if (dq)
+    sm = rowq ? kScaleDqRow : kScaleDqLane;
+#define BNBX_GEMV_SM(SMV)                                                                      \
+  if (sm == SMV)                                                                               \
+    hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, SMV, F16>), dim3(p.grid), dim3(kThreads), 0,   \
+                       stream, x, ldx, packed, absmax, absmax2, mean, mvalid, N, K, y, ldy,     \
                        p.twl, p.xlds, lv);
-  else
-    hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, kScaleDqLane, F16>), dim3(p.grid), dim3(kThreads),
-                       0, stream, x, ldx, packed, absmax, absmax2, mean, mvalid, N, K, y, ldy,
-                       p.twl, p.xlds, lv);
+  BNBX_GEMV_SM(kScaleF32)
+  BNBX_GEMV_SM(kScaleDqLane)
+  BNBX_GEMV_SM(kScaleDqRow)
+  BNBX_GEMV_SM(kScaleDynLane)
+  BNBX_GEMV_SM(kScaleDynRow)
+#undef BNBX_GEMV_SM
   return hipGetLastError();
 }
 

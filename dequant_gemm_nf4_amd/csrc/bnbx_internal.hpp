@@ -34,6 +34,57 @@ struct LevelTable {
   float level[16];       // level of each code, binary32 (NF4: ascending)
 };
 
+// Second-level code maps (bnbx_nf4_state.double_quant): linear int8 codes,
+// or byte codes into the dynamic 8-bit map.
+constexpr int kDqNone = 0;
+constexpr int kDqLinear = 1;
+constexpr int kDqDynamic = 2;
+
+// The dynamic 8-bit map.  The csdn.net bitsandbytes feature page (sec. 1,
+// item 5) lists dynamic 8-bit quantization among the library's types and
+// the mlqm.cn article (sec. 3.3) quantizes the fp32 block scales a second
+// time; no page defines the map.  It is read as dynamic tree quantization
+// (Dettmers, 8-bit approximations for parallelism in deep learning, 2016):
+// after the sign bit, E zero bits give the decimal exponent 10^-E, a one
+// bit ends them, and the remaining 6 - E bits f pick one of 2^(6-E) equal
+// bins of [0.1, 1], valued at its midpoint: |v| = 10^-E (0.1 + 0.9 (f +
+// 1/2) / 2^(6-E)), E = 0..6; with 0 and 1 that makes 256 values.  Each is
+// formed in binary64 and rounded once to binary32.  In ascending order the
+// code of a value is its index: 0..126 negative, 127 zero, 128..254
+// positive, 255 one.  The decades are disjoint, so the positive values
+// ascend with the decade (E from 6 down to 0) and then with f.
+//
+// mid[i] is the midpoint of v[i] and v[i+1], exact in binary64 (neighbours
+// are within a factor of 10 of each other, or one of them is 0).  The code
+// of a binary32 t is #{i : t > mid[i]}: the nearest value, an exact tie
+// going to the lower code.
+struct DynMap {
+  float v[256];
+  double mid[255];
+};
+constexpr DynMap make_dyn_map() {
+  // 10^-E as the binary64 nearest each power (decimal literals round once)
+  const double p10[7] = {1.0, 0.1, 0.01, 0.001, 1e-4, 1e-5, 1e-6};
+  DynMap m{};
+  int i = 128;
+  for (int e = 6; e >= 0; --e) {
+    const int nf = 1 << (6 - e);
+    for (int f = 0; f < nf; ++f) {
+      const double mag = p10[e] * (0.1 + 0.9 * (f + 0.5) / nf);
+      m.v[i] = (float)mag;
+      m.v[254 - i] = -(float)mag;
+      ++i;
+    }
+  }
+  m.v[127] = 0.0f;
+  m.v[255] = 1.0f;
+  for (int k = 0; k < 255; ++k) m.mid[k] = ((double)m.v[k] + (double)m.v[k + 1]) / 2.0;
+  return m;
+}
+constexpr int kDynZeroCode = 127;
+// The device copy (constant memory, one per translation unit).
+static __constant__ DynMap kDynMapDev = make_dyn_map();
+
 // The one-time host tables (built on first use, immutable afterwards).
 const float* levels_f32(int quant_type);   // float[16], by code
 const EncodeTable& encode_table(int quant_type);
@@ -59,9 +110,10 @@ inline size_t dq_workspace_bytes(int64_t nb) {
 int quantize_grid(int64_t n);
 hipError_t launch_quantize(const uint16_t* w, uint8_t* packed, int64_t n, float* absmax_f32,
                            unsigned long long* slots, int quant_type, hipStream_t stream);
+// `dq`: kDqLinear (int8 codes) or kDqDynamic (codes into the dynamic map).
 hipError_t launch_double_quant(const float* absmax_f32, const unsigned long long* slots,
-                               int nslots, int64_t nb, int8_t* q, float* absmax2, float* mean,
-                               hipStream_t stream);
+                               int nslots, int64_t nb, uint8_t* q, float* absmax2, float* mean,
+                               int dq, hipStream_t stream);
 // `f16`: the 16-bit compute type is IEEE binary16 instead of bfloat16.
 hipError_t launch_dequantize(const uint8_t* packed, int64_t n, const void* absmax,
                              const float* absmax2, const float* mean, int double_quant,

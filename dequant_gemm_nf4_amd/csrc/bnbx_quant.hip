@@ -273,11 +273,20 @@ __device__ float exact_mean(const unsigned long long* __restrict__ slots, int ns
 // the mean is formed, so that one memory latency covers both.
 constexpr int kDqGroups = 4;
 
+// Second level of the double quantization (mlqm.cn article, sec. 3.3): the
+// exact mean, the group scales s_g = max |a_b - mean|, and per block the code
+// of t = fl32((a_b - mean) / s_g): linear, round-half-even(fl32(t * 127)) as
+// int8; DYN, the index of the nearest value of the dynamic 8-bit map (exact
+// ties to the lower index), found by binary search over the exact binary64
+// midpoints of neighbouring values.  A group with s_g = 0 stores the code of
+// the value 0.
+template <bool DYN>
 __global__ __launch_bounds__(256) void double_quant_kernel(
     const float* __restrict__ a, const unsigned long long* __restrict__ slots, int nslots,
-    int64_t nb, int8_t* __restrict__ q, float* __restrict__ s_out, float* __restrict__ mean_out) {
+    int64_t nb, uint8_t* __restrict__ q, float* __restrict__ s_out, float* __restrict__ mean_out) {
   __shared__ unsigned long long digits[kSumDigits];
   __shared__ float red[kDqGroups][4];
+  __shared__ double mids[DYN ? 256 : 1];
   const int tid = threadIdx.x;
   const int64_t g0 = (int64_t)blockIdx.x * kDqGroups;
   float v[kDqGroups];
@@ -286,6 +295,7 @@ __global__ __launch_bounds__(256) void double_quant_kernel(
     const int64_t b = (g0 + i) * kGroup + tid;
     v[i] = b < nb ? a[b] : 0.0f;
   }
+  if (DYN && tid < 255) mids[tid] = kDynMapDev.mid[tid];   // visible after exact_mean's barriers
   const float mu = exact_mean(slots, nslots, nb, digits);
   if (blockIdx.x == 0 && tid == 0) *mean_out = mu;
   const int64_t ng = (nb + kGroup - 1) / kGroup;
@@ -304,13 +314,22 @@ __global__ __launch_bounds__(256) void double_quant_kernel(
     if (g >= ng) break;   // uniform
     const int64_t b = g * kGroup + tid;
     const float s = fmaxf(fmaxf(red[i][0], red[i][1]), fmaxf(red[i][2], red[i][3]));
-    int qv = 0;
+    int qv = DYN ? kDynZeroCode : 0;
     if (s > 0.0f) {
       const float t = c[i] / s;       // correctly rounded binary32 division
-      const float u = t * 127.0f;
-      qv = (int)rintf(u);             // round half to even
+      if (DYN) {
+        // #{k : t > mid[k]} over the 255 ascending midpoints
+        int idx = 0;
+#pragma unroll
+        for (int step = 128; step >= 1; step >>= 1)
+          if ((double)t > mids[idx + step - 1]) idx += step;
+        qv = idx;
+      } else {
+        const float u = t * 127.0f;
+        qv = (int)rintf(u);           // round half to even
+      }
     }
-    if (b < nb) q[b] = (int8_t)qv;
+    if (b < nb) q[b] = (uint8_t)qv;
     if (tid == 0) s_out[g] = s;
   }
 }
@@ -353,13 +372,17 @@ hipError_t launch_quantize(const uint16_t* w, uint8_t* packed, int64_t n, float*
 }
 
 hipError_t launch_double_quant(const float* absmax_f32, const unsigned long long* slots,
-                               int nslots, int64_t nb, int8_t* q, float* absmax2, float* mean,
-                               hipStream_t stream) {
+                               int nslots, int64_t nb, uint8_t* q, float* absmax2, float* mean,
+                               int dq, hipStream_t stream) {
   const int64_t ng = (nb + kGroup - 1) / kGroup;
   const int64_t grid = (ng + kDqGroups - 1) / kDqGroups;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(double_quant_kernel, dim3((unsigned)grid), dim3(256), 0, stream, absmax_f32,
-                     slots, nslots, nb, q, absmax2, mean);
+  if (dq == kDqDynamic)
+    hipLaunchKernelGGL(double_quant_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream,
+                       absmax_f32, slots, nslots, nb, q, absmax2, mean);
+  else
+    hipLaunchKernelGGL(double_quant_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream,
+                       absmax_f32, slots, nslots, nb, q, absmax2, mean);
   return hipGetLastError();
 }
 

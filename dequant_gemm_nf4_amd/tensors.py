@@ -14,6 +14,8 @@ from . import (Nf4State, bnbx_dequantize_nf4, bnbx_gemm_nf4, bnbx_gemm_nf4_dx, b
 BLOCKSIZE = 64
 GROUP = 256
 QUANT_TYPES = {"nf4": 0, "fp4": 1}
+# second-level maps of the block scales (bnbx_nf4_state.double_quant)
+DQ_MAPS = {"linear": 1, "dynamic": 2}
 DTYPES = {torch.bfloat16: 0, torch.float16: 1}
 
 
@@ -21,7 +23,9 @@ DTYPES = {torch.bfloat16: 0, torch.float16: 1}
 class QuantizedWeight:
     """Device buffers of one 4-bit tensor plus its C descriptor.  ``dtype``
     is the compute dtype (bf16 or fp16) of its dequantized values and of the
-    activations it multiplies."""
+    activations it multiplies; ``dq_map`` the second-level map of the block
+    scales with double quant ("linear": int8 codes, "dynamic": uint8 codes
+    into the dynamic 8-bit map)."""
 
     n: int
     shape: tuple
@@ -32,11 +36,13 @@ class QuantizedWeight:
     absmax_mean: torch.Tensor | None  # float32 [1]
     quant_type: str = "nf4"
     dtype: torch.dtype = torch.bfloat16
+    dq_map: str = "linear"
 
     @property
     def state(self) -> Nf4State:
         return Nf4State(
-            n=self.n, blocksize=BLOCKSIZE, double_quant=int(self.double_quant),
+            n=self.n, blocksize=BLOCKSIZE,
+            double_quant=DQ_MAPS[self.dq_map] if self.double_quant else 0,
             quant_type=QUANT_TYPES[self.quant_type], compute_dtype=DTYPES[self.dtype],
             absmax=self.absmax.data_ptr(),
             absmax2=self.absmax2.data_ptr() if self.absmax2 is not None else None,
@@ -44,7 +50,7 @@ class QuantizedWeight:
 
 
 def empty_quantized(shape, double_quant: bool, device="cuda", quant_type: str = "nf4",
-                    dtype: torch.dtype = torch.bfloat16) -> QuantizedWeight:
+                    dtype: torch.dtype = torch.bfloat16, dq_map: str = "linear") -> QuantizedWeight:
     n = 1
     for s in shape:
         n *= int(s)
@@ -52,14 +58,17 @@ def empty_quantized(shape, double_quant: bool, device="cuda", quant_type: str = 
     ng = -(-nb // GROUP)
     packed = torch.empty(n // 2, dtype=torch.uint8, device=device)
     if double_quant:
-        absmax = torch.empty(nb, dtype=torch.int8, device=device)
+        absmax = torch.empty(nb, dtype=torch.uint8 if dq_map == "dynamic" else torch.int8,
+                             device=device)
         absmax2 = torch.empty(ng, dtype=torch.float32, device=device)
         mean = torch.empty(1, dtype=torch.float32, device=device)
     else:
         absmax = torch.empty(nb, dtype=torch.float32, device=device)
         absmax2 = mean = None
+    if dq_map not in DQ_MAPS:
+        raise ValueError(f"unknown second-level map {dq_map!r}")
     return QuantizedWeight(n, tuple(shape), double_quant, packed, absmax, absmax2, mean,
-                           quant_type, dtype)
+                           quant_type, dtype, dq_map)
 
 
 def workspace_for(n: int, double_quant: bool, device="cuda") -> torch.Tensor | None:
@@ -71,12 +80,14 @@ def workspace_for(n: int, double_quant: bool, device="cuda") -> torch.Tensor | N
 
 def quantize(w: torch.Tensor, double_quant: bool, out: QuantizedWeight | None = None,
              workspace: torch.Tensor | None = None, stream=None, quant_type: str = "nf4",
-             dtype: torch.dtype = torch.bfloat16) -> QuantizedWeight:
+             dtype: torch.dtype = torch.bfloat16, dq_map: str = "linear") -> QuantizedWeight:
     """bnbx_quantize_nf4 on a bf16 tensor (any shape, contiguous); ``dtype``
-    is the compute dtype recorded for later dequantize / matmul calls."""
+    is the compute dtype recorded for later dequantize / matmul calls,
+    ``dq_map`` the second-level map with double quant (ignored with ``out``,
+    which carries its own)."""
     assert w.dtype == torch.bfloat16 and w.is_contiguous()
     q = out if out is not None else empty_quantized(w.shape, double_quant, w.device, quant_type,
-                                                    dtype)
+                                                    dtype, dq_map)
     ws = workspace if workspace is not None else workspace_for(q.n, double_quant, w.device)
     bnbx_quantize_nf4(w, q.packed, q.state, ws, 0 if ws is None else ws.numel(), stream)
     return q

@@ -12,7 +12,9 @@ arithmetic runs in the library's kernels (GEMV for at most 16 rows of X,
 GEMM otherwise) on the current stream.  Its backward is
 ``torch.ops.bnbx.linear4bit_dx`` (dX = dY . W_hat, the input gradient; the
 4-bit weights are frozen, as the base layer under QLoRA in the pomoai.com
-overview, and get none).  Nothing here computes.
+overview, and get none).  The second-level map of double quantization
+follows the dtype of ``absmax``: int8 codes are the linear map, uint8 codes
+the dynamic 8-bit map.  Nothing here computes.
 """
 
 from __future__ import annotations
@@ -26,13 +28,17 @@ from . import tensors as T
 _DTYPES = (torch.bfloat16, torch.float16)
 
 
+def _dq_map(absmax: torch.Tensor) -> str:
+    return "dynamic" if absmax.dtype == torch.uint8 else "linear"
+
+
 def _state(x: torch.Tensor, packed, absmax, absmax2, absmax_mean, out_features: int,
            quant_type: str) -> T.QuantizedWeight:
     K = x.shape[-1]
     return T.QuantizedWeight(n=out_features * K, shape=(out_features, K),
                              double_quant=absmax2 is not None, packed=packed, absmax=absmax,
                              absmax2=absmax2, absmax_mean=absmax_mean, quant_type=quant_type,
-                             dtype=x.dtype)
+                             dtype=x.dtype, dq_map=_dq_map(absmax))
 
 
 @torch.library.custom_op("bnbx::linear4bit", mutates_args=())
@@ -77,7 +83,7 @@ def linear4bit_dx(dy: torch.Tensor, packed: torch.Tensor, absmax: torch.Tensor,
         q = T.QuantizedWeight(n=N * in_features, shape=(N, in_features),
                               double_quant=absmax2 is not None, packed=packed, absmax=absmax,
                               absmax2=absmax2, absmax_mean=absmax_mean, quant_type=quant_type,
-                              dtype=dy.dtype)
+                              dtype=dy.dtype, dq_map=_dq_map(absmax))
         T.gemm_dx(dy2, q, out=dx)
     return dx.reshape(*dy.shape[:-1], in_features)
 
@@ -108,17 +114,20 @@ linear4bit.register_autograd(_backward, setup_context=_setup_context)
 
 class Linear4bit(torch.nn.Module):
     """A bias-free ``nn.Linear(in_features, out_features)`` whose weight is
-    held as 4-bit codes (NF4 or FP4, blocks of 64, optional double quant) and
-    whose forward runs ``torch.ops.bnbx.linear4bit`` in ``compute_dtype``.
+    held as 4-bit codes (NF4 or FP4, blocks of 64, optional double quant
+    with the linear or the dynamic second-level map) and whose forward runs
+    ``torch.ops.bnbx.linear4bit`` in ``compute_dtype``.
     ``load_weight`` quantizes a bf16 [out, in] weight on the device.  The
     input gradient (backward) needs out_features % 64 == 0."""
 
     def __init__(self, in_features: int, out_features: int, quant_type: str = "nf4",
                  double_quant: bool = True, compute_dtype: torch.dtype = torch.bfloat16,
-                 device="cuda"):
+                 device="cuda", dq_map: str = "linear"):
         super().__init__()
         if quant_type not in T.QUANT_TYPES:
             raise ValueError(f"quant_type must be one of {sorted(T.QUANT_TYPES)}")
+        if dq_map not in T.DQ_MAPS:
+            raise ValueError(f"dq_map must be one of {sorted(T.DQ_MAPS)}")
         if compute_dtype not in _DTYPES:
             raise ValueError("compute_dtype must be torch.bfloat16 or torch.float16")
         if in_features % 64 != 0:
@@ -126,8 +135,9 @@ class Linear4bit(torch.nn.Module):
         self.in_features, self.out_features = in_features, out_features
         self.quant_type, self.double_quant, self.compute_dtype = quant_type, double_quant, \
             compute_dtype
+        self.dq_map = dq_map if double_quant else "linear"
         q = T.empty_quantized((out_features, in_features), double_quant, device, quant_type,
-                              compute_dtype)
+                              compute_dtype, self.dq_map)
         self.register_buffer("packed", q.packed)
         self.register_buffer("absmax", q.absmax)
         self.register_buffer("absmax2", q.absmax2)
@@ -137,7 +147,7 @@ class Linear4bit(torch.nn.Module):
         return T.QuantizedWeight(self.in_features * self.out_features,
                                  (self.out_features, self.in_features), self.double_quant,
                                  self.packed, self.absmax, self.absmax2, self.absmax_mean,
-                                 self.quant_type, self.compute_dtype)
+                                 self.quant_type, self.compute_dtype, self.dq_map)
 
     @torch.no_grad()
     def load_weight(self, w: torch.Tensor) -> "Linear4bit":
@@ -168,4 +178,5 @@ class Linear4bit(torch.nn.Module):
     def extra_repr(self) -> str:
         return (f"in_features={self.in_features}, out_features={self.out_features}, "
                 f"quant_type={self.quant_type}, double_quant={self.double_quant}, "
+                f"dq_map={self.dq_map}, "
                 f"compute_dtype={self.compute_dtype}")

@@ -45,13 +45,19 @@
  *   Without double quant:
  *     absmax   float[nb]  a_b = max |w| over block b.
  *   With double quant (second-level groups of 256 consecutive blocks,
- *   ng = ceil(nb / 256)):
- *     absmax      int8_t[nb]  q_b, the block scale a_b minus the mean, in
- *                             units of s_g / 127, rounded half-even
+ *   ng = ceil(nb / 256)), t_b = fl32((a_b - mean) / s_g):
+ *     absmax      linear map (double_quant 1): int8_t[nb], q_b =
+ *                 round-half-even(fl32(t_b * 127)), the block scale minus
+ *                 the mean in units of s_g / 127;
+ *                 dynamic map (double_quant 2): uint8_t[nb], q_b = the code
+ *                 of the value of the dynamic 8-bit map nearest t_b, exact
+ *                 ties to the lower code (bnbx_dynamic_map);
+ *                 a group with s_g = 0 stores the code of 0 (0, or 127)
  *     absmax2     float[ng]   s_g = max |a_b - mean| over group g
  *     absmax_mean float[1]    mean = fl32(fl64(sum_b a_b) / nb), the sum exact
- *   Dequantized scale: without DQ a_b; with DQ
- *     fl32(fl32(q_b * fl32(s_g / 127)) + mean).
+ *   Dequantized scale: without DQ a_b; with the linear map
+ *     fl32(fl32(q_b * fl32(s_g / 127)) + mean); with the dynamic map
+ *     fl32(fl32(map[q_b] * s_g) + mean).
  *   Code of element j: x = fl32(w_j * fl32(1 / a_b)) (for a nonzero a_b
  *   below 2^-100, w_j and a_b are first multiplied by 2^64, exactly, so the
  *   reciprocal stays finite); s = #{i : x >= T_i}
@@ -97,6 +103,8 @@ typedef enum {
 
 /* 4-bit quant types (bnbx_nf4_state.quant_type). */
 enum { BNBX_QUANT_NF4 = 0, BNBX_QUANT_FP4 = 1 };
+/* Second-level maps of the block scales (bnbx_nf4_state.double_quant). */
+enum { BNBX_DQ_NONE = 0, BNBX_DQ_LINEAR = 1, BNBX_DQ_DYNAMIC = 2 };
 /* 16-bit compute types (bnbx_nf4_state.compute_dtype). */
 enum { BNBX_DTYPE_BF16 = 0, BNBX_DTYPE_F16 = 1 };
 
@@ -105,12 +113,16 @@ enum { BNBX_DTYPE_BF16 = 0, BNBX_DTYPE_F16 = 1 };
 typedef struct {
   int64_t n;             /* number of weights, even, >= 2                      */
   int32_t blocksize;     /* weights per block; only 64 is supported            */
-  int32_t double_quant;  /* 0: absmax is float[nb]; 1: int8 + absmax2 + mean  */
+  int32_t double_quant;  /* BNBX_DQ_NONE (0): absmax is float[nb];
+                            BNBX_DQ_LINEAR (1): int8 codes + absmax2 + mean;
+                            BNBX_DQ_DYNAMIC (2): uint8 codes into the dynamic
+                            8-bit map + absmax2 + mean                        */
   int32_t quant_type;    /* BNBX_QUANT_NF4 (0) or BNBX_QUANT_FP4 (1)            */
   int32_t compute_dtype; /* BNBX_DTYPE_BF16 (0) or BNBX_DTYPE_F16 (1): the type
                             of dequantized weights and of X and Y; the quantize
                             input is always bf16 and ignores it               */
-  void*   absmax;        /* device: float[nb] (dq=0) or int8_t[nb] (dq=1)      */
+  void*   absmax;        /* device: float[nb] (dq=0), int8_t[nb] (dq=1) or
+                            uint8_t[nb] (dq=2)                                */
   float*  absmax2;       /* device: float[ng] (dq=1), else NULL                */
   float*  absmax_mean;   /* device: float[1]  (dq=1), else NULL                */
 } bnbx_nf4_state;
@@ -132,6 +144,19 @@ BNBX_API int bnbx_nf4_codebook(float levels_host[16]);
  * quant type offered beside nf4.  Host-only, synchronous.
  * Returns BNBX_E_INVAL if levels_host is NULL. */
 BNBX_API int bnbx_fp4_codebook(float levels_host[16]);
+
+/* The 256 values of the dynamic 8-bit map, ascending (the value of code c
+ * is values_host[c]), into host memory.  The csdn.net bitsandbytes feature
+ * page (sec. 1, item 5) lists dynamic 8-bit quantization among the library's
+ * types and the mlqm.cn article (sec. 3.3) quantizes the fp32 block scales a
+ * second time; no page defines the map.  It is read as dynamic tree
+ * quantization (Dettmers, 2016): a sign bit, then E zero bits for the decimal
+ * exponent 10^-E, a one bit, and 6 - E bits f of a linear fraction, valued at
+ * the bin midpoint: |v| = 10^-E (0.1 + 0.9 (f + 1/2) / 2^(6-E)), E = 0..6,
+ * formed in binary64 and rounded once to binary32; with 0 and 1 that makes
+ * 256 values: codes 0-126 negative, 127 zero, 128-254 positive, 255 one.
+ * Host-only, synchronous.  Returns BNBX_E_INVAL if values_host is NULL. */
+BNBX_API int bnbx_dynamic_map(float values_host[256]);
 
 /* Bytes of device workspace bnbx_quantize_nf4 needs for (n, blocksize,
  * double_quant); 0 without double quant.  Returns 0 for invalid arguments. */

@@ -27,11 +27,13 @@ def host_bits(t: torch.Tensor) -> np.ndarray:
 
 
 def gpu_quantize(w_bits: np.ndarray, shape, dq: bool, quant_type: str = "nf4",
-                 dtype: str = "bf16") -> dict:
+                 dtype: str = "bf16", dq_map: str = "linear") -> dict:
     w = dev_bf16(w_bits, shape)
-    q = T.quantize(w, dq, quant_type=quant_type, dtype=TORCH_DTYPE[dtype])
+    q = T.quantize(w, dq, quant_type=quant_type, dtype=TORCH_DTYPE[dtype], dq_map=dq_map)
     torch.cuda.synchronize()
     out = {"packed": q.packed.cpu().numpy(), "double_quant": dq, "n": q.n, "blocksize": 64}
+    if dq:
+        out["dq_map"] = dq_map
     if dq:
         out["absmax"] = q.absmax.cpu().numpy()
         out["absmax2"] = q.absmax2.cpu().numpy()
@@ -46,11 +48,13 @@ def upload_state(ostate: dict, shape, dtype: str = "bf16") -> T.QuantizedWeight:
     """Device copy of a quant state the oracle produced (its quant type; the
     given compute dtype)."""
     dq = ostate["double_quant"]
+    dq_map = ostate.get("dq_map", "linear") if dq else "linear"
     q = T.empty_quantized(shape, dq, quant_type=ostate.get("quant_type", "nf4"),
-                          dtype=TORCH_DTYPE[dtype])
+                          dtype=TORCH_DTYPE[dtype], dq_map=dq_map)
     q.packed.copy_(torch.from_numpy(np.ascontiguousarray(ostate["packed"])))
     if dq:
-        q.absmax.copy_(torch.from_numpy(np.ascontiguousarray(ostate["absmax"], np.int8)))
+        code_type = np.uint8 if dq_map == "dynamic" else np.int8
+        q.absmax.copy_(torch.from_numpy(np.ascontiguousarray(ostate["absmax"], code_type)))
         q.absmax2.copy_(torch.from_numpy(np.ascontiguousarray(ostate["absmax2"], np.float32)))
         q.absmax_mean.copy_(torch.tensor([float(ostate["absmax_mean"])], dtype=torch.float32))
     else:

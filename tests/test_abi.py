@@ -30,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 13
+    assert len(declared) == 14
     assert sorted(bnbx.EXPORTED_SYMBOLS) == declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -48,6 +48,14 @@ def test_codebook_equals_oracle_bit_for_bit():
 def test_fp4_codebook_equals_oracle_bit_for_bit():
     ours = np.array(bnbx.bnbx_fp4_codebook(), dtype=np.float32)
     assert np.array_equal(ours.view(np.uint32), oracle.fp4_codebook().view(np.uint32))
+
+
+def test_dynamic_map_equals_oracle_bit_for_bit():
+    """The library's compile-time dynamic 8-bit map against the oracle's
+    (two independent constructions of the same definition)."""
+    ours = np.array(bnbx.bnbx_dynamic_map(), dtype=np.float32)
+    assert ours.shape == (256,)
+    assert np.array_equal(ours.view(np.uint32), oracle.dynamic_map().view(np.uint32))
 
 
 def test_status_strings():
@@ -116,7 +124,7 @@ def test_quantize_rejects(case, expect):
     elif case == "blocksize":
         st = state(n, blocksize=128)
     elif case == "dq_flag":
-        st = state(n, dq=2)
+        st = state(n, dq=3)
     elif case == "quant_type":
         st = state(n, qt=2)
     elif case == "compute_dtype":

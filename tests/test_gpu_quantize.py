@@ -13,9 +13,9 @@ from tests.gpu_helpers import assert_state_equal, gpu_quantize, host_bits, uploa
 pytestmark = pytest.mark.gpu
 
 
-def check_quantize(bits, shape, dq):
-    ref = oracle.quantize(bits, dq)
-    got = gpu_quantize(bits, shape, dq)
+def check_quantize(bits, shape, dq, dq_map="linear"):
+    ref = oracle.quantize(bits, dq, dq_map=dq_map)
+    got = gpu_quantize(bits, shape, dq, dq_map=dq_map)
     assert_state_equal(got, ref)
     return got, ref
 
@@ -111,8 +111,8 @@ def test_quantize_special_blocks():
         blocks.append(blk)
     f = np.concatenate(blocks)
     bits = oracle.f32_to_bf16_bits(f)
-    for dq in (False, True):
-        got, ref = check_quantize(bits, bits.shape, dq)
+    for dq, dq_map in ((False, "linear"), (True, "linear"), (True, "dynamic")):
+        got, ref = check_quantize(bits, bits.shape, dq, dq_map)
         assert np.all(ref["codes"][:64] == 7)
         assert np.array_equal(ref["codes"][64 + 1:64 + 16], np.arange(15))
         assert np.array_equal(ref["codes"][64 + 16:64 + 31], np.arange(1, 16))

@@ -17,22 +17,24 @@ pytestmark = pytest.mark.gpu
 TOL = 5e-3
 
 
-def make(N, K, qt, dt, dq=True, seed=9900):
+def make(N, K, qt, dt, dq=True, seed=9900, dq_map="linear"):
     w = synth.normal_bf16((N, K), 0.02, seed)
-    m = Linear4bit(K, N, quant_type=qt, double_quant=dq, compute_dtype=TORCH_DTYPE[dt])
+    m = Linear4bit(K, N, quant_type=qt, double_quant=dq, compute_dtype=TORCH_DTYPE[dt],
+                   dq_map=dq_map)
     m.load_weight(dev_bf16(w, (N, K)))
     torch.cuda.synchronize()
     return w, m
 
 
 @pytest.mark.parametrize("qt,dt", [("nf4", "bf16"), ("fp4", "f16")])
-@pytest.mark.parametrize("dq", [False, True])
+@pytest.mark.parametrize("dq,dq_map", [(False, "linear"), (True, "linear"), (True, "dynamic")])
 @pytest.mark.parametrize("lead", [(1,), (5,), (2, 32)])
-def test_module_against_oracle(qt, dt, dq, lead):
+def test_module_against_oracle(qt, dt, dq, dq_map, lead):
     N, K = 384, 1024
-    w, m = make(N, K, qt, dt, dq)
-    ref = oracle.quantize(w, dq, quant_type=qt)
+    w, m = make(N, K, qt, dt, dq, dq_map=dq_map)
+    ref = oracle.quantize(w, dq, quant_type=qt, dq_map=dq_map)
     assert np.array_equal(m.packed.cpu().numpy(), ref["packed"])
+    assert np.array_equal(m.absmax.cpu().numpy(), ref["absmax"])
     M = int(np.prod(lead))
     xb = synth.normal_16((M, K), 1.0, 9901 + M, dt)
     x = dev_bf16(xb, (*lead, K), dt)
@@ -104,13 +106,14 @@ def test_captured_graph_replays_match_eager():
         assert torch.equal(y, eager)
 
 
-@pytest.mark.parametrize("qt,dt", [("nf4", "bf16"), ("fp4", "f16")])
-def test_backward_against_oracle(qt, dt):
+@pytest.mark.parametrize("qt,dt,dq_map", [("nf4", "bf16", "linear"), ("fp4", "f16", "linear"),
+                                         ("nf4", "bf16", "dynamic")])
+def test_backward_against_oracle(qt, dt, dq_map):
     """x.grad of sum(g * Linear4bit(x)) is g . W_hat (the bnbx_gemm_nf4_dx
     kernel through the op's autograd), against the oracle."""
     N, K, M = 256, 512, 48
-    w, m = make(N, K, qt, dt, True, seed=9940)
-    ref = oracle.quantize(w, True, quant_type=qt)
+    w, m = make(N, K, qt, dt, True, seed=9940, dq_map=dq_map)
+    ref = oracle.quantize(w, True, quant_type=qt, dq_map=dq_map)
     x = dev_bf16(synth.normal_16((M, K), 1.0, 9941, dt), (M, K), dt).requires_grad_(True)
     gb = synth.normal_16((M, N), 1.0, 9942, dt)
     m(x).backward(dev_bf16(gb, (M, N), dt))
