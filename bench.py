@@ -83,37 +83,109 @@ def recorded_gemv_traffic():
         return None
 
 
-def cpu_baseline(budget_s: float = 12.0):
-    """The oracle as it stands, on one decode layer (4096x4096, double quant):
-    fp64 reference GEMV = dequantize + binary64 matmul, repeated until the
-    budget is spent.  Reported in the GEMV metric's unit."""
+def cpu_threads():
+    """(CPUs this process may run on, BLAS threads of the all-core mode): the
+    affinity set, capped by OMP_NUM_THREADS where the host sets a CPU share."""
+    avail = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS")
+    return avail, min(avail, int(share)) if share and share.isdigit() else avail
+
+
+def cpu_baseline(gemv_reps: int = 3):
+    """The oracle as it stands, timed on the host in two modes: 1 BLAS thread
+    and all cores (NumPy's elementwise work, most of the oracle's time, runs
+    on one thread in both).  Each configuration of the GPU workload is timed
+    on a bounded sample, in its own unit:
+
+    * decode GEMV M=1 on the three decode shapes (double quant; GB/s of the
+      GEMV's algorithmic bytes): fp64 reference GEMV = dequantize + binary64
+      matmul, ``gemv_reps`` times per shape; the headline ``value`` is its
+      all-core rate over the three shapes, the same weighting as the GPU
+      ``value``;
+    * batched decode M=16 on 14336x4096 (GB/s), ``gemv_reps`` times;
+    * prefill M=2048, N=K=8192 (TFLOP/s), the whole product;
+    * quantize with double quant (GB/s of bf16 input read): layers 0 and 31
+      of the stack (7 linears each), whose rate stands for the 32-layer stack
+      (x16 for its time).
+
+    Inputs come from ``synth`` (host draws of the same shapes and
+    distributions as the GPU workload)."""
     import numpy as np
     import oracle
     import synth
+    from threadpoolctl import threadpool_limits
 
-    w, x = synth.decode(0)
-    N, K = DECODE_SHAPES[0]
-    state = oracle.quantize(w, True)
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.dequant_matmul_ref(x, state["packed"], state, N, K)
-        reps += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
+    avail, allc = cpu_threads()
+    gemv_in = []
+    for s in range(len(DECODE_SHAPES)):
+        w, x = synth.decode(s)
+        gemv_in.append((x, oracle.quantize(w, True), DECODE_SHAPES[s]))
+    wb, xb = synth.batched()
+    N16, K16 = wb.shape
+    st16 = oracle.quantize(wb, True)
+    del wb
+    wp, xp = synth.prefill()
+    Np, Kp = wp.shape
+    stp = oracle.quantize(wp, True)
+    del wp
+    Mp = xp.shape[0]
+    qweights = [w for l in (0, 31) for w in synth.bulk_layer(l)]
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    configs = []
+    t_total = time.perf_counter()
+    for mode, threads in (("1-thread", 1), ("all-core", allc)):
+        with threadpool_limits(threads):
+            secs = [sum(timed(lambda: oracle.dequant_matmul_ref(x, st["packed"], st, N, K))
+                        for _ in range(gemv_reps))
+                    for x, st, (N, K) in gemv_in]
+            byts = [gemv_reps * gemv_bytes(1, N, K) for _, _, (N, K) in gemv_in]
+            configs.append({"config": "decode GEMV M=1, 4096x4096 + 11008x4096 + 4096x11008",
+                            "mode": mode, "threads": threads,
+                            "value": sum(byts) / sum(secs) / 1e9, "unit": "GB/s",
+                            "seconds": sum(secs),
+                            "by_shape_s": {f"{N}x{K}": round(t, 3)
+                                           for t, (_, _, (N, K)) in zip(secs, gemv_in)},
+                            "sample": f"{gemv_reps} reference GEMVs per shape"})
+            t = sum(timed(lambda: oracle.dequant_matmul_ref(xb, st16["packed"], st16, N16, K16))
+                    for _ in range(gemv_reps))
+            configs.append({"config": f"batched decode M=16, {N16}x{K16}", "mode": mode,
+                            "threads": threads,
+                            "value": gemv_reps * gemv_bytes(16, N16, K16) / t / 1e9,
+                            "unit": "GB/s", "seconds": t,
+                            "sample": f"{gemv_reps} reference GEMVs"})
+            t = timed(lambda: oracle.dequant_matmul_ref(xp, stp["packed"], stp, Np, Kp))
+            configs.append({"config": f"prefill GEMM M=2048, N=K={Kp}", "mode": mode,
+                            "threads": threads, "value": 2.0 * Mp * Np * Kp / t / 1e12,
+                            "unit": "TFLOP/s", "seconds": t,
+                            "sample": "the whole product, all 2048 rows"})
+            t = sum(timed(lambda w=w: oracle.quantize(w, True)) for w in qweights)
+            nin = sum(2 * w.size for w in qweights)
+            configs.append({"config": "quantize with double quant", "mode": mode,
+                            "threads": threads, "value": nin / t / 1e9,
+                            "unit": "GB/s (bf16 input read)", "seconds": t,
+                            "sample": ("layers 0 and 31 of the 32-layer stack (14 linears); "
+                                       f"the stack would take x16 = {16 * t:.0f} s")})
+    for c in configs:
+        c["value"] = round(c["value"], 6)
+        c["seconds"] = round(c["seconds"], 3)
+    head = configs[len(configs) // 2]   # decode GEMV, all-core
     return {
-        "value": gemv_bytes(1, N, K) * reps / dt / 1e9,
+        "value": head["value"],
         "unit": "GB/s",
-        "cores": int(cores),
+        "cores": allc,
+        "affinity_cpus": avail,
         "kind": "oracle",
-        "sample": f"{reps} x fp64 reference GEMV (dequantize + matmul) of one 4096x4096 "
-                  f"double-quant layer, M=1, {dt:.1f} s",
+        "sample": (f"fp64 reference GEMV (oracle dequantize + binary64 matmul) {gemv_reps} times "
+                   f"per decode shape, double quant, M=1, {allc} BLAS threads; every "
+                   f"configuration in "
+                   f"both modes in 'configs' ({time.perf_counter() - t_total:.0f} s of CPU work "
+                   f"in all)"),
+        "configs": configs,
     }
 
 
@@ -124,11 +196,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-only", action="store_true",
+                    help="only the CPU baseline (no GPU work); prints its JSON object")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the FP4 / FP16 measurements (profiling runs)")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="run a 256 MiB plain copy first (counter scaling reference)")
     args = ap.parse_args()
+    if args.cpu_only:
+        print(json.dumps(cpu_baseline()))
+        return
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
               f"(the multi-GPU sharding is described, not built)", file=sys.stderr)

@@ -27,7 +27,9 @@ quantize input type.
 
 The bulk quantize-on-load stack (32 layers of Llama-7B-shaped linears) is
 drawn on the device by the benchmark, because 6.5e9 host draws would take
-minutes; its shapes are listed in ``BULK_LAYER_SHAPES``.
+minutes; its shapes are listed in ``BULK_LAYER_SHAPES``.  ``bulk_layer(l)``
+draws one such layer on the host (W N(0, 0.02), seeds 4000 + 10 l + i for
+linear i), for CPU timings of the oracle on a sample of the stack.
 """
 
 from __future__ import annotations
@@ -121,3 +123,8 @@ def prefill(x_dtype: str = "bf16"):
                   outlier_cols=4)
     return w, x
 
+
+def bulk_layer(l: int):
+    """The seven linears of layer l of the bulk stack (q, k, v, o, gate, up,
+    down), bf16 bit patterns."""
+    return [normal_bf16(shape, 0.02, 4000 + 10 * l + i) for i, shape in enumerate(BULK_LAYER_SHAPES)]
