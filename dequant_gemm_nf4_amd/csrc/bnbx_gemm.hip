@@ -436,6 +436,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   if (kb + 2 < nkb) step(K3{}, F0{}, kb + 2, tB, tA);
   mfmas(1);   // substep 3 of the last step
 
+  // The lane's position again, from an instruction the compiler cannot see
+  // through: values derived from it before the K loop would otherwise stay
+  // live across the loop (where every register is in use) only to address
+  // the epilogue, and the LoRA variant spilled them.
+  int lane_e;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
+  const int col_e = lane_e & 31, half_e = lane_e >> 5;
+
   if constexpr (LORA) {
     // The low-rank term as r / 16 more MFMAs per tile, with XA rows as A and
     // rows of B as B operands in the same lane layout as X and the weights
@@ -447,15 +455,15 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
       u32x4_t xa[8], lb[2];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int64_t row = m0 + 32 * i + col;
+        const int64_t row = m0 + 32 * i + col_e;
         xa[i] = __builtin_amdgcn_raw_buffer_load_b128(
-            ra, (uint32_t)((row * la.ldxa + k0 + 8 * half) * 2), 0, 0);
+            ra, (uint32_t)((row * la.ldxa + k0 + 8 * half_e) * 2), 0, 0);
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int64_t n = n0 + wave * 64 + 32 * j + col;
+        const int64_t n = n0 + wave * 64 + 32 * j + col_e;
         lb[j] = __builtin_amdgcn_raw_buffer_load_b128(
-            rb, (uint32_t)((n * la.ldb + k0 + 8 * half) * 2), 0, 0);
+            rb, (uint32_t)((n * la.ldb + k0 + 8 * half_e) * 2), 0, 0);
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i)
@@ -470,10 +478,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int c = n0 + wave * 64 + 32 * j + col;
+      const int c = n0 + wave * 64 + 32 * j + col_e;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int r = m0 + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+        const int r = m0 + i * 32 + 8 * (v >> 2) + 4 * half_e + (v & 3);
         if (r < M && c < N) y[(int64_t)r * ldy + c] = f32_to_16<F16>(acc[i][j][v]);
       }
     }

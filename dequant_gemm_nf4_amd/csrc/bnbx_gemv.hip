@@ -808,9 +808,11 @@ int rr_max(int mm, int ni) {
   return r;
 }
 
-bool make_plan(int mm, int N, int K, Plan& p) {
+// nicap: at most this many chunks per lane (the dynamic map's per-lane
+// scale mode spills registers at four).
+bool make_plan(int mm, int N, int K, Plan& p, int nicap = 4) {
   const int C = K >> 5;
-  const int nimax = 4 / mm;
+  const int nimax = (4 / mm) < nicap ? (4 / mm) : nicap;
   int best_twl = -1, best_ni = 0;
   double best_util = 0.0;
   for (int twl = 0; (1 << twl) <= kWaves; ++twl) {
@@ -862,7 +864,11 @@ hipError_t launch_k(const Plan& p, const uint16_t* x, int64_t ldx, const uint8_t
   BNBX_GEMV_SM(kScaleF32)
   BNBX_GEMV_SM(kScaleDqLane)
   BNBX_GEMV_SM(kScaleDqRow)
-  BNBX_GEMV_SM(kScaleDynLane)
+  if constexpr (NI < 4) {
+    BNBX_GEMV_SM(kScaleDynLane)
+  } else {
+    if (sm == kScaleDynLane) return hipErrorNotSupported;   // planned out (nicap)
+  }
   BNBX_GEMV_SM(kScaleDynRow)
 #undef BNBX_GEMV_SM
   return hipGetLastError();
@@ -924,13 +930,16 @@ hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* packed, co
   // Rows of X in groups of up to four (each group streams W once); a group
   // of three runs the four-row kernel with its last row empty.  Long rows
   // take smaller groups (the X slice must fit the registers).
+  const bool dyn_lane = double_quant == kDqDynamic &&
+                        !(nkb <= 256 && nkb % 4 == 0 && ((uintptr_t)absmax & 3u) == 0);
+  const int nicap = dyn_lane ? 3 : 4;
   for (int m0 = 0; m0 < M;) {
     const int left = M - m0;
     Plan p;
     int mv = 0;
     for (int mm : {4, 2, 1}) {
       if (left < (mm == 4 ? 3 : mm)) continue;       // a group of 3 uses mm = 4
-      if (make_plan(mm, N < slab ? N : (int)slab, K, p)) {
+      if (make_plan(mm, N < slab ? N : (int)slab, K, p, nicap)) {
         mv = left < mm ? left : mm;
         break;
       }
@@ -938,7 +947,7 @@ hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* packed, co
     if (mv == 0) return hipErrorNotSupported;
     for (int64_t r0 = 0; r0 < N; r0 += slab) {
       const int n = (int)(N - r0 < slab ? N - r0 : slab);
-      if (!make_plan(p.mm, n, K, p)) return hipErrorNotSupported;
+      if (!make_plan(p.mm, n, K, p, nicap)) return hipErrorNotSupported;
       const void* am = double_quant ? (const void*)((const int8_t*)absmax + r0 * nkb)
                                     : (const void*)((const float*)absmax + r0 * nkb);
       const float* am2 = double_quant ? absmax2 + (r0 * nkb) / 256 : absmax2;

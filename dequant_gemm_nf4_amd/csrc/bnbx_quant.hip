@@ -238,21 +238,33 @@ __device__ float exact_mean(const unsigned long long* __restrict__ slots, int ns
   __syncthreads();
   double S = 0.0;
   if (tid == 0) {
-    uint32_t dig[10];
+    // Every digit index below is a compile-time constant (unrolled loops and
+    // selects), so the digits stay in registers: a private array indexed at
+    // run time would live in scratch memory.
+    uint32_t dig[kSumDigits];
     unsigned long long carry = 0;
-    for (int j = 0; j < 10; ++j) {
+#pragma unroll
+    for (int j = 0; j < kSumDigits; ++j) {
       const unsigned long long t = digits[j] + carry;
       dig[j] = (uint32_t)t;
       carry = t >> 32;
     }
-    int hj = 9;
-    while (hj >= 0 && dig[hj] == 0) --hj;
+    int hj = -1;   // the highest nonzero digit
+#pragma unroll
+    for (int j = 0; j < kSumDigits; ++j) hj = dig[j] != 0u ? j : hj;
     if (hj >= 0) {
-      const int lz = __clz(dig[hj]);
-      const unsigned long long whi = ((unsigned long long)dig[hj] << 32) | (hj >= 1 ? dig[hj - 1] : 0u);
-      const uint32_t wlo = hj >= 2 ? dig[hj - 2] : 0u;
-      bool sticky = false;
-      for (int j = 0; j < hj - 2; ++j) sticky |= dig[j] != 0u;
+      uint32_t d2 = 0u, d1 = 0u, d0 = 0u;   // digits hj, hj - 1, hj - 2
+      bool sticky = false;                   // any nonzero digit below hj - 2
+#pragma unroll
+      for (int j = 0; j < kSumDigits; ++j) {
+        d2 = j == hj ? dig[j] : d2;
+        d1 = j == hj - 1 ? dig[j] : d1;
+        d0 = j == hj - 2 ? dig[j] : d0;
+        sticky |= j < hj - 2 && dig[j] != 0u;
+      }
+      const int lz = __clz(d2);
+      const unsigned long long whi = ((unsigned long long)d2 << 32) | d1;
+      const uint32_t wlo = d0;
       const unsigned long long top = lz ? (whi << lz) | (wlo >> (32 - lz)) : whi;
       const uint32_t rest = lz ? (wlo << lz) : wlo;
       sticky |= rest != 0u;

@@ -137,7 +137,7 @@ def as_f64(bits, dt, shape):
 @pytest.mark.parametrize("qt,dt", [("nf4", "bf16"), ("fp4", "f16")])
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 16])
 @pytest.mark.parametrize("N,K", [(4096, 4096), (11008, 4096), (4096, 11008), (300, 4160),
-                                 (70, 20480)])
+                                 (70, 20480), (40, 32768)])
 def test_dyn_gemv(M, N, K, qt, dt):
     w = synth.normal_bf16((N, K), 0.02, 12300 + N + K)
     x = synth.normal_16((M, K), 1.0, 12301 + M, dt)
