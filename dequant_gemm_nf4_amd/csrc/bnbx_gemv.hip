@@ -1,901 +1,9 @@
-// Decode GEMV with 4-bit (NF4 or FP4) weights for gfx950:
-// Y[M, N] = X[M, K] . W_hat[N, K]^T,
-// M <= 16 (mlqm.cn bitsandbytes article, sec. 3.4 "4-bit storage, 16-bit
-// compute", and the sec. 7 pitfall that 4-bit only pays off when the layer is
-// bound by weight traffic: so the packed weight is streamed exactly once:
-// gemv_kernel below for up to four rows of X, gemv16_kernel further down for
-// 4 < M <= 16).
-//
-// Work layout.  A row of W is C = K/32 chunks of 16 packed bytes (32
-// weights, half of one 64-block).  A row is owned by a team of TW waves
-// (S = 64 TW lanes); lane s of a team owns chunks s, s+S, ..., s+(NI-1)S of
-// every row the team takes, so its slice of X is read once into registers.
-// A workgroup is 16 waves and the grid has at most one workgroup per CU; a
-// team takes RR rows per pass, so for the decode shapes one pass covers the
-// matrix.  The first row's loads go out before the lookup table is built,
-// the others right after the workgroup barrier (a wave stalled issuing loads
-// into a full memory pipeline would otherwise hold the barrier for all).
-//
-// Loads are buffer loads whose resource is the row (a scalar base and a
-// length), with a per-lane offset fixed for the whole kernel.  The hardware
-// range check returns zero past the end of the row (the ragged last chunks)
-// and for rows past N, so there is no per-load address arithmetic or bounds
-// branch.  With double quant a row's int8 codes come in one dword per lane and
-// reach the lanes that need them by ds_bpermute, and its (at most two) group
-// scales in one vector load.  Nothing the table build needs waits on a
-// memory load: the kernel issues no scalar loads from memory (the table
-// build's wait for its scalar kernel-argument loads would cover them too),
-// and the mean is loaded first so that its use waits for nothing else.  X is
-// staged once per workgroup in LDS.
-//
-// Dequant in registers.  An LDS table maps each packed byte to the level pair
-// (L[high nibble], L[low nibble]) in the compute type (bf16, or FP16 with
-// v_dot2_f32_f16 and the _f16 MFMA); it is replicated in 32 lane columns with a
-// 256-byte stride so that the lanes of each half-wave read distinct banks, and
-// the byte address (byte << 8 | lane << 2) is one v_perm_b32.  The pair feeds
-// v_dot2_f32_bf16 against the matching X pair and the 32-weight partial sum
-// is scaled once by its block scale, so dequant costs one VALU instruction per
-// weight plus one LDS read per two.  Chunks are consumed one at a time in
-// load order (scheduling barriers keep the compiler from hoisting work above
-// the waits).  Sums over a wave use DPP row shifts and row broadcasts; a
-// multi-wave team adds its waves' sums through LDS.
-#include "bnbx_device.hpp"
-#include "bnbx_internal.hpp"
+// Decode GEMV entry (bnbx_gemv_nf4): M <= 4 rows of X per launch of
+// gemv_kernel (bnbx_gemv_common.hpp), 4 < M <= 16 in one launch of the
+// batched kernel (bnbx_gemv16.hip).  mlqm.cn bitsandbytes article, sec. 3.4.
+#include "bnbx_gemv_common.hpp"
 
 namespace bnbx {
-namespace {
-
-constexpr int kWaves = 16;                  // waves per workgroup (one workgroup per CU)
-constexpr int kThreads = kWaves * 64;
-constexpr int kCopies = 32;                 // lane columns of the byte table (128 B)
-constexpr int kTabBytes = 256 * 256;        // 256 B per byte value
-// X staged in LDS when MM*K*2 fits (the table takes 64 KB of the CU's 160 KB).
-constexpr int kXBytes = 64 * 1024;
-constexpr int kMaxMM = 4;
-constexpr int kMaxRR = 4;
-constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
-
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           (int)kRsrcWord3);
-}
-template <int AUX>
-__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-template <int CTRL, int ROWMASK, bool BOUND_ZERO>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(
-      __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWMASK, 0xf, BOUND_ZERO));
-}
-// Sum over the 64 lanes of a wave, left in lane 63: prefix sums within each
-// row of 16 lanes (row_shr 1, 2, 4, 8), then row_bcast:15 and row_bcast:31
-// carry the row totals up to lane 63.
-__device__ __forceinline__ float wave_sum_to_63(float v) {
-  v += dpp<0x111, 0xf, true>(v);
-  v += dpp<0x112, 0xf, true>(v);
-  v += dpp<0x114, 0xf, true>(v);
-  v += dpp<0x118, 0xf, true>(v);
-  v += dpp<0x142, 0xa, false>(v);
-  v += dpp<0x143, 0xc, false>(v);
-  return v;
-}
-
-// Block-scale storage: fp32 absmax, or double quant (code byte + fp32 group
-// scale + mean) read per lane, or double quant read per row; the code bytes
-// are int8 steps of s_g / 127 (linear map) or indices into the dynamic 8-bit
-// map (Dyn modes, a copy of the map in LDS).  The row-wise read loads whole
-// dwords of codes, and the buffer range check zeroes a dword that is only
-// partly inside the row, so it needs a row of 4k blocks (at most 256:
-// K <= 16384, K % 256 == 0) and 4-byte aligned codes.
-enum ScaleMode {
-  kScaleF32 = 0,
-  kScaleDqLane = 1,
-  kScaleDqRow = 2,
-  kScaleDynLane = 3,
-  kScaleDynRow = 4
-};
-constexpr bool scale_dyn(int sm) { return sm == kScaleDynLane || sm == kScaleDynRow; }
-constexpr bool scale_row(int sm) { return sm == kScaleDqRow || sm == kScaleDynRow; }
-constexpr int kMapBytes = 256 * 4;
-
-// Lane t % 256's value of the dynamic map, one load per lane with no
-// condition (so that the wait for it, in load order, names nothing later).
-__device__ __forceinline__ float dyn_map_value(int t) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(kDynMapDev.v, (uint32_t)kMapBytes),
-                                                  (uint32_t)(t & 255) * 4u, 0, 0));
-}
-
-// MM rows of X per launch (rows >= mvalid are zero), NI chunks per lane, RR
-// rows of W per team and pass.  TW = 1 << twl waves per team.
-template <int MM, int NI, int RR, int SM, bool F16>
-__global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
-    const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ packed,
-    const void* __restrict__ absmax, const float* __restrict__ absmax2,
-    const float* __restrict__ mean, int mvalid, int N, int K, uint16_t* __restrict__ y,
-    int64_t ldy, int twl, int xlds, LevelTable lv) {
-  constexpr bool DQ = SM != kScaleF32;
-  constexpr bool DYN = scale_dyn(SM);
-  // One LDS block with the table at offset 0, so that a table address is the
-  // v_perm result itself (the ds_read offset field cannot hold a 64 KB base),
-  // then X, then the team sums, then the dynamic map (DYN).  X is stored in 64-byte chunks whose four
-  // 16-byte pieces are rotated by (chunk / 4) % 4: piece q of chunk c sits at
-  // 64 c + 16 (q ^ ((c >> 2) & 3)), so that 16 lanes reading piece q of 16
-  // consecutive chunks hit 64 distinct banks.
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kTabBytes + kXBytes +
-                                                             kWaves * MM * RR * 4 +
-                                                             (DYN ? kMapBytes : 0)];
-  unsigned char* const tab = smem;
-  unsigned char* const xs = smem + kTabBytes;
-  float* const red = (float*)(smem + kTabBytes + kXBytes);
-  unsigned char* const dmap = smem + kTabBytes + kXBytes + kWaves * MM * RR * 4;
-
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int TW = 1 << twl;
-  const int tpw = kWaves >> twl;              // teams per workgroup
-  const int team_l = wave >> twl;
-  const int wit = wave - (team_l << twl);     // wave within team
-  const int S = 64 << twl;
-  const int s = wit * 64 + lane;              // lane slot within team
-  const int C = K >> 5;
-  const uint32_t rowK2 = (uint32_t)K >> 1;
-  const uint32_t nkb = (uint32_t)K >> 6;
-  const uint32_t xbytes = (uint32_t)K * 2u;
-  const int64_t pass_rows = (int64_t)gridDim.x * tpw * RR;
-  const int64_t rb_first = (int64_t)blockIdx.x * tpw * RR;   // workgroup's first row
-  const uint32_t ng_bytes = DQ ? (uint32_t)((((uint64_t)N * nkb + 255) >> 8) * 4) : 0u;
-  const rsrc_t rg = make_rsrc(absmax2, ng_bytes);
-
-  // Fixed per-lane offsets: chunk c of the row (bytes), its block (index).
-  uint32_t woff[NI], boff[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const uint32_t c = (uint32_t)(s + i * S);
-    woff[i] = c * 16u;
-    boff[i] = c >> 1;
-  }
-
-  // 0. The mean, by lane 0 alone and before every other load: loads
-  //    complete in issue order, so its first use (broadcast with
-  //    v_readfirstlane) then waits for nothing else.
-  float mul = 0.0f;
-  if (DQ && lane == 0)
-    mul = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(mean, 4u), 0u, 0, 0));
-  const float dmv = DYN ? dyn_map_value(t) : 0.0f;
-
-  // 1. X: staging loads (LDS path) or the lane's slice directly.
-  uint32_t xr[MM][NI][16];
-  constexpr int kStage = kXBytes / 16 / kThreads;   // 16-byte pieces per thread (max)
-  uint4 xst[kStage];
-  const int xpieces = (int)(xbytes >> 4);          // per row of X
-  if (xlds) {
-    // One resource over the valid rows of X; rows at or past mvalid (and
-    // pieces past MM rows) fall outside it and read as zero.
-    const rsrc_t rx = make_rsrc(x, (uint32_t)((int64_t)(mvalid - 1) * ldx * 2) + xbytes);
-#pragma unroll
-    for (int k = 0; k < kStage; ++k) {
-      const int e = t + k * kThreads;
-      if (e < MM * xpieces) {          // whole waves drop out: no idle loads
-        const int m = e / xpieces;
-        const int p = e - m * xpieces;
-        xst[k] = buf_load16<0>(rx, (uint32_t)((int64_t)m * ldx * 2) + (uint32_t)p * 16u);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int m = 0; m < MM; ++m) {
-      const rsrc_t rx = make_rsrc(x + (int64_t)m * ldx, m < mvalid ? xbytes : 0u);
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint4 v = buf_load16<0>(rx, woff[i] * 4u + q * 16u);
-          xr[m][i][4 * q] = v.x;
-          xr[m][i][4 * q + 1] = v.y;
-          xr[m][i][4 * q + 2] = v.z;
-          xr[m][i][4 * q + 3] = v.w;
-        }
-      }
-    }
-  }
-
-  // 2. Weight and scale loads of RR rows.  Rows past N get an empty resource.
-  //    Double quant with rows of at most 256 blocks (K <= 16384) loads a
-  //    row's int8 codes with one dword per lane (lane l: blocks 4l..4l+3,
-  //    handed to the lanes that need them by ds_bpermute) and its group
-  //    scales with scalar loads (a row spans at most two groups); otherwise
-  //    every lane loads its own block's scales.
-  constexpr bool rowsc = scale_row(SM);
-  const uint32_t ng = DQ ? (uint32_t)(((uint64_t)N * nkb + 255) >> 8) : 1u;
-  uint4 w[RR][NI];
-  int qv[RR][NI];
-  float gv[RR][NI];
-  int qd[RR];
-  float gsl[RR];      // the row's group scales: g0 in even lanes, g1 in odd ones
-  uint32_t split[RR];
-  auto issue_part = [&](int64_t rb, int lo, int hi) {
-#pragma unroll
-    for (int j = 0; j < RR; ++j) {
-      if ((j + 1) * NI <= lo || j * NI >= hi) continue;
-      const int64_t row = rb + j;
-      const bool ok = row < N;
-      const rsrc_t rw = make_rsrc(packed + row * rowK2, ok ? rowK2 : 0u);
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-        if (j * NI + i >= lo && j * NI + i < hi) w[j][i] = buf_load16<2>(rw, woff[i]);   // nt
-      if (j * NI < lo) continue;              // the row's scales went with its first chunk
-      if (rowsc) {
-        const rsrc_t rq = make_rsrc((const int8_t*)absmax + row * nkb, ok ? nkb : 0u);
-        qd[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(rq, (uint32_t)lane * 4u, 0, 0);
-        const uint32_t blk0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(row * nkb));
-        uint32_t g0 = blk0 >> 8;
-        g0 = g0 < ng ? g0 : ng - 1u;
-        const uint32_t g1 = g0 + 1u < ng ? g0 + 1u : ng - 1u;
-        // Both group scales in one vector load, g0 in the even lanes and g1
-        // in the odd ones, spread to every lane by DPP where they are used.
-        // (A scalar load here would make the table build, which waits for all
-        // scalar loads, wait for a memory latency: 4.5 against 4.1 us per
-        // 4096^2 launch.  Loading them with two lanes active, or broadcasting
-        // with v_readlane, measured slower still.)
-        gsl[j] = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(rg, ((lane & 1) ? g1 : g0) * 4u, 0, 0));
-        split[j] = 256u - (blk0 & 255u);     // blocks of the row in group g0
-      } else if (DQ) {
-        const rsrc_t rq = make_rsrc((const int8_t*)absmax + row * nkb, ok ? nkb : 0u);
-        const uint32_t blk0 = (uint32_t)(row * nkb);
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const uint32_t cb = __builtin_amdgcn_raw_buffer_load_b8(rq, boff[i], 0, 0);
-          qv[j][i] = DYN ? (int)(uint8_t)cb : (int)(int8_t)(uint8_t)cb;
-          gv[j][i] = __builtin_bit_cast(
-              float, __builtin_amdgcn_raw_buffer_load_b32(rg, ((blk0 + boff[i]) >> 8) * 4u, 0, 0));
-        }
-      } else {
-        const rsrc_t ra = make_rsrc((const float*)absmax + row * nkb, ok ? nkb * 4u : 0u);
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          qv[j][i] = 0;
-          gv[j][i] = __builtin_bit_cast(
-              float, __builtin_amdgcn_raw_buffer_load_b32(ra, boff[i] * 4u, 0, 0));
-        }
-      }
-    }
-  };
-  auto issue = [&](int64_t rb) { issue_part(rb, 0, RR * NI); };
-  // The first row of the first pass goes out now, before the table build;
-  // the other rows after the barrier, so that a wave held up issuing loads
-  // into a full memory pipeline does not hold the barrier for the others.
-  issue_part(rb_first + (int64_t)team_l * RR, 0, NI);
-
-  // 3. Byte -> level-pair table (compute type), then X into LDS.
-  const int lvl = level_lanes(lv);
-  for (int e = t; e < 256 * kCopies / 4; e += kThreads) {
-    const uint32_t b = (uint32_t)e / (kCopies / 4);
-    const uint32_t v = pack16x2<F16>(level_lookup(lvl, b >> 4), level_lookup(lvl, b & 15u));
-    *(uint4*)(tab + b * 256u + ((uint32_t)e % (kCopies / 4)) * 16u) = make_uint4(v, v, v, v);
-  }
-  if (DYN && t < 256) *(float*)(dmap + t * 4) = dmv;
-  if (xlds) {
-#pragma unroll
-    for (int k = 0; k < kStage; ++k) {
-      const int e = t + k * kThreads;
-      if (e < MM * xpieces) {
-        const uint32_t c = (uint32_t)e >> 2, q = (uint32_t)e & 3u;   // chunk and piece
-        *(uint4*)(xs + c * 64u + ((q ^ ((c >> 2) & 3u)) << 4)) = xst[k];
-      }
-    }
-  }
-  // Nothing may move across the barrier: a weight use hoisted above it would
-  // make every wave wait there for its first row.
-  __builtin_amdgcn_sched_barrier(0);
-  __syncthreads();
-  __builtin_amdgcn_sched_barrier(0);
-  // X slice of this lane (LDS path), read up front.
-  auto read_x = [&](int i) {
-#pragma unroll
-    for (int m = 0; m < MM; ++m) {
-      {
-        const int c = s + i * S;
-        const bool in = c < C;
-        const uint32_t cg = (uint32_t)(m * C + (in ? c : 0));   // chunk of the staged X
-        const unsigned char* src = xs + cg * 64u;
-        const uint32_t rot = (cg >> 2) & 3u;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint4 v = *(const uint4*)(src + (((uint32_t)q ^ rot) << 4));
-          xr[m][i][4 * q] = in ? v.x : 0u;
-          xr[m][i][4 * q + 1] = in ? v.y : 0u;
-          xr[m][i][4 * q + 2] = in ? v.z : 0u;
-          xr[m][i][4 * q + 3] = in ? v.w : 0u;
-        }
-      }
-    }
-  };
-  if (xlds) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) read_x(i);
-  }
-
-  issue_part(rb_first + (int64_t)team_l * RR, NI, RR * NI);
-  const uint32_t lanebyte = (uint32_t)(lane & (kCopies - 1)) << 2;
-  // 4. Dequant-in-register dot products of one pass, one chunk at a time in
-  //    load order, then the sums over the team and the stores.
-  auto pass = [&](int64_t rb) {
-    const float mu = DQ ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mul))) : 0.0f;
-    float acc[MM][RR];
-#pragma unroll
-    for (int j = 0; j < RR; ++j) {
-#pragma unroll
-      for (int m = 0; m < MM; ++m) acc[m][j] = 0.0f;
-      // the row's (at most two) group factors, once per row: the steps
-      // fl32(s_g / 127) (linear map) or s_g itself (dynamic map);
-      // quad_perm(0,0,0,0) / (1,1,1,1): every lane takes its quad's g0 / g1
-      auto factor = [&](float g) { return DYN ? g : dq_step_normal(g); };
-      const float step0 =
-          rowsc ? factor(__int_as_float(__builtin_amdgcn_update_dpp(
-                      0, __float_as_int(gsl[j]), 0x00, 0xF, 0xF, false)))
-                : 0.0f;
-      const float step1 =
-          rowsc ? factor(__int_as_float(__builtin_amdgcn_update_dpp(
-                      0, __float_as_int(gsl[j]), 0x55, 0xF, 0xF, false)))
-                : 0.0f;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        float sc;
-        if (rowsc) {
-          const int qw = __builtin_amdgcn_ds_bpermute((int)((boff[i] >> 2) << 2), qd[j]);
-          float qf;
-          if (DYN)
-            qf = *(const float*)(dmap + __builtin_amdgcn_ubfe((uint32_t)qw, (boff[i] & 3u) * 8u, 8) * 4u);
-          else
-            qf = (float)(int)__builtin_amdgcn_sbfe(qw, (boff[i] & 3u) * 8u, 8);   // signed
-          const float prod = qf * (boff[i] < split[j] ? step0 : step1);
-          sc = prod + mu;
-        } else if (DYN) {
-          const float prod = *(const float*)(dmap + (uint32_t)qv[j][i] * 4u) * gv[j][i];
-          sc = prod + mu;
-        } else {
-          sc = DQ ? (float)qv[j][i] * dq_step_normal(gv[j][i]) + mu : gv[j][i];
-        }
-        const uint32_t d[4] = {w[j][i].x, w[j][i].y, w[j][i].z, w[j][i].w};
-        float part[MM];
-#pragma unroll
-        for (int m = 0; m < MM; ++m) part[m] = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const uint32_t addr = perm(d[q], lanebyte, 0x0c0c0000u | ((4u + b) << 8));
-            const uint32_t pair = *(const uint32_t*)(tab + addr);
-#pragma unroll
-            for (int m = 0; m < MM; ++m) part[m] = dot2_16<F16>(pair, xr[m][i][4 * q + b], part[m]);
-          }
-        }
-#pragma unroll
-        for (int m = 0; m < MM; ++m) acc[m][j] = __builtin_fmaf(part[m], sc, acc[m][j]);
-        // Only one chunk's table addresses and pairs live at a time.
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < RR; ++j)
-#pragma unroll
-      for (int m = 0; m < MM; ++m) acc[m][j] = wave_sum_to_63(acc[m][j]);
-    if (TW == 1) {
-      if (lane == 63) {
-#pragma unroll
-        for (int j = 0; j < RR; ++j)
-#pragma unroll
-          for (int m = 0; m < MM; ++m)
-            if (rb + j < N && m < mvalid) y[(int64_t)m * ldy + rb + j] = f32_to_16<F16>(acc[m][j]);
-      }
-    } else {
-      if (lane == 63) {
-#pragma unroll
-        for (int j = 0; j < RR; ++j)
-#pragma unroll
-          for (int m = 0; m < MM; ++m) red[(wave * MM + m) * RR + j] = acc[m][j];
-      }
-      __syncthreads();
-      if (wit == 0 && lane < MM * RR) {
-        const int m = lane / RR, j = lane - (lane / RR) * RR;
-        float v = 0.0f;
-        for (int u = 0; u < TW; ++u) v += red[((team_l * TW + u) * MM + m) * RR + j];
-        if (rb + j < N && m < mvalid) y[(int64_t)m * ldy + rb + j] = f32_to_16<F16>(v);
-      }
-      __syncthreads();
-    }
-  };
-  // The first pass uses the loads issued before the table build; later
-  // passes (more rows than the grid holds at once) issue their own.  The
-  // loop condition is the workgroup's, so its barriers are uniform.
-  pass(rb_first + (int64_t)team_l * RR);
-  for (int64_t rb0 = rb_first + pass_rows; rb0 < N; rb0 += pass_rows) {
-    issue(rb0 + (int64_t)team_l * RR);
-    pass(rb0 + (int64_t)team_l * RR);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// 4 < M <= 16: one launch for any K; the weights are streamed once into
-// v_mfma_f32_16x16x32_bf16 (or _f16) operands.
-//
-// MFMA roles: A is X (lane l: row l % 16, eight k), B is the dequantized
-// weight (lane l: weight row l % 16 of a group of 16, eight k), and lane l
-// ends with Y[4 (l / 16) + v][16 g + l % 16], v = 0..3.
-//
-// Loads are quad-coalesced: lane x reads 16 bytes of row x / 4 at piece
-// x % 4, so the four lanes of a quad read 64 contiguous bytes and one
-// instruction covers 16 rows x 64 bytes.  (MFMA-layout loads, where
-// neighbouring lanes read different rows, made every lane its own memory
-// request; the address path then held the kernel at 17 us on 14336 x 4096.)
-// A per-wave 1 KB LDS stage turns that into the MFMA layout: lane x writes
-// its piece to slot 16 p + ((r + 4 p) mod 16) and lane (q, r) reads slot
-// 16 q + ((r + 4 q) mod 16), both bank-conflict free; lane (q, r) then holds
-// piece q of row r.  For the weights, a 4 x 4 transpose across the quarters
-// (two v_permlane32_swap, two v_permlane16_swap) then gives lane (q, r) the
-// dword q of every piece m: MFMA m covers the 32 k [128 h + 32 m, +32) of
-// the slice, half of block 2 h + m / 2, and its B operand is four byte ->
-// level-pair lookups in the LDS table of gemv_kernel.  The two MFMAs of a
-// block go to a zeroed accumulator scaled by the block scale of the lane's
-// weight row; scales are formed where they load (lane x: row x / 4, block
-// x % 4) and fetched with ds_bpermute.
-//
-// Work split.  K is cut into slices of 256 k (4 blocks); wave w of the
-// 16-wave workgroup owns slices w, w + 16, ... (one per chunk of 4096 k)
-// and keeps the X operands of its current slice in registers.  The
-// workgroup owns row groups blockIdx.x + j * gridDim.x and takes NB of them
-// at a time.  Every load is unconditional (items past the end get offsets
-// outside their buffer, which read as zero), so each wait names exactly the
-// loads it needs.  With one chunk (K <= 4096) all of a batch's loads go out
-// at once; with more, each half of the next chunk's X goes into the
-// registers of the half just multiplied, and the weights two chunks ahead
-// into the set just used.  The 16 waves' partial sums meet in LDS, two row
-// groups at a time.
-// ---------------------------------------------------------------------------
-constexpr int k16Waves = 16;
-constexpr int k16SliceK = 256;    // k per wave slice (4 blocks)
-constexpr int k16ChunkK = k16Waves * k16SliceK;
-constexpr uint32_t kFar = 0x80000000u;   // an offset past every buffer resource
-
-template <int SM, bool F16, int NB, bool MULTI>
-__global__ __launch_bounds__(k16Waves * 64, 1) void gemv16_kernel(
-    const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ packed,
-    const void* __restrict__ absmax, const float* __restrict__ absmax2,
-    const float* __restrict__ mean, int M, int N, int K, uint16_t* __restrict__ y, int64_t ldy,
-    LevelTable lv) {
-  constexpr bool DQ = SM != kScaleF32;
-  constexpr bool DYN = scale_dyn(SM);
-  constexpr int kSets = MULTI ? 2 : 1;
-  constexpr int kRed = NB < 2 ? NB : 2;   // row groups reduced at once
-  static_assert(!MULTI || NB == 1, "several chunks take one row group at a time");
-  // Table at LDS offset 0 (its addresses are v_perm results), then the
-  // waves' 1 KB stages, then the partial sums, then the dynamic map (DYN).
-  __shared__ __attribute__((aligned(16))) unsigned char
-      smem[kTabBytes + k16Waves * 1024 + kRed * k16Waves * 256 * 4 + (DYN ? kMapBytes : 0)];
-  unsigned char* const tab = smem;
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  unsigned char* const stage = smem + kTabBytes + wave * 1024;
-  float* const red = (float*)(smem + kTabBytes + k16Waves * 1024);
-  unsigned char* const dmap = smem + kTabBytes + k16Waves * 1024 + kRed * k16Waves * 256 * 4;
-  const int r = lane & 15, q = lane >> 4;        // MFMA layout
-  const int lr = lane >> 2, lp = lane & 3;       // load layout: row, piece
-  const uint32_t wslot = 16u * (uint32_t)(16 * lp + ((lr + 4 * lp) & 15));
-  const uint32_t rslot = 16u * (uint32_t)(16 * q + ((r + 4 * q) & 15));
-  const uint32_t rowK2 = (uint32_t)K >> 1;
-  const uint32_t nkb = (uint32_t)K >> 6;
-  const int nchunks = (K + k16ChunkK - 1) / k16ChunkK;
-  const int ngroups = (N + 15) >> 4;
-  const int nrg = ngroups > (int)blockIdx.x
-                      ? (ngroups - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x
-                      : 0;
-
-  // The mean first, by lane 0 (loads complete in issue order, so its use
-  // waits for nothing else); broadcast where it is used.
-  float mul = 0.0f;
-  if (DQ && lane == 0)
-    mul = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(mean, 4u), 0u, 0, 0));
-  const float dmv = DYN ? dyn_map_value(t) : 0.0f;
-
-  const rsrc_t rw = make_rsrc(packed, (uint32_t)N * rowK2);
-  const uint32_t nblocks = (uint32_t)N * nkb;
-  const rsrc_t rq = make_rsrc(absmax, DQ ? nblocks : nblocks * 4u);
-  const rsrc_t rg = make_rsrc(absmax2, DQ ? (nblocks + 255u) / 256u * 4u : 4u);
-  const rsrc_t rx = make_rsrc(x, (uint32_t)((int64_t)(M - 1) * ldx * 2 + (int64_t)K * 2));
-  const uint32_t xrow = (uint32_t)((int64_t)lr * ldx * 2);
-
-  // One item (a row group's piece of one slice), in the load layout: the
-  // lane's two 16-byte weight pieces (row 16 g + x / 4, bytes 64 h + 16 (x %
-  // 4) of the slice) and the raw scale of block x % 4 of that row.
-  struct Item {
-    u32x4_t w[2];
-    uint32_t qc;   // code byte(s): the row modes hold the row's four codes
-    float gs;      // group scale, or the fp32 absmax
-  };
-  struct Set {
-    Item it[NB];
-  };
-  // X of slice u, half h, in the load layout: xa[h][m] holds row x / 4,
-  // k [256 u + 128 h + 32 m + 8 (x % 4), +8) (zero past K; rows past M read
-  // as zero through the resource).
-  u32x4_t xa[2][4];
-  auto load_x = [&](int u, int h) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int k0 = u * k16SliceK + 128 * h + 32 * m;
-      xa[h][m] = __builtin_amdgcn_raw_buffer_load_b128(
-          rx, k0 < K ? xrow + (uint32_t)(k0 + 8 * lp) * 2u : kFar, 0, 0);
-    }
-  };
-  // Item of slice u, row group j of the workgroup.
-  auto load_item = [&](Item& it, int u, int j) {
-    {
-      const bool uin = u * k16SliceK < K;
-      const int g = (int)blockIdx.x + j * (int)gridDim.x;
-      const bool in = uin && j < nrg;
-      const uint32_t row = (uint32_t)(16 * g + lr);
-      const uint32_t wo = in ? row * rowK2 + (uint32_t)u * (k16SliceK / 2) + 16u * (uint32_t)lp : kFar;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) it.w[h] = __builtin_amdgcn_raw_buffer_load_b128(rw, wo + 64u * h, 0, 2);
-      const uint32_t blk = row * nkb + 4u * (uint32_t)u;   // the slice's first block in the row
-      if (scale_row(SM)) {
-        it.qc = __builtin_amdgcn_raw_buffer_load_b32(rq, in ? blk : kFar, 0, 0);
-        it.gs = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(rg, in ? (blk >> 8) * 4u : kFar, 0, 0));
-      } else if (DQ) {
-        const uint32_t b = blk + (uint32_t)lp;
-        it.qc = __builtin_amdgcn_raw_buffer_load_b8(rq, in ? b : kFar, 0, 0);
-        it.gs = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(rg, in ? (b >> 8) * 4u : kFar, 0, 0));
-      } else {
-        it.qc = 0u;
-        it.gs = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(rq, in ? (blk + lp) * 4u : kFar, 0, 0));
-      }
-    }
-  };
-  auto load_set = [&](Set& st, int u, int j0) {
-#pragma unroll
-    for (int jj = 0; jj < NB; ++jj) load_item(st.it[jj], u, j0 + jj);
-  };
-  // Scale of block x % 4 of row x / 4 (load layout).
-  auto load_scale = [&](const Item& it, float mu) {
-    if (!DQ) return it.gs;
-    if (DYN) {
-      const uint32_t code = scale_row(SM) ? __builtin_amdgcn_ubfe(it.qc, lp * 8, 8) : it.qc & 0xffu;
-      const float prod = *(const float*)(dmap + code * 4u) * it.gs;
-      return prod + mu;
-    }
-    const int code = scale_row(SM) ? __builtin_amdgcn_sbfe((int)it.qc, lp * 8, 8)
-                                   : (int)(int8_t)(uint8_t)it.qc;
-    const float prod = (float)code * dq_step_normal(it.gs);
-    return prod + mu;
-  };
-  // Load layout -> lane (q, r) holds piece q of row r, through the stage.
-  auto relayout = [&](u32x4_t& v) {
-    *(u32x4_t*)(stage + wslot) = v;
-    v = *(const u32x4_t*)(stage + rslot);
-  };
-
-  const uint32_t lanebyte = (uint32_t)(lane & (kCopies - 1)) << 2;
-  auto lut = [&](uint32_t d) {
-    u32x4_t b;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      b[j] = *(const uint32_t*)(tab + perm(d, lanebyte, 0x0c0c0000u | ((4u + j) << 8)));
-    return b;
-  };
-  // One item's half h (128 k of its row group) into its sums; X must be in
-  // the MFMA layout.
-  auto mul_item_half = [&](Item& it, int h, f32x4_t& acc, float sl) {
-    relayout(it.w[h]);
-    const auto a = __builtin_amdgcn_permlane32_swap(it.w[h][0], it.w[h][2], false, false);
-    const auto b = __builtin_amdgcn_permlane32_swap(it.w[h][1], it.w[h][3], false, false);
-    const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
-    const auto e = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
-    const uint32_t E[4] = {c[0], c[1], e[0], e[1]};
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      f32x4_t blk = {0.0f, 0.0f, 0.0f, 0.0f};
-      blk = mfma_16x16x32<F16>(xa[h][2 * hb], lut(E[2 * hb]), blk);
-      blk = mfma_16x16x32<F16>(xa[h][2 * hb + 1], lut(E[2 * hb + 1]), blk);
-      // block 2 h + hb of row r was formed by lane 4 r + 2 h + hb
-      const float sc = __int_as_float(
-          __builtin_amdgcn_ds_bpermute((4 * r + 2 * h + hb) << 2, __float_as_int(sl)));
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(blk[v], sc, acc[v]);
-    }
-  };
-  // A set's slice into the batch's sums, item by item (each item's work
-  // starts as soon as its own loads are in).
-  auto mul_set = [&](Set& st, f32x4_t (&acc)[NB], float mu) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) relayout(xa[h][m]);
-#pragma unroll
-    for (int jj = 0; jj < NB; ++jj) {
-      const float sl = load_scale(st.it[jj], mu);
-      mul_item_half(st.it[jj], 0, acc[jj], sl);
-      mul_item_half(st.it[jj], 1, acc[jj], sl);
-    }
-  };
-
-  Set sets[kSets];
-  for (int j0 = 0; j0 < nrg; j0 += NB) {   // the workgroup's loop: barriers are uniform
-    // Only the first item's loads go out before the table build: the
-    // barrier after it waits for the slowest wave, and a wave issuing many
-    // loads into a full memory pipeline stalls for microseconds.  Then X
-    // (cache hits) and the other items.
-    load_item(sets[0].it[0], wave, j0);
-    if (j0 == 0) {
-      // byte -> level-pair table, behind the first loads (no memory waits)
-      const int lvl = level_lanes(lv);
-      for (int e = t; e < 256 * kCopies / 4; e += k16Waves * 64) {
-        const uint32_t b = (uint32_t)e / (kCopies / 4);
-        const uint32_t v = pack16x2<F16>(level_lookup(lvl, b >> 4), level_lookup(lvl, b & 15u));
-        *(uint4*)(tab + b * 256u + ((uint32_t)e % (kCopies / 4)) * 16u) = make_uint4(v, v, v, v);
-      }
-      if (DYN && t < 256) *(float*)(dmap + t * 4) = dmv;
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    load_x(wave, 0);
-    load_x(wave, 1);
-#pragma unroll
-    for (int jj = 1; jj < NB; ++jj) load_item(sets[0].it[jj], wave, j0 + jj);
-    if (MULTI) load_set(sets[kSets - 1], k16Waves + wave, j0);
-    const float mu = DQ ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mul))) : 0.0f;
-    f32x4_t acc[NB];
-#pragma unroll
-    for (int jj = 0; jj < NB; ++jj) acc[jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    if (!MULTI) {
-      mul_set(sets[0], acc, mu);
-    } else {
-      // Chunk c uses weight set c % 2 (one row group).  Once half h of
-      // chunk c is multiplied, half h of chunk c + 1's X goes into the same
-      // registers; once the whole chunk is, chunk c + 2's weights go into its
-      // set.
-      for (int c = 0; c < nchunks; c += 2) {
-        const int u = c * k16Waves + wave;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) relayout(xa[0][m]);
-        const float s0 = load_scale(sets[0].it[0], mu);
-        mul_item_half(sets[0].it[0], 0, acc[0], s0);
-        load_x(u + k16Waves, 0);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) relayout(xa[1][m]);
-        mul_item_half(sets[0].it[0], 1, acc[0], s0);
-        load_x(u + k16Waves, 1);
-        load_set(sets[0], u + 2 * k16Waves, j0);
-        if (c + 1 < nchunks) {   // workgroup-uniform, no loads inside
-#pragma unroll
-          for (int m = 0; m < 4; ++m) relayout(xa[0][m]);
-          const float s1 = load_scale(sets[kSets - 1].it[0], mu);
-          mul_item_half(sets[kSets - 1].it[0], 0, acc[0], s1);
-        }
-        load_x(u + 2 * k16Waves, 0);
-        if (c + 1 < nchunks) {
-#pragma unroll
-          for (int m = 0; m < 4; ++m) relayout(xa[1][m]);
-          const float s1 = load_scale(sets[kSets - 1].it[0], mu);
-          mul_item_half(sets[kSets - 1].it[0], 1, acc[0], s1);
-        }
-        load_x(u + 2 * k16Waves, 1);
-        load_set(sets[kSets - 1], u + 3 * k16Waves, j0);
-      }
-    }
-
-    // the batch's partial sums meet in LDS, kRed row groups at a time;
-    // Y[m][16 g + n] sits at lane 16 (m / 4) + n, value m % 4 of every
-    // wave's fragment
-#pragma unroll
-    for (int j1 = 0; j1 < NB; j1 += kRed) {
-#pragma unroll
-      for (int jj = 0; jj < kRed; ++jj)
-        *(f32x4_t*)(red + (jj * k16Waves + wave) * 256 + lane * 4) = acc[j1 + jj];
-      __syncthreads();
-      for (int e = t; e < kRed * 256; e += k16Waves * 64) {
-        const int jj = e >> 8, m = (e >> 4) & 15, nn = e & 15;
-        const int n = 16 * ((int)blockIdx.x + (j0 + j1 + jj) * (int)gridDim.x) + nn;
-        if (j0 + j1 + jj < nrg && m < M && n < N) {
-          const int src = ((m >> 2) * 16 + nn) * 4 + (m & 3);
-          float sum = 0.0f;
-#pragma unroll
-          for (int w = 0; w < k16Waves; ++w) sum += red[(jj * k16Waves + w) * 256 + src];
-          y[(int64_t)m * ldy + n] = f32_to_16<F16>(sum);
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
-
-// Scale layout of the M > 4 kernel: the four codes of a slice as one dword
-// (shared by a quad) when every row holds a multiple of 4 blocks and the
-// codes are 4-byte aligned (the four blocks then share one group), else one
-// code per lane.  NB, the
-// row groups a workgroup multiplies at once: up to 4 with one chunk of K,
-// 1 with several (two weight sets); larger counts spill registers.
-template <int SM, bool F16>
-hipError_t launch_gemv16_sm(int grid, int nb, bool multi, const uint16_t* x, int64_t ldx,
-                            const uint8_t* packed, const void* absmax, const float* absmax2,
-                            const float* mean, int M, int N, int K, uint16_t* y, int64_t ldy,
-                            const LevelTable& lv, hipStream_t stream) {
-#define BNBX_G16(NB, MULTI)                                                                    \
-  hipLaunchKernelGGL((gemv16_kernel<SM, F16, NB, MULTI>), dim3(grid), dim3(k16Waves * 64), 0, \
-                     stream, x, ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, lv)
-  if (multi) {
-    BNBX_G16(1, true);
-  } else if (nb == 1) {
-    BNBX_G16(1, false);
-  } else if (nb == 2) {
-    BNBX_G16(2, false);
-  } else {
-    BNBX_G16(4, false);
-  }
-#undef BNBX_G16
-  return hipGetLastError();
-}
-
-template <bool F16>
-hipError_t launch_gemv16(int grid, const uint16_t* x, int64_t ldx, const uint8_t* packed,
-                         const void* absmax, const float* absmax2, const float* mean, int dq,
-                         int M, int N, int K, uint16_t* y, int64_t ldy, const LevelTable& lv,
-                         hipStream_t stream) {
-  const bool multi = K > k16ChunkK;
-  const int ngroups = (N + 15) / 16;
-  const int per_wg = (ngroups + grid - 1) / grid;
-  const int nb = multi ? 1 : (per_wg >= 3 ? 4 : per_wg);
-  const bool rowq = dq && ((K >> 6) % 4 == 0) && ((uintptr_t)absmax & 3u) == 0;
-  if (dq == kDqDynamic && rowq)
-    return launch_gemv16_sm<kScaleDynRow, F16>(grid, nb, multi, x, ldx, packed, absmax, absmax2,
-                                               mean, M, N, K, y, ldy, lv, stream);
-  if (dq == kDqDynamic)
-    return launch_gemv16_sm<kScaleDynLane, F16>(grid, nb, multi, x, ldx, packed, absmax, absmax2,
-                                                mean, M, N, K, y, ldy, lv, stream);
-  if (rowq)
-    return launch_gemv16_sm<kScaleDqRow, F16>(grid, nb, multi, x, ldx, packed, absmax, absmax2,
-                                              mean, M, N, K, y, ldy, lv, stream);
-  if (dq)
-    return launch_gemv16_sm<kScaleDqLane, F16>(grid, nb, multi, x, ldx, packed, absmax, absmax2,
-                                               mean, M, N, K, y, ldy, lv, stream);
-  return launch_gemv16_sm<kScaleF32, F16>(grid, nb, multi, x, ldx, packed, absmax, absmax2, mean,
-                                          M, N, K, y, ldy, lv, stream);
-}
-
-// ---------------------------------------------------------------------------
-// host side: plan and dispatch
-// ---------------------------------------------------------------------------
-struct Plan {
-  int mm, ni, rr, twl, grid, xlds;
-};
-
-int cu_count() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        v > 0)
-      n = v;
-    else
-      n = 256;
-  }
-  return n;
-}
-
-// Largest rows-per-pass the registers allow for (mm, ni): the X slice takes
-// 16*mm*ni VGPRs and each row 6*ni more (weights and scales), within the
-// 128 VGPRs of four waves per SIMD.
-int rr_max(int mm, int ni) {
-  int r = (100 - 16 * mm * ni) / (6 * ni);
-  if (r > kMaxRR) r = kMaxRR;
-  if (r < 1) r = 1;
-  if (mm == 1 && ni == 3) r = 2;
-  if (mm == 1 && ni == 4) r = 1;
-  if (mm == 2 && ni == 2) r = 2;
-  return r;
-}
-
-// nicap: at most this many chunks per lane (the dynamic map's per-lane
-// scale mode spills registers at four).
-bool make_plan(int mm, int N, int K, Plan& p, int nicap = 4) {
-  const int C = K >> 5;
-  const int nimax = (4 / mm) < nicap ? (4 / mm) : nicap;
-  int best_twl = -1, best_ni = 0;
-  double best_util = 0.0;
-  for (int twl = 0; (1 << twl) <= kWaves; ++twl) {
-    const int S = 64 << twl;
-    const int ni = (C + S - 1) / S;
-    if (ni > nimax) continue;
-    const double util = (double)C / ((double)S * ni);
-    if (util > best_util + 1e-9) {
-      best_util = util;
-      best_twl = twl;
-      best_ni = ni;
-    }
-  }
-  if (best_twl < 0) return false;
-  const int tpw = kWaves >> best_twl;
-  const int cus = cu_count();
-  const int rmax = rr_max(mm, best_ni);
-  const int64_t slots = (int64_t)cus * tpw;   // teams resident at once
-  int64_t rr = ((int64_t)N + slots - 1) / slots;
-  if (rr < 1) rr = 1;
-  if (rr > rmax) rr = rmax;
-  int64_t grid = ((int64_t)N + tpw * rr - 1) / (tpw * rr);
-  if (grid > (int64_t)cus) grid = (int64_t)cus;
-  p.mm = mm;
-  p.ni = best_ni;
-  p.rr = (int)rr;
-  p.twl = best_twl;
-  p.grid = (int)grid;
-  p.xlds = (int64_t)mm * K * 2 <= kXBytes ? 1 : 0;
-  return true;
-}
-
-template <int MM, int NI, int RR, bool F16>
-hipError_t launch_k(const Plan& p, const uint16_t* x, int64_t ldx, const uint8_t* packed,
-                    const void* absmax, const float* absmax2, const float* mean, int dq,
-                    int mvalid, int N, int K, uint16_t* y, int64_t ldy, const LevelTable& lv,
-                    hipStream_t stream) {
-  const bool rowq = (K >> 6) <= 256 && (K >> 6) % 4 == 0 && ((uintptr_t)absmax & 3u) == 0;
-  int sm = kScaleF32;
-  if (dq == kDqDynamic)
-    sm = rowq ? kScaleDynRow : kScaleDynLane;
-  else if (dq)
-    sm = rowq ? kScaleDqRow : kScaleDqLane;
-#define BNBX_GEMV_SM(SMV)                                                                      \
-  if (sm == SMV)                                                                               \
-    hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, SMV, F16>), dim3(p.grid), dim3(kThreads), 0,   \
-                       stream, x, ldx, packed, absmax, absmax2, mean, mvalid, N, K, y, ldy,     \
-                       p.twl, p.xlds, lv);
-  BNBX_GEMV_SM(kScaleF32)
-  BNBX_GEMV_SM(kScaleDqLane)
-  BNBX_GEMV_SM(kScaleDqRow)
-  if constexpr (NI < 4) {
-    BNBX_GEMV_SM(kScaleDynLane)
-  } else {
-    if (sm == kScaleDynLane) return hipErrorNotSupported;   // planned out (nicap)
-  }
-  BNBX_GEMV_SM(kScaleDynRow)
-#undef BNBX_GEMV_SM
-  return hipGetLastError();
-}
-
-hipError_t dispatch(const Plan& p, const uint16_t* x, int64_t ldx, const uint8_t* packed,
-                    const void* absmax, const float* absmax2, const float* mean, int dq,
-                    int mvalid, int N, int K, uint16_t* y, int64_t ldy, const LevelTable& lv,
-                    bool f16, hipStream_t stream) {
-#define BNBX_GEMV_CASE(MM, NI, RR)                                                              \
-  if (p.mm == MM && p.ni == NI && p.rr == RR)                                                   \
-    return f16 ? launch_k<MM, NI, RR, true>(p, x, ldx, packed, absmax, absmax2, mean, dq, mvalid, \
-                                            N, K, y, ldy, lv, stream)                           \
-               : launch_k<MM, NI, RR, false>(p, x, ldx, packed, absmax, absmax2, mean, dq,      \
-                                             mvalid, N, K, y, ldy, lv, stream);
-  BNBX_GEMV_CASE(1, 1, 1) BNBX_GEMV_CASE(1, 1, 2) BNBX_GEMV_CASE(1, 1, 3) BNBX_GEMV_CASE(1, 1, 4)
-  BNBX_GEMV_CASE(1, 2, 1) BNBX_GEMV_CASE(1, 2, 2) BNBX_GEMV_CASE(1, 2, 3) BNBX_GEMV_CASE(1, 2, 4)
-  BNBX_GEMV_CASE(1, 3, 1) BNBX_GEMV_CASE(1, 3, 2)
-  BNBX_GEMV_CASE(1, 4, 1)
-  BNBX_GEMV_CASE(2, 1, 1) BNBX_GEMV_CASE(2, 1, 2) BNBX_GEMV_CASE(2, 1, 3) BNBX_GEMV_CASE(2, 1, 4)
-  BNBX_GEMV_CASE(2, 2, 1) BNBX_GEMV_CASE(2, 2, 2)
-  BNBX_GEMV_CASE(4, 1, 1) BNBX_GEMV_CASE(4, 1, 2) BNBX_GEMV_CASE(4, 1, 3) BNBX_GEMV_CASE(4, 1, 4)
-#undef BNBX_GEMV_CASE
-  return hipErrorNotSupported;
-}
-
-}  // namespace
 
 hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* packed, const void* absmax,
                        const float* absmax2, const float* mean, int double_quant, int quant_type,
@@ -918,11 +26,9 @@ hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* packed, co
       const void* am = double_quant ? (const void*)((const int8_t*)absmax + r0 * nkb)
                                     : (const void*)((const float*)absmax + r0 * nkb);
       const float* am2 = double_quant ? absmax2 + (r0 * nkb) / 256 : absmax2;
-      const hipError_t e =
-          f16 ? launch_gemv16<true>(grid, x, ldx, packed + r0 * rowK2, am, am2, mean, double_quant,
-                                    M, n, K, y + r0, ldy, lv, stream)
-              : launch_gemv16<false>(grid, x, ldx, packed + r0 * rowK2, am, am2, mean,
-                                     double_quant, M, n, K, y + r0, ldy, lv, stream);
+      const hipError_t e = launch_gemv16_batch(grid, x, ldx, packed + r0 * rowK2, am, am2, mean,
+                                               double_quant, f16, M, n, K, y + r0, ldy, lv,
+                                               stream);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;

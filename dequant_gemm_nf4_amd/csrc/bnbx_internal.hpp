@@ -123,6 +123,12 @@ hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* packed, co
                        const float* absmax2, const float* mean, int double_quant, int quant_type,
                        bool f16, int M, int N, int K, uint16_t* y, int64_t ldy,
                        hipStream_t stream);
+// 4 < M <= 16 rows of X over one slab of rows, one launch of `grid`
+// workgroups (bnbx_gemv16.hip).
+hipError_t launch_gemv16_batch(int grid, const uint16_t* x, int64_t ldx, const uint8_t* packed,
+                               const void* absmax, const float* absmax2, const float* mean,
+                               int dq, bool f16, int M, int N, int K, uint16_t* y, int64_t ldy,
+                               const LevelTable& lv, hipStream_t stream);
 hipError_t launch_gemm(const uint16_t* x, int64_t ldx, const uint8_t* packed, const void* absmax,
                        const float* absmax2, const float* mean, int double_quant, int quant_type,
                        bool f16, int M, int N, int K, uint16_t* y, int64_t ldy,
