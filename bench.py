@@ -457,6 +457,32 @@ def main():
 
     variants = None if args.no_variants else measure_variants()
 
+    # Grouped decode GEMV (bnbx_gemv_nf4_grouped), M=1: per layer of the
+    # stack, q, k, v in one call and gate, up in another (they share X), in
+    # one graph over all layers, beside the same weights launched one by one.
+    xg = xs[0]                                          # [1, 4096]
+    yq = [torch.empty(1, 4096, dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    yg = [torch.empty(1, 11008, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    per_layer = len(LAYER)
+    qkv = [[qs[l * per_layer + i] for i in range(3)] for l in range(L)]
+    gu = [[qs[l * per_layer + i] for i in (4, 5)] for l in range(L)]
+    reps_g = max(2, args.steps)
+    grouped = {}
+    for name, groups, outs, shape in (("qkv", qkv, yq, (4096, 4096)),
+                                      ("gate_up", gu, yg, (11008, 4096))):
+        nbytes = sum(gemv_bytes(1, *shape) for _ in groups[0])
+        g_ms = timed_ms(lambda: [T.gemv_grouped(xg, grp, outs=outs) for grp in groups],
+                        reps_g) / len(groups)
+        s_ms = timed_ms(lambda: [T.gemv(xg, q, out=o) for grp in groups
+                                 for q, o in zip(grp, outs)], reps_g) / len(groups)
+        grouped[name] = {"weights": f"{len(groups[0])} x {shape[0]}x{shape[1]}",
+                         "call_us": round(g_ms * 1e3, 3),
+                         "gbs": round(nbytes / (g_ms * 1e-3) / 1e9, 1),
+                         "hbm_frac": round(nbytes / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "separate_launches_us": round(s_ms * 1e3, 3),
+                         "separate_gbs": round(nbytes / (s_ms * 1e-3) / 1e9, 1)}
+    del yq, yg
+
     # Batched decode on the down projection, M=16 on 4096x11008 (K = 11008:
     # three 4096-k chunks per wave), one launch per weight, over 24 distinct
     # weights (540 MB), timed after the steps like the above.
@@ -600,6 +626,7 @@ def main():
                          "gbs": round(b_b / (us_b * 1e-6) / 1e9, 1),
                          "hbm_frac": round(b_b / (us_b * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                          "tflops": round(2.0 * Mb * Nb * Kb / (us_b * 1e-6) / 1e12, 2)},
+            "gemv_grouped": grouped,
             "gemv_m16_down": {"shape": f"{Mb}x{Nd}x{Kd}", "launches_per_call": 1,
                               "launch_us": round(down_us, 3),
                               "gbs": round(gemv_bytes(Mb, Nd, Kd) / (down_us * 1e-6) / 1e9, 1),

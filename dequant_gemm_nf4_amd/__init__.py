@@ -23,7 +23,8 @@ __all__ = [
     "bnbx_status_str", "bnbx_nf4_codebook", "bnbx_fp4_codebook", "bnbx_dynamic_map",
     "bnbx_quantize_nf4_workspace_bytes",
     "bnbx_quantize_nf4", "bnbx_quantize_nf4_noalloc", "BNBX_NOALLOC_MAX_WEIGHTS",
-    "bnbx_dequantize_nf4", "bnbx_gemv_nf4",
+    "bnbx_dequantize_nf4", "bnbx_gemv_nf4", "bnbx_gemv_nf4_grouped", "GemvItem",
+    "BNBX_GEMV_MAX_ITEMS",
     "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4", "bnbx_gemm_nf4_dx", "bnbx_gemm_nf4_lora",
     "bnbx_probe_stream_read", "BNBX_PROBE_SINK_WORDS", "EXPORTED_SYMBOLS", "BNBX_QUANT_NF4", "BNBX_QUANT_FP4",
     "BNBX_DTYPE_BF16", "BNBX_DTYPE_F16", "BNBX_DQ_NONE", "BNBX_DQ_LINEAR", "BNBX_DQ_DYNAMIC",
@@ -46,11 +47,13 @@ BNBX_DQ_LINEAR = 1
 BNBX_DQ_DYNAMIC = 2
 
 BNBX_NOALLOC_MAX_WEIGHTS = 1 << 28
+BNBX_GEMV_MAX_ITEMS = 4
 
 EXPORTED_SYMBOLS = (
     "bnbx_status_str", "bnbx_nf4_codebook", "bnbx_fp4_codebook", "bnbx_dynamic_map",
     "bnbx_quantize_nf4_workspace_bytes",
     "bnbx_quantize_nf4", "bnbx_quantize_nf4_noalloc", "bnbx_dequantize_nf4", "bnbx_gemv_nf4",
+    "bnbx_gemv_nf4_grouped",
     "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4", "bnbx_gemm_nf4_dx", "bnbx_gemm_nf4_lora",
     "bnbx_probe_stream_read",          # include/bnbx_probe.h (measurement aid)
 )
@@ -85,6 +88,19 @@ class Nf4State(ctypes.Structure):
         ("absmax", ctypes.c_void_p),
         ("absmax2", ctypes.c_void_p),
         ("absmax_mean", ctypes.c_void_p),
+    ]
+
+
+class GemvItem(ctypes.Structure):
+    """bnbx_gemv_item: one weight of a grouped GEMV (device pointers; the
+    state pointer is a host address)."""
+
+    _fields_ = [
+        ("packed", ctypes.c_void_p),
+        ("st", ctypes.POINTER(Nf4State)),
+        ("N", ctypes.c_int32),
+        ("y", ctypes.c_void_p),
+        ("ldy", ctypes.c_int64),
     ]
 
 
@@ -128,6 +144,8 @@ def lib() -> ctypes.CDLL:
     L.bnbx_dequantize_nf4.restype = i32
     L.bnbx_gemv_nf4.argtypes = [vp, i64, vp, sp, i32, i32, i32, vp, i64, vp]
     L.bnbx_gemv_nf4.restype = i32
+    L.bnbx_gemv_nf4_grouped.argtypes = [vp, i64, ctypes.POINTER(GemvItem), i32, i32, i32, vp]
+    L.bnbx_gemv_nf4_grouped.restype = i32
     L.bnbx_gemm_nf4_workspace_bytes.argtypes = [i32, i32, i32]
     L.bnbx_gemm_nf4_workspace_bytes.restype = sz
     L.bnbx_gemm_nf4.argtypes = [vp, i64, vp, sp, i32, i32, i32, vp, i64, vp, sz, vp]
@@ -217,6 +235,18 @@ def bnbx_gemv_nf4(x, ldx: int, packed, state: Nf4State, M: int, N: int, K: int, 
     _check(lib().bnbx_gemv_nf4(_ptr(x), int(ldx), _ptr(packed), ctypes.byref(state), int(M),
                                int(N), int(K), _ptr(y), int(ldy), _stream(stream)),
            "bnbx_gemv_nf4")
+
+
+def bnbx_gemv_nf4_grouped(x, ldx: int, items, M: int, K: int, stream=None) -> None:
+    """items: sequence of (packed, state, N, y, ldy)."""
+    n = len(items)
+    arr = (GemvItem * max(n, 1))()
+    states = [st for _, st, _, _, _ in items]    # kept alive for the call
+    for i, (packed, st, N, y, ldy) in enumerate(items):
+        arr[i] = GemvItem(_ptr(packed), ctypes.pointer(st), int(N), _ptr(y), int(ldy))
+    _check(lib().bnbx_gemv_nf4_grouped(_ptr(x), int(ldx), arr, n, int(M), int(K),
+                                       _stream(stream)), "bnbx_gemv_nf4_grouped")
+    del states
 
 
 def bnbx_gemm_nf4_workspace_bytes(M: int, N: int, K: int) -> int:

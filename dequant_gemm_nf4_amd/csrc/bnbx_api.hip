@@ -355,6 +355,30 @@ int bnbx_gemv_nf4(const uint16_t* x, int64_t ldx, const uint8_t* packed,
   return hip_status(e);
 }
 
+int bnbx_gemv_nf4_grouped(const uint16_t* x, int64_t ldx, const bnbx_gemv_item* items,
+                          int count, int M, int K, void* stream) {
+  if (items == nullptr || count < 1 || count > BNBX_GEMV_MAX_ITEMS) return BNBX_E_INVAL;
+  static_assert(BNBX_GEMV_MAX_ITEMS <= 4, "the grouped kernel takes at most four weights");
+  GemvItem it[BNBX_GEMV_MAX_ITEMS];
+  for (int w = 0; w < count; ++w) {
+    const bnbx_gemv_item& a = items[w];
+    const int s = check_matmul(x, ldx, a.packed, a.st, M, a.N, K, a.y, a.ldy);
+    if (s != BNBX_OK) return s;
+    const bnbx_nf4_state* s0 = items[0].st;
+    if (a.st->quant_type != s0->quant_type || a.st->compute_dtype != s0->compute_dtype ||
+        a.st->double_quant != s0->double_quant)
+      return BNBX_E_INVAL;
+    it[w] = GemvItem{a.packed, a.st->absmax, a.st->absmax2, a.st->absmax_mean, a.N, a.y, a.ldy};
+  }
+  if (M > 16) return BNBX_E_INVAL;
+  const bnbx_nf4_state* s0 = items[0].st;
+  const hipError_t e = launch_gemv_grouped(x, ldx, it, count, s0->double_quant, s0->quant_type,
+                                           s0->compute_dtype == BNBX_DTYPE_F16, M, K,
+                                           (hipStream_t)stream);
+  if (e == hipErrorNotSupported) return BNBX_E_UNSUPPORTED;
+  return hip_status(e);
+}
+
 size_t bnbx_gemm_nf4_workspace_bytes(int M, int N, int K) {
   (void)M;
   (void)N;

@@ -36,30 +36,25 @@ hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* packed, co
   // Rows of X in groups of up to four (each group streams W once); a group
   // of three runs the four-row kernel with its last row empty.  Long rows
   // take smaller groups (the X slice must fit the registers).
-  const bool dyn_lane = double_quant == kDqDynamic &&
-                        !(nkb <= 256 && nkb % 4 == 0 && ((uintptr_t)absmax & 3u) == 0);
-  const int nicap = dyn_lane ? 3 : 4;
+  const bool rowq = nkb <= 256 && nkb % 4 == 0 && ((uintptr_t)absmax & 3u) == 0;
+  const int nicap = double_quant == kDqDynamic && !rowq ? 3 : 4;
   for (int m0 = 0; m0 < M;) {
-    const int left = M - m0;
     Plan p;
-    int mv = 0;
-    for (int mm : {4, 2, 1}) {
-      if (left < (mm == 4 ? 3 : mm)) continue;       // a group of 3 uses mm = 4
-      if (make_plan(mm, N < slab ? N : (int)slab, K, p, nicap)) {
-        mv = left < mm ? left : mm;
-        break;
-      }
-    }
+    const int mv = next_x_group(M - m0, N < slab ? N : (int)slab, K, nicap, p);
     if (mv == 0) return hipErrorNotSupported;
     for (int64_t r0 = 0; r0 < N; r0 += slab) {
       const int n = (int)(N - r0 < slab ? N - r0 : slab);
       if (!make_plan(p.mm, n, K, p, nicap)) return hipErrorNotSupported;
-      const void* am = double_quant ? (const void*)((const int8_t*)absmax + r0 * nkb)
-                                    : (const void*)((const float*)absmax + r0 * nkb);
-      const float* am2 = double_quant ? absmax2 + (r0 * nkb) / 256 : absmax2;
-      const hipError_t e =
-          dispatch(p, x + (int64_t)m0 * ldx, ldx, packed + r0 * rowK2, am, am2, mean,
-                   double_quant, mv, n, K, y + (int64_t)m0 * ldy + r0, ldy, lv, f16, stream);
+      GemvOne it;
+      it.packed = packed + r0 * rowK2;
+      it.absmax = double_quant ? (const void*)((const int8_t*)absmax + r0 * nkb)
+                               : (const void*)((const float*)absmax + r0 * nkb);
+      it.absmax2 = double_quant ? absmax2 + (r0 * nkb) / 256 : absmax2;
+      it.mean = mean;
+      it.y = y + (int64_t)m0 * ldy + r0;
+      it.ldy = ldy;
+      const hipError_t e = dispatch<false>(p, x + (int64_t)m0 * ldx, ldx, it, 1, double_quant,
+                                           rowq, mv, n, K, lv, f16, stream);
       if (e != hipSuccess) return e;
     }
     m0 += mv;

@@ -46,6 +46,8 @@
 // multi-wave team adds its waves' sums through LDS.
 #pragma once
 
+#include <type_traits>
+
 #include "bnbx_device.hpp"
 #include "bnbx_internal.hpp"
 
@@ -60,6 +62,9 @@ constexpr int kTabBytes = 256 * 256;        // 256 B per byte value
 constexpr int kXBytes = 64 * 1024;
 constexpr int kMaxMM = 4;
 constexpr int kMaxRR = 4;
+// Rows per team in a grouped launch: more spill registers (the item lookups
+// of the rolling row window).
+constexpr int kMaxGroupRR = 3;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -118,14 +123,47 @@ __device__ __forceinline__ float dyn_map_value(int t) {
                                                   (uint32_t)(t & 255) * 4u, 0, 0));
 }
 
+// The weights of one launch: one (GemvOne), or (GRP) up to kMaxItems
+// weights that multiply the same X (GemvItems), their rows concatenated in
+// item order: item w owns rows [end[w-1], end[w]) (end[-1] = 0; entries
+// past the last item hold INT_MAX).  Y of item w, row m, is at
+// y[w] + m * ldy[w].  A single weight keeps the short argument block.
+constexpr int kMaxItems = 4;
+struct GemvOne {
+  const uint8_t* packed;
+  const void* absmax;
+  const float* absmax2;
+  const float* mean;
+  uint16_t* y;
+  int64_t ldy;
+};
+struct GemvItems {
+  int end[kMaxItems];
+  const uint8_t* packed[kMaxItems];
+  const void* absmax[kMaxItems];
+  const float* absmax2[kMaxItems];
+  const float* mean[kMaxItems];
+  uint16_t* y[kMaxItems];
+  int64_t ldy[kMaxItems];
+};
+
+// Field of item w by selects (indexing the argument struct with a run-time
+// w would copy it to scratch memory).
+template <typename T>
+__device__ __forceinline__ T pick_item(const T (&a)[kMaxItems], int w) {
+  return w == 0 ? a[0] : w == 1 ? a[1] : w == 2 ? a[2] : a[3];
+}
+
+template <bool GRP>
+using GemvArgs = typename std::conditional<GRP, GemvItems, GemvOne>::type;
+
 // MM rows of X per launch (rows >= mvalid are zero), NI chunks per lane, RR
-// rows of W per team and pass.  TW = 1 << twl waves per team.
-template <int MM, int NI, int RR, int SM, bool F16>
+// rows of W per team and pass.  TW = 1 << twl waves per team.  N rows in
+// all (of every item).
+template <int MM, int NI, int RR, int SM, bool F16, bool GRP>
 __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
-    const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ packed,
-    const void* __restrict__ absmax, const float* __restrict__ absmax2,
-    const float* __restrict__ mean, int mvalid, int N, int K, uint16_t* __restrict__ y,
-    int64_t ldy, int twl, int xlds, LevelTable lv) {
+    const uint16_t* __restrict__ x, int64_t ldx, GemvArgs<GRP> items, int nitems, int mvalid,
+    int N, int K, int twl, int xlds, LevelTable lv) {
   constexpr bool DQ = SM != kScaleF32;
   constexpr bool DYN = scale_dyn(SM);
   // One LDS block with the table at offset 0, so that a table address is the
@@ -157,8 +195,36 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
   const uint32_t xbytes = (uint32_t)K * 2u;
   const int64_t pass_rows = (int64_t)gridDim.x * tpw * RR;
   const int64_t rb_first = (int64_t)blockIdx.x * tpw * RR;   // workgroup's first row
-  const uint32_t ng_bytes = DQ ? (uint32_t)((((uint64_t)N * nkb + 255) >> 8) * 4) : 0u;
-  const rsrc_t rg = make_rsrc(absmax2, ng_bytes);
+
+  // The item of a row, the item's first and end rows, and its fields (item
+  // 0 and the single weight's fields without GRP).
+  auto item_of = [&](int64_t row) -> int {
+    if constexpr (GRP)
+      return (int)(row >= items.end[0]) + (int)(row >= items.end[1]) + (int)(row >= items.end[2]);
+    else
+      return 0;
+  };
+  auto item_start = [&](int wi) -> int64_t {
+    if constexpr (GRP)
+      return wi == 0 ? 0 : wi == 1 ? items.end[0] : wi == 2 ? items.end[1] : items.end[2];
+    else
+      return 0;
+  };
+  auto item_end = [&](int wi) -> int64_t {
+    if constexpr (GRP) return pick_item(items.end, wi); else return N;
+  };
+#define BNBX_ITEM_FIELD(NAME, T)                                   \
+  auto item_##NAME = [&](int wi) -> T {                            \
+    if constexpr (GRP) return pick_item(items.NAME, wi);           \
+    else return items.NAME;                                        \
+  };
+  BNBX_ITEM_FIELD(packed, const uint8_t*)
+  BNBX_ITEM_FIELD(absmax, const void*)
+  BNBX_ITEM_FIELD(absmax2, const float*)
+  BNBX_ITEM_FIELD(mean, const float*)
+  BNBX_ITEM_FIELD(y, uint16_t*)
+  BNBX_ITEM_FIELD(ldy, int64_t)
+#undef BNBX_ITEM_FIELD
 
   // Fixed per-lane offsets: chunk c of the row (bytes), its block (index).
   uint32_t woff[NI], boff[NI];
@@ -172,9 +238,14 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
   // 0. The mean, by lane 0 alone and before every other load: loads
   //    complete in issue order, so its first use (broadcast with
   //    v_readfirstlane) then waits for nothing else.
+  //    With GRP, lane w loads item w's mean.
   float mul = 0.0f;
-  if (DQ && lane == 0)
-    mul = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(mean, 4u), 0u, 0, 0));
+  if (GRP) {
+    if (DQ && lane < nitems) mul = *item_mean(lane);
+  } else if (DQ && lane == 0) {
+    mul = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(item_mean(0), 4u), 0u, 0, 0));
+  }
   const float dmv = DYN ? dyn_map_value(t) : 0.0f;
 
   // 1. X: staging loads (LDS path) or the lane's slice directly.
@@ -220,20 +291,26 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
   //    scales with scalar loads (a row spans at most two groups); otherwise
   //    every lane loads its own block's scales.
   constexpr bool rowsc = scale_row(SM);
-  const uint32_t ng = DQ ? (uint32_t)(((uint64_t)N * nkb + 255) >> 8) : 1u;
   uint4 w[RR][NI];
   int qv[RR][NI];
   float gv[RR][NI];
   int qd[RR];
   float gsl[RR];      // the row's group scales: g0 in even lanes, g1 in odd ones
   uint32_t split[RR];
+  // Loads of the team's rows that start at row rb (rows at or past N get
+  // empty resources).
   auto issue_part = [&](int64_t rb, int lo, int hi) {
 #pragma unroll
     for (int j = 0; j < RR; ++j) {
       if ((j + 1) * NI <= lo || j * NI >= hi) continue;
-      const int64_t row = rb + j;
-      const bool ok = row < N;
-      const rsrc_t rw = make_rsrc(packed + row * rowK2, ok ? rowK2 : 0u);
+      const bool ok = rb + j < N;
+      const int wi = item_of(ok ? rb + j : 0);
+      const int64_t row = rb + j - item_start(wi);   // row within its item
+      const uint32_t ng =
+          DQ ? (uint32_t)(((uint64_t)(item_end(wi) - item_start(wi)) * nkb + 255) >> 8) : 1u;
+      const rsrc_t rg = make_rsrc(item_absmax2(wi), DQ ? ng * 4u : 0u);
+      const void* const absmax = item_absmax(wi);
+      const rsrc_t rw = make_rsrc(item_packed(wi) + row * rowK2, ok ? rowK2 : 0u);
 #pragma unroll
       for (int i = 0; i < NI; ++i)
         if (j * NI + i >= lo && j * NI + i < hi) w[j][i] = buf_load16<2>(rw, woff[i]);   // nt
@@ -330,15 +407,24 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
     for (int i = 0; i < NI; ++i) read_x(i);
   }
 
-  issue_part(rb_first + (int64_t)team_l * RR, NI, RR * NI);
+  // In the first pass at most kRowWindow rows per team are in flight: the
+  // next ones are requested as rows are consumed, which keeps the memory
+  // pipeline fed evenly instead of with one burst per wave.
+  constexpr int kRowWindow = 2;
+  constexpr int kFirstRows = RR < kRowWindow ? RR : kRowWindow;
+  issue_part(rb_first + (int64_t)team_l * RR, NI, kFirstRows * NI);
   const uint32_t lanebyte = (uint32_t)(lane & (kCopies - 1)) << 2;
   // 4. Dequant-in-register dot products of one pass, one chunk at a time in
   //    load order, then the sums over the team and the stores.
-  auto pass = [&](int64_t rb) {
-    const float mu = DQ ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mul))) : 0.0f;
+  auto pass = [&](int64_t rb, bool first) {
     float acc[MM][RR];
 #pragma unroll
     for (int j = 0; j < RR; ++j) {
+      const float mu =
+          !DQ ? 0.0f
+              : GRP ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mul),
+                                                               item_of(rb + j < N ? rb + j : 0)))
+                    : __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mul)));
 #pragma unroll
       for (int m = 0; m < MM; ++m) acc[m][j] = 0.0f;
       // the row's (at most two) group factors, once per row: the steps
@@ -390,6 +476,8 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
         // Only one chunk's table addresses and pairs live at a time.
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (first && j + kRowWindow < RR)
+        issue_part(rb, (j + kRowWindow) * NI, (j + kRowWindow + 1) * NI);
     }
 #pragma unroll
     for (int j = 0; j < RR; ++j)
@@ -398,10 +486,15 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
     if (TW == 1) {
       if (lane == 63) {
 #pragma unroll
-        for (int j = 0; j < RR; ++j)
+        for (int j = 0; j < RR; ++j) {
+          if (rb + j >= N) continue;
+          const int wi = item_of(rb + j);
+          uint16_t* const yw = item_y(wi) + (rb + j - item_start(wi));
+          const int64_t ldw = item_ldy(wi);
 #pragma unroll
           for (int m = 0; m < MM; ++m)
-            if (rb + j < N && m < mvalid) y[(int64_t)m * ldy + rb + j] = f32_to_16<F16>(acc[m][j]);
+            if (m < mvalid) yw[(int64_t)m * ldw] = f32_to_16<F16>(acc[m][j]);
+        }
       }
     } else {
       if (lane == 63) {
@@ -415,7 +508,12 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
         const int m = lane / RR, j = lane - (lane / RR) * RR;
         float v = 0.0f;
         for (int u = 0; u < TW; ++u) v += red[((team_l * TW + u) * MM + m) * RR + j];
-        if (rb + j < N && m < mvalid) y[(int64_t)m * ldy + rb + j] = f32_to_16<F16>(v);
+        const int64_t row = rb + j;   // differs across these lanes
+        if (row < N && m < mvalid) {
+          // item_of and the fields by per-lane selects (row is not uniform)
+          const int wi = item_of(row);
+          item_y(wi)[(int64_t)m * item_ldy(wi) + (row - item_start(wi))] = f32_to_16<F16>(v);
+        }
       }
       __syncthreads();
     }
@@ -423,10 +521,10 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
   // The first pass uses the loads issued before the table build; later
   // passes (more rows than the grid holds at once) issue their own.  The
   // loop condition is the workgroup's, so its barriers are uniform.
-  pass(rb_first + (int64_t)team_l * RR);
+  pass(rb_first + (int64_t)team_l * RR, true);
   for (int64_t rb0 = rb_first + pass_rows; rb0 < N; rb0 += pass_rows) {
     issue(rb0 + (int64_t)team_l * RR);
-    pass(rb0 + (int64_t)team_l * RR);
+    pass(rb0 + (int64_t)team_l * RR, false);
   }
 }
 
@@ -460,12 +558,12 @@ int rr_max(int mm, int ni) {
   if (r < 1) r = 1;
   if (mm == 1 && ni == 3) r = 2;
   if (mm == 1 && ni == 4) r = 1;
+  if (mm == 1 && ni == 2) r = 6;   // 116-125 VGPRs, no spills (K = 4096 decode rows)
   if (mm == 2 && ni == 2) r = 2;
   return r;
 }
 
-// nicap: at most this many chunks per lane (the dynamic map's per-lane
-// scale mode spills registers at four).
+// nicap: at most this many chunks per lane (see launch_k).
 bool make_plan(int mm, int N, int K, Plan& p, int nicap = 4) {
   const int C = K >> 5;
   const int nimax = (4 / mm) < nicap ? (4 / mm) : nicap;
@@ -501,47 +599,59 @@ bool make_plan(int mm, int N, int K, Plan& p, int nicap = 4) {
   return true;
 }
 
-template <int MM, int NI, int RR, bool F16>
-hipError_t launch_k(const Plan& p, const uint16_t* x, int64_t ldx, const uint8_t* packed,
-                    const void* absmax, const float* absmax2, const float* mean, int dq,
-                    int mvalid, int N, int K, uint16_t* y, int64_t ldy, const LevelTable& lv,
+template <int MM, int NI, int RR, bool F16, bool GRP>
+hipError_t launch_k(const Plan& p, const uint16_t* x, int64_t ldx, const GemvArgs<GRP>& it,
+                    int nitems, int dq, bool rowq, int mvalid, int N, int K, const LevelTable& lv,
                     hipStream_t stream) {
-  const bool rowq = (K >> 6) <= 256 && (K >> 6) % 4 == 0 && ((uintptr_t)absmax & 3u) == 0;
+  if constexpr (GRP && RR > kMaxGroupRR) {
+    return hipErrorNotSupported;   // planned out (launch_gemv_grouped)
+  } else {
   int sm = kScaleF32;
   if (dq == kDqDynamic)
     sm = rowq ? kScaleDynRow : kScaleDynLane;
   else if (dq)
     sm = rowq ? kScaleDqRow : kScaleDqLane;
-#define BNBX_GEMV_SM(SMV)                                                                      \
-  if (sm == SMV)                                                                               \
-    hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, SMV, F16>), dim3(p.grid), dim3(kThreads), 0,   \
-                       stream, x, ldx, packed, absmax, absmax2, mean, mvalid, N, K, y, ldy,     \
-                       p.twl, p.xlds, lv);
+#define BNBX_GEMV_SM(SMV)                                                                       \
+  if (sm == SMV)                                                                                \
+    hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, SMV, F16, GRP>), dim3(p.grid), dim3(kThreads), \
+                       0, stream, x, ldx, it, nitems, mvalid, N, K, p.twl, p.xlds, lv);
+  // Four chunks per lane with per-lane scales spill registers for the
+  // dynamic map, and for both maps with GRP: those plans are capped at three
+  // chunks (nicap) and the variants not built.
   BNBX_GEMV_SM(kScaleF32)
-  BNBX_GEMV_SM(kScaleDqLane)
+  if constexpr (NI < 4 || !GRP) {
+    BNBX_GEMV_SM(kScaleDqLane)
+  } else {
+    if (sm == kScaleDqLane) return hipErrorNotSupported;
+  }
   BNBX_GEMV_SM(kScaleDqRow)
   if constexpr (NI < 4) {
     BNBX_GEMV_SM(kScaleDynLane)
   } else {
-    if (sm == kScaleDynLane) return hipErrorNotSupported;   // planned out (nicap)
+    if (sm == kScaleDynLane) return hipErrorNotSupported;
   }
   BNBX_GEMV_SM(kScaleDynRow)
 #undef BNBX_GEMV_SM
   return hipGetLastError();
+  }
 }
 
-hipError_t dispatch(const Plan& p, const uint16_t* x, int64_t ldx, const uint8_t* packed,
-                    const void* absmax, const float* absmax2, const float* mean, int dq,
-                    int mvalid, int N, int K, uint16_t* y, int64_t ldy, const LevelTable& lv,
+// Launch of the plan's (MM, NI, RR) instantiation over the items.  rowq:
+// the row-wise code reads apply (every item's codes 4-byte aligned, K/64 a
+// multiple of 4 and at most 256).
+template <bool GRP>
+hipError_t dispatch(const Plan& p, const uint16_t* x, int64_t ldx, const GemvArgs<GRP>& it,
+                    int nitems, int dq, bool rowq, int mvalid, int N, int K, const LevelTable& lv,
                     bool f16, hipStream_t stream) {
 #define BNBX_GEMV_CASE(MM, NI, RR)                                                              \
   if (p.mm == MM && p.ni == NI && p.rr == RR)                                                   \
-    return f16 ? launch_k<MM, NI, RR, true>(p, x, ldx, packed, absmax, absmax2, mean, dq, mvalid, \
-                                            N, K, y, ldy, lv, stream)                           \
-               : launch_k<MM, NI, RR, false>(p, x, ldx, packed, absmax, absmax2, mean, dq,      \
-                                             mvalid, N, K, y, ldy, lv, stream);
+    return f16 ? launch_k<MM, NI, RR, true, GRP>(p, x, ldx, it, nitems, dq, rowq, mvalid, N, K, \
+                                                 lv, stream)                                    \
+               : launch_k<MM, NI, RR, false, GRP>(p, x, ldx, it, nitems, dq, rowq, mvalid, N,  \
+                                                  K, lv, stream);
   BNBX_GEMV_CASE(1, 1, 1) BNBX_GEMV_CASE(1, 1, 2) BNBX_GEMV_CASE(1, 1, 3) BNBX_GEMV_CASE(1, 1, 4)
   BNBX_GEMV_CASE(1, 2, 1) BNBX_GEMV_CASE(1, 2, 2) BNBX_GEMV_CASE(1, 2, 3) BNBX_GEMV_CASE(1, 2, 4)
+  BNBX_GEMV_CASE(1, 2, 5) BNBX_GEMV_CASE(1, 2, 6)
   BNBX_GEMV_CASE(1, 3, 1) BNBX_GEMV_CASE(1, 3, 2)
   BNBX_GEMV_CASE(1, 4, 1)
   BNBX_GEMV_CASE(2, 1, 1) BNBX_GEMV_CASE(2, 1, 2) BNBX_GEMV_CASE(2, 1, 3) BNBX_GEMV_CASE(2, 1, 4)
@@ -549,6 +659,18 @@ hipError_t dispatch(const Plan& p, const uint16_t* x, int64_t ldx, const uint8_t
   BNBX_GEMV_CASE(4, 1, 1) BNBX_GEMV_CASE(4, 1, 2) BNBX_GEMV_CASE(4, 1, 3) BNBX_GEMV_CASE(4, 1, 4)
 #undef BNBX_GEMV_CASE
   return hipErrorNotSupported;
+}
+
+// Row groups of X for one launch each (up to four rows; a group of three
+// runs the four-row kernel with its last row empty; long rows take smaller
+// groups, the X slice must fit the registers): the next group's size and
+// its plan for N rows, or 0.
+int next_x_group(int left, int N, int K, int nicap, Plan& p) {
+  for (int mm : {4, 2, 1}) {
+    if (left < (mm == 4 ? 3 : mm)) continue;
+    if (make_plan(mm, N, K, p, nicap)) return left < mm ? left : mm;
+  }
+  return 0;
 }
 
 }  // namespace

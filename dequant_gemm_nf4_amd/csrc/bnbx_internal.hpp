@@ -123,6 +123,21 @@ hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* packed, co
                        const float* absmax2, const float* mean, int double_quant, int quant_type,
                        bool f16, int M, int N, int K, uint16_t* y, int64_t ldy,
                        hipStream_t stream);
+// One weight of a grouped GEMV (device pointers; Y row m at y + m * ldy).
+struct GemvItem {
+  const uint8_t* packed;
+  const void* absmax;
+  const float* absmax2;
+  const float* mean;
+  int N;
+  uint16_t* y;
+  int64_t ldy;
+};
+// Up to four weights with the same K, quant type, compute type and second
+// level that multiply the same X.
+hipError_t launch_gemv_grouped(const uint16_t* x, int64_t ldx, const GemvItem* items, int count,
+                               int double_quant, int quant_type, bool f16, int M, int K,
+                               hipStream_t stream);
 // 4 < M <= 16 rows of X over one slab of rows, one launch of `grid`
 // workgroups (bnbx_gemv16.hip).
 hipError_t launch_gemv16_batch(int grid, const uint16_t* x, int64_t ldx, const uint8_t* packed,

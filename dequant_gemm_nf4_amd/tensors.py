@@ -9,7 +9,8 @@ import dataclasses
 import torch
 
 from . import (Nf4State, bnbx_dequantize_nf4, bnbx_gemm_nf4, bnbx_gemm_nf4_dx, bnbx_gemm_nf4_lora,
-               bnbx_gemm_nf4_workspace_bytes, bnbx_gemv_nf4, bnbx_quantize_nf4, bnbx_quantize_nf4_workspace_bytes)
+               bnbx_gemm_nf4_workspace_bytes, bnbx_gemv_nf4, bnbx_gemv_nf4_grouped,
+               bnbx_quantize_nf4, bnbx_quantize_nf4_workspace_bytes)
 
 BLOCKSIZE = 64
 GROUP = 256
@@ -109,6 +110,20 @@ def gemv(x: torch.Tensor, q: QuantizedWeight, out: torch.Tensor | None = None,
     y = out if out is not None else torch.empty(M, N, dtype=q.dtype, device=x.device)
     bnbx_gemv_nf4(x, x.stride(0), q.packed, q.state, M, N, K, y, y.stride(0), stream)
     return y
+
+
+def gemv_grouped(x: torch.Tensor, qs: list, outs: list | None = None, stream=None) -> list:
+    """Y_i = X . W_hat_i^T for up to four weights sharing X [M, K] (M <= 16),
+    in one call (bnbx_gemv_nf4_grouped)."""
+    M, K = x.shape
+    ys = outs if outs is not None else [
+        torch.empty(M, q.shape[0], dtype=q.dtype, device=x.device) for q in qs]
+    for q in qs:
+        assert x.dtype == q.dtype and q.shape[1] == K
+    bnbx_gemv_nf4_grouped(x, x.stride(0),
+                          [(q.packed, q.state, q.shape[0], y, y.stride(0)) for q, y in zip(qs, ys)],
+                          M, K, stream)
+    return ys
 
 
 def gemm(x: torch.Tensor, q: QuantizedWeight, out: torch.Tensor | None = None,

@@ -225,6 +225,38 @@ BNBX_API int bnbx_gemv_nf4(const uint16_t* x, int64_t ldx, const uint8_t* packed
                   const bnbx_nf4_state* st, int M, int N, int K,
                   uint16_t* y, int64_t ldy, void* stream);
 
+/* One weight of a grouped decode GEMV. */
+typedef struct {
+  const uint8_t* packed;        /* device: the quantized [N, K] weight, 16-byte aligned */
+  const bnbx_nf4_state* st;     /* host descriptor (st->n == N*K), read during the call */
+  int32_t N;                    /* rows of this weight, >= 1 */
+  uint16_t* y;                  /* device: row m of this weight's Y at y + m*ldy */
+  int64_t ldy;                  /* >= N */
+} bnbx_gemv_item;
+
+/* Most weights one grouped GEMV takes. */
+#define BNBX_GEMV_MAX_ITEMS 4
+
+/* Grouped decode GEMV: Y_i = X . W_hat_i^T for up to BNBX_GEMV_MAX_ITEMS
+ * weights that multiply the same X (the q, k and v projections of an
+ * attention layer, or the gate and up projections of its MLP), 1 <= M <= 16.
+ * Same arithmetic and results as one bnbx_gemv_nf4 call per weight (mlqm.cn
+ * article sec. 3.4 and the sec. 7 pitfall: each weight is streamed once).
+ * For M <= 4 the weights' rows run as one launch per group of up to four
+ * rows of X, so the fixed part of a launch is paid once for all of them; for
+ * 4 < M <= 16 each weight gets its own launch of the batched kernel.
+ *   x, ldx      as bnbx_gemv_nf4
+ *   items       host array of `count` items, read during the call
+ *   count       1 .. BNBX_GEMV_MAX_ITEMS
+ *   M, K        rows of X and the common K of every weight
+ * Every item's state must have the same quant_type, compute_dtype and
+ * double_quant; each weight's packed bytes must stay below 2^31.
+ * Errors: as bnbx_gemv_nf4 for each item; BNBX_E_INVAL if items is NULL,
+ * count is out of range or the items' states differ; BNBX_E_UNSUPPORTED if
+ * a weight is too large for one launch. */
+BNBX_API int bnbx_gemv_nf4_grouped(const uint16_t* x, int64_t ldx, const bnbx_gemv_item* items,
+                                   int count, int M, int K, void* stream);
+
 /* Bytes of device workspace bnbx_gemm_nf4 needs for (M, N, K); the current
  * kernels need none, so it returns 0 for valid sizes. */
 BNBX_API size_t bnbx_gemm_nf4_workspace_bytes(int M, int N, int K);

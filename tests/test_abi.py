@@ -30,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 14
+    assert len(declared) == 15
     assert sorted(bnbx.EXPORTED_SYMBOLS) == declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -157,6 +157,31 @@ def test_dequantize_rejects():
         bnbx.BNBX_E_UNSUPPORTED
     assert status_of(bnbx.bnbx_dequantize_nf4, A, state(qt=5), B, 0) == bnbx.BNBX_E_INVAL
     assert status_of(bnbx.bnbx_dequantize_nf4, A, state(dt=2), B, 0) == bnbx.BNBX_E_INVAL
+
+
+def test_gemv_grouped_rejects():
+    """Checked on the host before any launch: item count, NULL items, states
+    that differ, and each item's own checks."""
+    f = bnbx.bnbx_gemv_nf4_grouped
+    K, N = 256, 64
+    n = N * K
+
+    def item(st=None, y=D, N_=N, ldy=N, packed=B):
+        return (packed, st if st is not None else state(n), N_, y, ldy)
+
+    ok = [item(), item()]
+    # a valid call would launch: only invalid ones are made here
+    assert status_of(f, A, K, [], 1, K, None) == bnbx.BNBX_E_INVAL                 # count 0
+    assert status_of(f, A, K, [item()] * 5, 1, K, None) == bnbx.BNBX_E_INVAL       # count 5
+    assert status_of(f, A, K, ok, 17, K, None) == bnbx.BNBX_E_INVAL                # M > 16
+    assert status_of(f, A, K, ok, 0, K, None) == bnbx.BNBX_E_INVAL                 # M < 1
+    assert status_of(f, A, K, [item(), item(state(n, qt=1))], 1, K, None) == bnbx.BNBX_E_INVAL
+    assert status_of(f, A, K, [item(), item(state(n, dt=1))], 1, K, None) == bnbx.BNBX_E_INVAL
+    assert status_of(f, A, K, [item(), item(state(n, dq=2))], 1, K, None) == bnbx.BNBX_E_INVAL
+    assert status_of(f, A, K, [item(), item(N_=N + 1)], 1, K, None) == bnbx.BNBX_E_INVAL  # n != N*K
+    assert status_of(f, A, K, [item(), item(ldy=N - 1)], 1, K, None) == bnbx.BNBX_E_INVAL
+    assert status_of(f, A, K, [item(), item(packed=B + 8)], 1, K, None) == bnbx.BNBX_E_ALIGN
+    assert status_of(f, A, K, [item(), item(y=None)], 1, K, None) == bnbx.BNBX_E_INVAL
 
 
 def test_probe_stream_read_rejects():
