@@ -68,15 +68,24 @@ def dequant_bytes(N, K):
     return n // 2 + nb + 4 * ng + 4 + 2 * n
 
 
+GEMV_SOURCES = ("bnbx_gemv_common.hpp", "bnbx_gemv.hip")   # the M=1 kernel and its launcher
+
+
+def gemv_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMV_SOURCES:
+        h.update(open(os.path.join(ROOT, "dequant_gemm_nf4_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
 def recorded_gemv_traffic():
     """Per-launch HBM bytes of the GEMV from the committed counter runs
     (profiles/gemv_traffic.txt), or None if the kernel source changed since."""
-    import hashlib
     try:
         rec = dict(line.split(None, 1) for line in open(os.path.join(ROOT, "profiles", "gemv_traffic.txt"))
                    if line.strip() and not line.startswith("#"))
-        src = open(os.path.join(ROOT, "dequant_gemm_nf4_amd", "csrc", "bnbx_gemv.hip"), "rb").read()
-        if hashlib.sha256(src).hexdigest() != rec["source_sha256"].strip():
+        if gemv_source_hash() != rec["source_sha256"].strip():
             return None
         return int(rec["bytes_per_launch"])
     except (OSError, KeyError, ValueError):
