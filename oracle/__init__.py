@@ -59,6 +59,7 @@ from .nf4 import (  # noqa: F401
     dequant_matmul_ref,
     dequant_matmul_dx_ref,
     lora_matmul_ref,
+    lora_down_ref,
     rel_frobenius,
     storage_bytes,
 )

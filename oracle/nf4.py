@@ -522,6 +522,18 @@ def lora_matmul_ref(x_bits: np.ndarray, packed: np.ndarray, state: dict, N: int,
     return dequant_matmul_ref(x_bits, packed, state, N, K, dtype) + xa @ b.T
 
 
+def lora_down_ref(x_bits: np.ndarray, a_bits: np.ndarray, scale: float, M: int, K: int,
+                  dtype: str = "bf16") -> np.ndarray:
+    """The adapter's scaled down-projection XA = s . X . A^T (QLoRA, pomoai.com
+    overview: low-rank adapters beside the frozen 4-bit base; A [r, K] is the
+    nn.Linear(K, r) weight, s the adapter's scale), X [M, K] and A in the
+    compute dtype, in binary64 (no rounding).  Library primitive: NumPy's
+    binary64 matmul."""
+    x = bits_to_f32(np.asarray(x_bits).reshape(M, K), dtype).astype(np.float64)
+    a = bits_to_f32(np.asarray(a_bits).reshape(-1, K), dtype).astype(np.float64)
+    return float(scale) * (x @ a.T)
+
+
 def rel_frobenius(y, y_ref) -> float:
     """||y - y_ref||_F / ||y_ref||_F in binary64."""
     y = np.asarray(y, dtype=np.float64)

@@ -855,3 +855,31 @@ def test_lora_reference_adds_the_low_rank_term():
     for m in range(M):
         for n in range(N):
             assert abs(got[m, n] - bf[n, (3 * m) % r]) <= 1e-12
+
+
+def test_lora_down_reference_pins():
+    """XA = s . X . A^T: one-hot rows of X pick scaled columns of A exactly,
+    a brute-force triple loop agrees on a small case, and s = 0 gives 0."""
+    rng = np.random.default_rng(77)
+    M, K, r = 5, 64, 16
+    a_f = rng.standard_normal((r, K)).astype(np.float32)
+    a = oracle.f32_to_bf16_bits(a_f)
+    a64 = oracle.bf16_bits_to_f32(a).astype(np.float64).reshape(r, K)
+    ks = [0, 7, 31, 32, 63]
+    x = np.zeros((M, K), np.uint16)
+    x[np.arange(M), ks] = 0x3F80                          # 1.0
+    got = oracle.lora_down_ref(x, a, 0.5, M, K)
+    assert np.array_equal(got, 0.5 * a64[:, ks].T)
+    xf = rng.standard_normal((M, K)).astype(np.float32)
+    xb = oracle.f32_to_bf16_bits(xf)
+    x64 = oracle.bf16_bits_to_f32(xb).astype(np.float64).reshape(M, K)
+    want = np.zeros((M, r))
+    for m in range(M):
+        for j in range(r):
+            acc = 0.0
+            for k in range(K):
+                acc += x64[m, k] * a64[j, k]
+            want[m, j] = 2.0 * acc
+    assert np.allclose(oracle.lora_down_ref(xb, a, 2.0, M, K), want, rtol=1e-12, atol=1e-12)
+    assert not np.any(oracle.lora_down_ref(xb, a, 0.0, M, K))
+
