@@ -527,10 +527,16 @@ def main():
     for r in (16, 64):
         gen.manual_seed(7100 + r)
         lora_in[r] = ((torch.randn(Mp, r, generator=gen, device=dev) * 0.5).to(torch.bfloat16),
-                      (torch.randn(Np, r, generator=gen, device=dev) * 0.05).to(torch.bfloat16))
+                      (torch.randn(Np, r, generator=gen, device=dev) * 0.05).to(torch.bfloat16),
+                      (torch.randn(r, Kp, generator=gen, device=dev) * 0.02).to(torch.bfloat16))
     fns = {"plain": lambda: T.gemm(xp, qp, out=yp)}
-    for r, (xa, lb) in lora_in.items():
+    for r, (xa, lb, la) in lora_in.items():
         fns[f"r{r}"] = (lambda xa=xa, lb=lb: T.gemm_lora(xp, qp, xa, lb, out=yp))
+        # the adapter's down-projection in the library too: XA = s X A^T, then
+        # the GEMM with the low-rank epilogue
+        fns[f"r{r}_down"] = (lambda xa=xa, la=la: T.lora_down(xp, la, 2.0, out=xa))
+        fns[f"r{r}_full"] = (lambda xa=xa, lb=lb, la=la: (T.lora_down(xp, la, 2.0, out=xa),
+                                                          T.gemm_lora(xp, qp, xa, lb, out=yp)))
     graphs = {}
     for name, fn in fns.items():
         fn()
@@ -557,7 +563,12 @@ def main():
         ms = med[f"r{r}"]
         lora[f"r{r}"] = {"ms": round(ms, 4),
                          "tflops": round(2.0 * Mp * Np * (Kp + r) / (ms * 1e-3) / 1e12, 1),
-                         "over_plain": round(ms / plain_ms, 4)}
+                         "over_plain": round(ms / plain_ms, 4),
+                         "down_ms": round(med[f"r{r}_down"], 4),
+                         "down_gbs": round(2.0 * (Mp * Kp + r * Kp + Mp * r) /
+                                           (med[f"r{r}_down"] * 1e-3) / 1e9, 1),
+                         "with_down_ms": round(med[f"r{r}_full"], 4),
+                         "with_down_over_plain": round(med[f"r{r}_full"] / plain_ms, 4)}
     del graphs, lora_in
 
     t_q = stage_ms(0) / 1e3

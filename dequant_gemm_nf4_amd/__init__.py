@@ -26,7 +26,7 @@ __all__ = [
     "bnbx_dequantize_nf4", "bnbx_gemv_nf4", "bnbx_gemv_nf4_grouped", "GemvItem",
     "BNBX_GEMV_MAX_ITEMS",
     "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4", "bnbx_gemm_nf4_dx", "bnbx_gemm_nf4_lora",
-    "bnbx_probe_stream_read", "BNBX_PROBE_SINK_WORDS", "EXPORTED_SYMBOLS", "BNBX_QUANT_NF4", "BNBX_QUANT_FP4",
+    "bnbx_lora_down", "bnbx_probe_stream_read", "BNBX_PROBE_SINK_WORDS", "EXPORTED_SYMBOLS", "BNBX_QUANT_NF4", "BNBX_QUANT_FP4",
     "BNBX_DTYPE_BF16", "BNBX_DTYPE_F16", "BNBX_DQ_NONE", "BNBX_DQ_LINEAR", "BNBX_DQ_DYNAMIC",
 ]
 
@@ -55,6 +55,7 @@ EXPORTED_SYMBOLS = (
     "bnbx_quantize_nf4", "bnbx_quantize_nf4_noalloc", "bnbx_dequantize_nf4", "bnbx_gemv_nf4",
     "bnbx_gemv_nf4_grouped",
     "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4", "bnbx_gemm_nf4_dx", "bnbx_gemm_nf4_lora",
+    "bnbx_lora_down",
     "bnbx_probe_stream_read",          # include/bnbx_probe.h (measurement aid)
 )
 BNBX_PROBE_SINK_WORDS = 1024
@@ -155,6 +156,8 @@ def lib() -> ctypes.CDLL:
     L.bnbx_gemm_nf4_lora.restype = i32
     L.bnbx_gemm_nf4_dx.argtypes = [vp, i64, vp, sp, i32, i32, i32, vp, i64, vp]
     L.bnbx_gemm_nf4_dx.restype = i32
+    L.bnbx_lora_down.argtypes = [vp, i64, vp, i64, i32, i32, i32, ctypes.c_float, i32, vp, i64, vp]
+    L.bnbx_lora_down.restype = i32
     L.bnbx_probe_stream_read.argtypes = [vp, sz, vp, sz, vp, vp]
     L.bnbx_probe_stream_read.restype = i32
     _lib = L
@@ -273,6 +276,13 @@ def bnbx_gemm_nf4_dx(dy, lddy: int, packed, state: Nf4State, M: int, N: int, K: 
     _check(lib().bnbx_gemm_nf4_dx(_ptr(dy), int(lddy), _ptr(packed), ctypes.byref(state), int(M),
                                   int(N), int(K), _ptr(dx), int(lddx), _stream(stream)),
            "bnbx_gemm_nf4_dx")
+
+
+def bnbx_lora_down(x, ldx: int, lora_a, lda: int, M: int, K: int, r: int, scale: float,
+                   compute_dtype: int, xa, ldxa: int, stream=None) -> None:
+    _check(lib().bnbx_lora_down(_ptr(x), int(ldx), _ptr(lora_a), int(lda), int(M), int(K), int(r),
+                                float(scale), int(compute_dtype), _ptr(xa), int(ldxa),
+                                _stream(stream)), "bnbx_lora_down")
 
 
 def _nbytes(t) -> int | None:

@@ -15,7 +15,7 @@ LIB = os.path.join(PKG, "libbnbx.so")
 SOURCES = ["bnbx_api.hip", "bnbx_quant.hip", "bnbx_dequant.hip", "bnbx_gemv.hip", "bnbx_gemv16.hip",
            "bnbx_gemv_grouped.hip",
            "bnbx_gemm.hip",
-           "bnbx_gemm_dx.hip", "bnbx_probe.hip"]
+           "bnbx_gemm_dx.hip", "bnbx_lora.hip", "bnbx_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -379,6 +379,22 @@ int bnbx_gemv_nf4_grouped(const uint16_t* x, int64_t ldx, const bnbx_gemv_item* 
   return hip_status(e);
 }
 
+int bnbx_lora_down(const uint16_t* x, int64_t ldx, const uint16_t* lora_a, int64_t lda, int M,
+                   int K, int r, float scale, int compute_dtype, uint16_t* xa, int64_t ldxa,
+                   void* stream) {
+  if (x == nullptr || lora_a == nullptr || xa == nullptr) return BNBX_E_INVAL;
+  if (compute_dtype != BNBX_DTYPE_BF16 && compute_dtype != BNBX_DTYPE_F16) return BNBX_E_INVAL;
+  if (M < 1 || K < 32 || K % 32 != 0 || r < 16 || r > 256 || r % 16 != 0) return BNBX_E_INVAL;
+  if (ldx < K || lda < K || ldxa < r) return BNBX_E_INVAL;
+  if (ldx % 8 != 0 || lda % 8 != 0) return BNBX_E_ALIGN;
+  if (!aligned(x, 16) || !aligned(lora_a, 16) || !aligned(xa, 2)) return BNBX_E_ALIGN;
+  const hipError_t e = launch_lora_down(x, ldx, lora_a, lda, M, K, r, scale,
+                                        compute_dtype == BNBX_DTYPE_F16, xa, ldxa,
+                                        (hipStream_t)stream);
+  if (e == hipErrorNotSupported) return BNBX_E_UNSUPPORTED;
+  return hip_status(e);
+}
+
 size_t bnbx_gemm_nf4_workspace_bytes(int M, int N, int K) {
   (void)M;
   (void)N;

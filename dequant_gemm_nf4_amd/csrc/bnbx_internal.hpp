@@ -154,6 +154,11 @@ hipError_t launch_gemm_lora(const uint16_t* x, int64_t ldx, const uint8_t* packe
                             int double_quant, int quant_type, bool f16, int M, int N, int K,
                             const uint16_t* xa, int64_t ldxa, const uint16_t* lora_b,
                             int64_t ldb, int r, uint16_t* y, int64_t ldy, hipStream_t stream);
+// XA[M, r] = rnd(fl32(s * X . A^T)), A [r, K], 16 <= r <= 256, r % 16 == 0,
+// K % 32 == 0.
+hipError_t launch_lora_down(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t lda,
+                            int M, int K, int r, float scale, bool f16, uint16_t* xa,
+                            int64_t ldxa, hipStream_t stream);
 // dX[M, K] = dY[M, N] . W_hat[N, K]; hipErrorNotSupported unless N % 64 == 0
 // and the offsets fit 32 bits.
 hipError_t launch_gemm_dx(const uint16_t* dy, int64_t lddy, const uint8_t* packed,

@@ -9,7 +9,7 @@ import dataclasses
 import torch
 
 from . import (Nf4State, bnbx_dequantize_nf4, bnbx_gemm_nf4, bnbx_gemm_nf4_dx, bnbx_gemm_nf4_lora,
-               bnbx_gemm_nf4_workspace_bytes, bnbx_gemv_nf4, bnbx_gemv_nf4_grouped,
+               bnbx_gemm_nf4_workspace_bytes, bnbx_gemv_nf4, bnbx_gemv_nf4_grouped, bnbx_lora_down,
                bnbx_quantize_nf4, bnbx_quantize_nf4_workspace_bytes)
 
 BLOCKSIZE = 64
@@ -161,3 +161,24 @@ def gemm_lora(x: torch.Tensor, q: QuantizedWeight, xa: torch.Tensor, lora_b: tor
     bnbx_gemm_nf4_lora(x, x.stride(0), q.packed, q.state, M, N, K, xa, xa.stride(0), lora_b,
                        lora_b.stride(0), r, y, y.stride(0), stream)
     return y
+
+
+def lora_down(x: torch.Tensor, lora_a: torch.Tensor, scale: float,
+              out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """XA = s . X . A^T for X [M, K] and the adapter weight A [r, K]."""
+    M, K = x.shape
+    r = lora_a.shape[0]
+    assert x.dtype == lora_a.dtype and lora_a.shape[1] == K
+    xa = out if out is not None else torch.empty(M, r, dtype=x.dtype, device=x.device)
+    bnbx_lora_down(x, x.stride(0), lora_a, lora_a.stride(0), M, K, r, scale, DTYPES[x.dtype], xa,
+                   xa.stride(0), stream)
+    return xa
+
+
+def linear_lora(x: torch.Tensor, q: QuantizedWeight, lora_a: torch.Tensor, lora_b: torch.Tensor,
+                scale: float, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Y = X . W_hat^T + s . (X . A^T) . B^T: the down-projection, then the GEMM
+    with the low-rank term in its epilogue (both in the library)."""
+    xa = lora_down(x, lora_a, scale, stream=stream)
+    return gemm_lora(x, q, xa, lora_b, out=out, stream=stream)
+

@@ -293,6 +293,25 @@ BNBX_API int bnbx_gemm_nf4_lora(const uint16_t* x, int64_t ldx, const uint8_t* p
                        const uint16_t* xa, int64_t ldxa, const uint16_t* lora_b, int64_t ldb,
                        int r, uint16_t* y, int64_t ldy, void* stream);
 
+/* LoRA down-projection, XA = rnd(fl32(s . X . A^T)) with fp32 accumulation:
+ * the adapter input that bnbx_gemm_nf4_lora takes (pomoai.com overview,
+ * QLoRA: trainable low-rank adapters beside the frozen 4-bit base; A is the
+ * adapter's nn.Linear(K, r) weight, s its scale).  Values are of
+ * compute_dtype (BNBX_DTYPE_BF16 or BNBX_DTYPE_F16).
+ *   x       device, X [M, K], row m at x + m*ldx; ldx >= K, ldx % 8 == 0,
+ *           16-byte aligned
+ *   lora_a  device, A [r, K], row j at lora_a + j*lda; lda >= K, lda % 8 == 0,
+ *           16-byte aligned
+ *   M, K, r M >= 1; K a multiple of 32; r a multiple of 16, 16 <= r <= 256
+ *   scale   s, applied once to the fp32 sum before the rounding
+ *   xa      device, XA [M, r], row m at xa + m*ldxa; ldxa >= r (written)
+ * The sum over K runs in a fixed order, so results repeat bit for bit.
+ * Errors: BNBX_E_INVAL (null, sizes, compute_dtype), BNBX_E_ALIGN,
+ * BNBX_E_UNSUPPORTED (leading dimensions too large for 32-bit offsets). */
+BNBX_API int bnbx_lora_down(const uint16_t* x, int64_t ldx, const uint16_t* lora_a, int64_t lda,
+                            int M, int K, int r, float scale, int compute_dtype, uint16_t* xa,
+                            int64_t ldxa, void* stream);
+
 /* Input gradient of the 4-bit linear layer, dX[M, K] = dY[M, N] . W_hat[N, K]
  * (the weights stay frozen, as for the 4-bit base layer under QLoRA in the
  * pomoai.com overview; W_hat as in bnbx_dequantize_nf4, mlqm.cn article

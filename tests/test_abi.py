@@ -30,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 15
+    assert len(declared) == 16
     assert sorted(bnbx.EXPORTED_SYMBOLS) == declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -182,6 +182,34 @@ def test_gemv_grouped_rejects():
     assert status_of(f, A, K, [item(), item(ldy=N - 1)], 1, K, None) == bnbx.BNBX_E_INVAL
     assert status_of(f, A, K, [item(), item(packed=B + 8)], 1, K, None) == bnbx.BNBX_E_ALIGN
     assert status_of(f, A, K, [item(), item(y=None)], 1, K, None) == bnbx.BNBX_E_INVAL
+
+
+def test_lora_down_rejects():
+    f = bnbx.bnbx_lora_down
+    K, r = 256, 16
+    ok = dict(x=A, ldx=K, a=B, lda=K, M=4, K=K, r=r, s=1.0, dt=0, xa=C, ldxa=r)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return status_of(f, a["x"], a["ldx"], a["a"], a["lda"], a["M"], a["K"], a["r"], a["s"],
+                         a["dt"], a["xa"], a["ldxa"], None)
+
+    assert call(x=None) == bnbx.BNBX_E_INVAL
+    assert call(a=None) == bnbx.BNBX_E_INVAL
+    assert call(xa=None) == bnbx.BNBX_E_INVAL
+    assert call(dt=2) == bnbx.BNBX_E_INVAL
+    assert call(M=0) == bnbx.BNBX_E_INVAL
+    assert call(K=48, ldx=48, lda=48) == bnbx.BNBX_E_INVAL        # K % 32
+    assert call(r=8) == bnbx.BNBX_E_INVAL
+    assert call(r=24) == bnbx.BNBX_E_INVAL
+    assert call(r=272, ldxa=272) == bnbx.BNBX_E_INVAL
+    assert call(ldx=K - 8) == bnbx.BNBX_E_INVAL
+    assert call(lda=K - 8) == bnbx.BNBX_E_INVAL
+    assert call(ldxa=r - 1) == bnbx.BNBX_E_INVAL
+    assert call(ldx=K + 4) == bnbx.BNBX_E_ALIGN
+    assert call(x=A + 8) == bnbx.BNBX_E_ALIGN
+    assert call(a=B + 2) == bnbx.BNBX_E_ALIGN
+    assert call(xa=C + 1) == bnbx.BNBX_E_ALIGN
 
 
 def test_probe_stream_read_rejects():

@@ -50,3 +50,72 @@ def test_lora_zero_adapter_equals_plain_gemm():
     y2 = T.gemm_lora(x, q, xa, zb)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+# --------------------------------------------------------------------------
+# the adapter's down-projection inside the library (bnbx_lora_down)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("M,K,r", [(1, 64, 16), (7, 1024, 48), (16, 4096, 64), (300, 512, 256),
+                                   (2048, 8192, 16), (33, 8192, 128)])
+def test_lora_down_against_oracle(M, K, r, dt):
+    x = synth.normal_16((M, K), 1.0, 9900 + M, dt)
+    a = synth.normal_16((r, K), 0.02, 9901 + r, dt)
+    print(f"lora_down M={M} K={K} r={r} {dt}", flush=True)
+    xa = T.lora_down(dev_bf16(x, (M, K), dt), dev_bf16(a, (r, K), dt), 0.75)
+    torch.cuda.synchronize()
+    got = oracle.bits_to_f32(host_bits(xa), dt).astype(np.float64).reshape(M, r)
+    err = product_error(got, oracle.lora_down_ref(x, a, 0.75, M, K, dt))
+    assert err <= TOL, err
+
+
+def test_lora_down_one_hot_rows_are_scaled_adapter_columns():
+    """X = unit rows: XA[m] = rnd(0.5 * A[:, k_m]), exactly (one product by
+    1.0, sums of zeros, a scale by a power of two)."""
+    M, K, r = 40, 1024, 32
+    a = synth.normal_16((r, K), 0.02, 9910)
+    ks = (np.arange(M) * 37 + 3) % K
+    x = np.zeros((M, K), np.uint16)
+    x[np.arange(M), ks] = 0x3F80
+    xa = T.lora_down(dev_bf16(x, (M, K)), dev_bf16(a, (r, K)), 0.5)
+    torch.cuda.synchronize()
+    a64 = oracle.bf16_bits_to_f32(a).astype(np.float64).reshape(r, K)
+    want = oracle.f32_to_bits((0.5 * a64[:, ks].T).astype(np.float32), "bf16")
+    assert np.array_equal(host_bits(xa).reshape(M, r), want.reshape(M, r))
+
+
+def test_lora_down_repeats_bit_for_bit_and_writes_only_its_block():
+    M, K, r = 300, 2048, 64
+    x = dev_bf16(synth.normal_16((M, K), 1.0, 9920), (M, K))
+    a = dev_bf16(synth.normal_16((r, K), 0.02, 9921), (r, K))
+    big = torch.full((M, r + 32), 7.0, dtype=torch.bfloat16, device="cuda")
+    T.lora_down(x, a, 1.0, out=big[:, :r])
+    first = big.clone()
+    T.lora_down(x, a, 1.0, out=big[:, :r])
+    torch.cuda.synchronize()
+    assert torch.equal(first, big)
+    assert torch.all(big[:, r:] == 7.0)
+
+
+@pytest.mark.parametrize("qt,dt", [("nf4", "bf16"), ("fp4", "f16")])
+def test_linear_lora_end_to_end(qt, dt):
+    """Y = X . W_hat^T + s . (X . A^T) . B^T through the two library calls
+    (the down-projection, then the GEMM with the low-rank epilogue)."""
+    M, N, K, r = 257, 384, 1024, 32
+    w = synth.normal_bf16((N, K), 0.02, 9930)
+    x = synth.normal_16((M, K), 1.0, 9931, dt)
+    a = synth.normal_16((r, K), 0.02, 9932, dt)
+    b = synth.normal_16((N, r), 0.05, 9933, dt)
+    ref = oracle.quantize(w, True, quant_type=qt)
+    y = T.linear_lora(dev_bf16(x, (M, K), dt), upload_state(ref, (N, K), dt),
+                      dev_bf16(a, (r, K), dt), dev_bf16(b, (N, r), dt), 2.0)
+    torch.cuda.synchronize()
+    got = oracle.bits_to_f32(host_bits(y), dt).astype(np.float64).reshape(M, N)
+    xa = oracle.lora_down_ref(x, a, 2.0, M, K, dt)
+    b64 = oracle.bits_to_f32(b, dt).astype(np.float64).reshape(N, r)
+    want = oracle.dequant_matmul_ref(x, ref["packed"], ref, N, K, dt) + xa @ b64.T
+    err = product_error(got, want)
+    assert err <= TOL, err
+    base = oracle.dequant_matmul_ref(x, ref["packed"], ref, N, K, dt)
+    assert oracle.rel_frobenius(base, want) > 10 * TOL
+
