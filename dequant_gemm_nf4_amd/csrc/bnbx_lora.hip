@@ -4,12 +4,13 @@
 // nn.Linear(K, r) weight, s its scale).  XA then feeds the fused low-rank
 // term of the 4-bit GEMM's epilogue (bnbx_gemm_nf4_lora), which adds XA . B^T.
 //
-// One workgroup of 8 waves takes 16 rows of X and all r columns; wave w takes
-// the w-th eighth of K (in steps of 32) and runs v_mfma_f32_16x16x32 with X
+// One workgroup of W waves (16 for r <= 128, else 8) takes 16 rows of X and
+// all r columns; wave w takes the w-th of W parts of K (in steps of 32, four
+// steps' loads in flight) and runs v_mfma_f32_16x16x32 with X
 // as the A operand (lane l: row l % 16, k 8 (l / 16) .. +8 of the step) and
 // rows of the adapter weight as the B operand in the same lane layout, one
-// accumulator per 16 columns.  The eight waves' partial sums are added in LDS
-// in wave order (a fixed order: the result does not depend on timing), scaled
+// accumulator per 16 columns.  The waves' partial sums are added in LDS in
+// wave order (a fixed order: the result does not depend on timing), scaled
 // once and rounded once to the compute type.  Rows of X past M and rows of A
 // past r read zero through the buffer range check.
 #include "bnbx_device.hpp"
@@ -17,9 +18,6 @@
 
 namespace bnbx {
 namespace {
-
-constexpr int kLWaves = 8;
-constexpr int kLThreads = kLWaves * 64;
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -29,10 +27,12 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 }
 
 // RT column tiles of 16 (r <= 16 RT); kq: K per wave, a multiple of 32.
-template <bool F16, int RT>
-__global__ __launch_bounds__(kLThreads) void lora_down_kernel(
+template <bool F16, int RT, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void lora_down_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ a, int64_t lda,
     int M, int K, int r, float scale, uint16_t* __restrict__ xa, int64_t ldxa, int kq) {
+  constexpr int kLWaves = WAVES;
+  constexpr int kLThreads = WAVES * 64;
   __shared__ f32x4_t red[kLWaves][RT][64];
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kLThreads) void lora_down_kernel(
   for (int c = 0; c < RT; ++c) acc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   const int k0 = wave * kq;
   const int k1 = k0 + kq < K ? k0 + kq : K;
-#pragma unroll 2
+#pragma unroll 4
   for (int k = k0; k < k1; k += 32) {
     const uint32_t kb = (uint32_t)k * 2u;
     const u32x4_t xv = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, kb, 0);
@@ -86,11 +86,11 @@ hipError_t launch_rt(int rt, const uint16_t* x, int64_t ldx, const uint16_t* a, 
                      int M, int K, int r, float scale, uint16_t* xa, int64_t ldxa,
                      hipStream_t stream) {
   const int64_t grid = ((int64_t)M + 15) / 16;
-  int kq = (K + kLWaves - 1) / kLWaves;
-  kq = (kq + 31) / 32 * 32;
 #define BNBX_LORA_RT(RT)                                                                       \
   if (rt == RT) {                                                                              \
-    hipLaunchKernelGGL((lora_down_kernel<F16, RT>), dim3((unsigned)grid), dim3(kLThreads), 0,  \
+    constexpr int W = RT <= 8 ? 16 : 8;   /* LDS: W x RT KB of partial sums */                  \
+    const int kq = ((K + W - 1) / W + 31) / 32 * 32;                                           \
+    hipLaunchKernelGGL((lora_down_kernel<F16, RT, W>), dim3((unsigned)grid), dim3(W * 64), 0,  \
                        stream, x, ldx, a, lda, M, K, r, scale, xa, ldxa, kq);                  \
     return hipGetLastError();                                                                  \
   }
