@@ -5,7 +5,9 @@ The workload is every linear weight of an L-layer Llama-7B-shaped stack
 down 4096x11008; bf16 weights N(0, 0.02), distinct per layer; 6.5e9
 parameters, 13 GB in bf16, 3.3 GB in NF4).  One step is one pass of every
 step of the path over it: quantize-on-load with double quantization of the
-whole stack, dequantize of the whole stack to bf16, the M=1 decode GEMV
+whole stack (layer by layer, one grouped call for the seven linears of a
+layer; one call per tensor is timed beside it), dequantize of the whole
+stack to bf16, the M=1 decode GEMV
 (dequant fused) on every weight, and one prefill GEMM, M=2048, N=K=8192, on a
 weight quantized once before timing.  Inputs are resident in HBM before
 timing; no GEMV weight is re-read before the other weights of its shape have
@@ -247,6 +249,9 @@ def main():
     qs = [T.empty_quantized(w.shape, True, dev) for w in weights]
     maxn = max(N * K for N, K in DECODE_SHAPES)
     ws = T.workspace_for(maxn, True, dev)
+    per_layer = len(LAYER)
+    # quantize-on-load layer by layer: one grouped call per layer
+    wsg = T.grouped_workspace_for([w.numel() for w in weights[:per_layer]], True, dev)
     deq = torch.empty(maxn, dtype=torch.bfloat16, device=dev)
     ys = [torch.empty(1, N, dtype=torch.bfloat16, device=dev) for N, K in DECODE_SHAPES]
     by_shape = [[i for i, si in enumerate(wshape) if si == s] for s in range(len(DECODE_SHAPES))]
@@ -291,8 +296,9 @@ def main():
     # the graph time over its launches (kernel time plus the GPU's
     # back-to-back dispatch gap).
     def stage_quantize():
-        for i, w in enumerate(weights):
-            T.quantize(w, True, out=qs[i], workspace=ws)
+        for l in range(L):
+            sl = slice(l * per_layer, (l + 1) * per_layer)
+            T.quantize_grouped(weights[sl], True, outs=qs[sl], workspace=wsg)
 
     def stage_dequantize():
         for q in qs:
@@ -422,8 +428,10 @@ def main():
         qp_by = {"nf4": qp, "fp4": T.quantize(wp, True, quant_type="fp4")}
         del wp
         qs_fp4 = [T.empty_quantized(w.shape, True, dev, "fp4") for w in weights]
-        q_fp4_ms = timed_ms(lambda: [T.quantize(w, True, out=qs_fp4[i], workspace=ws)
-                                     for i, w in enumerate(weights)], reps)
+        q_fp4_ms = timed_ms(lambda: [
+            T.quantize_grouped(weights[l * per_layer:(l + 1) * per_layer], True,
+                               outs=qs_fp4[l * per_layer:(l + 1) * per_layer], workspace=wsg)
+            for l in range(L)], reps)
         stack_by = {"nf4": qs, "fp4": qs_fp4}
         deq16 = torch.empty(maxn, dtype=torch.float16, device=dev)
         ys16 = [torch.empty(1, N, dtype=torch.float16, device=dev) for N, K in DECODE_SHAPES]
@@ -466,13 +474,18 @@ def main():
 
     variants = None if args.no_variants else measure_variants()
 
+    # Quantize with one bnbx_quantize_nf4 call per tensor (two launches each)
+    # instead of one grouped call per layer, over the same stack, timed after
+    # the steps like the above.
+    q1_ms = timed_ms(lambda: [T.quantize(w, True, out=qs[i], workspace=ws)
+                              for i, w in enumerate(weights)], max(2, args.steps))
+
     # Grouped decode GEMV (bnbx_gemv_nf4_grouped), M=1: per layer of the
     # stack, q, k, v in one call and gate, up in another (they share X), in
     # one graph over all layers, beside the same weights launched one by one.
     xg = xs[0]                                          # [1, 4096]
     yq = [torch.empty(1, 4096, dtype=torch.bfloat16, device=dev) for _ in range(3)]
     yg = [torch.empty(1, 11008, dtype=torch.bfloat16, device=dev) for _ in range(2)]
-    per_layer = len(LAYER)
     qkv = [[qs[l * per_layer + i] for i in range(3)] for l in range(L)]
     gu = [[qs[l * per_layer + i] for i in (4, 5)] for l in range(L)]
     reps_g = max(2, args.steps)
@@ -613,7 +626,8 @@ def main():
             "workload": "decode GEMV M=1 on Llama-7B-shaped linears 4096x4096, 11008x4096, "
                         "4096x11008 (NF4 blocksize 64, double quant), every weight of a "
                         f"{L}-layer stack (q,k,v,o,gate,up,down per layer, distinct weights, "
-                        "streamed from HBM); plus quantize and dequantize of the stack and a "
+                        "streamed from HBM); plus quantize (one grouped call per layer) and "
+                        "dequantize of the stack and a "
                         "prefill GEMM M=2048 N=K=8192; batched decode M=16 on 14336x4096 "
                         "(0.1% of weights x20) in kernels.gemv_m16",
             "layers": L,
@@ -637,6 +651,12 @@ def main():
         "kernels": {
             "quantize_gbs": round(gb_q / t_q / 1e9, 1),
             "quantize_input_read_gbs": round(gb_in / t_q / 1e9, 1),
+            "quantize_per_tensor": {
+                "what": "one bnbx_quantize_nf4 call per tensor instead of one grouped call "
+                        "per layer",
+                "gbs": round(gb_q / K_ / (q1_ms * 1e-3) / 1e9, 1),
+                "input_read_gbs": round(gb_in / K_ / (q1_ms * 1e-3) / 1e9, 1),
+                "ms": round(q1_ms, 3)},
             "dequantize_gbs": round(gb_d / t_d / 1e9, 1),
             "gemv_gbs": round(gemv_gbs, 1),
             "gemv_stack_gbs": round(stack_gbs, 1),

@@ -23,6 +23,8 @@ __all__ = [
     "bnbx_status_str", "bnbx_nf4_codebook", "bnbx_fp4_codebook", "bnbx_dynamic_map",
     "bnbx_quantize_nf4_workspace_bytes",
     "bnbx_quantize_nf4", "bnbx_quantize_nf4_noalloc", "BNBX_NOALLOC_MAX_WEIGHTS",
+    "bnbx_quantize_nf4_grouped_workspace_bytes", "bnbx_quantize_nf4_grouped", "QuantizeItem",
+    "BNBX_QUANTIZE_MAX_ITEMS",
     "bnbx_dequantize_nf4", "bnbx_gemv_nf4", "bnbx_gemv_nf4_grouped", "GemvItem",
     "BNBX_GEMV_MAX_ITEMS",
     "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4", "bnbx_gemm_nf4_dx", "bnbx_gemm_nf4_lora",
@@ -48,11 +50,13 @@ BNBX_DQ_DYNAMIC = 2
 
 BNBX_NOALLOC_MAX_WEIGHTS = 1 << 28
 BNBX_GEMV_MAX_ITEMS = 4
+BNBX_QUANTIZE_MAX_ITEMS = 8
 
 EXPORTED_SYMBOLS = (
     "bnbx_status_str", "bnbx_nf4_codebook", "bnbx_fp4_codebook", "bnbx_dynamic_map",
     "bnbx_quantize_nf4_workspace_bytes",
-    "bnbx_quantize_nf4", "bnbx_quantize_nf4_noalloc", "bnbx_dequantize_nf4", "bnbx_gemv_nf4",
+    "bnbx_quantize_nf4", "bnbx_quantize_nf4_noalloc", "bnbx_quantize_nf4_grouped_workspace_bytes",
+    "bnbx_quantize_nf4_grouped", "bnbx_dequantize_nf4", "bnbx_gemv_nf4",
     "bnbx_gemv_nf4_grouped",
     "bnbx_gemm_nf4_workspace_bytes", "bnbx_gemm_nf4", "bnbx_gemm_nf4_dx", "bnbx_gemm_nf4_lora",
     "bnbx_lora_down",
@@ -89,6 +93,17 @@ class Nf4State(ctypes.Structure):
         ("absmax", ctypes.c_void_p),
         ("absmax2", ctypes.c_void_p),
         ("absmax_mean", ctypes.c_void_p),
+    ]
+
+
+class QuantizeItem(ctypes.Structure):
+    """bnbx_quantize_item: one tensor of a grouped quantize (device pointers;
+    the state pointer is a host address)."""
+
+    _fields_ = [
+        ("w", ctypes.c_void_p),
+        ("packed", ctypes.c_void_p),
+        ("st", ctypes.POINTER(Nf4State)),
     ]
 
 
@@ -141,6 +156,10 @@ def lib() -> ctypes.CDLL:
     L.bnbx_quantize_nf4.restype = i32
     L.bnbx_quantize_nf4_noalloc.argtypes = [vp, vp, sp, vp]
     L.bnbx_quantize_nf4_noalloc.restype = i32
+    L.bnbx_quantize_nf4_grouped_workspace_bytes.argtypes = [ctypes.POINTER(i64), i32, i32, i32]
+    L.bnbx_quantize_nf4_grouped_workspace_bytes.restype = sz
+    L.bnbx_quantize_nf4_grouped.argtypes = [ctypes.POINTER(QuantizeItem), i32, vp, sz, vp]
+    L.bnbx_quantize_nf4_grouped.restype = i32
     L.bnbx_dequantize_nf4.argtypes = [vp, sp, vp, vp]
     L.bnbx_dequantize_nf4.restype = i32
     L.bnbx_gemv_nf4.argtypes = [vp, i64, vp, sp, i32, i32, i32, vp, i64, vp]
@@ -226,6 +245,26 @@ def bnbx_quantize_nf4(w, packed, state: Nf4State, workspace=None, workspace_byte
 def bnbx_quantize_nf4_noalloc(w, packed, state: Nf4State, stream=None) -> None:
     _check(lib().bnbx_quantize_nf4_noalloc(_ptr(w), _ptr(packed), ctypes.byref(state),
                                            _stream(stream)), "bnbx_quantize_nf4_noalloc")
+
+
+def bnbx_quantize_nf4_grouped_workspace_bytes(ns, blocksize: int = 64,
+                                              double_quant: int = 1) -> int:
+    arr = (ctypes.c_int64 * max(len(ns), 1))(*[int(n) for n in ns])
+    return int(lib().bnbx_quantize_nf4_grouped_workspace_bytes(arr, len(ns), int(blocksize),
+                                                               int(double_quant)))
+
+
+def bnbx_quantize_nf4_grouped(items, workspace=None, workspace_bytes: int = 0,
+                              stream=None) -> None:
+    """items: sequence of (w, packed, state)."""
+    n = len(items)
+    arr = (QuantizeItem * max(n, 1))()
+    states = [st for _, _, st in items]    # kept alive for the call
+    for i, (w, packed, st) in enumerate(items):
+        arr[i] = QuantizeItem(_ptr(w), _ptr(packed), ctypes.pointer(st))
+    _check(lib().bnbx_quantize_nf4_grouped(arr, n, _ptr(workspace), int(workspace_bytes),
+                                           _stream(stream)), "bnbx_quantize_nf4_grouped")
+    del states
 
 
 def bnbx_dequantize_nf4(packed, state: Nf4State, out, stream=None) -> None:

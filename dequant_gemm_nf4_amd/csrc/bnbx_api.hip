@@ -185,7 +185,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? BNBX_OK : BNBX_E_HIP; }
 // (bnbx_quantize_nf4_noalloc): a file-scope device array, one copy per GPU
 // the library runs on, held until the process ends.  Its size is the
 // workspace of BNBX_NOALLOC_MAX_WEIGHTS weights.
-constexpr size_t kNoAllocScratchBytes = (size_t)round_up(kSlotBytes, 256) +
+constexpr size_t kNoAllocScratchBytes = dq_slot_bytes(1) +
                                         (size_t)(BNBX_NOALLOC_MAX_WEIGHTS / kBlock) * sizeof(float);
 static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
@@ -213,18 +213,26 @@ hipError_t scratch_address(void** out) {
   return hipSuccess;
 }
 
-// Double quant: quantize (slots + fp32 absmax into the workspace), then the
-// second-level quantization reading them.
+// The job of one tensor: fp32 block absmax into the state (no double
+// quant) or into the workspace at `a32`.
+QuantJob job_of(const uint16_t* w, uint8_t* packed, const bnbx_nf4_state* st, float* a32) {
+  QuantJob j;
+  j.w = w;
+  j.packed = packed;
+  j.n = st->n;
+  j.absmax_f32 = st->double_quant ? a32 : (float*)st->absmax;
+  j.q = (uint8_t*)st->absmax;
+  j.absmax2 = st->absmax2;
+  j.mean = st->absmax_mean;
+  return j;
+}
+
+// One tensor with double quant: slots, then its fp32 absmax, in the workspace.
 int quantize_dq(const uint16_t* w, uint8_t* packed, const bnbx_nf4_state* st, void* workspace,
                 hipStream_t hs) {
-  const int64_t n = st->n, nb = (n + kBlock - 1) / kBlock;
   unsigned long long* slots = (unsigned long long*)workspace;
-  float* a32 = (float*)((char*)workspace + round_up(kSlotBytes, 256));
-  hipError_t e = launch_quantize(w, packed, n, a32, slots, st->quant_type, hs);
-  if (e == hipSuccess)
-    e = launch_double_quant(a32, slots, quantize_grid(n), nb, (uint8_t*)st->absmax, st->absmax2,
-                            st->absmax_mean, st->double_quant, hs);
-  return hip_status(e);
+  const QuantJob j = job_of(w, packed, st, (float*)((char*)workspace + dq_slot_bytes(1)));
+  return hip_status(launch_quantize(&j, 1, slots, st->double_quant, st->quant_type, hs));
 }
 
 // The dynamic map ascends strictly, holds 0 at its zero code and 1 at the
@@ -238,6 +246,7 @@ constexpr bool dyn_map_ok() {
   return m.v[kDynZeroCode] == 0.0f && m.v[255] == 1.0f;
 }
 static_assert(dyn_map_ok(), "dynamic 8-bit map");
+static_assert(BNBX_QUANTIZE_MAX_ITEMS == kMaxQItems, "grouped quantize bound");
 
 }  // namespace
 
@@ -302,7 +311,8 @@ int bnbx_quantize_nf4(const uint16_t* w, uint8_t* packed, const bnbx_nf4_state* 
   const int64_t n = st->n, nb = nblocks(n);
   hipStream_t hs = (hipStream_t)stream;
   if (!st->double_quant) {
-    return hip_status(launch_quantize(w, packed, n, (float*)st->absmax, nullptr, st->quant_type, hs));
+    const QuantJob j = job_of(w, packed, st, nullptr);
+    return hip_status(launch_quantize(&j, 1, nullptr, kDqNone, st->quant_type, hs));
   }
   const size_t need = dq_workspace_bytes(nb);
   if (workspace == nullptr || workspace_bytes < need) return BNBX_E_WORKSPACE;
@@ -317,16 +327,62 @@ int bnbx_quantize_nf4_noalloc(const uint16_t* w, uint8_t* packed, const bnbx_nf4
   if (s != BNBX_OK) return s;
   if (!aligned(w, 16) || !aligned(packed, 16)) return BNBX_E_ALIGN;
   hipStream_t hs = (hipStream_t)stream;
-  if (!st->double_quant)
-    return hip_status(launch_quantize(w, packed, st->n, (float*)st->absmax, nullptr,
-                                      st->quant_type, hs));
+  if (!st->double_quant) {
+    const QuantJob j = job_of(w, packed, st, nullptr);
+    return hip_status(launch_quantize(&j, 1, nullptr, kDqNone, st->quant_type, hs));
+  }
   if (st->n > BNBX_NOALLOC_MAX_WEIGHTS) return BNBX_E_WORKSPACE;
-  static_assert(kNoAllocScratchBytes >= kSlotBytes, "scratch holds the slots");
+  static_assert(kNoAllocScratchBytes >= dq_slot_bytes(1), "scratch holds the slots");
   void* ws = nullptr;
   const hipError_t e = scratch_address(&ws);
   if (e != hipSuccess) return BNBX_E_HIP;
   if (dq_workspace_bytes((st->n + kBlock - 1) / kBlock) > kNoAllocScratchBytes) return BNBX_E_WORKSPACE;
   return quantize_dq(w, packed, st, ws, hs);
+}
+
+size_t bnbx_quantize_nf4_grouped_workspace_bytes(const int64_t* n, int count, int blocksize,
+                                                 int double_quant) {
+  if (n == nullptr || count < 1 || count > BNBX_QUANTIZE_MAX_ITEMS || blocksize != kBlock)
+    return 0;
+  size_t bytes = dq_slot_bytes(count);
+  for (int i = 0; i < count; ++i) {
+    if (n[i] < 2 || (n[i] & 1)) return 0;
+    bytes += dq_absmax_bytes(nblocks(n[i]));
+  }
+  return double_quant ? bytes : 0;
+}
+
+int bnbx_quantize_nf4_grouped(const bnbx_quantize_item* items, int count, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (items == nullptr || count < 1 || count > BNBX_QUANTIZE_MAX_ITEMS) return BNBX_E_INVAL;
+  const bnbx_nf4_state* s0 = items[0].st;
+  int64_t ns[BNBX_QUANTIZE_MAX_ITEMS];
+  for (int i = 0; i < count; ++i) {
+    const bnbx_quantize_item& a = items[i];
+    if (a.w == nullptr || a.packed == nullptr) return BNBX_E_INVAL;
+    const int s = check_state(a.st);
+    if (s != BNBX_OK) return s;
+    if (!aligned(a.w, 16) || !aligned(a.packed, 16)) return BNBX_E_ALIGN;
+    if (a.st->quant_type != s0->quant_type || a.st->double_quant != s0->double_quant)
+      return BNBX_E_INVAL;
+    ns[i] = a.st->n;
+  }
+  QuantJob jobs[BNBX_QUANTIZE_MAX_ITEMS];
+  unsigned long long* slots = nullptr;
+  if (s0->double_quant) {
+    const size_t need = bnbx_quantize_nf4_grouped_workspace_bytes(ns, count, kBlock, 1);
+    if (workspace == nullptr || workspace_bytes < need) return BNBX_E_WORKSPACE;
+    if (!aligned(workspace, 256)) return BNBX_E_ALIGN;
+    slots = (unsigned long long*)workspace;
+  }
+  char* a32 = (char*)workspace + dq_slot_bytes(count);
+  for (int i = 0; i < count; ++i) {
+    jobs[i] = job_of(items[i].w, items[i].packed, items[i].st,
+                     s0->double_quant ? (float*)a32 : nullptr);
+    if (s0->double_quant) a32 += dq_absmax_bytes(nblocks(ns[i]));
+  }
+  return hip_status(launch_quantize(jobs, count, slots, s0->double_quant, s0->quant_type,
+                                    (hipStream_t)stream));
 }
 
 int bnbx_dequantize_nf4(const uint8_t* packed, const bnbx_nf4_state* st, uint16_t* out,

@@ -90,30 +90,40 @@ const float* levels_f32(int quant_type);   // float[16], by code
 const EncodeTable& encode_table(int quant_type);
 const LevelTable& level_table(int quant_type);
 
-// Workspace layout of the double-quant quantize: one slot per quantize
-// workgroup (at most kMaxQGrid) holding that workgroup's exact partial sum of
-// its block absmax values as kSumDigits base-2^32 digits (each slot is fully
-// overwritten by every call, so nothing needs clearing), then the fp32
-// absmax of every block.
+// Workspace layout of the double-quant quantize, for a call on `count`
+// tensors: per tensor, one slot per quantize workgroup (at most kMaxQGrid)
+// holding that workgroup's exact partial sum of the tensor's block absmax
+// values as kSumDigits base-2^32 digits (every slot is fully overwritten by
+// every call, so nothing needs clearing); then the fp32 absmax of every
+// block of each tensor, each tensor's array 256-byte aligned.
 constexpr int kMaxQGrid = 512;
+constexpr int kMaxQItems = 8;   // tensors per grouped quantize call
 constexpr int kSumDigits = 10;
 constexpr size_t kHistBins = 256;   // binary exponent fields of a bf16 absmax
 constexpr size_t kSlotBytes = (size_t)kMaxQGrid * kSumDigits * sizeof(unsigned long long);
 constexpr size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
-inline size_t dq_workspace_bytes(int64_t nb) {
-  return round_up(kSlotBytes, 256) + round_up((size_t)nb * sizeof(float), 256);
-}
+constexpr size_t dq_slot_bytes(int count) { return round_up((size_t)count * kSlotBytes, 256); }
+constexpr size_t dq_absmax_bytes(int64_t nb) { return round_up((size_t)nb * sizeof(float), 256); }
+constexpr size_t dq_workspace_bytes(int64_t nb) { return dq_slot_bytes(1) + dq_absmax_bytes(nb); }
 
 // ---- kernel launchers (return hipError_t of the launch) ----
-// quantize_grid(n) workgroups write slots [0, quantize_grid(n)) when
-// `slots` is given (double quant); double_quant reads as many.
-int quantize_grid(int64_t n);
-hipError_t launch_quantize(const uint16_t* w, uint8_t* packed, int64_t n, float* absmax_f32,
-                           unsigned long long* slots, int quant_type, hipStream_t stream);
-// `dq`: kDqLinear (int8 codes) or kDqDynamic (codes into the dynamic map).
-hipError_t launch_double_quant(const float* absmax_f32, const unsigned long long* slots,
-                               int nslots, int64_t nb, uint8_t* q, float* absmax2, float* mean,
-                               int dq, hipStream_t stream);
+// One tensor of a (grouped) quantize call.
+struct QuantJob {
+  const uint16_t* w;    // bf16[n]
+  uint8_t* packed;      // uint8[n / 2]
+  int64_t n;
+  float* absmax_f32;    // fp32 block absmax: the state's absmax without double
+                        // quant, the tensor's workspace array with it
+  uint8_t* q;           // double quant: code bytes (the state's absmax),
+  float* absmax2;       //   group scales
+  float* mean;          //   and the mean
+};
+// Quantizes `count` (1..kMaxQItems) tensors of one quant type in one launch;
+// with double quant (dq = kDqLinear or kDqDynamic; `slots` the workspace's
+// slot region, dq_slot_bytes(count) bytes) a second launch forms every
+// tensor's mean, group scales and codes.
+hipError_t launch_quantize(const QuantJob* jobs, int count, unsigned long long* slots, int dq,
+                           int quant_type, hipStream_t stream);
 // `f16`: the 16-bit compute type is IEEE binary16 instead of bfloat16.
 hipError_t launch_dequantize(const uint8_t* packed, int64_t n, const void* absmax,
                              const float* absmax2, const float* mean, int double_quant,

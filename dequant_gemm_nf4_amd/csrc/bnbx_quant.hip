@@ -17,6 +17,12 @@
 // exponent) in LDS, which it turns into its exact partial sum (an integer in
 // base-2^32 digits) and writes to its own workspace slot; double_quant_kernel
 // adds the slots and forms the exactly rounded mean.
+//
+// The grouped kernels (quantize_group_kernel, double_quant_group_kernel) do
+// the same for up to kMaxQItems tensors per launch: the quantize kernel walks
+// the tensors one after another with one histogram and one slot per tensor,
+// and each double-quant workgroup takes groups of one tensor.  Per tensor the
+// arithmetic is the single kernels' (the same device functions).
 #include "bnbx_device.hpp"
 #include "bnbx_internal.hpp"
 
@@ -113,38 +119,20 @@ __device__ __forceinline__ void record_block(int lane, int64_t e, uint32_t m, fl
   }
 }
 
+// Tile pairs wv, wv + nwaves, ... of one tensor for one wave, and its ragged
+// last tile (fewer than 512 weights) when `ragged` is set for this wave.
+// Each round a wave loads kUnroll whole tiles (addresses clamped, so no
+// per-lane branches), then encodes them; only the stores are skipped for
+// tiles past the end.  Latency is hidden by the many resident waves.
 template <bool DQ, bool FP4>
-__global__ __launch_bounds__(kQThreads, 2) void quantize_kernel(
-    const uint16_t* __restrict__ w, uint8_t* __restrict__ packed, float* __restrict__ absmax,
-    unsigned long long* __restrict__ slots, int64_t n, EncodeTable et) {
-  __shared__ __attribute__((aligned(16))) unsigned char tab[kBuckets * kTabStride];
-  __shared__ uint32_t lhist[kHistBins];
-  __shared__ unsigned long long ldig[kSumDigits];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
+__device__ __forceinline__ void quantize_tensor(const uint16_t* __restrict__ w,
+                                                uint8_t* __restrict__ packed,
+                                                float* __restrict__ absmax, int64_t n,
+                                                uint32_t* lhist, int64_t wv, int64_t nwaves,
+                                                bool ragged, const unsigned char* tab,
+                                                uint32_t lanebase, int lane) {
   const int64_t full = n / kTile;                       // whole 512-weight tiles
-  const int64_t gw = (int64_t)blockIdx.x * kQWaves + (tid >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * kQWaves;
-
-  // Replicated bucket table in LDS (entry (b, copy) at b*256 + copy*8).
-  for (int e = tid; e < kBuckets * 32; e += kQThreads) {
-    uint2 t;
-    t.x = __float_as_uint(et.thr[e >> 5]);
-    t.y = et.base[e >> 5];
-    *(uint2*)(tab + (e >> 5) * kTabStride + (e & 31) * 8) = t;
-  }
-  if (DQ) {
-    for (int e = tid; e < (int)kHistBins; e += kQThreads) lhist[e] = 0;
-    if (tid < kSumDigits) ldig[tid] = 0ull;
-  }
-  __syncthreads();
-  const uint32_t lanebase = (uint32_t)(lane & 31) << 3;
-
-  // Each round a wave loads kUnroll whole tiles (addresses clamped, so no
-  // per-lane branches), then encodes them; only the stores are skipped for
-  // tiles past the end.  Latency is hidden by the many resident waves.
-  for (int64_t t0 = gw * kUnroll; t0 < full; t0 += nwaves * kUnroll) {
+  for (int64_t t0 = wv * kUnroll; t0 < full; t0 += nwaves * kUnroll) {
     uint4 v[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -165,8 +153,7 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_kernel(
     }
   }
 
-  // The ragged last tile (fewer than 512 weights) goes to the last wave.
-  if (n % kTile != 0 && gw == nwaves - 1) {
+  if (n % kTile != 0 && ragged) {
     const int64_t e = full * kTile + lane * 8;
     uint16_t h[8];
 #pragma unroll
@@ -182,24 +169,127 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_kernel(
       record_block(lane, e, m, amax, absmax, lhist, DQ);
     }
   }
+}
 
-  if (DQ) {
-    // The workgroup's partial sum I_w = sum_e lhist[e] * 2^(max(e,1)-1) (see
-    // exact_mean) in base-2^32 digits: a bin (below 2^32) shifted by less
-    // than 32 spans two digits.  Every workgroup writes its whole slot.
-    __syncthreads();
-    for (int e = tid; e < (int)kHistBins; e += kQThreads) {
-      const unsigned long long h = lhist[e];
-      if (h) {
-        const int sh = (e > 1 ? e : 1) - 1;
-        const int k = sh >> 5, bit = sh & 31;
-        const unsigned long long p = h << bit;
-        atomicAdd(&ldig[k], p & 0xffffffffull);
-        if (p >> 32) atomicAdd(&ldig[k + 1], p >> 32);
-      }
+// The workgroup's partial sum I_w = sum_e lhist[e] * 2^(max(e,1)-1) (see
+// exact_mean) into the base-2^32 digits ldig (zero on entry): a bin (below
+// 2^32) shifted by less than 32 spans two digits.
+__device__ __forceinline__ void histogram_digits(const uint32_t* lhist, unsigned long long* ldig,
+                                                 int tid) {
+  for (int e = tid; e < (int)kHistBins; e += kQThreads) {
+    const unsigned long long h = lhist[e];
+    if (h) {
+      const int sh = (e > 1 ? e : 1) - 1;
+      const int k = sh >> 5, bit = sh & 31;
+      const unsigned long long p = h << bit;
+      atomicAdd(&ldig[k], p & 0xffffffffull);
+      if (p >> 32) atomicAdd(&ldig[k + 1], p >> 32);
     }
+  }
+}
+
+// Replicated bucket table in LDS (entry (b, copy) at b*256 + copy*8).
+__device__ __forceinline__ void fill_table(unsigned char* tab, const EncodeTable& et, int tid) {
+  for (int e = tid; e < kBuckets * 32; e += kQThreads) {
+    uint2 t;
+    t.x = __float_as_uint(et.thr[e >> 5]);
+    t.y = et.base[e >> 5];
+    *(uint2*)(tab + (e >> 5) * kTabStride + (e & 31) * 8) = t;
+  }
+}
+
+template <bool DQ, bool FP4>
+__global__ __launch_bounds__(kQThreads, 2) void quantize_kernel(
+    const uint16_t* __restrict__ w, uint8_t* __restrict__ packed, float* __restrict__ absmax,
+    unsigned long long* __restrict__ slots, int64_t n, EncodeTable et) {
+  __shared__ __attribute__((aligned(16))) unsigned char tab[kBuckets * kTabStride];
+  __shared__ uint32_t lhist[kHistBins];
+  __shared__ unsigned long long ldig[kSumDigits];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int64_t gw = (int64_t)blockIdx.x * kQWaves + (tid >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * kQWaves;
+
+  fill_table(tab, et, tid);
+  if (DQ) {
+    for (int e = tid; e < (int)kHistBins; e += kQThreads) lhist[e] = 0;
+    if (tid < kSumDigits) ldig[tid] = 0ull;
+  }
+  __syncthreads();
+  const uint32_t lanebase = (uint32_t)(lane & 31) << 3;
+  // The ragged last tile goes to the last wave.
+  quantize_tensor<DQ, FP4>(w, packed, absmax, n, lhist, gw, nwaves, gw == nwaves - 1, tab,
+                           lanebase, lane);
+  if (DQ) {
+    // Every workgroup writes its whole slot.
+    __syncthreads();
+    histogram_digits(lhist, ldig, tid);
     __syncthreads();
     if (tid < kSumDigits) slots[(int64_t)blockIdx.x * kSumDigits + tid] = ldig[tid];
+  }
+}
+
+// The tensors of one grouped launch (entries past `count` unused).  Tensor
+// i's 512-weight tile pairs continue the round-robin over the grid's waves
+// where tensor i - 1's left off: wave v takes pairs p = v - rot[i] (mod the
+// wave count) of tensor i.
+struct QuantItems {
+  int count;
+  int64_t n[kMaxQItems];
+  int64_t rot[kMaxQItems];
+  const uint16_t* w[kMaxQItems];
+  uint8_t* packed[kMaxQItems];
+  float* absmax[kMaxQItems];
+};
+
+// Entry i of a per-tensor argument array, by selects (indexing the argument
+// block with a run-time i would copy it to scratch memory).
+template <typename T>
+__device__ __forceinline__ T pick_item(const T (&a)[kMaxQItems], int i) {
+  T r = a[0];
+#pragma unroll
+  for (int k = 1; k < kMaxQItems; ++k) r = i == k ? a[k] : r;
+  return r;
+}
+
+// Slots: tensor i's slot of workgroup b at slots + (i * grid + b) * kSumDigits.
+template <bool DQ, bool FP4>
+__global__ __launch_bounds__(kQThreads, 2) void quantize_group_kernel(
+    QuantItems it, unsigned long long* __restrict__ slots, EncodeTable et) {
+  __shared__ __attribute__((aligned(16))) unsigned char tab[kBuckets * kTabStride];
+  __shared__ uint32_t lhist[DQ ? kMaxQItems : 1][kHistBins];
+  __shared__ unsigned long long ldig[DQ ? kMaxQItems : 1][kSumDigits];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int64_t gw = (int64_t)blockIdx.x * kQWaves + __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * kQWaves;
+
+  fill_table(tab, et, tid);
+  if (DQ) {
+    for (int e = tid; e < it.count * (int)kHistBins; e += kQThreads)
+      lhist[e / kHistBins][e % kHistBins] = 0;
+    if (tid < it.count * kSumDigits) ldig[tid / kSumDigits][tid % kSumDigits] = 0ull;
+  }
+  __syncthreads();
+  const uint32_t lanebase = (uint32_t)(lane & 31) << 3;
+  for (int i = 0; i < it.count; ++i) {
+    int64_t wv = gw - pick_item(it.rot, i);
+    wv = wv < 0 ? wv + nwaves : wv;
+    // Tensor i's ragged last tile goes to wave nwaves - 1 - i.
+    quantize_tensor<DQ, FP4>(pick_item(it.w, i), pick_item(it.packed, i), pick_item(it.absmax, i),
+                             pick_item(it.n, i), lhist[DQ ? i : 0], wv, nwaves,
+                             gw == nwaves - 1 - i, tab, lanebase, lane);
+  }
+  if (DQ) {
+    __syncthreads();
+    for (int i = 0; i < it.count; ++i) histogram_digits(lhist[i], ldig[i], tid);
+    __syncthreads();
+    if (tid < it.count * kSumDigits) {
+      const int i = tid / kSumDigits, d = tid % kSumDigits;
+      slots[((int64_t)i * gridDim.x + blockIdx.x) * kSumDigits + d] = ldig[i][d];
+    }
   }
 }
 
@@ -281,39 +371,41 @@ __device__ float exact_mean(const unsigned long long* __restrict__ slots, int ns
   return (float)mean;
 }
 
-// Groups per double_quant workgroup; their absmax values are loaded before
-// the mean is formed, so that one memory latency covers both.
+// Groups per double_quant workgroup (single tensor, grouped launch); their
+// absmax values are loaded before the mean is formed, so that one memory
+// latency covers both.  Every workgroup also reads all of its tensor's
+// slots, which the grouped launch, with many more groups, pays back by
+// taking more groups per workgroup.
 constexpr int kDqGroups = 4;
+constexpr int kDqGroupsGrouped = 8;
 
-// Second level of the double quantization (mlqm.cn article, sec. 3.3): the
-// exact mean, the group scales s_g = max |a_b - mean|, and per block the code
-// of t = fl32((a_b - mean) / s_g): linear, round-half-even(fl32(t * 127)) as
-// int8; DYN, the index of the nearest value of the dynamic 8-bit map (exact
-// ties to the lower index), found by binary search over the exact binary64
-// midpoints of neighbouring values.  A group with s_g = 0 stores the code of
-// the value 0.
-template <bool DYN>
-__global__ __launch_bounds__(256) void double_quant_kernel(
+// Second level of the double quantization (mlqm.cn article, sec. 3.3) for
+// groups g0 .. g0 + NG - 1 of one tensor: the exact mean, the group
+// scales s_g = max |a_b - mean|, and per block the code of t = fl32((a_b -
+// mean) / s_g): linear, round-half-even(fl32(t * 127)) as int8; DYN, the
+// index of the nearest value of the dynamic 8-bit map (exact ties to the
+// lower index), found by binary search over the exact binary64 midpoints of
+// neighbouring values.  A group with s_g = 0 stores the code of the value 0.
+// The mean goes to mean_out when write_mean is set.
+template <bool DYN, int NG>
+__device__ __forceinline__ void double_quant_groups(
     const float* __restrict__ a, const unsigned long long* __restrict__ slots, int nslots,
-    int64_t nb, uint8_t* __restrict__ q, float* __restrict__ s_out, float* __restrict__ mean_out) {
-  __shared__ unsigned long long digits[kSumDigits];
-  __shared__ float red[kDqGroups][4];
-  __shared__ double mids[DYN ? 256 : 1];
+    int64_t nb, uint8_t* __restrict__ q, float* __restrict__ s_out, float* __restrict__ mean_out,
+    bool write_mean, int64_t g0, unsigned long long* digits, float (*red)[4], double* mids) {
   const int tid = threadIdx.x;
-  const int64_t g0 = (int64_t)blockIdx.x * kDqGroups;
-  float v[kDqGroups];
+  float v[NG];
 #pragma unroll
-  for (int i = 0; i < kDqGroups; ++i) {
+  for (int i = 0; i < NG; ++i) {
     const int64_t b = (g0 + i) * kGroup + tid;
     v[i] = b < nb ? a[b] : 0.0f;
   }
   if (DYN && tid < 255) mids[tid] = kDynMapDev.mid[tid];   // visible after exact_mean's barriers
   const float mu = exact_mean(slots, nslots, nb, digits);
-  if (blockIdx.x == 0 && tid == 0) *mean_out = mu;
+  if (write_mean && tid == 0) *mean_out = mu;
   const int64_t ng = (nb + kGroup - 1) / kGroup;
-  float c[kDqGroups];
+  float c[NG];
 #pragma unroll
-  for (int i = 0; i < kDqGroups; ++i) {
+  for (int i = 0; i < NG; ++i) {
     const int64_t b = (g0 + i) * kGroup + tid;
     c[i] = b < nb ? v[i] - mu : 0.0f;
     const float m = wave_max(fabsf(c[i]));
@@ -321,7 +413,7 @@ __global__ __launch_bounds__(256) void double_quant_kernel(
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kDqGroups; ++i) {
+  for (int i = 0; i < NG; ++i) {
     const int64_t g = g0 + i;
     if (g >= ng) break;   // uniform
     const int64_t b = g * kGroup + tid;
@@ -346,6 +438,48 @@ __global__ __launch_bounds__(256) void double_quant_kernel(
   }
 }
 
+template <bool DYN>
+__global__ __launch_bounds__(256) void double_quant_kernel(
+    const float* __restrict__ a, const unsigned long long* __restrict__ slots, int nslots,
+    int64_t nb, uint8_t* __restrict__ q, float* __restrict__ s_out, float* __restrict__ mean_out) {
+  __shared__ unsigned long long digits[kSumDigits];
+  __shared__ float red[kDqGroups][4];
+  __shared__ double mids[DYN ? 256 : 1];
+  double_quant_groups<DYN, kDqGroups>(a, slots, nslots, nb, q, s_out, mean_out, blockIdx.x == 0,
+                           (int64_t)blockIdx.x * kDqGroups, digits, red, mids);
+}
+
+// The tensors of one grouped double_quant launch: workgroups
+// [wg_end[i-1], wg_end[i]) take tensor i (wg_end[-1] = 0, entries past
+// `count` hold INT_MAX), whose quantize slots start at
+// slots + i * nslots * kSumDigits.
+struct DqItems {
+  int count;
+  int wg_end[kMaxQItems];
+  int64_t nb[kMaxQItems];
+  const float* a[kMaxQItems];
+  uint8_t* q[kMaxQItems];
+  float* s[kMaxQItems];
+  float* mean[kMaxQItems];
+};
+
+template <bool DYN>
+__global__ __launch_bounds__(256) void double_quant_group_kernel(
+    DqItems it, const unsigned long long* __restrict__ slots, int nslots) {
+  __shared__ unsigned long long digits[kSumDigits];
+  __shared__ float red[kDqGroupsGrouped][4];
+  __shared__ double mids[DYN ? 256 : 1];
+  const int wg = blockIdx.x;
+  int i = 0;
+#pragma unroll
+  for (int k = 0; k < kMaxQItems - 1; ++k) i += wg >= it.wg_end[k] ? 1 : 0;
+  const int wg0 = i == 0 ? 0 : pick_item(it.wg_end, i - 1);
+  double_quant_groups<DYN, kDqGroupsGrouped>(pick_item(it.a, i), slots + (int64_t)i * nslots * kSumDigits, nslots,
+                           pick_item(it.nb, i), pick_item(it.q, i), pick_item(it.s, i),
+                           pick_item(it.mean, i), wg == wg0, (int64_t)(wg - wg0) * kDqGroupsGrouped,
+                           digits, red, mids);
+}
+
 int grid_for(int64_t work_items, int per_block, int cap) {
   int64_t g = (work_items + per_block - 1) / per_block;
   if (g < 1) g = 1;
@@ -353,48 +487,103 @@ int grid_for(int64_t work_items, int per_block, int cap) {
   return (int)g;
 }
 
-}  // namespace
-
 int quantize_grid(int64_t n) {
   const int64_t ntiles = (n + kTile - 1) / kTile;
   return grid_for(ntiles, kQWaves * kUnroll, kMaxQGrid);
 }
 
-hipError_t launch_quantize(const uint16_t* w, uint8_t* packed, int64_t n, float* absmax_f32,
-                           unsigned long long* slots, int quant_type, hipStream_t stream) {
-  const int grid = quantize_grid(n);
+hipError_t launch_single(const QuantJob& j, unsigned long long* slots, int dq, int quant_type,
+                         hipStream_t stream) {
+  const int grid = quantize_grid(j.n);
   const EncodeTable& et = encode_table(quant_type);
-  const bool dq = slots != nullptr;
-  if (quant_type == kQuantFP4) {
-    if (dq)
-      hipLaunchKernelGGL((quantize_kernel<true, true>), dim3(grid), dim3(kQThreads), 0, stream, w,
-                         packed, absmax_f32, slots, n, et);
-    else
-      hipLaunchKernelGGL((quantize_kernel<false, true>), dim3(grid), dim3(kQThreads), 0, stream, w,
-                         packed, absmax_f32, slots, n, et);
-  } else {
-    if (dq)
-      hipLaunchKernelGGL((quantize_kernel<true, false>), dim3(grid), dim3(kQThreads), 0, stream, w,
-                         packed, absmax_f32, slots, n, et);
-    else
-      hipLaunchKernelGGL((quantize_kernel<false, false>), dim3(grid), dim3(kQThreads), 0, stream,
-                         w, packed, absmax_f32, slots, n, et);
+  const bool fp4 = quant_type == kQuantFP4;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kQThreads), 0, stream, j.w, j.packed,
+                       j.absmax_f32, slots, j.n, et);
+  };
+  if (dq == kDqNone) {
+    if (fp4) go(quantize_kernel<false, true>);
+    else go(quantize_kernel<false, false>);
+    return hipGetLastError();
   }
+  if (fp4) go(quantize_kernel<true, true>);
+  else go(quantize_kernel<true, false>);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t nb = (j.n + kBlock - 1) / kBlock;
+  const int64_t ng = (nb + kGroup - 1) / kGroup;
+  const int64_t wgs = (ng + kDqGroups - 1) / kDqGroups;
+  if (wgs > 0x7fffffff) return hipErrorInvalidValue;
+  if (dq == kDqDynamic)
+    hipLaunchKernelGGL(double_quant_kernel<true>, dim3((unsigned)wgs), dim3(256), 0, stream,
+                       j.absmax_f32, slots, grid, nb, j.q, j.absmax2, j.mean);
+  else
+    hipLaunchKernelGGL(double_quant_kernel<false>, dim3((unsigned)wgs), dim3(256), 0, stream,
+                       j.absmax_f32, slots, grid, nb, j.q, j.absmax2, j.mean);
   return hipGetLastError();
 }
 
-hipError_t launch_double_quant(const float* absmax_f32, const unsigned long long* slots,
-                               int nslots, int64_t nb, uint8_t* q, float* absmax2, float* mean,
-                               int dq, hipStream_t stream) {
-  const int64_t ng = (nb + kGroup - 1) / kGroup;
-  const int64_t grid = (ng + kDqGroups - 1) / kDqGroups;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+}  // namespace
+
+hipError_t launch_quantize(const QuantJob* jobs, int count, unsigned long long* slots, int dq,
+                           int quant_type, hipStream_t stream) {
+  if (count < 1 || count > kMaxQItems) return hipErrorInvalidValue;
+  if (count == 1) return launch_single(jobs[0], slots, dq, quant_type, stream);
+  int64_t total = 0;
+  for (int i = 0; i < count; ++i) total += jobs[i].n;
+  const int grid = quantize_grid(total);
+  const int64_t nwaves = (int64_t)grid * kQWaves;
+  QuantItems it{};
+  it.count = count;
+  int64_t pairs = 0;   // tile pairs of the tensors before i
+  for (int i = 0; i < count; ++i) {
+    it.n[i] = jobs[i].n;
+    it.rot[i] = pairs % nwaves;
+    it.w[i] = jobs[i].w;
+    it.packed[i] = jobs[i].packed;
+    it.absmax[i] = jobs[i].absmax_f32;
+    pairs += (jobs[i].n / kTile + kUnroll - 1) / kUnroll;
+  }
+  const EncodeTable& et = encode_table(quant_type);
+  const bool fp4 = quant_type == kQuantFP4;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kQThreads), 0, stream, it, slots, et);
+  };
+  if (dq == kDqNone) {
+    if (fp4) go(quantize_group_kernel<false, true>);
+    else go(quantize_group_kernel<false, false>);
+    return hipGetLastError();
+  }
+  if (fp4) go(quantize_group_kernel<true, true>);
+  else go(quantize_group_kernel<true, false>);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  DqItems dqi{};
+  dqi.count = count;
+  int64_t wgs = 0;
+  for (int i = 0; i < kMaxQItems; ++i) {
+    if (i < count) {
+      const int64_t nb = (jobs[i].n + kBlock - 1) / kBlock;
+      const int64_t ng = (nb + kGroup - 1) / kGroup;
+      wgs += (ng + kDqGroupsGrouped - 1) / kDqGroupsGrouped;
+      if (wgs > 0x7fffffff) return hipErrorInvalidValue;
+      dqi.wg_end[i] = (int)wgs;
+      dqi.nb[i] = nb;
+      dqi.a[i] = jobs[i].absmax_f32;
+      dqi.q[i] = jobs[i].q;
+      dqi.s[i] = jobs[i].absmax2;
+      dqi.mean[i] = jobs[i].mean;
+    } else {
+      dqi.wg_end[i] = 0x7fffffff;
+    }
+  }
   if (dq == kDqDynamic)
-    hipLaunchKernelGGL(double_quant_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream,
-                       absmax_f32, slots, nslots, nb, q, absmax2, mean);
+    hipLaunchKernelGGL(double_quant_group_kernel<true>, dim3((unsigned)wgs), dim3(256), 0, stream,
+                       dqi, slots, grid);
   else
-    hipLaunchKernelGGL(double_quant_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream,
-                       absmax_f32, slots, nslots, nb, q, absmax2, mean);
+    hipLaunchKernelGGL(double_quant_group_kernel<false>, dim3((unsigned)wgs), dim3(256), 0,
+                       stream, dqi, slots, grid);
   return hipGetLastError();
 }
 

@@ -10,7 +10,8 @@ import torch
 
 from . import (Nf4State, bnbx_dequantize_nf4, bnbx_gemm_nf4, bnbx_gemm_nf4_dx, bnbx_gemm_nf4_lora,
                bnbx_gemm_nf4_workspace_bytes, bnbx_gemv_nf4, bnbx_gemv_nf4_grouped, bnbx_lora_down,
-               bnbx_quantize_nf4, bnbx_quantize_nf4_workspace_bytes)
+               bnbx_quantize_nf4, bnbx_quantize_nf4_grouped,
+               bnbx_quantize_nf4_grouped_workspace_bytes, bnbx_quantize_nf4_workspace_bytes)
 
 BLOCKSIZE = 64
 GROUP = 256
@@ -92,6 +93,29 @@ def quantize(w: torch.Tensor, double_quant: bool, out: QuantizedWeight | None = 
     ws = workspace if workspace is not None else workspace_for(q.n, double_quant, w.device)
     bnbx_quantize_nf4(w, q.packed, q.state, ws, 0 if ws is None else ws.numel(), stream)
     return q
+
+
+def grouped_workspace_for(ns, double_quant: bool, device="cuda") -> torch.Tensor | None:
+    nbytes = bnbx_quantize_nf4_grouped_workspace_bytes(ns, BLOCKSIZE, int(double_quant))
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def quantize_grouped(ws: list, double_quant: bool, outs: list | None = None,
+                     workspace: torch.Tensor | None = None, stream=None, quant_type: str = "nf4",
+                     dtype: torch.dtype = torch.bfloat16,
+                     dq_map: str = "linear") -> list:
+    """bnbx_quantize_nf4_grouped on up to eight bf16 tensors (a layer's
+    weights) in one call; each result equals quantize() on that tensor."""
+    assert all(w.dtype == torch.bfloat16 and w.is_contiguous() for w in ws)
+    qs = outs if outs is not None else [
+        empty_quantized(w.shape, double_quant, w.device, quant_type, dtype, dq_map) for w in ws]
+    wsp = workspace if workspace is not None else grouped_workspace_for(
+        [q.n for q in qs], double_quant, ws[0].device)
+    bnbx_quantize_nf4_grouped([(w, q.packed, q.state) for w, q in zip(ws, qs)], wsp,
+                              0 if wsp is None else wsp.numel(), stream)
+    return qs
 
 
 def dequantize(q: QuantizedWeight, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:

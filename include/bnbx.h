@@ -200,6 +200,44 @@ BNBX_API int bnbx_quantize_nf4(const uint16_t* w, uint8_t* packed, const bnbx_nf
 BNBX_API int bnbx_quantize_nf4_noalloc(const uint16_t* w, uint8_t* packed,
                                        const bnbx_nf4_state* st, void* stream);
 
+/* One tensor of a grouped quantize. */
+typedef struct {
+  const uint16_t* w;            /* device: bf16[st->n], 16-byte aligned (read only) */
+  uint8_t* packed;              /* device: uint8[st->n / 2], 16-byte aligned (written) */
+  const bnbx_nf4_state* st;     /* host descriptor, read during the call; its
+                                   device arrays are written                  */
+} bnbx_quantize_item;
+
+/* Most tensors one grouped quantize takes (the seven linears of a
+ * Llama-style layer fit). */
+#define BNBX_QUANTIZE_MAX_ITEMS 8
+
+/* Bytes of device workspace bnbx_quantize_nf4_grouped needs for `count`
+ * tensors of n[0..count-1] weights; 0 without double quant.  Returns 0 for
+ * invalid arguments. */
+BNBX_API size_t bnbx_quantize_nf4_grouped_workspace_bytes(const int64_t* n, int count,
+                                                         int blocksize, int double_quant);
+
+/* Grouped quantize-on-load: bnbx_quantize_nf4 on up to
+ * BNBX_QUANTIZE_MAX_ITEMS tensors at once, for a loader that quantizes a
+ * layer's weights as they arrive (mlqm.cn article sec. 2.2: weights are
+ * quantized while they are loaded; sec. 3.2-3.3, 4 as bnbx_quantize_nf4).
+ * One launch quantizes every tensor's blocks and, with double quant, one
+ * more forms every tensor's mean, group scales and codes, so the fixed cost
+ * of a launch is paid once per group instead of once per tensor.  Each
+ * tensor is quantized on its own (its own blocks, mean and groups): its
+ * results are bit-identical to a bnbx_quantize_nf4 call on it.
+ *   items      host array of `count` items, read during the call
+ *   count      1 .. BNBX_QUANTIZE_MAX_ITEMS
+ *   workspace  device, >= bnbx_quantize_nf4_grouped_workspace_bytes(...)
+ *              bytes, 256-byte aligned (may be NULL without double quant);
+ *              contents are scratch, overwritten by the call
+ * Every item's state must have the same quant_type and double_quant.
+ * Errors: as bnbx_quantize_nf4 for each item; BNBX_E_INVAL if items is NULL,
+ * count is out of range or the items' states differ. */
+BNBX_API int bnbx_quantize_nf4_grouped(const bnbx_quantize_item* items, int count,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Dequantize to the compute dtype, bf16 or binary16 (mlqm.cn article
  * sec. 3.4, 4).
  *   packed  device, uint8[n/2], 16-byte aligned

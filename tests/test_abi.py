@@ -30,7 +30,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 16
+    assert len(declared) == 18
     assert sorted(bnbx.EXPORTED_SYMBOLS) == declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -73,6 +73,18 @@ def test_workspace_queries():
     assert bnbx.bnbx_quantize_nf4_workspace_bytes(n + 1, 64, 1) == 0
     assert bnbx.bnbx_quantize_nf4_workspace_bytes(n, 32, 1) == 0
     assert bnbx.bnbx_gemm_nf4_workspace_bytes(2048, 8192, 8192) == 0
+    # grouped: one tensor needs what the single call needs; more add their
+    # slots and fp32 absmax arrays
+    g = bnbx.bnbx_quantize_nf4_grouped_workspace_bytes
+    assert g([n], 64, 1) == ws
+    n2 = 11008 * 4096
+    both = g([n, n2], 64, 1)
+    assert both >= ws + bnbx.bnbx_quantize_nf4_workspace_bytes(n2, 64, 1) and both % 256 == 0
+    assert g([n, n2], 64, 0) == 0
+    assert g([], 64, 1) == 0
+    assert g([n] * 9, 64, 1) == 0
+    assert g([n, n + 1], 64, 1) == 0
+    assert g([n], 32, 1) == 0
 
 
 A = 1 << 20          # fake, 256-byte aligned "device" addresses: never touched
@@ -145,6 +157,34 @@ def test_quantize_rejects(case, expect):
     elif case == "misaligned_workspace":
         ws = C + 128
     assert status_of(bnbx.bnbx_quantize_nf4, w, p, st, ws, wsb, 0) == expect
+
+
+def test_quantize_grouped_rejects():
+    """Checked on the host before any launch: item count, states that differ,
+    each item's own checks and the workspace."""
+    f = bnbx.bnbx_quantize_nf4_grouped
+    n = 4096
+    need = bnbx.bnbx_quantize_nf4_grouped_workspace_bytes([n, n], 64, 1)
+    ws = C + (1 << 16)
+
+    def item(st=None, w=A, p=B):
+        return (w, p, st if st is not None else state(n))
+
+    ok = [item(), item()]
+    assert status_of(f, [], ws, need, None) == bnbx.BNBX_E_INVAL                  # count 0
+    assert status_of(f, [item()] * 9, ws, need, None) == bnbx.BNBX_E_INVAL        # count 9
+    assert status_of(f, [item(), item(state(n, qt=1))], ws, need, None) == bnbx.BNBX_E_INVAL
+    assert status_of(f, [item(), item(state(n, dq=2))], ws, need, None) == bnbx.BNBX_E_INVAL
+    assert status_of(f, [item(), item(state(n, dq=0))], ws, need, None) == bnbx.BNBX_E_INVAL
+    assert status_of(f, [item(), item(w=None)], ws, need, None) == bnbx.BNBX_E_INVAL
+    assert status_of(f, [item(), item(state(n + 1))], ws, need, None) == bnbx.BNBX_E_INVAL
+    assert status_of(f, [item(), item(state(n, blocksize=32))], ws, need, None) == \
+        bnbx.BNBX_E_UNSUPPORTED
+    assert status_of(f, [item(), item(w=A + 2)], ws, need, None) == bnbx.BNBX_E_ALIGN
+    assert status_of(f, [item(), item(p=B + 8)], ws, need, None) == bnbx.BNBX_E_ALIGN
+    assert status_of(f, ok, None, need, None) == bnbx.BNBX_E_WORKSPACE
+    assert status_of(f, ok, ws, need - 1, None) == bnbx.BNBX_E_WORKSPACE
+    assert status_of(f, ok, ws + 128, need, None) == bnbx.BNBX_E_ALIGN
 
 
 def test_dequantize_rejects():
