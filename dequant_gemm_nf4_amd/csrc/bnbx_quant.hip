@@ -18,11 +18,13 @@
 // base-2^32 digits) and writes to its own workspace slot; double_quant_kernel
 // adds the slots and forms the exactly rounded mean.
 //
-// The grouped kernels (quantize_group_kernel, double_quant_group_kernel) do
-// the same for up to kMaxQItems tensors per launch: the quantize kernel walks
-// the tensors one after another with one histogram and one slot per tensor,
-// and each double-quant workgroup takes groups of one tensor.  Per tensor the
-// arithmetic is the single kernels' (the same device functions).
+// The grouped kernels do the same for up to kMaxQItems tensors per call:
+// quantize_group_kernel walks the tensors one after another with one
+// histogram and one slot per tensor (the single kernel's per-tensor device
+// function), dq_mean_kernel forms each tensor's exact mean in one workgroup,
+// and dq_codes_kernel gives each group of 256 block scales one wave (group
+// max by a wave reduction, no workgroup barrier), with the arithmetic of
+// double_quant_groups.
 #include "bnbx_device.hpp"
 #include "bnbx_internal.hpp"
 
@@ -371,31 +373,27 @@ __device__ float exact_mean(const unsigned long long* __restrict__ slots, int ns
   return (float)mean;
 }
 
-// Groups per double_quant workgroup (single tensor, grouped launch); their
-// absmax values are loaded before the mean is formed, so that one memory
-// latency covers both.  Every workgroup also reads all of its tensor's
-// slots, which the grouped launch, with many more groups, pays back by
-// taking more groups per workgroup.
+// Groups per double_quant workgroup; their absmax values are loaded before
+// the mean is formed, so that one memory latency covers both.
 constexpr int kDqGroups = 4;
-constexpr int kDqGroupsGrouped = 8;
 
 // Second level of the double quantization (mlqm.cn article, sec. 3.3) for
-// groups g0 .. g0 + NG - 1 of one tensor: the exact mean, the group
+// groups g0 .. g0 + kDqGroups - 1 of one tensor: the exact mean, the group
 // scales s_g = max |a_b - mean|, and per block the code of t = fl32((a_b -
 // mean) / s_g): linear, round-half-even(fl32(t * 127)) as int8; DYN, the
 // index of the nearest value of the dynamic 8-bit map (exact ties to the
 // lower index), found by binary search over the exact binary64 midpoints of
 // neighbouring values.  A group with s_g = 0 stores the code of the value 0.
 // The mean goes to mean_out when write_mean is set.
-template <bool DYN, int NG>
+template <bool DYN>
 __device__ __forceinline__ void double_quant_groups(
     const float* __restrict__ a, const unsigned long long* __restrict__ slots, int nslots,
     int64_t nb, uint8_t* __restrict__ q, float* __restrict__ s_out, float* __restrict__ mean_out,
     bool write_mean, int64_t g0, unsigned long long* digits, float (*red)[4], double* mids) {
   const int tid = threadIdx.x;
-  float v[NG];
+  float v[kDqGroups];
 #pragma unroll
-  for (int i = 0; i < NG; ++i) {
+  for (int i = 0; i < kDqGroups; ++i) {
     const int64_t b = (g0 + i) * kGroup + tid;
     v[i] = b < nb ? a[b] : 0.0f;
   }
@@ -403,9 +401,9 @@ __device__ __forceinline__ void double_quant_groups(
   const float mu = exact_mean(slots, nslots, nb, digits);
   if (write_mean && tid == 0) *mean_out = mu;
   const int64_t ng = (nb + kGroup - 1) / kGroup;
-  float c[NG];
+  float c[kDqGroups];
 #pragma unroll
-  for (int i = 0; i < NG; ++i) {
+  for (int i = 0; i < kDqGroups; ++i) {
     const int64_t b = (g0 + i) * kGroup + tid;
     c[i] = b < nb ? v[i] - mu : 0.0f;
     const float m = wave_max(fabsf(c[i]));
@@ -413,7 +411,7 @@ __device__ __forceinline__ void double_quant_groups(
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < NG; ++i) {
+  for (int i = 0; i < kDqGroups; ++i) {
     const int64_t g = g0 + i;
     if (g >= ng) break;   // uniform
     const int64_t b = g * kGroup + tid;
@@ -445,17 +443,16 @@ __global__ __launch_bounds__(256) void double_quant_kernel(
   __shared__ unsigned long long digits[kSumDigits];
   __shared__ float red[kDqGroups][4];
   __shared__ double mids[DYN ? 256 : 1];
-  double_quant_groups<DYN, kDqGroups>(a, slots, nslots, nb, q, s_out, mean_out, blockIdx.x == 0,
+  double_quant_groups<DYN>(a, slots, nslots, nb, q, s_out, mean_out, blockIdx.x == 0,
                            (int64_t)blockIdx.x * kDqGroups, digits, red, mids);
 }
 
-// The tensors of one grouped double_quant launch: workgroups
-// [wg_end[i-1], wg_end[i]) take tensor i (wg_end[-1] = 0, entries past
-// `count` hold INT_MAX), whose quantize slots start at
-// slots + i * nslots * kSumDigits.
+// The tensors of the grouped second level: tensor i owns global groups
+// [gend[i-1], gend[i]) (gend[-1] = 0, entries past `count` hold INT64_MAX);
+// its quantize slots start at slots + i * nslots * kSumDigits.
 struct DqItems {
   int count;
-  int wg_end[kMaxQItems];
+  int64_t gend[kMaxQItems];
   int64_t nb[kMaxQItems];
   const float* a[kMaxQItems];
   uint8_t* q[kMaxQItems];
@@ -463,21 +460,90 @@ struct DqItems {
   float* mean[kMaxQItems];
 };
 
-template <bool DYN>
-__global__ __launch_bounds__(256) void double_quant_group_kernel(
+// Grouped second level, first launch: workgroup i forms tensor i's exact
+// mean and writes it to the tensor's state.
+__global__ __launch_bounds__(256) void dq_mean_kernel(
     DqItems it, const unsigned long long* __restrict__ slots, int nslots) {
   __shared__ unsigned long long digits[kSumDigits];
-  __shared__ float red[kDqGroupsGrouped][4];
+  const int i = blockIdx.x;
+  const float mu = exact_mean(slots + (int64_t)i * nslots * kSumDigits, nslots,
+                              pick_item(it.nb, i), digits);
+  if (threadIdx.x == 0) *pick_item(it.mean, i) = mu;
+}
+
+constexpr int kDqcThreads = 1024;
+
+// Grouped second level, second launch: one wave per group of 256 blocks,
+// lane l taking blocks 4l .. 4l + 3 (one 16-byte load), the group max |a_b -
+// mean| by a wave reduction, then the codes of the double_quant_groups rule
+// (the same operations on the same values); four codes per lane leave in one
+// dword store when the code array allows it.  Wave w of the grid takes the
+// global groups w, w + W, ... (W waves).
+template <bool DYN>
+__global__ __launch_bounds__(kDqcThreads) void dq_codes_kernel(DqItems it, int64_t total_groups) {
   __shared__ double mids[DYN ? 256 : 1];
-  const int wg = blockIdx.x;
-  int i = 0;
+  if (DYN) {
+    for (int e = threadIdx.x; e < 255; e += kDqcThreads) mids[e] = kDynMapDev.mid[e];
+    __syncthreads();
+  }
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (int64_t)gridDim.x * (kDqcThreads / 64);
+  for (int64_t gg = (int64_t)blockIdx.x * (kDqcThreads / 64) +
+                    __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+       gg < total_groups; gg += nw) {
+    int i = 0;
 #pragma unroll
-  for (int k = 0; k < kMaxQItems - 1; ++k) i += wg >= it.wg_end[k] ? 1 : 0;
-  const int wg0 = i == 0 ? 0 : pick_item(it.wg_end, i - 1);
-  double_quant_groups<DYN, kDqGroupsGrouped>(pick_item(it.a, i), slots + (int64_t)i * nslots * kSumDigits, nslots,
-                           pick_item(it.nb, i), pick_item(it.q, i), pick_item(it.s, i),
-                           pick_item(it.mean, i), wg == wg0, (int64_t)(wg - wg0) * kDqGroupsGrouped,
-                           digits, red, mids);
+    for (int k = 0; k < kMaxQItems - 1; ++k) i += gg >= it.gend[k] ? 1 : 0;
+    const int64_t g = gg - (i == 0 ? 0 : pick_item(it.gend, i - 1));
+    const int64_t nb = pick_item(it.nb, i);
+    const float* const a = pick_item(it.a, i);
+    uint8_t* const q = pick_item(it.q, i);
+    const float mu = *pick_item(it.mean, i);
+    const int64_t b0 = g * kGroup + lane * 4;
+    const bool whole = b0 + 4 <= nb;
+    float v[4];
+    if (whole) {
+      const float4 t = *(const float4*)(a + b0);
+      v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = b0 + k < nb ? a[b0 + k] : 0.0f;
+    }
+    float c[4], m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      c[k] = b0 + k < nb ? v[k] - mu : 0.0f;
+      m = fmaxf(m, fabsf(c[k]));
+    }
+    const float s = wave_max(m);
+    uint32_t word = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      int qv = DYN ? kDynZeroCode : 0;
+      if (s > 0.0f) {
+        const float t = c[k] / s;       // correctly rounded binary32 division
+        if (DYN) {
+          int idx = 0;
+#pragma unroll
+          for (int step = 128; step >= 1; step >>= 1)
+            if ((double)t > mids[idx + step - 1]) idx += step;
+          qv = idx;
+        } else {
+          const float u = t * 127.0f;
+          qv = (int)rintf(u);           // round half to even
+        }
+      }
+      word |= ((uint32_t)qv & 0xffu) << (8 * k);
+    }
+    if (whole && ((uintptr_t)q & 3u) == 0) {
+      *(uint32_t*)(q + b0) = word;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (b0 + k < nb) q[b0 + k] = (uint8_t)(word >> (8 * k));
+    }
+    if (lane == 0) pick_item(it.s, i)[g] = s;
+  }
 }
 
 int grid_for(int64_t work_items, int per_block, int cap) {
@@ -561,29 +627,33 @@ hipError_t launch_quantize(const QuantJob* jobs, int count, unsigned long long* 
 
   DqItems dqi{};
   dqi.count = count;
-  int64_t wgs = 0;
+  int64_t groups = 0;
   for (int i = 0; i < kMaxQItems; ++i) {
     if (i < count) {
       const int64_t nb = (jobs[i].n + kBlock - 1) / kBlock;
-      const int64_t ng = (nb + kGroup - 1) / kGroup;
-      wgs += (ng + kDqGroupsGrouped - 1) / kDqGroupsGrouped;
-      if (wgs > 0x7fffffff) return hipErrorInvalidValue;
-      dqi.wg_end[i] = (int)wgs;
+      groups += (nb + kGroup - 1) / kGroup;
+      dqi.gend[i] = groups;
       dqi.nb[i] = nb;
       dqi.a[i] = jobs[i].absmax_f32;
       dqi.q[i] = jobs[i].q;
       dqi.s[i] = jobs[i].absmax2;
       dqi.mean[i] = jobs[i].mean;
     } else {
-      dqi.wg_end[i] = 0x7fffffff;
+      dqi.gend[i] = INT64_MAX;
     }
   }
+  hipLaunchKernelGGL(dq_mean_kernel, dim3(count), dim3(256), 0, stream, dqi, slots, grid);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t per_wg = kDqcThreads / 64;
+  int64_t cgrid = (groups + per_wg - 1) / per_wg;
+  cgrid = cgrid < 1024 ? cgrid : 1024;
   if (dq == kDqDynamic)
-    hipLaunchKernelGGL(double_quant_group_kernel<true>, dim3((unsigned)wgs), dim3(256), 0, stream,
-                       dqi, slots, grid);
+    hipLaunchKernelGGL(dq_codes_kernel<true>, dim3((unsigned)cgrid), dim3(kDqcThreads), 0, stream,
+                       dqi, groups);
   else
-    hipLaunchKernelGGL(double_quant_group_kernel<false>, dim3((unsigned)wgs), dim3(256), 0,
-                       stream, dqi, slots, grid);
+    hipLaunchKernelGGL(dq_codes_kernel<false>, dim3((unsigned)cgrid), dim3(kDqcThreads), 0,
+                       stream, dqi, groups);
   return hipGetLastError();
 }
 

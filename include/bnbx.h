@@ -222,9 +222,10 @@ BNBX_API size_t bnbx_quantize_nf4_grouped_workspace_bytes(const int64_t* n, int 
  * BNBX_QUANTIZE_MAX_ITEMS tensors at once, for a loader that quantizes a
  * layer's weights as they arrive (mlqm.cn article sec. 2.2: weights are
  * quantized while they are loaded; sec. 3.2-3.3, 4 as bnbx_quantize_nf4).
- * One launch quantizes every tensor's blocks and, with double quant, one
- * more forms every tensor's mean, group scales and codes, so the fixed cost
- * of a launch is paid once per group instead of once per tensor.  Each
+ * One launch quantizes every tensor's blocks and, with double quant, two
+ * short ones form every tensor's mean and then its group scales and codes,
+ * so the fixed cost of the launches is paid once per group of tensors
+ * instead of once per tensor.  Each
  * tensor is quantized on its own (its own blocks, mean and groups): its
  * results are bit-identical to a bnbx_quantize_nf4 call on it.
  *   items      host array of `count` items, read during the call
