@@ -531,7 +531,7 @@ def main():
     dx_tflops = 2.0 * Mp * Np * Kp / (dx_ms * 1e-3) / 1e12
     del dyp, dxp
 
-    # The GEMM with a LoRA term in its epilogue (ranks 16 and 64), same
+    # The GEMM with a LoRA term fused in (ranks 16 and 64), same
     # weight and X, and the plain GEMM beside it: one graph each, timed in
     # interleaved rounds (the clock under load drifts between consecutive
     # measurements by more than the difference being measured), the median
@@ -546,7 +546,7 @@ def main():
     for r, (xa, lb, la) in lora_in.items():
         fns[f"r{r}"] = (lambda xa=xa, lb=lb: T.gemm_lora(xp, qp, xa, lb, out=yp))
         # the adapter's down-projection in the library too: XA = s X A^T, then
-        # the GEMM with the low-rank epilogue
+        # the GEMM with the low-rank term
         fns[f"r{r}_down"] = (lambda xa=xa, la=la: T.lora_down(xp, la, 2.0, out=xa))
         fns[f"r{r}_full"] = (lambda xa=xa, lb=lb, la=la: (T.lora_down(xp, la, 2.0, out=xa),
                                                           T.gemm_lora(xp, qp, xa, lb, out=yp)))

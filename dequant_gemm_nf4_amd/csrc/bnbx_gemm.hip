@@ -61,6 +61,7 @@ constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 constexpr int kABuf = BM * BK;   // bf16 elements per X buffer (128 B rows)
+constexpr int kMaxLoraRank = 256;   // the largest r bnbx_gemm_nf4_lora takes
 
 // Scheduling-group masks (AMDGPU sched_group_barrier).
 constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgSalu = 0x004, kSgVmem = 0x010,
@@ -165,8 +166,9 @@ __device__ __forceinline__ void share_tab16(const Tab16& own, Tab16* t) {
   }
 }
 
-// Low-rank term added in the epilogue (LoRA: Y += XA . B^T, XA = s X A^T
-// given as [M, r], B the up-projection [N, r]); r a multiple of 16.
+// Low-rank term accumulated before the main loop (LoRA: Y += XA . B^T,
+// XA = s X A^T given as [M, r], B the up-projection [N, r]); r a multiple of
+// 16.
 struct LoraArgs {
   const uint16_t* xa;
   int64_t ldxa;
@@ -338,6 +340,50 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   auto wset = [&](int i) -> WSet& { return i == 0 ? ws0 : i == 1 ? ws1 : i == 2 ? ws2 : ws3; };
   auto qset = [&](int i) -> QSet& { return i == 0 ? qs0 : i == 1 ? qs1 : i == 2 ? qs2 : qs3; };
 
+  if constexpr (LORA) {
+    // The low-rank term first, as r / 16 MFMAs per tile into the zeroed
+    // accumulators, with XA rows as A and rows of B as B operands in the same
+    // lane layout as X and the weights (lane half h takes k 8h .. 8h + 8 of
+    // each 16); rows past M or N read zero through the buffer range check.
+    const rsrc_t ra = make_rsrc(la.xa, (uint32_t)((int64_t)(M - 1) * la.ldxa * 2 + la.r * 2));
+    const rsrc_t rb = make_rsrc(la.b, (uint32_t)((int64_t)(N - 1) * la.ldb * 2 + la.r * 2));
+    auto load_lr = [&](u32x4_t (&xa)[8], u32x4_t (&lb)[2], int k0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t row = m0 + 32 * i + col;
+        xa[i] = __builtin_amdgcn_raw_buffer_load_b128(
+            ra, (uint32_t)((row * la.ldxa + k0 + 8 * half) * 2), 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t n = n0 + wave * 64 + 32 * j + col;
+        lb[j] = __builtin_amdgcn_raw_buffer_load_b128(
+            rb, (uint32_t)((n * la.ldb + k0 + 8 * half) * 2), 0, 0);
+      }
+    };
+    auto mfma_lr = [&](const u32x4_t (&xa)[8], const u32x4_t (&lb)[2]) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16<F16>(xa[i], lb[j], acc[i][j]);
+    };
+    // Two operand sets: the loads of step s + 1 go out before the MFMAs of
+    // step s.  Unrolled over the largest rank with the two sets named apart
+    // (a loop carrying the accumulators, or one array of sets indexed by the
+    // step, spilled); steps past r are skipped by uniform branches.
+    u32x4_t xa0[8], lb0[2], xa1[8], lb1[2];
+    load_lr(xa0, lb0, 0);
+#pragma unroll
+    for (int st = 0; st < kMaxLoraRank / 16; st += 2) {
+      if (16 * st >= la.r) break;
+      if (16 * (st + 1) < la.r) load_lr(xa1, lb1, 16 * (st + 1));
+      mfma_lr(xa0, lb0);
+      if (16 * (st + 1) >= la.r) break;
+      if (16 * (st + 2) < la.r) load_lr(xa0, lb0, 16 * (st + 2));
+      mfma_lr(xa1, lb1);
+    }
+  }
+
   // Prologue: X of step 0, weights of steps 0..2, scales, tables of step 0.
   copy_x(As0, 0, 0, 8);
   load_w(ws0, 0);
@@ -439,38 +485,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   // The lane's position again, from an instruction the compiler cannot see
   // through: values derived from it before the K loop would otherwise stay
   // live across the loop (where every register is in use) only to address
-  // the epilogue, and the LoRA variant spilled them.
+  // the stores of Y, and the LoRA variant spilled them.
   int lane_e;
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
   const int col_e = lane_e & 31, half_e = lane_e >> 5;
-
-  if constexpr (LORA) {
-    // The low-rank term as r / 16 more MFMAs per tile, with XA rows as A and
-    // rows of B as B operands in the same lane layout as X and the weights
-    // (lane half h takes k 8h .. 8h + 8 of each 16); rows past M or N read
-    // zero through the buffer range check.
-    const rsrc_t ra = make_rsrc(la.xa, (uint32_t)((int64_t)(M - 1) * la.ldxa * 2 + la.r * 2));
-    const rsrc_t rb = make_rsrc(la.b, (uint32_t)((int64_t)(N - 1) * la.ldb * 2 + la.r * 2));
-    for (int k0 = 0; k0 < la.r; k0 += 16) {
-      u32x4_t xa[8], lb[2];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t row = m0 + 32 * i + col_e;
-        xa[i] = __builtin_amdgcn_raw_buffer_load_b128(
-            ra, (uint32_t)((row * la.ldxa + k0 + 8 * half_e) * 2), 0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t n = n0 + wave * 64 + 32 * j + col_e;
-        lb[j] = __builtin_amdgcn_raw_buffer_load_b128(
-            rb, (uint32_t)((n * la.ldb + k0 + 8 * half_e) * 2), 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16<F16>(xa[i], lb[j], acc[i][j]);
-    }
-  }
 
   // D layout of a 32x32 MFMA tile: lane l, value v -> column l%32,
   // row 8*(v/4) + 4*(l/32) + v%4.

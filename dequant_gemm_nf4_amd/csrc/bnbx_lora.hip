@@ -2,7 +2,7 @@
 // with fp32 accumulation (the pomoai.com overview, QLoRA: trainable low-rank
 // adapters beside the frozen 4-bit base layer; A is the adapter's
 // nn.Linear(K, r) weight, s its scale).  XA then feeds the fused low-rank
-// term of the 4-bit GEMM's epilogue (bnbx_gemm_nf4_lora), which adds XA . B^T.
+// term of the 4-bit GEMM (bnbx_gemm_nf4_lora), which adds XA . B^T.
 //
 // One workgroup of W waves (16 for r <= 128, else 8) takes 16 rows of X and
 // all r columns; wave w takes the w-th of W parts of K (in steps of 32, four

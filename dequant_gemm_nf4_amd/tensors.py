@@ -202,7 +202,7 @@ def lora_down(x: torch.Tensor, lora_a: torch.Tensor, scale: float,
 def linear_lora(x: torch.Tensor, q: QuantizedWeight, lora_a: torch.Tensor, lora_b: torch.Tensor,
                 scale: float, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Y = X . W_hat^T + s . (X . A^T) . B^T: the down-projection, then the GEMM
-    with the low-rank term in its epilogue (both in the library)."""
+    with the low-rank term fused in (both in the library)."""
     xa = lora_down(x, lora_a, scale, stream=stream)
     return gemm_lora(x, q, xa, lora_b, out=out, stream=stream)
 

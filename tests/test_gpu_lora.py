@@ -1,5 +1,5 @@
 """GPU parity of bnbx_gemm_nf4_lora, Y = X . W_hat^T + XA . B^T (a LoRA term
-fused into the 4-bit GEMM's epilogue), against the oracle's binary64 result:
+fused into the 4-bit GEMM), against the oracle's binary64 result:
 relative Frobenius error <= 5e-3.  Called through the C ABI."""
 
 import numpy as np
@@ -100,7 +100,7 @@ def test_lora_down_repeats_bit_for_bit_and_writes_only_its_block():
 @pytest.mark.parametrize("qt,dt", [("nf4", "bf16"), ("fp4", "f16")])
 def test_linear_lora_end_to_end(qt, dt):
     """Y = X . W_hat^T + s . (X . A^T) . B^T through the two library calls
-    (the down-projection, then the GEMM with the low-rank epilogue)."""
+    (the down-projection, then the GEMM with the low-rank term)."""
     M, N, K, r = 257, 384, 1024, 32
     w = synth.normal_bf16((N, K), 0.02, 9930)
     x = synth.normal_16((M, K), 1.0, 9931, dt)
