@@ -531,6 +531,46 @@ def main():
     dx_tflops = 2.0 * Mp * Np * Kp / (dx_ms * 1e-3) / 1e12
     del dyp, dxp
 
+    # Prefill GEMMs of one Llama-7B layer at M=2048 (q, k, v, o 4096x4096;
+    # gate, up 11008x4096; down 4096x11008), timed after the steps like the
+    # above: each shape with the workspace bnbx_gemm_nf4_workspace_bytes asks
+    # for (split K where the 256x256 tiles fill at most half of the CUs) and
+    # without one (whole tiles).
+    import dequant_gemm_nf4_amd as bnbx_lib
+    llama_prefill = {}
+    layer_us = {"planned": 0.0, "whole_tiles": 0.0}
+    for name, (Nl, Kl), count in (("qkvo", (4096, 4096), 4), ("gate_up", (11008, 4096), 2),
+                                  ("down", (4096, 11008), 1)):
+        gen.manual_seed(7200 + Nl + Kl)
+        wl = (torch.randn(Nl, Kl, generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+        ql = T.quantize(wl, True)
+        del wl
+        xl = torch.randn(Mp, Kl, generator=gen, device=dev).to(torch.bfloat16)
+        yl = torch.empty(Mp, Nl, dtype=torch.bfloat16, device=dev)
+        need = bnbx_lib.bnbx_gemm_nf4_workspace_bytes(Mp, Nl, Kl)
+        wsl = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        reps_l = max(2, args.steps)
+        ms_plan = timed_ms(lambda: bnbx_lib.bnbx_gemm_nf4(
+            xl, Kl, ql.packed, ql.state, Mp, Nl, Kl, yl, Nl, wsl if need else None, need), reps_l)
+        ms_whole = timed_ms(lambda: bnbx_lib.bnbx_gemm_nf4(
+            xl, Kl, ql.packed, ql.state, Mp, Nl, Kl, yl, Nl, None, 0), reps_l)
+        fl = 2.0 * Mp * Nl * Kl
+        llama_prefill[name] = {"shape": f"{Mp}x{Nl}x{Kl}", "per_layer": count,
+                               "split_workspace_bytes": need,
+                               "us": round(ms_plan * 1e3, 1),
+                               "tflops": round(fl / (ms_plan * 1e-3) / 1e12, 1),
+                               "whole_tiles_us": round(ms_whole * 1e3, 1),
+                               "whole_tiles_tflops": round(fl / (ms_whole * 1e-3) / 1e12, 1)}
+        layer_us["planned"] += count * ms_plan * 1e3
+        layer_us["whole_tiles"] += count * ms_whole * 1e3
+        del ql, xl, yl, wsl
+    layer_flops = sum(2.0 * Mp * n * k * c for (n, k), c in
+                      (((4096, 4096), 4), ((11008, 4096), 2), ((4096, 11008), 1)))
+    llama_prefill["layer"] = {
+        "us": round(layer_us["planned"], 1),
+        "tflops": round(layer_flops / (layer_us["planned"] * 1e-6) / 1e12, 1),
+        "whole_tiles_us": round(layer_us["whole_tiles"], 1)}
+
     # The GEMM with a LoRA term fused in (ranks 16 and 64), same
     # weight and X, and the plain GEMM beside it: one graph each, timed in
     # interleaved rounds (the clock under load drifts between consecutive
@@ -684,6 +724,7 @@ def main():
             },
             "variants": variants,
             "gemm_lora": lora,
+            "gemm_llama7b_prefill": llama_prefill,
             "gemm_dx": {"what": "dX = dY . W_hat, M=2048 N=K=8192, NF4 double quant, bf16",
                         "ms": round(dx_ms, 4), "tflops": round(dx_tflops, 1),
                         "frac": round(dx_tflops / BF16_PEAK_TFLOPS, 4)},

@@ -452,23 +452,20 @@ int bnbx_lora_down(const uint16_t* x, int64_t ldx, const uint16_t* lora_a, int64
 }
 
 size_t bnbx_gemm_nf4_workspace_bytes(int M, int N, int K) {
-  (void)M;
-  (void)N;
-  (void)K;
-  return 0;
+  if (M < 1 || N < 1 || K < kBlock || K % kBlock != 0) return 0;
+  return gemm_workspace_bytes(M, N, K);
 }
 
 int bnbx_gemm_nf4(const uint16_t* x, int64_t ldx, const uint8_t* packed,
                   const bnbx_nf4_state* st, int M, int N, int K, uint16_t* y, int64_t ldy,
                   void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   const int s = check_matmul(x, ldx, packed, st, M, N, K, y, ldy);
   if (s != BNBX_OK) return s;
+  if (workspace != nullptr && workspace_bytes > 0 && !aligned(workspace, 16)) return BNBX_E_ALIGN;
   const hipError_t e = launch_gemm(x, ldx, packed, st->absmax, st->absmax2, st->absmax_mean,
                                    st->double_quant, st->quant_type,
                                    st->compute_dtype == BNBX_DTYPE_F16, M, N, K, y, ldy,
-                                   (hipStream_t)stream);
+                                   workspace, workspace_bytes, (hipStream_t)stream);
   if (e == hipErrorNotSupported) return BNBX_E_UNSUPPORTED;
   return hip_status(e);
 }

@@ -177,12 +177,22 @@ struct LoraArgs {
   int r;
 };
 
-template <int DQ, bool Q4, bool FP4, bool F16, bool LORA>
+// Split K (SPLIT): workgroups [s W, (s + 1) W) take K steps [s kb_per,
+// (s + 1) kb_per) of every tile (W workgroups per split) and store their fp32
+// partial tiles at part + (s M + r) ldp + c; reduce_kernel adds the splits in
+// order and rounds once.
+struct SplitArgs {
+  int kb_per;   // K steps per split, a multiple of 4
+  float* part;
+  int64_t ldp;
+};
+
+template <int DQ, bool Q4, bool FP4, bool F16, bool LORA, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ packed,
     const void* __restrict__ absmax, const float* __restrict__ absmax2,
     const float* __restrict__ mean, int M, int N, int K, uint16_t* __restrict__ y, int64_t ldy,
-    int tiles_m, int tiles_n, LevelTable lv, LoraArgs la) {
+    int tiles_m, int tiles_n, LevelTable lv, LoraArgs la, SplitArgs sp) {
   __shared__ __attribute__((aligned(16))) uint16_t As0[kABuf], As1[kABuf];
   constexpr bool DYN = DQ == kDqDynamic;
   __shared__ float dmap[DYN ? 256 : 1];   // the dynamic 8-bit map (DYN)
@@ -195,7 +205,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   // XCD-aware tile id: workgroups b, b+8, b+16, ... share an XCD.
   const int ntiles = tiles_m * tiles_n;
   const int per_xcd = (ntiles + kXcds - 1) / kXcds;
-  const int b = blockIdx.x;
+  int b = blockIdx.x;
+  int split = 0;
+  if constexpr (SPLIT) {
+    split = b / (per_xcd * kXcds);   // both splits of a tile share its XCD
+    b -= split * per_xcd * kXcds;
+  }
   const int tile = (b % kXcds) * per_xcd + b / kXcds;
   if (tile >= ntiles) return;
   const int m0 = (tile / tiles_n) * BM;
@@ -208,6 +223,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   const float mu = DQ ? *mean : 0.0f;
   const uint32_t rowK2 = (uint32_t)K >> 1;   // packed bytes per weight row
   const int nkb = K >> 6;
+  // This workgroup's K steps [kb0, kb1) (all of them without SPLIT).
+  const int kb0 = SPLIT ? split * sp.kb_per : 0;
+  const int kb1 = SPLIT ? (kb0 + sp.kb_per < nkb ? kb0 + sp.kb_per : nkb) : nkb;
 
   // The lane's weight rows (B columns) n0 + 64 w + 32 j + l % 32, j = 0, 1;
   // rows past N are clamped to N-1 (their tables are zero).
@@ -245,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     xvoff[i] = (uint32_t)(((int64_t)gm * ldx + chunk * 8) * 2);
   }
   auto copy_x = [&](uint16_t* xbuf, int kb, int i0, int i1) {
-    kb = kb < nkb ? kb : nkb - 1;
+    kb = kb < kb1 ? kb : kb1 - 1;
 #pragma unroll
     for (int i = i0; i < i1; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -253,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
           xvoff[i], (uint32_t)kb * (BK * 2), 0, 0);
   };
   auto load_w = [&](WSet& s, int kb) {
-    kb = kb < nkb ? kb : nkb - 1;
+    kb = kb < kb1 ? kb : kb1 - 1;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       s.w[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, wvoff[j], (uint32_t)kb * 32u, 0);
@@ -261,12 +279,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   // Own-row scale of one step (Q4 = false) or of the four steps 4g..4g+3 (Q4).
   auto load_q = [&](QSet& s, int idx) {
     if (Q4) {
-      const int g = idx < (nkb >> 2) ? idx : (nkb >> 2) - 1;
+      const int g = idx < (kb1 >> 2) ? idx : (kb1 >> 2) - 1;
       const uint32_t blk = qvoff + 4u * (uint32_t)g;
       s.q = __builtin_amdgcn_raw_buffer_load_b32(rq, blk, 0, 0);
       s.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, (blk >> 8) * 4u, 0, 0));
     } else {
-      const int kb = idx < nkb ? idx : nkb - 1;
+      const int kb = idx < kb1 ? idx : kb1 - 1;
       const uint32_t blk = qvoff + (uint32_t)kb;
       if (DQ) {
         // Kept as the raw byte; the sign extension is done where the scale
@@ -384,18 +402,19 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     }
   }
 
-  // Prologue: X of step 0, weights of steps 0..2, scales, tables of step 0.
-  copy_x(As0, 0, 0, 8);
-  load_w(ws0, 0);
-  load_w(ws1, 1);
-  load_w(ws2, 2);
+  // Prologue: X of step kb0, weights of steps kb0..kb0+2, scales, tables of
+  // step kb0 (kb0 is a multiple of 4, so step t's sets are those of t % 4).
+  copy_x(As0, kb0, 0, 8);
+  load_w(ws0, kb0);
+  load_w(ws1, kb0 + 1);
+  load_w(ws2, kb0 + 2);
   if (Q4) {
-    load_q(qs0, 0);   // current group
-    load_q(qs1, 1);   // next group
+    load_q(qs0, kb0 / 4);       // current group
+    load_q(qs1, kb0 / 4 + 1);   // next group
   } else {
-    load_q(qs0, 0);
-    load_q(qs1, 1);
-    load_q(qs2, 2);
+    load_q(qs0, kb0);
+    load_q(qs1, kb0 + 1);
+    load_q(qs2, kb0 + 2);
   }
   share_tab16(make_tab16<FP4, F16>(lv, scale_of(qs0, 0)), tA);
   Tab16 own;
@@ -469,17 +488,17 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   using K3 = std::integral_constant<int, 3>;
   using F0 = std::integral_constant<bool, false>;
   using F1 = std::integral_constant<bool, true>;
-  step(K0{}, F1{}, 0, tA, tB);
-  int kb = 1;
-  for (; kb + 3 < nkb; kb += 4) {
+  step(K0{}, F1{}, kb0, tA, tB);
+  int kb = kb0 + 1;
+  for (; kb + 3 < kb1; kb += 4) {
     step(K1{}, F0{}, kb, tB, tA);
     step(K2{}, F0{}, kb + 1, tA, tB);
     step(K3{}, F0{}, kb + 2, tB, tA);
     step(K0{}, F0{}, kb + 3, tA, tB);
   }
-  if (kb < nkb) step(K1{}, F0{}, kb, tB, tA);
-  if (kb + 1 < nkb) step(K2{}, F0{}, kb + 1, tA, tB);
-  if (kb + 2 < nkb) step(K3{}, F0{}, kb + 2, tB, tA);
+  if (kb < kb1) step(K1{}, F0{}, kb, tB, tA);
+  if (kb + 1 < kb1) step(K2{}, F0{}, kb + 1, tA, tB);
+  if (kb + 2 < kb1) step(K3{}, F0{}, kb + 2, tB, tA);
   mfmas(1);   // substep 3 of the last step
 
   // The lane's position again, from an instruction the compiler cannot see
@@ -500,37 +519,140 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = m0 + i * 32 + 8 * (v >> 2) + 4 * half_e + (v & 3);
-        if (r < M && c < N) y[(int64_t)r * ldy + c] = f32_to_16<F16>(acc[i][j][v]);
+        if constexpr (SPLIT) {
+          if (r < M && c < N) sp.part[((int64_t)split * M + r) * sp.ldp + c] = acc[i][j][v];
+        } else {
+          if (r < M && c < N) y[(int64_t)r * ldy + c] = f32_to_16<F16>(acc[i][j][v]);
+        }
       }
     }
+}
+
+// Split K: the fp32 partial tiles of the splits, added in split order and
+// rounded once (four columns per thread; columns past N of the padded rows
+// are read and dropped).
+template <bool F16>
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part,
+                                                           int64_t ldp, int nsplit, int M, int N,
+                                                           uint16_t* __restrict__ y,
+                                                           int64_t ldy) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t quads = ldp / 4;
+  const int64_t r = idx / quads;
+  const int c = (int)(idx - r * quads) * 4;
+  if (r >= M) return;
+  float4 a = *(const float4*)(part + r * ldp + c);
+  for (int s = 1; s < nsplit; ++s) {
+    const float4 b = *(const float4*)(part + ((int64_t)s * M + r) * ldp + c);
+    a.x += b.x;
+    a.y += b.y;
+    a.z += b.z;
+    a.w += b.w;
+  }
+  const float v[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (c + k < N) y[r * ldy + c + k] = f32_to_16<F16>(v[k]);
+}
+
+int device_cus() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
+// Split-K plan: when the tiles fill at most half of the CUs and K has at
+// least 32 steps, K is split into nsplit ranges of kb_per steps (a multiple
+// of 4, at least 16 each, at most 4 splits) so that the tiles times the
+// splits come closer to one workgroup per CU.  Returns the fp32 partials'
+// bytes, 0 without a split.
+struct SplitPlan {
+  int nsplit, kb_per;
+  int64_t ldp;
+};
+size_t split_plan(int M, int N, int K, SplitPlan& sp) {
+  sp = SplitPlan{1, 0, 0};
+  const int64_t tiles = (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int nkb = K / 64;
+  const int cus = device_cus();
+  if (tiles * 2 > cus || nkb < 32) return 0;
+  int s = (int)(cus / tiles);
+  s = s < 4 ? s : 4;
+  s = s < nkb / 16 ? s : nkb / 16;
+  if (s < 2) return 0;
+  const int kb_per = ((nkb + s - 1) / s + 3) / 4 * 4;
+  const int n = (nkb + kb_per - 1) / kb_per;
+  if (n < 2) return 0;
+  sp.nsplit = n;
+  sp.kb_per = kb_per;
+  sp.ldp = ((int64_t)N + 3) / 4 * 4;
+  return (size_t)n * (size_t)M * (size_t)sp.ldp * sizeof(float);
 }
 
 template <int DQ, bool Q4, bool LORA>
 void launch_one(const uint16_t* x, int64_t ldx, const uint8_t* packed, const void* absmax,
                 const float* absmax2, const float* mean, int M, int N, int K, uint16_t* y,
-                int64_t ldy, int quant_type, bool f16, const LoraArgs& la, hipStream_t stream) {
+                int64_t ldy, int quant_type, bool f16, const LoraArgs& la, const SplitPlan& plan,
+                float* part, hipStream_t stream) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
   const int per_xcd = (tm * tn + kXcds - 1) / kXcds;
   const LevelTable& lv = level_table(quant_type);
+  if constexpr (!LORA) {
+    if (plan.nsplit > 1) {
+      const SplitArgs sa{plan.kb_per, part, plan.ldp};
+      auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3((unsigned)(plan.nsplit * per_xcd * kXcds)),
+                           dim3(kThreads), 0, stream, x, ldx, packed, absmax, absmax2, mean, M,
+                           N, K, y, ldy, tm, tn, lv, la, sa);
+      };
+      if (quant_type == kQuantFP4) {
+        if (f16) go(gemm_kernel<DQ, Q4, true, true, false, true>);
+        else go(gemm_kernel<DQ, Q4, true, false, false, true>);
+      } else {
+        if (f16) go(gemm_kernel<DQ, Q4, false, true, false, true>);
+        else go(gemm_kernel<DQ, Q4, false, false, false, true>);
+      }
+      const int64_t quads = (int64_t)M * (plan.ldp / 4);
+      const unsigned rgrid = (unsigned)((quads + 255) / 256);
+      if (f16)
+        hipLaunchKernelGGL(split_reduce_kernel<true>, dim3(rgrid), dim3(256), 0, stream, part,
+                           plan.ldp, plan.nsplit, M, N, y, ldy);
+      else
+        hipLaunchKernelGGL(split_reduce_kernel<false>, dim3(rgrid), dim3(256), 0, stream, part,
+                           plan.ldp, plan.nsplit, M, N, y, ldy);
+      return;
+    }
+  }
+  const SplitArgs none{0, nullptr, 0};
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3((unsigned)(per_xcd * kXcds)), dim3(kThreads), 0, stream, x,
-                       ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, tm, tn, lv, la);
+                       ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, tm, tn, lv, la, none);
   };
   if (quant_type == kQuantFP4) {
-    if (f16) go(gemm_kernel<DQ, Q4, true, true, LORA>);
-    else go(gemm_kernel<DQ, Q4, true, false, LORA>);
+    if (f16) go(gemm_kernel<DQ, Q4, true, true, LORA, false>);
+    else go(gemm_kernel<DQ, Q4, true, false, LORA, false>);
   } else {
-    if (f16) go(gemm_kernel<DQ, Q4, false, true, LORA>);
-    else go(gemm_kernel<DQ, Q4, false, false, LORA>);
+    if (f16) go(gemm_kernel<DQ, Q4, false, true, LORA, false>);
+    else go(gemm_kernel<DQ, Q4, false, false, LORA, false>);
   }
 }
 
-// The M-slab loop of both entry points.
+// The M-slab loop of both entry points.  Split K (no LoRA term) needs one
+// slab and a workspace of split_plan's size; otherwise the tiles run whole.
 template <bool LORA>
 hipError_t launch_gemm_any(const uint16_t* x, int64_t ldx, const uint8_t* packed,
                            const void* absmax, const float* absmax2, const float* mean,
                            int double_quant, int quant_type, bool f16, int M, int N, int K,
-                           uint16_t* y, int64_t ldy, LoraArgs la, hipStream_t stream) {
+                           uint16_t* y, int64_t ldy, LoraArgs la, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
   // Buffer offsets are 32-bit: the weights and their scales must fit, and M
   // is walked in slabs whose X (and XA) rows do.
   const int64_t kLimit = (int64_t)1 << 31;
@@ -543,11 +665,17 @@ hipError_t launch_gemm_any(const uint16_t* x, int64_t ldx, const uint8_t* packed
   }
   slab = slab / BM * BM;
   if (slab < BM) return hipErrorNotSupported;
+  SplitPlan plan;
+  const size_t need = LORA ? 0 : split_plan(M, N, K, plan);
+  if (need == 0 || M > slab || workspace == nullptr || workspace_bytes < need ||
+      ((uintptr_t)workspace & 15) != 0)
+    plan = SplitPlan{1, 0, 0};
   const int nkb = K / 64;
   // Four block codes per dword load: needs whole groups of four blocks per
   // row (then four blocks never straddle a group of 256) and an aligned
   // code array.
   const bool q4 = double_quant && nkb % 4 == 0 && ((uintptr_t)absmax & 3) == 0;
+  float* part = (float*)workspace;
   for (int64_t r0 = 0; r0 < M; r0 += slab) {
     const int m = (int)(M - r0 < slab ? M - r0 : slab);
     const uint16_t* xs = x + r0 * ldx;
@@ -556,19 +684,19 @@ hipError_t launch_gemm_any(const uint16_t* x, int64_t ldx, const uint8_t* packed
     if (LORA) ls.xa = la.xa + r0 * la.ldxa;
     if (!double_quant)
       launch_one<kDqNone, false, LORA>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys, ldy,
-                                       quant_type, f16, ls, stream);
+                                       quant_type, f16, ls, plan, part, stream);
     else if (double_quant == kDqDynamic && q4)
       launch_one<kDqDynamic, true, LORA>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys,
-                                         ldy, quant_type, f16, ls, stream);
+                                         ldy, quant_type, f16, ls, plan, part, stream);
     else if (double_quant == kDqDynamic)
       launch_one<kDqDynamic, false, LORA>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys,
-                                          ldy, quant_type, f16, ls, stream);
+                                          ldy, quant_type, f16, ls, plan, part, stream);
     else if (q4)
       launch_one<kDqLinear, true, LORA>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys, ldy,
-                                        quant_type, f16, ls, stream);
+                                        quant_type, f16, ls, plan, part, stream);
     else
       launch_one<kDqLinear, false, LORA>(xs, ldx, packed, absmax, absmax2, mean, m, N, K, ys,
-                                         ldy, quant_type, f16, ls, stream);
+                                         ldy, quant_type, f16, ls, plan, part, stream);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -577,12 +705,18 @@ hipError_t launch_gemm_any(const uint16_t* x, int64_t ldx, const uint8_t* packed
 
 }  // namespace
 
+size_t gemm_workspace_bytes(int M, int N, int K) {
+  SplitPlan plan;
+  return split_plan(M, N, K, plan);
+}
+
 hipError_t launch_gemm(const uint16_t* x, int64_t ldx, const uint8_t* packed, const void* absmax,
                        const float* absmax2, const float* mean, int double_quant, int quant_type,
-                       bool f16, int M, int N, int K, uint16_t* y, int64_t ldy,
-                       hipStream_t stream) {
+                       bool f16, int M, int N, int K, uint16_t* y, int64_t ldy, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
   return launch_gemm_any<false>(x, ldx, packed, absmax, absmax2, mean, double_quant, quant_type,
-                                f16, M, N, K, y, ldy, LoraArgs{nullptr, 0, nullptr, 0, 0}, stream);
+                                f16, M, N, K, y, ldy, LoraArgs{nullptr, 0, nullptr, 0, 0},
+                                workspace, workspace_bytes, stream);
 }
 
 hipError_t launch_gemm_lora(const uint16_t* x, int64_t ldx, const uint8_t* packed,
@@ -591,7 +725,8 @@ hipError_t launch_gemm_lora(const uint16_t* x, int64_t ldx, const uint8_t* packe
                             const uint16_t* xa, int64_t ldxa, const uint16_t* lora_b,
                             int64_t ldb, int r, uint16_t* y, int64_t ldy, hipStream_t stream) {
   return launch_gemm_any<true>(x, ldx, packed, absmax, absmax2, mean, double_quant, quant_type,
-                               f16, M, N, K, y, ldy, LoraArgs{xa, ldxa, lora_b, ldb, r}, stream);
+                               f16, M, N, K, y, ldy, LoraArgs{xa, ldxa, lora_b, ldb, r}, nullptr,
+                               0, stream);
 }
 
 }  // namespace bnbx

@@ -154,10 +154,15 @@ hipError_t launch_gemv16_batch(int grid, const uint16_t* x, int64_t ldx, const u
                                const void* absmax, const float* absmax2, const float* mean,
                                int dq, bool f16, int M, int N, int K, uint16_t* y, int64_t ldy,
                                const LevelTable& lv, hipStream_t stream);
+// Workspace of the GEMM's split-K path for (M, N, K) on the current device
+// (fp32 partial tiles; 0 when the tiles already fill the GPU).
+size_t gemm_workspace_bytes(int M, int N, int K);
+// Splits K when the workspace holds gemm_workspace_bytes(M, N, K) bytes
+// (16-byte aligned); otherwise runs the tiles whole.
 hipError_t launch_gemm(const uint16_t* x, int64_t ldx, const uint8_t* packed, const void* absmax,
                        const float* absmax2, const float* mean, int double_quant, int quant_type,
-                       bool f16, int M, int N, int K, uint16_t* y, int64_t ldy,
-                       hipStream_t stream);
+                       bool f16, int M, int N, int K, uint16_t* y, int64_t ldy, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
 // Y = X . W_hat^T + XA . B^T (XA [M, r], B [N, r], r % 16 == 0).
 hipError_t launch_gemm_lora(const uint16_t* x, int64_t ldx, const uint8_t* packed,
                             const void* absmax, const float* absmax2, const float* mean,

@@ -296,17 +296,28 @@ typedef struct {
 BNBX_API int bnbx_gemv_nf4_grouped(const uint16_t* x, int64_t ldx, const bnbx_gemv_item* items,
                                    int count, int M, int K, void* stream);
 
-/* Bytes of device workspace bnbx_gemm_nf4 needs for (M, N, K); the current
- * kernels need none, so it returns 0 for valid sizes. */
+/* Bytes of device workspace bnbx_gemm_nf4 can use for (M, N, K) on the
+ * current device: when the 256 x 256 output tiles fill at most half of the
+ * GPU's compute units and K has at least 32 blocks (2048 values), the GEMM
+ * splits K over up to four workgroups per tile, which write fp32 partial
+ * tiles here, and a second launch adds them in split order and rounds once
+ * (e.g. M = 2048 with N = 4096: 128 tiles on 256 CUs).  Returns 0 when the
+ * tiles already fill the GPU, and for invalid sizes. */
 BNBX_API size_t bnbx_gemm_nf4_workspace_bytes(int M, int N, int K);
 
 /* Prefill GEMM, Y[M, N] = X[M, K] . W_hat[N, K]^T for any M >= 1: weights
  * are dequantized in registers straight into 16-bit matrix-core operands
  * (bf16 or binary16 MFMA by st->compute_dtype) with fp32 accumulation; Y is
  * rounded to the compute dtype (mlqm.cn article sec. 3.4, "4-bit storage,
- * 16-bit compute").  Arguments as bnbx_gemv_nf4; workspace as
- * sized by bnbx_gemm_nf4_workspace_bytes (may be NULL when that is 0).
- * Errors: as bnbx_gemv_nf4 (M >= 1), BNBX_E_WORKSPACE. */
+ * 16-bit compute").  Arguments as bnbx_gemv_nf4.
+ *   workspace  device, 16-byte aligned, or NULL: with at least
+ *              bnbx_gemm_nf4_workspace_bytes(M, N, K) bytes the GEMM may
+ *              split K (see there); with less (or none) it runs the tiles
+ *              whole.  Either way Y is the fp32 sum rounded once; the split
+ *              changes only the order of the fp32 additions.  Contents are
+ *              scratch, overwritten by the call.
+ * Errors: as bnbx_gemv_nf4 (M >= 1); BNBX_E_ALIGN for a misaligned workspace
+ * of nonzero size. */
 BNBX_API int bnbx_gemm_nf4(const uint16_t* x, int64_t ldx, const uint8_t* packed,
                   const bnbx_nf4_state* st, int M, int N, int K,
                   uint16_t* y, int64_t ldy, void* workspace, size_t workspace_bytes,

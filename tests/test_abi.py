@@ -73,6 +73,13 @@ def test_workspace_queries():
     assert bnbx.bnbx_quantize_nf4_workspace_bytes(n + 1, 64, 1) == 0
     assert bnbx.bnbx_quantize_nf4_workspace_bytes(n, 32, 1) == 0
     assert bnbx.bnbx_gemm_nf4_workspace_bytes(2048, 8192, 8192) == 0
+    # split K for shapes whose 256 x 256 tiles fill at most half of the CUs
+    # (256 on MI355X, also the count assumed without a device): fp32 partials
+    assert bnbx.bnbx_gemm_nf4_workspace_bytes(2048, 4096, 4096) == 2 * 2048 * 4096 * 4
+    assert bnbx.bnbx_gemm_nf4_workspace_bytes(300, 500, 4096) == 4 * 300 * 500 * 4
+    assert bnbx.bnbx_gemm_nf4_workspace_bytes(2048, 4096, 1024) == 0   # K too short
+    assert bnbx.bnbx_gemm_nf4_workspace_bytes(0, 4096, 4096) == 0
+    assert bnbx.bnbx_gemm_nf4_workspace_bytes(2048, 4096, 100) == 0
     # grouped: one tensor needs what the single call needs; more add their
     # slots and fp32 absmax arrays
     g = bnbx.bnbx_quantize_nf4_grouped_workspace_bytes
@@ -303,6 +310,9 @@ def test_matmul_rejects(fn):
     assert call(st=state(N * K, blocksize=32)) == bnbx.BNBX_E_UNSUPPORTED
     if fn == "gemv":
         assert call(M=17) == bnbx.BNBX_E_INVAL
+    else:
+        assert status_of(bnbx.bnbx_gemm_nf4, A, K, B, state(N * K), 1, N, K, C, N, D + 8, 64,
+                         0) == bnbx.BNBX_E_ALIGN      # workspace not 16-byte aligned
 
 
 def test_binding_names_match_header():
