@@ -177,14 +177,20 @@ struct LoraArgs {
   int r;
 };
 
-// Split K (SPLIT): workgroups [s W, (s + 1) W) take K steps [s kb_per,
-// (s + 1) kb_per) of every tile (W workgroups per split) and store their fp32
-// partial tiles at part + (s M + r) ldp + c; reduce_kernel adds the splits in
-// order and rounds once.
+// Split K (SPLIT).  Workgroups [0, tile0) take tiles [0, tile0) whole (tile0
+// a multiple of 8, XCD-aware as without SPLIT); the others take the tail
+// tiles [tile0, tiles) in nsplit ranges of K: workgroup tile0 + s W + l
+// (W = 8 per_xcd workgroups per split) takes K steps [s kb_per, (s + 1)
+// kb_per) of tail tile tile0 + (l % 8) per_xcd + l / 8, both splits of a
+// tile on one XCD, and stores its fp32 partial tile (256 x 256, row-major)
+// at part + ((s ntail + t) 256 + r) 256 + c for tail tile t;
+// split_reduce_kernel adds the splits in order and rounds once.
 struct SplitArgs {
-  int kb_per;   // K steps per split, a multiple of 4
+  int kb_per;    // K steps per split, a multiple of 4
+  int tile0;     // tiles run whole
+  int per_xcd;   // tail tiles per XCD
+  int ntail;     // tail tiles
   float* part;
-  int64_t ldp;
 };
 
 template <int DQ, bool Q4, bool FP4, bool F16, bool LORA, bool SPLIT>
@@ -205,13 +211,21 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   // XCD-aware tile id: workgroups b, b+8, b+16, ... share an XCD.
   const int ntiles = tiles_m * tiles_n;
   const int per_xcd = (ntiles + kXcds - 1) / kXcds;
-  int b = blockIdx.x;
-  int split = 0;
+  const int b = blockIdx.x;
+  int split = -1;   // -1: the whole tile
+  int tile;
   if constexpr (SPLIT) {
-    split = b / (per_xcd * kXcds);   // both splits of a tile share its XCD
-    b -= split * per_xcd * kXcds;
+    if (b < sp.tile0) {
+      tile = (b % kXcds) * (sp.tile0 / kXcds) + b / kXcds;
+    } else {
+      int l = b - sp.tile0;
+      split = l / (sp.per_xcd * kXcds);
+      l -= split * sp.per_xcd * kXcds;
+      tile = sp.tile0 + (l % kXcds) * sp.per_xcd + l / kXcds;
+    }
+  } else {
+    tile = (b % kXcds) * per_xcd + b / kXcds;
   }
-  const int tile = (b % kXcds) * per_xcd + b / kXcds;
   if (tile >= ntiles) return;
   const int m0 = (tile / tiles_n) * BM;
   const int n0 = (tile % tiles_n) * BN;
@@ -224,8 +238,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   const uint32_t rowK2 = (uint32_t)K >> 1;   // packed bytes per weight row
   const int nkb = K >> 6;
   // This workgroup's K steps [kb0, kb1) (all of them without SPLIT).
-  const int kb0 = SPLIT ? split * sp.kb_per : 0;
-  const int kb1 = SPLIT ? (kb0 + sp.kb_per < nkb ? kb0 + sp.kb_per : nkb) : nkb;
+  const int kb0 = SPLIT && split >= 0 ? split * sp.kb_per : 0;
+  const int kb1 = SPLIT && split >= 0 ? (kb0 + sp.kb_per < nkb ? kb0 + sp.kb_per : nkb) : nkb;
 
   // The lane's weight rows (B columns) n0 + 64 w + 32 j + l % 32, j = 0, 1;
   // rows past N are clamped to N-1 (their tables are zero).
@@ -520,7 +534,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
       for (int v = 0; v < 16; ++v) {
         const int r = m0 + i * 32 + 8 * (v >> 2) + 4 * half_e + (v & 3);
         if constexpr (SPLIT) {
-          if (r < M && c < N) sp.part[((int64_t)split * M + r) * sp.ldp + c] = acc[i][j][v];
+          if (split >= 0) {
+            const int64_t t = (int64_t)split * sp.ntail + (tile - sp.tile0);
+            sp.part[((t * BM) + (r - m0)) * BN + (c - n0)] = acc[i][j][v];
+          } else if (r < M && c < N) {
+            y[(int64_t)r * ldy + c] = f32_to_16<F16>(acc[i][j][v]);
+          }
         } else {
           if (r < M && c < N) y[(int64_t)r * ldy + c] = f32_to_16<F16>(acc[i][j][v]);
         }
@@ -528,31 +547,36 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     }
 }
 
-// Split K: the fp32 partial tiles of the splits, added in split order and
-// rounded once (four columns per thread; columns past N of the padded rows
-// are read and dropped).
+// Split K: the fp32 partial tiles of the tail tiles, added in split order
+// and rounded once; four columns per thread, only rows and columns inside
+// Y are stored.
 template <bool F16>
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part,
-                                                           int64_t ldp, int nsplit, int M, int N,
+                                                           int nsplit, int ntail, int tile0,
+                                                           int tiles_n, int M, int N,
                                                            uint16_t* __restrict__ y,
                                                            int64_t ldy) {
+  constexpr int kQuads = BM * BN / 4;   // per tile
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t quads = ldp / 4;
-  const int64_t r = idx / quads;
-  const int c = (int)(idx - r * quads) * 4;
+  const int t = (int)(idx / kQuads);
+  if (t >= ntail) return;
+  const int e = (int)(idx - (int64_t)t * kQuads) * 4;
+  const int tile = tile0 + t;
+  const int r = (tile / tiles_n) * BM + e / BN;
+  const int c = (tile % tiles_n) * BN + e % BN;
   if (r >= M) return;
-  float4 a = *(const float4*)(part + r * ldp + c);
+  float4 a = *(const float4*)(part + (int64_t)t * BM * BN + e);
   for (int s = 1; s < nsplit; ++s) {
-    const float4 b = *(const float4*)(part + ((int64_t)s * M + r) * ldp + c);
-    a.x += b.x;
-    a.y += b.y;
-    a.z += b.z;
-    a.w += b.w;
+    const float4 b4 = *(const float4*)(part + ((int64_t)s * ntail + t) * BM * BN + e);
+    a.x += b4.x;
+    a.y += b4.y;
+    a.z += b4.z;
+    a.w += b4.w;
   }
   const float v[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
   for (int k = 0; k < 4; ++k)
-    if (c + k < N) y[r * ldy + c + k] = f32_to_16<F16>(v[k]);
+    if (c + k < N) y[(int64_t)r * ldy + c + k] = f32_to_16<F16>(v[k]);
 }
 
 int device_cus() {
@@ -569,22 +593,29 @@ int device_cus() {
   return n;
 }
 
-// Split-K plan: when the tiles fill at most half of the CUs and K has at
-// least 32 steps, K is split into nsplit ranges of kb_per steps (a multiple
-// of 4, at least 16 each, at most 4 splits) so that the tiles times the
-// splits come closer to one workgroup per CU.  Returns the fp32 partials'
-// bytes, 0 without a split.
+// Split-K plan (K of at least 32 blocks).  Tiles that fill at most half of
+// the CUs all split, into up to four ranges; more tiles than CUs but fewer
+// than twice as many run the first round whole (tile0 = the CUs, rounded
+// down to a multiple of 8) and split the tail tiles, whose round would
+// otherwise leave most CUs idle.  Ranges are multiples of 4 steps, at least
+// 16.  Returns the partial tiles' bytes, 0 without a split.
 struct SplitPlan {
-  int nsplit, kb_per;
-  int64_t ldp;
+  int nsplit, kb_per, tile0, ntail, per_xcd;
 };
 size_t split_plan(int M, int N, int K, SplitPlan& sp) {
-  sp = SplitPlan{1, 0, 0};
+  sp = SplitPlan{1, 0, 0, 0, 0};
   const int64_t tiles = (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int nkb = K / 64;
   const int cus = device_cus();
-  if (tiles * 2 > cus || nkb < 32) return 0;
-  int s = (int)(cus / tiles);
+  if (nkb < 32) return 0;
+  int64_t tile0 = 0;
+  if (tiles * 2 > cus) {
+    if (tiles <= cus || tiles >= 2 * (int64_t)cus) return 0;
+    tile0 = cus / kXcds * kXcds;
+  }
+  const int64_t ntail = tiles - tile0;
+  if (ntail < 1 || ntail * 2 > cus) return 0;
+  int s = (int)(cus / ntail);
   s = s < 4 ? s : 4;
   s = s < nkb / 16 ? s : nkb / 16;
   if (s < 2) return 0;
@@ -593,8 +624,10 @@ size_t split_plan(int M, int N, int K, SplitPlan& sp) {
   if (n < 2) return 0;
   sp.nsplit = n;
   sp.kb_per = kb_per;
-  sp.ldp = ((int64_t)N + 3) / 4 * 4;
-  return (size_t)n * (size_t)M * (size_t)sp.ldp * sizeof(float);
+  sp.tile0 = (int)tile0;
+  sp.ntail = (int)ntail;
+  sp.per_xcd = (int)((ntail + kXcds - 1) / kXcds);
+  return (size_t)n * (size_t)ntail * BM * BN * sizeof(float);
 }
 
 template <int DQ, bool Q4, bool LORA>
@@ -607,11 +640,11 @@ void launch_one(const uint16_t* x, int64_t ldx, const uint8_t* packed, const voi
   const LevelTable& lv = level_table(quant_type);
   if constexpr (!LORA) {
     if (plan.nsplit > 1) {
-      const SplitArgs sa{plan.kb_per, part, plan.ldp};
+      const SplitArgs sa{plan.kb_per, plan.tile0, plan.per_xcd, plan.ntail, part};
+      const unsigned grid = (unsigned)(plan.tile0 + plan.nsplit * plan.per_xcd * kXcds);
       auto go = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, dim3((unsigned)(plan.nsplit * per_xcd * kXcds)),
-                           dim3(kThreads), 0, stream, x, ldx, packed, absmax, absmax2, mean, M,
-                           N, K, y, ldy, tm, tn, lv, la, sa);
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, stream, x, ldx, packed,
+                           absmax, absmax2, mean, M, N, K, y, ldy, tm, tn, lv, la, sa);
       };
       if (quant_type == kQuantFP4) {
         if (f16) go(gemm_kernel<DQ, Q4, true, true, false, true>);
@@ -620,18 +653,18 @@ void launch_one(const uint16_t* x, int64_t ldx, const uint8_t* packed, const voi
         if (f16) go(gemm_kernel<DQ, Q4, false, true, false, true>);
         else go(gemm_kernel<DQ, Q4, false, false, false, true>);
       }
-      const int64_t quads = (int64_t)M * (plan.ldp / 4);
+      const int64_t quads = (int64_t)plan.ntail * (BM * BN / 4);
       const unsigned rgrid = (unsigned)((quads + 255) / 256);
       if (f16)
         hipLaunchKernelGGL(split_reduce_kernel<true>, dim3(rgrid), dim3(256), 0, stream, part,
-                           plan.ldp, plan.nsplit, M, N, y, ldy);
+                           plan.nsplit, plan.ntail, plan.tile0, tn, M, N, y, ldy);
       else
         hipLaunchKernelGGL(split_reduce_kernel<false>, dim3(rgrid), dim3(256), 0, stream, part,
-                           plan.ldp, plan.nsplit, M, N, y, ldy);
+                           plan.nsplit, plan.ntail, plan.tile0, tn, M, N, y, ldy);
       return;
     }
   }
-  const SplitArgs none{0, nullptr, 0};
+  const SplitArgs none{0, 0, 0, 0, nullptr};
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3((unsigned)(per_xcd * kXcds)), dim3(kThreads), 0, stream, x,
                        ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, tm, tn, lv, la, none);
@@ -669,7 +702,7 @@ hipError_t launch_gemm_any(const uint16_t* x, int64_t ldx, const uint8_t* packed
   const size_t need = LORA ? 0 : split_plan(M, N, K, plan);
   if (need == 0 || M > slab || workspace == nullptr || workspace_bytes < need ||
       ((uintptr_t)workspace & 15) != 0)
-    plan = SplitPlan{1, 0, 0};
+    plan = SplitPlan{1, 0, 0, 0, 0};
   const int nkb = K / 64;
   // Four block codes per dword load: needs whole groups of four blocks per
   // row (then four blocks never straddle a group of 256) and an aligned

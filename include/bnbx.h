@@ -297,12 +297,14 @@ BNBX_API int bnbx_gemv_nf4_grouped(const uint16_t* x, int64_t ldx, const bnbx_ge
                                    int count, int M, int K, void* stream);
 
 /* Bytes of device workspace bnbx_gemm_nf4 can use for (M, N, K) on the
- * current device: when the 256 x 256 output tiles fill at most half of the
- * GPU's compute units and K has at least 32 blocks (2048 values), the GEMM
- * splits K over up to four workgroups per tile, which write fp32 partial
- * tiles here, and a second launch adds them in split order and rounds once
- * (e.g. M = 2048 with N = 4096: 128 tiles on 256 CUs).  Returns 0 when the
- * tiles already fill the GPU, and for invalid sizes. */
+ * current device.  With K of at least 32 blocks (2048 values): when the
+ * 256 x 256 output tiles fill at most half of the GPU's compute units, the
+ * GEMM splits K over up to four workgroups per tile (e.g. M = 2048 with
+ * N = 4096: 128 tiles on 256 CUs); when they fill more than one round but
+ * less than two, it runs the first round's tiles whole and splits the rest.
+ * The split workgroups write fp32 partial tiles here and a second launch
+ * adds them in split order and rounds once.  Returns 0 when no split is
+ * planned, and for invalid sizes. */
 BNBX_API size_t bnbx_gemm_nf4_workspace_bytes(int M, int N, int K);
 
 /* Prefill GEMM, Y[M, N] = X[M, K] . W_hat[N, K]^T for any M >= 1: weights

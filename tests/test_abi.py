@@ -74,9 +74,14 @@ def test_workspace_queries():
     assert bnbx.bnbx_quantize_nf4_workspace_bytes(n, 32, 1) == 0
     assert bnbx.bnbx_gemm_nf4_workspace_bytes(2048, 8192, 8192) == 0
     # split K for shapes whose 256 x 256 tiles fill at most half of the CUs
-    # (256 on MI355X, also the count assumed without a device): fp32 partials
-    assert bnbx.bnbx_gemm_nf4_workspace_bytes(2048, 4096, 4096) == 2 * 2048 * 4096 * 4
-    assert bnbx.bnbx_gemm_nf4_workspace_bytes(300, 500, 4096) == 4 * 300 * 500 * 4
+    # (256 on MI355X, also the count assumed without a device), and for the
+    # tail beyond one full round of tiles: fp32 partial tiles of 256 x 256
+    tile = 256 * 256 * 4
+    assert bnbx.bnbx_gemm_nf4_workspace_bytes(2048, 4096, 4096) == 2 * 128 * tile
+    assert bnbx.bnbx_gemm_nf4_workspace_bytes(300, 500, 4096) == 4 * 4 * tile
+    assert bnbx.bnbx_gemm_nf4_workspace_bytes(2048, 11008, 4096) == 2 * 88 * tile   # 344 tiles
+    assert bnbx.bnbx_gemm_nf4_workspace_bytes(2304, 8192, 4096) == 4 * 32 * tile    # 288 tiles
+    assert bnbx.bnbx_gemm_nf4_workspace_bytes(4096, 8192, 4096) == 0   # 512 tiles: two rounds
     assert bnbx.bnbx_gemm_nf4_workspace_bytes(2048, 4096, 1024) == 0   # K too short
     assert bnbx.bnbx_gemm_nf4_workspace_bytes(0, 4096, 4096) == 0
     assert bnbx.bnbx_gemm_nf4_workspace_bytes(2048, 4096, 100) == 0

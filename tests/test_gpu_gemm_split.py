@@ -1,8 +1,9 @@
 """GPU parity of the GEMM's split-K path (bnbx_gemm_nf4 with the workspace
 bnbx_gemm_nf4_workspace_bytes asks for: when the 256 x 256 output tiles fill
 at most half of the compute units, K is split over up to four workgroups
-per tile and their fp32 partial tiles are added in split order), through
-the C ABI:
+per tile; when they fill more than one round but less than two, the tiles
+past the first round are split; the fp32 partial tiles are added in split
+order), through the C ABI:
 
 * against the oracle's binary64 product (relative Frobenius <= 5e-3 per
   matrix, row and 32 x 32 tile) at the Llama-7B prefill shapes with N = 4096
@@ -39,12 +40,13 @@ def gemm_with(x, q, ws_bytes):
     return y
 
 
-def check(M, N, K, seed, qt="nf4", dt="bf16", dq=True, dq_map="linear", splits=None):
+def check(M, N, K, seed, qt="nf4", dt="bf16", dq=True, dq_map="linear", splits=None,
+          tail=None):
     need = bnbx.bnbx_gemm_nf4_workspace_bytes(M, N, K)
     assert need > 0, "shape does not split"
-    ldp = (N + 3) // 4 * 4
+    tiles = -(-M // 256) * -(-N // 256)
     if splits is not None:
-        assert need == splits * M * ldp * 4
+        assert need == splits * (tail if tail is not None else tiles) * 256 * 256 * 4
     w = synth.normal_bf16((N, K), 0.02, seed)
     xb = synth.normal_16((M, K), 1.0, seed + 1, dt)
     ref = oracle.quantize(w, dq, quant_type=qt, dq_map=dq_map)
@@ -93,3 +95,16 @@ def test_split_last_range_not_a_multiple_of_four():
 def test_split_one_row():
     """M = 1 through the GEMM: one row tile, every split."""
     check(1, 1000, 8192, 15040, splits=4)
+
+
+def test_split_tail_llama_gate_up_shape():
+    """gate/up at prefill: 2048 x 11008 x 4096, 344 tiles: 256 whole, the
+    88 past the first round split in two."""
+    check(2048, 11008, 4096, 15050, splits=2, tail=88)
+
+
+@pytest.mark.parametrize("qt,dt,dq_map", [("nf4", "bf16", "linear"), ("fp4", "f16", "dynamic")])
+def test_split_tail_ragged(qt, dt, dq_map):
+    """2500 x 7400 x 2048: 290 tiles (ragged last row and column of tiles),
+    34 tail tiles split in two."""
+    check(2500, 7400, 2048, 15060, qt=qt, dt=dt, dq_map=dq_map, splits=2, tail=34)
