@@ -18,7 +18,8 @@ TOL = 5e-3
 
 @pytest.mark.parametrize("qt,dt", [("nf4", "bf16"), ("fp4", "f16")])
 @pytest.mark.parametrize("M,N,K,r", [(7, 200, 512, 16), (300, 260, 1024, 64), (513, 384, 256, 32),
-                                     (2048, 1024, 2048, 16)])
+                                     (2048, 1024, 2048, 16), (260, 300, 512, 48),
+                                     (130, 520, 1024, 256), (64, 256, 512, 240)])
 def test_lora_shapes(M, N, K, r, qt, dt):
     w = synth.normal_bf16((N, K), 0.02, 9800 + r)
     x = synth.normal_16((M, K), 1.0, 9801 + M, dt)
