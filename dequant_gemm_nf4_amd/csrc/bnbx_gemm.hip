@@ -116,24 +116,27 @@ __device__ __forceinline__ Tab16 make_tab16(const LevelTable& lv, float sc) {
 // 2j+1) -> 4 dwords of bf16 pairs in weight order.  Four 4-bit codes held one
 // per byte select their entries with v_perm_b32 from each half of the table
 // (entries 0-7 and 8-15); a per-byte mask made from bit 3 of the codes
-// (v_perm's sign-replicating selectors 8-11) picks between the halves.
+// (v_perm's sign-replicating selectors 8-11) picks between the halves.  The
+// codes are grouped as weights (0, 1, 4, 5) and (2, 3, 6, 7), so each output
+// dword is one v_perm of a high-byte and a low-byte pick (26 vector
+// instructions per 8 weights; grouping even and odd weights took 28).
 __device__ __forceinline__ void decode8(uint32_t d, const Tab16& t, uint32_t* o) {
   auto pick = [&](uint32_t sel, uint32_t m, const uint32_t* tt) {
     const uint32_t a = perm(tt[1], tt[0], sel), b = perm(tt[3], tt[2], sel);
     return (m & b) | (~m & a);
   };
-  const uint32_t sE = (d >> 4) & 0x07070707u, sO = d & 0x07070707u;
-  const uint32_t mE = perm(d << 8, d, 0x090B080Au);     // bit 7 of each byte
-  const uint32_t d4 = d << 4;
-  const uint32_t mO = perm(d4 << 8, d4, 0x090B080Au);   // bit 3 of each byte
-  const uint32_t hiE = pick(sE, mE, t.h), loE = pick(sE, mE, t.l);
-  const uint32_t hiO = pick(sO, mO, t.h), loO = pick(sO, mO, t.l);
-  const uint32_t t0 = perm(hiE, loE, 0x05010400u), t1 = perm(hiE, loE, 0x07030602u);
-  const uint32_t u0 = perm(hiO, loO, 0x05010400u), u1 = perm(hiO, loO, 0x07030602u);
-  o[0] = perm(u0, t0, 0x05040100u);
-  o[1] = perm(u0, t0, 0x07060302u);
-  o[2] = perm(u1, t1, 0x05040100u);
-  o[3] = perm(u1, t1, 0x07060302u);
+  // selectors in weight order: (0, 1, 4, 5) and (2, 3, 6, 7)
+  const uint32_t lo3 = d & 0x07070707u, hi3 = (d >> 4) & 0x07070707u;
+  const uint32_t sA = perm(hi3, lo3, 0x02060004u), sB = perm(hi3, lo3, 0x03070105u);
+  // bit 3 of each selected code: d bits 7, 3, 23, 19 and 15, 11, 31, 27
+  const uint32_t mA = perm(d << 12, d << 8, 0x0B090A08u);
+  const uint32_t mB = perm(d << 4, d, 0x0B090A08u);
+  const uint32_t hiA = pick(sA, mA, t.h), loA = pick(sA, mA, t.l);
+  const uint32_t hiB = pick(sB, mB, t.h), loB = pick(sB, mB, t.l);
+  o[0] = perm(hiA, loA, 0x05010400u);
+  o[1] = perm(hiB, loB, 0x05010400u);
+  o[2] = perm(hiA, loA, 0x07030602u);
+  o[3] = perm(hiB, loB, 0x07030602u);
 }
 
 // One K step of a lane's weights: 16 packed bytes (32 weights) of each of
