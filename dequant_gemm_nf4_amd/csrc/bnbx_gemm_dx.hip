@@ -198,9 +198,11 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(
 
   // Piece p (0..3) of the dequant into a B tile: packed byte p of the unit's
   // four rows (columns 8 kg + 2 p and 8 kg + 2 p + 1).
-  auto put_piece = [&](const WUnit& u, int sbuf, int p, uint16_t* buf) {
+  // The four block scales of the thread's unit (the same for all four
+  // pieces of a step: its 8 columns lie in one block), read once per step.
+  auto scales4 = [&](int sbuf) { return *(const float4*)&scl[sbuf][kg >> 3][4 * rg]; };
+  auto put_piece = [&](const WUnit& u, const float4 sc4, int p, uint16_t* buf) {
     char* base = (char*)buf;
-    const float4 sc4 = *(const float4*)&scl[sbuf][kg >> 3][4 * rg];
     float2 lp[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) lp[i] = tab[((u.d[i] >> (8 * p)) & 0xffu) * kCopies];
@@ -258,8 +260,11 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(
   put_scale(r0, 0);
   put_scale(r1, 1);
   __syncthreads();   // byte table and first scales complete
+  {
+    const float4 sc4 = scales4(0);
 #pragma unroll
-  for (int p = 0; p < 4; ++p) put_piece(wa, 0, p, Bs0);
+    for (int p = 0; p < 4; ++p) put_piece(wa, sc4, p, Bs0);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -271,6 +276,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(
     copy_dy(Anext, clampstep(t + 1));
     const char* a = (const char*)A;
     const char* bq = (const char*)B;
+    const float4 sc4 = scales4(sb);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       u32x4_t av[4], bv[2];
@@ -282,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16<F16>(av[i], bv[j], acc[i][j]);
-      put_piece(wput, sb, s, Bnext);
+      put_piece(wput, sc4, s, Bnext);
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_waitcnt(0);
