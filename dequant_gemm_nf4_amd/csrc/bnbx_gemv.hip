@@ -44,7 +44,7 @@ hipError_t launch_gemv(const uint16_t* x, int64_t ldx, const uint8_t* packed, co
     if (mv == 0) return hipErrorNotSupported;
     for (int64_t r0 = 0; r0 < N; r0 += slab) {
       const int n = (int)(N - r0 < slab ? N - r0 : slab);
-      if (!make_plan(p.mm, n, K, p, nicap)) return hipErrorNotSupported;
+      if (!make_plan(p.mm, n, K, p, nicap, true)) return hipErrorNotSupported;
       GemvOne it;
       it.packed = packed + r0 * rowK2;
       it.absmax = double_quant ? (const void*)((const int8_t*)absmax + r0 * nkb)

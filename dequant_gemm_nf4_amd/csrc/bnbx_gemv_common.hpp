@@ -56,10 +56,14 @@ namespace {
 
 constexpr int kWaves = 16;                  // waves per workgroup (one workgroup per CU)
 constexpr int kThreads = kWaves * 64;
+// The single-weight M = 1 kernel may instead run 8-wave workgroups, two per
+// CU (their X stage is then 8 KB, so that both fit the LDS).
+constexpr int kWavesHalf = 8;
 constexpr int kCopies = 32;                 // lane columns of the byte table (128 B)
 constexpr int kTabBytes = 256 * 256;        // 256 B per byte value
 // X staged in LDS when MM*K*2 fits (the table takes 64 KB of the CU's 160 KB).
 constexpr int kXBytes = 64 * 1024;
+constexpr int x_stage_bytes(int wv) { return wv == kWaves ? kXBytes : 8 * 1024; }
 constexpr int kMaxMM = 4;
 constexpr int kMaxRR = 4;
 // Rows per team in a grouped launch: more spill registers (the item lookups
@@ -160,12 +164,15 @@ using GemvArgs = typename std::conditional<GRP, GemvItems, GemvOne>::type;
 // MM rows of X per launch (rows >= mvalid are zero), NI chunks per lane, RR
 // rows of W per team and pass.  TW = 1 << twl waves per team.  N rows in
 // all (of every item).
-template <int MM, int NI, int RR, int SM, bool F16, bool GRP>
-__global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
+template <int MM, int NI, int RR, int SM, bool F16, bool GRP, int WV>
+__global__ __launch_bounds__(WV * 64, 4) void gemv_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, GemvArgs<GRP> items, int nitems, int mvalid,
     int N, int K, int twl, int xlds, LevelTable lv) {
   constexpr bool DQ = SM != kScaleF32;
   constexpr bool DYN = scale_dyn(SM);
+  constexpr int kWaves = WV;                 // this instantiation's workgroup
+  constexpr int kThreads = WV * 64;
+  constexpr int kXBytes = x_stage_bytes(WV);
   // One LDS block with the table at offset 0, so that a table address is the
   // v_perm result itself (the ds_read offset field cannot hold a 64 KB base),
   // then X, then the team sums, then the dynamic map (DYN).  X is stored in 64-byte chunks whose four
@@ -533,6 +540,7 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(
 // ---------------------------------------------------------------------------
 struct Plan {
   int mm, ni, rr, twl, grid, xlds;
+  int wv;   // waves per workgroup: kWaves, or kWavesHalf (two workgroups per CU)
 };
 
 int cu_count() {
@@ -563,8 +571,9 @@ int rr_max(int mm, int ni) {
   return r;
 }
 
-// nicap: at most this many chunks per lane (see launch_k).
-bool make_plan(int mm, int N, int K, Plan& p, int nicap = 4) {
+// nicap: at most this many chunks per lane (see launch_k).  half: the
+// 8-wave workgroups may be chosen (a single weight at M = 1).
+bool make_plan(int mm, int N, int K, Plan& p, int nicap = 4, bool half = false) {
   const int C = K >> 5;
   const int nimax = (4 / mm) < nicap ? (4 / mm) : nicap;
   int best_twl = -1, best_ni = 0;
@@ -596,6 +605,22 @@ bool make_plan(int mm, int N, int K, Plan& p, int nicap = 4) {
   p.twl = best_twl;
   p.grid = (int)grid;
   p.xlds = (int64_t)mm * K * 2 <= kXBytes ? 1 : 0;
+  p.wv = kWaves;
+  // Rows chained three or more deep per wave: two 8-wave workgroups per CU,
+  // each with its own table and barrier, when X still fits their 8 KB stage
+  // (measured at M = 1 on 11008 x 4096: 6.46 against 6.86 us; with one row
+  // per wave, 4096 x 4096, or X not staged, 4096 x 11008, they were slower).
+  if (half && mm == 1 && best_ni <= 2 && rr >= 3 && (int64_t)K * 2 <= x_stage_bytes(kWavesHalf)) {
+    const int tpw8 = kWavesHalf >> best_twl;
+    const int64_t slots8 = (int64_t)cus * 2 * tpw8;
+    int64_t rr8 = ((int64_t)N + slots8 - 1) / slots8;
+    if (rr8 < 1) rr8 = 1;
+    if (tpw8 >= 1 && rr8 <= rmax && rr8 == rr) {
+      p.wv = kWavesHalf;
+      p.grid = (int)(((int64_t)N + tpw8 * rr8 - 1) / (tpw8 * rr8));
+      p.xlds = 1;
+    }
+  }
   return true;
 }
 
@@ -611,10 +636,19 @@ hipError_t launch_k(const Plan& p, const uint16_t* x, int64_t ldx, const GemvArg
     sm = rowq ? kScaleDynRow : kScaleDynLane;
   else if (dq)
     sm = rowq ? kScaleDqRow : kScaleDqLane;
-#define BNBX_GEMV_SM(SMV)                                                                       \
-  if (sm == SMV)                                                                                \
-    hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, SMV, F16, GRP>), dim3(p.grid), dim3(kThreads), \
-                       0, stream, x, ldx, it, nitems, mvalid, N, K, p.twl, p.xlds, lv);
+  // The 8-wave form is instantiated for the plans that can choose it.
+  constexpr bool kHalfOk = MM == 1 && !GRP && NI <= 2;
+#define BNBX_GEMV_SM(SMV)                                                                      \
+  if (sm == SMV) {                                                                             \
+    if (kHalfOk && p.wv == kWavesHalf)                                                         \
+      hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, SMV, F16, GRP, kHalfOk ? kWavesHalf : kWaves>), \
+                         dim3(p.grid), dim3(kWavesHalf * 64), 0, stream, x, ldx, it, nitems,   \
+                         mvalid, N, K, p.twl, p.xlds, lv);                                     \
+    else                                                                                       \
+      hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, SMV, F16, GRP, kWaves>), dim3(p.grid),       \
+                         dim3(kThreads), 0, stream, x, ldx, it, nitems, mvalid, N, K, p.twl,   \
+                         p.xlds, lv);                                                          \
+  }
   // Four chunks per lane with per-lane scales spill registers for the
   // dynamic map, and for both maps with GRP: those plans are capped at three
   // chunks (nicap) and the variants not built.
