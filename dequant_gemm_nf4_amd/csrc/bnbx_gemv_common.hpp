@@ -572,7 +572,7 @@ int rr_max(int mm, int ni) {
 }
 
 // nicap: at most this many chunks per lane (see launch_k).  half: the
-// 8-wave workgroups may be chosen (a single weight at M = 1).
+// 8-wave workgroups may be chosen (M = 1).
 bool make_plan(int mm, int N, int K, Plan& p, int nicap = 4, bool half = false) {
   const int C = K >> 5;
   const int nimax = (4 / mm) < nicap ? (4 / mm) : nicap;
@@ -637,7 +637,7 @@ hipError_t launch_k(const Plan& p, const uint16_t* x, int64_t ldx, const GemvArg
   else if (dq)
     sm = rowq ? kScaleDqRow : kScaleDqLane;
   // The 8-wave form is instantiated for the plans that can choose it.
-  constexpr bool kHalfOk = MM == 1 && !GRP && NI <= 2;
+  constexpr bool kHalfOk = MM == 1 && NI <= 2;
 #define BNBX_GEMV_SM(SMV)                                                                      \
   if (sm == SMV) {                                                                             \
     if (kHalfOk && p.wv == kWavesHalf)                                                         \
@@ -699,10 +699,10 @@ hipError_t dispatch(const Plan& p, const uint16_t* x, int64_t ldx, const GemvArg
 // runs the four-row kernel with its last row empty; long rows take smaller
 // groups, the X slice must fit the registers): the next group's size and
 // its plan for N rows, or 0.
-int next_x_group(int left, int N, int K, int nicap, Plan& p) {
+int next_x_group(int left, int N, int K, int nicap, Plan& p, bool half = false) {
   for (int mm : {4, 2, 1}) {
     if (left < (mm == 4 ? 3 : mm)) continue;
-    if (make_plan(mm, N, K, p, nicap)) return left < mm ? left : mm;
+    if (make_plan(mm, N, K, p, nicap, half)) return left < mm ? left : mm;
   }
   return 0;
 }

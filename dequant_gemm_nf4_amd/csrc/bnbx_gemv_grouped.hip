@@ -30,7 +30,7 @@ hipError_t launch_group(const uint16_t* x, int64_t ldx, const GemvItem* items, i
   }
   for (int m0 = 0; m0 < M;) {
     Plan p;
-    const int mv = next_x_group(M - m0, rows, K, nicap, p);
+    const int mv = next_x_group(M - m0, rows, K, nicap, p, true);
     if (mv == 0) return hipErrorNotSupported;
     GemvItems im = it;
     for (int w = 0; w < count; ++w) im.y[w] = it.y[w] + (int64_t)m0 * it.ldy[w];
@@ -74,8 +74,9 @@ hipError_t launch_gemv_grouped(const uint16_t* x, int64_t ldx, const GemvItem* i
   // the single-weight kernel.
   auto fits = [&](int64_t rows) {
     Plan p;
-    if (rows >= ((int64_t)1 << 31) || next_x_group(M, (int)rows, K, nicap, p) == 0) return false;
-    return p.rr <= kMaxGroupRR && rows <= (int64_t)p.grid * (kWaves >> p.twl) * p.rr;
+    if (rows >= ((int64_t)1 << 31) || next_x_group(M, (int)rows, K, nicap, p, true) == 0)
+      return false;
+    return p.rr <= kMaxGroupRR && rows <= (int64_t)p.grid * (p.wv >> p.twl) * p.rr;
   };
   for (int w0 = 0; w0 < count;) {
     int w1 = w0 + 1;
