@@ -72,16 +72,52 @@ __global__ __launch_bounds__(WAVES * 64) void lora_down_kernel(
   for (int c = 0; c < RT; ++c) acc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   const int k0 = wave * kq;
   const int k1 = k0 + kq < K ? k0 + kq : K;
-#pragma unroll 4
-  for (int k = k0; k < k1; k += 32) {
-    const uint32_t kb = (uint32_t)k * 2u;
-    const u32x4_t xl = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, kb, 0);
-    u32x4_t al[RT];
+  // Groups of U steps; the next group's loads go out before the current
+  // group is multiplied (two register sets; with 8 or more column tiles one
+  // step's loads are many already, and a second set would spill).  Steps
+  // past the wave's part of K load from an offset outside both buffers and
+  // read zero.
+  constexpr int U = RT == 1 ? 4 : RT == 2 ? 2 : 1;
+  constexpr bool kRoll = RT <= 4;
+  struct Grp {
+    u32x4_t x[U];
+    u32x4_t a[U][RT];
+  };
+  auto load_grp = [&](Grp& gr, int k) {
 #pragma unroll
-    for (int c = 0; c < RT; ++c) al[c] = __builtin_amdgcn_raw_buffer_load_b128(ra, ao[c], kb, 0);
-    const u32x4_t xv = relayout(xl);
+    for (int u = 0; u < U; ++u) {
+      const bool in = k + 32 * u < k1;
+      const uint32_t kb = (uint32_t)(k + 32 * u) * 2u;
+      gr.x[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, in ? xo : kFar, kb, 0);
 #pragma unroll
-    for (int c = 0; c < RT; ++c) acc[c] = mfma_16x16x32<F16>(xv, relayout(al[c]), acc[c]);
+      for (int c = 0; c < RT; ++c)
+        gr.a[u][c] = __builtin_amdgcn_raw_buffer_load_b128(ra, in ? ao[c] : kFar, kb, 0);
+    }
+  };
+  auto mul_grp = [&](const Grp& gr) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const u32x4_t xv = relayout(gr.x[u]);
+#pragma unroll
+      for (int c = 0; c < RT; ++c) acc[c] = mfma_16x16x32<F16>(xv, relayout(gr.a[u][c]), acc[c]);
+    }
+  };
+  if constexpr (kRoll) {
+    Grp g0, g1;
+    load_grp(g0, k0);
+    for (int k = k0; k < k1; k += 64 * U) {
+      if (k + 32 * U < k1) load_grp(g1, k + 32 * U);
+      mul_grp(g0);
+      if (k + 32 * U >= k1) break;
+      if (k + 64 * U < k1) load_grp(g0, k + 64 * U);
+      mul_grp(g1);
+    }
+  } else {
+    for (int k = k0; k < k1; k += 32) {
+      Grp g0;
+      load_grp(g0, k);
+      mul_grp(g0);
+    }
   }
 
 #pragma unroll
