@@ -58,7 +58,8 @@ def test_lora_zero_adapter_equals_plain_gemm():
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 @pytest.mark.parametrize("M,K,r", [(1, 64, 16), (7, 1024, 48), (16, 4096, 64), (300, 512, 256),
-                                   (2048, 8192, 16), (33, 8192, 128)])
+                                   (2048, 8192, 16), (33, 8192, 128), (4100, 256, 32),
+                                   (4099, 96, 256)])
 def test_lora_down_against_oracle(M, K, r, dt):
     x = synth.normal_16((M, K), 1.0, 9900 + M, dt)
     a = synth.normal_16((r, K), 0.02, 9901 + r, dt)

@@ -105,6 +105,21 @@ def test_gemv_more_than_four_rows(M, N, K, dq):
     assert err <= TOL, err
 
 
+@pytest.mark.parametrize("N,K,dq", [(12289, 4096, True), (9000, 2048, False), (16000, 1024, True),
+                                    (8193, 4096, True)])
+def test_gemv_m1_two_workgroups_per_cu(N, K, dq):
+    """M=1 shapes whose rows chain three or more deep per wave and whose X
+    fits an 8 KB stage run 8-wave workgroups, two per CU: a ragged last
+    workgroup (rows not a multiple of 24 or 32), one and two chunks per lane,
+    per-row and fp32 block scales; 8193 rows is the smallest count at K=4096
+    that chains three rows per wave (its last workgroup holds one row)."""
+    w = synth.normal_bf16((N, K), 0.02, 8300 + N % 97 + K)
+    x = synth.normal_bf16((1, K), 1.0, 8400 + K)
+    ref, q = setup(w, (N, K), dq, check_state=False)
+    err = product_error(run("gemv", x, 1, K, q), ref_product(x, ref, N, K))
+    assert err <= TOL, err
+
+
 @pytest.mark.parametrize("N,K", [(4096, 11008), (11008, 4096)])
 def test_gemv_m16_llama_shapes(N, K):
     """M=16 on the Llama-7B down projection (K = 11008, three chunks of
