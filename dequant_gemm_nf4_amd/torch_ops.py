@@ -1,6 +1,7 @@
-"""PyTorch custom op and module over the C ABI: the 4-bit linear layer as
+"""PyTorch custom ops and modules over the C ABI: the 4-bit linear layer as
 ``torch.ops.bnbx.linear4bit`` and a ``Linear4bit`` module that quantizes its
-weight on load.
+weight on load; the same layer with a LoRA adapter as
+``torch.ops.bnbx.linear4bit_lora`` and ``Linear4bitLoRA``.
 
 The pomoai.com overview (module list) has ``Linear4bit`` replacing
 ``torch.nn.Linear`` and the mlqm.cn article (section 4) loads a model in
@@ -112,6 +113,38 @@ def _backward(ctx, grad):
 linear4bit.register_autograd(_backward, setup_context=_setup_context)
 
 
+@torch.library.custom_op("bnbx::linear4bit_lora", mutates_args=())
+def linear4bit_lora(x: torch.Tensor, packed: torch.Tensor, absmax: torch.Tensor,
+                    absmax2: Optional[torch.Tensor], absmax_mean: Optional[torch.Tensor],
+                    lora_a: torch.Tensor, lora_b: torch.Tensor, scale: float,
+                    out_features: int, quant_type: str) -> torch.Tensor:
+    """Y[..., N] = X . W_hat^T + rnd(s . X . A^T) . B^T: the frozen 4-bit base
+    layer with a LoRA adapter (A [r, K], B [N, r], r a multiple of 16 up to
+    256), as the library's down-projection followed by the GEMM with the
+    low-rank term fused in (at any number of rows: there is no GEMV form of
+    the fused term).  Inference only: no autograd is registered, so a
+    backward through it raises."""
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"linear4bit_lora: x must be bfloat16 or float16, not {x.dtype}")
+    if lora_a.dtype != x.dtype or lora_b.dtype != x.dtype:
+        raise TypeError("linear4bit_lora: the adapter must have the dtype of x")
+    K = x.shape[-1]
+    x2 = x.reshape(-1, K)
+    if x2.stride(-1) != 1 or x2.stride(0) % 8 != 0 or x2.data_ptr() % 16 != 0:
+        x2 = x2.contiguous()
+    M = x2.shape[0]
+    y = torch.empty(M, out_features, dtype=x.dtype, device=x.device)
+    if M > 0:
+        q = _state(x, packed, absmax, absmax2, absmax_mean, out_features, quant_type)
+        T.linear_lora(x2, q, lora_a.contiguous(), lora_b.contiguous(), scale, out=y)
+    return y.reshape(*x.shape[:-1], out_features)
+
+
+@linear4bit_lora.register_fake
+def _(x, packed, absmax, absmax2, absmax_mean, lora_a, lora_b, scale, out_features, quant_type):
+    return x.new_empty(*x.shape[:-1], out_features)
+
+
 class Linear4bit(torch.nn.Module):
     """A bias-free ``nn.Linear(in_features, out_features)`` whose weight is
     held as 4-bit codes (NF4 or FP4, blocks of 64, optional double quant
@@ -180,3 +213,46 @@ class Linear4bit(torch.nn.Module):
                 f"quant_type={self.quant_type}, double_quant={self.double_quant}, "
                 f"dq_map={self.dq_map}, "
                 f"compute_dtype={self.compute_dtype}")
+
+
+class Linear4bitLoRA(Linear4bit):
+    """``Linear4bit`` with a LoRA adapter beside the frozen 4-bit weight (the
+    pomoai.com overview, QLoRA): Y = X . W_hat^T + s . (X . A^T) . B^T with
+    A [rank, in_features], B [out_features, rank] in ``compute_dtype`` and
+    s = ``scale``; forward runs ``torch.ops.bnbx.linear4bit_lora``.  The
+    adapter starts at zero (the layer then equals ``Linear4bit``) and is set
+    with ``load_adapter``; training it is not supported here."""
+
+    def __init__(self, in_features: int, out_features: int, rank: int = 16,
+                 scale: float = 1.0, **kw):
+        super().__init__(in_features, out_features, **kw)
+        if rank < 16 or rank > 256 or rank % 16 != 0:
+            raise ValueError("rank must be a multiple of 16 between 16 and 256")
+        self.rank, self.scale = rank, float(scale)
+        dev = self.packed.device
+        self.register_buffer("lora_a", torch.zeros(rank, in_features, dtype=self.compute_dtype,
+                                                   device=dev))
+        self.register_buffer("lora_b", torch.zeros(out_features, rank, dtype=self.compute_dtype,
+                                                   device=dev))
+
+    @torch.no_grad()
+    def load_adapter(self, a: torch.Tensor, b: torch.Tensor,
+                     scale: Optional[float] = None) -> "Linear4bitLoRA":
+        if tuple(a.shape) != tuple(self.lora_a.shape) or tuple(b.shape) != tuple(self.lora_b.shape):
+            raise ValueError(f"adapter shapes {tuple(a.shape)}, {tuple(b.shape)} != "
+                             f"{tuple(self.lora_a.shape)}, {tuple(self.lora_b.shape)}")
+        self.lora_a.copy_(a)
+        self.lora_b.copy_(b)
+        if scale is not None:
+            self.scale = float(scale)
+        return self
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        if x.dtype != self.compute_dtype:
+            raise TypeError(f"input dtype {x.dtype} != compute dtype {self.compute_dtype}")
+        return torch.ops.bnbx.linear4bit_lora(x, self.packed, self.absmax, self.absmax2,
+                                              self.absmax_mean, self.lora_a, self.lora_b,
+                                              self.scale, self.out_features, self.quant_type)
+
+    def extra_repr(self) -> str:
+        return super().extra_repr() + f", rank={self.rank}, scale={self.scale}"

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import synth
-from dequant_gemm_nf4_amd.torch_ops import Linear4bit
+from dequant_gemm_nf4_amd.torch_ops import Linear4bit, Linear4bitLoRA
 from tests.gpu_helpers import TORCH_DTYPE, dev_bf16, host_bits, product_error
 
 pytestmark = pytest.mark.gpu
@@ -147,3 +147,54 @@ def test_opcheck_with_grad():
     dy = dev_bf16(synth.normal_16((3, N), 1.0, 9962), (3, N))
     torch.library.opcheck(torch.ops.bnbx.linear4bit_dx.default,
                           (dy, m.packed, m.absmax, m.absmax2, m.absmax_mean, K, "nf4"))
+
+
+@pytest.mark.parametrize("qt,dt", [("nf4", "bf16"), ("fp4", "f16")])
+@pytest.mark.parametrize("lead", [(3,), (2, 160)])
+def test_lora_module_against_oracle(qt, dt, lead):
+    """Linear4bitLoRA: Y = X . W_hat^T + s . rnd(X . A^T) . B^T against the
+    oracle; with a zero adapter it equals the plain layer (bit for bit where
+    both run the GEMM)."""
+    N, K, r, s = 256, 512, 32, 0.5
+    w = synth.normal_bf16((N, K), 0.02, 9950)
+    m = Linear4bitLoRA(K, N, rank=r, scale=s, quant_type=qt, compute_dtype=TORCH_DTYPE[dt])
+    m.load_weight(dev_bf16(w, (N, K)))
+    M = int(np.prod(lead))
+    xb = synth.normal_16((M, K), 1.0, 9951, dt)
+    x = dev_bf16(xb, (*lead, K), dt)
+    plain = Linear4bit(K, N, quant_type=qt, compute_dtype=TORCH_DTYPE[dt])
+    plain.load_weight(dev_bf16(w, (N, K)))
+    y0, yp = m(x), plain(x)
+    if M > 16:   # both run the GEMM: a zero adapter adds exact zeros
+        assert torch.equal(y0.view(torch.int16), yp.view(torch.int16))
+    else:        # the plain layer runs the GEMV at up to 16 rows
+        assert product_error(y0.float().cpu().numpy().astype(np.float64).reshape(M, N),
+                             yp.float().cpu().numpy().astype(np.float64).reshape(M, N)) <= TOL
+    a = synth.normal_16((r, K), 0.02, 9952, dt)
+    b = synth.normal_16((N, r), 0.05, 9953, dt)
+    m.load_adapter(dev_bf16(a, (r, K), dt), dev_bf16(b, (N, r), dt))
+    y = m(x)
+    torch.cuda.synchronize()
+    assert y.shape == (*lead, N)
+    got = oracle.bits_to_f32(host_bits(y), dt).astype(np.float64).reshape(M, N)
+    ref = oracle.quantize(w, True, quant_type=qt)
+    xa = oracle.lora_down_ref(xb, a, s, M, K, dt)
+    b64 = oracle.bits_to_f32(b, dt).astype(np.float64).reshape(N, r)
+    base = oracle.dequant_matmul_ref(xb, ref["packed"], ref, N, K, dt)
+    want = base + xa @ b64.T
+    assert product_error(got, want) <= TOL
+    assert oracle.rel_frobenius(base, want) > 10 * TOL
+
+
+def test_lora_module_compiled_equals_eager():
+    N, K, r = 192, 256, 16
+    w = synth.normal_bf16((N, K), 0.02, 9960)
+    m = Linear4bitLoRA(K, N, rank=r, scale=2.0)
+    m.load_weight(dev_bf16(w, (N, K)))
+    m.load_adapter(dev_bf16(synth.normal_16((r, K), 0.02, 9961, "bf16"), (r, K)),
+                   dev_bf16(synth.normal_16((N, r), 0.05, 9962, "bf16"), (N, r)))
+    x = dev_bf16(synth.normal_16((40, K), 1.0, 9963, "bf16"), (40, K))
+    eager = m(x)
+    compiled = torch.compile(m, fullgraph=True, backend="aot_eager")(x)
+    torch.cuda.synchronize()
+    assert torch.equal(eager.view(torch.int16), compiled.view(torch.int16))

@@ -67,3 +67,32 @@ def test_autograd_shapes_on_meta():
     y = m(x)
     (g,) = torch.autograd.grad(y, x, torch.empty_like(y))
     assert g.shape == x.shape and g.dtype == x.dtype
+
+
+def test_lora_op_and_module_on_meta():
+    from dequant_gemm_nf4_amd.torch_ops import Linear4bitLoRA
+    assert hasattr(torch.ops.bnbx, "linear4bit_lora")
+    schema = str(torch.ops.bnbx.linear4bit_lora.default._schema)
+    assert "lora_a" in schema and "lora_b" in schema and "float scale" in schema
+    m = Linear4bitLoRA(128, 96, rank=32, scale=2.0, device="meta")
+    assert m.lora_a.shape == (32, 128) and m.lora_b.shape == (96, 32)
+    y = m(torch.empty(2, 3, 128, dtype=torch.bfloat16, device="meta"))
+    assert y.shape == (2, 3, 96) and y.dtype == torch.bfloat16
+    assert "rank=32" in repr(m)
+
+
+def test_lora_module_checks_and_no_backward():
+    from dequant_gemm_nf4_amd.torch_ops import Linear4bitLoRA
+    for r in (0, 8, 24, 272):
+        with pytest.raises(ValueError):
+            Linear4bitLoRA(128, 64, rank=r, device="meta")
+    m = Linear4bitLoRA(128, 64, rank=16, device="meta")
+    with pytest.raises(ValueError):
+        m.load_adapter(torch.empty(16, 64, dtype=torch.bfloat16, device="meta"),
+                       torch.empty(64, 16, dtype=torch.bfloat16, device="meta"))
+    with pytest.raises(TypeError):
+        m(torch.empty(1, 128, dtype=torch.float16, device="meta"))
+    # inference only: a backward through the adapter layer fails loudly
+    x = torch.empty(3, 128, dtype=torch.bfloat16, device="meta", requires_grad=True)
+    with pytest.raises(RuntimeError, match="autograd"):
+        m(x).sum().backward()
