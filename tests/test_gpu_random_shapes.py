@@ -88,3 +88,53 @@ def test_random_size_quantize_dequantize_bit_exact(i, size, sigma, qt, dq, dt):
     q = upload_state(ref, (size,), dt)
     out = host_bits(T.dequantize(q))
     assert np.array_equal(out, oracle.dequantize(ref["packed"], ref, dtype=dt))
+
+
+def tall_cases(n=8, seed=20261204):
+    """M=1 with more than 8192 rows and K <= 4096: rows chained three or four
+    deep per wave (two 8-wave workgroups per CU) or, past 16384 rows, more
+    than one pass of 16-wave workgroups."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        qt = ["nf4", "fp4"][i % 2]
+        dt = ["bf16", "f16"][rng.integers(2)]
+        dq = ["none", "linear", "dynamic"][rng.integers(3)]
+        N = int(rng.integers(8193, 20001))
+        K = 64 * int(rng.integers(1, 1 + min(64, 40_000_000 // (64 * N))))
+        out.append((i, qt, dt, dq, N, K))
+    return out
+
+
+@pytest.mark.parametrize("i,qt,dt,dq,N,K", tall_cases())
+def test_random_tall_gemv_m1(i, qt, dt, dq, N, K):
+    w = synth.normal_bf16((N, K), 0.03, 12500 + i)
+    ref = oracle.quantize(w, dq != "none", quant_type=qt,
+                          dq_map="dynamic" if dq == "dynamic" else "linear")
+    q = upload_state(ref, (N, K), dt)
+    x = synth.normal_16((1, K), 1.0, 12600 + i, dt)
+    got = T.gemv(dev_bf16(x, (1, K), dt), q)
+    torch.cuda.synchronize()
+    want = oracle.dequant_matmul_ref(x, ref["packed"], ref, N, K, dt)
+    g = oracle.bits_to_f32(host_bits(got), dt).astype(np.float64).reshape(1, N)
+    err = product_error(g, want)
+    assert err <= TOL, (i, qt, dt, dq, N, K, err)
+
+
+def down_cases(n=8, seed=20261205):
+    """The LoRA down-projection at random M (both row counts per workgroup),
+    K and rank."""
+    rng = np.random.default_rng(seed)
+    return [(i, ["bf16", "f16"][rng.integers(2)], int(rng.integers(1, 5001)),
+             32 * int(rng.integers(1, 97)), 16 * int(rng.integers(1, 17))) for i in range(n)]
+
+
+@pytest.mark.parametrize("i,dt,M,K,r", down_cases())
+def test_random_lora_down(i, dt, M, K, r):
+    x = synth.normal_16((M, K), 1.0, 12700 + i, dt)
+    a = synth.normal_16((r, K), 0.02, 12800 + i, dt)
+    got = T.lora_down(dev_bf16(x, (M, K), dt), dev_bf16(a, (r, K), dt), 0.25)
+    torch.cuda.synchronize()
+    g = oracle.bits_to_f32(host_bits(got), dt).astype(np.float64).reshape(M, r)
+    err = product_error(g, oracle.lora_down_ref(x, a, 0.25, M, K, dt))
+    assert err <= TOL, (i, dt, M, K, r, err)
