@@ -158,15 +158,39 @@ __device__ __forceinline__ T pick_item(const T (&a)[kMaxItems], int w) {
   return w == 0 ? a[0] : w == 1 ? a[1] : w == 2 ? a[2] : a[3];
 }
 
-template <bool GRP>
-using GemvArgs = typename std::conditional<GRP, GemvItems, GemvOne>::type;
+// A single weight with a LoRA term (LORA): Y += XA . B^T with XA [M, r] and
+// the up-projection B [N, r] in the compute type, r a multiple of 16 up to
+// 256.
+struct GemvOneLora : GemvOne {
+  const uint16_t* xa;
+  int64_t ldxa;
+  const uint16_t* lb;
+  int64_t ldb;
+  int r;
+};
+
+template <bool GRP, bool LORA = false>
+using GemvArgs = typename std::conditional<
+    GRP, GemvItems, typename std::conditional<LORA, GemvOneLora, GemvOne>::type>::type;
+
+// 16-bit value (bf16 or binary16) to binary32, exactly.
+template <bool F16>
+__device__ __forceinline__ float half_to_f32(uint32_t h) {
+  if constexpr (F16)
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+  else
+    return __uint_as_float(h << 16);
+}
+constexpr uint32_t kLoraFar = 0x80000000u;   // an offset past every buffer resource
+constexpr int kLoraPer = 4;                  // ranks per lane slot: r <= 256, 64 slots or more
+constexpr int kLoraMaxRR = 3;                // rows per team with a LoRA term (registers)
 
 // MM rows of X per launch (rows >= mvalid are zero), NI chunks per lane, RR
 // rows of W per team and pass.  TW = 1 << twl waves per team.  N rows in
 // all (of every item).
-template <int MM, int NI, int RR, int SM, bool F16, bool GRP, int WV>
+template <int MM, int NI, int RR, int SM, bool F16, bool GRP, int WV, bool LORA = false>
 __global__ __launch_bounds__(WV * 64, 4) void gemv_kernel(
-    const uint16_t* __restrict__ x, int64_t ldx, GemvArgs<GRP> items, int nitems, int mvalid,
+    const uint16_t* __restrict__ x, int64_t ldx, GemvArgs<GRP, LORA> items, int nitems, int mvalid,
     int N, int K, int twl, int xlds, LevelTable lv) {
   constexpr bool DQ = SM != kScaleF32;
   constexpr bool DYN = scale_dyn(SM);
@@ -255,6 +279,28 @@ __global__ __launch_bounds__(WV * 64, 4) void gemv_kernel(
   }
   const float dmv = DYN ? dyn_map_value(t) : 0.0f;
 
+  // LoRA term: lane slot s takes ranks s, s + S, ... of XA's rows (binary32)
+  // and of each row of B; unused ranks read zero from an offset past the
+  // buffers, so no load sits behind a branch.
+  constexpr int kLP = LORA ? kLoraPer : 1;
+  uint32_t lof[kLP];
+  float xav[MM][kLP];
+  if constexpr (LORA) {
+#pragma unroll
+    for (int i = 0; i < kLP; ++i) {
+      const int j = s + i * S;
+      lof[i] = j < items.r ? (uint32_t)j * 2u : kLoraFar;
+    }
+    const rsrc_t rxa =
+        make_rsrc(items.xa, (uint32_t)(((int64_t)(mvalid - 1) * items.ldxa + items.r) * 2));
+#pragma unroll
+    for (int m = 0; m < MM; ++m)
+#pragma unroll
+      for (int i = 0; i < kLP; ++i)
+        xav[m][i] = half_to_f32<F16>(__builtin_amdgcn_raw_buffer_load_b16(
+            rxa, lof[i] + (uint32_t)((int64_t)m * items.ldxa * 2), 0, 0));
+  }
+
   // 1. X: staging loads (LDS path) or the lane's slice directly.
   uint32_t xr[MM][NI][16];
   constexpr int kStage = kXBytes / 16 / kThreads;   // 16-byte pieces per thread (max)
@@ -304,6 +350,7 @@ __global__ __launch_bounds__(WV * 64, 4) void gemv_kernel(
   int qd[RR];
   float gsl[RR];      // the row's group scales: g0 in even lanes, g1 in odd ones
   uint32_t split[RR];
+  uint32_t lbv[RR][kLP];   // LoRA: the row's ranks of B (16-bit values)
   // Loads of the team's rows that start at row rb (rows at or past N get
   // empty resources).
   auto issue_part = [&](int64_t rb, int lo, int hi) {
@@ -322,6 +369,11 @@ __global__ __launch_bounds__(WV * 64, 4) void gemv_kernel(
       for (int i = 0; i < NI; ++i)
         if (j * NI + i >= lo && j * NI + i < hi) w[j][i] = buf_load16<2>(rw, woff[i]);   // nt
       if (j * NI < lo) continue;              // the row's scales went with its first chunk
+      if constexpr (LORA) {
+        const rsrc_t rbl = make_rsrc(items.lb + row * items.ldb, ok ? (uint32_t)items.r * 2u : 0u);
+#pragma unroll
+        for (int i = 0; i < kLP; ++i) lbv[j][i] = __builtin_amdgcn_raw_buffer_load_b16(rbl, lof[i], 0, 0);
+      }
       if (rowsc) {
         const rsrc_t rq = make_rsrc((const int8_t*)absmax + row * nkb, ok ? nkb : 0u);
         qd[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(rq, (uint32_t)lane * 4u, 0, 0);
@@ -483,6 +535,15 @@ __global__ __launch_bounds__(WV * 64, 4) void gemv_kernel(
         // Only one chunk's table addresses and pairs live at a time.
         __builtin_amdgcn_sched_barrier(0);
       }
+      if constexpr (LORA) {
+        // the lane's ranks of XA . B^T join the row's partial sums before
+        // the reduction, so that Y is rounded once
+#pragma unroll
+        for (int m = 0; m < MM; ++m)
+#pragma unroll
+          for (int i = 0; i < kLP; ++i)
+            acc[m][j] = __builtin_fmaf(xav[m][i], half_to_f32<F16>(lbv[j][i]), acc[m][j]);
+      }
       if (first && j + kRowWindow < RR)
         issue_part(rb, (j + kRowWindow) * NI, (j + kRowWindow + 1) * NI);
     }
@@ -624,12 +685,12 @@ bool make_plan(int mm, int N, int K, Plan& p, int nicap = 4, bool half = false) 
   return true;
 }
 
-template <int MM, int NI, int RR, bool F16, bool GRP>
-hipError_t launch_k(const Plan& p, const uint16_t* x, int64_t ldx, const GemvArgs<GRP>& it,
+template <int MM, int NI, int RR, bool F16, bool GRP, bool LORA = false>
+hipError_t launch_k(const Plan& p, const uint16_t* x, int64_t ldx, const GemvArgs<GRP, LORA>& it,
                     int nitems, int dq, bool rowq, int mvalid, int N, int K, const LevelTable& lv,
                     hipStream_t stream) {
-  if constexpr (GRP && RR > kMaxGroupRR) {
-    return hipErrorNotSupported;   // planned out (launch_gemv_grouped)
+  if constexpr ((GRP && RR > kMaxGroupRR) || (LORA && (GRP || RR > kLoraMaxRR))) {
+    return hipErrorNotSupported;   // planned out (launch_gemv_grouped, launch_gemv_lora)
   } else {
   int sm = kScaleF32;
   if (dq == kDqDynamic)
@@ -637,15 +698,15 @@ hipError_t launch_k(const Plan& p, const uint16_t* x, int64_t ldx, const GemvArg
   else if (dq)
     sm = rowq ? kScaleDqRow : kScaleDqLane;
   // The 8-wave form is instantiated for the plans that can choose it.
-  constexpr bool kHalfOk = MM == 1 && NI <= 2;
+  constexpr bool kHalfOk = MM == 1 && NI <= 2 && !LORA;
 #define BNBX_GEMV_SM(SMV)                                                                      \
   if (sm == SMV) {                                                                             \
     if (kHalfOk && p.wv == kWavesHalf)                                                         \
-      hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, SMV, F16, GRP, kHalfOk ? kWavesHalf : kWaves>), \
+      hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, SMV, F16, GRP, kHalfOk ? kWavesHalf : kWaves, LORA>), \
                          dim3(p.grid), dim3(kWavesHalf * 64), 0, stream, x, ldx, it, nitems,   \
                          mvalid, N, K, p.twl, p.xlds, lv);                                     \
     else                                                                                       \
-      hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, SMV, F16, GRP, kWaves>), dim3(p.grid),       \
+      hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, SMV, F16, GRP, kWaves, LORA>), dim3(p.grid), \
                          dim3(kThreads), 0, stream, x, ldx, it, nitems, mvalid, N, K, p.twl,   \
                          p.xlds, lv);                                                          \
   }
@@ -673,16 +734,16 @@ hipError_t launch_k(const Plan& p, const uint16_t* x, int64_t ldx, const GemvArg
 // Launch of the plan's (MM, NI, RR) instantiation over the items.  rowq:
 // the row-wise code reads apply (every item's codes 4-byte aligned, K/64 a
 // multiple of 4 and at most 256).
-template <bool GRP>
-hipError_t dispatch(const Plan& p, const uint16_t* x, int64_t ldx, const GemvArgs<GRP>& it,
+template <bool GRP, bool LORA = false>
+hipError_t dispatch(const Plan& p, const uint16_t* x, int64_t ldx, const GemvArgs<GRP, LORA>& it,
                     int nitems, int dq, bool rowq, int mvalid, int N, int K, const LevelTable& lv,
                     bool f16, hipStream_t stream) {
 #define BNBX_GEMV_CASE(MM, NI, RR)                                                              \
   if (p.mm == MM && p.ni == NI && p.rr == RR)                                                   \
-    return f16 ? launch_k<MM, NI, RR, true, GRP>(p, x, ldx, it, nitems, dq, rowq, mvalid, N, K, \
-                                                 lv, stream)                                    \
-               : launch_k<MM, NI, RR, false, GRP>(p, x, ldx, it, nitems, dq, rowq, mvalid, N,  \
-                                                  K, lv, stream);
+    return f16 ? launch_k<MM, NI, RR, true, GRP, LORA>(p, x, ldx, it, nitems, dq, rowq, mvalid, \
+                                                       N, K, lv, stream)                        \
+               : launch_k<MM, NI, RR, false, GRP, LORA>(p, x, ldx, it, nitems, dq, rowq, mvalid,\
+                                                        N, K, lv, stream);
   BNBX_GEMV_CASE(1, 1, 1) BNBX_GEMV_CASE(1, 1, 2) BNBX_GEMV_CASE(1, 1, 3) BNBX_GEMV_CASE(1, 1, 4)
   BNBX_GEMV_CASE(1, 2, 1) BNBX_GEMV_CASE(1, 2, 2) BNBX_GEMV_CASE(1, 2, 3) BNBX_GEMV_CASE(1, 2, 4)
   BNBX_GEMV_CASE(1, 2, 5) BNBX_GEMV_CASE(1, 2, 6)

@@ -164,6 +164,13 @@ hipError_t launch_gemm(const uint16_t* x, int64_t ldx, const uint8_t* packed, co
                        bool f16, int M, int N, int K, uint16_t* y, int64_t ldy, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
 // Y = X . W_hat^T + XA . B^T (XA [M, r], B [N, r], r % 16 == 0).
+// Y = X . W_hat^T + XA . B^T for 1 <= M <= 4 (the decode GEMV with the
+// low-rank term added before its reduction; bnbx_gemv_lora.hip).
+hipError_t launch_gemv_lora(const uint16_t* x, int64_t ldx, const uint8_t* packed,
+                            const void* absmax, const float* absmax2, const float* mean,
+                            int double_quant, int quant_type, bool f16, int M, int N, int K,
+                            const uint16_t* xa, int64_t ldxa, const uint16_t* lora_b, int64_t ldb,
+                            int r, uint16_t* y, int64_t ldy, hipStream_t stream);
 hipError_t launch_gemm_lora(const uint16_t* x, int64_t ldx, const uint8_t* packed,
                             const void* absmax, const float* absmax2, const float* mean,
                             int double_quant, int quant_type, bool f16, int M, int N, int K,

@@ -121,9 +121,9 @@ def linear4bit_lora(x: torch.Tensor, packed: torch.Tensor, absmax: torch.Tensor,
     """Y[..., N] = X . W_hat^T + rnd(s . X . A^T) . B^T: the frozen 4-bit base
     layer with a LoRA adapter (A [r, K], B [N, r], r a multiple of 16 up to
     256), as the library's down-projection followed by the GEMM with the
-    low-rank term fused in (at any number of rows: there is no GEMV form of
-    the fused term).  Inference only: no autograd is registered, so a
-    backward through it raises."""
+    low-rank term fused in (the decode GEMV form for up to 4 rows).
+    Inference only: no autograd is registered, so a backward through it
+    raises."""
     if x.dtype not in _DTYPES:
         raise TypeError(f"linear4bit_lora: x must be bfloat16 or float16, not {x.dtype}")
     if lora_a.dtype != x.dtype or lora_b.dtype != x.dtype:

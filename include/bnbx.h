@@ -325,14 +325,16 @@ BNBX_API int bnbx_gemm_nf4(const uint16_t* x, int64_t ldx, const uint8_t* packed
                   uint16_t* y, int64_t ldy, void* workspace, size_t workspace_bytes,
                   void* stream);
 
-/* Prefill GEMM with a LoRA term fused in:
+/* 4-bit linear layer with a LoRA term fused in (any M):
  * Y = X . W_hat^T + XA . B^T, where XA [M, r] = s . X . A^T is the
  * adapter's down-projection already applied (and scaled) by the caller and
  * B [N, r] its up-projection (the nn.Linear(r, N) weight).  The pomoai.com
  * overview: QLoRA trains low-rank adapters beside the frozen 4-bit base
- * layer.  The adapter term runs as r / 16 more matrix-core products per
- * output tile, into the same fp32 accumulators as the 4-bit product (before
- * it), and Y is rounded once to the compute dtype.
+ * layer.  For M > 4 the adapter term runs as r / 16 more matrix-core
+ * products per output tile, into the same fp32 accumulators as the 4-bit
+ * product (before it); for M <= 4 the decode GEMV streams the weight once and
+ * adds each lane's ranks of XA . B^T to its partial sums before the
+ * reduction.  Either way Y is rounded once to the compute dtype.
  *   x, packed, st, M, N, K, y, ldy  as bnbx_gemm_nf4
  *   xa      device, 16-bit, row m at xa + m*ldxa; ldxa >= r, ldxa % 8 == 0,
  *           16-byte aligned

@@ -38,6 +38,48 @@ def test_lora_shapes(M, N, K, r, qt, dt):
     assert oracle.rel_frobenius(base, want) > 10 * TOL
 
 
+@pytest.mark.parametrize("qt,dt,dq_map", [("nf4", "bf16", "linear"), ("fp4", "f16", "linear"),
+                                          ("nf4", "bf16", "dynamic"), ("nf4", "f16", None)])
+@pytest.mark.parametrize("M,N,K,r", [(1, 4096, 4096, 16), (1, 11008, 4096, 64), (2, 300, 11008, 256),
+                                     (3, 777, 1024, 48), (4, 1000, 512, 240), (1, 20000, 256, 32)])
+def test_lora_decode_rows(M, N, K, r, qt, dt, dq_map):
+    """At most 4 rows of X: the decode GEMV adds the low-rank term before its
+    reduction (ragged N, K = 11008 over two waves per row, more rows than one
+    pass holds, every scale layout)."""
+    w = synth.normal_bf16((N, K), 0.02, 9840 + r)
+    x = synth.normal_16((M, K), 1.0, 9841 + M, dt)
+    xa = synth.normal_16((M, r), 0.5, 9842 + r, dt)
+    b = synth.normal_16((N, r), 0.05, 9843 + r, dt)
+    ref = oracle.quantize(w, dq_map is not None, quant_type=qt, dq_map=dq_map or "linear")
+    q = upload_state(ref, (N, K), dt)
+    print(f"lora decode M={M} N={N} K={K} r={r} {qt} {dt} {dq_map}", flush=True)
+    y = T.gemm_lora(dev_bf16(x, (M, K), dt), q, dev_bf16(xa, (M, r), dt), dev_bf16(b, (N, r), dt))
+    torch.cuda.synchronize()
+    got = oracle.bits_to_f32(host_bits(y), dt).astype(np.float64).reshape(M, N)
+    want = oracle.lora_matmul_ref(x, ref["packed"], ref, N, K, xa, b, dt)
+    err = product_error(got, want)
+    assert err <= TOL, err
+    base = oracle.dequant_matmul_ref(x, ref["packed"], ref, N, K, dt)
+    assert oracle.rel_frobenius(base, want) > 10 * TOL
+
+
+def test_lora_decode_zero_adapter_equals_plain_gemv():
+    """B = 0 at M <= 4: the result equals bnbx_gemv_nf4 bit for bit (the same
+    kernel, plus exact zeros)."""
+    N, K, r = 1500, 2048, 32
+    w = synth.normal_bf16((N, K), 0.02, 9850)
+    ref = oracle.quantize(w, True)
+    q = upload_state(ref, (N, K))
+    for M in (1, 2, 3, 4):
+        x = dev_bf16(synth.normal_16((M, K), 1.0, 9851 + M), (M, K))
+        xa = dev_bf16(synth.normal_16((M, r), 1.0, 9855 + M), (M, r))
+        zb = torch.zeros((N, r), dtype=torch.bfloat16, device="cuda")
+        y1 = T.gemv(x, q)
+        y2 = T.gemm_lora(x, q, xa, zb)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2), M
+
+
 def test_lora_zero_adapter_equals_plain_gemm():
     """B = 0: the fused result equals bnbx_gemm_nf4 bit for bit."""
     M, N, K, r = 300, 512, 1024, 16
