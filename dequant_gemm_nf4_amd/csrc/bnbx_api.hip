@@ -481,10 +481,10 @@ int bnbx_gemm_nf4_lora(const uint16_t* x, int64_t ldx, const uint8_t* packed,
   if (ldxa < r || ldb < r) return BNBX_E_INVAL;
   if (ldxa % 8 != 0 || ldb % 8 != 0) return BNBX_E_ALIGN;
   if (!aligned(xa, 16) || !aligned(lora_b, 16)) return BNBX_E_ALIGN;
-  // Up to 4 rows of X: the decode GEMV with the low-rank term; else the GEMM.
+  // Up to 16 rows of X: the decode GEMVs with the low-rank term; else the GEMM.
   const bool f16 = st->compute_dtype == BNBX_DTYPE_F16;
   const hipError_t e =
-      M <= 4 ? launch_gemv_lora(x, ldx, packed, st->absmax, st->absmax2, st->absmax_mean,
+      M <= 16 ? launch_gemv_lora(x, ldx, packed, st->absmax, st->absmax2, st->absmax_mean,
                                 st->double_quant, st->quant_type, f16, M, N, K, xa, ldxa, lora_b,
                                 ldb, r, y, ldy, (hipStream_t)stream)
              : launch_gemm_lora(x, ldx, packed, st->absmax, st->absmax2, st->absmax_mean,

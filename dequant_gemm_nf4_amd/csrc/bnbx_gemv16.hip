@@ -48,12 +48,23 @@ constexpr int k16SliceK = 256;    // k per wave slice (4 blocks)
 constexpr int k16ChunkK = k16Waves * k16SliceK;
 constexpr uint32_t kFar = 0x80000000u;   // an offset past every buffer resource
 
-template <int SM, bool F16, int NB, bool MULTI>
+// LoRA term (LORA): Y += XA . B^T with XA [M, r] and B [N, r] in the
+// compute type, r a multiple of 16 up to 256 (at most 8 chunks of 32 ranks).
+struct Gemv16Lora {
+  const uint16_t* xa;
+  int64_t ldxa;
+  const uint16_t* lb;
+  int64_t ldb;
+  int r;
+};
+struct NoLora {};
+
+template <int SM, bool F16, int NB, bool MULTI, bool LORA = false>
 __global__ __launch_bounds__(k16Waves * 64, 1) void gemv16_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ packed,
     const void* __restrict__ absmax, const float* __restrict__ absmax2,
     const float* __restrict__ mean, int M, int N, int K, uint16_t* __restrict__ y, int64_t ldy,
-    LevelTable lv) {
+    LevelTable lv, typename std::conditional<LORA, Gemv16Lora, NoLora>::type la) {
   constexpr bool DQ = SM != kScaleF32;
   constexpr bool DYN = scale_dyn(SM);
   constexpr int kSets = MULTI ? 2 : 1;
@@ -237,6 +248,24 @@ __global__ __launch_bounds__(k16Waves * 64, 1) void gemv16_kernel(
     load_x(wave, 1);
 #pragma unroll
     for (int jj = 1; jj < NB; ++jj) load_item(sets[0].it[jj], wave, j0 + jj);
+    // LoRA: wave w takes ranks [32 w, 32 w + 32) of XA . B^T for each row
+    // group of the batch, in the MFMA layout (lane (q, r): row r, ranks
+    // 32 w + 8 q .. +8); ranks past r, rows past M or N read zero.
+    u32x4_t lxa, lbo[LORA ? NB : 1];
+    if constexpr (LORA) {
+      const int k8 = 32 * wave + 8 * q;
+      const bool kin = k8 < la.r;
+      const rsrc_t rxa = make_rsrc(la.xa, (uint32_t)(((int64_t)(M - 1) * la.ldxa + la.r) * 2));
+      lxa = __builtin_amdgcn_raw_buffer_load_b128(
+          rxa, kin ? (uint32_t)(((int64_t)r * la.ldxa + k8) * 2) : kFar, 0, 0);
+      const rsrc_t rlb = make_rsrc(la.lb, (uint32_t)(((int64_t)(N - 1) * la.ldb + la.r) * 2));
+#pragma unroll
+      for (int jj = 0; jj < NB; ++jj) {
+        const int64_t n = 16 * ((int64_t)blockIdx.x + (int64_t)(j0 + jj) * gridDim.x) + r;
+        lbo[jj] = __builtin_amdgcn_raw_buffer_load_b128(
+            rlb, kin && j0 + jj < nrg ? (uint32_t)((n * la.ldb + k8) * 2) : kFar, 0, 0);
+      }
+    }
     if (MULTI) load_set(sets[kSets - 1], k16Waves + wave, j0);
     const float mu = DQ ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mul))) : 0.0f;
     f32x4_t acc[NB];
@@ -279,6 +308,10 @@ __global__ __launch_bounds__(k16Waves * 64, 1) void gemv16_kernel(
       }
     }
 
+    if constexpr (LORA) {
+#pragma unroll
+      for (int jj = 0; jj < NB; ++jj) acc[jj] = mfma_16x16x32<F16>(lxa, lbo[jj], acc[jj]);
+    }
     // the batch's partial sums meet in LDS, kRed row groups at a time;
     // Y[m][16 g + n] sits at lane 16 (m / 4) + n, value m % 4 of every
     // wave's fragment
@@ -310,54 +343,73 @@ __global__ __launch_bounds__(k16Waves * 64, 1) void gemv16_kernel(
 // code per lane.  NB, the
 // row groups a workgroup multiplies at once: up to 4 with one chunk of K,
 // 1 with several (two weight sets); larger counts spill registers.
-template <int SM, bool F16>
+template <int SM, bool F16, bool LORA = false>
 hipError_t launch_gemv16_sm(int grid, int nb, bool multi, const uint16_t* x, int64_t ldx,
                             const uint8_t* packed, const void* absmax, const float* absmax2,
                             const float* mean, int M, int N, int K, uint16_t* y, int64_t ldy,
-                            const LevelTable& lv, hipStream_t stream) {
+                            const LevelTable& lv, hipStream_t stream,
+                            typename std::conditional<LORA, Gemv16Lora, NoLora>::type la = {}) {
 #define BNBX_G16(NB, MULTI)                                                                    \
-  hipLaunchKernelGGL((gemv16_kernel<SM, F16, NB, MULTI>), dim3(grid), dim3(k16Waves * 64), 0, \
-                     stream, x, ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, lv)
+  hipLaunchKernelGGL((gemv16_kernel<SM, F16, NB, MULTI, LORA>), dim3(grid), dim3(k16Waves * 64), \
+                     0, stream, x, ldx, packed, absmax, absmax2, mean, M, N, K, y, ldy, lv, la)
   if (multi) {
     BNBX_G16(1, true);
   } else if (nb == 1) {
     BNBX_G16(1, false);
-  } else if (nb == 2) {
+  } else if (nb == 2 || LORA) {   // four row groups with the LoRA operands spill registers
     BNBX_G16(2, false);
   } else {
-    BNBX_G16(4, false);
+    if constexpr (!LORA) BNBX_G16(4, false);
   }
 #undef BNBX_G16
   return hipGetLastError();
 }
 
-template <bool F16>
+template <bool F16, bool LORA = false>
 hipError_t launch_gemv16(int grid, const uint16_t* x, int64_t ldx, const uint8_t* packed,
                          const void* absmax, const float* absmax2, const float* mean, int dq,
                          int M, int N, int K, uint16_t* y, int64_t ldy, const LevelTable& lv,
-                         hipStream_t stream) {
+                         hipStream_t stream,
+                         typename std::conditional<LORA, Gemv16Lora, NoLora>::type la = {}) {
   const bool multi = K > k16ChunkK;
   const int ngroups = (N + 15) / 16;
   const int per_wg = (ngroups + grid - 1) / grid;
   const int nb = multi ? 1 : (per_wg >= 3 ? 4 : per_wg);
   const bool rowq = dq && ((K >> 6) % 4 == 0) && ((uintptr_t)absmax & 3u) == 0;
   if (dq == kDqDynamic && rowq)
-    return launch_gemv16_sm<kScaleDynRow, F16>(grid, nb, multi, x, ldx, packed, absmax, absmax2,
-                                               mean, M, N, K, y, ldy, lv, stream);
+    return launch_gemv16_sm<kScaleDynRow, F16, LORA>(grid, nb, multi, x, ldx, packed, absmax,
+                                                     absmax2, mean, M, N, K, y, ldy, lv, stream,
+                                                     la);
   if (dq == kDqDynamic)
-    return launch_gemv16_sm<kScaleDynLane, F16>(grid, nb, multi, x, ldx, packed, absmax, absmax2,
-                                                mean, M, N, K, y, ldy, lv, stream);
+    return launch_gemv16_sm<kScaleDynLane, F16, LORA>(grid, nb, multi, x, ldx, packed, absmax,
+                                                      absmax2, mean, M, N, K, y, ldy, lv, stream,
+                                                      la);
   if (rowq)
-    return launch_gemv16_sm<kScaleDqRow, F16>(grid, nb, multi, x, ldx, packed, absmax, absmax2,
-                                              mean, M, N, K, y, ldy, lv, stream);
+    return launch_gemv16_sm<kScaleDqRow, F16, LORA>(grid, nb, multi, x, ldx, packed, absmax,
+                                                    absmax2, mean, M, N, K, y, ldy, lv, stream,
+                                                    la);
   if (dq)
-    return launch_gemv16_sm<kScaleDqLane, F16>(grid, nb, multi, x, ldx, packed, absmax, absmax2,
-                                               mean, M, N, K, y, ldy, lv, stream);
-  return launch_gemv16_sm<kScaleF32, F16>(grid, nb, multi, x, ldx, packed, absmax, absmax2, mean,
-                                          M, N, K, y, ldy, lv, stream);
+    return launch_gemv16_sm<kScaleDqLane, F16, LORA>(grid, nb, multi, x, ldx, packed, absmax,
+                                                     absmax2, mean, M, N, K, y, ldy, lv, stream,
+                                                     la);
+  return launch_gemv16_sm<kScaleF32, F16, LORA>(grid, nb, multi, x, ldx, packed, absmax, absmax2,
+                                                mean, M, N, K, y, ldy, lv, stream, la);
 }
 
 }  // namespace
+
+hipError_t launch_gemv16_lora_batch(int grid, const uint16_t* x, int64_t ldx,
+                                    const uint8_t* packed, const void* absmax,
+                                    const float* absmax2, const float* mean, int dq, bool f16,
+                                    int M, int N, int K, const uint16_t* xa, int64_t ldxa,
+                                    const uint16_t* lora_b, int64_t ldb, int r, uint16_t* y,
+                                    int64_t ldy, const LevelTable& lv, hipStream_t stream) {
+  const Gemv16Lora la{xa, ldxa, lora_b, ldb, r};
+  return f16 ? launch_gemv16<true, true>(grid, x, ldx, packed, absmax, absmax2, mean, dq, M, N,
+                                         K, y, ldy, lv, stream, la)
+             : launch_gemv16<false, true>(grid, x, ldx, packed, absmax, absmax2, mean, dq, M, N,
+                                          K, y, ldy, lv, stream, la);
+}
 
 hipError_t launch_gemv16_batch(int grid, const uint16_t* x, int64_t ldx, const uint8_t* packed,
                                const void* absmax, const float* absmax2, const float* mean,

@@ -154,6 +154,14 @@ hipError_t launch_gemv16_batch(int grid, const uint16_t* x, int64_t ldx, const u
                                const void* absmax, const float* absmax2, const float* mean,
                                int dq, bool f16, int M, int N, int K, uint16_t* y, int64_t ldy,
                                const LevelTable& lv, hipStream_t stream);
+// The same with a LoRA term, Y += XA . B^T (XA [M, r], B [N, r], r a multiple
+// of 16 up to 256).
+hipError_t launch_gemv16_lora_batch(int grid, const uint16_t* x, int64_t ldx,
+                                    const uint8_t* packed, const void* absmax,
+                                    const float* absmax2, const float* mean, int dq, bool f16,
+                                    int M, int N, int K, const uint16_t* xa, int64_t ldxa,
+                                    const uint16_t* lora_b, int64_t ldb, int r, uint16_t* y,
+                                    int64_t ldy, const LevelTable& lv, hipStream_t stream);
 // Workspace of the GEMM's split-K path for (M, N, K) on the current device
 // (fp32 partial tiles; 0 when the tiles already fill the GPU).
 size_t gemm_workspace_bytes(int M, int N, int K);
@@ -164,8 +172,8 @@ hipError_t launch_gemm(const uint16_t* x, int64_t ldx, const uint8_t* packed, co
                        bool f16, int M, int N, int K, uint16_t* y, int64_t ldy, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
 // Y = X . W_hat^T + XA . B^T (XA [M, r], B [N, r], r % 16 == 0).
-// Y = X . W_hat^T + XA . B^T for 1 <= M <= 4 (the decode GEMV with the
-// low-rank term added before its reduction; bnbx_gemv_lora.hip).
+// Y = X . W_hat^T + XA . B^T for 1 <= M <= 16 (the decode GEMVs with the
+// low-rank term added before their reductions; bnbx_gemv_lora.hip).
 hipError_t launch_gemv_lora(const uint16_t* x, int64_t ldx, const uint8_t* packed,
                             const void* absmax, const float* absmax2, const float* mean,
                             int double_quant, int quant_type, bool f16, int M, int N, int K,

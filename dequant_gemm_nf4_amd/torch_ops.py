@@ -121,7 +121,7 @@ def linear4bit_lora(x: torch.Tensor, packed: torch.Tensor, absmax: torch.Tensor,
     """Y[..., N] = X . W_hat^T + rnd(s . X . A^T) . B^T: the frozen 4-bit base
     layer with a LoRA adapter (A [r, K], B [N, r], r a multiple of 16 up to
     256), as the library's down-projection followed by the GEMM with the
-    low-rank term fused in (the decode GEMV form for up to 4 rows).
+    low-rank term fused in (the decode GEMV forms for up to 16 rows).
     Inference only: no autograd is registered, so a backward through it
     raises."""
     if x.dtype not in _DTYPES:

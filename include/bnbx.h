@@ -330,11 +330,13 @@ BNBX_API int bnbx_gemm_nf4(const uint16_t* x, int64_t ldx, const uint8_t* packed
  * adapter's down-projection already applied (and scaled) by the caller and
  * B [N, r] its up-projection (the nn.Linear(r, N) weight).  The pomoai.com
  * overview: QLoRA trains low-rank adapters beside the frozen 4-bit base
- * layer.  For M > 4 the adapter term runs as r / 16 more matrix-core
+ * layer.  For M > 16 the adapter term runs as r / 16 more matrix-core
  * products per output tile, into the same fp32 accumulators as the 4-bit
- * product (before it); for M <= 4 the decode GEMV streams the weight once and
- * adds each lane's ranks of XA . B^T to its partial sums before the
- * reduction.  Either way Y is rounded once to the compute dtype.
+ * product (before it); for M <= 16 the decode GEMVs stream the weight once
+ * and add the term to their partial sums before the reduction (M <= 4: each
+ * lane's ranks; 4 < M <= 16: one matrix-core product of 32 ranks per wave
+ * and group of 16 weight rows).  Either way Y is rounded once to the compute
+ * dtype.
  *   x, packed, st, M, N, K, y, ldy  as bnbx_gemm_nf4
  *   xa      device, 16-bit, row m at xa + m*ldxa; ldxa >= r, ldxa % 8 == 0,
  *           16-byte aligned

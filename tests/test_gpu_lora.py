@@ -41,11 +41,15 @@ def test_lora_shapes(M, N, K, r, qt, dt):
 @pytest.mark.parametrize("qt,dt,dq_map", [("nf4", "bf16", "linear"), ("fp4", "f16", "linear"),
                                           ("nf4", "bf16", "dynamic"), ("nf4", "f16", None)])
 @pytest.mark.parametrize("M,N,K,r", [(1, 4096, 4096, 16), (1, 11008, 4096, 64), (2, 300, 11008, 256),
-                                     (3, 777, 1024, 48), (4, 1000, 512, 240), (1, 20000, 256, 32)])
+                                     (3, 777, 1024, 48), (4, 1000, 512, 240), (1, 20000, 256, 32),
+                                     (5, 4100, 4096, 16), (8, 333, 11008, 80), (16, 14336, 4096, 64),
+                                     (13, 999, 512, 256), (16, 64, 64, 32)])
 def test_lora_decode_rows(M, N, K, r, qt, dt, dq_map):
-    """At most 4 rows of X: the decode GEMV adds the low-rank term before its
-    reduction (ragged N, K = 11008 over two waves per row, more rows than one
-    pass holds, every scale layout)."""
+    """Up to 16 rows of X: the decode GEMVs add the low-rank term before
+    their reductions (up to 4 rows: ragged N, K = 11008 over two waves per
+    row, more rows than one pass holds; 5 to 16 rows: one or several K chunks,
+    ragged row groups, ranks past one 32-rank chunk per wave; every scale
+    layout)."""
     w = synth.normal_bf16((N, K), 0.02, 9840 + r)
     x = synth.normal_16((M, K), 1.0, 9841 + M, dt)
     xa = synth.normal_16((M, r), 0.5, 9842 + r, dt)
@@ -64,13 +68,13 @@ def test_lora_decode_rows(M, N, K, r, qt, dt, dq_map):
 
 
 def test_lora_decode_zero_adapter_equals_plain_gemv():
-    """B = 0 at M <= 4: the result equals bnbx_gemv_nf4 bit for bit (the same
-    kernel, plus exact zeros)."""
+    """B = 0 at M <= 16: the result equals bnbx_gemv_nf4 bit for bit (the same
+    kernels, plus exact zeros)."""
     N, K, r = 1500, 2048, 32
     w = synth.normal_bf16((N, K), 0.02, 9850)
     ref = oracle.quantize(w, True)
     q = upload_state(ref, (N, K))
-    for M in (1, 2, 3, 4):
+    for M in (1, 2, 3, 4, 6, 16):
         x = dev_bf16(synth.normal_16((M, K), 1.0, 9851 + M), (M, K))
         xa = dev_bf16(synth.normal_16((M, r), 1.0, 9855 + M), (M, r))
         zb = torch.zeros((N, r), dtype=torch.bfloat16, device="cuda")
