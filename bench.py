@@ -590,26 +590,32 @@ def main():
         fns[f"r{r}_down"] = (lambda xa=xa, la=la: T.lora_down(xp, la, 2.0, out=xa))
         fns[f"r{r}_full"] = (lambda xa=xa, lb=lb, la=la: (T.lora_down(xp, la, 2.0, out=xa),
                                                           T.gemm_lora(xp, qp, xa, lb, out=yp)))
-    graphs = {}
-    for name, fn in fns.items():
-        fn()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap):
+    def interleaved_ms(fns):
+        # one graph per function, replayed in 5 interleaved rounds; the
+        # median round of each, in ms per replay
+        graphs = {}
+        for name, fn in fns.items():
             fn()
-        graphs[name] = g
-    rounds = {name: [] for name in graphs}
-    reps = max(2, args.steps)
-    for _ in range(5):
-        for name, g in graphs.items():
-            g.replay()
-            e0, e1 = ev(), ev()
-            e0.record(stream)
-            for _ in range(reps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                fn()
+            graphs[name] = g
+        rounds = {name: [] for name in graphs}
+        reps = max(2, args.steps)
+        for _ in range(5):
+            for name, g in graphs.items():
                 g.replay()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            rounds[name].append(e0.elapsed_time(e1) / reps)
-    med = {name: sorted(v)[len(v) // 2] for name, v in rounds.items()}
+                e0, e1 = ev(), ev()
+                e0.record(stream)
+                for _ in range(reps):
+                    g.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                rounds[name].append(e0.elapsed_time(e1) / reps)
+        del graphs
+        return {name: sorted(v)[len(v) // 2] for name, v in rounds.items()}
+
+    med = interleaved_ms(fns)
     plain_ms = med["plain"]
     lora = {"plain_ms": round(plain_ms, 4), "timing": "median of 5 interleaved rounds"}
     for r in (16, 64):
@@ -622,7 +628,35 @@ def main():
                                            (med[f"r{r}_down"] * 1e-3) / 1e9, 1),
                          "with_down_ms": round(med[f"r{r}_full"], 4),
                          "with_down_over_plain": round(med[f"r{r}_full"] / plain_ms, 4)}
-    del graphs, lora_in
+    del lora_in
+
+    # The LoRA term at decode sizes (its GEMV forms): M=1 over the stack's
+    # 4096x4096 weights and M=16 over the batched decode's 14336x4096
+    # weights, so each launch streams its weight from HBM; XA given, one
+    # adapter B per run; the plain GEMV over the same weights beside it.
+    dec_fns, dec_runs = {}, {}
+    for tag, (xd, qd, yd) in {"m1": (xs[0], [qs[i] for i in by_shape[0]], ys[0]),
+                              "m16": (xb, qb, yb)}.items():
+        Md, Nw, Kw = xd.shape[0], qd[0].shape[0], qd[0].shape[1]
+        dec_runs[tag] = (f"{Md}x{Nw}x{Kw}", len(qd))
+        dec_fns[f"{tag}_plain"] = (lambda xd=xd, qd=qd, yd=yd:
+                                   [T.gemv(xd, q, out=yd) for q in qd])
+        for r in (16, 64):
+            gen.manual_seed(7300 + r + Md)
+            xa = (torch.randn(Md, r, generator=gen, device=dev) * 0.5).to(torch.bfloat16)
+            lb = (torch.randn(Nw, r, generator=gen, device=dev) * 0.05).to(torch.bfloat16)
+            dec_fns[f"{tag}_r{r}"] = (lambda xd=xd, qd=qd, yd=yd, xa=xa, lb=lb:
+                                      [T.gemm_lora(xd, q, xa, lb, out=yd) for q in qd])
+    dmed = interleaved_ms(dec_fns)
+    gemv_lora = {"timing": "median of 5 interleaved rounds, per launch"}
+    for tag, (shape, n) in dec_runs.items():
+        e = {"shape": shape, "weights": n,
+             "plain_us": round(dmed[f"{tag}_plain"] * 1e3 / n, 3)}
+        for r in (16, 64):
+            e[f"r{r}_us"] = round(dmed[f"{tag}_r{r}"] * 1e3 / n, 3)
+            e[f"r{r}_over_plain"] = round(dmed[f"{tag}_r{r}"] / dmed[f"{tag}_plain"], 4)
+        gemv_lora[tag] = e
+    del dec_fns
 
     t_q = stage_ms(0) / 1e3
     t_d = stage_ms(1) / 1e3
@@ -724,6 +758,7 @@ def main():
             },
             "variants": variants,
             "gemm_lora": lora,
+            "gemv_lora": gemv_lora,
             "gemm_llama7b_prefill": llama_prefill,
             "gemm_dx": {"what": "dX = dY . W_hat, M=2048 N=K=8192, NF4 double quant, bf16",
                         "ms": round(dx_ms, 4), "tflops": round(dx_tflops, 1),
