@@ -187,8 +187,9 @@ constexpr int kLoraMaxRR = 3;                // rows per team with a LoRA term (
 
 // MM rows of X per launch (rows >= mvalid are zero), NI chunks per lane, RR
 // rows of W per team and pass.  TW = 1 << twl waves per team.  N rows in
-// all (of every item).
-template <int MM, int NI, int RR, int SM, bool F16, bool GRP, int WV, bool LORA = false>
+// all (of every item).  LP: ranks of the LoRA term per lane slot.
+template <int MM, int NI, int RR, int SM, bool F16, bool GRP, int WV, bool LORA = false,
+          int LP = 1>
 __global__ __launch_bounds__(WV * 64, 4) void gemv_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, GemvArgs<GRP, LORA> items, int nitems, int mvalid,
     int N, int K, int twl, int xlds, LevelTable lv) {
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(WV * 64, 4) void gemv_kernel(
   // LoRA term: lane slot s takes ranks s, s + S, ... of XA's rows (binary32)
   // and of each row of B; unused ranks read zero from an offset past the
   // buffers, so no load sits behind a branch.
-  constexpr int kLP = LORA ? kLoraPer : 1;
+  constexpr int kLP = LORA ? LP : 1;
   uint32_t lof[kLP];
   float xav[MM][kLP];
   if constexpr (LORA) {
@@ -699,16 +700,26 @@ hipError_t launch_k(const Plan& p, const uint16_t* x, int64_t ldx, const GemvArg
     sm = rowq ? kScaleDqRow : kScaleDqLane;
   // The 8-wave form is instantiated for the plans that can choose it.
   constexpr bool kHalfOk = MM == 1 && NI <= 2 && !LORA;
+  // A LoRA term of rank 64 or less takes one rank per lane slot (a team has
+  // 64 slots or more): one load of XA and one per row of B instead of
+  // kLoraPer, most of them past the buffers.
+  bool lp1 = false;
+  if constexpr (LORA) lp1 = it.r <= 64;
 #define BNBX_GEMV_SM(SMV)                                                                      \
   if (sm == SMV) {                                                                             \
     if (kHalfOk && p.wv == kWavesHalf)                                                         \
       hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, SMV, F16, GRP, kHalfOk ? kWavesHalf : kWaves, LORA>), \
                          dim3(p.grid), dim3(kWavesHalf * 64), 0, stream, x, ldx, it, nitems,   \
                          mvalid, N, K, p.twl, p.xlds, lv);                                     \
+    else if (lp1)                                                                              \
+      hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, SMV, F16, GRP, kWaves, LORA, 1>),            \
+                         dim3(p.grid), dim3(kThreads), 0, stream, x, ldx, it, nitems, mvalid,  \
+                         N, K, p.twl, p.xlds, lv);                                             \
     else                                                                                       \
-      hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, SMV, F16, GRP, kWaves, LORA>), dim3(p.grid), \
-                         dim3(kThreads), 0, stream, x, ldx, it, nitems, mvalid, N, K, p.twl,   \
-                         p.xlds, lv);                                                          \
+      hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, SMV, F16, GRP, kWaves, LORA,                 \
+                                      LORA ? kLoraPer : 1>),                                   \
+                         dim3(p.grid), dim3(kThreads), 0, stream, x, ldx, it, nitems, mvalid,  \
+                         N, K, p.twl, p.xlds, lv);                                             \
   }
   // Four chunks per lane with per-lane scales spill registers for the
   // dynamic map, and for both maps with GRP: those plans are capped at three
