@@ -701,10 +701,13 @@ hipError_t launch_k(const Plan& p, const uint16_t* x, int64_t ldx, const GemvArg
   // The 8-wave form is instantiated for the plans that can choose it.
   constexpr bool kHalfOk = MM == 1 && NI <= 2 && !LORA;
   // A LoRA term of rank 64 or less takes one rank per lane slot (a team has
-  // 64 slots or more): one load of XA and one per row of B instead of
-  // kLoraPer, most of them past the buffers.
-  bool lp1 = false;
-  if constexpr (LORA) lp1 = it.r <= 64;
+  // 64 slots or more), of rank 128 or less two: one or two loads of XA and
+  // per row of B instead of kLoraPer, most of them past the buffers.
+  bool lp1 = false, lp2 = false;
+  if constexpr (LORA) {
+    lp1 = it.r <= 64;
+    lp2 = !lp1 && it.r <= 128;
+  }
 #define BNBX_GEMV_SM(SMV)                                                                      \
   if (sm == SMV) {                                                                             \
     if (kHalfOk && p.wv == kWavesHalf)                                                         \
@@ -713,6 +716,10 @@ hipError_t launch_k(const Plan& p, const uint16_t* x, int64_t ldx, const GemvArg
                          mvalid, N, K, p.twl, p.xlds, lv);                                     \
     else if (lp1)                                                                              \
       hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, SMV, F16, GRP, kWaves, LORA, 1>),            \
+                         dim3(p.grid), dim3(kThreads), 0, stream, x, ldx, it, nitems, mvalid,  \
+                         N, K, p.twl, p.xlds, lv);                                             \
+    else if (lp2)                                                                              \
+      hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, SMV, F16, GRP, kWaves, LORA, LORA ? 2 : 1>), \
                          dim3(p.grid), dim3(kThreads), 0, stream, x, ldx, it, nitems, mvalid,  \
                          N, K, p.twl, p.xlds, lv);                                             \
     else                                                                                       \

@@ -44,8 +44,9 @@ def test_lora_shapes(M, N, K, r, qt, dt):
                                      (3, 777, 1024, 48), (4, 1000, 512, 240), (1, 20000, 256, 32),
                                      (5, 4100, 4096, 16), (8, 333, 11008, 80), (16, 14336, 4096, 64),
                                      (13, 999, 512, 256), (16, 64, 64, 32),
-                                     # one rank per lane slot up to rank 64, four above it
-                                     (1, 1030, 8192, 64), (1, 1030, 8192, 80), (3, 257, 4096, 80)])
+                                     # one rank per lane slot up to rank 64, two up to 128, four above
+                                     (1, 1030, 8192, 64), (1, 1030, 8192, 80), (3, 257, 4096, 80),
+                                     (2, 4096, 4096, 128), (1, 700, 4096, 144)])
 def test_lora_decode_rows(M, N, K, r, qt, dt, dq_map):
     """Up to 16 rows of X: the decode GEMVs add the low-rank term before
     their reductions (up to 4 rows: ragged N, K = 11008 over two waves per
