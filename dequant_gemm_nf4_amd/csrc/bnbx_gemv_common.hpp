@@ -699,7 +699,7 @@ hipError_t launch_k(const Plan& p, const uint16_t* x, int64_t ldx, const GemvArg
   else if (dq)
     sm = rowq ? kScaleDqRow : kScaleDqLane;
   // The 8-wave form is instantiated for the plans that can choose it.
-  constexpr bool kHalfOk = MM == 1 && NI <= 2 && !LORA;
+  constexpr bool kHalfOk = MM == 1 && NI <= 2;
   // A LoRA term of rank 64 or less takes one rank per lane slot (a team has
   // 64 slots or more), of rank 128 or less two: one or two loads of XA and
   // per row of B instead of kLoraPer, most of them past the buffers.
@@ -708,25 +708,25 @@ hipError_t launch_k(const Plan& p, const uint16_t* x, int64_t ldx, const GemvArg
     lp1 = it.r <= 64;
     lp2 = !lp1 && it.r <= 128;
   }
+#define BNBX_GEMV_WV(SMV, LPV)                                                                 \
+  if (kHalfOk && p.wv == kWavesHalf)                                                           \
+    hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, SMV, F16, GRP, kHalfOk ? kWavesHalf : kWaves,  \
+                                    LORA, LPV>),                                               \
+                       dim3(p.grid), dim3(kWavesHalf * 64), 0, stream, x, ldx, it, nitems,     \
+                       mvalid, N, K, p.twl, p.xlds, lv);                                       \
+  else                                                                                         \
+    hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, SMV, F16, GRP, kWaves, LORA, LPV>),            \
+                       dim3(p.grid), dim3(kThreads), 0, stream, x, ldx, it, nitems, mvalid, N, \
+                       K, p.twl, p.xlds, lv);
 #define BNBX_GEMV_SM(SMV)                                                                      \
   if (sm == SMV) {                                                                             \
-    if (kHalfOk && p.wv == kWavesHalf)                                                         \
-      hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, SMV, F16, GRP, kHalfOk ? kWavesHalf : kWaves, LORA>), \
-                         dim3(p.grid), dim3(kWavesHalf * 64), 0, stream, x, ldx, it, nitems,   \
-                         mvalid, N, K, p.twl, p.xlds, lv);                                     \
-    else if (lp1)                                                                              \
-      hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, SMV, F16, GRP, kWaves, LORA, 1>),            \
-                         dim3(p.grid), dim3(kThreads), 0, stream, x, ldx, it, nitems, mvalid,  \
-                         N, K, p.twl, p.xlds, lv);                                             \
-    else if (lp2)                                                                              \
-      hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, SMV, F16, GRP, kWaves, LORA, LORA ? 2 : 1>), \
-                         dim3(p.grid), dim3(kThreads), 0, stream, x, ldx, it, nitems, mvalid,  \
-                         N, K, p.twl, p.xlds, lv);                                             \
-    else                                                                                       \
-      hipLaunchKernelGGL((gemv_kernel<MM, NI, RR, SMV, F16, GRP, kWaves, LORA,                 \
-                                      LORA ? kLoraPer : 1>),                                   \
-                         dim3(p.grid), dim3(kThreads), 0, stream, x, ldx, it, nitems, mvalid,  \
-                         N, K, p.twl, p.xlds, lv);                                             \
+    if (lp1) {                                                                                 \
+      BNBX_GEMV_WV(SMV, 1)                                                                     \
+    } else if (lp2) {                                                                          \
+      BNBX_GEMV_WV(SMV, LORA ? 2 : 1)                                                          \
+    } else {                                                                                   \
+      BNBX_GEMV_WV(SMV, LORA ? kLoraPer : 1)                                                   \
+    }                                                                                          \
   }
   // Four chunks per lane with per-lane scales spill registers for the
   // dynamic map, and for both maps with GRP: those plans are capped at three
@@ -745,6 +745,7 @@ hipError_t launch_k(const Plan& p, const uint16_t* x, int64_t ldx, const GemvArg
   }
   BNBX_GEMV_SM(kScaleDynRow)
 #undef BNBX_GEMV_SM
+#undef BNBX_GEMV_WV
   return hipGetLastError();
   }
 }

@@ -50,13 +50,17 @@ hipError_t launch_gemv_lora(const uint16_t* x, int64_t ldx, const uint8_t* packe
   const bool rowq = nkb <= 256 && nkb % 4 == 0 && ((uintptr_t)absmax & 3u) == 0;
   const int nicap = double_quant == kDqDynamic && !rowq ? 3 : 4;
   Plan p;
-  if (next_x_group(M, N < slab ? N : (int)slab, K, nicap, p) < M) return hipErrorNotSupported;
+  if (next_x_group(M, N < slab ? N : (int)slab, K, nicap, p, true) < M)
+    return hipErrorNotSupported;
   for (int64_t r0 = 0; r0 < N; r0 += slab) {
     const int n = (int)(N - r0 < slab ? N - r0 : slab);
-    if (!make_plan(p.mm, n, K, p, nicap)) return hipErrorNotSupported;
+    if (!make_plan(p.mm, n, K, p, nicap, true)) return hipErrorNotSupported;
     // at most kLoraMaxRR rows per team (the adapter's values take registers);
-    // rows past one pass are taken by further passes of the same launch
+    // rows past one pass are taken by further passes of the same launch, in
+    // 16-wave workgroups
     if (p.rr > kLoraMaxRR) {
+      p.wv = kWaves;
+      p.xlds = (int64_t)p.mm * K * 2 <= kXBytes ? 1 : 0;
       const int tpw = kWaves >> p.twl;
       p.rr = kLoraMaxRR;
       const int64_t g = ((int64_t)n + tpw * p.rr - 1) / (tpw * p.rr);

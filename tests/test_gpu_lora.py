@@ -46,7 +46,9 @@ def test_lora_shapes(M, N, K, r, qt, dt):
                                      (13, 999, 512, 256), (16, 64, 64, 32),
                                      # one rank per lane slot up to rank 64, two up to 128, four above
                                      (1, 1030, 8192, 64), (1, 1030, 8192, 80), (3, 257, 4096, 80),
-                                     (2, 4096, 4096, 128), (1, 700, 4096, 144)])
+                                     (2, 4096, 4096, 128), (1, 700, 4096, 144),
+                                     # two 8-wave workgroups per CU (three rows per wave)
+                                     (1, 9000, 512, 128), (1, 9000, 1024, 256), (1, 11008, 4096, 16)])
 def test_lora_decode_rows(M, N, K, r, qt, dt, dq_map):
     """Up to 16 rows of X: the decode GEMVs add the low-rank term before
     their reductions (up to 4 rows: ragged N, K = 11008 over two waves per
